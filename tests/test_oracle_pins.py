@@ -1,0 +1,463 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself through a retyped formula: each
+test checks it against a number printed on the pages (tests/golden), a closed
+form, a library routine (PyTorch, SciPy, Hugging Face transformers' Qwen3 and
+Llama layers), an invariant, or brute force over a tiny grid.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import synth
+from oracle import DualAROracle, Sampling, bf16_round, count_params, rope_table, sample_token
+from oracle.dualar_oracle import apply_rope, rms_norm, silu
+from tests.oracle_helpers import f32_weights, mini_model
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "s2_page_numbers.json")))
+
+
+def g(key):
+    return GOLD[key]["value"]
+
+
+# --------------------------------------------------------------------------
+# C1 / C2: parameter counts and weights read per frame
+# --------------------------------------------------------------------------
+
+def test_param_counts_match_checkpoint():
+    s2_noqk = synth.model("s2", fast_qk_norm=0)
+    slow = count_params(s2_noqk, "slow")
+    fast = count_params(s2_noqk, "fast")
+    fusion = count_params(s2_noqk, "fusion")
+    assert slow == g("text_model_params")
+    assert slow - g("qwen3_4b_params") == g("extra_embedding_rows") * 2560
+    assert fusion == g("fusion_rows") * 2560
+    assert round(fusion / 1e6, 1) == g("fusion_params_M")
+    assert round(fast / 1e6, 1) == g("fast_params_M")
+    assert slow + fast + fusion == g("checkpoint_params")
+    # The fast AR with QK-norm on (as the measured workloads use it) has two
+    # 128-gains more per layer; the exact checkpoint total then no longer holds.
+    s2_qk = synth.model("s2")
+    assert count_params(s2_qk, "fast") - fast == 4 * 2 * 128
+    assert count_params(s2_qk) != g("checkpoint_params")
+
+
+def test_weights_read_per_frame():
+    m = synth.model("s2", fast_qk_norm=0)
+    from oracle.dualar_oracle import param_shapes
+    sh = param_shapes(m)
+    slow_step = count_params(m, "slow")   # 36 layers + tied head (+ final norm)
+    fast_pass = sum(int(np.prod(v)) for k, v in sh.items()
+                    if k.startswith("fast_layers.") or k in ("fast_output", "fast_norm"))
+    assert round(slow_step / 1e9, 2) == g("slow_step_weights_B")
+    assert round(fast_pass / 1e6, 1) == g("fast_pass_weights_M")
+    assert round(10 * fast_pass / 1e9, 2) == g("ten_fast_passes_B")
+    # Flattened single-AR estimate: ten slow steps per frame instead of one
+    # slow step plus ten fast passes, scaled from RTF 0.34.
+    ratio = 10 * slow_step / (slow_step + 10 * fast_pass)
+    assert round(g("rtf_batch1") * ratio, 2) == g("flattened_rtf")
+
+
+def test_vocabulary_layout():
+    m = synth.model("s2")
+    assert m["semantic_begin_id"] == g("semantic_first_id")
+    assert m["semantic_end_id"] == g("semantic_last_id")
+    assert m["semantic_end_id"] - m["semantic_begin_id"] + 1 == m["codebook_size"]
+    assert g("bpe_ids") + g("added_tokens") == m["semantic_begin_id"]
+    assert m["semantic_end_id"] + 1 + g("padding_rows") == g("vocab_size") == m["vocab_size"]
+    assert g("bpe_ids") <= m["end_id"] < m["semantic_begin_id"]
+    assert 9 * (m["codebook_size"] - 1024) * 2560 / 1e6 == pytest.approx(g("unreachable_fusion_M"), abs=0.05)
+
+
+# --------------------------------------------------------------------------
+# C3: fusion closed form
+# --------------------------------------------------------------------------
+
+def test_fusion_closed_form_sqrt11():
+    m = mini_model(num_codebooks=10, codebook_size=16, semantic_begin_id=200, semantic_end_id=215)
+    w = f32_weights(m)
+    w["tok_embedding"][:] = 1.0
+    for k in range(10):
+        w["codebook_embedding"][k * 16:(k + 1) * 16] = k + 1.0
+    o = DualAROracle(m, w, max_seq=8)
+    col = np.array([203, 3] + [5] * 9)
+    assert np.allclose(o.embed(col), 56.0 / math.sqrt(11.0), rtol=0, atol=1e-14)
+    # text positions take the LM row alone, unscaled
+    assert np.array_equal(o.embed(np.array([7] + [0] * 10)), np.ones(32))
+
+
+def test_fusion_indexing():
+    m = mini_model(num_codebooks=10, codebook_size=16)
+    w = f32_weights(m)
+    w["tok_embedding"][:] = 0.0
+    w["tok_embedding"][205] = 1000.0
+    w["codebook_embedding"][:] = np.arange(160, dtype=np.float64)[:, None]  # row r = r
+    o = DualAROracle(m, w, max_seq=8)
+    q = [5, 1, 2, 3, 4, 5, 6, 7, 8, 15]
+    col = np.array([205] + q)
+    expect = (1000.0 + sum(k * 16 + q[k] for k in range(10))) / math.sqrt(11.0)
+    assert np.allclose(o.embed(col), expect, rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# C4: the semantic logit mask
+# --------------------------------------------------------------------------
+
+def _s2_vocab_oracle():
+    m = mini_model(vocab_size=155776, semantic_begin_id=151678, semantic_end_id=155773,
+                   end_id=151645, num_codebooks=10, codebook_size=4096, dim=16, fast_dim=16,
+                   head_dim=4, fast_head_dim=4, ffn_dim=16, fast_ffn_dim=16, n_layer=1, n_fast_layer=1)
+    return m, DualAROracle(m, f32_weights(m), max_seq=4)
+
+
+def test_mask_allows_exactly_4097():
+    m, o = _s2_vocab_oracle()
+    assert int(np.isfinite(o.bias).sum()) == g("unmasked_logits")
+    assert np.all(o.bias[np.isfinite(o.bias)] == 0.0)
+    assert np.isfinite(o.bias[m["end_id"]])
+
+
+def test_mask_rejects_text_argmax_and_takes_end():
+    m, o = _s2_vocab_oracle()
+    rng = np.random.default_rng(0)
+    logits = rng.standard_normal(m["vocab_size"])
+    logits[17] = 50.0                        # global argmax at an ordinary text id
+    logits[151700] = 10.0                    # best semantic id
+    s = Sampling(greedy=True)
+    assert o.slow_sample(logits, s, None, 0) == 151700
+    logits[m["end_id"]] = 20.0               # argmax at <|im_end|> -> end
+    assert o.slow_sample(logits, s, None, 0) == m["end_id"]
+    # min_frames keeps <|im_end|> masked until that many frames are out
+    s2 = Sampling(greedy=True, min_frames=3)
+    assert o.slow_sample(logits, s2, None, 2) == 151700
+    assert o.slow_sample(logits, s2, None, 3) == m["end_id"]
+    # top-p draws never leave the allowed set either
+    s3 = Sampling(greedy=False, top_p=0.95)
+    for u in np.linspace(0.0, 0.999, 40):
+        t = o.slow_sample(logits, s3, u, 0)
+        assert np.isfinite(o.bias[t])
+
+
+def test_end_stops_the_sequence():
+    m = mini_model()
+    o = DualAROracle(m, f32_weights(m), max_seq=64)
+    seq = o.new_sequence()
+    prompt = synth.make_prompts(m, ("fixed", 2, 4, 2), [8])[0]
+    o.prefill(seq, prompt, Sampling())
+    real = o.slow_logits
+
+    def forced(h):
+        z = real(h)
+        z[m["end_id"]] = 1e9
+        return z
+    o.slow_logits = forced
+    fr = o.decode_frame(seq, Sampling())
+    assert fr == [m["end_id"]] + [-1] * m["num_codebooks"]
+    assert seq.done
+    assert o.decode_frame(seq, Sampling()) == [-1] * (m["num_codebooks"] + 1)
+
+
+# --------------------------------------------------------------------------
+# C5: one slow pass, N fast passes and N-1 fast samples per frame
+# --------------------------------------------------------------------------
+
+def test_pass_counts_per_frame():
+    m = synth.model("tiny")
+    o = DualAROracle(m, f32_weights(m), max_seq=64)
+    seq = o.new_sequence()
+    prompt = synth.make_prompts(m, ("fixed", 4, 16, 12), [32])[0]
+    o.prefill(seq, prompt, Sampling())
+    frames = 5
+    for _ in range(frames):
+        o.decode_frame(seq, Sampling())
+    N = m["num_codebooks"]
+    assert o.count.slow_passes == 1 + frames          # prefill counts once
+    assert o.count.fast_passes == N * (frames + 1)
+    assert o.count.fast_samples == (N - 1) * (frames + 1)
+    assert o.count.slot_writes == list(range(N)) * (frames + 1)
+
+
+# --------------------------------------------------------------------------
+# C6: RoPE, RMSNorm, SwiGLU against library routines / invariants
+# --------------------------------------------------------------------------
+
+def test_rope_table_is_bf16_of_cos_sin():
+    P, hd, base = 300, 128, 1.0e6
+    cos, sin = rope_table(P, hd, base)
+    assert np.all(cos[0] == 1.0) and np.all(sin[0] == 0.0)
+    inv = 1.0 / (base ** (torch.arange(0, hd, 2, dtype=torch.float64) / hd))
+    ang = torch.arange(P, dtype=torch.float64)[:, None] * inv[None, :]
+    tc = torch.cos(ang).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    ts = torch.sin(ang).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    # double rounding through fp32 can differ from direct RNE only on exact ties
+    assert np.mean(cos == tc) > 0.999 and np.mean(sin == ts) > 0.999
+    assert np.max(np.abs(cos - tc)) <= 2.0 ** -8 and np.max(np.abs(sin - ts)) <= 2.0 ** -8
+
+
+def test_rope_is_complex_rotation_of_interleaved_pairs():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((3, 16))
+    ang = rng.uniform(-3, 3, size=8)
+    got = apply_rope(x, np.cos(ang), np.sin(ang))
+    xc = torch.view_as_complex(torch.from_numpy(x).reshape(3, 8, 2).contiguous())
+    ref = torch.view_as_real(xc * torch.polar(torch.ones(8, dtype=torch.float64),
+                                              torch.from_numpy(ang))).reshape(3, 16).numpy()
+    assert np.allclose(got, ref, atol=1e-14)
+
+
+def test_rope_relative_position():
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    theta = 1.0 / (1.0e6 ** (np.arange(32) * 2.0 / 64))
+
+    def rot(v, p):
+        return apply_rope(v, np.cos(p * theta), np.sin(p * theta))
+    d = [rot(q, m) @ rot(k, n) for m, n in [(5, 2), (13, 10), (103, 100)]]
+    assert np.allclose(d, d[0], atol=1e-12)
+    assert np.allclose(rot(q, 0), q)
+
+
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 37)) * 3
+    gsc = rng.standard_normal(37)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (37,), torch.from_numpy(gsc), eps=1e-6)
+    assert np.allclose(rms_norm(x, gsc, 1e-6), ref.numpy(), atol=1e-13)
+    assert np.allclose(rms_norm(7.5 * x, gsc, 0.0), rms_norm(x, gsc, 0.0), atol=1e-13)
+
+
+def test_silu_matches_scipy():
+    x = np.linspace(-30, 30, 1001)
+    assert np.allclose(silu(x), x * scipy.special.expit(x), atol=1e-14)
+
+
+def test_bf16_round_matches_torch_rne():
+    rng = np.random.default_rng(4)
+    f = rng.standard_normal(20000).astype(np.float32) * np.float32(10.0)
+    bits = f.view(np.uint32).copy()
+    bits[:2000] = (bits[:2000] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)   # exact ties
+    f = bits.view(np.float32)
+    ref = torch.from_numpy(f).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bf16_round(f.astype(np.float64)), ref)
+
+
+# --------------------------------------------------------------------------
+# Whole stacks against Hugging Face Qwen3 (QK-norm) and Llama (no QK-norm)
+# --------------------------------------------------------------------------
+
+def _hf_stack(m, w, which):
+    from transformers import LlamaConfig, LlamaForCausalLM, Qwen3Config, Qwen3ForCausalLM
+    if which == "slow":
+        pre, n, dim, nh, nkv, hd, ffn, qk = ("layers", m["n_layer"], m["dim"], m["n_head"],
+                                             m["n_kv_head"], m["head_dim"], m["ffn_dim"], m["slow_qk_norm"])
+        vocab, emb, head, norm, tied = m["vocab_size"], "tok_embedding", "tok_embedding", "norm", True
+    else:
+        pre, n, dim, nh, nkv, hd, ffn, qk = ("fast_layers", m["n_fast_layer"], m["fast_dim"], m["fast_n_head"],
+                                             m["fast_n_kv_head"], m["fast_head_dim"], m["fast_ffn_dim"],
+                                             m["fast_qk_norm"])
+        vocab, emb, head, norm, tied = m["codebook_size"], "fast_embeddings", "fast_output", "fast_norm", False
+    kw = dict(vocab_size=vocab, hidden_size=dim, intermediate_size=ffn, num_hidden_layers=n,
+              num_attention_heads=nh, num_key_value_heads=nkv, head_dim=hd, rms_norm_eps=m["norm_eps"],
+              tie_word_embeddings=tied, attention_bias=False, max_position_embeddings=4096)
+    cls, cfg = (Qwen3ForCausalLM, Qwen3Config(**kw)) if qk else (LlamaForCausalLM, LlamaConfig(mlp_bias=False, **kw))
+    cfg._attn_implementation = "eager"
+    model = cls(cfg).to(torch.float64).eval()
+    # The page's RoPE pairs (2i, 2i+1); HF pairs (i, i + hd/2).  Permuting the
+    # rows of wq/wk (and the QK-norm gains) within each head maps one onto the
+    # other and leaves every q.k product unchanged.
+    perm = np.concatenate([np.arange(0, hd, 2), np.arange(1, hd, 2)])
+
+    def rows(W, heads):
+        return W.reshape(heads, hd, -1)[:, perm, :].reshape(heads * hd, -1)
+    sd = {"model.embed_tokens.weight": w[emb], "model.norm.weight": w[norm], "lm_head.weight": w[head]}
+    for i in range(n):
+        p, hp = f"{pre}.{i}.", f"model.layers.{i}."
+        sd[hp + "self_attn.q_proj.weight"] = rows(w[p + "wq"], nh)
+        sd[hp + "self_attn.k_proj.weight"] = rows(w[p + "wk"], nkv)
+        sd[hp + "self_attn.v_proj.weight"] = w[p + "wv"]
+        sd[hp + "self_attn.o_proj.weight"] = w[p + "wo"]
+        if qk:
+            sd[hp + "self_attn.q_norm.weight"] = w[p + "q_norm"][perm]
+            sd[hp + "self_attn.k_norm.weight"] = w[p + "k_norm"][perm]
+        sd[hp + "mlp.gate_proj.weight"] = w[p + "w1"]
+        sd[hp + "mlp.up_proj.weight"] = w[p + "w3"]
+        sd[hp + "mlp.down_proj.weight"] = w[p + "w2"]
+        sd[hp + "input_layernorm.weight"] = w[p + "attention_norm"]
+        sd[hp + "post_attention_layernorm.weight"] = w[p + "ffn_norm"]
+    model.load_state_dict({k: torch.from_numpy(np.asarray(v, dtype=np.float64)) for k, v in sd.items()},
+                          strict=False)
+    base = m["rope_base"]
+    inv = 1.0 / (base ** (torch.arange(0, hd, 2, dtype=torch.float64) / hd))
+
+    def rotary(x, position_ids):
+        ang = position_ids[0].to(torch.float64)[:, None] * inv[None, :]
+        c = torch.cos(ang).to(torch.float32).to(torch.bfloat16).to(torch.float64)
+        s = torch.sin(ang).to(torch.float32).to(torch.bfloat16).to(torch.float64)
+        return torch.cat([c, c], -1)[None], torch.cat([s, s], -1)[None]
+    model.model.rotary_emb.forward = rotary
+    return model
+
+
+@pytest.mark.parametrize("qk", [1, 0])
+def test_slow_stack_matches_hf(qk):
+    m = mini_model(slow_qk_norm=qk, n_layer=3)
+    w = f32_weights(m, seed=5)
+    o = DualAROracle(m, w, max_seq=64)
+    ids = np.random.default_rng(6).integers(0, m["text_vocab"], size=20)
+    seq = o.new_sequence()
+    X = o.slow_seq(seq, np.stack([w["tok_embedding"][i].astype(np.float64) for i in ids]), 0)
+    ours = np.stack([o.slow_logits(x) for x in X])
+    with torch.no_grad():
+        ref = _hf_stack(m, w, "slow")(input_ids=torch.from_numpy(ids)[None]).logits[0].numpy()
+    # HF's RMSNorm and eager softmax run in fp32 even for a float64 model, so
+    # agreement is to fp32 rounding; a wrong term or index is off by O(1e-2).
+    assert np.allclose(ours, ref, rtol=1e-5, atol=1e-6)
+    assert np.max(np.abs(ours - ref)) < 1e-5 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("qk", [1, 0])
+def test_fast_stack_matches_hf(qk):
+    m = mini_model(fast_qk_norm=qk)
+    w = f32_weights(m, seed=7)
+    o = DualAROracle(m, w, max_seq=8)
+    rng = np.random.default_rng(8)
+    h = rng.standard_normal(m["fast_dim"])
+    codes = rng.integers(0, m["codebook_size"], size=m["num_codebooks"])
+    ours = o.fast_teacher_forced(h, codes)
+    X = np.concatenate([h[None], w["fast_embeddings"][codes[:-1]].astype(np.float64)])
+    with torch.no_grad():
+        ref = _hf_stack(m, w, "fast")(inputs_embeds=torch.from_numpy(X)[None]).logits[0].numpy()
+    assert np.allclose(ours, ref[1:], rtol=1e-5, atol=1e-6)
+    assert np.max(np.abs(ours - ref[1:])) < 1e-5 * np.max(np.abs(ref))
+
+
+# --------------------------------------------------------------------------
+# C8: incremental decoding equals the full causal forward
+# --------------------------------------------------------------------------
+
+def test_prefill_matrix_equals_stepwise():
+    m = synth.model("tiny")
+    w = f32_weights(m)
+    prompt = synth.make_prompts(m, ("fixed", 4, 16, 12), [32])[0]
+    a, b = DualAROracle(m, w, max_seq=64), DualAROracle(m, w, max_seq=64)
+    sa, sb = a.new_sequence(), b.new_sequence()
+    fa = a.prefill(sa, prompt, Sampling())
+    fb = b.prefill_stepwise(sb, prompt, Sampling())
+    assert fa == fb
+    assert np.allclose(sa.k[:, :32], sb.k[:, :32], atol=1e-12)
+    assert np.allclose(sa.v[:, :32], sb.v[:, :32], atol=1e-12)
+    assert np.allclose(a.taps["slow_logits"], b.taps["slow_logits"], atol=1e-10)
+
+
+def test_fast_incremental_equals_teacher_forced():
+    m = synth.model("tiny")
+    o = DualAROracle(m, f32_weights(m), max_seq=8)
+    h = np.random.default_rng(9).standard_normal(m["fast_dim"])
+    codes = o.fast_frame(h, 17, Sampling())
+    inc = o.taps["fast_logits"]
+    full = o.fast_teacher_forced(h, codes)
+    assert np.allclose(inc, full, atol=1e-10)
+    assert codes[1:] == [int(np.argmax(z)) for z in full]
+
+
+# --------------------------------------------------------------------------
+# C9: the sampler against brute force
+# --------------------------------------------------------------------------
+
+def test_greedy_lowest_id_on_ties():
+    z = np.array([0.1, 3.0, -1.0, 3.0, 2.0])
+    assert sample_token(z, Sampling(greedy=True)) == 1
+    z[0] = -np.inf
+    assert sample_token(z, Sampling(greedy=True)) == 1
+
+
+@pytest.mark.parametrize("top_p,expect", [
+    (1.0, [0.5, 0.25, 0.15, 0.07, 0.03]),
+    (0.8, [0.5 / 0.9, 0.25 / 0.9, 0.15 / 0.9, 0.0, 0.0]),
+    (0.4, [1.0, 0.0, 0.0, 0.0, 0.0]),
+])
+def test_top_p_frequencies_on_a_grid(top_p, expect):
+    p = np.array([0.25, 0.03, 0.5, 0.07, 0.15])       # shuffled ids
+    order = [2, 0, 4, 3, 1]                          # ids by descending p
+    _grid(p, order, top_p, expect)
+
+
+def test_top_p_nucleus_is_smallest_set_reaching_p():
+    # Nucleus sampling keeps the smallest prefix whose mass reaches top_p: with
+    # four equal probabilities (exact 0.25 each) and top_p = 0.5 the prefix of
+    # two ids reaches 0.5 exactly and is the nucleus; ties go by ascending id.
+    _grid(np.full(4, 0.25), [0, 1, 2, 3], 0.5, [0.5, 0.5, 0.0, 0.0])
+
+
+def _grid(p, order, top_p, expect):
+    M = 20000
+    counts = np.zeros(5)
+    s = Sampling(greedy=False, top_p=top_p)
+    for i in range(M):
+        counts[sample_token(np.log(p), s, (i + 0.5) / M)] += 1
+    assert np.allclose(counts[order] / M, expect, atol=2.0 / M)
+
+
+def test_temperature_sharpens():
+    p = np.array([0.6, 0.3, 0.1])
+    M = 6000
+    c = np.zeros(3)
+    for i in range(M):
+        c[sample_token(np.log(p), Sampling(greedy=False, temperature=0.5), (i + 0.5) / M)] += 1
+    q = p ** 2 / np.sum(p ** 2)
+    assert np.allclose(c / M, q, atol=2.0 / M)
+
+
+def test_masked_ids_never_drawn():
+    z = np.log(np.array([0.2, 0.2, 0.2, 0.2, 0.2]))
+    z[[1, 3]] = -np.inf
+    s = Sampling(greedy=False, top_p=1.0)
+    got = {sample_token(z, s, u) for u in np.linspace(0, 0.9999, 101)}
+    assert got == {0, 2, 4}
+
+
+# --------------------------------------------------------------------------
+# End-to-end sanity of the tiny workload
+# --------------------------------------------------------------------------
+
+def test_bf16_kv_cache_rounding():
+    # bf16 models keep the K/V cache in bf16: stored entries are bf16 values,
+    # within half an ulp of the unrounded ones (first layer: same inputs).
+    m = mini_model(weight_dtype="bf16")
+    w = synth.weights_as_f32(m, synth.make_weights(m, seed=3, threads=2))
+    prompt = synth.make_prompts(m, ("fixed", 2, 8, 2), [12])[0]
+    a = DualAROracle(m, w, max_seq=32)
+    b = DualAROracle(m, w, max_seq=32)
+    b.kv_bf16 = False
+    sa, sb = a.new_sequence(), b.new_sequence()
+    a.prefill(sa, prompt, Sampling())
+    b.prefill(sb, prompt, Sampling())
+    ka, kb = sa.k[0, :12], sb.k[0, :12]
+    assert np.array_equal(bf16_round(ka), ka) and np.any(ka != 0)
+    assert not np.array_equal(bf16_round(kb), kb)
+    assert np.all(np.abs(ka - kb) <= np.abs(kb) * 2.0 ** -8)
+    assert np.array_equal(bf16_round(sa.v[0, :12]), sa.v[0, :12])
+
+
+def test_tiny_workload_decodes_semantic_frames():
+    m = synth.model("tiny")
+    w = f32_weights(m)
+    prompt = synth.make_prompts(m, ("fixed", 4, 16, 12), [32])[0]
+    runs = []
+    for _ in range(2):
+        o = DualAROracle(m, w, max_seq=64)
+        seq = o.new_sequence()
+        fr = [o.prefill(seq, prompt, Sampling())]
+        fr += [o.decode_frame(seq, Sampling()) for _ in range(4)]
+        runs.append(fr)
+    assert runs[0] == runs[1]
+    for f in runs[0]:
+        assert m["semantic_begin_id"] <= f[0] <= m["semantic_end_id"]
+        assert f[1] == f[0] - m["semantic_begin_id"]
+        assert all(0 <= q < m["codebook_size"] for q in f[1:])
