@@ -1,0 +1,258 @@
+"""ctypes binding of libdualar.so (include/dualar.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+library.  PyTorch supplies device memory (weights, workspace, inputs,
+outputs) and the stream.  If the library is missing this module raises on
+import of the library; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdualar.so")
+
+OK = 0
+STATUS = {0: "OK", -1: "INVALID_ARG", -2: "NO_DEVICE", -3: "WORKSPACE", -4: "CONTEXT_FULL",
+          -5: "BAD_TOKEN", -6: "STATE", -7: "HIP", -8: "DEVICE_FAULT"}
+F32, BF16 = 0, 1
+
+
+class DualARError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class Config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "n_layer", "dim", "n_head", "n_kv_head", "head_dim", "ffn_dim", "vocab_size",
+        "n_fast_layer", "fast_dim", "fast_n_head", "fast_n_kv_head", "fast_head_dim", "fast_ffn_dim",
+        "slow_qk_norm", "fast_qk_norm", "num_codebooks", "codebook_size",
+        "semantic_begin_id", "semantic_end_id", "end_id", "scale_codebook_embeddings")] + [
+        ("rope_base", C.c_float), ("norm_eps", C.c_float),
+        ("weight_dtype", C.c_int32), ("max_batch", C.c_int32), ("max_seq_len", C.c_int32)]
+
+
+_LAYER_FIELDS = ("attention_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w1", "w3", "w2")
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in _LAYER_FIELDS]
+
+
+class Weights(C.Structure):
+    _fields_ = [("tok_embedding", C.c_void_p), ("codebook_embedding", C.c_void_p), ("norm", C.c_void_p),
+                ("layers", C.POINTER(LayerWeights)), ("fast_layers", C.POINTER(LayerWeights)),
+                ("fast_embeddings", C.c_void_p), ("fast_norm", C.c_void_p), ("fast_output", C.c_void_p)]
+
+
+class Sampling(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_p", C.c_float), ("greedy", C.c_int32),
+                ("min_frames", C.c_int32)]
+
+
+class Taps(C.Structure):
+    _fields_ = [("fused_x", C.c_void_p), ("slow_hidden", C.c_void_p), ("slow_logits", C.c_void_p),
+                ("fast_logits", C.c_void_p)]
+
+
+# Every symbol the header declares.
+EXPORTS = ("dualar_workspace_bytes", "dualar_create", "dualar_prefill", "dualar_decode_frames",
+           "dualar_fast_frames", "dualar_sync", "dualar_destroy", "dualar_status_string",
+           "dualar_last_error")
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdualar.so and declare its signatures (fails loudly if absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is not built; run `python -m dual_autoregressive_tts_amd.build`")
+    lib = C.CDLL(path)
+    P, I32, VP = C.POINTER, C.c_int32, C.c_void_p
+    lib.dualar_workspace_bytes.argtypes = [P(Config)]
+    lib.dualar_workspace_bytes.restype = C.c_size_t
+    lib.dualar_create.argtypes = [P(Config), P(Weights), VP, C.c_size_t, VP, P(VP)]
+    lib.dualar_create.restype = I32
+    lib.dualar_prefill.argtypes = [VP, I32, VP, I32, P(I32), P(Sampling), VP, VP]
+    lib.dualar_prefill.restype = I32
+    lib.dualar_decode_frames.argtypes = [VP, I32, P(Sampling), VP, VP, VP, P(Taps)]
+    lib.dualar_decode_frames.restype = I32
+    lib.dualar_fast_frames.argtypes = [VP, I32, I32, VP, VP, P(Sampling), VP, VP, P(Taps)]
+    lib.dualar_fast_frames.restype = I32
+    lib.dualar_sync.argtypes = [VP, P(I32)]
+    lib.dualar_sync.restype = I32
+    lib.dualar_destroy.argtypes = [VP]
+    lib.dualar_destroy.restype = None
+    lib.dualar_status_string.argtypes = [I32]
+    lib.dualar_status_string.restype = C.c_char_p
+    lib.dualar_last_error.argtypes = [VP]
+    lib.dualar_last_error.restype = C.c_char_p
+    _lib = lib
+    return lib
+
+
+def make_config(m: dict, max_batch: int, max_seq_len: int, inherit_fast: bool = False) -> Config:
+    """Model dict (synth.MODELS layout) -> dualar_config.  With inherit_fast,
+    fast_* sizes are passed as 0 (inherit) where they equal the slow ones."""
+    c = Config()
+    for f in ("n_layer", "dim", "n_head", "n_kv_head", "head_dim", "ffn_dim", "vocab_size",
+              "n_fast_layer", "fast_dim", "fast_n_head", "fast_n_kv_head", "fast_head_dim",
+              "fast_ffn_dim", "slow_qk_norm", "fast_qk_norm", "num_codebooks", "codebook_size",
+              "semantic_begin_id", "semantic_end_id", "end_id", "scale_codebook_embeddings"):
+        setattr(c, f, int(m[f]))
+    if inherit_fast:
+        for f, s in (("fast_dim", "dim"), ("fast_n_head", "n_head"), ("fast_n_kv_head", "n_kv_head"),
+                     ("fast_head_dim", "head_dim"), ("fast_ffn_dim", "ffn_dim")):
+            if m[f] == m[s]:
+                setattr(c, f, 0)
+        if m["fast_qk_norm"] == m["slow_qk_norm"]:
+            c.fast_qk_norm = -1
+    c.rope_base = float(m["rope_base"])
+    c.norm_eps = float(m["norm_eps"])
+    c.weight_dtype = BF16 if m["weight_dtype"] == "bf16" else F32
+    c.max_batch = int(max_batch)
+    c.max_seq_len = int(max_seq_len)
+    return c
+
+
+def workspace_bytes(cfg: Config) -> int:
+    return int(load_library().dualar_workspace_bytes(C.byref(cfg)))
+
+
+def upload_weights(m: dict, w: dict, device="cuda"):
+    """numpy weights from synth.make_weights -> device tensors (bf16 or fp32)."""
+    import torch
+    out = {}
+    for k, v in w.items():
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        if m["weight_dtype"] == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        out[k] = t.to(device)
+    return out
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+class DualAR:
+    """One decode context (dualar_create) over device weights."""
+
+    def __init__(self, m: dict, dev_weights: dict, max_batch: int, max_seq_len: int, stream=None,
+                 inherit_fast: bool = False):
+        import torch
+        self.torch = torch
+        self.lib = load_library()
+        self.m = m
+        self.N = m["num_codebooks"]
+        self.cfg = make_config(m, max_batch, max_seq_len, inherit_fast)
+        self.ws_bytes = workspace_bytes(self.cfg)
+        if self.ws_bytes == 0:
+            raise DualARError(-1, "invalid config")
+        self.dev_weights = dev_weights
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self._keep = []
+        self.wstruct = self._weights_struct(dev_weights)
+        h = C.c_void_p()
+        st = self.lib.dualar_create(C.byref(self.cfg), C.byref(self.wstruct), _ptr(self.workspace),
+                                    self.ws_bytes, C.c_void_p(self.stream.cuda_stream), C.byref(h))
+        if st != OK:
+            raise DualARError(st, self.lib.dualar_last_error(None).decode())
+        self.h = h
+        self.batch = 0
+
+    def _weights_struct(self, w):
+        m = self.m
+
+        def layers(prefix, n):
+            arr = (LayerWeights * n)()
+            for i in range(n):
+                for f in _LAYER_FIELDS:
+                    t = w.get(f"{prefix}.{i}.{f}")
+                    setattr(arr[i], f, None if t is None else t.data_ptr())
+            self._keep.append(arr)
+            return arr
+        s = Weights()
+        s.tok_embedding = w["tok_embedding"].data_ptr()
+        s.codebook_embedding = w["codebook_embedding"].data_ptr()
+        s.norm = w["norm"].data_ptr()
+        s.layers = layers("layers", m["n_layer"])
+        s.fast_layers = layers("fast_layers", m["n_fast_layer"])
+        s.fast_embeddings = w["fast_embeddings"].data_ptr()
+        s.fast_norm = w["fast_norm"].data_ptr()
+        s.fast_output = w["fast_output"].data_ptr()
+        return s
+
+    def _check(self, st):
+        if st != OK:
+            raise DualARError(st, self.lib.dualar_last_error(self.h).decode())
+
+    @staticmethod
+    def sampling(greedy=True, temperature=1.0, top_p=1.0, min_frames=0) -> Sampling:
+        return Sampling(float(temperature), float(top_p), int(bool(greedy)), int(min_frames))
+
+    def prefill(self, tokens, prompt_len, sampling: Sampling, uniforms=None):
+        """tokens: cuda int32 [B][N+1][T]; prompt_len: host ints [B]."""
+        torch = self.torch
+        B, _, T = tokens.shape
+        plen = (C.c_int32 * B)(*[int(x) for x in prompt_len])
+        frame0 = torch.empty((B, self.N + 1), dtype=torch.int32, device="cuda")
+        self._check(self.lib.dualar_prefill(self.h, B, _ptr(tokens), T, plen, C.byref(sampling),
+                                            _ptr(uniforms), _ptr(frame0)))
+        self.batch = B
+        return frame0
+
+    def decode_frames(self, n: int, sampling: Sampling, uniforms=None, taps: bool = False, out=None):
+        torch = self.torch
+        B, N, m = self.batch, self.N, self.m
+        codes = out if out is not None else torch.empty((B, n, N + 1), dtype=torch.int32, device="cuda")
+        emitted = torch.empty(B, dtype=torch.int32, device="cuda")
+        tp, td = None, None
+        if taps:
+            td = {"fused_x": torch.empty((B, m["dim"]), device="cuda"),
+                  "slow_hidden": torch.empty((B, m["dim"]), device="cuda"),
+                  "slow_logits": torch.empty((B, m["vocab_size"]), device="cuda"),
+                  "fast_logits": torch.empty((B, N - 1, m["codebook_size"]), device="cuda")}
+            tp = Taps(*[td[k].data_ptr() for k in ("fused_x", "slow_hidden", "slow_logits", "fast_logits")])
+        self._check(self.lib.dualar_decode_frames(self.h, n, C.byref(sampling), _ptr(uniforms), _ptr(codes),
+                                                  _ptr(emitted), C.byref(tp) if tp is not None else None))
+        return codes, emitted, td
+
+    def fast_frames(self, hidden, q0, sampling: Sampling, uniforms=None, taps: bool = False, out=None):
+        """hidden: cuda fp32 [F][B][dim]; q0: cuda int32 [F][B] -> codes [B][F][N]."""
+        torch = self.torch
+        F, B = q0.shape
+        codes = out if out is not None else torch.empty((B, F, self.N), dtype=torch.int32, device="cuda")
+        tp, td = None, None
+        if taps:
+            td = {"fast_logits": torch.empty((B, self.N - 1, self.m["codebook_size"]), device="cuda")}
+            tp = Taps(None, None, None, td["fast_logits"].data_ptr())
+        self._check(self.lib.dualar_fast_frames(self.h, B, F, _ptr(hidden), _ptr(q0), C.byref(sampling),
+                                                _ptr(uniforms), _ptr(codes), C.byref(tp) if tp is not None else None))
+        return codes, td
+
+    def sync(self) -> int:
+        st = C.c_int32(0)
+        self._check(self.lib.dualar_sync(self.h, C.byref(st)))
+        return st.value
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.dualar_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

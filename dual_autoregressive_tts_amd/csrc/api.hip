@@ -1,0 +1,567 @@
+// Host side of the C ABI declared in include/dualar.h: validation, workspace
+// carve-up, per-sequence state and the launch order of one decode frame.
+//
+// One frame ([P2] "Two autoregressions, because ten codebooks is ten times
+// the sequence", the decode_one_token_ar order):
+//   fusion of the previous frame -> n_layer x {QKV(+RMSNorm), attention
+//   (+QK-norm, RoPE, cache append), O(+residual), W1|W3(+RMSNorm, SwiGLU),
+//   W2(+residual)} -> tied head (+final RMSNorm) -> biased slow sample ->
+//   fast pass 0 on the slow hidden state (slot 0) -> for k = 1..N-1:
+//   fast pass k on E_fast[q^(k-1)] (slot k), fast head, unmasked sample.
+// [P2] = "Fish Audio S2: a Qwen3-4B on the time axis, four layers on the
+// codebook axis, and tags that are only text".
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dualar.h"
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_create_err;
+
+constexpr size_t ALIGN = 256;
+inline size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Resolved {  // config with the inherit-on-unset fallback applied
+  int n_layer, dim, H, KV, hd, ffn, V;
+  int fn_layer, fdim, fH, fKV, fhd, fffn;
+  int slow_qk, fast_qk, N, C, sb, se, end_id, scale;
+  float base, eps;
+  int dtype, max_batch, max_seq;
+  size_t esz;
+};
+
+struct Layout {
+  size_t kslow, vslow, kfast, vfast, rope_s, rope_f, x_slow, x_fast, qkv, att, ffn, logits, flog, part,
+      counters, st_pos, st_done, st_frames, st_cur, st_plen, st_fidx, st_status, total;
+  size_t slow_layer_stride, fast_layer_stride;  // elements per layer of a cache
+  int max_splits, qkv_ld, att_ld, ffn_ld;
+};
+
+bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
+  if (!c) { *err = "config is NULL"; return false; }
+  auto inh = [](int v, int s) { return v > 0 ? v : s; };
+  r->n_layer = c->n_layer; r->dim = c->dim; r->H = c->n_head; r->KV = c->n_kv_head;
+  r->hd = c->head_dim; r->ffn = c->ffn_dim; r->V = c->vocab_size;
+  r->fn_layer = c->n_fast_layer;
+  r->fdim = inh(c->fast_dim, c->dim); r->fH = inh(c->fast_n_head, c->n_head);
+  r->fKV = inh(c->fast_n_kv_head, c->n_kv_head); r->fhd = inh(c->fast_head_dim, c->head_dim);
+  r->fffn = inh(c->fast_ffn_dim, c->ffn_dim);
+  r->slow_qk = c->slow_qk_norm != 0;
+  r->fast_qk = c->fast_qk_norm < 0 ? r->slow_qk : (c->fast_qk_norm != 0);
+  r->N = c->num_codebooks; r->C = c->codebook_size;
+  r->sb = c->semantic_begin_id; r->se = c->semantic_end_id; r->end_id = c->end_id;
+  r->scale = c->scale_codebook_embeddings != 0;
+  r->base = c->rope_base; r->eps = c->norm_eps;
+  r->dtype = c->weight_dtype; r->max_batch = c->max_batch; r->max_seq = c->max_seq_len;
+  char buf[256];
+#define REQ(cond, msg)                       \
+  if (!(cond)) {                             \
+    snprintf(buf, sizeof buf, "%s", msg);    \
+    *err = buf;                              \
+    return false;                            \
+  }
+  REQ(r->dtype == DUALAR_F32 || r->dtype == DUALAR_BF16, "weight_dtype must be DUALAR_F32 or DUALAR_BF16");
+  r->esz = r->dtype == DUALAR_BF16 ? 2 : 4;
+  const int unit = r->dtype == DUALAR_BF16 ? 512 : 256;  // one wave load of a row
+  REQ(r->n_layer >= 1 && r->n_layer <= 256, "n_layer out of range [1, 256]");
+  REQ(r->fn_layer >= 1 && r->fn_layer <= 256, "n_fast_layer out of range [1, 256]");
+  REQ(r->dim > 0 && r->dim % unit == 0 && r->dim <= 12288, "dim must be a multiple of 512 (bf16) / 256 (f32), <= 12288");
+  REQ(r->fdim == r->dim, "fast_dim must equal dim (no fast project_in)");
+  REQ(r->ffn > 0 && r->ffn % unit == 0 && r->ffn <= 12288, "ffn_dim must be a multiple of 512 (bf16) / 256 (f32), <= 12288");
+  REQ(r->fffn > 0 && r->fffn % unit == 0 && r->fffn <= 12288, "fast_ffn_dim must be a multiple of 512 (bf16) / 256 (f32), <= 12288");
+  REQ(r->hd == 64 || r->hd == 128, "head_dim must be 64 or 128");
+  REQ(r->fhd == 64 || r->fhd == 128, "fast_head_dim must be 64 or 128");
+  REQ(r->H > 0 && r->KV > 0 && r->H % r->KV == 0 && r->H / r->KV <= 8, "n_head must be a multiple (<= 8x) of n_kv_head");
+  REQ(r->fH > 0 && r->fKV > 0 && r->fH % r->fKV == 0 && r->fH / r->fKV <= 8, "fast_n_head must be a multiple (<= 8x) of fast_n_kv_head");
+  REQ((r->H * r->hd) % unit == 0 && (r->fH * r->fhd) % unit == 0, "n_head*head_dim must be a multiple of the row unit");
+  REQ(r->V > 0 && r->V < (1 << 30), "vocab_size out of range");
+  REQ(r->N >= 2 && r->N <= 32, "num_codebooks out of range [2, 32]");
+  REQ(r->C >= 2 && r->C <= 4096, "codebook_size out of range [2, 4096]");
+  REQ(r->sb >= 0 && r->se == r->sb + r->C - 1 && r->se < r->V, "semantic ids must be [sb, sb+C-1] inside the vocabulary");
+  REQ(r->end_id >= 0 && r->end_id < r->V && (r->end_id < r->sb || r->end_id > r->se), "end_id must be a vocabulary id outside the semantic range");
+  REQ(r->base > 1.0f && isfinite(r->base), "rope_base must be > 1");
+  REQ(r->eps >= 0.0f && isfinite(r->eps), "norm_eps must be >= 0");
+  REQ(r->max_batch >= 1 && r->max_batch <= 256, "max_batch out of range [1, 256]");
+  REQ(r->max_seq >= 2 && r->max_seq <= (1 << 20), "max_seq_len out of range [2, 2^20]");
+#undef REQ
+  return true;
+}
+
+Layout layout(const Resolved& r) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
+  L.max_splits = (r.max_seq + 31) / 32;
+  L.slow_layer_stride = (size_t)r.max_batch * r.KV * r.max_seq * r.hd;
+  L.fast_layer_stride = (size_t)r.max_batch * r.fKV * r.N * r.fhd;
+  L.kslow = take(L.slow_layer_stride * r.n_layer * r.esz);
+  L.vslow = take(L.slow_layer_stride * r.n_layer * r.esz);
+  L.kfast = take(L.fast_layer_stride * r.fn_layer * r.esz);
+  L.vfast = take(L.fast_layer_stride * r.fn_layer * r.esz);
+  L.rope_s = take((size_t)r.max_seq * (r.hd / 2) * sizeof(float2));
+  L.rope_f = take((size_t)r.N * (r.fhd / 2) * sizeof(float2));
+  L.x_slow = take((size_t)r.max_batch * r.dim * 4);
+  L.x_fast = take((size_t)r.max_batch * r.dim * 4);
+  L.qkv_ld = std::max((r.H + 2 * r.KV) * r.hd, (r.fH + 2 * r.fKV) * r.fhd);
+  L.att_ld = std::max(r.H * r.hd, r.fH * r.fhd);
+  L.ffn_ld = std::max(r.ffn, r.fffn);
+  L.qkv = take((size_t)r.max_batch * L.qkv_ld * 4);
+  L.att = take((size_t)r.max_batch * L.att_ld * 4);
+  L.ffn = take((size_t)r.max_batch * L.ffn_ld * 4);
+  L.logits = take((size_t)r.max_batch * r.V * 4);
+  L.flog = take((size_t)r.max_batch * r.C * 4);
+  const int maxH = std::max(r.H, r.fH), maxhd = std::max(r.hd, r.fhd);
+  L.part = take((size_t)r.max_batch * maxH * L.max_splits * (maxhd + 2) * 4);
+  L.counters = take((size_t)r.max_batch * std::max(r.KV, r.fKV) * 4);
+  L.st_pos = take(r.max_batch * 4);
+  L.st_done = take(r.max_batch * 4);
+  L.st_frames = take(r.max_batch * 4);
+  L.st_cur = take((size_t)r.max_batch * (r.N + 1) * 4);
+  L.st_plen = take(r.max_batch * 4);
+  L.st_fidx = take(4);
+  L.st_status = take(4);
+  L.total = off;
+  return L;
+}
+
+struct Stack {
+  int n_layer, dim, H, KV, hd, ffn, qk;
+  std::vector<dualar_layer_weights> lw;
+  char* k; char* v;        // cache bases
+  size_t layer_stride;     // elements
+  int max_pos;
+  const float2* rope;
+};
+
+}  // namespace
+
+struct dualar_ctx {
+  Resolved r;
+  Layout L;
+  dualar_weights w;
+  Stack slow, fast;
+  char* ws;
+  hipStream_t stream;
+  int device;
+  std::string err;
+  // host mirror of the sequence state
+  int batch = 0;
+  bool ready = false;
+  std::vector<int> plen;
+  int frames_done = 0;   // decode frames since prefill (same for every sequence)
+  SeqState st;
+};
+
+namespace {
+
+dualar_status fail(dualar_ctx* c, dualar_status s, const std::string& m) {
+  if (c) c->err = m; else g_create_err = m;
+  return s;
+}
+
+#define HIPCHK(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(c, DUALAR_ERR_HIP, std::string(#expr) + ": " + \
+                                                              hipGetErrorString(e_));  \
+  } while (0)
+
+template <typename T>
+dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const int* pos_dev,
+                        int pos_const, int Lmax) {
+  const Resolved& r = c->r;
+  const Layout& L = c->L;
+  const dualar_layer_weights& w = S.lw[l];
+  float* qkv = (float*)(c->ws + L.qkv);
+  float* att = (float*)(c->ws + L.att);
+  float* ffn = (float*)(c->ws + L.ffn);
+  GemvParams g{};
+  // q | k | v = W_qkv . RMSNorm(x)
+  g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
+  g.rows[0] = S.H * S.hd; g.rows[1] = S.KV * S.hd; g.rows[2] = S.KV * S.hd; g.n_seg = 3;
+  g.K = S.dim; g.n_out = (S.H + 2 * S.KV) * S.hd;
+  g.x = x; g.ldx = S.dim; g.gain = w.attention_norm; g.eps = r.eps;
+  g.y = qkv; g.ldy = L.qkv_ld; g.B = B; g.mode = GEMV_STORE;
+  HIPCHK(launch_gemv<T>(g, c->stream));
+  // attention over the cache (+QK-norm, RoPE, append)
+  AttnParams a{};
+  a.qkv = qkv; a.ld_qkv = L.qkv_ld;
+  a.kcache = S.k + (size_t)l * S.layer_stride * r.esz;
+  a.vcache = S.v + (size_t)l * S.layer_stride * r.esz;
+  a.max_pos = S.max_pos; a.pos = pos_dev; a.pos_const = pos_const; a.rope = S.rope;
+  a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
+  a.H = S.H; a.KV = S.KV; a.hd = S.hd;
+  a.chunk = B == 1 ? 32 : (B <= 4 ? 64 : 256);
+  a.max_splits = (Lmax + a.chunk - 1) / a.chunk;
+  if (a.max_splits > L.max_splits) a.max_splits = L.max_splits;
+  a.part = (float*)(c->ws + L.part);
+  a.counters = (unsigned*)(c->ws + L.counters);
+  a.out = att; a.ld_out = L.att_ld; a.B = B;
+  // partial buffer is indexed with the launch's own max_splits
+  HIPCHK(launch_attn<T>(a, c->stream));
+  // x += Wo . o
+  g = GemvParams{};
+  g.w[0] = w.wo; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.H * S.hd; g.n_out = S.dim;
+  g.x = att; g.ldx = L.att_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
+  HIPCHK(launch_gemv<T>(g, c->stream));
+  // h = silu(W1 n) * (W3 n), n = RMSNorm(x)
+  g = GemvParams{};
+  g.w[0] = w.w1; g.w[1] = w.w3; g.rows[0] = S.ffn; g.rows[1] = S.ffn; g.n_seg = 2;
+  g.K = S.dim; g.n_out = S.ffn; g.x = x; g.ldx = S.dim; g.gain = w.ffn_norm; g.eps = r.eps;
+  g.y = ffn; g.ldy = L.ffn_ld; g.B = B; g.mode = GEMV_SWIGLU;
+  HIPCHK(launch_gemv<T>(g, c->stream));
+  // x += W2 . h
+  g = GemvParams{};
+  g.w[0] = w.w2; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.ffn; g.n_out = S.dim;
+  g.x = ffn; g.ldx = L.ffn_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
+  HIPCHK(launch_gemv<T>(g, c->stream));
+  return DUALAR_OK;
+}
+
+struct FrameIO {
+  const dualar_sampling* s;
+  const float* uniforms; int u_fs, u_rs;
+  int* codes; long long c_rs; int c_fs;
+  const dualar_taps* taps;
+  bool fast_only;
+};
+
+template <typename T>
+SampleParams sample_params(dualar_ctx* c, const FrameIO& io, int B, int slow, int k, float* x_next) {
+  const Resolved& r = c->r;
+  SampleParams sp{};
+  sp.logits = (const float*)(c->ws + (slow ? c->L.logits : c->L.flog));
+  sp.ld = slow ? r.V : r.C;
+  sp.B = B; sp.slow = slow; sp.sb = r.sb; sp.se = r.se; sp.end_id = r.end_id; sp.C = r.C; sp.N = r.N;
+  sp.k = k; sp.greedy = io.s->greedy || !io.uniforms; sp.temperature = io.s->temperature;
+  sp.top_p = io.s->top_p; sp.min_frames = io.s->min_frames;
+  sp.uniforms = io.uniforms; sp.u_frame_stride = io.u_fs; sp.u_row_stride = io.u_rs;
+  sp.codes = io.codes; sp.c_row_stride = io.c_rs; sp.c_frame_stride = io.c_fs;
+  sp.c_col = io.fast_only ? k : (slow ? 0 : 1 + k);
+  sp.fast_emb = c->w.fast_embeddings; sp.fast_dim = r.dim; sp.x_next = x_next;
+  sp.fast_only = io.fast_only;
+  sp.st = c->st;
+  return sp;
+}
+
+// Everything after the slow pass: head, slow sample, N fast passes.  With
+// fast_only, x_slow/x_fast/q0 were set by fast_begin and there is no slow head.
+template <typename T>
+dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
+  const Resolved& r = c->r;
+  const Layout& L = c->L;
+  float* xs = (float*)(c->ws + L.x_slow);
+  float* xf = (float*)(c->ws + L.x_fast);
+  if (!io.fast_only) {
+    if (io.taps && io.taps->slow_hidden)
+      HIPCHK(hipMemcpyAsync(io.taps->slow_hidden, xs, (size_t)B * r.dim * 4, hipMemcpyDeviceToDevice, c->stream));
+    GemvParams g{};
+    g.w[0] = c->w.tok_embedding; g.rows[0] = r.V; g.n_seg = 1; g.K = r.dim; g.n_out = r.V;
+    g.x = xs; g.ldx = r.dim; g.gain = c->w.norm; g.eps = r.eps;
+    g.y = (float*)(c->ws + L.logits); g.ldy = r.V; g.B = B; g.mode = GEMV_STORE;
+    HIPCHK(launch_gemv<T>(g, c->stream));
+    if (io.taps && io.taps->slow_logits)
+      HIPCHK(hipMemcpyAsync(io.taps->slow_logits, c->ws + L.logits, (size_t)B * r.V * 4, hipMemcpyDeviceToDevice,
+                            c->stream));
+    HIPCHK(launch_sample<T>(sample_params<T>(c, io, B, 1, 0, xf), c->stream));
+  }
+  // fast pass 0: the slow hidden state at depth position 0
+  for (int l = 0; l < r.fn_layer; ++l) {
+    dualar_status st = run_layer<T>(c, c->fast, l, xs, B, nullptr, 0, 1);
+    if (st) return st;
+  }
+  for (int k = 1; k < r.N; ++k) {
+    for (int l = 0; l < r.fn_layer; ++l) {
+      dualar_status st = run_layer<T>(c, c->fast, l, xf, B, nullptr, k, k + 1);
+      if (st) return st;
+    }
+    GemvParams g{};
+    g.w[0] = c->w.fast_output; g.rows[0] = r.C; g.n_seg = 1; g.K = r.dim; g.n_out = r.C;
+    g.x = xf; g.ldx = r.dim; g.gain = c->w.fast_norm; g.eps = r.eps;
+    g.y = (float*)(c->ws + L.flog); g.ldy = r.C; g.B = B; g.mode = GEMV_STORE;
+    HIPCHK(launch_gemv<T>(g, c->stream));
+    if (io.taps && io.taps->fast_logits)
+      HIPCHK(hipMemcpy2DAsync(io.taps->fast_logits + (size_t)(k - 1) * r.C, (size_t)(r.N - 1) * r.C * 4,
+                              c->ws + L.flog, (size_t)r.C * 4, (size_t)r.C * 4, B, hipMemcpyDeviceToDevice,
+                              c->stream));
+    HIPCHK(launch_sample<T>(sample_params<T>(c, io, B, 0, k, k < r.N - 1 ? xf : nullptr), c->stream));
+  }
+  HIPCHK(launch_frame_end(c->st, B, io.fast_only ? 0 : 1, c->stream));
+  return DUALAR_OK;
+}
+
+template <typename T>
+dualar_status embed(dualar_ctx* c, int B, const int* tokens, int t_max, int step, int prefill) {
+  const Resolved& r = c->r;
+  EmbedParams e{};
+  e.tokens = tokens; e.t_max = t_max; e.step = step; e.prefill = prefill;
+  e.tok_emb = c->w.tok_embedding; e.cb_emb = c->w.codebook_embedding;
+  e.dim = r.dim; e.V = r.V; e.N = r.N; e.C = r.C; e.sb = r.sb; e.se = r.se; e.scale = r.scale;
+  e.x = (float*)(c->ws + c->L.x_slow); e.B = B; e.st = c->st;
+  HIPCHK(launch_embed<T>(e, c->stream));
+  return DUALAR_OK;
+}
+
+template <typename T>
+dualar_status do_prefill(dualar_ctx* c, int B, const int* tokens, int t_max, const FrameIO& io) {
+  HIPCHK(launch_prefill_begin(c->st, c->plen.data(), B, c->r.N, c->stream));
+  float* xs = (float*)(c->ws + c->L.x_slow);
+  for (int s = 0; s < t_max; ++s) {
+    dualar_status st = embed<T>(c, B, tokens, t_max, s, 1);
+    if (st) return st;
+    for (int l = 0; l < c->r.n_layer; ++l) {
+      st = run_layer<T>(c, c->slow, l, xs, B, c->st.pos, 0, s + 1);
+      if (st) return st;
+    }
+  }
+  return frame_tail<T>(c, B, io);
+}
+
+template <typename T>
+dualar_status do_decode(dualar_ctx* c, int n_frames, const FrameIO& io) {
+  const int B = c->batch;
+  HIPCHK(launch_frame_reset(c->st, c->stream));
+  int maxp = 0;
+  for (int b = 0; b < B; ++b) maxp = std::max(maxp, c->plen[b]);
+  float* xs = (float*)(c->ws + c->L.x_slow);
+  for (int f = 0; f < n_frames; ++f) {
+    dualar_status st = embed<T>(c, B, nullptr, 0, 0, 0);
+    if (st) return st;
+    const bool last = f == n_frames - 1;
+    if (last && io.taps && io.taps->fused_x)
+      HIPCHK(hipMemcpyAsync(io.taps->fused_x, xs, (size_t)B * c->r.dim * 4, hipMemcpyDeviceToDevice, c->stream));
+    const int Lmax = maxp + c->frames_done + f + 1;
+    for (int l = 0; l < c->r.n_layer; ++l) {
+      st = run_layer<T>(c, c->slow, l, xs, B, c->st.pos, 0, Lmax);
+      if (st) return st;
+    }
+    FrameIO fio = io;
+    if (!last) fio.taps = nullptr;
+    st = frame_tail<T>(c, B, fio);
+    if (st) return st;
+  }
+  return DUALAR_OK;
+}
+
+template <typename T>
+dualar_status do_fast(dualar_ctx* c, int B, int n_frames, const float* hidden, const int* q0, const FrameIO& io) {
+  HIPCHK(launch_frame_reset(c->st, c->stream));
+  for (int f = 0; f < n_frames; ++f) {
+    FastBeginParams fb{};
+    fb.hidden = hidden; fb.q0 = q0; fb.fast_emb = c->w.fast_embeddings; fb.dim = c->r.dim; fb.C = c->r.C;
+    fb.N = c->r.N; fb.x_slow = (float*)(c->ws + c->L.x_slow); fb.x_fast = (float*)(c->ws + c->L.x_fast);
+    fb.codes = io.codes; fb.c_row_stride = io.c_rs; fb.c_frame_stride = io.c_fs; fb.B = B; fb.st = c->st;
+    HIPCHK(launch_fast_begin<T>(fb, c->stream));
+    FrameIO fio = io;
+    if (f != n_frames - 1) fio.taps = nullptr;
+    dualar_status st = frame_tail<T>(c, B, fio);
+    if (st) return st;
+  }
+  return DUALAR_OK;
+}
+
+dualar_status check_sampling(dualar_ctx* c, const dualar_sampling* s, const float* uniforms) {
+  if (!s) return fail(c, DUALAR_ERR_INVALID_ARG, "sampling is NULL");
+  if (!s->greedy) {
+    if (!uniforms) return fail(c, DUALAR_ERR_INVALID_ARG, "top-p sampling needs uniforms");
+    if (!(s->temperature > 0.0f) || !isfinite(s->temperature))
+      return fail(c, DUALAR_ERR_INVALID_ARG, "temperature must be > 0");
+    if (!(s->top_p > 0.0f && s->top_p <= 1.0f)) return fail(c, DUALAR_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+  }
+  if (s->min_frames < 0) return fail(c, DUALAR_ERR_INVALID_ARG, "min_frames must be >= 0");
+  return DUALAR_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+size_t dualar_workspace_bytes(const dualar_config* cfg) {
+  Resolved r;
+  std::string err;
+  if (!resolve(cfg, &r, &err)) return 0;
+  return layout(r).total;
+}
+
+dualar_status dualar_create(const dualar_config* cfg, const dualar_weights* w, void* workspace,
+                            size_t workspace_bytes, void* hip_stream, dualar_ctx_t** out) {
+  dualar_ctx* c = nullptr;
+  Resolved r;
+  std::string err;
+  if (!out) return fail(c, DUALAR_ERR_INVALID_ARG, "out is NULL");
+  if (!resolve(cfg, &r, &err)) return fail(c, DUALAR_ERR_INVALID_ARG, err);
+  if (!w) return fail(c, DUALAR_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->tok_embedding || !w->codebook_embedding || !w->norm || !w->layers || !w->fast_layers ||
+      !w->fast_embeddings || !w->fast_norm || !w->fast_output)
+    return fail(c, DUALAR_ERR_INVALID_ARG, "a weight pointer is NULL");
+  auto layer_ok = [](const dualar_layer_weights& l, int qk) {
+    return l.attention_norm && l.wq && l.wk && l.wv && l.wo && l.ffn_norm && l.w1 && l.w3 && l.w2 &&
+           (!qk || (l.q_norm && l.k_norm));
+  };
+  for (int i = 0; i < r.n_layer; ++i)
+    if (!layer_ok(w->layers[i], r.slow_qk)) return fail(c, DUALAR_ERR_INVALID_ARG, "a slow layer weight is NULL");
+  for (int i = 0; i < r.fn_layer; ++i)
+    if (!layer_ok(w->fast_layers[i], r.fast_qk)) return fail(c, DUALAR_ERR_INVALID_ARG, "a fast layer weight is NULL");
+  const Layout L = layout(r);
+  if (!workspace) return fail(c, DUALAR_ERR_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)workspace) % ALIGN) return fail(c, DUALAR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total) return fail(c, DUALAR_ERR_WORKSPACE, "workspace smaller than dualar_workspace_bytes()");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(c, DUALAR_ERR_NO_DEVICE, "no HIP device");
+
+  c = new dualar_ctx();
+  c->r = r; c->L = L; c->w = *w; c->ws = (char*)workspace; c->stream = (hipStream_t)hip_stream;
+  if (hipGetDevice(&c->device) != hipSuccess) { delete c; return fail(nullptr, DUALAR_ERR_HIP, "hipGetDevice failed"); }
+  auto mk = [&](Stack& S, const dualar_layer_weights* lw, int n, int dim, int H, int KV, int hd, int ffn, int qk,
+                size_t k, size_t v, size_t stride, int max_pos, size_t rope) {
+    S.n_layer = n; S.dim = dim; S.H = H; S.KV = KV; S.hd = hd; S.ffn = ffn; S.qk = qk;
+    S.lw.assign(lw, lw + n);
+    S.k = c->ws + k; S.v = c->ws + v; S.layer_stride = stride; S.max_pos = max_pos;
+    S.rope = (const float2*)(c->ws + rope);
+  };
+  mk(c->slow, w->layers, r.n_layer, r.dim, r.H, r.KV, r.hd, r.ffn, r.slow_qk, L.kslow, L.vslow, L.slow_layer_stride,
+     r.max_seq, L.rope_s);
+  mk(c->fast, w->fast_layers, r.fn_layer, r.dim, r.fH, r.fKV, r.fhd, r.fffn, r.fast_qk, L.kfast, L.vfast,
+     L.fast_layer_stride, r.N, L.rope_f);
+  c->w.layers = c->slow.lw.data();
+  c->w.fast_layers = c->fast.lw.data();
+  c->st.pos = (int*)(c->ws + L.st_pos); c->st.done = (int*)(c->ws + L.st_done);
+  c->st.frames = (int*)(c->ws + L.st_frames); c->st.cur = (int*)(c->ws + L.st_cur);
+  c->st.plen = (int*)(c->ws + L.st_plen); c->st.frame_idx = (int*)(c->ws + L.st_fidx);
+  c->st.status = (int*)(c->ws + L.st_status);
+
+  // RoPE tables: theta_i = base^(-2i/hd), angle p*theta_i in double, cos/sin
+  // rounded to bf16 (the bf16 table of the pages).  Stored as (cos, sin) fp32.
+  auto table = [&](int n_pos, int hd) {
+    std::vector<float2> t((size_t)n_pos * (hd / 2));
+    for (int p = 0; p < n_pos; ++p)
+      for (int i = 0; i < hd / 2; ++i) {
+        const double theta = 1.0 / pow((double)r.base, 2.0 * i / hd);
+        const double a = (double)p * theta;
+        auto bf = [](double x) {  // nearest bf16, ties to even
+          int e;
+          const double m = frexp(x, &e);
+          return ldexp(nearbyint(m * 256.0), e - 8);
+        };
+        t[(size_t)p * (hd / 2) + i] = make_float2((float)bf(cos(a)), (float)bf(sin(a)));
+      }
+    return t;
+  };
+  std::vector<float2> ts = table(r.max_seq, r.hd), tf = table(r.N, r.fhd);
+  hipError_t e1 = hipMemsetAsync(c->ws + L.counters, 0, L.total - L.counters, c->stream);
+  hipError_t e2 = hipMemcpyAsync(c->ws + L.rope_s, ts.data(), ts.size() * sizeof(float2), hipMemcpyHostToDevice, c->stream);
+  hipError_t e3 = hipMemcpyAsync(c->ws + L.rope_f, tf.data(), tf.size() * sizeof(float2), hipMemcpyHostToDevice, c->stream);
+  hipError_t e4 = hipStreamSynchronize(c->stream);   // host tables go out of scope
+  if (e1 || e2 || e3 || e4) {
+    delete c;
+    return fail(nullptr, DUALAR_ERR_HIP, "workspace initialisation failed");
+  }
+  *out = c;
+  return DUALAR_OK;
+}
+
+dualar_status dualar_prefill(dualar_ctx_t* c, int32_t batch, const int32_t* tokens, int32_t t_max,
+                             const int32_t* prompt_len, const dualar_sampling* s, const float* uniforms,
+                             int32_t* frame0) {
+  if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
+  if (batch < 1 || batch > c->r.max_batch) return fail(c, DUALAR_ERR_INVALID_ARG, "batch out of range [1, max_batch]");
+  if (!tokens || !prompt_len || !frame0) return fail(c, DUALAR_ERR_INVALID_ARG, "tokens/prompt_len/frame0 is NULL");
+  if (t_max < 1) return fail(c, DUALAR_ERR_INVALID_ARG, "t_max must be >= 1");
+  for (int b = 0; b < batch; ++b) {
+    if (prompt_len[b] < 1 || prompt_len[b] > t_max) return fail(c, DUALAR_ERR_INVALID_ARG, "prompt_len out of [1, t_max]");
+    if (prompt_len[b] >= c->r.max_seq) return fail(c, DUALAR_ERR_CONTEXT_FULL, "prompt does not fit max_seq_len");
+  }
+  if (dualar_status st = check_sampling(c, s, uniforms)) return st;
+  c->plen.assign(prompt_len, prompt_len + batch);
+  c->batch = batch;
+  c->frames_done = 0;
+  c->ready = false;
+  FrameIO io{s, uniforms, 0, c->r.N, frame0, c->r.N + 1, 0, nullptr, false};
+  dualar_status st = c->r.dtype == DUALAR_BF16 ? do_prefill<bf16_t>(c, batch, tokens, t_max, io)
+                                               : do_prefill<float>(c, batch, tokens, t_max, io);
+  if (st == DUALAR_OK) c->ready = true;
+  return st;
+}
+
+dualar_status dualar_decode_frames(dualar_ctx_t* c, int32_t n_frames, const dualar_sampling* s,
+                                   const float* uniforms, int32_t* codes, int32_t* n_emitted,
+                                   const dualar_taps* taps) {
+  if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
+  if (!c->ready) return fail(c, DUALAR_ERR_STATE, "decode_frames before a successful prefill");
+  if (n_frames < 1) return fail(c, DUALAR_ERR_INVALID_ARG, "n_frames must be >= 1");
+  if (!codes) return fail(c, DUALAR_ERR_INVALID_ARG, "codes is NULL");
+  if (dualar_status st = check_sampling(c, s, uniforms)) return st;
+  for (int b = 0; b < c->batch; ++b)
+    if ((long long)c->plen[b] + c->frames_done + n_frames > c->r.max_seq)
+      return fail(c, DUALAR_ERR_CONTEXT_FULL, "decode would pass max_seq_len");
+  const int N = c->r.N;
+  FrameIO io{s, uniforms, c->batch * N, N, codes, (long long)n_frames * (N + 1), N + 1, taps, false};
+  dualar_status st = c->r.dtype == DUALAR_BF16 ? do_decode<bf16_t>(c, n_frames, io) : do_decode<float>(c, n_frames, io);
+  if (st) return st;
+  c->frames_done += n_frames;
+  if (n_emitted) HIPCHK(hipMemcpyAsync(n_emitted, c->st.frames, c->batch * 4, hipMemcpyDeviceToDevice, c->stream));
+  return DUALAR_OK;
+}
+
+dualar_status dualar_fast_frames(dualar_ctx_t* c, int32_t batch, int32_t n_frames, const float* hidden,
+                                 const int32_t* q0, const dualar_sampling* s, const float* uniforms,
+                                 int32_t* codes, const dualar_taps* taps) {
+  if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
+  if (batch < 1 || batch > c->r.max_batch) return fail(c, DUALAR_ERR_INVALID_ARG, "batch out of range [1, max_batch]");
+  if (n_frames < 1) return fail(c, DUALAR_ERR_INVALID_ARG, "n_frames must be >= 1");
+  if (!hidden || !q0 || !codes) return fail(c, DUALAR_ERR_INVALID_ARG, "hidden/q0/codes is NULL");
+  if (dualar_status st = check_sampling(c, s, uniforms)) return st;
+  const int N = c->r.N;
+  // the slow-AR sequence state is not touched by a fast-only call, except
+  // that the per-sequence done flags are used as scratch: a later decode
+  // needs a fresh prefill.
+  c->ready = false;
+  FrameIO io{s, uniforms, batch * N, N, codes, (long long)n_frames * N, N, taps, true};
+  return c->r.dtype == DUALAR_BF16 ? do_fast<bf16_t>(c, batch, n_frames, hidden, q0, io)
+                                   : do_fast<float>(c, batch, n_frames, hidden, q0, io);
+}
+
+dualar_status dualar_sync(dualar_ctx_t* c, int32_t* device_status) {
+  if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
+  HIPCHK(hipStreamSynchronize(c->stream));
+  int st = 0;
+  HIPCHK(hipMemcpy(&st, c->st.status, 4, hipMemcpyDeviceToHost));
+  if (device_status) *device_status = st;
+  if (st) {
+    HIPCHK(hipMemset(c->st.status, 0, 4));
+    if (st & ST_BAD_TOKEN) return fail(c, DUALAR_ERR_BAD_TOKEN, "an id outside its range reached the device");
+    return fail(c, DUALAR_ERR_DEVICE_FAULT, "a non-finite logit reached the sampler");
+  }
+  return DUALAR_OK;
+}
+
+void dualar_destroy(dualar_ctx_t* c) { delete c; }
+
+const char* dualar_status_string(dualar_status s) {
+  switch (s) {
+    case DUALAR_OK: return "ok";
+    case DUALAR_ERR_INVALID_ARG: return "invalid argument";
+    case DUALAR_ERR_NO_DEVICE: return "no device";
+    case DUALAR_ERR_WORKSPACE: return "workspace too small";
+    case DUALAR_ERR_CONTEXT_FULL: return "context full";
+    case DUALAR_ERR_BAD_TOKEN: return "bad token";
+    case DUALAR_ERR_STATE: return "bad state";
+    case DUALAR_ERR_HIP: return "HIP error";
+    case DUALAR_ERR_DEVICE_FAULT: return "device fault";
+  }
+  return "unknown status";
+}
+
+const char* dualar_last_error(const dualar_ctx_t* c) { return c ? c->err.c_str() : g_create_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum GemvMode { GEMV_STORE = 0, GEMV_ADD = 1, GEMV_SWIGLU = 2 };
+
+// y[b, :] = W . f(x[b, :]) for b < B, where f is RMSNorm-with-gain when
+// `gain` is set and the identity otherwise.  W is up to three [rows_i, K]
+// segments whose outputs are concatenated (STORE/ADD), or the gate/up pair
+// (w[0], w[1]) of a SwiGLU FFN whose output is silu(W1 h) * (W3 h).
+struct GemvParams {
+  const void* w[3];
+  int rows[3];
+  int n_seg;
+  int K;
+  int n_out;
+  const float* x; int ldx;
+  const void* gain; float eps;
+  float* y; int ldy;
+  const float* res; int ldres;   // GEMV_ADD: y = res + W.x (res may alias y)
+  int B;
+  int mode;
+};
+
+// Decode attention for one new position per sequence, split along the
+// context; also applies QK-norm + RoPE to the new q and k and appends the
+// new k, v to the cache.
+struct AttnParams {
+  const float* qkv; int ld_qkv;       // [B][ld]: q | k | v
+  void* kcache; void* vcache;         // this layer: [max_batch][KV][max_pos][hd]
+  int max_pos;
+  const int* pos;                     // device [B] (slow), or NULL -> pos_const
+  int pos_const;
+  const float2* rope;                 // [max_pos][hd/2] (cos, sin), bf16 values
+  const void* q_norm; const void* k_norm; float eps;
+  int H, KV, hd;
+  int chunk, max_splits;
+  float* part;                        // [B][H][max_splits][hd + 2]
+  unsigned* counters;                 // [B][KV], zero between launches
+  float* out; int ld_out;             // [B][H*hd]
+  int B;
+};
+
+// Per-sequence decode state kept in the workspace.
+struct SeqState {
+  int* pos;        // [max_batch] next slow position (prefill: position of this step)
+  int* done;       // [max_batch]
+  int* frames;     // [max_batch] frames emitted
+  int* cur;        // [max_batch][N+1] codes of the last frame
+  int* plen;       // [max_batch] prompt lengths
+  int* frame_idx;  // [1] frame index inside the current call
+  int* status;     // [1] latched device faults
+};
+
+// Candidate set / bookkeeping for the sampler.
+struct SampleParams {
+  const float* logits; int ld;
+  int B;
+  int slow;                     // 1: semantic ids + end id, 0: all C fast codes
+  int sb, se, end_id, C, N;
+  int k;                        // codebook index written (0 = slow sample)
+  int greedy; float temperature, top_p; int min_frames;
+  const float* uniforms; int u_frame_stride; int u_row_stride;   // uniforms[f*fs + b*rs + slot]
+  int* codes; long long c_row_stride; int c_frame_stride; int c_col;   // codes out (NULL = none)
+  const void* fast_emb; int fast_dim; float* x_next;   // x_next[b] = E_fast[q] (NULL = none)
+  int last;                     // 1: end of frame bookkeeping
+  int fast_only;
+  SeqState st;
+};
+
+struct EmbedParams {
+  // source of the token column: prompt tokens (prefill) or the state's last frame
+  const int* tokens; int t_max; int step;   // prefill: step s, row b uses t = s - (t_max - plen[b])
+  int prefill;
+  const void* tok_emb; const void* cb_emb;
+  int dim, V, N, C, sb, se, scale;
+  float* x;
+  int B;
+  SeqState st;
+};
+
+struct FastBeginParams {
+  const float* hidden; const int* q0;   // [n_frames][B][dim], [n_frames][B]
+  const void* fast_emb; int dim, C, N;
+  float* x_slow; float* x_fast;
+  int* codes; long long c_row_stride; int c_frame_stride;
+  int B;
+  SeqState st;
+};
+
+template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
+template <typename T> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+template <typename T> hipError_t launch_sample(const SampleParams& p, hipStream_t s);
+template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s);
+template <typename T> hipError_t launch_fast_begin(const FastBeginParams& p, hipStream_t s);
+hipError_t launch_frame_reset(SeqState st, hipStream_t s);
+hipError_t launch_frame_end(SeqState st, int B, int advance_pos, hipStream_t s);
+hipError_t launch_prefill_begin(SeqState st, const int* plen_host, int B, int N, hipStream_t s);

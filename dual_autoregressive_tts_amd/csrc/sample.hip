@@ -1,0 +1,344 @@
+// Token-level kernels of the decode step: multi-codebook fusion (the slow-AR
+// input), the semantic-logit-biased slow sampler, the unmasked fast sampler,
+// and per-frame bookkeeping.
+//
+// Fusion (Fish Audio S2 report Eq. 1, with the sqrt(N+1) divide applied when
+// scale_codebook_embeddings is on): for a semantic id the input is
+//   (E_tok[id] + E_F[0*C + q0] + ... + E_F[(N-1)*C + q_{N-1}]) / sqrt(N+1),
+// summed in fp32 in that order; a text id takes E_tok[id] alone.
+//
+// Sampler: one workgroup of 1024 threads per sequence.  The slow candidates
+// are the semantic ids and <|im_end|> (every other logit carries the -inf
+// bias, so it can never be drawn); the fast candidates are all C codes.
+// Greedy = argmax with the lowest id on ties.  Top-p: e_i = exp((z_i -
+// zmax)/T), a bitonic sort by (e desc, id asc) in LDS, an inclusive scan,
+// keep the shortest prefix whose mass reaches top_p * total, draw the first
+// kept index whose cumulative mass exceeds u * kept mass.
+#include "common.h"
+#include "internal.h"
+
+#define SMP_THREADS 1024
+#define SMP_MAXN 8192
+
+// ---------------------------------------------------------------------------
+// fusion / embedding
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(DUALAR_WG) embed_kernel(EmbedParams p) {
+  const int b = blockIdx.x;
+  __shared__ int col[64];
+  __shared__ int active;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int act = 1;
+    if (p.prefill) {
+      const int t = p.step - (p.t_max - p.st.plen[b]);
+      act = t >= 0;
+      p.st.pos[b] = act ? t : -1;
+      if (act)
+        for (int r = 0; r <= p.N; ++r) col[r] = p.tokens[((size_t)b * (p.N + 1) + r) * p.t_max + t];
+    } else {
+      act = !p.st.done[b];
+      if (act)
+        for (int r = 0; r <= p.N; ++r) col[r] = p.st.cur[b * (p.N + 1) + r];
+    }
+    if (act) {
+      int bad = 0;
+      if (col[0] < 0 || col[0] >= p.V) { bad = 1; col[0] = 0; }
+      if (col[0] >= p.sb && col[0] <= p.se) {
+        for (int k = 0; k < p.N; ++k)
+          if (col[1 + k] < 0 || col[1 + k] >= p.C) { bad = 1; col[1 + k] = 0; }
+      }
+      if (bad) atomicOr(p.st.status, ST_BAD_TOKEN);
+    }
+    active = act;
+  }
+  __syncthreads();
+  float* x = p.x + (size_t)b * p.dim;
+  if (!active) {
+    for (int d = tid; d < p.dim; d += DUALAR_WG) x[d] = 0.f;
+    return;
+  }
+  const int id = col[0];
+  const bool sem = id >= p.sb && id <= p.se;
+  const float denom = sqrtf((float)(p.N + 1));
+  for (int d = tid; d < p.dim; d += DUALAR_WG) {
+    float s = ElemT<T>::load(p.tok_emb, (size_t)id * p.dim + d);
+    if (sem) {
+      for (int k = 0; k < p.N; ++k) s += ElemT<T>::load(p.cb_emb, ((size_t)k * p.C + col[1 + k]) * p.dim + d);
+      if (p.scale) s = s / denom;
+    }
+    x[d] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// sampler
+// ---------------------------------------------------------------------------
+struct Best { float v; int i; };
+__device__ __forceinline__ Best better(Best a, Best b) {
+  // larger value wins; equal values -> lower index (ids are ascending in index)
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+__device__ __forceinline__ Best block_best(Best x, Best* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Best y;
+    y.v = __shfl_xor(x.v, o);
+    y.i = __shfl_xor(x.i, o);
+    x = better(x, y);
+  }
+  if (lane == 0) sh[wave] = x;
+  __syncthreads();
+  Best r = sh[0];
+  for (int w = 1; w < SMP_THREADS / 64; ++w) r = better(r, sh[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int block_count(int c, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 0) sh[wave] = c;
+  __syncthreads();
+  int r = 0;
+  for (int w = 0; w < SMP_THREADS / 64; ++w) r += sh[w];
+  __syncthreads();
+  return r;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ float ev[SMP_MAXN];       // e values, then their inclusive scan
+  __shared__ uint16_t ix[SMP_MAXN];    // candidate index
+  __shared__ Best shb[SMP_THREADS / 64];
+  __shared__ int shc[SMP_THREADS / 64];
+  __shared__ float wsum[SMP_THREADS / 64];
+  __shared__ int choice;
+
+  const int f = *p.st.frame_idx;
+  const int was_done = p.st.done[b];
+  int* crow = p.codes ? p.codes + (size_t)b * p.c_row_stride + (size_t)f * p.c_frame_stride : nullptr;
+  if (was_done) {
+    if (p.slow && crow && tid <= p.N) crow[p.c_col + tid] = -1;
+    return;
+  }
+
+  const int C = p.C;
+  const int nc = p.slow ? C + 1 : C;
+  const bool end_first = p.end_id < p.sb;
+  const bool allow_end = p.slow && (p.st.frames[b] >= p.min_frames);
+  const float* z = p.logits + (size_t)b * p.ld;
+  // candidate index -> token id (ascending)
+  auto cand_id = [&](int i) -> int {
+    if (!p.slow) return i;
+    if (end_first) return i == 0 ? p.end_id : p.sb + i - 1;
+    return i == C ? p.end_id : p.sb + i;
+  };
+  auto cand_ok = [&](int i) -> bool { return !p.slow || cand_id(i) != p.end_id || allow_end; };
+
+  // max (and argmax) over the candidates
+  Best best{-INFINITY, 0x7fffffff};
+  int bad = 0;
+  for (int i = tid; i < nc; i += SMP_THREADS) {
+    if (!cand_ok(i)) continue;
+    const float v = z[cand_id(i)];
+    if (!(v == v) || v == INFINITY) bad = 1;
+    best = better(best, Best{v, i});
+  }
+  if (bad) atomicOr(p.st.status, ST_NONFINITE);
+  best = block_best(best, shb);
+
+  if (p.greedy) {
+    if (tid == 0) choice = best.i;
+  } else {
+    // ---- top-p ----
+    int NP = 1;
+    while (NP < nc) NP <<= 1;
+    const float zmax = best.v;
+    const float invT = 1.0f / p.temperature;
+    for (int i = tid; i < NP; i += SMP_THREADS) {
+      float e = 0.f;
+      if (i < nc && cand_ok(i)) e = expf((z[cand_id(i)] - zmax) * invT);
+      ev[i] = e;
+      ix[i] = (uint16_t)i;
+    }
+    __syncthreads();
+    // bitonic sort, order: e descending, then index ascending
+    for (int kk = 2; kk <= NP; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < NP; i += SMP_THREADS) {
+          const int l = i ^ j;
+          if (l > i) {
+            const float ei = ev[i], el = ev[l];
+            const int ii = ix[i], il = ix[l];
+            // "i before l" under the target order
+            const bool i_first = (ei > el) || (ei == el && ii < il);
+            const bool up = (i & kk) == 0;   // this run sorted in target order
+            if (up != i_first) {
+              ev[i] = el; ev[l] = ei;
+              ix[i] = (uint16_t)il; ix[l] = (uint16_t)ii;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // inclusive scan: each thread owns NP/1024 consecutive entries (or one)
+    const int per = NP >= SMP_THREADS ? NP / SMP_THREADS : 1;
+    const int beg = tid * per;
+    float run = 0.f;
+    if (beg < NP) {
+      for (int q = 0; q < per; ++q) { run += ev[beg + q]; ev[beg + q] = run; }
+    }
+    // exclusive scan of thread totals (wave scan, then across waves)
+    const int lane = tid & 63, wave = tid >> 6;
+    float incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    float woff = 0.f;
+    for (int w = 0; w < wave; ++w) woff += wsum[w];
+    const float off = woff + (incl - run);
+    if (beg < NP)
+      for (int q = 0; q < per; ++q) ev[beg + q] += off;
+    __syncthreads();
+    const float total = ev[NP - 1];
+    const float thr = p.top_p * total;
+    int cnt = 0;
+    for (int i = tid; i < NP; i += SMP_THREADS) cnt += ev[i] < thr;
+    int n_keep = block_count(cnt, shc) + 1;
+    if (n_keep > nc) n_keep = nc;
+    const float kept = ev[n_keep - 1];
+    const float u = p.uniforms[(size_t)f * p.u_frame_stride + (size_t)b * p.u_row_stride + p.k];
+    const float target = u * kept;
+    int c2 = 0;
+    for (int i = tid; i < n_keep; i += SMP_THREADS) c2 += ev[i] <= target;
+    int pick = block_count(c2, shc);
+    if (pick > n_keep - 1) pick = n_keep - 1;
+    if (tid == 0) choice = ix[pick];
+  }
+  __syncthreads();
+
+  const int ci = (choice >= 0 && choice < nc) ? choice : 0;   // NaN logits: stay in range
+  const int id = cand_id(ci);
+  if (p.slow) {
+    if (id == p.end_id) {
+      if (tid == 0) p.st.done[b] = 1;
+      if (crow && tid <= p.N) crow[p.c_col + tid] = tid == 0 ? id : -1;
+      if (p.x_next)
+        for (int d = tid; d < p.fast_dim; d += SMP_THREADS) p.x_next[(size_t)b * p.fast_dim + d] = 0.f;
+      return;
+    }
+    const int q0 = id - p.sb;
+    if (tid == 0) {
+      p.st.cur[b * (p.N + 1)] = id;
+      p.st.cur[b * (p.N + 1) + 1] = q0;
+      if (crow) { crow[p.c_col] = id; crow[p.c_col + 1] = q0; }
+    }
+    if (p.x_next)
+      for (int d = tid; d < p.fast_dim; d += SMP_THREADS)
+        p.x_next[(size_t)b * p.fast_dim + d] = ElemT<T>::load(p.fast_emb, (size_t)q0 * p.fast_dim + d);
+  } else {
+    if (tid == 0) {
+      if (!p.fast_only) p.st.cur[b * (p.N + 1) + 1 + p.k] = id;
+      if (crow) crow[p.c_col] = id;
+    }
+    if (p.x_next)
+      for (int d = tid; d < p.fast_dim; d += SMP_THREADS)
+        p.x_next[(size_t)b * p.fast_dim + d] = ElemT<T>::load(p.fast_emb, (size_t)id * p.fast_dim + d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fast-AR-only frame start: x_slow <- given hidden, x_fast <- E_fast[q0]
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(DUALAR_WG) fast_begin_kernel(FastBeginParams p) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int f = *p.st.frame_idx;
+  int q = p.q0[(size_t)f * p.B + b];
+  if (q < 0 || q >= p.C) {
+    if (tid == 0) atomicOr(p.st.status, ST_BAD_TOKEN);
+    q = 0;
+  }
+  if (tid == 0) {
+    p.st.done[b] = 0;
+    if (p.codes) p.codes[(size_t)b * p.c_row_stride + (size_t)f * p.c_frame_stride] = q;
+  }
+  const float* h = p.hidden + ((size_t)f * p.B + b) * p.dim;
+  for (int d = tid; d < p.dim; d += DUALAR_WG) {
+    p.x_slow[(size_t)b * p.dim + d] = h[d];
+    p.x_fast[(size_t)b * p.dim + d] = ElemT<T>::load(p.fast_emb, (size_t)q * p.dim + d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bookkeeping
+// ---------------------------------------------------------------------------
+__global__ void frame_end_kernel(SeqState st, int B, int advance_pos) {
+  const int b = threadIdx.x;
+  if (b < B && advance_pos) {
+    st.pos[b] += 1;
+    if (!st.done[b]) st.frames[b] += 1;
+  }
+  if (b == 0) *st.frame_idx += 1;
+}
+
+__global__ void frame_reset_kernel(SeqState st) { *st.frame_idx = 0; }
+
+struct PlenArg { int v[256]; };
+__global__ void prefill_begin_kernel(SeqState st, PlenArg plen, int B, int N) {
+  const int b = threadIdx.x;
+  if (b < B) {
+    st.plen[b] = plen.v[b];
+    st.done[b] = 0;
+    st.frames[b] = 0;
+    for (int r = 0; r <= N; ++r) st.cur[b * (N + 1) + r] = 0;
+  }
+  if (b == 0) *st.frame_idx = 0;
+}
+
+template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel<T>, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
+  return hipGetLastError();
+}
+template <typename T> hipError_t launch_sample(const SampleParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(sample_kernel<T>, dim3(p.B), dim3(SMP_THREADS), 0, s, p);
+  return hipGetLastError();
+}
+template <typename T> hipError_t launch_fast_begin(const FastBeginParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(fast_begin_kernel<T>, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
+  return hipGetLastError();
+}
+hipError_t launch_frame_end(SeqState st, int B, int advance_pos, hipStream_t s) {
+  hipLaunchKernelGGL(frame_end_kernel, dim3(1), dim3(256), 0, s, st, B, advance_pos);
+  return hipGetLastError();
+}
+hipError_t launch_frame_reset(SeqState st, hipStream_t s) {
+  hipLaunchKernelGGL(frame_reset_kernel, dim3(1), dim3(1), 0, s, st);
+  return hipGetLastError();
+}
+hipError_t launch_prefill_begin(SeqState st, const int* plen, int B, int N, hipStream_t s) {
+  PlenArg a;
+  for (int b = 0; b < 256; ++b) a.v[b] = b < B ? plen[b] : 0;
+  hipLaunchKernelGGL(prefill_begin_kernel, dim3(1), dim3(256), 0, s, st, a, B, N);
+  return hipGetLastError();
+}
+
+template hipError_t launch_embed<float>(const EmbedParams&, hipStream_t);
+template hipError_t launch_embed<bf16_t>(const EmbedParams&, hipStream_t);
+template hipError_t launch_sample<float>(const SampleParams&, hipStream_t);
+template hipError_t launch_sample<bf16_t>(const SampleParams&, hipStream_t);
+template hipError_t launch_fast_begin<float>(const FastBeginParams&, hipStream_t);
+template hipError_t launch_fast_begin<bf16_t>(const FastBeginParams&, hipStream_t);

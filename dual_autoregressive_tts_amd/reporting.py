@@ -1,0 +1,68 @@
+"""Rates and byte counts used to report throughput (no model arithmetic).
+
+Codec rates ([P2] "The codec: 44.1 kHz in, 21.53 frames out"): 44,100 Hz
+audio, hop 2,048 -> 21.53 frames of audio per second, N codec tokens per
+frame.  RTF = seconds of compute per second of audio = frame_rate / fps.
+[P2] = "Fish Audio S2: a Qwen3-4B on the time axis, four layers on the
+codebook axis, and tags that are only text".
+
+Bytes per decode step ([P2] "The slow AR is Qwen3-4B. The fast AR is not
+small": batch-1 decode is bound by reading weights; one slow step reads the
+36 layers plus the whole tied 155,776-row head, one fast pass the four fast
+layers plus the 4,096-row head).
+"""
+from __future__ import annotations
+
+SAMPLE_RATE = 44100
+HOP = 2048
+FRAME_RATE = SAMPLE_RATE / HOP
+
+
+def codec_tokens_per_s(fps: float, num_codebooks: int = 10) -> float:
+    return fps * num_codebooks
+
+
+def rtf(fps_per_sequence: float) -> float:
+    return FRAME_RATE / fps_per_sequence
+
+
+def _layer_elems(dim, nh, nkv, hd, ffn, qk):
+    return dim * (nh * hd + 2 * nkv * hd) + nh * hd * dim + 3 * dim * ffn + 2 * dim + (2 * hd if qk else 0)
+
+
+def slow_step_weight_elems(m: dict) -> int:
+    """Slow layers + tied head + final norm."""
+    per = _layer_elems(m["dim"], m["n_head"], m["n_kv_head"], m["head_dim"], m["ffn_dim"], m["slow_qk_norm"])
+    return m["n_layer"] * per + m["vocab_size"] * m["dim"] + m["dim"]
+
+
+def fast_pass_weight_elems(m: dict) -> int:
+    """Fast layers + fast head + fast norm (one pass)."""
+    per = _layer_elems(m["fast_dim"], m["fast_n_head"], m["fast_n_kv_head"], m["fast_head_dim"],
+                       m["fast_ffn_dim"], m["fast_qk_norm"])
+    return m["n_fast_layer"] * per + m["codebook_size"] * m["fast_dim"] + m["fast_dim"]
+
+
+def frame_bytes(m: dict, ctx_lengths, fast_only: bool = False) -> dict:
+    """Algorithmic HBM bytes of one decode frame-step over a batch whose
+    sequences attend over `ctx_lengths` slow positions (new one included).
+
+    Weights are read once per step whatever the batch; K/V and gathers scale
+    with the batch."""
+    esz = 2 if m["weight_dtype"] == "bf16" else 4
+    N, D = m["num_codebooks"], m["dim"]
+    B = len(ctx_lengths)
+    fast_w = N * fast_pass_weight_elems(m) * esz
+    # fast K/V: pass k reads slots 0..k-1 and writes slot k, every layer
+    fkv = m["n_fast_layer"] * 2 * m["fast_n_kv_head"] * m["fast_head_dim"] * esz
+    fast_kv = B * fkv * sum(k + 1 for k in range(N))
+    fast_gather = B * (N - 1) * D * esz        # E_fast rows for passes 1..N-1
+    out = {"fast_weights": fast_w, "fast_kv": fast_kv, "gathers": fast_gather}
+    if not fast_only:
+        skv = m["n_layer"] * 2 * m["n_kv_head"] * m["head_dim"] * esz
+        out["slow_weights"] = slow_step_weight_elems(m) * esz
+        # a sequence attending over L positions reads L-1 cached entries and appends one
+        out["slow_kv"] = sum(int(L) for L in ctx_lengths) * skv
+        out["gathers"] += B * (N + 1) * D * esz   # fusion rows
+    out["total"] = sum(out.values())
+    return out

@@ -1,0 +1,201 @@
+/*
+ * dualar.h -- C ABI of the Dual-AR per-frame decode step on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (Fish Audio S2 pages):
+ *   [P1] "How the Dual-Autoregressive Architecture Works in Fish Speech S2:
+ *        A Deep Dive" -- sections "Slow Transformer: BaseTransformer",
+ *        "Fast Transformer: The Codebook Decoder", "DualARModelArgs
+ *        Configuration", "Inference Pipeline".
+ *   [P2] "Fish Audio S2: a Qwen3-4B on the time axis, four layers on the
+ *        codebook axis, and tags that are only text" -- sections "Two
+ *        autoregressions, because ten codebooks is ten times the sequence"
+ *        (decode loop, logit bias, Eq. 1 fusion and its sqrt(N+1) scale),
+ *        "The slow AR is Qwen3-4B. The fast AR is not small" (shapes),
+ *        "Streaming: whose numbers" (bf16 RoPE table).
+ *
+ * One decode frame = multi-codebook fusion of the previous frame, one slow-AR
+ * pass at the next time position, the semantic-logit-biased sample of the
+ * semantic token, then N fast-AR passes along codebook depth against an
+ * N-slot cache rewritten every frame ([P2] "Two autoregressions").
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are HIP device memory; "host" is host memory.
+ *   - Weights, workspace, prompts, uniforms, outputs and taps belong to the
+ *     caller and must outlive the context (weights, workspace) or the call.
+ *   - Matrices are [out, in] row-major (nn.Linear layout); element type is
+ *     bf16 (raw uint16 bit patterns) or fp32 per dualar_config.weight_dtype.
+ *   - Activations, norms, softmax and accumulation are fp32; the K/V caches
+ *     hold the weight type; the RoPE tables hold bf16 values.
+ *   - Every call validates its arguments on the host first.  On failure it
+ *     enqueues nothing, leaves the context unchanged and returns an error;
+ *     dualar_last_error() then gives a message.
+ *   - Work is enqueued asynchronously on the context's stream.  Faults found
+ *     on the device (an out-of-range id in a prompt, a non-finite logit) are
+ *     latched in a status word and reported by dualar_sync().
+ *   - A context is bound to one stream and one device and is not thread-safe.
+ */
+#ifndef DUALAR_H
+#define DUALAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DUALAR_OK = 0,
+  DUALAR_ERR_INVALID_ARG = -1,   /* bad config / pointer / size            */
+  DUALAR_ERR_NO_DEVICE = -2,     /* no HIP device visible                  */
+  DUALAR_ERR_WORKSPACE = -3,     /* workspace smaller than required        */
+  DUALAR_ERR_CONTEXT_FULL = -4,  /* positions would pass max_seq_len       */
+  DUALAR_ERR_BAD_TOKEN = -5,     /* device saw an id outside its range     */
+  DUALAR_ERR_STATE = -6,         /* call out of order (decode before prefill) */
+  DUALAR_ERR_HIP = -7,           /* a HIP runtime call failed              */
+  DUALAR_ERR_DEVICE_FAULT = -8   /* device saw a non-finite logit          */
+} dualar_status;
+
+typedef enum { DUALAR_F32 = 0, DUALAR_BF16 = 1 } dualar_dtype;
+
+typedef struct dualar_ctx dualar_ctx_t;   /* opaque */
+
+/* Model hyper-parameters.  [P1] "DualARModelArgs Configuration": a fast_*
+ * field left unset falls back to the slow value -- here 0 means "inherit"
+ * for every fast_* size, and -1 means "inherit" for fast_qk_norm. */
+typedef struct {
+  int32_t n_layer, dim, n_head, n_kv_head, head_dim, ffn_dim, vocab_size;
+  int32_t n_fast_layer, fast_dim, fast_n_head, fast_n_kv_head, fast_head_dim, fast_ffn_dim;
+  int32_t slow_qk_norm;          /* 1: per-head RMSNorm of q and k before RoPE */
+  int32_t fast_qk_norm;          /* 1 / 0 / -1 (inherit)                        */
+  int32_t num_codebooks;         /* N: codebooks per frame (10 at S2)           */
+  int32_t codebook_size;         /* C: rows per codebook (4096 at S2)           */
+  int32_t semantic_begin_id;     /* first <|semantic:i|> id (inclusive)         */
+  int32_t semantic_end_id;       /* last  <|semantic:i|> id (inclusive)         */
+  int32_t end_id;                /* <|im_end|>                                  */
+  int32_t scale_codebook_embeddings; /* 1: divide the fused sum by sqrt(N+1)   */
+  float rope_base;               /* 1e6 at S2; the fast AR uses the same base   */
+  float norm_eps;                /* RMSNorm epsilon                             */
+  int32_t weight_dtype;          /* dualar_dtype                                */
+  int32_t max_batch;             /* sequences held by the workspace             */
+  int32_t max_seq_len;           /* slow-AR positions per sequence              */
+} dualar_config;
+
+/* One transformer layer.  q_norm / k_norm are [head_dim] gains shared by all
+ * heads, used only when QK-norm is on (else may be NULL). */
+typedef struct {
+  const void *attention_norm;    /* [dim]                      */
+  const void *wq, *wk, *wv;      /* [H*hd, dim], [KV*hd, dim]  */
+  const void *q_norm, *k_norm;   /* [hd] or NULL               */
+  const void *wo;                /* [dim, H*hd]                */
+  const void *ffn_norm;          /* [dim]                      */
+  const void *w1, *w3;           /* [ffn, dim]  (gate, up)     */
+  const void *w2;                /* [dim, ffn]  (down)         */
+} dualar_layer_weights;
+
+/* All device pointers; the two layer arrays are HOST arrays of n_layer and
+ * n_fast_layer entries (copied at create). */
+typedef struct {
+  const void *tok_embedding;        /* [vocab, dim]; also the tied slow head   */
+  const void *codebook_embedding;   /* [N*C, dim]; codebook k = rows k*C..     */
+  const void *norm;                 /* [dim] final slow norm                   */
+  const dualar_layer_weights *layers;
+  const dualar_layer_weights *fast_layers;
+  const void *fast_embeddings;      /* [C, fast_dim]                           */
+  const void *fast_norm;            /* [fast_dim]                              */
+  const void *fast_output;          /* [C, fast_dim]                           */
+} dualar_weights;
+
+/* Sampling ([P2] `decode_one_token_ar` excerpt): greedy, or temperature +
+ * top-p driven by caller-supplied uniforms.  Top-p keeps the shortest
+ * prefix, in (probability desc, id asc) order, whose mass reaches top_p and
+ * draws the first kept id whose renormalised cumulative mass exceeds u.
+ * <|im_end|> stays masked until a sequence has emitted min_frames frames. */
+typedef struct {
+  float temperature;             /* > 0 */
+  float top_p;                   /* (0, 1] */
+  int32_t greedy;                /* 1: argmax (lowest id on ties) */
+  int32_t min_frames;
+} dualar_sampling;
+
+/* Optional fp32 device buffers filled with the LAST frame of a call. */
+typedef struct {
+  float *fused_x;                /* [batch][dim]   slow-AR input of the frame     */
+  float *slow_hidden;            /* [batch][dim]   residual before the final norm */
+  float *slow_logits;            /* [batch][vocab] unbiased slow logits           */
+  float *fast_logits;            /* [batch][N-1][C] logits of q^(1..N-1)          */
+} dualar_taps;
+
+/* Bytes of device workspace a context needs for this config: slow and fast
+ * K/V caches, RoPE tables, activations, logits, per-sequence state.  Returns
+ * 0 for an invalid config. */
+size_t dualar_workspace_bytes(const dualar_config *cfg);
+
+/* Create a context.  Validates cfg and weights, binds the stream (a
+ * hipStream_t, NULL = default stream) and the current device, and enqueues
+ * the workspace initialisation (zeroed state, RoPE tables).  *out is set
+ * only on success. */
+dualar_status dualar_create(const dualar_config *cfg, const dualar_weights *w,
+                            void *workspace, size_t workspace_bytes,
+                            void *hip_stream, dualar_ctx_t **out);
+
+/* Prefill a batch of prompts and emit frame 0 of every sequence.
+ *   tokens     device int32 [batch][N+1][t_max]: row 0 = LM ids, rows 1..N =
+ *              codebook ids q^(0..N-1) (read at semantic positions only);
+ *              a semantic position is fused as in decode, a text position
+ *              takes its LM embedding alone.
+ *   prompt_len host int32 [batch], 1 <= prompt_len[b] <= t_max.
+ *   uniforms   device fp32 [batch][N] for top-p, or NULL when greedy.
+ *   frame0     device int32 [batch][N+1]: (id, q^(0..N-1)); a sequence whose
+ *              first sample is <|im_end|> gets (end_id, -1, ..., -1).
+ * Resets every sequence of the context.  Requires batch <= max_batch and
+ * prompt_len[b] < max_seq_len. */
+dualar_status dualar_prefill(dualar_ctx_t *ctx, int32_t batch, const int32_t *tokens,
+                             int32_t t_max, const int32_t *prompt_len,
+                             const dualar_sampling *s, const float *uniforms,
+                             int32_t *frame0);
+
+/* Decode n_frames frames for every sequence of the last prefill.
+ *   uniforms  device fp32 [n_frames][batch][N] (slot 0: slow draw, slot k:
+ *             draw of q^(k)), or NULL when greedy.
+ *   codes     device int32 [batch][n_frames][N+1]; rows after a sequence has
+ *             ended are -1; the row that samples <|im_end|> is
+ *             (end_id, -1, ..., -1).
+ *   n_emitted device int32 [batch] or NULL: frames emitted so far by each
+ *             sequence, frame 0 included.
+ *   taps      NULL, or buffers filled with the last frame's intermediates.
+ * Fails with DUALAR_ERR_CONTEXT_FULL if a sequence would pass max_seq_len. */
+dualar_status dualar_decode_frames(dualar_ctx_t *ctx, int32_t n_frames,
+                                   const dualar_sampling *s, const float *uniforms,
+                                   int32_t *codes, int32_t *n_emitted,
+                                   const dualar_taps *taps);
+
+/* The fast AR alone (no slow pass): for each frame f and sequence b, N fast
+ * passes seeded by a given slow hidden state and first code.
+ *   hidden   device fp32 [n_frames][batch][fast_dim]
+ *   q0       device int32 [n_frames][batch], 0 <= q0 < C
+ *   uniforms device fp32 [n_frames][batch][N] (slot k draws q^(k)) or NULL
+ *   codes    device int32 [batch][n_frames][N]: q^(0..N-1)
+ *   taps     only fast_logits is used (last frame). */
+dualar_status dualar_fast_frames(dualar_ctx_t *ctx, int32_t batch, int32_t n_frames,
+                                 const float *hidden, const int32_t *q0,
+                                 const dualar_sampling *s, const float *uniforms,
+                                 int32_t *codes, const dualar_taps *taps);
+
+/* Block until the stream's work is done; report latched device faults.
+ * *device_status (host, may be NULL) receives the raw status word. */
+dualar_status dualar_sync(dualar_ctx_t *ctx, int32_t *device_status);
+
+void dualar_destroy(dualar_ctx_t *ctx);
+
+const char *dualar_status_string(dualar_status s);
+
+/* Message of the last failing call on ctx (or of the last failing
+ * dualar_create in this thread when ctx is NULL). */
+const char *dualar_last_error(const dualar_ctx_t *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DUALAR_H */

@@ -1,0 +1,322 @@
+"""HIP path vs the CPU oracle, through the C ABI, on seeded synthetic inputs.
+
+Per frame: fused slow input, slow hidden state, slow logits and the fast
+logits must agree to relative L2 <= 2e-3 (bf16 weights, fp32 accumulation;
+the fp32 tiny model is held to 1e-4); sampled ids must match exactly where
+the decision is clear (tests/parity.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import DualAROracle, Sampling as OSampling
+from tests.parity import REL_L2, decision_margin, margin_ok, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    from dual_autoregressive_tts_amd import DualAR, load_library
+    from dual_autoregressive_tts_amd.binding import upload_weights
+    load_library()
+    return DualAR, upload_weights
+
+
+def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=REL_L2, min_frames=0,
+                    tag="", weights_f32=None):
+    """Prefill + n_frames single-frame decode calls on the GPU; the oracle
+    replays every sequence.  Returns per-row counts of frames compared."""
+    DualAR, upload = _dev()
+    B, N = len(plen), m["num_codebooks"]
+    greedy = samp["greedy"]
+    say(f"[{tag}] GPU: B={B} prompt_len={list(plen)[:8]} frames={n_frames} greedy={greedy}")
+    dw = upload(m, w_np)
+    ctx = DualAR(m, dw, max_batch=B, max_seq_len=int(max(plen)) + n_frames + 2)
+    S = DualAR.sampling(min_frames=min_frames, **samp)
+    tok = torch.from_numpy(np.ascontiguousarray(prompts)).cuda()
+    U = None if uniforms is None else torch.from_numpy(np.ascontiguousarray(uniforms)).cuda()
+    g_frames = [ctx.prefill(tok, plen, S, None if U is None else U[0]).cpu().numpy()]
+    g_taps = [None]
+    for f in range(n_frames):
+        codes, emitted, taps = ctx.decode_frames(1, S, None if U is None else U[1 + f:2 + f], taps=True)
+        g_frames.append(codes[:, 0].cpu().numpy())
+        g_taps.append({k: v.cpu().numpy() for k, v in taps.items()})
+    g_emitted = emitted.cpu().numpy()
+    assert ctx.sync() == 0
+    ctx.close()
+    del dw
+    torch.cuda.empty_cache()
+
+    say(f"[{tag}] oracle")
+    wf = weights_f32 if weights_f32 is not None else synth.weights_as_f32(m, w_np)
+    osamp = OSampling(greedy=bool(greedy), temperature=samp.get("temperature", 1.0),
+                      top_p=samp.get("top_p", 1.0), min_frames=min_frames)
+    compared = []
+    worst = {"fused_x": 0.0, "slow_hidden": 0.0, "slow_logits": 0.0, "fast_logits": 0.0}
+    for b in range(B):
+        o = DualAROracle(m, wf, max_seq=int(plen[b]) + n_frames + 2)
+        seq = o.new_sequence()
+        u = None if uniforms is None else uniforms[:, b, :].astype(np.float64)
+        n_ok = 0
+        for f in range(n_frames + 1):
+            ofr = o.prefill(seq, prompts[b][:, :plen[b]], osamp, None if u is None else u[0]) if f == 0 \
+                else o.decode_frame(seq, osamp, None if u is None else u[f])
+            gfr = g_frames[f][b].tolist()
+            if f > 0 and g_taps[f] is not None and ofr[0] != -1:
+                t = g_taps[f]
+                for k in ("fused_x", "slow_hidden", "slow_logits"):
+                    e = rel_l2(t[k][b], o.taps[k])
+                    worst[k] = max(worst[k], e)
+                    assert e <= (1e-5 if k == "fused_x" else tol), (tag, b, f, k, e)
+            if f > 0 and g_taps[f] is not None and ofr[0] not in (-1, m["end_id"]):
+                e = rel_l2(g_taps[f]["fast_logits"][b], o.taps["fast_logits"])
+                worst["fast_logits"] = max(worst["fast_logits"], e)
+                assert e <= tol, (tag, b, f, "fast_logits", e)
+            if gfr == ofr:
+                n_ok += 1
+                if seq.done:
+                    assert all(g_frames[ff][b].tolist() == [-1] * (N + 1) for ff in range(f + 1, n_frames + 1))
+                    break
+                continue
+            # first differing id: allowed only where the oracle's decision is close
+            bias = o.bias.copy()
+            if f < osamp.min_frames:          # frames emitted before this one = f
+                bias[m["end_id"]] = -np.inf
+            zs = o.taps["slow_logits"] + bias
+            if gfr[0] != ofr[0]:
+                mg = decision_margin(zs, greedy, osamp.temperature, osamp.top_p, None if u is None else u[f][0])
+                assert not margin_ok(mg, greedy), (tag, b, f, "slow id", gfr[0], ofr[0], mg)
+            else:
+                k = next(i for i in range(1, N) if gfr[1 + i] != ofr[1 + i])
+                mg = decision_margin(o.taps["fast_logits"][k - 1], greedy, osamp.temperature, osamp.top_p,
+                                     None if u is None else u[f][k])
+                assert not margin_ok(mg, greedy), (tag, b, f, "fast id", k, gfr, ofr, mg)
+            say(f"[{tag}] row {b} frame {f}: near-tie (margin {mg:.2e}); stop comparing this row")
+            break
+        compared.append(n_ok)
+        if n_ok == n_frames + 1 and not seq.done:
+            assert g_emitted[b] == seq.frames, (tag, b, g_emitted[b], seq.frames)
+    say(f"[{tag}] frames compared per row {compared}; worst rel L2 {worst}")
+    return compared, worst
+
+
+# ----------------------------------------------------------------------------
+# tiny model (the fp32 workload and variants)
+# ----------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def tiny():
+    m = synth.model("tiny")
+    return m, synth.make_weights(m, seed=0)
+
+
+def test_tiny_greedy_16_frames(tiny):
+    m, w = tiny
+    P = synth.make_prompts(m, ("fixed", 4, 16, 12), [32])
+    c, worst = run_and_compare(m, w, P, [32], 16, dict(greedy=1), tol=1e-4, tag="tiny-b1")
+    assert c[0] >= 12
+    assert worst["slow_logits"] < 1e-4
+
+
+def test_tiny_ragged_batch_top_p(tiny):
+    m, w = tiny
+    plen = np.array([32, 7, 1, 45, 20], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=3)
+    U = synth.make_uniforms((9, 5, m["num_codebooks"]), seed=3)
+    c, _ = run_and_compare(m, w, P, plen, 8, dict(greedy=0, temperature=1.0, top_p=0.9), U, tol=1e-4,
+                           tag="tiny-topp")
+    assert sum(c) >= 30
+
+
+def test_tiny_temperature_top_p_half(tiny):
+    m, w = tiny
+    plen = np.array([12, 30], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=5)
+    U = synth.make_uniforms((6, 2, m["num_codebooks"]), seed=5)
+    c, _ = run_and_compare(m, w, P, plen, 5, dict(greedy=0, temperature=0.7, top_p=0.5), U, tol=1e-4,
+                           tag="tiny-T0.7")
+    assert sum(c) >= 8
+
+
+@pytest.mark.parametrize("fast_qk", [1, 0])
+def test_tiny_bf16_kv(fast_qk):
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
+                    n_head=8, n_kv_head=2, fast_n_head=8, fast_n_kv_head=2, fast_qk_norm=fast_qk)
+    w = synth.make_weights(m, seed=1)
+    plen = np.array([40, 9, 64], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=1)
+    c, worst = run_and_compare(m, w, P, plen, 6, dict(greedy=1), tag=f"tiny-bf16-fqk{fast_qk}")
+    assert sum(c) >= 12
+
+
+def test_end_token_stops_and_pads(tiny):
+    m, w = tiny
+    w = {k: v.copy() for k, v in w.items()}
+    P = synth.make_prompts(m, ("fixed", 4, 16, 12), [32])
+    # Make <|im_end|> win once the semantic logit it copies is large: its row
+    # becomes a scaled copy of the row of the oracle's greedy frame-3 id.
+    o = DualAROracle(m, synth.weights_as_f32(m, w), max_seq=64)
+    seq = o.new_sequence()
+    fr = [o.prefill(seq, P[0], OSampling())] + [o.decode_frame(seq, OSampling()) for _ in range(3)]
+    w["tok_embedding"][m["end_id"]] = 3.0 * w["tok_embedding"][fr[3][0]]
+    for mf in (0, 3):
+        c, _ = run_and_compare(m, w, P, [32], 8, dict(greedy=1), tol=1e-4, min_frames=mf, tag=f"end-mf{mf}")
+        assert c[0] >= 1
+
+
+def test_bad_prompt_id_is_reported(tiny):
+    DualAR, upload = _dev()
+    from dual_autoregressive_tts_amd import DualARError
+    m, w = tiny
+    P = synth.make_prompts(m, ("fixed", 4, 16, 12), [32])
+    P[0, 0, 3] = m["vocab_size"] + 7
+    ctx = DualAR(m, upload(m, w), max_batch=1, max_seq_len=40)
+    say("[bad-id] GPU prefill with an out-of-range id")
+    ctx.prefill(torch.from_numpy(P).cuda(), [32], DualAR.sampling())
+    with pytest.raises(DualARError) as e:
+        ctx.sync()
+    assert e.value.name == "BAD_TOKEN"
+    assert ctx.sync() == 0
+
+
+def test_context_full_and_state_errors(tiny):
+    DualAR, upload = _dev()
+    from dual_autoregressive_tts_amd import DualARError
+    m, w = tiny
+    ctx = DualAR(m, upload(m, w), max_batch=2, max_seq_len=36)
+    S = DualAR.sampling()
+    with pytest.raises(DualARError) as e:
+        ctx.decode_frames(1, S)
+    assert e.value.name == "STATE"
+    P = synth.make_prompts(m, ("fixed", 4, 16, 12), [32])
+    ctx.prefill(torch.from_numpy(P).cuda(), [32], S)
+    ctx.decode_frames(4, S)
+    with pytest.raises(DualARError) as e:
+        ctx.decode_frames(1, S)
+    assert e.value.name == "CONTEXT_FULL"
+    with pytest.raises(DualARError) as e:
+        ctx.decode_frames(1, DualAR.sampling(greedy=False))   # top-p without uniforms
+    assert e.value.name == "INVALID_ARG"
+    assert ctx.sync() == 0
+
+
+def test_decode_is_deterministic(tiny):
+    DualAR, upload = _dev()
+    m, w = tiny
+    plen = np.array([20, 33], dtype=np.int32)
+    P = torch.from_numpy(synth.make_prompts(m, ("ragged", 1, 1), plen, seed=9)).cuda()
+    U = torch.from_numpy(synth.make_uniforms((10, 2, m["num_codebooks"]), seed=9)).cuda()
+    dw = upload(m, w)
+    outs = []
+    for _ in range(2):
+        ctx = DualAR(m, dw, max_batch=2, max_seq_len=64)
+        S = DualAR.sampling(greedy=False, top_p=0.9)
+        f0 = ctx.prefill(P, plen, S, U[0])
+        codes, _, taps = ctx.decode_frames(9, S, U[1:], taps=True)
+        outs.append((f0.cpu(), codes.cpu(), {k: v.cpu() for k, v in taps.items()}))
+        ctx.close()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    for k in outs[0][2]:
+        assert torch.equal(outs[0][2][k], outs[1][2][k]), k
+
+
+def test_multi_frame_call_equals_single_frame_calls(tiny):
+    DualAR, upload = _dev()
+    m, w = tiny
+    plen = np.array([25, 31, 8], dtype=np.int32)
+    P = torch.from_numpy(synth.make_prompts(m, ("ragged", 1, 1), plen, seed=4)).cuda()
+    dw = upload(m, w)
+    S = DualAR.sampling()
+    a = DualAR(m, dw, max_batch=3, max_seq_len=64)
+    a.prefill(P, plen, S)
+    ca, ea, _ = a.decode_frames(7, S)
+    b = DualAR(m, dw, max_batch=3, max_seq_len=64)
+    b.prefill(P, plen, S)
+    cb = torch.cat([b.decode_frames(1, S)[0] for _ in range(7)], dim=1)
+    assert torch.equal(ca.cpu(), cb.cpu())
+
+
+# ----------------------------------------------------------------------------
+# S2-shaped fast AR alone (batch 1 and 16)
+# ----------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def s2_fast():
+    m = synth.model("s2")
+    names = {n for n, _, _ in synth.tensor_specs(m) if n.startswith("fast_")}
+    say("[s2-fast] generating fast-AR weights")
+    return m, synth.make_weights(m, seed=0, only=names)
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_s2_fast_only(s2_fast, B):
+    DualAR, upload = _dev()
+    m, w = s2_fast
+    F = 3
+    h, q0 = synth.make_fast_inputs(m, F, B, seed=0)
+    # only the fast tensors are real; the slow ones are small placeholders
+    full = dict(w)
+    dev = upload(m, full)
+    dummy = torch.zeros(16, dtype=torch.bfloat16, device="cuda")
+    for n, _, _ in synth.tensor_specs(m):
+        dev.setdefault(n, dummy)
+    say(f"[s2-fast] GPU B={B} frames={F}")
+    ctx = DualAR(m, dev, max_batch=B, max_seq_len=16)
+    codes, taps = ctx.fast_frames(torch.from_numpy(h).cuda(), torch.from_numpy(q0).cuda(), DualAR.sampling(),
+                                  taps=True)
+    codes = codes.cpu().numpy()
+    fl = taps["fast_logits"].cpu().numpy()
+    assert ctx.sync() == 0
+    ctx.close()
+    say("[s2-fast] oracle")
+    wf = synth.weights_as_f32(m, w)
+    fo = _FastOracle(m, wf)
+    agree = 0
+    for b in range(B):
+        for f in range(F):
+            ref = fo.frame(h[f, b], int(q0[f, b]))
+            if f == F - 1:
+                e = rel_l2(fl[b], fo.logits)
+                assert e <= REL_L2, (b, e)
+            got = codes[b, f].tolist()
+            if got != ref:
+                k = next(i for i in range(m["num_codebooks"]) if got[i] != ref[i])
+                assert k >= 1, (b, f, got, ref)       # q^(0) is an input
+                mg = decision_margin(fo.logits[k - 1], True)
+                assert not margin_ok(mg, True), (b, f, k, got, ref, mg)
+            else:
+                agree += 1
+    assert agree >= 0.8 * B * F
+
+
+class _FastOracle:
+    """The oracle's fast loop with only the fast weights present."""
+
+    def __init__(self, m, wf):
+        # a full oracle whose (unused) slow stack is one tiny layer of zeros
+        shell = synth.model("s2", n_layer=1, dim=64, n_head=1, n_kv_head=1, head_dim=64, ffn_dim=64,
+                            vocab_size=4160, semantic_begin_id=0, semantic_end_id=4095, end_id=4100)
+        spec = {n: s for n, s, _ in synth.tensor_specs(shell)}
+        w = {n: (wf[n] if n.startswith("fast_") else np.zeros(s, dtype=np.float32)) for n, s in spec.items()}
+        self.o = DualAROracle(shell, w, max_seq=4)
+        self.logits = None
+
+    def frame(self, h, q0):
+        codes = self.o.fast_frame(h.astype(np.float64), q0, OSampling())
+        self.logits = self.o.taps["fast_logits"]
+        return codes
+
+
+# ----------------------------------------------------------------------------
+# Full S2-shaped model, short prompt (oracle in seconds), batch 1
+# ----------------------------------------------------------------------------
+
+@pytest.mark.timeout(400)
+def test_s2_full_short_prompt():
+    m = synth.model("s2")
+    say("[s2-full] generating 4.56 B weights")
+    w = synth.make_weights(m, seed=0)
+    P = synth.make_prompts(m, ("fixed", 5, 20, 15), [40], seed=0)
+    c, worst = run_and_compare(m, w, P, [40], 2, dict(greedy=1), tag="s2-full")
+    assert c[0] >= 2

@@ -1,0 +1,48 @@
+"""Reporting helpers against the numbers printed on the page (tests/golden)."""
+import json
+import os
+
+import pytest
+
+import synth
+from dual_autoregressive_tts_amd import reporting as rp
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "s2_page_numbers.json")))
+
+
+def g(k):
+    return GOLD[k]["value"]
+
+
+def test_codec_rates():
+    assert g("sample_rate_hz") / g("hop") == rp.FRAME_RATE
+    assert round(rp.FRAME_RATE, 2) == g("frames_per_s")
+    assert round(1000.0 / rp.FRAME_RATE, 1) == g("frame_ms")
+    assert round(rp.codec_tokens_per_s(rp.FRAME_RATE)) == g("codec_tokens_per_s")
+    assert round(rp.rtf(g("fps_batch1")), 2) == g("rtf_batch1")
+    assert round(rp.FRAME_RATE / g("rtf_fish")) == g("fps_implied_by_0195")
+    assert round(1000.0 / g("fps_batch1"), 1) == g("ms_per_frame_at_63_3")
+    assert round(g("context_tokens") / rp.FRAME_RATE / 60, 1) == g("frame_axis_minutes")
+    assert round(g("context_tokens") / rp.codec_tokens_per_s(rp.FRAME_RATE)) == g("flattened_audio_s")
+    assert round(g("max_new_tokens") / rp.FRAME_RATE, 1) == g("max_new_tokens_audio_s")
+    bits = 12 + 9 * 10
+    assert bits == g("bits_per_frame")
+    assert round(bits * rp.FRAME_RATE / 1000, 2) == g("kbit_per_s")
+
+
+def test_weights_per_frame_model():
+    m = synth.model("s2", fast_qk_norm=0)
+    assert round(rp.slow_step_weight_elems(m) / 1e9, 2) == g("slow_step_weights_B")
+    assert round(rp.fast_pass_weight_elems(m) / 1e6, 1) == g("fast_pass_weights_M")
+    assert round(10 * rp.fast_pass_weight_elems(m) / 1e9, 2) == g("ten_fast_passes_B")
+    assert rp.slow_step_weight_elems(m) == g("text_model_params")
+
+
+def test_frame_bytes_s2():
+    m = synth.model("s2")
+    fb = rp.frame_bytes(m, [1025])
+    # weights with fast QK-norm on: 16,348,828,672 B per frame
+    assert fb["slow_weights"] + fb["fast_weights"] == 16348828672
+    assert fb["slow_kv"] == 147456 * 1025
+    fo = rp.frame_bytes(m, [1, 1], fast_only=True)
+    assert fo["fast_weights"] == 10 * 2 * rp.fast_pass_weight_elems(m)
