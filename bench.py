@@ -1,0 +1,248 @@
+"""Benchmark: Dual-AR frames/s on one MI355X, with the HBM roofline of the
+dominant kernel and the CPU oracle timed beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload s2_b1|s2_b32|fast_s2|fast_s2_b16|tiny_b1]
+
+A step is one decode frame of the whole hot path (fusion, slow pass, biased
+sample, ten fast passes with their samples) over one batch.  Inputs are
+seeded synthetic data of the workload's shape, resident in HBM before the
+timed region.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "Dual-AR frames/sec (codec tokens/s) at batch 1 & 32; % of HBM roofline"
+
+WORKLOADS = {
+    # name: (synth workload, batch override, description)
+    "s2_b1": ("s2_b1", None, "full S2-shaped Dual-AR decode, batch 1, 1,024-token prompt, greedy"),
+    "s2_b32": ("s2_b32", None, "full S2-shaped Dual-AR decode, batch 32, ragged prompts 512..4,096, top-p 0.9"),
+    "fast_s2": ("fast_s2", 1, "S2-shaped fast AR alone, batch 1, greedy"),
+    "fast_s2_b16": ("fast_s2", 16, "S2-shaped fast AR alone, batch 16, greedy"),
+    "tiny_b1": ("tiny_b1", None, "tiny fp32 Dual-AR, batch 1, 32-token prompt, greedy"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class _LazyF32(dict):
+    """bf16 bit arrays -> float32 on access (the oracle copies each to float64)."""
+
+    def __init__(self, m, w):
+        super().__init__()
+        self.m, self.w = m, w
+
+    def __getitem__(self, k):
+        import synth
+        v = self.w[k]
+        return synth.bf16_bits_to_f32(v).reshape(v.shape) if self.m["weight_dtype"] == "bf16" else v
+
+
+def cpu_baseline(m, w, fast_only, seed, budget_s=20.0):
+    """The oracle, untuned, on the host cores: frames/s on a bounded sample."""
+    import synth
+    from oracle import DualAROracle, Sampling
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        cores = os.cpu_count()
+    t0 = time.time()
+    if fast_only:
+        shell = dict(m, n_layer=1, dim=m["fast_dim"], vocab_size=m["codebook_size"] + 64, semantic_begin_id=0,
+                     semantic_end_id=m["codebook_size"] - 1, end_id=m["codebook_size"] + 8)
+        spec = {n: s for n, s, _ in synth.tensor_specs(shell)}
+        lw = _LazyF32(m, w)
+        wf = {n: (lw[n] if n.startswith("fast_") else np.zeros(s, dtype=np.float32)) for n, s in spec.items()}
+        o = DualAROracle(shell, wf, max_seq=8)
+        h, q0 = synth.make_fast_inputs(m, 64, 1, seed=seed)
+        log(f"[cpu] oracle built in {time.time() - t0:.1f}s")
+        n, t1 = 0, time.time()
+        while n < 64 and (n == 0 or time.time() - t1 < budget_s):
+            o.fast_frame(h[n, 0].astype(np.float64), int(q0[n, 0]), Sampling())
+            n += 1
+        dt = time.time() - t1
+        return {"value": n / dt, "unit": "frames/s", "cores": int(cores), "kind": "oracle",
+                "sample": f"{n} fast-AR frames (10 passes each) at batch 1, float64 oracle"}
+    o = DualAROracle(m, _LazyF32(m, w), max_seq=64)
+    P = synth.make_prompts(m, ("fixed", 2, 8, 6), [16], seed=seed)
+    seq = o.new_sequence()
+    o.prefill(seq, P[0], Sampling())
+    log(f"[cpu] oracle built + 16-token prefill in {time.time() - t0:.1f}s")
+    n, t1 = 0, time.time()
+    while n < 32 and (n == 0 or time.time() - t1 < budget_s):
+        o.decode_frame(seq, Sampling())
+        n += 1
+    dt = time.time() - t1
+    return {"value": n / dt, "unit": "frames/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} decode frames at batch 1 after a 16-token prompt, float64 oracle "
+                      f"(the workload's per-frame weight traffic is the same; its longer context adds "
+                      f"<2% to the oracle's per-frame work)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="s2_b1", choices=sorted(WORKLOADS))
+    ap.add_argument("--profile-frames", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences are independent, so batch sharding would replicate the weights per GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from dual_autoregressive_tts_amd import DualAR, reporting
+    from dual_autoregressive_tts_amd.binding import K_ATTN, K_GEMV, upload_weights
+
+    wl_name, b_over, desc = WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[wl_name]
+    m = synth.model(wl["model"])
+    B = b_over or wl["batch"]
+    fast_only = wl.get("fast_only", False)
+    K = args.steps if args.steps is not None else min(wl["frames"], 256)
+    W = args.warmup
+    N = m["num_codebooks"]
+    samp = wl["sampling"]
+
+    t0 = time.time()
+    w = synth.make_weights(m, seed=args.seed)
+    log(f"[bench] {args.workload}: weights generated in {time.time() - t0:.1f}s")
+    dev_w = upload_weights(m, w)
+    torch.cuda.synchronize()
+    log(f"[bench] weights on device ({sum(t.numel() * t.element_size() for t in dev_w.values()) / 1e9:.2f} GB)")
+
+    S = DualAR.sampling(greedy=samp["greedy"], temperature=samp["temperature"], top_p=samp["top_p"],
+                        min_frames=1 << 30)   # fixed-length runs: <|im_end|> stays masked
+    P_frames = W + K + args.profile_frames + 1
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    if fast_only:
+        h, q0 = synth.make_fast_inputs(m, P_frames, B, seed=args.seed)
+        ctx = DualAR(m, dev_w, max_batch=B, max_seq_len=16)
+        H = torch.from_numpy(h).cuda()
+        Q = torch.from_numpy(q0).cuda()
+        U = None
+        if not samp["greedy"]:
+            U = torch.from_numpy(synth.make_uniforms((P_frames, B, N), seed=args.seed)).cuda()
+        run = lambda a, b, prof=False: ctx.fast_frames(H[a:b], Q[a:b], S, None if U is None else U[a:b])  # noqa
+        ctx_len = [1] * B
+        ttff_ms = None
+    else:
+        plen = synth.prompt_lengths(wl, seed=args.seed)
+        prompts = synth.make_prompts(m, wl["prompt"], plen, seed=args.seed)
+        ctx = DualAR(m, dev_w, max_batch=B, max_seq_len=int(plen.max()) + P_frames + 2)
+        U = None
+        if not samp["greedy"]:
+            U = torch.from_numpy(synth.make_uniforms((1 + P_frames, B, N), seed=args.seed)).cuda()
+        T = torch.from_numpy(prompts).cuda()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        ctx.prefill(T, plen, S, None if U is None else U[0])
+        e1.record()
+        torch.cuda.synchronize()
+        ttff_ms = e0.elapsed_time(e1)
+        log(f"[bench] prefill + frame 0: {ttff_ms:.1f} ms")
+        run = lambda a, b, prof=False: ctx.decode_frames(b - a, S, None if U is None else U[1 + a:1 + b])  # noqa
+        ctx_len = None
+
+    # ---- warm-up, then exactly K timed steps ----
+    run(0, W)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    run(W, W + K)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ctx.sync()
+    ms_per_step = ms / K
+    fps = B * K / (ms / 1e3)
+    log(f"[bench] {K} steps in {ms:.1f} ms: {ms_per_step:.3f} ms/step, {fps:.1f} frames/s")
+
+    # ---- algorithmic bytes of the timed steps ----
+    if fast_only:
+        per_step = reporting.frame_bytes(m, ctx_len, fast_only=True)["total"]
+        step_bytes = per_step * K
+    else:
+        step_bytes = 0
+        for f in range(K):
+            L = [int(p) + W + f + 1 for p in plen]
+            step_bytes += reporting.frame_bytes(m, L)["total"]
+    step_gbps = step_bytes / (ms / 1e3) / 1e9
+
+    # ---- live per-launch timing of the dominant kernel (GEMV) ----
+    Pf = args.profile_frames
+    ctx.profile_begin(K_GEMV)
+    run(W + K, W + K + Pf)
+    g = ctx.profile_end()
+    gemv_avg_us = g["total_ms"] * 1e3 / g["launches"]
+    gemv_bytes = g["bytes"] / g["launches"]
+    gemv_gbps = gemv_bytes / (gemv_avg_us * 1e-6) / 1e9
+    gemv_share = g["total_ms"] / (Pf * ms_per_step)
+    log(f"[bench] GEMV: {g['launches']} launches, avg {gemv_avg_us:.2f} us, {gemv_bytes / 1e6:.2f} MB/launch, "
+        f"{gemv_gbps:.0f} GB/s, {100 * gemv_share:.1f}% of step time")
+    roofline = {"bound": "hbm", "kernel": "gemv_kernel (all weight-streaming matrix-vector launches)",
+                "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "avg_launch_us": round(gemv_avg_us, 3), "bytes_per_launch": round(gemv_bytes),
+                "launches_profiled": g["launches"], "share_of_step_time": round(gemv_share, 4)}
+    extra = {}
+    if not fast_only:
+        ctx.profile_begin(K_ATTN)
+        run(W + K + Pf, W + K + Pf + 1)   # nothing left to decode: profile needs one more frame
+        a = ctx.profile_end()
+        extra["attention"] = {"avg_launch_us": round(a["total_ms"] * 1e3 / max(a["launches"], 1), 3),
+                              "launches": a["launches"]}
+    ctx.sync()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del dev_w
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(m, w, fast_only, args.seed)
+        log(f"[cpu] oracle {cpu['value']:.4f} frames/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": round(fps, 3), "unit": "frames/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if m["weight_dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded random-init weights of the S2 shapes, synthetic prompts)",
+        "config": {"workload": f"{args.workload}: {desc}", "batch": B,
+                   "prompt_len": None if fast_only else [int(x) for x in plen][:4] + (["..."] if B > 4 else []),
+                   "accumulate": "f32", "kv_cache": m["weight_dtype"]},
+        "codec_tokens_per_s": round(reporting.codec_tokens_per_s(fps, N), 1),
+        "rtf_per_sequence": round(reporting.rtf(fps / B), 5),
+        "step_hbm": {"bytes_per_step": round(step_bytes / K), "achieved_GBps": round(step_gbps, 1),
+                     "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
+        "ttff_ms": None if ttff_ms is None else round(ttff_ms, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        **extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,7 +35,8 @@ class Config(C.Structure):
         "slow_qk_norm", "fast_qk_norm", "num_codebooks", "codebook_size",
         "semantic_begin_id", "semantic_end_id", "end_id", "scale_codebook_embeddings")] + [
         ("rope_base", C.c_float), ("norm_eps", C.c_float),
-        ("weight_dtype", C.c_int32), ("max_batch", C.c_int32), ("max_seq_len", C.c_int32)]
+        ("weight_dtype", C.c_int32), ("max_batch", C.c_int32), ("max_seq_len", C.c_int32),
+        ("kv_dtype", C.c_int32)]
 
 
 _LAYER_FIELDS = ("attention_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w1", "w3", "w2")
@@ -63,8 +64,9 @@ class Taps(C.Structure):
 
 # Every symbol the header declares.
 EXPORTS = ("dualar_workspace_bytes", "dualar_create", "dualar_prefill", "dualar_decode_frames",
-           "dualar_fast_frames", "dualar_sync", "dualar_destroy", "dualar_status_string",
-           "dualar_last_error")
+           "dualar_fast_frames", "dualar_sync", "dualar_profile_begin", "dualar_profile_end",
+           "dualar_destroy", "dualar_status_string", "dualar_last_error")
+K_GEMV, K_ATTN, K_SAMPLE, K_EMBED = 0, 1, 2, 3
 
 _lib = None
 
@@ -90,6 +92,10 @@ def load_library(path: str = LIB_PATH):
     lib.dualar_fast_frames.restype = I32
     lib.dualar_sync.argtypes = [VP, P(I32)]
     lib.dualar_sync.restype = I32
+    lib.dualar_profile_begin.argtypes = [VP, I32]
+    lib.dualar_profile_begin.restype = I32
+    lib.dualar_profile_end.argtypes = [VP, P(C.c_int64), P(C.c_double), P(C.c_double)]
+    lib.dualar_profile_end.restype = I32
     lib.dualar_destroy.argtypes = [VP]
     lib.dualar_destroy.restype = None
     lib.dualar_status_string.argtypes = [I32]
@@ -121,6 +127,8 @@ def make_config(m: dict, max_batch: int, max_seq_len: int, inherit_fast: bool = 
     c.weight_dtype = BF16 if m["weight_dtype"] == "bf16" else F32
     c.max_batch = int(max_batch)
     c.max_seq_len = int(max_seq_len)
+    kv = m.get("kv_dtype")
+    c.kv_dtype = -1 if kv is None else (BF16 if kv == "bf16" else F32)
     return c
 
 
@@ -201,10 +209,22 @@ class DualAR:
     def sampling(greedy=True, temperature=1.0, top_p=1.0, min_frames=0) -> Sampling:
         return Sampling(float(temperature), float(top_p), int(bool(greedy)), int(min_frames))
 
+    def _need(self, t, shape, dtype, what):
+        torch = self.torch
+        if t is None:
+            return
+        if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+            raise DualARError(-1, f"{what}: expected contiguous cuda {dtype} {tuple(shape)}, got "
+                                  f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
     def prefill(self, tokens, prompt_len, sampling: Sampling, uniforms=None):
         """tokens: cuda int32 [B][N+1][T]; prompt_len: host ints [B]."""
         torch = self.torch
         B, _, T = tokens.shape
+        self._need(tokens, (B, self.N + 1, T), torch.int32, "tokens")
+        self._need(uniforms, (B, self.N), torch.float32, "uniforms")
+        if len(prompt_len) != B:
+            raise DualARError(-1, "prompt_len must have one entry per sequence")
         plen = (C.c_int32 * B)(*[int(x) for x in prompt_len])
         frame0 = torch.empty((B, self.N + 1), dtype=torch.int32, device="cuda")
         self._check(self.lib.dualar_prefill(self.h, B, _ptr(tokens), T, plen, C.byref(sampling),
@@ -216,6 +236,8 @@ class DualAR:
         torch = self.torch
         B, N, m = self.batch, self.N, self.m
         codes = out if out is not None else torch.empty((B, n, N + 1), dtype=torch.int32, device="cuda")
+        self._need(uniforms, (n, B, N), torch.float32, "uniforms")
+        self._need(codes, (B, n, N + 1), torch.int32, "codes")
         emitted = torch.empty(B, dtype=torch.int32, device="cuda")
         tp, td = None, None
         if taps:
@@ -233,6 +255,10 @@ class DualAR:
         torch = self.torch
         F, B = q0.shape
         codes = out if out is not None else torch.empty((B, F, self.N), dtype=torch.int32, device="cuda")
+        self._need(hidden, (F, B, self.m["fast_dim"]), torch.float32, "hidden")
+        self._need(q0, (F, B), torch.int32, "q0")
+        self._need(uniforms, (F, B, self.N), torch.float32, "uniforms")
+        self._need(codes, (B, F, self.N), torch.int32, "codes")
         tp, td = None, None
         if taps:
             td = {"fast_logits": torch.empty((B, self.N - 1, self.m["codebook_size"]), device="cuda")}
@@ -240,6 +266,14 @@ class DualAR:
         self._check(self.lib.dualar_fast_frames(self.h, B, F, _ptr(hidden), _ptr(q0), C.byref(sampling),
                                                 _ptr(uniforms), _ptr(codes), C.byref(tp) if tp is not None else None))
         return codes, td
+
+    def profile_begin(self, kernel_class: int):
+        self._check(self.lib.dualar_profile_begin(self.h, kernel_class))
+
+    def profile_end(self):
+        n, ms, by = C.c_int64(), C.c_double(), C.c_double()
+        self._check(self.lib.dualar_profile_end(self.h, C.byref(n), C.byref(ms), C.byref(by)))
+        return {"launches": n.value, "total_ms": ms.value, "bytes": by.value}
 
     def sync(self) -> int:
         st = C.c_int32(0)

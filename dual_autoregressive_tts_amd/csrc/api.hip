@@ -33,8 +33,8 @@ struct Resolved {  // config with the inherit-on-unset fallback applied
   int fn_layer, fdim, fH, fKV, fhd, fffn;
   int slow_qk, fast_qk, N, C, sb, se, end_id, scale;
   float base, eps;
-  int dtype, max_batch, max_seq;
-  size_t esz;
+  int dtype, kvdtype, max_batch, max_seq;
+  size_t esz, kvesz;
 };
 
 struct Layout {
@@ -60,6 +60,7 @@ bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
   r->scale = c->scale_codebook_embeddings != 0;
   r->base = c->rope_base; r->eps = c->norm_eps;
   r->dtype = c->weight_dtype; r->max_batch = c->max_batch; r->max_seq = c->max_seq_len;
+  r->kvdtype = c->kv_dtype < 0 ? c->weight_dtype : c->kv_dtype;
   char buf[256];
 #define REQ(cond, msg)                       \
   if (!(cond)) {                             \
@@ -68,7 +69,9 @@ bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
     return false;                            \
   }
   REQ(r->dtype == DUALAR_F32 || r->dtype == DUALAR_BF16, "weight_dtype must be DUALAR_F32 or DUALAR_BF16");
+  REQ(r->kvdtype == DUALAR_F32 || r->kvdtype == DUALAR_BF16, "kv_dtype must be -1, DUALAR_F32 or DUALAR_BF16");
   r->esz = r->dtype == DUALAR_BF16 ? 2 : 4;
+  r->kvesz = r->kvdtype == DUALAR_BF16 ? 2 : 4;
   const int unit = r->dtype == DUALAR_BF16 ? 512 : 256;  // one wave load of a row
   REQ(r->n_layer >= 1 && r->n_layer <= 256, "n_layer out of range [1, 256]");
   REQ(r->fn_layer >= 1 && r->fn_layer <= 256, "n_fast_layer out of range [1, 256]");
@@ -101,10 +104,10 @@ Layout layout(const Resolved& r) {
   L.max_splits = (r.max_seq + 31) / 32;
   L.slow_layer_stride = (size_t)r.max_batch * r.KV * r.max_seq * r.hd;
   L.fast_layer_stride = (size_t)r.max_batch * r.fKV * r.N * r.fhd;
-  L.kslow = take(L.slow_layer_stride * r.n_layer * r.esz);
-  L.vslow = take(L.slow_layer_stride * r.n_layer * r.esz);
-  L.kfast = take(L.fast_layer_stride * r.fn_layer * r.esz);
-  L.vfast = take(L.fast_layer_stride * r.fn_layer * r.esz);
+  L.kslow = take(L.slow_layer_stride * r.n_layer * r.kvesz);
+  L.vslow = take(L.slow_layer_stride * r.n_layer * r.kvesz);
+  L.kfast = take(L.fast_layer_stride * r.fn_layer * r.kvesz);
+  L.vfast = take(L.fast_layer_stride * r.fn_layer * r.kvesz);
   L.rope_s = take((size_t)r.max_seq * (r.hd / 2) * sizeof(float2));
   L.rope_f = take((size_t)r.N * (r.fhd / 2) * sizeof(float2));
   L.x_slow = take((size_t)r.max_batch * r.dim * 4);
@@ -156,7 +159,17 @@ struct dualar_ctx {
   bool ready = false;
   std::vector<int> plen;
   int frames_done = 0;   // decode frames since prefill (same for every sequence)
+  std::vector<int> step_pos;  // host mirror of the positions of the current slow step
   SeqState st;
+  // measurement (dualar_profile_begin/end)
+  int prof_cls = -1;
+  std::vector<hipEvent_t> ev;
+  size_t ev_used = 0;
+  long long prof_launches = 0;
+  double prof_bytes = 0.0;
+  ~dualar_ctx() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -166,6 +179,37 @@ dualar_status fail(dualar_ctx* c, dualar_status s, const std::string& m) {
   return s;
 }
 
+// Bracket one launch of kernel class `cls` with events when it is profiled.
+hipError_t prof_pre(dualar_ctx* c, int cls) {
+  if (c->prof_cls != cls) return hipSuccess;
+  while (c->ev.size() < c->ev_used + 2) {
+    hipEvent_t e;
+    hipError_t er = hipEventCreate(&e);
+    if (er != hipSuccess) return er;
+    c->ev.push_back(e);
+  }
+  return hipEventRecord(c->ev[c->ev_used], c->stream);
+}
+hipError_t prof_post(dualar_ctx* c, int cls, double bytes) {
+  if (c->prof_cls != cls) return hipSuccess;
+  hipError_t er = hipEventRecord(c->ev[c->ev_used + 1], c->stream);
+  c->ev_used += 2;
+  c->prof_launches += 1;
+  c->prof_bytes += bytes;
+  return er;
+}
+
+template <typename T>
+hipError_t gemv(dualar_ctx* c, const GemvParams& g) {
+  hipError_t e = prof_pre(c, DUALAR_K_GEMV);
+  if (e != hipSuccess) return e;
+  e = launch_gemv<T>(g, c->stream);
+  if (e != hipSuccess) return e;
+  const double wbytes = (double)g.n_out * (g.mode == GEMV_SWIGLU ? 2 : 1) * g.K * c->r.esz;
+  const double act = 4.0 * g.B * ((double)g.K + g.n_out * (g.mode == GEMV_ADD ? 2 : 1));
+  return prof_post(c, DUALAR_K_GEMV, wbytes + act);
+}
+
 #define HIPCHK(expr)                                                                   \
   do {                                                                                 \
     hipError_t e_ = (expr);                                                            \
@@ -173,7 +217,17 @@ dualar_status fail(dualar_ctx* c, dualar_status s, const std::string& m) {
                                                               hipGetErrorString(e_));  \
   } while (0)
 
-template <typename T>
+// Positions attended by the rows of the current slow step (host mirror).
+double attn_positions(dualar_ctx* c, int B) {
+  double s = 0;
+  for (int b = 0; b < B; ++b) {
+    const int p = c->step_pos.empty() ? 0 : c->step_pos[b];
+    if (p >= 0) s += p + 1;
+  }
+  return s;
+}
+
+template <typename T, typename KT>
 dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const int* pos_dev,
                         int pos_const, int Lmax) {
   const Resolved& r = c->r;
@@ -189,12 +243,12 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g.K = S.dim; g.n_out = (S.H + 2 * S.KV) * S.hd;
   g.x = x; g.ldx = S.dim; g.gain = w.attention_norm; g.eps = r.eps;
   g.y = qkv; g.ldy = L.qkv_ld; g.B = B; g.mode = GEMV_STORE;
-  HIPCHK(launch_gemv<T>(g, c->stream));
+  HIPCHK(gemv<T>(c, g));
   // attention over the cache (+QK-norm, RoPE, append)
   AttnParams a{};
   a.qkv = qkv; a.ld_qkv = L.qkv_ld;
-  a.kcache = S.k + (size_t)l * S.layer_stride * r.esz;
-  a.vcache = S.v + (size_t)l * S.layer_stride * r.esz;
+  a.kcache = S.k + (size_t)l * S.layer_stride * r.kvesz;
+  a.vcache = S.v + (size_t)l * S.layer_stride * r.kvesz;
   a.max_pos = S.max_pos; a.pos = pos_dev; a.pos_const = pos_const; a.rope = S.rope;
   a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
   a.H = S.H; a.KV = S.KV; a.hd = S.hd;
@@ -204,24 +258,30 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.part = (float*)(c->ws + L.part);
   a.counters = (unsigned*)(c->ws + L.counters);
   a.out = att; a.ld_out = L.att_ld; a.B = B;
-  // partial buffer is indexed with the launch's own max_splits
-  HIPCHK(launch_attn<T>(a, c->stream));
+  HIPCHK(prof_pre(c, DUALAR_K_ATTN));
+  HIPCHK((launch_attn<T, KT>(a, c->stream)));
+  if (c->prof_cls == DUALAR_K_ATTN) {
+    // cache bytes: every attended position of every row, K and V, plus the append
+    double pos_sum = pos_dev ? attn_positions(c, B) : (double)B * (pos_const + 1);
+    HIPCHK(prof_post(c, DUALAR_K_ATTN, pos_sum * 2.0 * S.KV * S.hd * r.kvesz +
+                                           4.0 * B * ((S.H + 2 * S.KV) * S.hd + S.H * S.hd)));
+  }
   // x += Wo . o
   g = GemvParams{};
   g.w[0] = w.wo; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.H * S.hd; g.n_out = S.dim;
   g.x = att; g.ldx = L.att_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
-  HIPCHK(launch_gemv<T>(g, c->stream));
+  HIPCHK(gemv<T>(c, g));
   // h = silu(W1 n) * (W3 n), n = RMSNorm(x)
   g = GemvParams{};
   g.w[0] = w.w1; g.w[1] = w.w3; g.rows[0] = S.ffn; g.rows[1] = S.ffn; g.n_seg = 2;
   g.K = S.dim; g.n_out = S.ffn; g.x = x; g.ldx = S.dim; g.gain = w.ffn_norm; g.eps = r.eps;
   g.y = ffn; g.ldy = L.ffn_ld; g.B = B; g.mode = GEMV_SWIGLU;
-  HIPCHK(launch_gemv<T>(g, c->stream));
+  HIPCHK(gemv<T>(c, g));
   // x += W2 . h
   g = GemvParams{};
   g.w[0] = w.w2; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.ffn; g.n_out = S.dim;
   g.x = ffn; g.ldx = L.ffn_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
-  HIPCHK(launch_gemv<T>(g, c->stream));
+  HIPCHK(gemv<T>(c, g));
   return DUALAR_OK;
 }
 
@@ -251,9 +311,20 @@ SampleParams sample_params(dualar_ctx* c, const FrameIO& io, int B, int slow, in
   return sp;
 }
 
+template <typename T>
+hipError_t sample(dualar_ctx* c, const SampleParams& sp) {
+  hipError_t e = prof_pre(c, DUALAR_K_SAMPLE);
+  if (e != hipSuccess) return e;
+  e = launch_sample<T>(sp, c->stream);
+  if (e != hipSuccess) return e;
+  const double cand = sp.slow ? sp.C + 1 : sp.C;
+  const double nxt = sp.x_next ? (double)sp.fast_dim * (4 + c->r.esz) : 0.0;
+  return prof_post(c, DUALAR_K_SAMPLE, sp.B * (cand * 4 + nxt));
+}
+
 // Everything after the slow pass: head, slow sample, N fast passes.  With
 // fast_only, x_slow/x_fast/q0 were set by fast_begin and there is no slow head.
-template <typename T>
+template <typename T, typename KT>
 dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
   const Resolved& r = c->r;
   const Layout& L = c->L;
@@ -266,32 +337,32 @@ dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
     g.w[0] = c->w.tok_embedding; g.rows[0] = r.V; g.n_seg = 1; g.K = r.dim; g.n_out = r.V;
     g.x = xs; g.ldx = r.dim; g.gain = c->w.norm; g.eps = r.eps;
     g.y = (float*)(c->ws + L.logits); g.ldy = r.V; g.B = B; g.mode = GEMV_STORE;
-    HIPCHK(launch_gemv<T>(g, c->stream));
+    HIPCHK(gemv<T>(c, g));
     if (io.taps && io.taps->slow_logits)
       HIPCHK(hipMemcpyAsync(io.taps->slow_logits, c->ws + L.logits, (size_t)B * r.V * 4, hipMemcpyDeviceToDevice,
                             c->stream));
-    HIPCHK(launch_sample<T>(sample_params<T>(c, io, B, 1, 0, xf), c->stream));
+    HIPCHK(sample<T>(c, sample_params<T>(c, io, B, 1, 0, xf)));
   }
   // fast pass 0: the slow hidden state at depth position 0
   for (int l = 0; l < r.fn_layer; ++l) {
-    dualar_status st = run_layer<T>(c, c->fast, l, xs, B, nullptr, 0, 1);
+    dualar_status st = run_layer<T, KT>(c, c->fast, l, xs, B, nullptr, 0, 1);
     if (st) return st;
   }
   for (int k = 1; k < r.N; ++k) {
     for (int l = 0; l < r.fn_layer; ++l) {
-      dualar_status st = run_layer<T>(c, c->fast, l, xf, B, nullptr, k, k + 1);
+      dualar_status st = run_layer<T, KT>(c, c->fast, l, xf, B, nullptr, k, k + 1);
       if (st) return st;
     }
     GemvParams g{};
     g.w[0] = c->w.fast_output; g.rows[0] = r.C; g.n_seg = 1; g.K = r.dim; g.n_out = r.C;
     g.x = xf; g.ldx = r.dim; g.gain = c->w.fast_norm; g.eps = r.eps;
     g.y = (float*)(c->ws + L.flog); g.ldy = r.C; g.B = B; g.mode = GEMV_STORE;
-    HIPCHK(launch_gemv<T>(g, c->stream));
+    HIPCHK(gemv<T>(c, g));
     if (io.taps && io.taps->fast_logits)
       HIPCHK(hipMemcpy2DAsync(io.taps->fast_logits + (size_t)(k - 1) * r.C, (size_t)(r.N - 1) * r.C * 4,
                               c->ws + L.flog, (size_t)r.C * 4, (size_t)r.C * 4, B, hipMemcpyDeviceToDevice,
                               c->stream));
-    HIPCHK(launch_sample<T>(sample_params<T>(c, io, B, 0, k, k < r.N - 1 ? xf : nullptr), c->stream));
+    HIPCHK(sample<T>(c, sample_params<T>(c, io, B, 0, k, k < r.N - 1 ? xf : nullptr)));
   }
   HIPCHK(launch_frame_end(c->st, B, io.fast_only ? 0 : 1, c->stream));
   return DUALAR_OK;
@@ -305,26 +376,30 @@ dualar_status embed(dualar_ctx* c, int B, const int* tokens, int t_max, int step
   e.tok_emb = c->w.tok_embedding; e.cb_emb = c->w.codebook_embedding;
   e.dim = r.dim; e.V = r.V; e.N = r.N; e.C = r.C; e.sb = r.sb; e.se = r.se; e.scale = r.scale;
   e.x = (float*)(c->ws + c->L.x_slow); e.B = B; e.st = c->st;
+  HIPCHK(prof_pre(c, DUALAR_K_EMBED));
   HIPCHK(launch_embed<T>(e, c->stream));
+  HIPCHK(prof_post(c, DUALAR_K_EMBED, (double)B * r.dim * ((r.N + 1) * r.esz + 4)));
   return DUALAR_OK;
 }
 
-template <typename T>
+template <typename T, typename KT>
 dualar_status do_prefill(dualar_ctx* c, int B, const int* tokens, int t_max, const FrameIO& io) {
   HIPCHK(launch_prefill_begin(c->st, c->plen.data(), B, c->r.N, c->stream));
   float* xs = (float*)(c->ws + c->L.x_slow);
+  c->step_pos.assign(B, -1);
   for (int s = 0; s < t_max; ++s) {
+    for (int b = 0; b < B; ++b) c->step_pos[b] = s - (t_max - c->plen[b]);
     dualar_status st = embed<T>(c, B, tokens, t_max, s, 1);
     if (st) return st;
     for (int l = 0; l < c->r.n_layer; ++l) {
-      st = run_layer<T>(c, c->slow, l, xs, B, c->st.pos, 0, s + 1);
+      st = run_layer<T, KT>(c, c->slow, l, xs, B, c->st.pos, 0, s + 1);
       if (st) return st;
     }
   }
-  return frame_tail<T>(c, B, io);
+  return frame_tail<T, KT>(c, B, io);
 }
 
-template <typename T>
+template <typename T, typename KT>
 dualar_status do_decode(dualar_ctx* c, int n_frames, const FrameIO& io) {
   const int B = c->batch;
   HIPCHK(launch_frame_reset(c->st, c->stream));
@@ -338,19 +413,21 @@ dualar_status do_decode(dualar_ctx* c, int n_frames, const FrameIO& io) {
     if (last && io.taps && io.taps->fused_x)
       HIPCHK(hipMemcpyAsync(io.taps->fused_x, xs, (size_t)B * c->r.dim * 4, hipMemcpyDeviceToDevice, c->stream));
     const int Lmax = maxp + c->frames_done + f + 1;
+    c->step_pos.resize(B);
+    for (int b = 0; b < B; ++b) c->step_pos[b] = c->plen[b] + c->frames_done + f;
     for (int l = 0; l < c->r.n_layer; ++l) {
-      st = run_layer<T>(c, c->slow, l, xs, B, c->st.pos, 0, Lmax);
+      st = run_layer<T, KT>(c, c->slow, l, xs, B, c->st.pos, 0, Lmax);
       if (st) return st;
     }
     FrameIO fio = io;
     if (!last) fio.taps = nullptr;
-    st = frame_tail<T>(c, B, fio);
+    st = frame_tail<T, KT>(c, B, fio);
     if (st) return st;
   }
   return DUALAR_OK;
 }
 
-template <typename T>
+template <typename T, typename KT>
 dualar_status do_fast(dualar_ctx* c, int B, int n_frames, const float* hidden, const int* q0, const FrameIO& io) {
   HIPCHK(launch_frame_reset(c->st, c->stream));
   for (int f = 0; f < n_frames; ++f) {
@@ -361,10 +438,20 @@ dualar_status do_fast(dualar_ctx* c, int B, int n_frames, const float* hidden, c
     HIPCHK(launch_fast_begin<T>(fb, c->stream));
     FrameIO fio = io;
     if (f != n_frames - 1) fio.taps = nullptr;
-    dualar_status st = frame_tail<T>(c, B, fio);
+    dualar_status st = frame_tail<T, KT>(c, B, fio);
     if (st) return st;
   }
   return DUALAR_OK;
+}
+
+// Call f(weight type, cache type) with the context's element types.
+template <typename F>
+dualar_status dispatch(dualar_ctx* c, F&& f) {
+  const bool wb = c->r.dtype == DUALAR_BF16, kb = c->r.kvdtype == DUALAR_BF16;
+  if (wb && kb) return f(bf16_t{}, bf16_t{});
+  if (wb) return f(bf16_t{}, float{});
+  if (kb) return f(float{}, bf16_t{});
+  return f(float{}, float{});
 }
 
 dualar_status check_sampling(dualar_ctx* c, const dualar_sampling* s, const float* uniforms) {
@@ -487,8 +574,9 @@ dualar_status dualar_prefill(dualar_ctx_t* c, int32_t batch, const int32_t* toke
   c->frames_done = 0;
   c->ready = false;
   FrameIO io{s, uniforms, 0, c->r.N, frame0, c->r.N + 1, 0, nullptr, false};
-  dualar_status st = c->r.dtype == DUALAR_BF16 ? do_prefill<bf16_t>(c, batch, tokens, t_max, io)
-                                               : do_prefill<float>(c, batch, tokens, t_max, io);
+  dualar_status st = dispatch(c, [&](auto wt, auto kt) {
+    return do_prefill<decltype(wt), decltype(kt)>(c, batch, tokens, t_max, io);
+  });
   if (st == DUALAR_OK) c->ready = true;
   return st;
 }
@@ -506,7 +594,9 @@ dualar_status dualar_decode_frames(dualar_ctx_t* c, int32_t n_frames, const dual
       return fail(c, DUALAR_ERR_CONTEXT_FULL, "decode would pass max_seq_len");
   const int N = c->r.N;
   FrameIO io{s, uniforms, c->batch * N, N, codes, (long long)n_frames * (N + 1), N + 1, taps, false};
-  dualar_status st = c->r.dtype == DUALAR_BF16 ? do_decode<bf16_t>(c, n_frames, io) : do_decode<float>(c, n_frames, io);
+  dualar_status st = dispatch(c, [&](auto wt, auto kt) {
+    return do_decode<decltype(wt), decltype(kt)>(c, n_frames, io);
+  });
   if (st) return st;
   c->frames_done += n_frames;
   if (n_emitted) HIPCHK(hipMemcpyAsync(n_emitted, c->st.frames, c->batch * 4, hipMemcpyDeviceToDevice, c->stream));
@@ -527,8 +617,9 @@ dualar_status dualar_fast_frames(dualar_ctx_t* c, int32_t batch, int32_t n_frame
   // needs a fresh prefill.
   c->ready = false;
   FrameIO io{s, uniforms, batch * N, N, codes, (long long)n_frames * N, N, taps, true};
-  return c->r.dtype == DUALAR_BF16 ? do_fast<bf16_t>(c, batch, n_frames, hidden, q0, io)
-                                   : do_fast<float>(c, batch, n_frames, hidden, q0, io);
+  return dispatch(c, [&](auto wt, auto kt) {
+    return do_fast<decltype(wt), decltype(kt)>(c, batch, n_frames, hidden, q0, io);
+  });
 }
 
 dualar_status dualar_sync(dualar_ctx_t* c, int32_t* device_status) {
@@ -542,6 +633,35 @@ dualar_status dualar_sync(dualar_ctx_t* c, int32_t* device_status) {
     if (st & ST_BAD_TOKEN) return fail(c, DUALAR_ERR_BAD_TOKEN, "an id outside its range reached the device");
     return fail(c, DUALAR_ERR_DEVICE_FAULT, "a non-finite logit reached the sampler");
   }
+  return DUALAR_OK;
+}
+
+dualar_status dualar_profile_begin(dualar_ctx_t* c, int32_t kernel_class) {
+  if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
+  if (kernel_class < DUALAR_K_GEMV || kernel_class > DUALAR_K_EMBED)
+    return fail(c, DUALAR_ERR_INVALID_ARG, "unknown kernel class");
+  c->prof_cls = kernel_class;
+  c->ev_used = 0;
+  c->prof_launches = 0;
+  c->prof_bytes = 0.0;
+  return DUALAR_OK;
+}
+
+dualar_status dualar_profile_end(dualar_ctx_t* c, int64_t* launches, double* total_ms, double* bytes) {
+  if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
+  if (c->prof_cls < 0) return fail(c, DUALAR_ERR_STATE, "profiling was not begun");
+  HIPCHK(hipStreamSynchronize(c->stream));
+  double ms = 0.0;
+  for (size_t i = 0; i + 1 < c->ev_used; i += 2) {
+    float t = 0.f;
+    HIPCHK(hipEventElapsedTime(&t, c->ev[i], c->ev[i + 1]));
+    ms += t;
+  }
+  if (launches) *launches = c->prof_launches;
+  if (total_ms) *total_ms = ms;
+  if (bytes) *bytes = c->prof_bytes;
+  c->prof_cls = -1;
+  c->ev_used = 0;
   return DUALAR_OK;
 }
 

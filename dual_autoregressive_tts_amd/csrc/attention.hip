@@ -12,7 +12,7 @@
 //      unnormalised P.V, and writes (o, m, l) partials;
 //   4. the last workgroup of a (sequence, KV head) to finish (atomic
 //      counter) merges the partials: o = sum_s e^(m_s-M) o_s / sum_s e^(m_s-M) l_s.
-// K/V rows are read with 16-byte lane loads: LPP = hd*sizeof(T)/16 lanes
+// K/V rows are read with 16-byte lane loads: LPP = hd*sizeof(KT)/16 lanes
 // cover one position, so a wave reads 64/LPP positions per load.
 #include "common.h"
 #include "internal.h"
@@ -21,7 +21,7 @@
 #define ATT_MAXHD 128
 #define ATT_MAXCHUNK 256
 
-template <typename T>
+template <typename T, typename KT>
 __global__ void __launch_bounds__(DUALAR_WG) attn_kernel(AttnParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int pos = p.pos ? p.pos[b] : p.pos_const;
@@ -77,36 +77,36 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_kernel(AttnParams p) {
       }
       if (pair_live) {
         const float2 cs = rope[lane];
-        const float ra = ElemT<T>::round(a * cs.x - c * cs.y);
-        const float rc = ElemT<T>::round(a * cs.y + c * cs.x);
+        const float ra = ElemT<KT>::round(a * cs.x - c * cs.y);
+        const float rc = ElemT<KT>::round(a * cs.y + c * cs.x);
         knew[2 * lane] = ra;
         knew[2 * lane + 1] = rc;
-        ElemT<T>::store(p.kcache, (head_base + pos) * hd + 2 * lane, ra);
-        ElemT<T>::store(p.kcache, (head_base + pos) * hd + 2 * lane + 1, rc);
+        ElemT<KT>::store(p.kcache, (head_base + pos) * hd + 2 * lane, ra);
+        ElemT<KT>::store(p.kcache, (head_base + pos) * hd + 2 * lane + 1, rc);
       }
     } else if (wave == 1) {
       const float* vp = row + (size_t)(p.H + p.KV) * hd + (size_t)g * hd;
       for (int e = lane; e < hd; e += 64) {
-        const float v = ElemT<T>::round(vp[e]);
+        const float v = ElemT<KT>::round(vp[e]);
         vnew[e] = v;
-        ElemT<T>::store(p.vcache, (head_base + pos) * hd + e, v);
+        ElemT<KT>::store(p.vcache, (head_base + pos) * hd + e, v);
       }
     }
   }
   __syncthreads();
 
   // ---- 3a. scores ----
-  constexpr int EPL = ElemT<T>::EPV;
+  constexpr int EPL = ElemT<KT>::EPV;
   const int LPP = hd / EPL;
   const int PPW = 64 / LPP;
   const int sub = lane % LPP, grp = lane / LPP;
-  const char* kbase = (const char*)p.kcache + head_base * hd * sizeof(T);
-  const char* vbase = (const char*)p.vcache + head_base * hd * sizeof(T);
+  const char* kbase = (const char*)p.kcache + head_base * hd * sizeof(KT);
+  const char* vbase = (const char*)p.vcache + head_base * hd * sizeof(KT);
   for (int j0 = c0 + wave * PPW; j0 < c1; j0 += 4 * PPW) {
     const int j = j0 + grp;
     float kv[EPL];
     if (j < c1 && j != pos) {
-      ElemT<T>::unpack(ld_vec(kbase + ((size_t)j * hd + sub * EPL) * sizeof(T)), kv);
+      ElemT<KT>::unpack(ld_vec(kbase + ((size_t)j * hd + sub * EPL) * sizeof(KT)), kv);
     } else {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) kv[e] = (j == pos) ? knew[sub * EPL + e] : 0.f;
@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_kernel(AttnParams p) {
     if (j < c1) {
       float vv[EPL];
       if (j != pos) {
-        ElemT<T>::unpack(ld_vec(vbase + ((size_t)j * hd + sub * EPL) * sizeof(T)), vv);
+        ElemT<KT>::unpack(ld_vec(vbase + ((size_t)j * hd + sub * EPL) * sizeof(KT)), vv);
       } else {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) vv[e] = vnew[sub * EPL + e];
@@ -217,11 +217,13 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_kernel(AttnParams p) {
   if (tid == 0) atomicExch(&p.counters[b * p.KV + g], 0u);
 }
 
-template <typename T> hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
+template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   dim3 grid(p.max_splits, p.KV, p.B);
-  hipLaunchKernelGGL(attn_kernel<T>, grid, dim3(DUALAR_WG), 0, s, p);
+  hipLaunchKernelGGL((attn_kernel<T, KT>), grid, dim3(DUALAR_WG), 0, s, p);
   return hipGetLastError();
 }
 
-template hipError_t launch_attn<float>(const AttnParams&, hipStream_t);
-template hipError_t launch_attn<bf16_t>(const AttnParams&, hipStream_t);
+template hipError_t launch_attn<float, float>(const AttnParams&, hipStream_t);
+template hipError_t launch_attn<float, bf16_t>(const AttnParams&, hipStream_t);
+template hipError_t launch_attn<bf16_t, float>(const AttnParams&, hipStream_t);
+template hipError_t launch_attn<bf16_t, bf16_t>(const AttnParams&, hipStream_t);

@@ -90,7 +90,7 @@ struct FastBeginParams {
 };
 
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
-template <typename T> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 template <typename T> hipError_t launch_sample(const SampleParams& p, hipStream_t s);
 template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s);
 template <typename T> hipError_t launch_fast_begin(const FastBeginParams& p, hipStream_t s);

@@ -50,16 +50,17 @@ def frame_bytes(m: dict, ctx_lengths, fast_only: bool = False) -> dict:
     Weights are read once per step whatever the batch; K/V and gathers scale
     with the batch."""
     esz = 2 if m["weight_dtype"] == "bf16" else 4
+    kvesz = 2 if m.get("kv_dtype", m["weight_dtype"]) == "bf16" else 4
     N, D = m["num_codebooks"], m["dim"]
     B = len(ctx_lengths)
     fast_w = N * fast_pass_weight_elems(m) * esz
     # fast K/V: pass k reads slots 0..k-1 and writes slot k, every layer
-    fkv = m["n_fast_layer"] * 2 * m["fast_n_kv_head"] * m["fast_head_dim"] * esz
+    fkv = m["n_fast_layer"] * 2 * m["fast_n_kv_head"] * m["fast_head_dim"] * kvesz
     fast_kv = B * fkv * sum(k + 1 for k in range(N))
     fast_gather = B * (N - 1) * D * esz        # E_fast rows for passes 1..N-1
     out = {"fast_weights": fast_w, "fast_kv": fast_kv, "gathers": fast_gather}
     if not fast_only:
-        skv = m["n_layer"] * 2 * m["n_kv_head"] * m["head_dim"] * esz
+        skv = m["n_layer"] * 2 * m["n_kv_head"] * m["head_dim"] * kvesz
         out["slow_weights"] = slow_step_weight_elems(m) * esz
         # a sequence attending over L positions reads L-1 cached entries and appends one
         out["slow_kv"] = sum(int(L) for L in ctx_lengths) * skv

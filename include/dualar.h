@@ -26,7 +26,8 @@
  *   - Matrices are [out, in] row-major (nn.Linear layout); element type is
  *     bf16 (raw uint16 bit patterns) or fp32 per dualar_config.weight_dtype.
  *   - Activations, norms, softmax and accumulation are fp32; the K/V caches
- *     hold the weight type; the RoPE tables hold bf16 values.
+ *     hold kv_dtype (default: the weight type); the RoPE tables hold bf16
+ *     values.
  *   - Every call validates its arguments on the host first.  On failure it
  *     enqueues nothing, leaves the context unchanged and returns an error;
  *     dualar_last_error() then gives a message.
@@ -80,6 +81,7 @@ typedef struct {
   int32_t weight_dtype;          /* dualar_dtype                                */
   int32_t max_batch;             /* sequences held by the workspace             */
   int32_t max_seq_len;           /* slow-AR positions per sequence              */
+  int32_t kv_dtype;              /* K/V cache type: dualar_dtype, -1 = weight_dtype */
 } dualar_config;
 
 /* One transformer layer.  q_norm / k_norm are [head_dim] gains shared by all
@@ -186,6 +188,18 @@ dualar_status dualar_fast_frames(dualar_ctx_t *ctx, int32_t batch, int32_t n_fra
 /* Block until the stream's work is done; report latched device faults.
  * *device_status (host, may be NULL) receives the raw status word. */
 dualar_status dualar_sync(dualar_ctx_t *ctx, int32_t *device_status);
+
+/* Measurement: after dualar_profile_begin(ctx, class), every launch of that
+ * kernel class on the context's stream is bracketed by a pair of hipEvents;
+ * dualar_profile_end() synchronises the stream and returns the number of
+ * launches, their summed event-to-event time (ms) and their summed
+ * algorithmic HBM bytes (weights + activations read and written, caches
+ * read and appended).  Classes: 0 matrix-vector (GEMV), 1 attention,
+ * 2 sampler, 3 fusion.  Profiling adds a few microseconds per launch; do not
+ * time throughput with it on. */
+typedef enum { DUALAR_K_GEMV = 0, DUALAR_K_ATTN = 1, DUALAR_K_SAMPLE = 2, DUALAR_K_EMBED = 3 } dualar_kernel_class;
+dualar_status dualar_profile_begin(dualar_ctx_t *ctx, int32_t kernel_class);
+dualar_status dualar_profile_end(dualar_ctx_t *ctx, int64_t *launches, double *total_ms, double *bytes);
 
 void dualar_destroy(dualar_ctx_t *ctx);
 

@@ -47,6 +47,7 @@ checkpoint's outputs, and the readings above measured against it.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -224,16 +225,22 @@ class Counters:
 
 
 class DualAROracle:
-    """Float64 Dual-AR decoder over given weights (numpy arrays by name)."""
+    """Dual-AR decoder over given weights (numpy arrays by name).
 
-    def __init__(self, cfg: dict, weights: dict, max_seq: int = 4096):
+    `dtype` is the compute precision: float64 by default.  float32 exists only
+    to measure how far an fp32 evaluation of the same steps drifts from the
+    float64 one (a floor for comparing fp32 kernels).  The K/V caches are
+    rounded to bf16 when cfg["kv_dtype"] (default: the weight dtype) is bf16."""
+
+    def __init__(self, cfg: dict, weights: dict, max_seq: int = 4096, dtype=F64):
         self.cfg = cfg
+        self.dt = dtype
         shapes = param_shapes(cfg)
         for name, shp in shapes.items():
             if tuple(weights[name].shape) != tuple(shp):
                 raise ValueError(f"{name}: shape {weights[name].shape} != {shp}")
-        self.w = {k: np.asarray(weights[k], dtype=F64) for k in shapes}
-        self.kv_bf16 = cfg["weight_dtype"] == "bf16"
+        self.w = {k: np.asarray(weights[k], dtype=dtype) for k in shapes}
+        self.kv_bf16 = cfg.get("kv_dtype", cfg["weight_dtype"]) == "bf16"
         self.eps = float(cfg["norm_eps"])
         self.N = cfg["num_codebooks"]
         self.C = cfg["codebook_size"]
@@ -252,9 +259,9 @@ class DualAROracle:
                          c["head_dim"], c["slow_qk_norm"])
         self.fast = part("fast_layers", c["n_fast_layer"], c["fast_dim"], c["fast_n_head"],
                          c["fast_n_kv_head"], c["fast_head_dim"], c["fast_qk_norm"])
-        self.slow_cos, self.slow_sin = rope_table(max_seq, c["head_dim"], c["rope_base"])
+        self.slow_cos, self.slow_sin = (t.astype(dtype) for t in rope_table(max_seq, c["head_dim"], c["rope_base"]))
         # The fast AR inherits the slow rope base; its positions are 0..N-1.
-        self.fast_cos, self.fast_sin = rope_table(self.N, c["fast_head_dim"], c["rope_base"])
+        self.fast_cos, self.fast_sin = (t.astype(dtype) for t in rope_table(self.N, c["fast_head_dim"], c["rope_base"]))
         # semantic_logit_bias: 0 on the semantic ids and <|im_end|>, -inf elsewhere.
         bias = np.full(c["vocab_size"], -np.inf)
         bias[self.sb:self.se + 1] = 0.0
@@ -265,12 +272,12 @@ class DualAROracle:
 
     # --- cache helpers -----------------------------------------------------
     def _kv(self, t):
-        return bf16_round(t) if self.kv_bf16 else t
+        return bf16_round(t).astype(self.dt) if self.kv_bf16 else t
 
     def new_sequence(self) -> SeqState:
         s = self.slow
         shp = (s.n_layer, self.max_seq, s.n_kv_head, s.head_dim)
-        return SeqState(k=np.zeros(shp), v=np.zeros(shp))
+        return SeqState(k=np.zeros(shp, dtype=self.dt), v=np.zeros(shp, dtype=self.dt))
 
     # --- a0: embedding + multi-codebook fusion -----------------------------
     def embed(self, col) -> np.ndarray:
@@ -285,7 +292,7 @@ class DualAROracle:
             for k in range(self.N):
                 x = x + self.w["codebook_embedding"][k * self.C + int(col[1 + k])]
             if self.cfg["scale_codebook_embeddings"]:
-                x = x / np.sqrt(self.N + 1.0)
+                x = x / math.sqrt(self.N + 1.0)
         return x
 
     # --- one transformer layer, one new position ---------------------------
@@ -303,10 +310,10 @@ class DualAROracle:
         K[pos] = self._kv(k)
         V[pos] = self._kv(v)
         rep = P.n_head // P.n_kv_head
-        o = np.empty((P.n_head, P.head_dim))
+        o = np.empty((P.n_head, P.head_dim), dtype=self.dt)
         for hh in range(P.n_head):
             g = hh // rep
-            s = K[:pos + 1, g, :] @ q[hh] / np.sqrt(P.head_dim)
+            s = K[:pos + 1, g, :] @ q[hh] / math.sqrt(P.head_dim)
             p = np.exp(s - s.max())
             p /= p.sum()
             o[hh] = p @ V[:pos + 1, g, :]
@@ -334,10 +341,10 @@ class DualAROracle:
         L = pos0 + T
         rep = P.n_head // P.n_kv_head
         mask = np.arange(L)[None, :] > pos[:, None]          # [T, L] future positions
-        O = np.empty((T, P.n_head, P.head_dim))
+        O = np.empty((T, P.n_head, P.head_dim), dtype=self.dt)
         for hh in range(P.n_head):
             g = hh // rep
-            S = Q[:, hh, :] @ K[:L, g, :].T / np.sqrt(P.head_dim)
+            S = Q[:, hh, :] @ K[:L, g, :].T / math.sqrt(P.head_dim)
             S[mask] = -np.inf
             Pm = np.exp(S - S.max(axis=1, keepdims=True))
             Pm /= Pm.sum(axis=1, keepdims=True)
@@ -392,9 +399,9 @@ class DualAROracle:
         (its output is not used); pass k = 1..N-1 embeds q^(k-1) at position k
         and samples q^(k) from the unmasked fast head.  Returns q^(0..N-1)."""
         F = self.fast
-        Kf = np.zeros((F.n_layer, self.N, F.n_kv_head, F.head_dim))
+        Kf = np.zeros((F.n_layer, self.N, F.n_kv_head, F.head_dim), dtype=self.dt)
         Vf = np.zeros_like(Kf)
-        self._fast_pass(np.asarray(h_slow, dtype=F64), 0, Kf, Vf)
+        self._fast_pass(np.asarray(h_slow, dtype=self.dt), 0, Kf, Vf)
         codes = [int(q0)]
         flog = []
         for k in range(1, self.N):
@@ -412,9 +419,9 @@ class DualAROracle:
         [h, E_fast(q^(0)), ..., E_fast(q^(N-2))]; returns the fast head's logits
         at positions 1..N-1 (the predictions of q^(1..N-1))."""
         F = self.fast
-        X = np.concatenate([np.asarray(h_slow, dtype=F64)[None, :],
+        X = np.concatenate([np.asarray(h_slow, dtype=self.dt)[None, :],
                             self.w["fast_embeddings"][np.asarray(codes[:self.N - 1])]], axis=0)
-        Kf = np.zeros((F.n_layer, self.N, F.n_kv_head, F.head_dim))
+        Kf = np.zeros((F.n_layer, self.N, F.n_kv_head, F.head_dim), dtype=self.dt)
         Vf = np.zeros_like(Kf)
         for i, lw in enumerate(F.layers):
             X = self._layer_seq(F, lw, X, 0, Kf[i], Vf[i], self.fast_cos, self.fast_sin)

@@ -24,9 +24,15 @@ def _dev():
 
 
 def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=REL_L2, min_frames=0,
-                    tag="", weights_f32=None):
+                    tag="", weights_f32=None, floor=False):
     """Prefill + n_frames single-frame decode calls on the GPU; the oracle
-    replays every sequence.  Returns per-row counts of frames compared."""
+    replays every sequence.  Returns per-row counts of frames compared.
+
+    With floor=True the oracle is also run in fp32, and each tap's bound is
+    max(tol, 4 x the fp32 oracle's distance to the fp64 oracle on the same
+    frame): with bf16 K/V caches, rounding to bf16 turns last-bit differences
+    of fp32 arithmetic into occasional one-ulp (2^-8) cache differences, so an
+    exact fp32 evaluation of the same steps already sits at that distance."""
     DualAR, upload = _dev()
     B, N = len(plen), m["num_codebooks"]
     greedy = samp["greedy"]
@@ -54,25 +60,49 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
                       top_p=samp.get("top_p", 1.0), min_frames=min_frames)
     compared = []
     worst = {"fused_x": 0.0, "slow_hidden": 0.0, "slow_logits": 0.0, "fast_logits": 0.0}
+    floors = []
     for b in range(B):
         o = DualAROracle(m, wf, max_seq=int(plen[b]) + n_frames + 2)
         seq = o.new_sequence()
+        if floor:
+            o32 = DualAROracle(m, wf, max_seq=int(plen[b]) + n_frames + 2, dtype=np.float32)
+            seq32 = o32.new_sequence()
+            fl = {"fused_x": 0.0, "slow_hidden": 0.0, "slow_logits": 0.0, "fast_logits": 0.0}
+            in_step = True
         u = None if uniforms is None else uniforms[:, b, :].astype(np.float64)
         n_ok = 0
         for f in range(n_frames + 1):
             ofr = o.prefill(seq, prompts[b][:, :plen[b]], osamp, None if u is None else u[0]) if f == 0 \
                 else o.decode_frame(seq, osamp, None if u is None else u[f])
             gfr = g_frames[f][b].tolist()
+            bound = dict.fromkeys(worst, tol)
+            bound["fused_x"] = 1e-5
+            if floor and in_step:
+                o32fr = o32.prefill(seq32, prompts[b][:, :plen[b]], osamp, None if u is None else u[0]) if f == 0 \
+                    else o32.decode_frame(seq32, osamp, None if u is None else u[f])
+                if f > 0:
+                    for k in ("fused_x", "slow_hidden", "slow_logits"):
+                        fl[k] = max(fl[k], rel_l2(o32.taps[k], o.taps[k]))
+                    if o32fr[:2] == ofr[:2] and ofr[0] != m["end_id"]:
+                        kd = next((i for i in range(1, N) if o32fr[1 + i] != ofr[1 + i]), N)
+                        fl["fast_logits"] = max(fl["fast_logits"],
+                                                rel_l2(o32.taps["fast_logits"][:kd], o.taps["fast_logits"][:kd]))
+                in_step = o32fr == ofr
+            if floor:
+                for k in ("slow_hidden", "slow_logits", "fast_logits"):
+                    bound[k] = max(tol, 4.0 * fl[k])
             if f > 0 and g_taps[f] is not None and ofr[0] != -1:
                 t = g_taps[f]
                 for k in ("fused_x", "slow_hidden", "slow_logits"):
                     e = rel_l2(t[k][b], o.taps[k])
                     worst[k] = max(worst[k], e)
-                    assert e <= (1e-5 if k == "fused_x" else tol), (tag, b, f, k, e)
-            if f > 0 and g_taps[f] is not None and ofr[0] not in (-1, m["end_id"]):
-                e = rel_l2(g_taps[f]["fast_logits"][b], o.taps["fast_logits"])
+                    assert e <= bound[k], (tag, b, f, k, e, bound[k])
+            if f > 0 and g_taps[f] is not None and ofr[0] not in (-1, m["end_id"]) and gfr[0] == ofr[0]:
+                # fast logits of pass k depend on q^(0..k-1): compare up to the first differing code
+                kd = next((i for i in range(1, N) if gfr[1 + i] != ofr[1 + i]), N)
+                e = rel_l2(g_taps[f]["fast_logits"][b][:kd], o.taps["fast_logits"][:kd])
                 worst["fast_logits"] = max(worst["fast_logits"], e)
-                assert e <= tol, (tag, b, f, "fast_logits", e)
+                assert e <= bound["fast_logits"], (tag, b, f, "fast_logits", e, bound["fast_logits"])
             if gfr == ofr:
                 n_ok += 1
                 if seq.done:
@@ -95,9 +125,13 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
             say(f"[{tag}] row {b} frame {f}: near-tie (margin {mg:.2e}); stop comparing this row")
             break
         compared.append(n_ok)
+        if floor:
+            floors.append(fl)
         if n_ok == n_frames + 1 and not seq.done:
             assert g_emitted[b] == seq.frames, (tag, b, g_emitted[b], seq.frames)
     say(f"[{tag}] frames compared per row {compared}; worst rel L2 {worst}")
+    if floor:
+        say(f"[{tag}] fp32-oracle distance to the fp64 oracle per row: {floors}")
     return compared, worst
 
 
@@ -276,10 +310,12 @@ def test_s2_fast_only(s2_fast, B):
     for b in range(B):
         for f in range(F):
             ref = fo.frame(h[f, b], int(q0[f, b]))
-            if f == F - 1:
-                e = rel_l2(fl[b], fo.logits)
-                assert e <= REL_L2, (b, e)
             got = codes[b, f].tolist()
+            if f == F - 1:
+                # pass k's logits depend on q^(0..k-1): compare up to the first differing code
+                kd = next((i for i in range(1, m["num_codebooks"]) if got[i] != ref[i]), m["num_codebooks"])
+                e = rel_l2(fl[b][:kd], fo.logits[:kd])
+                assert e <= REL_L2, (b, e, kd)
             if got != ref:
                 k = next(i for i in range(m["num_codebooks"]) if got[i] != ref[i])
                 assert k >= 1, (b, f, got, ref)       # q^(0) is an input
@@ -312,11 +348,28 @@ class _FastOracle:
 # Full S2-shaped model, short prompt (oracle in seconds), batch 1
 # ----------------------------------------------------------------------------
 
-@pytest.mark.timeout(400)
-def test_s2_full_short_prompt():
+@pytest.fixture(scope="module")
+def s2_full():
     m = synth.model("s2")
     say("[s2-full] generating 4.56 B weights")
-    w = synth.make_weights(m, seed=0)
+    return m, synth.make_weights(m, seed=0)
+
+
+@pytest.mark.timeout(400)
+def test_s2_full_fp32_kv_strict(s2_full):
+    # fp32 K/V caches: no rounding point between the two sides, so the bar is
+    # the plain 2e-3 relative L2 on every tap.
+    m, w = s2_full
+    m = dict(m, kv_dtype="f32")
     P = synth.make_prompts(m, ("fixed", 5, 20, 15), [40], seed=0)
-    c, worst = run_and_compare(m, w, P, [40], 2, dict(greedy=1), tag="s2-full")
+    c, worst = run_and_compare(m, w, P, [40], 2, dict(greedy=1), tag="s2-full-kvf32")
+    assert c[0] >= 2
+    assert max(worst.values()) < 2e-4
+
+
+@pytest.mark.timeout(600)
+def test_s2_full_bf16_kv(s2_full):
+    m, w = s2_full
+    P = synth.make_prompts(m, ("fixed", 5, 20, 15), [40], seed=0)
+    c, worst = run_and_compare(m, w, P, [40], 2, dict(greedy=1), tag="s2-full-kvbf16", floor=True)
     assert c[0] >= 2
