@@ -81,8 +81,11 @@ bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
   REQ(r->fffn > 0 && r->fffn % unit == 0 && r->fffn <= 12288, "fast_ffn_dim must be a multiple of 512 (bf16) / 256 (f32), <= 12288");
   REQ(r->hd == 64 || r->hd == 128, "head_dim must be 64 or 128");
   REQ(r->fhd == 64 || r->fhd == 128, "fast_head_dim must be 64 or 128");
-  REQ(r->H > 0 && r->KV > 0 && r->H % r->KV == 0 && r->H / r->KV <= 8, "n_head must be a multiple (<= 8x) of n_kv_head");
-  REQ(r->fH > 0 && r->fKV > 0 && r->fH % r->fKV == 0 && r->fH / r->fKV <= 8, "fast_n_head must be a multiple (<= 8x) of fast_n_kv_head");
+  auto rep_ok = [](int h, int kv) {
+    return h > 0 && kv > 0 && h % kv == 0 && (h / kv == 1 || h / kv == 2 || h / kv == 4 || h / kv == 8);
+  };
+  REQ(rep_ok(r->H, r->KV), "n_head must be 1, 2, 4 or 8 times n_kv_head");
+  REQ(rep_ok(r->fH, r->fKV), "fast_n_head must be 1, 2, 4 or 8 times fast_n_kv_head");
   REQ((r->H * r->hd) % unit == 0 && (r->fH * r->fhd) % unit == 0, "n_head*head_dim must be a multiple of the row unit");
   REQ(r->V > 0 && r->V < (1 << 30), "vocab_size out of range");
   REQ(r->N >= 2 && r->N <= 32, "num_codebooks out of range [2, 32]");
@@ -92,7 +95,7 @@ bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
   REQ(r->base > 1.0f && isfinite(r->base), "rope_base must be > 1");
   REQ(r->eps >= 0.0f && isfinite(r->eps), "norm_eps must be >= 0");
   REQ(r->max_batch >= 1 && r->max_batch <= 256, "max_batch out of range [1, 256]");
-  REQ(r->max_seq >= 2 && r->max_seq <= (1 << 20), "max_seq_len out of range [2, 2^20]");
+  REQ(r->max_seq >= 2 && r->max_seq <= 65536, "max_seq_len out of range [2, 65536]");
 #undef REQ
   return true;
 }
@@ -101,7 +104,7 @@ Layout layout(const Resolved& r) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
-  L.max_splits = (r.max_seq + 31) / 32;
+  L.max_splits = (r.max_seq + 15) / 16;   // smallest attention chunk is 16 positions
   L.slow_layer_stride = (size_t)r.max_batch * r.KV * r.max_seq * r.hd;
   L.fast_layer_stride = (size_t)r.max_batch * r.fKV * r.N * r.fhd;
   L.kslow = take(L.slow_layer_stride * r.n_layer * r.kvesz);
@@ -252,9 +255,8 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.max_pos = S.max_pos; a.pos = pos_dev; a.pos_const = pos_const; a.rope = S.rope;
   a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
   a.H = S.H; a.KV = S.KV; a.hd = S.hd;
-  a.chunk = B == 1 ? 32 : (B <= 4 ? 64 : 256);
-  a.max_splits = (Lmax + a.chunk - 1) / a.chunk;
-  if (a.max_splits > L.max_splits) a.max_splits = L.max_splits;
+  a.it = B == 1 ? 2 : (B <= 4 ? 4 : 8);
+  a.lmax = Lmax;
   a.part = (float*)(c->ws + L.part);
   a.counters = (unsigned*)(c->ws + L.counters);
   a.out = att; a.ld_out = L.att_ld; a.B = B;

@@ -1,28 +1,33 @@
 // GQA decode attention for one new position per sequence (slow AR over the
 // time cache, fast AR over the N-slot depth cache).
 //
-// Grid (split, kv_head, batch).  A workgroup takes `chunk` consecutive cache
-// positions of one KV head and the rep = H/KV query heads that share it
-// (contiguous grouping: query head h uses KV head h / rep).  It
-//   1. applies QK-norm (per-head RMSNorm, one [hd] gain) and RoPE to the new
-//      q heads, folding in the 1/sqrt(hd) score scale;
-//   2. if its chunk holds the new position, normalises/rotates the new k,
-//      rounds k and v to the cache type and appends them;
-//   3. computes scores, a chunk-local softmax (max m, sum l) and the
-//      unnormalised P.V, and writes (o, m, l) partials;
-//   4. the last workgroup of a (sequence, KV head) to finish (atomic
-//      counter) merges the partials: o = sum_s e^(m_s-M) o_s / sum_s e^(m_s-M) l_s.
+// attn_partial_kernel, grid (split, kv_head, batch): a workgroup takes one
+// chunk of CH = 4 waves x PPW x IT consecutive cache positions of one KV
+// head and the rep = H/KV query heads sharing it (contiguous grouping: query
+// head h uses KV head h / rep).  It
+//   1. issues every K and V load of its chunk up front (they do not depend on
+//      q), so one memory latency covers the chunk;
+//   2. applies QK-norm (per-head RMSNorm with one [hd] gain) and RoPE to the
+//      new q heads, folding in the 1/sqrt(hd) score scale;
+//   3. if its chunk holds the new position, normalises/rotates the new k,
+//      rounds k and v to the cache type and appends them (the new entry is
+//      taken from LDS, never re-read from memory);
+//   4. computes scores, a chunk-local softmax (max m, sum l) and the
+//      unnormalised P.V, and writes (o, m, l) -- or, when the whole context
+//      fits one chunk, the final o = P.V / l.
+// attn_merge_kernel, grid (batch, H): o = sum_s e^(m_s-M) o_s / sum_s e^(m_s-M) l_s.
+// There are no atomics or cross-workgroup fences: the merge is its own launch.
 // K/V rows are read with 16-byte lane loads: LPP = hd*sizeof(KT)/16 lanes
-// cover one position, so a wave reads 64/LPP positions per load.
+// cover one position, so a wave reads PPW = 64/LPP positions per load.
 #include "common.h"
 #include "internal.h"
 
-#define ATT_MAXREP 8
 #define ATT_MAXHD 128
-#define ATT_MAXCHUNK 256
+#define ATT_MAXCH 256
+#define ATT_MAXSPLIT 4096   // max_seq_len <= 65536 and chunks of >= 16 positions
 
-template <typename T, typename KT>
-__global__ void __launch_bounds__(DUALAR_WG) attn_kernel(AttnParams p) {
+template <typename T, typename KT, int IT, int REP>
+__global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int pos = p.pos ? p.pos[b] : p.pos_const;
   if (pos < 0) return;                      // inactive row (prefill padding)
@@ -30,89 +35,130 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_kernel(AttnParams p) {
   const int n_splits = (L + p.chunk - 1) / p.chunk;
   if (split >= n_splits) return;
   const int c0 = split * p.chunk, c1 = min(c0 + p.chunk, L);
-  const int hd = p.hd, rep = p.H / p.KV;
+  const int hd = p.hd;
+  constexpr int rep = REP;   // query heads per KV head
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  __shared__ float qs[ATT_MAXREP][ATT_MAXHD];
-  __shared__ float knew[ATT_MAXHD], vnew[ATT_MAXHD];
-  __shared__ float sc[ATT_MAXREP][ATT_MAXCHUNK];
-  __shared__ float accs[4][ATT_MAXREP][ATT_MAXHD];
-  __shared__ float ml[ATT_MAXREP][2];
-  __shared__ int is_last;
-
-  const float* row = p.qkv + (size_t)b * p.ld_qkv;
-  const float2* rope = p.rope + (size_t)pos * (hd / 2);
-  const bool pair_live = 2 * lane < hd;
-  const float qscale = 1.0f / sqrtf((float)hd);
-
-  // ---- 1. new q heads: QK-norm, RoPE, scale ----
-  for (int hl = wave; hl < rep; hl += 4) {
-    const float* qp = row + (size_t)(g * rep + hl) * hd;
-    float a = pair_live ? qp[2 * lane] : 0.f, c = pair_live ? qp[2 * lane + 1] : 0.f;
-    if (p.q_norm) {
-      const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)hd + p.eps);
-      if (pair_live) {
-        a = a * inv * ElemT<T>::load(p.q_norm, 2 * lane);
-        c = c * inv * ElemT<T>::load(p.q_norm, 2 * lane + 1);
-      }
-    }
-    if (pair_live) {
-      const float2 cs = rope[lane];
-      qs[hl][2 * lane] = (a * cs.x - c * cs.y) * qscale;
-      qs[hl][2 * lane + 1] = (a * cs.y + c * cs.x) * qscale;
-    }
-  }
-  // ---- 2. new k / v (only the workgroup holding position pos) ----
-  const size_t head_base = ((size_t)b * p.KV + g) * p.max_pos;
-  if (c1 == L) {
-    if (wave == 0) {
-      const float* kp = row + (size_t)p.H * hd + (size_t)g * hd;
-      float a = pair_live ? kp[2 * lane] : 0.f, c = pair_live ? kp[2 * lane + 1] : 0.f;
-      if (p.k_norm) {
-        const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)hd + p.eps);
-        if (pair_live) {
-          a = a * inv * ElemT<T>::load(p.k_norm, 2 * lane);
-          c = c * inv * ElemT<T>::load(p.k_norm, 2 * lane + 1);
-        }
-      }
-      if (pair_live) {
-        const float2 cs = rope[lane];
-        const float ra = ElemT<KT>::round(a * cs.x - c * cs.y);
-        const float rc = ElemT<KT>::round(a * cs.y + c * cs.x);
-        knew[2 * lane] = ra;
-        knew[2 * lane + 1] = rc;
-        ElemT<KT>::store(p.kcache, (head_base + pos) * hd + 2 * lane, ra);
-        ElemT<KT>::store(p.kcache, (head_base + pos) * hd + 2 * lane + 1, rc);
-      }
-    } else if (wave == 1) {
-      const float* vp = row + (size_t)(p.H + p.KV) * hd + (size_t)g * hd;
-      for (int e = lane; e < hd; e += 64) {
-        const float v = ElemT<KT>::round(vp[e]);
-        vnew[e] = v;
-        ElemT<KT>::store(p.vcache, (head_base + pos) * hd + e, v);
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- 3a. scores ----
   constexpr int EPL = ElemT<KT>::EPV;
   const int LPP = hd / EPL;
   const int PPW = 64 / LPP;
   const int sub = lane % LPP, grp = lane / LPP;
+
+  __shared__ float qs[REP][ATT_MAXHD];
+  __shared__ float knew[ATT_MAXHD], vnew[ATT_MAXHD];
+  __shared__ float sc[REP][ATT_MAXCH];
+  __shared__ float accs[4][REP][ATT_MAXHD];
+  __shared__ float ml[REP][2];
+
+  const size_t head_base = ((size_t)b * p.KV + g) * p.max_pos;
   const char* kbase = (const char*)p.kcache + head_base * hd * sizeof(KT);
   const char* vbase = (const char*)p.vcache + head_base * hd * sizeof(KT);
-  for (int j0 = c0 + wave * PPW; j0 < c1; j0 += 4 * PPW) {
-    const int j = j0 + grp;
-    float kv[EPL];
-    if (j < c1 && j != pos) {
-      ElemT<KT>::unpack(ld_vec(kbase + ((size_t)j * hd + sub * EPL) * sizeof(KT)), kv);
-    } else {
+
+  // ---- 1. the chunk's K/V loads, first ----
+  // Lanes whose position is outside the chunk, or is the entry being
+  // appended, read entry 0 of this head instead and discard it.
+  u32x4 kr[IT], vr[IT];
+  int jj[IT];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) kv[e] = (j == pos) ? knew[sub * EPL + e] : 0.f;
+  for (int it = 0; it < IT; ++it) {
+    const int j = c0 + (it * 4 + wave) * PPW + grp;
+    jj[it] = j;
+    const bool ok = j < c1 && j != pos;
+    const size_t off = ((size_t)(ok ? j : 0) * hd + sub * EPL) * sizeof(KT);
+    kr[it] = ld_vec(kbase + off);
+    vr[it] = ld_vec(vbase + off);
+  }
+
+  const float* row = p.qkv + (size_t)b * p.ld_qkv;
+  const float2* rope = p.rope + (size_t)pos * (hd / 2);
+  const bool pair_live = 2 * lane < hd;
+  const int pl = pair_live ? 2 * lane : 0;
+  const float qscale = 1.0f / sqrtf((float)hd);
+  const bool has_new = c1 == L;
+
+  // ---- 2. every other global load, before any of them is used ----
+  // q pairs of this wave's heads (hl = wave, wave + 4), the gains, the RoPE
+  // entry of the pair, and (workgroup holding pos) the new k pair / v values.
+  float qa[2], qc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int hl = min(wave + 4 * i, rep - 1);
+    const float* qp = row + (size_t)(g * rep + hl) * hd;
+    qa[i] = qp[pl];
+    qc[i] = qp[pl + 1];
+  }
+  const float2 cs = rope[pair_live ? lane : 0];
+  float qga = 1.f, qgc = 1.f, kga = 1.f, kgc = 1.f;
+  if (p.q_norm) { qga = ElemT<T>::load(p.q_norm, pl); qgc = ElemT<T>::load(p.q_norm, pl + 1); }
+  float ka = 0.f, kc = 0.f, vv0 = 0.f, vv1 = 0.f;
+  if (has_new && wave == 0) {
+    const float* kp = row + (size_t)p.H * hd + (size_t)g * hd;
+    ka = kp[pl];
+    kc = kp[pl + 1];
+    if (p.k_norm) { kga = ElemT<T>::load(p.k_norm, pl); kgc = ElemT<T>::load(p.k_norm, pl + 1); }
+  }
+  if (has_new && wave == 1) {
+    const float* vp = row + (size_t)(p.H + p.KV) * hd + (size_t)g * hd;
+    vv0 = vp[lane];
+    vv1 = vp[min(lane + 64, hd - 1)];
+  }
+
+  // ---- 3. new q heads: QK-norm, RoPE, scale ----
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int hl = wave + 4 * i;
+    if (hl >= rep) break;
+    float a = pair_live ? qa[i] : 0.f, c = pair_live ? qc[i] : 0.f;
+    if (p.q_norm) {
+      const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)hd + p.eps);
+      a = a * inv * qga;
+      c = c * inv * qgc;
+    }
+    if (pair_live) {
+      qs[hl][2 * lane] = (a * cs.x - c * cs.y) * qscale;
+      qs[hl][2 * lane + 1] = (a * cs.y + c * cs.x) * qscale;
+    }
+  }
+  // ---- new k / v appended by the workgroup holding position pos ----
+  if (has_new && wave == 0) {
+    float a = pair_live ? ka : 0.f, c = pair_live ? kc : 0.f;
+    if (p.k_norm) {
+      const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)hd + p.eps);
+      a = a * inv * kga;
+      c = c * inv * kgc;
+    }
+    if (pair_live) {
+      const float ra = ElemT<KT>::round(a * cs.x - c * cs.y);
+      const float rc = ElemT<KT>::round(a * cs.y + c * cs.x);
+      knew[2 * lane] = ra;
+      knew[2 * lane + 1] = rc;
+      ElemT<KT>::store(p.kcache, (head_base + pos) * hd + 2 * lane, ra);
+      ElemT<KT>::store(p.kcache, (head_base + pos) * hd + 2 * lane + 1, rc);
+    }
+  } else if (has_new && wave == 1) {
+    const float r0 = ElemT<KT>::round(vv0);
+    vnew[lane] = r0;
+    ElemT<KT>::store(p.vcache, (head_base + pos) * hd + lane, r0);
+    if (lane + 64 < hd) {
+      const float r1 = ElemT<KT>::round(vv1);
+      vnew[lane + 64] = r1;
+      ElemT<KT>::store(p.vcache, (head_base + pos) * hd + lane + 64, r1);
+    }
+  }
+  __syncthreads();
+
+  // ---- 4a. scores ----
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j = jj[it];
+    float kv[EPL];
+    ElemT<KT>::unpack(kr[it], kv);
+    if (j == pos) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kv[e] = knew[sub * EPL + e];
     }
 #pragma unroll
-    for (int hl = 0; hl < ATT_MAXREP; ++hl) {
+    for (int hl = 0; hl < REP; ++hl) {
       if (hl >= rep) break;
       float d = 0.f;
 #pragma unroll
@@ -123,7 +169,7 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  // ---- 3b. chunk-local softmax ----
+  // ---- 4b. chunk-local softmax ----
   const int n = c1 - c0;
   for (int hl = wave; hl < rep; hl += 4) {
     float m = -INFINITY;
@@ -140,39 +186,36 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  // ---- 3c. unnormalised P.V ----
-  float acc[ATT_MAXREP][EPL];
+  // ---- 4c. unnormalised P.V ----
+  float acc[REP][EPL];
 #pragma unroll
-  for (int hl = 0; hl < ATT_MAXREP; ++hl)
+  for (int hl = 0; hl < REP; ++hl)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[hl][e] = 0.f;
-  for (int j0 = c0 + wave * PPW; j0 < c1; j0 += 4 * PPW) {
-    const int j = j0 + grp;
-    if (j < c1) {
-      float vv[EPL];
-      if (j != pos) {
-        ElemT<KT>::unpack(ld_vec(vbase + ((size_t)j * hd + sub * EPL) * sizeof(KT)), vv);
-      } else {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) vv[e] = vnew[sub * EPL + e];
-      }
+  for (int it = 0; it < IT; ++it) {
+    const int j = jj[it];
+    if (j >= c1) continue;
+    float vv[EPL];
+    ElemT<KT>::unpack(vr[it], vv);
+    if (j == pos) {
 #pragma unroll
-      for (int hl = 0; hl < ATT_MAXREP; ++hl) {
-        if (hl >= rep) break;
-        const float pj = sc[hl][j - c0];
+      for (int e = 0; e < EPL; ++e) vv[e] = vnew[sub * EPL + e];
+    }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[hl][e] = fmaf(pj, vv[e], acc[hl][e]);
-      }
+    for (int hl = 0; hl < REP; ++hl) {
+      if (hl >= rep) break;
+      const float pj = sc[hl][j - c0];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[hl][e] = fmaf(pj, vv[e], acc[hl][e]);
     }
   }
 #pragma unroll
-  for (int hl = 0; hl < ATT_MAXREP; ++hl) {
+  for (int hl = 0; hl < REP; ++hl) {
     if (hl >= rep) break;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      float v = acc[hl][e];
-      for (int o = LPP; o < 64; o <<= 1) v += __shfl_xor(v, o);
-      acc[hl][e] = v;
+      acc[hl][e] = across_groups_sum(acc[hl][e], LPP);
     }
   }
   if (grp == 0) {
@@ -184,42 +227,90 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_kernel(AttnParams p) {
   for (int i = tid; i < rep * hd; i += DUALAR_WG) {
     const int hl = i / hd, e = i % hd;
     const float o = (accs[0][hl][e] + accs[1][hl][e]) + (accs[2][hl][e] + accs[3][hl][e]);
-    float* pp = p.part + (((size_t)b * p.H + g * rep + hl) * p.max_splits + split) * (hd + 2);
-    pp[e] = o;
-    if (e == 0) { pp[hd] = ml[hl][0]; pp[hd + 1] = ml[hl][1]; }
-  }
-
-  // ---- 4. last workgroup merges the splits ----
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&p.counters[b * p.KV + g], 1u);
-    is_last = (prev == (unsigned)(n_splits - 1));
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int i = tid; i < rep * hd; i += DUALAR_WG) {
-    const int hl = i / hd, e = i % hd;
-    const int h = g * rep + hl;
-    const float* pp = p.part + ((size_t)b * p.H + h) * p.max_splits * (hd + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, pp[(size_t)s * (hd + 2) + hd]);
-    float lsum = 0.f, o = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-      const float* q = pp + (size_t)s * (hd + 2);
-      const float w = expf(q[hd] - M);
-      lsum = fmaf(q[hd + 1], w, lsum);
-      o = fmaf(q[e], w, o);
+    if (n_splits == 1) {
+      p.out[(size_t)b * p.ld_out + (size_t)(g * rep + hl) * hd + e] = o / ml[hl][1];
+    } else {
+      float* pp = p.part + (((size_t)b * p.H + g * rep + hl) * p.max_splits + split) * (hd + 2);
+      pp[e] = o;
+      if (e == 0) { pp[hd] = ml[hl][0]; pp[hd + 1] = ml[hl][1]; }
     }
-    p.out[(size_t)b * p.ld_out + (size_t)h * hd + e] = o / lsum;
   }
-  if (tid == 0) atomicExch(&p.counters[b * p.KV + g], 0u);
 }
 
-template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
+// One workgroup per (sequence, query head) merges the split partials:
+// M = max_s m_s and the weights w_s = e^(m_s - M) are computed for all splits
+// at once (one split per thread), then o[e] = sum_s w_s o_s[e] / sum_s w_s l_s
+// with the o_s loads issued 16 at a time.  Fixed summation order.
+#define MERGE_T 128
+__global__ void __launch_bounds__(MERGE_T) attn_merge_kernel(AttnParams p) {
+  const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
+  const int pos = p.pos ? p.pos[b] : p.pos_const;
+  if (pos < 0) return;
+  const int n_splits = (pos + 1 + p.chunk - 1) / p.chunk;
+  if (n_splits == 1) return;                   // the partial kernel wrote o
+  const int hd = p.hd;
+  const float* pp = p.part + ((size_t)b * p.H + h) * p.max_splits * (hd + 2);
+  __shared__ float wsh[ATT_MAXSPLIT];
+  __shared__ float red[2];
+  __shared__ float lred[2];
+  // 1. weights of every split
+  float mloc = -INFINITY;
+  for (int s = t; s < n_splits; s += MERGE_T) mloc = fmaxf(mloc, pp[(size_t)s * (hd + 2) + hd]);
+  mloc = wave_max(mloc);
+  if (lane == 0) red[wv] = mloc;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
+  float lloc = 0.f;
+  for (int s = t; s < n_splits; s += MERGE_T) {
+    const float* q = pp + (size_t)s * (hd + 2);
+    const float w = expf(q[hd] - M);
+    wsh[s] = w;
+    lloc += q[hd + 1] * w;
+  }
+  lloc = wave_sum(lloc);
+  if (lane == 0) lred[wv] = lloc;
+  __syncthreads();
+  const float lsum = lred[0] + lred[1];
+  // 2. weighted sum of the partial outputs
+  if (t >= hd) return;
+  float o = 0.f;
+  for (int s0 = 0; s0 < n_splits; s0 += 16) {
+    float ov[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ov[i] = pp[(size_t)min(s0 + i, n_splits - 1) * (hd + 2) + t];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (s0 + i < n_splits) o = fmaf(ov[i], wsh[s0 + i], o);
+  }
+  p.out[(size_t)b * p.ld_out + (size_t)h * hd + t] = o / lsum;
+}
+
+int attn_chunk(int kv_esz, int hd, int it) {
+  const int lpp = hd * kv_esz / 16;
+  return 4 * (64 / lpp) * it;
+}
+
+template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p0, hipStream_t s) {
+  AttnParams p = p0;
+  p.chunk = attn_chunk((int)sizeof(KT), p.hd, p.it);
+  p.max_splits = (p.lmax + p.chunk - 1) / p.chunk;
   dim3 grid(p.max_splits, p.KV, p.B);
-  hipLaunchKernelGGL((attn_kernel<T, KT>), grid, dim3(DUALAR_WG), 0, s, p);
+  const int rep = p.H / p.KV;
+#define ATT_GO(IT, REP) hipLaunchKernelGGL((attn_partial_kernel<T, KT, IT, REP>), grid, dim3(DUALAR_WG), 0, s, p)
+#define ATT_REP(IT)                       \
+  if (rep == 1) ATT_GO(IT, 1);            \
+  else if (rep == 2) ATT_GO(IT, 2);       \
+  else if (rep == 4) ATT_GO(IT, 4);       \
+  else ATT_GO(IT, 8);
+  if (p.it == 2) { ATT_REP(2) }
+  else if (p.it == 4) { ATT_REP(4) }
+  else { ATT_REP(8) }
+#undef ATT_REP
+#undef ATT_GO
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_splits == 1) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(p.B, p.H), dim3(MERGE_T), 0, s, p);
   return hipGetLastError();
 }
 

@@ -53,21 +53,63 @@ __device__ __forceinline__ u32x4 ld_stream(const void* p) {
 }
 __device__ __forceinline__ u32x4 ld_vec(const void* p) { return *(const u32x4*)p; }
 
-// Butterfly sum over the 64 lanes of a wave (fixed order: deterministic).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// Cross-lane reductions on VALU instructions: DPP row permutations inside a
+// row of 16 lanes and the gfx950 permlane16/32 swaps across rows.  Every
+// step adds a lane's value to its partner's with the same two operands in
+// the same order on both lanes, so results are identical across lanes and
+// deterministic.
+#define DPP_F(v, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, true))
+__device__ __forceinline__ float xor1_of(float v) { return DPP_F(v, 0xB1); }   // quad_perm [1,0,3,2]
+__device__ __forceinline__ float xor2_of(float v) { return DPP_F(v, 0x4E); }   // quad_perm [2,3,0,1]
+__device__ __forceinline__ float mir8_of(float v) { return DPP_F(v, 0x141); }  // row_half_mirror
+__device__ __forceinline__ float mir16_of(float v) { return DPP_F(v, 0x140); } // row_mirror
+__device__ __forceinline__ float xor8_of(float v) { return DPP_F(v, 0x128); }  // row_ror:8
+// v(lane) + v(lane ^ 16) and v(lane) + v(lane ^ 32), lower lane's value first
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum over aligned groups of `width` lanes (8, 16, 32 or 64); every lane of a
+// group ends with the group's sum.  The pairing (x + partner) is arranged so
+// that both lanes of a pair add the same operands: after each step all lanes
+// of the group-so-far hold one value.
 __device__ __forceinline__ float group_sum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  v = v + xor1_of(v);
+  v = v + xor2_of(v);
+  v = v + mir8_of(v);
+  if (width >= 16) v = v + mir16_of(v);
+  if (width >= 32) v = add_xor16(v);
+  if (width >= 64) v = add_xor32(v);
   return v;
+}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, xor1_of(v));
+  v = fmaxf(v, xor2_of(v));
+  v = fmaxf(v, mir8_of(v));
+  v = fmaxf(v, mir16_of(v));
+  v = max_xor16(v);
+  return max_xor32(v);
+}
+// Sum over the lanes sharing (lane % width), width 8, 16 or 32: the 64/width
+// groups are added together.
+__device__ __forceinline__ float across_groups_sum(float v, int width) {
+  if (width <= 8) v = v + xor8_of(v);
+  if (width <= 16) v = add_xor16(v);
+  return add_xor32(v);
 }
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + expf(-a)); }

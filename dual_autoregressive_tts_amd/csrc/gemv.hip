@@ -1,14 +1,21 @@
-// Bandwidth-bound matrix-vector products of the decode step (batch <= 4 per
-// pass): y = W . f(x) with W streamed once from HBM in 16-byte lane loads.
+// Bandwidth-bound matrix-vector products of the decode step (up to 4
+// activation rows per pass): y = W . f(x), W streamed once from HBM in
+// 16-byte lane loads.
 //
-// Layout: a workgroup is 4 waves; each wave owns RPW output rows (RPW pairs
-// for the SwiGLU gate/up product).  Lane l reads elements
-// [u*64*EPV + l*EPV, +EPV) of a row for unit u, so one wave load covers 1 KB
-// of one row, contiguous.  The activation rows (BT of them, fp32) are staged
-// in LDS once per workgroup; when a norm gain is given the RMSNorm of the
-// activations is applied while staging (fused prologue).  Partial dot
-// products are reduced across the wave with a fixed butterfly, so results
-// are deterministic.
+// A workgroup is 4 waves; each wave owns RPW output rows (RPW gate/up row
+// pairs for SwiGLU).  Lane l reads elements [u*64*EPV + l*EPV, +EPV) of a row
+// for unit u, so one wave load covers 1 KB of one row, contiguous.
+//
+// gemv_unrolled_kernel (rows of exactly NU units, NU a compile-time
+// constant): every weight load of the wave is issued first -- NU*RPW*NR
+// 16-byte loads per lane in flight -- and only then are the activations
+// staged into LDS (with the fused RMSNorm prologue when a gain is given), so
+// staging hides under the weight latency.  gemv_loop_kernel serves any other
+// row length with a two-deep software pipeline.
+//
+// Partial dot products are reduced across the wave with a fixed butterfly,
+// so results are deterministic.  Epilogues: store, residual add, SwiGLU
+// (silu(gate) * up).
 #include "common.h"
 #include "internal.h"
 
@@ -22,24 +29,42 @@ template <typename T> __device__ __forceinline__ const char* seg_row(const GemvP
   return (const char*)p.w[2] + (size_t)row * p.K * sizeof(T);
 }
 
-template <typename T, int BT, int RPW, int NR>
-__global__ void __launch_bounds__(DUALAR_WG) gemv_kernel(GemvParams p) {
-  extern __shared__ float xs[];  // [BT][K]
-  __shared__ float red[BT][4];
-  constexpr int EPV = ElemT<T>::EPV;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = p.K;
-  const int b0 = blockIdx.y * BT;
+// Activation rows for the LDS-staged kernels: a thread's share of BT rows
+// (XR float4 per row) is loaded into registers first, before any weight load
+// of the wave, then written to LDS once the weights are in flight.
+template <int BT, int XR>
+struct XRegs { float4 v[BT][XR]; };
 
-  // ---- stage activations (+ fused RMSNorm) ----
+template <int BT, int XR>
+__device__ __forceinline__ void load_x(const GemvParams& p, XRegs<BT, XR>& xr, int b0) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) {
     const int b = b0 + bb;
+    const float4* src = (const float4*)(p.x + (size_t)b * p.ldx);
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int k4 = tid + i * DUALAR_WG;
+      xr.v[bb][i] = (b < p.B && k4 < p.K / 4) ? src[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+// Write the staged rows to LDS, then apply RMSNorm * gain when a gain is set.
+template <typename T, int BT, int XR>
+__device__ __forceinline__ void store_x(const GemvParams& p, const XRegs<BT, XR>& xr, float* xs, float (*red)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = p.K;
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) {
     float ss = 0.f;
-    for (int k = tid; k < K; k += DUALAR_WG) {
-      float v = (b < p.B) ? p.x[(size_t)b * p.ldx + k] : 0.f;
-      xs[bb * K + k] = v;
-      ss += v * v;
+    float4* dst = (float4*)(xs + bb * K);
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int k4 = tid + i * DUALAR_WG;
+      const float4 v = xr.v[bb][i];
+      if (k4 < K / 4) dst[k4] = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
     if (p.gain) {
       ss = wave_sum(ss);
@@ -52,25 +77,94 @@ __global__ void __launch_bounds__(DUALAR_WG) gemv_kernel(GemvParams p) {
     for (int bb = 0; bb < BT; ++bb) {
       const float tot = (red[bb][0] + red[bb][1]) + (red[bb][2] + red[bb][3]);
       const float inv = 1.0f / sqrtf(tot / (float)K + p.eps);
-      for (int k = tid; k < K; k += DUALAR_WG)
-        xs[bb * K + k] = xs[bb * K + k] * inv * ElemT<T>::load(p.gain, k);
+      for (int k = tid; k < K; k += DUALAR_WG) xs[bb * K + k] = xs[bb * K + k] * inv * ElemT<T>::load(p.gain, k);
     }
     __syncthreads();
   }
+}
 
-  // ---- rows ----
-  const int row0 = (blockIdx.x * 4 + wave) * RPW;
-  if (row0 >= p.n_out) return;
-  const int n_units = K / (64 * EPV);
-  const char* wp[RPW][NR];
-  bool live[RPW];
+// Generic staging for arbitrary K (loop kernel).
+template <typename T, int BT>
+__device__ __forceinline__ void stage_x(const GemvParams& p, float* xs, float (*red)[4], int b0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = p.K;
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) {
+    const int b = b0 + bb;
+    float ss = 0.f;
+    const float4* src = (const float4*)(p.x + (size_t)b * p.ldx);
+    float4* dst = (float4*)(xs + bb * K);
+    for (int k4 = tid; k4 < K / 4; k4 += DUALAR_WG) {
+      const float4 v = (b < p.B) ? src[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      dst[k4] = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    if (p.gain) {
+      ss = wave_sum(ss);
+      if (lane == 0) red[bb][wave] = ss;
+    }
+  }
+  __syncthreads();
+  if (p.gain) {
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb) {
+      const float tot = (red[bb][0] + red[bb][1]) + (red[bb][2] + red[bb][3]);
+      const float inv = 1.0f / sqrtf(tot / (float)K + p.eps);
+      for (int k = tid; k < K; k += DUALAR_WG) xs[bb * K + k] = xs[bb * K + k] * inv * ElemT<T>::load(p.gain, k);
+    }
+    __syncthreads();
+  }
+}
+
+template <int RPW, int NR, int BT>
+__device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (&acc)[RPW][NR][BT], int row0, int b0) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    live[r] = (row0 + r) < p.n_out;
-    const int row = live[r] ? row0 + r : row0;
 #pragma unroll
-    for (int s = 0; s < NR; ++s) wp[r][s] = seg_row<T>(p, row, s) + (size_t)lane * EPV * sizeof(T);
+    for (int bb = 0; bb < BT; ++bb) {
+      const float v0 = wave_sum(acc[r][0][bb]);
+      const float v1 = (NR == 2) ? wave_sum(acc[r][NR - 1][bb]) : 0.f;
+      const int b = b0 + bb, row = row0 + r;
+      if (lane == 0 && row < p.n_out && b < p.B) {
+        float out;
+        if (p.mode == GEMV_SWIGLU) out = silu_f(v0) * v1;
+        else if (p.mode == GEMV_ADD) out = p.res[(size_t)b * p.ldres + row] + v0;
+        else out = v0;
+        p.y[(size_t)b * p.ldy + row] = out;
+      }
+    }
   }
+}
+
+template <typename T, int BT, int RPW, int NR, int NU>
+__global__ void __launch_bounds__(DUALAR_WG) gemv_unrolled_kernel(GemvParams p) {
+  extern __shared__ float xs[];  // [BT][K]
+  __shared__ float red[BT][4];
+  constexpr int EPV = ElemT<T>::EPV;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b0 = blockIdx.y * BT;
+  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+
+  // 1. this thread's share of the activation rows, then all weight loads
+  constexpr int XR = (NU * 64 * EPV / 4 + DUALAR_WG - 1) / DUALAR_WG;
+  XRegs<BT, XR> xr;
+  load_x<BT, XR>(p, xr, b0);
+  u32x4 w[NU][RPW][NR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = min(row0 + r, p.n_out - 1);
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      const char* base = seg_row<T>(p, row, s) + (size_t)lane * EPV * sizeof(T);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) w[u][r][s] = ld_stream(base + (size_t)u * 64 * EPV * sizeof(T));
+    }
+  }
+  // 2. activations to LDS (+ RMSNorm) while the weights are in flight
+  store_x<T, BT, XR>(p, xr, xs, red);
+
+  // 3. dot products
   float acc[RPW][NR][BT];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
@@ -78,13 +172,254 @@ __global__ void __launch_bounds__(DUALAR_WG) gemv_kernel(GemvParams p) {
     for (int s = 0; s < NR; ++s)
 #pragma unroll
       for (int bb = 0; bb < BT; ++bb) acc[r][s][bb] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int kb = u * 64 * EPV + lane * EPV;
+    float xv[BT][EPV];
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb)
+#pragma unroll
+      for (int e = 0; e < EPV; e += 4) {
+        const float4 t = *(const float4*)&xs[bb * p.K + kb + e];
+        xv[bb][e] = t.x; xv[bb][e + 1] = t.y; xv[bb][e + 2] = t.z; xv[bb][e + 3] = t.w;
+      }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        float wf[EPV];
+        ElemT<T>::unpack(w[u][r][s], wf);
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb)
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[r][s][bb] = fmaf(wf[e], xv[bb][e], acc[r][s][bb]);
+      }
+  }
+  gemv_epilogue<RPW, NR, BT>(p, acc, row0, b0);
+}
 
+// One activation row, rows of NU units: every lane loads the activation
+// slice it multiplies (NU * EPV floats, the same k indices for every row it
+// owns) before issuing its weight loads, so waiting for the activations never
+// waits behind the weights (loads complete in order).  The 64 lanes of a wave
+// hold all of x between them, so the RMSNorm prologue is a wave reduction: no
+// LDS, no barrier.
+template <typename T, int RPW, int NR, int NU>
+__global__ void __launch_bounds__(DUALAR_WG) gemv_rx_kernel(GemvParams p) {
+  constexpr int EPV = ElemT<T>::EPV;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+
+  // 1. activation slice (+ gain slice)
+  float xv[NU][EPV];
+  const float* xb = p.x + lane * EPV;
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int e = 0; e < EPV; e += 4) {
+      const float4 t = *(const float4*)(xb + u * 64 * EPV + e);
+      xv[u][e] = t.x; xv[u][e + 1] = t.y; xv[u][e + 2] = t.z; xv[u][e + 3] = t.w;
+    }
+  u32x4 gv[NU];
+  if (p.gain) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) gv[u] = ld_vec((const char*)p.gain + (size_t)(u * 64 + lane) * EPV * sizeof(T));
+  }
+  // 2. weights
+  u32x4 w[NU][RPW][NR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = min(row0 + r, p.n_out - 1);
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      const char* base = seg_row<T>(p, row, s) + (size_t)lane * EPV * sizeof(T);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) w[u][r][s] = ld_stream(base + (size_t)u * 64 * EPV * sizeof(T));
+    }
+  }
+  // 3. RMSNorm * gain, in registers
+  if (p.gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) ss += xv[u][e] * xv[u][e];
+    const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)p.K + p.eps);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      float g[EPV];
+      ElemT<T>::unpack(gv[u], g);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) xv[u][e] = xv[u][e] * inv * g[e];
+    }
+  }
+  // 4. dot products
+  float acc[RPW][NR][1];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int s = 0; s < NR; ++s) acc[r][s][0] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        float wf[EPV];
+        ElemT<T>::unpack(w[u][r][s], wf);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[r][s][0] = fmaf(wf[e], xv[u][e], acc[r][s][0]);
+      }
+  gemv_epilogue<RPW, NR, 1>(p, acc, row0, 0);
+}
+
+// One activation row, rows of NU units split in KS parts: the 4 waves of a
+// workgroup are 4/KS row groups x KS k-parts.  Each wave loads its
+// activation (and gain) slice first (NUP units), then its weights; the KS
+// partial sums of squares (RMSNorm) and the KS partial dot products of a row
+// meet in LDS.
+template <typename T, int RPW, int NR, int NU, int KS>
+__global__ void __launch_bounds__(DUALAR_WG) gemv_ks_kernel(GemvParams p) {
+  constexpr int EPV = ElemT<T>::EPV;
+  constexpr int NUP = (NU + KS - 1) / KS;
+  __shared__ float part[4][RPW][NR];
+  __shared__ float ssq[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kp = wave % KS;
+  const int row0 = (blockIdx.x * (4 / KS) + wave / KS) * RPW;
+  const int u0 = kp * NUP;
+
+  float xv[NUP][EPV];
+  const float* xb = p.x + lane * EPV;
+#pragma unroll
+  for (int u = 0; u < NUP; ++u) {
+    const int uu = min(u0 + u, NU - 1);
+#pragma unroll
+    for (int e = 0; e < EPV; e += 4) {
+      const float4 t = *(const float4*)(xb + uu * 64 * EPV + e);
+      const bool live = u0 + u < NU;
+      xv[u][e] = live ? t.x : 0.f; xv[u][e + 1] = live ? t.y : 0.f;
+      xv[u][e + 2] = live ? t.z : 0.f; xv[u][e + 3] = live ? t.w : 0.f;
+    }
+  }
+  u32x4 gv[NUP];
+  if (p.gain) {
+#pragma unroll
+    for (int u = 0; u < NUP; ++u) {
+      const int uu = min(u0 + u, NU - 1);
+      gv[u] = ld_vec((const char*)p.gain + (size_t)(uu * 64 + lane) * EPV * sizeof(T));
+    }
+  }
+  u32x4 w[NUP][RPW][NR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = min(row0 + r, p.n_out - 1);
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      const char* base = seg_row<T>(p, row, s) + (size_t)lane * EPV * sizeof(T);
+#pragma unroll
+      for (int u = 0; u < NUP; ++u) {
+        const int uu = min(u0 + u, NU - 1);
+        w[u][r][s] = ld_stream(base + (size_t)uu * 64 * EPV * sizeof(T));
+      }
+    }
+  }
+  if (p.gain) {
+    // every row group holds the whole activation row across its KS waves
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < NUP; ++u)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) ss += xv[u][e] * xv[u][e];
+    ss = wave_sum(ss);
+    if (lane == 0) ssq[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    const int g0 = wave - kp;
+    for (int q = 0; q < KS; ++q) tot += ssq[g0 + q];
+    const float inv = 1.0f / sqrtf(tot / (float)p.K + p.eps);
+#pragma unroll
+    for (int u = 0; u < NUP; ++u) {
+      float g[EPV];
+      ElemT<T>::unpack(gv[u], g);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) xv[u][e] = xv[u][e] * inv * g[e];
+    }
+  }
+  float acc[RPW][NR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int s = 0; s < NR; ++s) acc[r][s] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NUP; ++u)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        float wf[EPV];
+        ElemT<T>::unpack(w[u][r][s], wf);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[r][s] = fmaf(wf[e], xv[u][e], acc[r][s]);
+      }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      const float v = wave_sum(acc[r][s]);
+      if (lane == 0) part[wave][r][s] = v;
+    }
+  __syncthreads();
+  if (kp != 0 || lane != 0) return;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = row0 + r;
+    if (row >= p.n_out) continue;
+    float v[NR];
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      v[s] = 0.f;
+      for (int q = 0; q < KS; ++q) v[s] += part[wave + q][r][s];
+    }
+    float out;
+    if (p.mode == GEMV_SWIGLU) out = silu_f(v[0]) * v[NR - 1];
+    else if (p.mode == GEMV_ADD) out = p.res[row] + v[0];
+    else out = v[0];
+    p.y[row] = out;
+  }
+}
+
+template <typename T, int BT, int RPW, int NR>
+__global__ void __launch_bounds__(DUALAR_WG) gemv_loop_kernel(GemvParams p) {
+  extern __shared__ float xs[];  // [BT][K]
+  __shared__ float red[BT][4];
+  constexpr int EPV = ElemT<T>::EPV;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b0 = blockIdx.y * BT;
+  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+  const int n_units = p.K / (64 * EPV);
+
+  const char* wp[RPW][NR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = min(row0 + r, p.n_out - 1);
+#pragma unroll
+    for (int s = 0; s < NR; ++s) wp[r][s] = seg_row<T>(p, row, s) + (size_t)lane * EPV * sizeof(T);
+  }
   u32x4 cur[RPW][NR];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
     for (int s = 0; s < NR; ++s) cur[r][s] = ld_stream(wp[r][s]);
+  stage_x<T, BT>(p, xs, red, b0);
 
+  float acc[RPW][NR][BT];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int s = 0; s < NR; ++s)
+#pragma unroll
+      for (int bb = 0; bb < BT; ++bb) acc[r][s][bb] = 0.f;
   for (int u = 0; u < n_units; ++u) {
     u32x4 nxt[RPW][NR];
     const bool more = (u + 1) < n_units;
@@ -93,14 +428,13 @@ __global__ void __launch_bounds__(DUALAR_WG) gemv_kernel(GemvParams p) {
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
       for (int s = 0; s < NR; ++s) nxt[r][s] = more ? ld_stream(wp[r][s] + off) : cur[r][s];
-
     const int kb = u * 64 * EPV + lane * EPV;
     float xv[BT][EPV];
 #pragma unroll
     for (int bb = 0; bb < BT; ++bb)
 #pragma unroll
       for (int e = 0; e < EPV; e += 4) {
-        const float4 t = *(const float4*)&xs[bb * K + kb + e];
+        const float4 t = *(const float4*)&xs[bb * p.K + kb + e];
         xv[bb][e] = t.x; xv[bb][e + 1] = t.y; xv[bb][e + 2] = t.z; xv[bb][e + 3] = t.w;
       }
 #pragma unroll
@@ -119,48 +453,84 @@ __global__ void __launch_bounds__(DUALAR_WG) gemv_kernel(GemvParams p) {
 #pragma unroll
       for (int s = 0; s < NR; ++s) cur[r][s] = nxt[r][s];
   }
-
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-#pragma unroll
-    for (int bb = 0; bb < BT; ++bb) {
-      float v0 = wave_sum(acc[r][0][bb]);
-      float v1 = (NR == 2) ? wave_sum(acc[r][NR - 1][bb]) : 0.f;
-      const int b = b0 + bb;
-      if (lane == 0 && live[r] && b < p.B) {
-        const int row = row0 + r;
-        float out;
-        if (p.mode == GEMV_SWIGLU) out = silu_f(v0) * v1;
-        else if (p.mode == GEMV_ADD) out = p.res[(size_t)b * p.ldres + row] + v0;
-        else out = v0;
-        p.y[(size_t)b * p.ldy + row] = out;
-      }
-    }
-  }
+  gemv_epilogue<RPW, NR, BT>(p, acc, row0, b0);
 }
 
-template <typename T, int BT, int RPW, int NR>
+// ---------------------------------------------------------------------------
+// launch selection
+// ---------------------------------------------------------------------------
+template <typename T, int BT, int RPW, int NR, int NU>
 static hipError_t go(const GemvParams& p, hipStream_t s) {
   dim3 grid((p.n_out + 4 * RPW - 1) / (4 * RPW), (p.B + BT - 1) / BT);
-  size_t lds = (size_t)BT * p.K * sizeof(float);
-  hipLaunchKernelGGL((gemv_kernel<T, BT, RPW, NR>), grid, dim3(DUALAR_WG), lds, s, p);
+  const size_t lds = (size_t)BT * p.K * sizeof(float);
+  if (NU > 0 && NU <= 8 && BT == 1 && p.B == 1)   // the register-staged kernels take one row
+    hipLaunchKernelGGL((gemv_rx_kernel<T, RPW, NR, (NU > 0 ? NU : 1)>), grid, dim3(DUALAR_WG), 0, s, p);
+  else if constexpr (NU > 0)
+    hipLaunchKernelGGL((gemv_unrolled_kernel<T, BT, RPW, NR, NU>), grid, dim3(DUALAR_WG), lds, s, p);
+  else
+    hipLaunchKernelGGL((gemv_loop_kernel<T, BT, RPW, NR>), grid, dim3(DUALAR_WG), lds, s, p);
   return hipGetLastError();
 }
 
-template <typename T, int BT, int NR>
+// Rows per wave: enough workgroups (>= 512 when the matrix allows) and at
+// most 20 weight loads per lane in flight.
+template <typename T, int BT, int NR, int NU>
 static hipError_t pick_rpw(const GemvParams& p, hipStream_t s) {
-  // Enough workgroups to cover 256 CUs several times over.
-  if (p.n_out >= 8192 * 4 / NR) return go<T, BT, 4, NR>(p, s);
-  if (p.n_out >= 4096) return go<T, BT, 2, NR>(p, s);
-  return go<T, BT, 1, NR>(p, s);
+  constexpr int nu = NU > 0 ? NU : 2;
+  auto wgs = [&](int rpw) { return (p.n_out + 4 * rpw - 1) / (4 * rpw); };
+  if (nu * 4 * NR <= 20 && wgs(4) >= 512) return go<T, BT, 4, NR, NU>(p, s);
+  if (nu * 2 * NR <= 20 && wgs(2) >= 512) return go<T, BT, 2, NR, NU>(p, s);
+  return go<T, BT, 1, NR, NU>(p, s);
+}
+
+template <typename T, int RPW, int NR, int NU, int KS>
+static hipError_t go_ks(const GemvParams& p, hipStream_t s) {
+  dim3 grid((p.n_out + (4 / KS) * RPW - 1) / ((4 / KS) * RPW));
+  hipLaunchKernelGGL((gemv_ks_kernel<T, RPW, NR, NU, KS>), grid, dim3(DUALAR_WG), 0, s, p);
+  return hipGetLastError();
+}
+
+// One activation row of bf16 rows of 2560 / 4096 / 9728: the variants that
+// measured fastest for each S2 matrix (rows per wave, k-split).
+template <typename T, int NR>
+static hipError_t pick_b1(const GemvParams& p, hipStream_t s, bool* done) {
+  *done = true;
+  const int units = p.K / (64 * ElemT<T>::EPV);
+  if constexpr (sizeof(T) == 2) {
+    if (units == 5) {
+      if (NR == 2) return go<T, 1, 2, NR, 5>(p, s);                    // W1|W3
+      if (p.n_out >= 65536) return go<T, 1, 4, NR, 5>(p, s);           // tied head
+      return go<T, 1, 2, NR, 5>(p, s);                                 // QKV, fast head
+    }
+    if (NR == 1 && units == 8) return go_ks<T, 2, 1, 8, 4>(p, s);      // O
+    if (NR == 1 && units == 19) return go_ks<T, 2, 1, 19, 4>(p, s);    // W2
+  }
+  *done = false;
+  return hipSuccess;
+}
+
+template <typename T, int BT, int NR>
+static hipError_t pick_nu(const GemvParams& p, hipStream_t s) {
+  if (BT == 1 && p.B == 1) {
+    bool done;
+    hipError_t e = pick_b1<T, NR>(p, s, &done);
+    if (done) return e;
+  }
+  const int units = p.K / (64 * ElemT<T>::EPV);
+  if constexpr (sizeof(T) == 2) {
+    if (units == 5) return pick_rpw<T, BT, NR, 5>(p, s);     // 2560
+    if (units == 8) return pick_rpw<T, BT, NR, 8>(p, s);     // 4096
+    if (NR == 1 && units == 19) return pick_rpw<T, BT, NR, 19>(p, s);   // 9728
+  }
+  return pick_rpw<T, BT, NR, 0>(p, s);
 }
 
 template <typename T, int NR>
 static hipError_t pick_bt(const GemvParams& p, hipStream_t s) {
   const size_t lim = 48 * 1024;   // dynamic LDS for the staged activations
-  if (p.B >= 3 && 4 * (size_t)p.K * 4 <= lim) return pick_rpw<T, 4, NR>(p, s);
-  if (p.B >= 2 && 2 * (size_t)p.K * 4 <= lim) return pick_rpw<T, 2, NR>(p, s);
-  return pick_rpw<T, 1, NR>(p, s);
+  if (p.B >= 3 && 4 * (size_t)p.K * 4 <= lim) return pick_nu<T, 4, NR>(p, s);
+  if (p.B >= 2 && 2 * (size_t)p.K * 4 <= lim) return pick_nu<T, 2, NR>(p, s);
+  return pick_nu<T, 1, NR>(p, s);
 }
 
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s) {

@@ -35,7 +35,9 @@ struct AttnParams {
   const float2* rope;                 // [max_pos][hd/2] (cos, sin), bf16 values
   const void* q_norm; const void* k_norm; float eps;
   int H, KV, hd;
-  int chunk, max_splits;
+  int it;                             // K/V loads per lane (2, 4 or 8): sets the chunk
+  int lmax;                           // max over rows of pos + 1
+  int chunk, max_splits;              // set by the launcher
   float* part;                        // [B][H][max_splits][hd + 2]
   unsigned* counters;                 // [B][KV], zero between launches
   float* out; int ld_out;             // [B][H*hd]

@@ -25,51 +25,48 @@
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(DUALAR_WG) embed_kernel(EmbedParams p) {
+  // grid (B, ceil(dim / 256)): one element of one row per thread
   const int b = blockIdx.x;
-  __shared__ int col[64];
-  __shared__ int active;
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    int act = 1;
-    if (p.prefill) {
-      const int t = p.step - (p.t_max - p.st.plen[b]);
-      act = t >= 0;
-      p.st.pos[b] = act ? t : -1;
-      if (act)
-        for (int r = 0; r <= p.N; ++r) col[r] = p.tokens[((size_t)b * (p.N + 1) + r) * p.t_max + t];
-    } else {
-      act = !p.st.done[b];
-      if (act)
-        for (int r = 0; r <= p.N; ++r) col[r] = p.st.cur[b * (p.N + 1) + r];
-    }
-    if (act) {
-      int bad = 0;
-      if (col[0] < 0 || col[0] >= p.V) { bad = 1; col[0] = 0; }
-      if (col[0] >= p.sb && col[0] <= p.se) {
-        for (int k = 0; k < p.N; ++k)
-          if (col[1 + k] < 0 || col[1 + k] >= p.C) { bad = 1; col[1 + k] = 0; }
-      }
-      if (bad) atomicOr(p.st.status, ST_BAD_TOKEN);
-    }
-    active = act;
+  int col[33];
+  int act = 1;
+  if (p.prefill) {
+    const int t = p.step - (p.t_max - p.st.plen[b]);
+    act = t >= 0;
+    if (blockIdx.y == 0 && tid == 0) p.st.pos[b] = act ? t : -1;
+    if (act)
+      for (int r = 0; r <= p.N; ++r) col[r] = p.tokens[((size_t)b * (p.N + 1) + r) * p.t_max + t];
+  } else {
+    act = !p.st.done[b];
+    if (act)
+      for (int r = 0; r <= p.N; ++r) col[r] = p.st.cur[b * (p.N + 1) + r];
   }
-  __syncthreads();
+  const int d = blockIdx.y * DUALAR_WG + tid;
   float* x = p.x + (size_t)b * p.dim;
-  if (!active) {
-    for (int d = tid; d < p.dim; d += DUALAR_WG) x[d] = 0.f;
+  if (!act) {
+    if (d < p.dim) x[d] = 0.f;
     return;
   }
-  const int id = col[0];
-  const bool sem = id >= p.sb && id <= p.se;
-  const float denom = sqrtf((float)(p.N + 1));
-  for (int d = tid; d < p.dim; d += DUALAR_WG) {
-    float s = ElemT<T>::load(p.tok_emb, (size_t)id * p.dim + d);
-    if (sem) {
-      for (int k = 0; k < p.N; ++k) s += ElemT<T>::load(p.cb_emb, ((size_t)k * p.C + col[1 + k]) * p.dim + d);
-      if (p.scale) s = s / denom;
-    }
-    x[d] = s;
-  }
+  int bad = 0;
+  if (col[0] < 0 || col[0] >= p.V) { bad = 1; col[0] = 0; }
+  const bool sem = col[0] >= p.sb && col[0] <= p.se;
+  if (sem)
+    for (int k = 0; k < p.N; ++k)
+      if (col[1 + k] < 0 || col[1 + k] >= p.C) { bad = 1; col[1 + k] = 0; }
+  if (bad && blockIdx.y == 0 && tid == 0) atomicOr(p.st.status, ST_BAD_TOKEN);
+  if (d >= p.dim) return;
+  const float e0 = ElemT<T>::load(p.tok_emb, (size_t)col[0] * p.dim + d);
+  if (!sem) { x[d] = e0; return; }
+  float v[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    if (k < p.N) v[k] = ElemT<T>::load(p.cb_emb, ((size_t)k * p.C + col[1 + k]) * p.dim + d);
+  float s = e0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    if (k < p.N) s += v[k];
+  if (p.scale) s = s / sqrtf((float)(p.N + 1));
+  x[d] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -82,15 +79,31 @@ __device__ __forceinline__ Best better(Best a, Best b) {
   return a;
 }
 
+#define DPP_I(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), ctrl, 0xF, 0xF, true)
+__device__ __forceinline__ Best best_dpp(Best x, int ctrl_sel) {
+  Best y;
+  switch (ctrl_sel) {
+    case 0: y.v = xor1_of(x.v); y.i = DPP_I(x.i, 0xB1); break;
+    case 1: y.v = xor2_of(x.v); y.i = DPP_I(x.i, 0x4E); break;
+    case 2: y.v = mir8_of(x.v); y.i = DPP_I(x.i, 0x141); break;
+    default: y.v = mir16_of(x.v); y.i = DPP_I(x.i, 0x140); break;
+  }
+  return better(x, y);
+}
+__device__ __forceinline__ Best best_swap(Best x, bool wide) {
+  const auto rv = wide ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x.v), __float_as_uint(x.v), false, false)
+                       : __builtin_amdgcn_permlane16_swap(__float_as_uint(x.v), __float_as_uint(x.v), false, false);
+  const auto ri = wide ? __builtin_amdgcn_permlane32_swap((unsigned)x.i, (unsigned)x.i, false, false)
+                       : __builtin_amdgcn_permlane16_swap((unsigned)x.i, (unsigned)x.i, false, false);
+  return better(Best{__uint_as_float(rv[0]), (int)ri[0]}, Best{__uint_as_float(rv[1]), (int)ri[1]});
+}
+
 __device__ __forceinline__ Best block_best(Best x, Best* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    Best y;
-    y.v = __shfl_xor(x.v, o);
-    y.i = __shfl_xor(x.i, o);
-    x = better(x, y);
-  }
+  for (int c = 0; c < 4; ++c) x = best_dpp(x, c);
+  x = best_swap(x, false);
+  x = best_swap(x, true);
   if (lane == 0) sh[wave] = x;
   __syncthreads();
   Best r = sh[0];
@@ -101,8 +114,7 @@ __device__ __forceinline__ Best block_best(Best x, Best* sh) {
 
 __device__ __forceinline__ int block_count(int c, int* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  c = (int)wave_sum((float)c);   // counts <= 8192 are exact in fp32
   if (lane == 0) sh[wave] = c;
   __syncthreads();
   int r = 0;
@@ -310,7 +322,7 @@ __global__ void prefill_begin_kernel(SeqState st, PlenArg plen, int B, int N) {
 }
 
 template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel<T>, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
+  hipLaunchKernelGGL(embed_kernel<T>, dim3(p.B, (p.dim + DUALAR_WG - 1) / DUALAR_WG), dim3(DUALAR_WG), 0, s, p);
   return hipGetLastError();
 }
 template <typename T> hipError_t launch_sample(const SampleParams& p, hipStream_t s) {
