@@ -102,6 +102,10 @@ def main():
     ap.add_argument("--profile-frames", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--prompt-len", type=int, default=None,
+                    help="override the prompt length (same three-segment layout); for counter runs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 10 times (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -111,9 +115,19 @@ def main():
 
     import torch
 
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "copies": 10}))
+        return
+
     import synth
     from dual_autoregressive_tts_amd import DualAR, reporting
-    from dual_autoregressive_tts_amd.binding import K_ATTN, K_GEMV, upload_weights
+    from dual_autoregressive_tts_amd.binding import K_ATTN, K_GEMV, K_GEMV_SWIGLU, upload_weights
 
     wl_name, b_over, desc = WORKLOADS[args.workload]
     wl = synth.WORKLOADS[wl_name]
@@ -150,7 +164,12 @@ def main():
         ttff_ms = None
     else:
         plen = synth.prompt_lengths(wl, seed=args.seed)
-        prompts = synth.make_prompts(m, wl["prompt"], plen, seed=args.seed)
+        layout = wl["prompt"]
+        if args.prompt_len:
+            P = args.prompt_len
+            plen = np.full(B, P, dtype=np.int32)
+            layout = ("fixed", P // 8, P // 2, P - P // 8 - P // 2)
+        prompts = synth.make_prompts(m, layout, plen, seed=args.seed)
         ctx = DualAR(m, dev_w, max_batch=B, max_seq_len=int(plen.max()) + P_frames + 2)
         U = None
         if not samp["greedy"]:
@@ -192,22 +211,34 @@ def main():
             step_bytes += reporting.frame_bytes(m, L)["total"]
     step_gbps = step_bytes / (ms / 1e3) / 1e9
 
-    # ---- live per-launch timing of the dominant kernel (GEMV) ----
+    # ---- live per-launch timing (HIP events on the context's stream) ----
     Pf = args.profile_frames
+    a0 = W + K
     ctx.profile_begin(K_GEMV)
-    run(W + K, W + K + Pf)
+    run(a0, a0 + Pf // 2)
     g = ctx.profile_end()
+    ctx.profile_begin(K_GEMV_SWIGLU)
+    run(a0 + Pf // 2, a0 + Pf)
+    f = ctx.profile_end()
     gemv_avg_us = g["total_ms"] * 1e3 / g["launches"]
-    gemv_bytes = g["bytes"] / g["launches"]
-    gemv_gbps = gemv_bytes / (gemv_avg_us * 1e-6) / 1e9
-    gemv_share = g["total_ms"] / (Pf * ms_per_step)
-    log(f"[bench] GEMV: {g['launches']} launches, avg {gemv_avg_us:.2f} us, {gemv_bytes / 1e6:.2f} MB/launch, "
-        f"{gemv_gbps:.0f} GB/s, {100 * gemv_share:.1f}% of step time")
-    roofline = {"bound": "hbm", "kernel": "gemv_kernel (all weight-streaming matrix-vector launches)",
-                "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                "avg_launch_us": round(gemv_avg_us, 3), "bytes_per_launch": round(gemv_bytes),
-                "launches_profiled": g["launches"], "share_of_step_time": round(gemv_share, 4)}
+    gemv_gbps = g["bytes"] / (g["total_ms"] * 1e-3) / 1e9
+    gemv_share = g["total_ms"] / ((Pf // 2) * ms_per_step)
+    sw_avg_us = f["total_ms"] * 1e3 / f["launches"]
+    sw_bytes = f["bytes"] / f["launches"]
+    sw_gbps = sw_bytes / (sw_avg_us * 1e-6) / 1e9
+    log(f"[bench] GEMV family: {g['launches']} launches, avg {gemv_avg_us:.2f} us, {gemv_gbps:.0f} GB/s, "
+        f"{100 * gemv_share:.1f}% of step time")
+    log(f"[bench] SwiGLU gate|up GEMV: {f['launches']} launches, avg {sw_avg_us:.2f} us, "
+        f"{sw_bytes / 1e6:.2f} MB/launch, {sw_gbps:.0f} GB/s")
+    roofline = {"bound": "hbm",
+                "kernel": "gemv_rx_kernel<bf16, 2 rows/wave, gate+up, 5 units> (SwiGLU W1|W3 GEMV, "
+                          "2 x 9728 x 2560 bf16)" if not m["weight_dtype"] == "f32" else "SwiGLU W1|W3 GEMV",
+                "achieved": round(sw_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(sw_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "avg_launch_us": round(sw_avg_us, 3), "bytes_per_launch": round(sw_bytes),
+                "launches_profiled": f["launches"],
+                "gemv_family": {"achieved_GBps": round(gemv_gbps, 1), "avg_launch_us": round(gemv_avg_us, 3),
+                                "launches": g["launches"], "share_of_step_time": round(gemv_share, 4)}}
     extra = {}
     if not fast_only:
         ctx.profile_begin(K_ATTN)

@@ -66,7 +66,7 @@ class Taps(C.Structure):
 EXPORTS = ("dualar_workspace_bytes", "dualar_create", "dualar_prefill", "dualar_decode_frames",
            "dualar_fast_frames", "dualar_sync", "dualar_profile_begin", "dualar_profile_end",
            "dualar_destroy", "dualar_status_string", "dualar_last_error")
-K_GEMV, K_ATTN, K_SAMPLE, K_EMBED = 0, 1, 2, 3
+K_GEMV, K_ATTN, K_SAMPLE, K_EMBED, K_GEMV_SWIGLU = 0, 1, 2, 3, 4
 
 _lib = None
 

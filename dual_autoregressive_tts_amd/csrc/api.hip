@@ -183,8 +183,13 @@ dualar_status fail(dualar_ctx* c, dualar_status s, const std::string& m) {
 }
 
 // Bracket one launch of kernel class `cls` with events when it is profiled.
-hipError_t prof_pre(dualar_ctx* c, int cls) {
-  if (c->prof_cls != cls) return hipSuccess;
+// A launch of class `cls` is profiled when that class is selected; the
+// SwiGLU GEMVs are also profiled under DUALAR_K_GEMV_SWIGLU.
+bool prof_on(dualar_ctx* c, int cls, bool swiglu = false) {
+  return c->prof_cls == cls || (swiglu && c->prof_cls == DUALAR_K_GEMV_SWIGLU);
+}
+hipError_t prof_pre(dualar_ctx* c, int cls, bool swiglu = false) {
+  if (!prof_on(c, cls, swiglu)) return hipSuccess;
   while (c->ev.size() < c->ev_used + 2) {
     hipEvent_t e;
     hipError_t er = hipEventCreate(&e);
@@ -193,8 +198,8 @@ hipError_t prof_pre(dualar_ctx* c, int cls) {
   }
   return hipEventRecord(c->ev[c->ev_used], c->stream);
 }
-hipError_t prof_post(dualar_ctx* c, int cls, double bytes) {
-  if (c->prof_cls != cls) return hipSuccess;
+hipError_t prof_post(dualar_ctx* c, int cls, double bytes, bool swiglu = false) {
+  if (!prof_on(c, cls, swiglu)) return hipSuccess;
   hipError_t er = hipEventRecord(c->ev[c->ev_used + 1], c->stream);
   c->ev_used += 2;
   c->prof_launches += 1;
@@ -204,13 +209,14 @@ hipError_t prof_post(dualar_ctx* c, int cls, double bytes) {
 
 template <typename T>
 hipError_t gemv(dualar_ctx* c, const GemvParams& g) {
-  hipError_t e = prof_pre(c, DUALAR_K_GEMV);
+  const bool sw = g.mode == GEMV_SWIGLU;
+  hipError_t e = prof_pre(c, DUALAR_K_GEMV, sw);
   if (e != hipSuccess) return e;
   e = launch_gemv<T>(g, c->stream);
   if (e != hipSuccess) return e;
-  const double wbytes = (double)g.n_out * (g.mode == GEMV_SWIGLU ? 2 : 1) * g.K * c->r.esz;
+  const double wbytes = (double)g.n_out * (sw ? 2 : 1) * g.K * c->r.esz;
   const double act = 4.0 * g.B * ((double)g.K + g.n_out * (g.mode == GEMV_ADD ? 2 : 1));
-  return prof_post(c, DUALAR_K_GEMV, wbytes + act);
+  return prof_post(c, DUALAR_K_GEMV, wbytes + act, sw);
 }
 
 #define HIPCHK(expr)                                                                   \
@@ -640,7 +646,7 @@ dualar_status dualar_sync(dualar_ctx_t* c, int32_t* device_status) {
 
 dualar_status dualar_profile_begin(dualar_ctx_t* c, int32_t kernel_class) {
   if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
-  if (kernel_class < DUALAR_K_GEMV || kernel_class > DUALAR_K_EMBED)
+  if (kernel_class < DUALAR_K_GEMV || kernel_class > DUALAR_K_GEMV_SWIGLU)
     return fail(c, DUALAR_ERR_INVALID_ARG, "unknown kernel class");
   c->prof_cls = kernel_class;
   c->ev_used = 0;

@@ -459,28 +459,20 @@ __global__ void __launch_bounds__(DUALAR_WG) gemv_loop_kernel(GemvParams p) {
 // ---------------------------------------------------------------------------
 // launch selection
 // ---------------------------------------------------------------------------
+// NU > 0 and BT == 1: register-staged kernel (one activation row, the
+// caller guarantees B == 1); NU > 0 and BT > 1: LDS-staged unrolled kernel;
+// NU == 0: loop kernel for any row length.
 template <typename T, int BT, int RPW, int NR, int NU>
 static hipError_t go(const GemvParams& p, hipStream_t s) {
   dim3 grid((p.n_out + 4 * RPW - 1) / (4 * RPW), (p.B + BT - 1) / BT);
   const size_t lds = (size_t)BT * p.K * sizeof(float);
-  if (NU > 0 && NU <= 8 && BT == 1 && p.B == 1)   // the register-staged kernels take one row
-    hipLaunchKernelGGL((gemv_rx_kernel<T, RPW, NR, (NU > 0 ? NU : 1)>), grid, dim3(DUALAR_WG), 0, s, p);
+  if constexpr (NU > 0 && BT == 1)
+    hipLaunchKernelGGL((gemv_rx_kernel<T, RPW, NR, NU>), grid, dim3(DUALAR_WG), 0, s, p);
   else if constexpr (NU > 0)
     hipLaunchKernelGGL((gemv_unrolled_kernel<T, BT, RPW, NR, NU>), grid, dim3(DUALAR_WG), lds, s, p);
   else
     hipLaunchKernelGGL((gemv_loop_kernel<T, BT, RPW, NR>), grid, dim3(DUALAR_WG), lds, s, p);
   return hipGetLastError();
-}
-
-// Rows per wave: enough workgroups (>= 512 when the matrix allows) and at
-// most 20 weight loads per lane in flight.
-template <typename T, int BT, int NR, int NU>
-static hipError_t pick_rpw(const GemvParams& p, hipStream_t s) {
-  constexpr int nu = NU > 0 ? NU : 2;
-  auto wgs = [&](int rpw) { return (p.n_out + 4 * rpw - 1) / (4 * rpw); };
-  if (nu * 4 * NR <= 20 && wgs(4) >= 512) return go<T, BT, 4, NR, NU>(p, s);
-  if (nu * 2 * NR <= 20 && wgs(2) >= 512) return go<T, BT, 2, NR, NU>(p, s);
-  return go<T, BT, 1, NR, NU>(p, s);
 }
 
 template <typename T, int RPW, int NR, int NU, int KS>
@@ -493,44 +485,45 @@ static hipError_t go_ks(const GemvParams& p, hipStream_t s) {
 // One activation row of bf16 rows of 2560 / 4096 / 9728: the variants that
 // measured fastest for each S2 matrix (rows per wave, k-split).
 template <typename T, int NR>
-static hipError_t pick_b1(const GemvParams& p, hipStream_t s, bool* done) {
-  *done = true;
-  const int units = p.K / (64 * ElemT<T>::EPV);
+static bool pick_b1(const GemvParams& p, hipStream_t s, hipError_t* e) {
   if constexpr (sizeof(T) == 2) {
+    const int units = p.K / (64 * ElemT<T>::EPV);
     if (units == 5) {
-      if (NR == 2) return go<T, 1, 2, NR, 5>(p, s);                    // W1|W3
-      if (p.n_out >= 65536) return go<T, 1, 4, NR, 5>(p, s);           // tied head
-      return go<T, 1, 2, NR, 5>(p, s);                                 // QKV, fast head
+      if (NR == 1 && p.n_out >= 65536) *e = go<T, 1, 4, NR, 5>(p, s);  // tied head
+      else *e = go<T, 1, 2, NR, 5>(p, s);                               // QKV, W1|W3, fast head
+      return true;
     }
-    if (NR == 1 && units == 8) return go_ks<T, 2, 1, 8, 4>(p, s);      // O
-    if (NR == 1 && units == 19) return go_ks<T, 2, 1, 19, 4>(p, s);    // W2
+    if constexpr (NR == 1) {
+      if (units == 8) { *e = go_ks<T, 2, 1, 8, 4>(p, s); return true; }   // O
+      if (units == 19) { *e = go_ks<T, 2, 1, 19, 4>(p, s); return true; } // W2
+    }
   }
-  *done = false;
-  return hipSuccess;
+  return false;
 }
 
+// Several activation rows (BT per workgroup, activations staged in LDS):
+// unrolled rows for the S2 row lengths 2560 / 4096, a loop otherwise.
 template <typename T, int BT, int NR>
-static hipError_t pick_nu(const GemvParams& p, hipStream_t s) {
-  if (BT == 1 && p.B == 1) {
-    bool done;
-    hipError_t e = pick_b1<T, NR>(p, s, &done);
-    if (done) return e;
-  }
-  const int units = p.K / (64 * ElemT<T>::EPV);
+static hipError_t pick_multi(const GemvParams& p, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (units == 5) return pick_rpw<T, BT, NR, 5>(p, s);     // 2560
-    if (units == 8) return pick_rpw<T, BT, NR, 8>(p, s);     // 4096
-    if (NR == 1 && units == 19) return pick_rpw<T, BT, NR, 19>(p, s);   // 9728
+    const int units = p.K / (64 * ElemT<T>::EPV);
+    if (units == 5) return go<T, BT, 2, NR, 5>(p, s);
+    if (units == 8 && NR == 1) return go<T, BT, 1, NR, 8>(p, s);
   }
-  return pick_rpw<T, BT, NR, 0>(p, s);
+  return go<T, BT, 1, NR, 0>(p, s);
 }
 
 template <typename T, int NR>
 static hipError_t pick_bt(const GemvParams& p, hipStream_t s) {
+  if (p.B == 1) {
+    hipError_t e;
+    if (pick_b1<T, NR>(p, s, &e)) return e;
+    return go<T, 1, 1, NR, 0>(p, s);
+  }
   const size_t lim = 48 * 1024;   // dynamic LDS for the staged activations
-  if (p.B >= 3 && 4 * (size_t)p.K * 4 <= lim) return pick_nu<T, 4, NR>(p, s);
-  if (p.B >= 2 && 2 * (size_t)p.K * 4 <= lim) return pick_nu<T, 2, NR>(p, s);
-  return pick_nu<T, 1, NR>(p, s);
+  if (p.B >= 3 && 4 * (size_t)p.K * 4 <= lim) return pick_multi<T, 4, NR>(p, s);
+  if (2 * (size_t)p.K * 4 <= lim) return pick_multi<T, 2, NR>(p, s);
+  return go<T, 1, 1, NR, 0>(p, s);
 }
 
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s) {

@@ -195,9 +195,11 @@ dualar_status dualar_sync(dualar_ctx_t *ctx, int32_t *device_status);
  * launches, their summed event-to-event time (ms) and their summed
  * algorithmic HBM bytes (weights + activations read and written, caches
  * read and appended).  Classes: 0 matrix-vector (GEMV), 1 attention,
- * 2 sampler, 3 fusion.  Profiling adds a few microseconds per launch; do not
- * time throughput with it on. */
-typedef enum { DUALAR_K_GEMV = 0, DUALAR_K_ATTN = 1, DUALAR_K_SAMPLE = 2, DUALAR_K_EMBED = 3 } dualar_kernel_class;
+ * 2 sampler, 3 fusion, 4 the SwiGLU gate|up GEMV alone (W1, W3).  Profiling
+ * adds a few microseconds per launch; do not time throughput with it on. */
+typedef enum {
+  DUALAR_K_GEMV = 0, DUALAR_K_ATTN = 1, DUALAR_K_SAMPLE = 2, DUALAR_K_EMBED = 3, DUALAR_K_GEMV_SWIGLU = 4
+} dualar_kernel_class;
 dualar_status dualar_profile_begin(dualar_ctx_t *ctx, int32_t kernel_class);
 dualar_status dualar_profile_end(dualar_ctx_t *ctx, int64_t *launches, double *total_ms, double *bytes);
 
