@@ -84,7 +84,7 @@ def load_library(path: str = LIB_PATH):
     lib.dualar_workspace_bytes.restype = C.c_size_t
     lib.dualar_create.argtypes = [P(Config), P(Weights), VP, C.c_size_t, VP, P(VP)]
     lib.dualar_create.restype = I32
-    lib.dualar_prefill.argtypes = [VP, I32, VP, I32, P(I32), P(Sampling), VP, VP]
+    lib.dualar_prefill.argtypes = [VP, I32, VP, I32, P(I32), P(Sampling), VP, VP, P(Taps)]
     lib.dualar_prefill.restype = I32
     lib.dualar_decode_frames.argtypes = [VP, I32, P(Sampling), VP, VP, VP, P(Taps)]
     lib.dualar_decode_frames.restype = I32
@@ -217,8 +217,20 @@ class DualAR:
             raise DualARError(-1, f"{what}: expected contiguous cuda {dtype} {tuple(shape)}, got "
                                   f"{t.dtype} {tuple(t.shape)} on {t.device}")
 
-    def prefill(self, tokens, prompt_len, sampling: Sampling, uniforms=None):
-        """tokens: cuda int32 [B][N+1][T]; prompt_len: host ints [B]."""
+    def _taps(self, B, with_fused=True):
+        torch, m, N = self.torch, self.m, self.N
+        td = {"slow_hidden": torch.empty((B, m["dim"]), device="cuda"),
+              "slow_logits": torch.empty((B, m["vocab_size"]), device="cuda"),
+              "fast_logits": torch.empty((B, N - 1, m["codebook_size"]), device="cuda")}
+        if with_fused:
+            td["fused_x"] = torch.empty((B, m["dim"]), device="cuda")
+        tp = Taps(*[td[k].data_ptr() if k in td else None
+                    for k in ("fused_x", "slow_hidden", "slow_logits", "fast_logits")])
+        return tp, td
+
+    def prefill(self, tokens, prompt_len, sampling: Sampling, uniforms=None, taps: bool = False):
+        """tokens: cuda int32 [B][N+1][T]; prompt_len: host ints [B].  Returns
+        frame 0 [B][N+1], or (frame 0, taps) when taps is set."""
         torch = self.torch
         B, _, T = tokens.shape
         self._need(tokens, (B, self.N + 1, T), torch.int32, "tokens")
@@ -227,10 +239,11 @@ class DualAR:
             raise DualARError(-1, "prompt_len must have one entry per sequence")
         plen = (C.c_int32 * B)(*[int(x) for x in prompt_len])
         frame0 = torch.empty((B, self.N + 1), dtype=torch.int32, device="cuda")
+        tp, td = self._taps(B, with_fused=False) if taps else (None, None)
         self._check(self.lib.dualar_prefill(self.h, B, _ptr(tokens), T, plen, C.byref(sampling),
-                                            _ptr(uniforms), _ptr(frame0)))
+                                            _ptr(uniforms), _ptr(frame0), C.byref(tp) if tp is not None else None))
         self.batch = B
-        return frame0
+        return (frame0, td) if taps else frame0
 
     def decode_frames(self, n: int, sampling: Sampling, uniforms=None, taps: bool = False, out=None):
         torch = self.torch
@@ -239,13 +252,7 @@ class DualAR:
         self._need(uniforms, (n, B, N), torch.float32, "uniforms")
         self._need(codes, (B, n, N + 1), torch.int32, "codes")
         emitted = torch.empty(B, dtype=torch.int32, device="cuda")
-        tp, td = None, None
-        if taps:
-            td = {"fused_x": torch.empty((B, m["dim"]), device="cuda"),
-                  "slow_hidden": torch.empty((B, m["dim"]), device="cuda"),
-                  "slow_logits": torch.empty((B, m["vocab_size"]), device="cuda"),
-                  "fast_logits": torch.empty((B, N - 1, m["codebook_size"]), device="cuda")}
-            tp = Taps(*[td[k].data_ptr() for k in ("fused_x", "slow_hidden", "slow_logits", "fast_logits")])
+        tp, td = self._taps(B) if taps else (None, None)
         self._check(self.lib.dualar_decode_frames(self.h, n, C.byref(sampling), _ptr(uniforms), _ptr(codes),
                                                   _ptr(emitted), C.byref(tp) if tp is not None else None))
         return codes, emitted, td

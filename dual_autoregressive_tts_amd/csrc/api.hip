@@ -39,6 +39,7 @@ struct Resolved {  // config with the inherit-on-unset fallback applied
 
 struct Layout {
   size_t kslow, vslow, kfast, vfast, rope_s, rope_f, x_slow, x_fast, qkv, att, ffn, logits, flog, part,
+      xn, gpart, gpart_elems,
       counters, st_pos, st_done, st_frames, st_cur, st_plen, st_fidx, st_status, total;
   size_t slow_layer_stride, fast_layer_stride;  // elements per layer of a cache
   int max_splits, qkv_ld, att_ld, ffn_ld;
@@ -126,6 +127,12 @@ Layout layout(const Resolved& r) {
   const int maxH = std::max(r.H, r.fH), maxhd = std::max(r.hd, r.fhd);
   L.part = take((size_t)r.max_batch * maxH * L.max_splits * (maxhd + 2) * 4);
   L.counters = take((size_t)r.max_batch * std::max(r.KV, r.fKV) * 4);
+  // matrix-core GEMM scratch: normalised activations and split-K partials
+  L.xn = take((size_t)r.max_batch * std::max(std::max(r.dim, r.ffn), std::max(r.fffn, L.att_ld)) * 4);
+  L.gpart_elems = r.max_batch >= 8 ? (size_t)8 * r.max_batch *
+                                         std::max(std::max(2 * r.ffn, 2 * r.fffn), std::max(L.qkv_ld, r.dim))
+                                   : 0;
+  L.gpart = take(L.gpart_elems * 4);
   L.st_pos = take(r.max_batch * 4);
   L.st_done = take(r.max_batch * 4);
   L.st_frames = take(r.max_batch * 4);
@@ -208,7 +215,11 @@ hipError_t prof_post(dualar_ctx* c, int cls, double bytes, bool swiglu = false) 
 }
 
 template <typename T>
-hipError_t gemv(dualar_ctx* c, const GemvParams& g) {
+hipError_t gemv(dualar_ctx* c, const GemvParams& g0) {
+  GemvParams g = g0;
+  g.xn = (float*)(c->ws + c->L.xn);
+  g.part = c->L.gpart_elems ? (float*)(c->ws + c->L.gpart) : nullptr;
+  g.part_elems = c->L.gpart_elems;
   const bool sw = g.mode == GEMV_SWIGLU;
   hipError_t e = prof_pre(c, DUALAR_K_GEMV, sw);
   if (e != hipSuccess) return e;
@@ -567,7 +578,7 @@ dualar_status dualar_create(const dualar_config* cfg, const dualar_weights* w, v
 
 dualar_status dualar_prefill(dualar_ctx_t* c, int32_t batch, const int32_t* tokens, int32_t t_max,
                              const int32_t* prompt_len, const dualar_sampling* s, const float* uniforms,
-                             int32_t* frame0) {
+                             int32_t* frame0, const dualar_taps* taps) {
   if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
   if (batch < 1 || batch > c->r.max_batch) return fail(c, DUALAR_ERR_INVALID_ARG, "batch out of range [1, max_batch]");
   if (!tokens || !prompt_len || !frame0) return fail(c, DUALAR_ERR_INVALID_ARG, "tokens/prompt_len/frame0 is NULL");
@@ -581,7 +592,7 @@ dualar_status dualar_prefill(dualar_ctx_t* c, int32_t batch, const int32_t* toke
   c->batch = batch;
   c->frames_done = 0;
   c->ready = false;
-  FrameIO io{s, uniforms, 0, c->r.N, frame0, c->r.N + 1, 0, nullptr, false};
+  FrameIO io{s, uniforms, 0, c->r.N, frame0, c->r.N + 1, 0, taps, false};
   dualar_status st = dispatch(c, [&](auto wt, auto kt) {
     return do_prefill<decltype(wt), decltype(kt)>(c, batch, tokens, t_max, io);
   });

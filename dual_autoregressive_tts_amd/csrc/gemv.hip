@@ -527,6 +527,10 @@ static hipError_t pick_bt(const GemvParams& p, hipStream_t s) {
 }
 
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    hipError_t e;
+    if (launch_gemm_mfma(p, s, &e)) return e;   // 8+ activation rows on the matrix cores
+  }
   if (p.mode == GEMV_SWIGLU) return pick_bt<T, 2>(p, s);
   return pick_bt<T, 1>(p, s);
 }

@@ -21,6 +21,11 @@ struct GemvParams {
   const float* res; int ldres;   // GEMV_ADD: y = res + W.x (res may alias y)
   int B;
   int mode;
+  // scratch for the matrix-core path (B >= 8): normalised activations
+  // [B][K] and split-K partial sums (part_elems floats)
+  float* xn;
+  float* part; size_t part_elems;
+  int ksw, ldp;                  // set by the launcher
 };
 
 // Decode attention for one new position per sequence, split along the
@@ -92,6 +97,7 @@ struct FastBeginParams {
 };
 
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
+bool launch_gemm_mfma(const GemvParams& p, hipStream_t s, hipError_t* err);
 template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 template <typename T> hipError_t launch_sample(const SampleParams& p, hipStream_t s);
 template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s);

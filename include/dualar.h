@@ -151,12 +151,14 @@ dualar_status dualar_create(const dualar_config *cfg, const dualar_weights *w,
  *   uniforms   device fp32 [batch][N] for top-p, or NULL when greedy.
  *   frame0     device int32 [batch][N+1]: (id, q^(0..N-1)); a sequence whose
  *              first sample is <|im_end|> gets (end_id, -1, ..., -1).
+ *   taps       NULL, or buffers for frame 0's slow hidden state, slow logits
+ *              and fast logits (fused_x is not written by prefill).
  * Resets every sequence of the context.  Requires batch <= max_batch and
  * prompt_len[b] < max_seq_len. */
 dualar_status dualar_prefill(dualar_ctx_t *ctx, int32_t batch, const int32_t *tokens,
                              int32_t t_max, const int32_t *prompt_len,
                              const dualar_sampling *s, const float *uniforms,
-                             int32_t *frame0);
+                             int32_t *frame0, const dualar_taps *taps);
 
 /* Decode n_frames frames for every sequence of the last prefill.
  *   uniforms  device fp32 [n_frames][batch][N] (slot 0: slow draw, slot k:

@@ -31,7 +31,11 @@ def rel_l2(a, b):
 
 def decision_margin(z, greedy, temperature=1.0, top_p=1.0, u=None):
     """How far the oracle's sampling decision on logits z (-inf = masked) is
-    from flipping."""
+    from flipping.  Greedy: the top-1 logit gap.  Top-p: the smallest of the
+    distance from u (and from top_p) to the cumulative boundaries around it,
+    and the scaled-logit gap between the chosen token and its neighbours in
+    the sort order.  A logit perturbation of at most dz moves each of these
+    by about 2 dz / T."""
     z = np.asarray(z, dtype=np.float32).astype(np.float64)
     if greedy or u is None:
         s = np.sort(z[np.isfinite(z)])[::-1]
@@ -49,7 +53,16 @@ def decision_margin(z, greedy, temperature=1.0, top_p=1.0, u=None):
     if n_keep > 1:
         edge.append(abs(cum[n_keep - 2] - top_p))
     ck = np.cumsum(p[order[:n_keep]]) / cum[n_keep - 1]
-    return float(min(min(edge), np.min(np.abs(ck - float(u)))))
+    # the draw also flips when the chosen token trades places with a
+    # neighbour in the (p desc, id asc) order, i.e. when their scaled logits
+    # are within the perturbation of each other, wherever u sits
+    j = min(int(np.searchsorted(ck, float(u), side="right")), n_keep - 1)
+    gaps = []
+    if j + 1 < len(order):
+        gaps.append(zz[order[j]] - zz[order[j + 1]])
+    if j > 0:
+        gaps.append(zz[order[j - 1]] - zz[order[j]])
+    return float(min(min(edge), np.min(np.abs(ck - float(u))), *gaps))
 
 
 def margin_ok(margin, greedy):

@@ -108,7 +108,7 @@ def test_create_without_gpu_reports_no_device(lib):
 
 def test_null_context_calls(lib):
     s = bd.Sampling(1.0, 1.0, 1, 0)
-    assert lib.dualar_prefill(None, 1, None, 1, None, C.byref(s), None, None) == -1
+    assert lib.dualar_prefill(None, 1, None, 1, None, C.byref(s), None, None, None) == -1
     assert lib.dualar_decode_frames(None, 1, C.byref(s), None, None, None, None) == -1
     assert lib.dualar_fast_frames(None, 1, 1, None, None, C.byref(s), None, None, None) == -1
     assert lib.dualar_sync(None, None) == -1
