@@ -507,17 +507,22 @@ dualar_status dualar_create(const dualar_config* cfg, const dualar_weights* w, v
   if (!out) return fail(c, DUALAR_ERR_INVALID_ARG, "out is NULL");
   if (!resolve(cfg, &r, &err)) return fail(c, DUALAR_ERR_INVALID_ARG, err);
   if (!w) return fail(c, DUALAR_ERR_INVALID_ARG, "weights is NULL");
-  if (!w->tok_embedding || !w->codebook_embedding || !w->norm || !w->layers || !w->fast_layers ||
-      !w->fast_embeddings || !w->fast_norm || !w->fast_output)
-    return fail(c, DUALAR_ERR_INVALID_ARG, "a weight pointer is NULL");
-  auto layer_ok = [](const dualar_layer_weights& l, int qk) {
-    return l.attention_norm && l.wq && l.wk && l.wv && l.wo && l.ffn_norm && l.w1 && l.w3 && l.w2 &&
-           (!qk || (l.q_norm && l.k_norm));
+  // every tensor is read with 16-byte vector loads
+  auto P = [](const void* q) { return q && ((uintptr_t)q % 16) == 0; };
+  if (!w->layers || !w->fast_layers) return fail(c, DUALAR_ERR_INVALID_ARG, "a layer array is NULL");
+  if (!P(w->tok_embedding) || !P(w->codebook_embedding) || !P(w->norm) || !P(w->fast_embeddings) ||
+      !P(w->fast_norm) || !P(w->fast_output))
+    return fail(c, DUALAR_ERR_INVALID_ARG, "a weight pointer is NULL or not 16-byte aligned");
+  auto layer_ok = [&](const dualar_layer_weights& l, int qk) {
+    return P(l.attention_norm) && P(l.wq) && P(l.wk) && P(l.wv) && P(l.wo) && P(l.ffn_norm) && P(l.w1) &&
+           P(l.w3) && P(l.w2) && (!qk || (P(l.q_norm) && P(l.k_norm)));
   };
   for (int i = 0; i < r.n_layer; ++i)
-    if (!layer_ok(w->layers[i], r.slow_qk)) return fail(c, DUALAR_ERR_INVALID_ARG, "a slow layer weight is NULL");
+    if (!layer_ok(w->layers[i], r.slow_qk))
+      return fail(c, DUALAR_ERR_INVALID_ARG, "a slow layer weight is NULL or not 16-byte aligned");
   for (int i = 0; i < r.fn_layer; ++i)
-    if (!layer_ok(w->fast_layers[i], r.fast_qk)) return fail(c, DUALAR_ERR_INVALID_ARG, "a fast layer weight is NULL");
+    if (!layer_ok(w->fast_layers[i], r.fast_qk))
+      return fail(c, DUALAR_ERR_INVALID_ARG, "a fast layer weight is NULL or not 16-byte aligned");
   const Layout L = layout(r);
   if (!workspace) return fail(c, DUALAR_ERR_INVALID_ARG, "workspace is NULL");
   if (((uintptr_t)workspace) % ALIGN) return fail(c, DUALAR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");

@@ -13,12 +13,10 @@ enum { ST_BAD_TOKEN = 1, ST_NONFINITE = 2 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
+// fp32 -> bf16, round to nearest even (NaN kept quiet): gfx950's
+// v_cvt_pk_bf16_f32, branch-free.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Element-type traits: a 16-byte vector holds EPV elements.

@@ -96,8 +96,10 @@ typedef struct {
   const void *w2;                /* [dim, ffn]  (down)         */
 } dualar_layer_weights;
 
-/* All device pointers; the two layer arrays are HOST arrays of n_layer and
- * n_fast_layer entries (copied at create). */
+/* All device pointers, each 16-byte aligned (tensors are read with 16-byte
+ * vector loads; dualar_create rejects others with DUALAR_ERR_INVALID_ARG);
+ * the two layer arrays are HOST arrays of n_layer and n_fast_layer entries
+ * (copied at create). */
 typedef struct {
   const void *tok_embedding;        /* [vocab, dim]; also the tied slow head   */
   const void *codebook_embedding;   /* [N*C, dim]; codebook k = rows k*C..     */

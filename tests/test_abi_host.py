@@ -91,6 +91,9 @@ def test_create_checks_before_device(lib):
     assert lib.dualar_create(C.byref(cfg), C.byref(w), C.c_void_p(256), need - 1, None, C.byref(h)) == -3
     w.layers[1].w2 = None
     assert lib.dualar_create(C.byref(cfg), C.byref(w), C.c_void_p(256), need, None, C.byref(h)) == -1
+    w.layers[1].w2 = 4096 + 8          # not 16-byte aligned
+    assert lib.dualar_create(C.byref(cfg), C.byref(w), C.c_void_p(256), need, None, C.byref(h)) == -1
+    assert b"aligned" in lib.dualar_last_error(None)
     assert not h.value
 
 
