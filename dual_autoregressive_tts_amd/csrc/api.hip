@@ -127,9 +127,10 @@ Layout layout(const Resolved& r) {
   const int maxH = std::max(r.H, r.fH), maxhd = std::max(r.hd, r.fhd);
   L.part = take((size_t)r.max_batch * maxH * L.max_splits * (maxhd + 2) * 4);
   L.counters = take((size_t)r.max_batch * std::max(r.KV, r.fKV) * 4);
-  // matrix-core GEMM scratch: normalised activations and split-K partials
-  L.xn = take((size_t)r.max_batch * std::max(std::max(r.dim, r.ffn), std::max(r.fffn, L.att_ld)) * 4);
-  L.gpart_elems = r.max_batch >= 8 ? (size_t)8 * r.max_batch *
+  // matrix-core GEMM scratch: the activations as three bf16 planes (6 bytes
+  // per element) and split-K partials (up to 32 splits)
+  L.xn = take((size_t)r.max_batch * std::max(std::max(r.dim, r.ffn), std::max(r.fffn, L.att_ld)) * 6);
+  L.gpart_elems = r.max_batch >= 8 ? (size_t)32 * r.max_batch *
                                          std::max(std::max(2 * r.ffn, 2 * r.fffn), std::max(L.qkv_ld, r.dim))
                                    : 0;
   L.gpart = take(L.gpart_elems * 4);
@@ -217,7 +218,7 @@ hipError_t prof_post(dualar_ctx* c, int cls, double bytes, bool swiglu = false) 
 template <typename T>
 hipError_t gemv(dualar_ctx* c, const GemvParams& g0) {
   GemvParams g = g0;
-  g.xn = (float*)(c->ws + c->L.xn);
+  g.xn = (void*)(c->ws + c->L.xn);
   g.part = c->L.gpart_elems ? (float*)(c->ws + c->L.gpart) : nullptr;
   g.part_elems = c->L.gpart_elems;
   const bool sw = g.mode == GEMV_SWIGLU;

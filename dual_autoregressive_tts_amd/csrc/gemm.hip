@@ -1,199 +1,310 @@
 // Matrix products for 8..32+ activation rows (batched decode, batched
 // prefill steps) on the gfx950 matrix cores: Y[b][n] = sum_k W[n][k] X[b][k].
 //
-// v_mfma_f32_32x32x16_bf16 with W as the A operand (32 output rows, lane l
-// holds W[n0 + l%32][k + 8*(l/32) .. +8], 16 contiguous bytes) and the
-// activations as the B operand (32 activation rows, lane l holds
-// X[b0 + l%32][k + 8*(l/32) .. +8]).  Activations are fp32: each is split
-// into three bf16 terms, x = t0 + t1 + t2 + r with t0 = bf16(x),
-// t1 = bf16(x - t0), t2 = bf16(x - t0 - t1) (every subtraction exact in
-// fp32, |r| <= 2^-24 |x|), and the three products are accumulated in fp32.
-// The weights are bf16 already, so the product is the fp32 product of the
-// stored weights and the fp32 activations up to accumulation order.  A
-// two-term split would leave ~2^-17 relative error per activation, which is
-// enough to move bf16-rounded K/V entries one ulp far more often than fp32
-// rounding order does.  The third product is cheap: at B <= 32 one 1 KB
-// weight tile feeds 3 x 32 MFMA cycles per SIMD, about 3x the HBM rate.
+// v_mfma_f32_32x32x16_bf16 with W as the A operand (32 output rows; lane l
+// holds W[n0 + l%32][k + 8*(l/32) .. +8]) and the activations as the B
+// operand (32 activation rows; lane l holds X[b0 + l%32][k + 8*(l/32) .. +8]).
+// Activations are fp32: xsplit_kernel splits each into three bf16 terms,
+// x = t0 + t1 + t2 + r with t0 = bf16(x), t1 = bf16(x - t0),
+// t2 = bf16(x - t0 - t1) (every subtraction exact in fp32, |r| <= 2^-24 |x|),
+// stored as three planes, and the three products are accumulated in fp32
+// (one accumulator per term, added smallest first at the end).  The weights are bf16
+// already, so the product is the fp32 product of the stored weights and the
+// fp32 activations up to accumulation order.  (Two terms would leave ~2^-17
+// relative error per activation, enough to move bf16-rounded K/V entries one
+// ulp far more often than fp32 rounding order does.)
 //
-// A workgroup owns one 32-row tile (gate and up tiles for SwiGLU) and a
-// 1/ksw slice of K, split again over its 4 waves; the 4 wave partials meet in
-// LDS in a fixed order.  With ksw > 1 the workgroups write partial sums and
-// mfma_finish_kernel adds them (fixed order) and applies the epilogue.
-// RMSNorm, when the product has a gain, runs first in rownorm_kernel.
-//
-// Each wave streams its K range in batches of U k-steps; the next batch's
-// loads are issued before the current batch's MFMAs so that a wave always
-// has a batch in flight.  Weight rows are read 32 B per lane-pair per step
-// (the operand layout), so the loads go through the cache: the four reads
-// that make up one 128-byte line then cost one HBM fetch.  Activation
-// columns past B are loaded from row 0 and never stored (MFMA output column
-// b depends only on operand column b).
+// Memory path.  Read straight in the operand layout, every load instruction
+// touches 32 rows, i.e. 32 cache lines per KB, and the activation operand
+// costs two such loads per step: the cache-line request rate, not HBM, then
+// bounds the kernel.  Here both operands go through LDS instead.  A workgroup
+// owns ROWS output rows (gate and up rows for SwiGLU) and one 32-row
+// activation tile, and walks its K range in chunks of 64: each chunk of
+// weights (ROWS*NR rows x 128 B) and activation planes (3 x 32 rows x 128 B)
+// is copied by LDS DMA (global_load_lds_dwordx4: lane i's 16 bytes land at
+// the wave's LDS base + 16 i), each instruction covering 8 whole 128-byte
+// lines.
+// Pieces are XOR-swizzled within their row so that the operand-layout LDS
+// reads are bank-conflict free.  Three stages: while a chunk is multiplied
+// the next two are in flight; one barrier per chunk.  Waves split rows, not
+// K, so no cross-wave reduction is needed; the epilogue goes through LDS so
+// that each store writes 128-byte runs.  With ksw > 1 the workgroups of a
+// row block write partial sums that mfma_finish_kernel adds in a fixed order.
+// RMSNorm, when the product has a gain, is applied by xsplit_kernel.
 #include "common.h"
 #include "internal.h"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ const char* mrow(const GemvParams& p, int row, int s) {
-  if (p.mode == GEMV_SWIGLU) return (const char*)p.w[s] + (size_t)row * p.K * 2;
-  if (row < p.rows[0]) return (const char*)p.w[0] + (size_t)row * p.K * 2;
-  row -= p.rows[0];
-  if (row < p.rows[1]) return (const char*)p.w[1] + (size_t)row * p.K * 2;
-  row -= p.rows[1];
-  return (const char*)p.w[2] + (size_t)row * p.K * 2;
-}
+#define GM_KC 64                     // k per chunk
+#define GM_STAGES 3
 
-// Output element of accumulator register r in lane `lane` of a 32x32 tile.
-__device__ __forceinline__ int tile_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
-
-template <int NR, int U>
-struct Batch {
-  u32x4 a[U][NR];
-  float4 x[U][2];
+// Workgroup shape: WAVES waves, each owning T 32-row output tiles (times NR
+// segments); the workgroup covers ROWS = 32*WAVES*T output rows.
+template <int NR, int WAVES, int T> struct Gm {
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROWS = 32 * WAVES * T;
+  static constexpr int W_BYTES = ROWS * NR * GM_KC * 2;     // weight chunk
+  static constexpr int X_BYTES = 3 * 32 * GM_KC * 2;        // activation planes chunk
+  static constexpr int STAGE = W_BYTES + X_BYTES;
+  static constexpr int W_INSTR = W_BYTES / 1024 / WAVES;     // DMA instructions per wave per chunk
+  static constexpr int X_INSTR = X_BYTES / 1024 / WAVES;
+  static constexpr int DMA = W_INSTR + X_INSTR;
+  static_assert(W_BYTES % (1024 * WAVES) == 0 && X_BYTES % (1024 * WAVES) == 0, "DMA split");
+  static_assert((WAVES > 3 ? 2 : 1) * NR * T * 32 * 33 * 4 <= STAGE, "epilogue transposes fit the stages");
 };
 
-template <int NR, int U>
-__device__ __forceinline__ void load_batch(Batch<NR, U>& bt, const char* const* wa, const float* xb, int st) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {   // activations first (cache-resident), then weights
-    bt.x[u][0] = *(const float4*)(xb + (st + u) * 16);
-    bt.x[u][1] = *(const float4*)(xb + (st + u) * 16 + 4);
+// The product's weight row space held in scalar registers: for SwiGLU,
+// segment s is W1 (s = 0) or W3; otherwise the rows of w[0], w[1], w[2]
+// follow each other.  (The empty asm pins each pointer in an SGPR: left
+// alone, the compiler turns the select below into a per-lane indexed load
+// of the kernel arguments.)
+struct RowSpace {
+  uint64_t w0, w1, w2;
+  int r0, r1, swiglu;
+  size_t ld;    // row bytes
+  __device__ __forceinline__ explicit RowSpace(const GemvParams& p) {
+    w0 = (uint64_t)p.w[0];
+    w1 = (uint64_t)p.w[1];
+    w2 = (uint64_t)p.w[2];
+    asm volatile("" : "+s"(w0), "+s"(w1), "+s"(w2));
+    r0 = p.rows[0];
+    r1 = p.rows[1];
+    swiglu = p.mode == GEMV_SWIGLU;
+    ld = (size_t)p.K * 2;
   }
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int s = 0; s < NR; ++s) bt.a[u][s] = ld_vec(wa[s] + (size_t)(st + u) * 32);
-}
-
-// x = t0 + t1 + t2 (+ a residual below 2^-24 |x|), each term bf16.
-template <int NR, int U>
-__device__ __forceinline__ void mma_batch(const Batch<NR, U>& bt, f32x16* acc) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const f32x8 v = {bt.x[u][0].x, bt.x[u][0].y, bt.x[u][0].z, bt.x[u][0].w,
-                     bt.x[u][1].x, bt.x[u][1].y, bt.x[u][1].z, bt.x[u][1].w};
-    const bf16x8 t0 = __builtin_convertvector(v, bf16x8);
-    const f32x8 r1 = v - __builtin_convertvector(t0, f32x8);
-    const bf16x8 t1 = __builtin_convertvector(r1, bf16x8);
-    const bf16x8 t2 = __builtin_convertvector(r1 - __builtin_convertvector(t1, f32x8), bf16x8);
-#pragma unroll
-    for (int s = 0; s < NR; ++s) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, bt.a[u][s]);
-      acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, t0, acc[s], 0, 0, 0);
-      acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, t1, acc[s], 0, 0, 0);
-      acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, t2, acc[s], 0, 0, 0);
-    }
-  }
-}
-
-// Grid (ceil(n_out/32), ksw, ceil(B/32)).  The host guarantees K % (ksw*64) == 0
-// and that each wave's step count (K/(ksw*64)) is a multiple of 2U.
-template <int NR, int U>
-__global__ void __launch_bounds__(DUALAR_WG) mfma_gemm_kernel(GemvParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 32, kw = blockIdx.y, b0 = blockIdx.z * 32;
-  const int Kw = p.K / p.ksw, Kq = Kw / 4;
-  const int kbeg = kw * Kw + wave * Kq;
-  const int nsteps = Kq / 16;
-  const int koff = kbeg + 8 * (lane >> 5);
-
-  const char* wa[NR];
-  const int arow = min(n0 + (lane & 31), p.n_out - 1);
-#pragma unroll
-  for (int s = 0; s < NR; ++s) wa[s] = mrow(p, arow, s) + (size_t)koff * 2;
-  const int brow = b0 + (lane & 31);
-  const float* xb = p.x + (size_t)(brow < p.B ? brow : 0) * p.ldx + koff;
-
-  f32x16 acc[NR];
-#pragma unroll
-  for (int s = 0; s < NR; ++s)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[s][r] = 0.f;
-
-  // Double-buffered, two batches per trip: the next batch's loads are
-  // always issued (past the end they re-read the last batch, a cache hit),
-  // and scheduling barriers keep each batch's loads together ahead of the
-  // other batch's MFMAs, so every wait leaves one whole batch in flight.  (A
-  // conditional prefetch, a loop with two exits, or letting the scheduler
-  // sink each load next to its use all make the compiler wait for
-  // everything.)
-  Batch<NR, U> b0b, b1b;
-  const int last = nsteps - U;
-  load_batch<NR, U>(b0b, wa, xb, 0);
-  int st = 0;
-  do {
-    load_batch<NR, U>(b1b, wa, xb, min(st + U, last));
-    __builtin_amdgcn_sched_barrier(0);
-    mma_batch<NR, U>(b0b, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    load_batch<NR, U>(b0b, wa, xb, min(st + 2 * U, last));
-    __builtin_amdgcn_sched_barrier(0);
-    mma_batch<NR, U>(b1b, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    st += 2 * U;
-  } while (st < nsteps);
-
-  // The 4 waves' partials, added in a fixed order.  The rows are padded to
-  // 65 floats so that reading them in output order is conflict-free; thread
-  // i then owns output row n0 + i%32 of activation row b0 + i/32 (+8j), so
-  // each store instruction writes whole 128-byte runs of y or part.
-  __shared__ float red[4][NR][16][65];
-#pragma unroll
-  for (int s = 0; s < NR; ++s)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][s][r][lane] = acc[s][r];
-  __syncthreads();
-  const int nl = threadIdx.x & 31;
-  const int n = n0 + nl;
-  const int r = ((nl >> 3) << 2) | (nl & 3);        // inverse of tile_row
-  const int lhi = ((nl >> 2) & 1) << 5;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int bl = (threadIdx.x >> 5) + 8 * j;
-    const int b = b0 + bl, l = lhi | bl;
-    if (n >= p.n_out || b >= p.B) continue;
-    float v[NR];
-#pragma unroll
-    for (int s = 0; s < NR; ++s) v[s] = (red[0][s][r][l] + red[1][s][r][l]) + (red[2][s][r][l] + red[3][s][r][l]);
-    if (p.ksw > 1) {
-      float* dst = p.part + ((size_t)kw * p.B + b) * p.ldp;
-#pragma unroll
-      for (int s = 0; s < NR; ++s) dst[(size_t)s * p.n_out + n] = v[s];
+  __device__ __forceinline__ const char* row(int r, int s) const {
+    uint64_t base;
+    if (swiglu) {
+      base = s == 0 ? w0 : w1;
     } else {
-      float out;
-      if (p.mode == GEMV_SWIGLU) out = silu_f(v[0]) * v[NR - 1];
-      else if (p.mode == GEMV_ADD) out = p.res[(size_t)b * p.ldres + n] + v[0];
-      else out = v[0];
-      p.y[(size_t)b * p.ldy + n] = out;
+      const int q1 = r - r0, q2 = q1 - r1;
+      base = r < r0 ? w0 : (q1 < r1 ? w1 : w2);
+      r = r < r0 ? r : (q1 < r1 ? q1 : q2);
+    }
+    return (const char*)base + (size_t)r * ld;
+  }
+};
+
+// LDS DMA of 16 bytes per lane: lane i's bytes land at lds + 16 i (lds is
+// wave-uniform).  Written as inline asm so that the compiler does not track
+// these copies: its conservative tracking of LDS DMA across the main loop's
+// back edge would wait for every copy in flight before each LDS read.  The
+// kernel waits for them itself (wait_vm_barrier) and issues no other vector
+// memory loads while any is in flight.
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+  const unsigned la = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector memory operations are
+// outstanding, then workgroup barrier.  One asm statement with a memory
+// clobber, so that no LDS access moves across it.
+template <int N> __device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Per-lane DMA sources of this workgroup's chunk 0; chunk c adds c*64
+// elements.
+template <class G> struct GmSrc {
+  const char* w[G::W_INSTR];
+  const char* x[G::X_INSTR];
+};
+
+// Weight row r of a chunk (segment r / ROWS, output row n0 + r % ROWS)
+// lands at r*128 + 16*(piece ^ ((r >> 1) & 7)); activation row rr at
+// rr*256 + 16*(piece ^ (rr & 15)).
+template <int NR, class G>
+__device__ __forceinline__ void gm_sources(const GemvParams& p, GmSrc<G>& src, int n0, int b0, int kbeg, int wave,
+                                           int lane) {
+  const RowSpace rs(p);
+#pragma unroll
+  for (int j = 0; j < G::W_INSTR; ++j) {
+    const int i = wave * G::W_INSTR + j;
+    const int r = 8 * i + (lane >> 3);
+    const int piece = (lane & 7) ^ ((r >> 1) & 7);
+    const int n = min(n0 + r % G::ROWS, p.n_out - 1);
+    src.w[j] = rs.row(n, r / G::ROWS) + (size_t)(kbeg + piece * 8) * 2;
+  }
+  // activation plane q, row rr (0..31) of a chunk lands at
+  // q*4096 + rr*128 + 16*(piece ^ ((rr >> 1) & 7)), like the weights
+  const uint16_t* xs = (const uint16_t*)p.xn;
+  const size_t plane = (size_t)p.B * p.K;
+#pragma unroll
+  for (int j = 0; j < G::X_INSTR; ++j) {
+    const int i = wave * G::X_INSTR + j;            // 0..11
+    const int q = i >> 2, rr = 8 * (i & 3) + (lane >> 3);
+    const int piece = (lane & 7) ^ ((rr >> 1) & 7);
+    const int b = b0 + rr < p.B ? b0 + rr : 0;      // padding columns: never stored
+    src.x[j] = (const char*)(xs + q * plane + (size_t)b * p.K + kbeg + piece * 8);
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void gm_issue(const GmSrc<G>& src, char* stage, int c, int wave) {
+#pragma unroll
+  for (int j = 0; j < G::W_INSTR; ++j)
+    dma16(src.w[j] + (size_t)c * GM_KC * 2, stage + (wave * G::W_INSTR + j) * 1024);
+  char* xs = stage + G::W_BYTES;
+#pragma unroll
+  for (int j = 0; j < G::X_INSTR; ++j)
+    dma16(src.x[j] + (size_t)c * GM_KC * 2, xs + (wave * G::X_INSTR + j) * 1024);
+}
+
+// The four 16-wide k-steps of one chunk.  The three activation terms are
+// read once per step and used for the wave's T tiles and NR segments; each
+// term has its own accumulator, so the three products of a step do not wait
+// on each other.
+template <int NR, int T, class G>
+__device__ __forceinline__ void gm_compute(const char* stage, int wave, int lane, f32x16 (*acc)[NR][3]) {
+  const char* xs = stage + G::W_BYTES;
+  const int h = lane >> 5, b = lane & 31;
+  const int bsw = (b >> 1) & 7;
+#pragma unroll
+  for (int t = 0; t < GM_KC / 16; ++t) {
+    const int pc = 2 * t + h;
+    bf16x8 tx[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) tx[q] = *(const bf16x8*)(xs + q * 4096 + b * 128 + ((pc ^ bsw) << 4));
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        const int r = s * G::ROWS + 32 * (wave * T + tt) + b;
+        const bf16x8 av = *(const bf16x8*)(stage + r * 128 + ((pc ^ ((r >> 1) & 7)) << 4));
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          acc[tt][s][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, tx[q], acc[tt][s][q], 0, 0, 0);
+      }
+  }
+}
+
+// One pipeline step: chunk cc from stage S; chunk cc+2 goes to stage
+// (S+2)%3.  This wave's copies of chunk cc are done once at most the next
+// chunk's are outstanding; after the barrier every wave's are, and every
+// wave has finished reading the stage that chunk cc+2 overwrites.
+template <int NR, int T, class G, int S>
+__device__ __forceinline__ void gm_step(const GmSrc<G>& src, char* st0, char* st1, char* st2, int cc, int nch,
+                                        int wave, int lane, f32x16 (*acc)[NR][3]) {
+  char* const cur = S == 0 ? st0 : (S == 1 ? st1 : st2);
+  char* const nxt = S == 0 ? st2 : (S == 1 ? st0 : st1);     // stage (S+2)%3
+  if (cc + 1 < nch) wait_vm_barrier<G::DMA>();
+  else wait_vm_barrier<0>();
+  if (cc + 2 < nch) gm_issue<G>(src, nxt, cc + 2, wave);
+  gm_compute<NR, T, G>(cur, wave, lane, acc);
+}
+
+// Grid (ceil(n_out/ROWS), ksw, ceil(B/32)), THREADS threads.  The host
+// guarantees K % (ksw*64) == 0.
+template <int NR, int WAVES, int T>
+__global__ void __launch_bounds__(64 * WAVES) mfma_gemm_kernel(GemvParams p) {
+  using G = Gm<NR, WAVES, T>;
+  __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[G::STAGE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * G::ROWS, kw = blockIdx.y, b0 = blockIdx.z * 32;
+  const int Kw = p.K / p.ksw, kbeg = kw * Kw;
+  const int nch = Kw / GM_KC;
+
+  f32x16 acc[T][NR][3];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+    for (int s = 0; s < NR; ++s)
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tt][s][j][r] = 0.f;
+
+  GmSrc<G> src;
+  gm_sources<NR, G>(p, src, n0, b0, kbeg, wave, lane);
+  gm_issue<G>(src, st0, 0, wave);
+  if (nch > 1) gm_issue<G>(src, st1, 1, wave);
+  for (int c = 0; c < nch; c += 3) {
+    gm_step<NR, T, G, 0>(src, st0, st1, st2, c, nch, wave, lane, acc);
+    if (c + 1 >= nch) break;
+    gm_step<NR, T, G, 1>(src, st0, st1, st2, c + 1, nch, wave, lane, acc);
+    if (c + 2 >= nch) break;
+    gm_step<NR, T, G, 2>(src, st0, st1, st2, c + 2, nch, wave, lane, acc);
+  }
+
+  // Epilogue.  The three term sums are added smallest first; D[row][col] of
+  // register r in lane l is at row (r/4)*8 + (l/32)*4 + r%4, col l%32.
+  // Transpose through this wave's slice of stage 0..2 so that lanes 0..31
+  // store 32 consecutive outputs of one b.
+  __syncthreads();
+  char* const mine = wave % 3 == 0 ? st0 : (wave % 3 == 1 ? st1 : st2);
+  float* tr = (float*)mine + (wave / 3) * (T * NR * 32 * 33);
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+    for (int s = 0; s < NR; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        tr[((tt * NR + s) * 32 + (lane & 31)) * 33 + row] = acc[tt][s][0][r] + (acc[tt][s][1][r] + acc[tt][s][2][r]);
+      }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  const int nl = lane & 31;
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    const int n = n0 + 32 * (wave * T + tt) + nl;
+    if (n >= p.n_out) continue;
+#pragma unroll 4
+    for (int j = 0; j < 16; ++j) {
+      const int bl = 2 * j + (lane >> 5), b = b0 + bl;
+      if (b >= p.B) continue;
+      float v[NR];
+#pragma unroll
+      for (int s = 0; s < NR; ++s) v[s] = tr[((tt * NR + s) * 32 + bl) * 33 + nl];
+      if (p.ksw > 1) {
+        float* dst = p.part + ((size_t)kw * p.B + b) * p.ldp;
+#pragma unroll
+        for (int s = 0; s < NR; ++s) dst[(size_t)s * p.n_out + n] = v[s];
+      } else {
+        float out;
+        if (p.mode == GEMV_SWIGLU) out = silu_f(v[0]) * v[NR - 1];
+        else if (p.mode == GEMV_ADD) out = p.res[(size_t)b * p.ldres + n] + v[0];
+        else out = v[0];
+        p.y[(size_t)b * p.ldy + n] = out;
+      }
     }
   }
 }
 
-#define FIN_MAXK 8   // largest ksw the finish kernel reads with all loads issued up front
+#define FIN_MAXK 32   // largest K split
+#define FIN_BATCH 8   // partials loaded together
 
-// Sum the ksw partials (fixed order) and apply the epilogue.
+// Sum the ksw partials (fixed order, kw = 0, 1, ...) and apply the epilogue.
 __global__ void __launch_bounds__(DUALAR_WG) mfma_finish_kernel(GemvParams p) {
   const size_t i = (size_t)blockIdx.x * DUALAR_WG + threadIdx.x;
   if (i >= (size_t)p.B * p.n_out) return;
   const int b = (int)(i / p.n_out), n = (int)(i % p.n_out);
   const bool glu = p.mode == GEMV_SWIGLU;
-  float g[FIN_MAXK], u[FIN_MAXK];
-#pragma unroll
-  for (int kw = 0; kw < FIN_MAXK; ++kw) {
-    if (kw < p.ksw) {
-      const float* src = p.part + ((size_t)kw * p.B + b) * p.ldp;
-      g[kw] = src[n];
-      u[kw] = glu ? src[(size_t)p.n_out + n] : 0.f;
-    }
-  }
   const float r = p.mode == GEMV_ADD ? p.res[(size_t)b * p.ldres + n] : 0.f;
   float v0 = 0.f, v1 = 0.f;
+  for (int k0 = 0; k0 < p.ksw; k0 += FIN_BATCH) {
+    float g[FIN_BATCH], u[FIN_BATCH];
 #pragma unroll
-  for (int kw = 0; kw < FIN_MAXK; ++kw) {
-    if (kw < p.ksw) {
-      v0 += g[kw];
-      v1 += u[kw];
+    for (int j = 0; j < FIN_BATCH; ++j) {
+      if (k0 + j < p.ksw) {
+        const float* src = p.part + ((size_t)(k0 + j) * p.B + b) * p.ldp;
+        g[j] = src[n];
+        u[j] = glu ? src[(size_t)p.n_out + n] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FIN_BATCH; ++j) {
+      if (k0 + j < p.ksw) {
+        v0 += g[j];
+        v1 += u[j];
+      }
     }
   }
   float out;
@@ -205,99 +316,105 @@ __global__ void __launch_bounds__(DUALAR_WG) mfma_finish_kernel(GemvParams p) {
 
 #define NORM_MAXV 12   // float4s per thread: K <= 12288
 
-// xn[b] = x[b] / sqrt(mean(x[b]^2) + eps) * g, one workgroup per row; the
-// row is read once, with every load issued before the first use.
-__global__ void __launch_bounds__(DUALAR_WG) rownorm_kernel(GemvParams p) {
+// Split row b of the activations into three bf16 planes (x = t0 + t1 + t2
+// + r, |r| <= 2^-24 |x|): plane q at xn + q*B*K.  With a gain the row is
+// first RMS-normalised: x / sqrt(mean(x^2) + eps) * g.  One workgroup per
+// row; the row is read once, with every load issued before the first use.
+__global__ void __launch_bounds__(DUALAR_WG) xsplit_kernel(GemvParams p) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float red[4];
   const float4* x = (const float4*)(p.x + (size_t)b * p.ldx);
   const int nv = p.K / 4;
   float4 v[NORM_MAXV];
-  float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < NORM_MAXV; ++j)
     if (tid + j * DUALAR_WG < nv) v[j] = x[tid + j * DUALAR_WG];
+  float inv = 1.f;
+  if (p.gain) {
+    float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < NORM_MAXV; ++j)
-    if (tid + j * DUALAR_WG < nv) ss += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
-  ss = wave_sum(ss);
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  const float inv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)p.K + p.eps);
-  float4* xn = (float4*)(p.xn + (size_t)b * p.K);
+    for (int j = 0; j < NORM_MAXV; ++j)
+      if (tid + j * DUALAR_WG < nv) ss += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    inv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)p.K + p.eps);
+  }
   const uint2* g = (const uint2*)p.gain;
+  uint2* xs = (uint2*)p.xn;
+  const size_t plane = (size_t)p.B * p.K / 4;      // in 4-element units
 #pragma unroll
   for (int j = 0; j < NORM_MAXV; ++j) {
     const int k = tid + j * DUALAR_WG;
     if (k < nv) {
-      const uint2 gg = g[k];
-      float4 o;
-      o.x = v[j].x * inv * bf16_bits_to_f32(gg.x & 0xffffu);
-      o.y = v[j].y * inv * bf16_bits_to_f32(gg.x >> 16);
-      o.z = v[j].z * inv * bf16_bits_to_f32(gg.y & 0xffffu);
-      o.w = v[j].w * inv * bf16_bits_to_f32(gg.y >> 16);
-      xn[k] = o;
+      float o[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      if (p.gain) {
+        const uint2 gg = g[k];
+        o[0] = o[0] * inv * bf16_bits_to_f32(gg.x & 0xffffu);
+        o[1] = o[1] * inv * bf16_bits_to_f32(gg.x >> 16);
+        o[2] = o[2] * inv * bf16_bits_to_f32(gg.y & 0xffffu);
+        o[3] = o[3] * inv * bf16_bits_to_f32(gg.y >> 16);
+      }
+      uint32_t t[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t a0 = f32_to_bf16_rne(o[e]);
+        const float r1 = o[e] - bf16_bits_to_f32(a0);
+        const uint16_t a1 = f32_to_bf16_rne(r1);
+        t[0][e] = a0;
+        t[1][e] = a1;
+        t[2][e] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(a1));
+      }
+      const size_t at = (size_t)b * nv + k;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) xs[q * plane + at] = make_uint2(t[q][0] | (t[q][1] << 16), t[q][2] | (t[q][3] << 16));
     }
   }
 }
 
-template <int NR, int U>
-static void launch_main(const GemvParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((mfma_gemm_kernel<NR, U>), grid, dim3(DUALAR_WG), 0, s, p);
-}
-
-// Matrix-core path for bf16 weights, B >= 8, K a multiple of 64 (returns
-// false when it does not apply).
-bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
-  if (p0.B < 8 || p0.K % 64 != 0 || !p0.part || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
-  GemvParams p = p0;
-  const int NR = p.mode == GEMV_SWIGLU ? 2 : 1;
-  const int tiles = ((p.n_out + 31) / 32) * ((p.B + 31) / 32);
-  // Split K over ksw workgroups.  Each wave must get a whole number of
-  // 16-wide k-steps (K % (ksw*64) == 0) and the partial buffer must hold
-  // ksw * B rows.  Take the smallest split that gives >= 512 workgroups with
-  // batches of >= 2 steps, else the one with the most workgroups among those
-  // with batches of >= 2 steps.  A caller may preset p.ksw.
-  // U = the largest of 4, 2, 1 with nsteps % (2U) == 0 (the main loop
-  // consumes two batches per trip); odd step counts are not launched.
-  auto u_of = [&](int c) { const int n = p.K / (c * 64); return n % 8 == 0 ? 4 : (n % 4 == 0 ? 2 : 1); };
-  auto ok = [&](int c) {
-    return p.K % (c * 64) == 0 && (p.K / (c * 64)) % 2 == 0 &&
-           (c == 1 || (size_t)c * p.B * p.n_out * NR <= p.part_elems);
+template <int NR, int WAVES, int T>
+static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, bool* ok) {
+  using G = Gm<NR, WAVES, T>;
+  const int tiles = ((p.n_out + G::ROWS - 1) / G::ROWS) * ((p.B + 31) / 32);
+  // Split K over ksw workgroups per row block (K % (ksw*64) == 0, partial
+  // buffer holds ksw*B rows): the smallest split that fills the slots while
+  // each workgroup keeps >= 4 chunks, else the largest that keeps 4 chunks.
+  auto fits = [&](int c) {
+    return p.K % (c * GM_KC) == 0 && (c == 1 || (size_t)c * p.B * p.n_out * NR <= p.part_elems);
   };
-  int ksw = 0;
-  if (p0.ksw > 0) {
-    if (p0.ksw > FIN_MAXK || !ok(p0.ksw)) return false;
-    ksw = p0.ksw;
+  int ksw = ksw_preset;
+  if (ksw > 0) {
+    if (ksw > FIN_MAXK || !fits(ksw)) { *ok = false; return; }
   } else {
-    int best = 0;
-    for (int c = 1; c <= FIN_MAXK; ++c) {
-      if (!ok(c) || (c > 1 && u_of(c) < 2)) continue;
-      if (tiles * c >= 512) { ksw = c; break; }
-      best = c;
-    }
-    if (!ksw) ksw = best;
-    if (!ksw) return false;
-  }
-  if (p.gain) {
-    hipLaunchKernelGGL(rownorm_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
-    p.x = p.xn;
-    p.ldx = p.K;
+    ksw = 1;
+    for (int c = 2; c <= FIN_MAXK && tiles * ksw < slots; ++c)
+      if (fits(c) && p.K / (c * GM_KC) >= 4) ksw = c;
   }
   p.ksw = ksw;
   p.ldp = p.n_out * NR;
-  const int U = u_of(ksw);
-  dim3 grid((p.n_out + 31) / 32, ksw, (p.B + 31) / 32);
-  if (NR == 2) {
-    if (U == 4) launch_main<2, 4>(p, grid, s);
-    else if (U == 2) launch_main<2, 2>(p, grid, s);
-    else launch_main<2, 1>(p, grid, s);
-  } else {
-    if (U == 4) launch_main<1, 4>(p, grid, s);
-    else if (U == 2) launch_main<1, 2>(p, grid, s);
-    else launch_main<1, 1>(p, grid, s);
+  dim3 grid((p.n_out + G::ROWS - 1) / G::ROWS, ksw, (p.B + 31) / 32);
+  hipLaunchKernelGGL((mfma_gemm_kernel<NR, WAVES, T>), grid, dim3(G::THREADS), 0, s, p);
+  *ok = true;
+}
+
+// Matrix-core path for bf16 weights, B >= 8, K a multiple of 64 (returns
+// false when it does not apply).  Shapes: SwiGLU 4 waves x 128 rows x (gate,
+// up); tall products (>= 16384 rows, e.g. the tied head) 4 waves x 2 tiles =
+// 256 rows; the rest 2 waves x 64 rows.  `slots` is how many such
+// workgroups the chip holds at once (LDS bound).
+bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
+  if (p0.B < 8 || p0.K % GM_KC != 0 || !p0.part || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
+  GemvParams p = p0;
+  hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
+  bool ok = false;
+  if (p.mode == GEMV_SWIGLU) launch_gm<2, 4, 1>(p, p0.ksw, 256, s, &ok);
+  else if (p.n_out >= 16384) launch_gm<1, 4, 2>(p, p0.ksw, 256, s, &ok);
+  else launch_gm<1, 2, 1>(p, p0.ksw, 512, s, &ok);
+  if (!ok) {
+    *err = hipErrorInvalidValue;
+    return true;
   }
-  if (ksw > 1) {
+  if (p.ksw > 1) {
     const size_t n = (size_t)p.B * p.n_out;
     hipLaunchKernelGGL(mfma_finish_kernel, dim3((unsigned)((n + DUALAR_WG - 1) / DUALAR_WG)), dim3(DUALAR_WG), 0, s, p);
   }
