@@ -36,7 +36,7 @@ class Config(C.Structure):
         "semantic_begin_id", "semantic_end_id", "end_id", "scale_codebook_embeddings")] + [
         ("rope_base", C.c_float), ("norm_eps", C.c_float),
         ("weight_dtype", C.c_int32), ("max_batch", C.c_int32), ("max_seq_len", C.c_int32),
-        ("kv_dtype", C.c_int32)]
+        ("kv_dtype", C.c_int32), ("prefill_chunk", C.c_int32)]
 
 
 _LAYER_FIELDS = ("attention_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w1", "w3", "w2")
@@ -106,9 +106,12 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
-def make_config(m: dict, max_batch: int, max_seq_len: int, inherit_fast: bool = False) -> Config:
+def make_config(m: dict, max_batch: int, max_seq_len: int, inherit_fast: bool = False,
+                prefill_chunk: int = 0) -> Config:
     """Model dict (synth.MODELS layout) -> dualar_config.  With inherit_fast,
-    fast_* sizes are passed as 0 (inherit) where they equal the slow ones."""
+    fast_* sizes are passed as 0 (inherit) where they equal the slow ones.
+    prefill_chunk: prompt positions per sequence per prefill step (0 = the
+    library's choice, 2048 rows per step)."""
     c = Config()
     for f in ("n_layer", "dim", "n_head", "n_kv_head", "head_dim", "ffn_dim", "vocab_size",
               "n_fast_layer", "fast_dim", "fast_n_head", "fast_n_kv_head", "fast_head_dim",
@@ -129,6 +132,7 @@ def make_config(m: dict, max_batch: int, max_seq_len: int, inherit_fast: bool = 
     c.max_seq_len = int(max_seq_len)
     kv = m.get("kv_dtype")
     c.kv_dtype = -1 if kv is None else (BF16 if kv == "bf16" else F32)
+    c.prefill_chunk = prefill_chunk
     return c
 
 
@@ -156,13 +160,13 @@ class DualAR:
     """One decode context (dualar_create) over device weights."""
 
     def __init__(self, m: dict, dev_weights: dict, max_batch: int, max_seq_len: int, stream=None,
-                 inherit_fast: bool = False):
+                 inherit_fast: bool = False, prefill_chunk: int = 0):
         import torch
         self.torch = torch
         self.lib = load_library()
         self.m = m
         self.N = m["num_codebooks"]
-        self.cfg = make_config(m, max_batch, max_seq_len, inherit_fast)
+        self.cfg = make_config(m, max_batch, max_seq_len, inherit_fast, prefill_chunk)
         self.ws_bytes = workspace_bytes(self.cfg)
         if self.ws_bytes == 0:
             raise DualARError(-1, "invalid config")

@@ -35,14 +35,16 @@ struct Resolved {  // config with the inherit-on-unset fallback applied
   float base, eps;
   int dtype, kvdtype, max_batch, max_seq;
   size_t esz, kvesz;
+  int pc;   // prefill: positions per sequence per step (rows = max_batch * pc)
 };
 
 struct Layout {
   size_t kslow, vslow, kfast, vfast, rope_s, rope_f, x_slow, x_fast, qkv, att, ffn, logits, flog, part,
-      xn, gpart, gpart_elems,
+      xn, gpart, gpart_elems, x_pre, ppos, qbuf,
       counters, st_pos, st_done, st_frames, st_cur, st_plen, st_fidx, st_status, total;
   size_t slow_layer_stride, fast_layer_stride;  // elements per layer of a cache
   int max_splits, qkv_ld, att_ld, ffn_ld;
+  int rows;     // activation rows the buffers hold: max(max_batch, max_batch * pc)
 };
 
 bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
@@ -96,6 +98,8 @@ bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
   REQ(r->base > 1.0f && isfinite(r->base), "rope_base must be > 1");
   REQ(r->eps >= 0.0f && isfinite(r->eps), "norm_eps must be >= 0");
   REQ(r->max_batch >= 1 && r->max_batch <= 256, "max_batch out of range [1, 256]");
+  REQ(c->prefill_chunk >= 0 && c->prefill_chunk <= 4096, "prefill_chunk out of range [0, 4096]");
+  r->pc = c->prefill_chunk > 0 ? c->prefill_chunk : std::max(1, 2048 / r->max_batch);
   REQ(r->max_seq >= 2 && r->max_seq <= 65536, "max_seq_len out of range [2, 65536]");
 #undef REQ
   return true;
@@ -119,9 +123,14 @@ Layout layout(const Resolved& r) {
   L.qkv_ld = std::max((r.H + 2 * r.KV) * r.hd, (r.fH + 2 * r.fKV) * r.fhd);
   L.att_ld = std::max(r.H * r.hd, r.fH * r.fhd);
   L.ffn_ld = std::max(r.ffn, r.fffn);
-  L.qkv = take((size_t)r.max_batch * L.qkv_ld * 4);
-  L.att = take((size_t)r.max_batch * L.att_ld * 4);
-  L.ffn = take((size_t)r.max_batch * L.ffn_ld * 4);
+  L.rows = r.max_batch * r.pc;
+  L.qkv = take((size_t)L.rows * L.qkv_ld * 4);
+  L.att = take((size_t)L.rows * L.att_ld * 4);
+  L.ffn = take((size_t)L.rows * L.ffn_ld * 4);
+  // prefill chunk: activations, positions, rotated q of every row
+  L.x_pre = take((size_t)L.rows * r.dim * 4);
+  L.ppos = take((size_t)L.rows * 4);
+  L.qbuf = take((size_t)L.rows * L.att_ld * 4);
   L.logits = take((size_t)r.max_batch * r.V * 4);
   L.flog = take((size_t)r.max_batch * r.C * 4);
   const int maxH = std::max(r.H, r.fH), maxhd = std::max(r.hd, r.fhd);
@@ -129,7 +138,7 @@ Layout layout(const Resolved& r) {
   L.counters = take((size_t)r.max_batch * std::max(r.KV, r.fKV) * 4);
   // matrix-core GEMM scratch: the activations as three bf16 planes (6 bytes
   // per element) and split-K partials (up to 32 splits)
-  L.xn = take((size_t)r.max_batch * std::max(std::max(r.dim, r.ffn), std::max(r.fffn, L.att_ld)) * 6);
+  L.xn = take((size_t)L.rows * std::max(std::max(r.dim, r.ffn), std::max(r.fffn, L.att_ld)) * 6);
   L.gpart_elems = r.max_batch >= 8 ? (size_t)32 * r.max_batch *
                                          std::max(std::max(2 * r.ffn, 2 * r.fffn), std::max(L.qkv_ld, r.dim))
                                    : 0;
@@ -248,9 +257,12 @@ double attn_positions(dualar_ctx* c, int B) {
   return s;
 }
 
+// One transformer layer over B activation rows.  Decode: row b is sequence
+// b at position pos_dev[b] (or pos_const).  Prefill (rows_per_seq > 0): row r
+// is position pos_dev[r] of sequence r / rows_per_seq (-1 = padding).
 template <typename T, typename KT>
 dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const int* pos_dev,
-                        int pos_const, int Lmax) {
+                        int pos_const, int Lmax, int rows_per_seq = 0) {
   const Resolved& r = c->r;
   const Layout& L = c->L;
   const dualar_layer_weights& w = S.lw[l];
@@ -265,6 +277,19 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g.x = x; g.ldx = S.dim; g.gain = w.attention_norm; g.eps = r.eps;
   g.y = qkv; g.ldy = L.qkv_ld; g.B = B; g.mode = GEMV_STORE;
   HIPCHK(gemv<T>(c, g));
+  if (rows_per_seq > 0) {
+    // prefill chunk: QK-norm, RoPE, append for every row, then causal attention
+    PrefillParams a{};
+    a.qkv = qkv; a.ld_qkv = L.qkv_ld;
+    a.qbuf = (float*)(c->ws + L.qbuf); a.ld_q = L.att_ld;
+    a.kcache = S.k + (size_t)l * S.layer_stride * r.kvesz;
+    a.vcache = S.v + (size_t)l * S.layer_stride * r.kvesz;
+    a.max_pos = S.max_pos; a.pos = pos_dev; a.C = rows_per_seq; a.rope = S.rope;
+    a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
+    a.H = S.H; a.KV = S.KV; a.hd = S.hd;
+    a.out = att; a.ld_out = L.att_ld; a.R = B; a.B = B / rows_per_seq;
+    HIPCHK((launch_prefill_attn<T, KT>(a, c->stream)));
+  } else {
   // attention over the cache (+QK-norm, RoPE, append)
   AttnParams a{};
   a.qkv = qkv; a.ld_qkv = L.qkv_ld;
@@ -285,6 +310,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     double pos_sum = pos_dev ? attn_positions(c, B) : (double)B * (pos_const + 1);
     HIPCHK(prof_post(c, DUALAR_K_ATTN, pos_sum * 2.0 * S.KV * S.hd * r.kvesz +
                                            4.0 * B * ((S.H + 2 * S.KV) * S.hd + S.H * S.hd)));
+  }
   }
   // x += Wo . o
   g = GemvParams{};
@@ -388,34 +414,52 @@ dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
   return DUALAR_OK;
 }
 
+// Fused embedding of the slow input.  Decode: one row per sequence into
+// x_slow.  Prefill: rows_per_seq rows per sequence (positions step + i -
+// (t_max - plen[b])) into x_pre, with their positions in ppos.
 template <typename T>
-dualar_status embed(dualar_ctx* c, int B, const int* tokens, int t_max, int step, int prefill) {
+dualar_status embed(dualar_ctx* c, int B, const int* tokens, int t_max, int step, int prefill,
+                    int rows_per_seq = 1) {
   const Resolved& r = c->r;
   EmbedParams e{};
   e.tokens = tokens; e.t_max = t_max; e.step = step; e.prefill = prefill;
+  e.rows_per_seq = rows_per_seq;
+  e.pos_out = prefill ? (int*)(c->ws + c->L.ppos) : nullptr;
   e.tok_emb = c->w.tok_embedding; e.cb_emb = c->w.codebook_embedding;
   e.dim = r.dim; e.V = r.V; e.N = r.N; e.C = r.C; e.sb = r.sb; e.se = r.se; e.scale = r.scale;
-  e.x = (float*)(c->ws + c->L.x_slow); e.B = B; e.st = c->st;
+  e.x = (float*)(c->ws + (prefill ? c->L.x_pre : c->L.x_slow)); e.B = B; e.st = c->st;
   HIPCHK(prof_pre(c, DUALAR_K_EMBED));
   HIPCHK(launch_embed<T>(e, c->stream));
-  HIPCHK(prof_post(c, DUALAR_K_EMBED, (double)B * r.dim * ((r.N + 1) * r.esz + 4)));
+  HIPCHK(prof_post(c, DUALAR_K_EMBED, (double)B * rows_per_seq * r.dim * ((r.N + 1) * r.esz + 4)));
   return DUALAR_OK;
 }
 
+// Prefill: the prompts are right-aligned (sequence b's position t is global
+// step t + t_max - plen[b]) and walked in steps of pc positions, every
+// sequence's pc rows at once, so every prompt ends in the last step.  Its
+// last row per sequence then feeds frame 0.
 template <typename T, typename KT>
 dualar_status do_prefill(dualar_ctx* c, int B, const int* tokens, int t_max, const FrameIO& io) {
-  HIPCHK(launch_prefill_begin(c->st, c->plen.data(), B, c->r.N, c->stream));
-  float* xs = (float*)(c->ws + c->L.x_slow);
+  const Resolved& r = c->r;
+  HIPCHK(launch_prefill_begin(c->st, c->plen.data(), B, r.N, c->stream));
+  const int C = std::min(r.pc, t_max);
+  const int n_steps = (t_max + C - 1) / C;
+  float* xp = (float*)(c->ws + c->L.x_pre);
+  const int* ppos = (const int*)(c->ws + c->L.ppos);
   c->step_pos.assign(B, -1);
-  for (int s = 0; s < t_max; ++s) {
-    for (int b = 0; b < B; ++b) c->step_pos[b] = s - (t_max - c->plen[b]);
-    dualar_status st = embed<T>(c, B, tokens, t_max, s, 1);
+  for (int k = 0; k < n_steps; ++k) {
+    const int s0 = t_max - (n_steps - k) * C;     // global step of row i = 0
+    for (int b = 0; b < B; ++b) c->step_pos[b] = s0 + C - 1 - (t_max - c->plen[b]);
+    dualar_status st = embed<T>(c, B, tokens, t_max, s0, 1, C);
     if (st) return st;
-    for (int l = 0; l < c->r.n_layer; ++l) {
-      st = run_layer<T, KT>(c, c->slow, l, xs, B, c->st.pos, 0, s + 1);
+    for (int l = 0; l < r.n_layer; ++l) {
+      st = run_layer<T, KT>(c, c->slow, l, xp, B * C, ppos, 0, s0 + C, C);
       if (st) return st;
     }
   }
+  // the last row of every sequence is its position plen - 1
+  HIPCHK(hipMemcpy2DAsync(c->ws + c->L.x_slow, (size_t)r.dim * 4, xp + (size_t)(C - 1) * r.dim, (size_t)C * r.dim * 4,
+                          (size_t)r.dim * 4, B, hipMemcpyDeviceToDevice, c->stream));
   return frame_tail<T, KT>(c, B, io);
 }
 

@@ -207,7 +207,15 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_gemm_kernel(GemvParams p) {
   __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[G::STAGE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * G::ROWS, kw = blockIdx.y, b0 = blockIdx.z * 32;
+  int nt = blockIdx.x, kw = blockIdx.y, zt = blockIdx.z;
+  if (p.zswz) {   // one-dimensional grid: id = 8 * (q * zswz + z) + xcd, row block 8 * q + xcd
+    const int id = blockIdx.x, xcd = id & 7, t = id >> 3;
+    nt = 8 * (t / p.zswz) + xcd;
+    zt = t % p.zswz;
+    kw = 0;
+    if (nt * G::ROWS >= p.n_out) return;
+  }
+  const int n0 = nt * G::ROWS, b0 = zt * 32;
   const int Kw = p.K / p.ksw, kbeg = kw * Kw;
   const int nch = Kw / GM_KC;
 
@@ -380,7 +388,7 @@ static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, b
   // buffer holds ksw*B rows): the smallest split that fills the slots while
   // each workgroup keeps >= 4 chunks, else the largest that keeps 4 chunks.
   auto fits = [&](int c) {
-    return p.K % (c * GM_KC) == 0 && (c == 1 || (size_t)c * p.B * p.n_out * NR <= p.part_elems);
+    return p.K % (c * GM_KC) == 0 && (c == 1 || (p.part && (size_t)c * p.B * p.n_out * NR <= p.part_elems));
   };
   int ksw = ksw_preset;
   if (ksw > 0) {
@@ -392,8 +400,18 @@ static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, b
   }
   p.ksw = ksw;
   p.ldp = p.n_out * NR;
-  dim3 grid((p.n_out + G::ROWS - 1) / G::ROWS, ksw, (p.B + 31) / 32);
-  hipLaunchKernelGGL((mfma_gemm_kernel<NR, WAVES, T>), grid, dim3(G::THREADS), 0, s, p);
+  const int n_tiles = (p.n_out + G::ROWS - 1) / G::ROWS, z_tiles = (p.B + 31) / 32;
+  if (ksw == 1 && z_tiles > 1) {
+    // several activation tiles: one-dimensional grid in which the z_tiles
+    // workgroups of a row block are consecutive ids on one XCD (id % 8), so
+    // they run together and share the block's weights through that L2
+    p.zswz = z_tiles;
+    hipLaunchKernelGGL((mfma_gemm_kernel<NR, WAVES, T>), dim3(8 * ((n_tiles + 7) / 8) * z_tiles), dim3(G::THREADS), 0,
+                       s, p);
+  } else {
+    p.zswz = 0;
+    hipLaunchKernelGGL((mfma_gemm_kernel<NR, WAVES, T>), dim3(n_tiles, ksw, z_tiles), dim3(G::THREADS), 0, s, p);
+  }
   *ok = true;
 }
 
@@ -403,7 +421,7 @@ static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, b
 // 256 rows; the rest 2 waves x 64 rows.  `slots` is how many such
 // workgroups the chip holds at once (LDS bound).
 bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
-  if (p0.B < 8 || p0.K % GM_KC != 0 || !p0.part || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
+  if (p0.B < 8 || p0.K % GM_KC != 0 || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
   GemvParams p = p0;
   hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
   bool ok = false;

@@ -27,6 +27,7 @@ struct GemvParams {
   void* xn;
   float* part; size_t part_elems;
   int ksw, ldp;                  // set by the launcher
+  int zswz;                      // set by the launcher: activation tiles of a swizzled 1-D grid (0 = 3-D grid)
 };
 
 // Decode attention for one new position per sequence, split along the
@@ -48,6 +49,25 @@ struct AttnParams {
   unsigned* counters;                 // [B][KV], zero between launches
   float* out; int ld_out;             // [B][H*hd]
   int B;
+};
+
+// Prefill of a chunk of positions: rows r = b*C + i hold position pos[r] of
+// sequence b (-1 = padding).  prefill_append_kernel applies QK-norm and RoPE
+// to every row's q and k, writes q (scaled by 1/sqrt(hd)) to qbuf and
+// appends k, v to the cache; prefill_attn_kernel then attends each row to
+// positions 0..pos[r] of its sequence.
+struct PrefillParams {
+  const float* qkv; int ld_qkv;       // [R][ld]: q | k | v
+  float* qbuf; int ld_q;              // [R][H*hd]
+  void* kcache; void* vcache;         // this layer: [max_batch][KV][max_pos][hd]
+  int max_pos;
+  const int* pos;                     // [R]
+  int C;                              // rows per sequence
+  const float2* rope;                 // [max_pos][hd/2] (cos, sin)
+  const void* q_norm; const void* k_norm; float eps;
+  int H, KV, hd;
+  float* out; int ld_out;             // [R][H*hd]
+  int R, B;
 };
 
 // Per-sequence decode state kept in the workspace.
@@ -79,8 +99,10 @@ struct SampleParams {
 
 struct EmbedParams {
   // source of the token column: prompt tokens (prefill) or the state's last frame
-  const int* tokens; int t_max; int step;   // prefill: step s, row b uses t = s - (t_max - plen[b])
-  int prefill;
+  const int* tokens; int t_max; int step;   // prefill: row r = b*rows_per_seq + i uses
+  int prefill;                              //   t = step + i - (t_max - plen[b])
+  int rows_per_seq;                         // prefill rows per sequence (decode: 1)
+  int* pos_out;                             // prefill: [B*rows_per_seq] t or -1
   const void* tok_emb; const void* cb_emb;
   int dim, V, N, C, sb, se, scale;
   float* x;
@@ -100,6 +122,7 @@ struct FastBeginParams {
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
 bool launch_gemm_mfma(const GemvParams& p, hipStream_t s, hipError_t* err);
 template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+template <typename T, typename KT> hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 template <typename T> hipError_t launch_sample(const SampleParams& p, hipStream_t s);
 template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s);
 template <typename T> hipError_t launch_fast_begin(const FastBeginParams& p, hipStream_t s);

@@ -25,15 +25,24 @@
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(DUALAR_WG) embed_kernel(EmbedParams p) {
-  // grid (B, ceil(dim / 256)): one element of one row per thread
-  const int b = blockIdx.x;
+  // grid (rows, ceil(dim / 256)): one element of one row per thread.  Prefill
+  // row r is position step + i - (t_max - plen[b]) of sequence b
+  // (r = b*rows_per_seq + i); the last row of a sequence also sets its state
+  // position.
+  const int row = blockIdx.x;
+  int b = row;
   const int tid = threadIdx.x;
   int col[33];
   int act = 1;
   if (p.prefill) {
-    const int t = p.step - (p.t_max - p.st.plen[b]);
+    b = row / p.rows_per_seq;
+    const int i = row % p.rows_per_seq;
+    const int t = p.step + i - (p.t_max - p.st.plen[b]);
     act = t >= 0;
-    if (blockIdx.y == 0 && tid == 0) p.st.pos[b] = act ? t : -1;
+    if (blockIdx.y == 0 && tid == 0) {
+      if (p.pos_out) p.pos_out[row] = act ? t : -1;
+      if (i == p.rows_per_seq - 1) p.st.pos[b] = act ? t : -1;
+    }
     if (act)
       for (int r = 0; r <= p.N; ++r) col[r] = p.tokens[((size_t)b * (p.N + 1) + r) * p.t_max + t];
   } else {
@@ -42,7 +51,7 @@ __global__ void __launch_bounds__(DUALAR_WG) embed_kernel(EmbedParams p) {
       for (int r = 0; r <= p.N; ++r) col[r] = p.st.cur[b * (p.N + 1) + r];
   }
   const int d = blockIdx.y * DUALAR_WG + tid;
-  float* x = p.x + (size_t)b * p.dim;
+  float* x = p.x + (size_t)row * p.dim;
   if (!act) {
     if (d < p.dim) x[d] = 0.f;
     return;
@@ -322,7 +331,8 @@ __global__ void prefill_begin_kernel(SeqState st, PlenArg plen, int B, int N) {
 }
 
 template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel<T>, dim3(p.B, (p.dim + DUALAR_WG - 1) / DUALAR_WG), dim3(DUALAR_WG), 0, s, p);
+  const int rows = p.prefill ? p.B * p.rows_per_seq : p.B;
+  hipLaunchKernelGGL(embed_kernel<T>, dim3(rows, (p.dim + DUALAR_WG - 1) / DUALAR_WG), dim3(DUALAR_WG), 0, s, p);
   return hipGetLastError();
 }
 template <typename T> hipError_t launch_sample(const SampleParams& p, hipStream_t s) {

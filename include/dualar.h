@@ -82,6 +82,10 @@ typedef struct {
   int32_t max_batch;             /* sequences held by the workspace             */
   int32_t max_seq_len;           /* slow-AR positions per sequence              */
   int32_t kv_dtype;              /* K/V cache type: dualar_dtype, -1 = weight_dtype */
+  int32_t prefill_chunk;         /* prompt positions per sequence per prefill
+                                    step (0 = max(1, 2048 / max_batch)); the
+                                    workspace holds max_batch * prefill_chunk
+                                    activation rows                             */
 } dualar_config;
 
 /* One transformer layer.  q_norm / k_norm are [head_dim] gains shared by all

@@ -24,7 +24,7 @@ def _dev():
 
 
 def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=REL_L2, min_frames=0,
-                    tag="", weights_f32=None, floor=False):
+                    tag="", weights_f32=None, floor=False, prefill_chunk=0):
     """Prefill + n_frames single-frame decode calls on the GPU; the oracle
     replays every sequence.  Returns per-row counts of frames compared.
 
@@ -38,7 +38,7 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
     greedy = samp["greedy"]
     say(f"[{tag}] GPU: B={B} prompt_len={list(plen)[:8]} frames={n_frames} greedy={greedy}")
     dw = upload(m, w_np)
-    ctx = DualAR(m, dw, max_batch=B, max_seq_len=int(max(plen)) + n_frames + 2)
+    ctx = DualAR(m, dw, max_batch=B, max_seq_len=int(max(plen)) + n_frames + 2, prefill_chunk=prefill_chunk)
     S = DualAR.sampling(min_frames=min_frames, **samp)
     tok = torch.from_numpy(np.ascontiguousarray(prompts)).cuda()
     U = None if uniforms is None else torch.from_numpy(np.ascontiguousarray(uniforms)).cuda()
@@ -183,6 +183,19 @@ def test_tiny_ragged_batch_top_p(tiny):
     c, _ = run_and_compare(m, w, P, plen, 8, dict(greedy=0, temperature=1.0, top_p=0.9), U, tol=1e-4,
                            tag="tiny-topp")
     assert sum(c) >= 30
+
+
+@pytest.mark.parametrize("pc", [1, 3, 16, 64])
+def test_tiny_prefill_chunking(tiny, pc):
+    # Prefill walks the right-aligned prompts pc positions at a time (pc = 1
+    # is the one-position-per-step form; 64 covers the longest prompt in one
+    # step); a chunk's rows attend to earlier rows of the same chunk.
+    m, w = tiny
+    plen = np.array([32, 7, 1, 45, 20], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=9)
+    c, worst = run_and_compare(m, w, P, plen, 3, dict(greedy=1), tol=1e-4, tag=f"tiny-pc{pc}", prefill_chunk=pc)
+    assert sum(c) >= 10
+    assert worst["slow_logits"] < 1e-4
 
 
 def test_tiny_temperature_top_p_half(tiny):
