@@ -40,7 +40,7 @@ struct Resolved {  // config with the inherit-on-unset fallback applied
 
 struct Layout {
   size_t kslow, vslow, kfast, vfast, rope_s, rope_f, x_slow, x_fast, qkv, att, ffn, logits, flog, part,
-      xn, gpart, gpart_elems, x_pre, ppos, qbuf,
+      xn, xn2, gpart, gpart_elems, x_pre, ppos, qbuf,
       counters, st_pos, st_done, st_frames, st_cur, st_plen, st_fidx, st_status, total;
   size_t slow_layer_stride, fast_layer_stride;  // elements per layer of a cache
   int max_splits, qkv_ld, att_ld, ffn_ld;
@@ -139,6 +139,9 @@ Layout layout(const Resolved& r) {
   // matrix-core GEMM scratch: the activations as three bf16 planes (6 bytes
   // per element) and split-K partials (up to 32 splits)
   L.xn = take((size_t)L.rows * std::max(std::max(r.dim, r.ffn), std::max(r.fffn, L.att_ld)) * 6);
+  // planes written by a producer (attention output, SwiGLU output) for the
+  // next product, while xn may still be read
+  L.xn2 = take((size_t)L.rows * std::max(std::max(r.dim, r.ffn), std::max(r.fffn, L.att_ld)) * 6);
   L.gpart_elems = r.max_batch >= 8 ? (size_t)32 * r.max_batch *
                                          std::max(std::max(2 * r.ffn, 2 * r.fffn), std::max(L.qkv_ld, r.dim))
                                    : 0;
@@ -269,6 +272,10 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   float* qkv = (float*)(c->ws + L.qkv);
   float* att = (float*)(c->ws + L.att);
   float* ffn = (float*)(c->ws + L.ffn);
+  // With 8+ rows and bf16 weights the products run on the matrix cores, which
+  // read their input as bf16 planes: the attention and SwiGLU outputs are then
+  // written as planes (xn2) and the next product reads them directly.
+  uint16_t* planes = (sizeof(T) == 2 && B >= 8) ? (uint16_t*)(c->ws + L.xn2) : nullptr;
   GemvParams g{};
   // q | k | v = W_qkv . RMSNorm(x)
   g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
@@ -287,7 +294,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     a.max_pos = S.max_pos; a.pos = pos_dev; a.C = rows_per_seq; a.rope = S.rope;
     a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
     a.H = S.H; a.KV = S.KV; a.hd = S.hd;
-    a.out = att; a.ld_out = L.att_ld; a.R = B; a.B = B / rows_per_seq;
+    a.out = att; a.ld_out = L.att_ld; a.out_planes = planes; a.R = B; a.B = B / rows_per_seq;
     HIPCHK((launch_prefill_attn<T, KT>(a, c->stream)));
   } else {
   // attention over the cache (+QK-norm, RoPE, append)
@@ -302,7 +309,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.lmax = Lmax;
   a.part = (float*)(c->ws + L.part);
   a.counters = (unsigned*)(c->ws + L.counters);
-  a.out = att; a.ld_out = L.att_ld; a.B = B;
+  a.out = att; a.ld_out = L.att_ld; a.out_planes = planes; a.B = B;
   HIPCHK(prof_pre(c, DUALAR_K_ATTN));
   HIPCHK((launch_attn<T, KT>(a, c->stream)));
   if (c->prof_cls == DUALAR_K_ATTN) {
@@ -316,17 +323,20 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g = GemvParams{};
   g.w[0] = w.wo; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.H * S.hd; g.n_out = S.dim;
   g.x = att; g.ldx = L.att_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
+  g.xplanes = planes;
   HIPCHK(gemv<T>(c, g));
   // h = silu(W1 n) * (W3 n), n = RMSNorm(x)
   g = GemvParams{};
   g.w[0] = w.w1; g.w[1] = w.w3; g.rows[0] = S.ffn; g.rows[1] = S.ffn; g.n_seg = 2;
   g.K = S.dim; g.n_out = S.ffn; g.x = x; g.ldx = S.dim; g.gain = w.ffn_norm; g.eps = r.eps;
   g.y = ffn; g.ldy = L.ffn_ld; g.B = B; g.mode = GEMV_SWIGLU;
+  g.yplanes = planes;
   HIPCHK(gemv<T>(c, g));
   // x += W2 . h
   g = GemvParams{};
   g.w[0] = w.w2; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.ffn; g.n_out = S.dim;
   g.x = ffn; g.ldx = L.ffn_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
+  g.xplanes = planes;
   HIPCHK(gemv<T>(c, g));
   return DUALAR_OK;
 }

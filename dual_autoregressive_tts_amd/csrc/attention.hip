@@ -228,7 +228,9 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
     const int hl = i / hd, e = i % hd;
     const float o = (accs[0][hl][e] + accs[1][hl][e]) + (accs[2][hl][e] + accs[3][hl][e]);
     if (n_splits == 1) {
-      p.out[(size_t)b * p.ld_out + (size_t)(g * rep + hl) * hd + e] = o / ml[hl][1];
+      const size_t col = (size_t)(g * rep + hl) * hd + e;
+      if (p.out_planes) store_planes(p.out_planes, (size_t)p.B * p.H * hd, (size_t)b * p.H * hd + col, o / ml[hl][1]);
+      else p.out[(size_t)b * p.ld_out + col] = o / ml[hl][1];
     } else {
       float* pp = p.part + (((size_t)b * p.H + g * rep + hl) * p.max_splits + split) * (hd + 2);
       pp[e] = o;
@@ -283,7 +285,8 @@ __global__ void __launch_bounds__(MERGE_T) attn_merge_kernel(AttnParams p) {
     for (int i = 0; i < 16; ++i)
       if (s0 + i < n_splits) o = fmaf(ov[i], wsh[s0 + i], o);
   }
-  p.out[(size_t)b * p.ld_out + (size_t)h * hd + t] = o / lsum;
+  if (p.out_planes) store_planes(p.out_planes, (size_t)p.B * p.H * hd, (size_t)b * p.H * hd + (size_t)h * hd + t, o / lsum);
+  else p.out[(size_t)b * p.ld_out + (size_t)h * hd + t] = o / lsum;
 }
 
 int attn_chunk(int kv_esz, int hd, int it) {

@@ -19,6 +19,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// v as three bf16 terms t0 + t1 + t2 (+ a residual below 2^-24 |v|) at
+// base[at], base[plane + at], base[2*plane + at]: the activation planes read
+// by the matrix-core products.
+__device__ __forceinline__ void store_planes(uint16_t* base, size_t plane, size_t at, float v) {
+  const uint16_t a0 = f32_to_bf16_rne(v);
+  const float r1 = v - bf16_bits_to_f32(a0);
+  const uint16_t a1 = f32_to_bf16_rne(r1);
+  base[at] = a0;
+  base[plane + at] = a1;
+  base[2 * plane + at] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(a1));
+}
+
 // Element-type traits: a 16-byte vector holds EPV elements.
 template <typename T> struct ElemT;
 template <> struct ElemT<float> {

@@ -280,7 +280,8 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_gemm_kernel(GemvParams p) {
         if (p.mode == GEMV_SWIGLU) out = silu_f(v[0]) * v[NR - 1];
         else if (p.mode == GEMV_ADD) out = p.res[(size_t)b * p.ldres + n] + v[0];
         else out = v[0];
-        p.y[(size_t)b * p.ldy + n] = out;
+        if (p.yplanes) store_planes((uint16_t*)p.yplanes, (size_t)p.B * p.n_out, (size_t)b * p.n_out + n, out);
+        else p.y[(size_t)b * p.ldy + n] = out;
       }
     }
   }
@@ -319,7 +320,8 @@ __global__ void __launch_bounds__(DUALAR_WG) mfma_finish_kernel(GemvParams p) {
   if (glu) out = silu_f(v0) * v1;
   else if (p.mode == GEMV_ADD) out = r + v0;
   else out = v0;
-  p.y[(size_t)b * p.ldy + n] = out;
+  if (p.yplanes) store_planes((uint16_t*)p.yplanes, (size_t)p.B * p.n_out, (size_t)b * p.n_out + n, out);
+  else p.y[(size_t)b * p.ldy + n] = out;
 }
 
 #define NORM_MAXV 12   // float4s per thread: K <= 12288
@@ -423,7 +425,8 @@ static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, b
 bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   if (p0.B < 8 || p0.K % GM_KC != 0 || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
   GemvParams p = p0;
-  hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
+  if (p.xplanes) p.xn = const_cast<void*>(p.xplanes);   // input already split by its producer
+  else hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
   bool ok = false;
   if (p.mode == GEMV_SWIGLU) launch_gm<2, 4, 1>(p, p0.ksw, 256, s, &ok);
   else if (p.n_out >= 16384) launch_gm<1, 4, 2>(p, p0.ksw, 256, s, &ok);

@@ -26,6 +26,11 @@ struct GemvParams {
   // partial sums (part_elems floats)
   void* xn;
   float* part; size_t part_elems;
+  // matrix-core path only: xplanes = the input already as planes [3][B][K]
+  // (no RMSNorm; x and xn unused); yplanes = write the output as planes
+  // [3][B][n_out] instead of y (GEMV_STORE / GEMV_SWIGLU)
+  const void* xplanes;
+  void* yplanes;
   int ksw, ldp;                  // set by the launcher
   int zswz;                      // set by the launcher: activation tiles of a swizzled 1-D grid (0 = 3-D grid)
 };
@@ -48,6 +53,7 @@ struct AttnParams {
   float* part;                        // [B][H][max_splits][hd + 2]
   unsigned* counters;                 // [B][KV], zero between launches
   float* out; int ld_out;             // [B][H*hd]
+  uint16_t* out_planes;               // if set: o as planes [3][B][H*hd] instead of out
   int B;
 };
 
@@ -67,6 +73,7 @@ struct PrefillParams {
   const void* q_norm; const void* k_norm; float eps;
   int H, KV, hd;
   float* out; int ld_out;             // [R][H*hd]
+  uint16_t* out_planes;               // if set: o as planes [3][R][H*hd] instead of out
   int R, B;
 };
 

@@ -166,6 +166,18 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillParams p) {
   }
   if (pos < 0) return;
   const float inv = 1.0f / l;
+  if (p.out_planes) {
+    const size_t plane = (size_t)p.R * p.H * hd, at = (size_t)r * p.H * hd + (size_t)h * hd;
+#pragma unroll
+    for (int e = 0; e < E4; ++e)
+      if (e < ne4) {
+        store_planes(p.out_planes, plane, at + 16 * e + 4 * sl + 0, o[e].x * inv);
+        store_planes(p.out_planes, plane, at + 16 * e + 4 * sl + 1, o[e].y * inv);
+        store_planes(p.out_planes, plane, at + 16 * e + 4 * sl + 2, o[e].z * inv);
+        store_planes(p.out_planes, plane, at + 16 * e + 4 * sl + 3, o[e].w * inv);
+      }
+    return;
+  }
   float* dst = p.out + (size_t)r * p.ld_out + (size_t)h * hd;
 #pragma unroll
   for (int e = 0; e < E4; ++e)
