@@ -263,9 +263,13 @@ double attn_positions(dualar_ctx* c, int B) {
 // One transformer layer over B activation rows.  Decode: row b is sequence
 // b at position pos_dev[b] (or pos_const).  Prefill (rows_per_seq > 0): row r
 // is position pos_dev[r] of sequence r / rows_per_seq (-1 = padding).
+//
+// in_planes: on entry, the previous layer already wrote RMSNorm(x) with this
+// layer's attention gain as planes (xn), so the QKV product reads them; on
+// exit, whether this layer did the same for layer l + 1.
 template <typename T, typename KT>
 dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const int* pos_dev,
-                        int pos_const, int Lmax, int rows_per_seq = 0) {
+                        int pos_const, int Lmax, bool& in_planes, int rows_per_seq = 0) {
   const Resolved& r = c->r;
   const Layout& L = c->L;
   const dualar_layer_weights& w = S.lw[l];
@@ -276,6 +280,10 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   // read their input as bf16 planes: the attention and SwiGLU outputs are then
   // written as planes (xn2) and the next product reads them directly.
   uint16_t* planes = (sizeof(T) == 2 && B >= 8) ? (uint16_t*)(c->ws + L.xn2) : nullptr;
+  // The residual products (O, W2) split K over workgroups at these sizes; their
+  // finish then also writes the next product's normalised input planes (xn).
+  void* const xn = c->ws + L.xn;
+  int fused = 0;
   GemvParams g{};
   // q | k | v = W_qkv . RMSNorm(x)
   g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
@@ -283,6 +291,8 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g.K = S.dim; g.n_out = (S.H + 2 * S.KV) * S.hd;
   g.x = x; g.ldx = S.dim; g.gain = w.attention_norm; g.eps = r.eps;
   g.y = qkv; g.ldy = L.qkv_ld; g.B = B; g.mode = GEMV_STORE;
+  if (planes && in_planes) g.xplanes = xn;
+  in_planes = false;
   HIPCHK(gemv<T>(c, g));
   if (rows_per_seq > 0) {
     // prefill chunk: QK-norm, RoPE, append for every row, then causal attention
@@ -324,6 +334,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g.w[0] = w.wo; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.H * S.hd; g.n_out = S.dim;
   g.x = att; g.ldx = L.att_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
   g.xplanes = planes;
+  if (planes) { g.next_gain = w.ffn_norm; g.next_planes = xn; g.next_done = &fused; g.eps = r.eps; }
   HIPCHK(gemv<T>(c, g));
   // h = silu(W1 n) * (W3 n), n = RMSNorm(x)
   g = GemvParams{};
@@ -331,13 +342,19 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g.K = S.dim; g.n_out = S.ffn; g.x = x; g.ldx = S.dim; g.gain = w.ffn_norm; g.eps = r.eps;
   g.y = ffn; g.ldy = L.ffn_ld; g.B = B; g.mode = GEMV_SWIGLU;
   g.yplanes = planes;
+  if (fused) g.xplanes = xn;
   HIPCHK(gemv<T>(c, g));
   // x += W2 . h
   g = GemvParams{};
   g.w[0] = w.w2; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.ffn; g.n_out = S.dim;
   g.x = ffn; g.ldx = L.ffn_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
   g.xplanes = planes;
+  fused = 0;
+  if (planes && l + 1 < S.n_layer) {
+    g.next_gain = S.lw[l + 1].attention_norm; g.next_planes = xn; g.next_done = &fused; g.eps = r.eps;
+  }
   HIPCHK(gemv<T>(c, g));
+  in_planes = fused != 0;
   return DUALAR_OK;
 }
 
@@ -400,13 +417,15 @@ dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
     HIPCHK(sample<T>(c, sample_params<T>(c, io, B, 1, 0, xf)));
   }
   // fast pass 0: the slow hidden state at depth position 0
+  bool pl = false;
   for (int l = 0; l < r.fn_layer; ++l) {
-    dualar_status st = run_layer<T, KT>(c, c->fast, l, xs, B, nullptr, 0, 1);
+    dualar_status st = run_layer<T, KT>(c, c->fast, l, xs, B, nullptr, 0, 1, pl);
     if (st) return st;
   }
   for (int k = 1; k < r.N; ++k) {
+    pl = false;
     for (int l = 0; l < r.fn_layer; ++l) {
-      dualar_status st = run_layer<T, KT>(c, c->fast, l, xf, B, nullptr, k, k + 1);
+      dualar_status st = run_layer<T, KT>(c, c->fast, l, xf, B, nullptr, k, k + 1, pl);
       if (st) return st;
     }
     GemvParams g{};
@@ -462,8 +481,9 @@ dualar_status do_prefill(dualar_ctx* c, int B, const int* tokens, int t_max, con
     for (int b = 0; b < B; ++b) c->step_pos[b] = s0 + C - 1 - (t_max - c->plen[b]);
     dualar_status st = embed<T>(c, B, tokens, t_max, s0, 1, C);
     if (st) return st;
+    bool pl = false;
     for (int l = 0; l < r.n_layer; ++l) {
-      st = run_layer<T, KT>(c, c->slow, l, xp, B * C, ppos, 0, s0 + C, C);
+      st = run_layer<T, KT>(c, c->slow, l, xp, B * C, ppos, 0, s0 + C, pl, C);
       if (st) return st;
     }
   }
@@ -489,8 +509,9 @@ dualar_status do_decode(dualar_ctx* c, int n_frames, const FrameIO& io) {
     const int Lmax = maxp + c->frames_done + f + 1;
     c->step_pos.resize(B);
     for (int b = 0; b < B; ++b) c->step_pos[b] = c->plen[b] + c->frames_done + f;
+    bool pl = false;
     for (int l = 0; l < c->r.n_layer; ++l) {
-      st = run_layer<T, KT>(c, c->slow, l, xs, B, c->st.pos, 0, Lmax);
+      st = run_layer<T, KT>(c, c->slow, l, xs, B, c->st.pos, 0, Lmax, pl);
       if (st) return st;
     }
     FrameIO fio = io;

@@ -382,6 +382,83 @@ __global__ void __launch_bounds__(DUALAR_WG) xsplit_kernel(GemvParams p) {
   }
 }
 
+// Split-K finish of a residual product fused with the next product's input
+// preparation, one workgroup per row b (n_out <= 4096): out = res +
+// sum_kw part[kw] (the partials added in kw order, as in mfma_finish_kernel,
+// loaded six splits at a time), written to y; then
+// out / sqrt(mean(out^2) + eps) * next_gain split into three bf16 planes
+// (plane stride B*n_out).
+__global__ void __launch_bounds__(DUALAR_WG) finish_split_kernel(GemvParams p) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float red[4];
+  const int nv = p.n_out / 4;
+  constexpr int J = 4;              // float4s per thread: n_out <= 4096 on this path
+  constexpr int KB = 6;             // partials loaded together
+  float4 v[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* pb = p.part + (size_t)b * p.ldp;
+  const size_t kstride = (size_t)p.B * p.ldp;
+  for (int k0 = 0; k0 < p.ksw; k0 += KB) {
+    float4 q[KB][J];
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int k = tid + j * DUALAR_WG;
+        q[u][j] = (k0 + u < p.ksw && k < nv) ? *(const float4*)(pb + (k0 + u) * kstride + 4 * k)
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int u = 0; u < KB; ++u)       // kw order, as in mfma_finish_kernel
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (k0 + u < p.ksw) { v[j].x += q[u][j].x; v[j].y += q[u][j].y; v[j].z += q[u][j].z; v[j].w += q[u][j].w; }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int k = tid + j * DUALAR_WG;
+    if (k < nv) {
+      const float4 r = *(const float4*)(p.res + (size_t)b * p.ldres + 4 * k);
+      float4 a = v[j];
+      a.x = r.x + a.x; a.y = r.y + a.y; a.z = r.z + a.z; a.w = r.w + a.w;
+      *(float4*)(p.y + (size_t)b * p.ldy + 4 * k) = a;
+      ss += (a.x * a.x + a.y * a.y) + (a.z * a.z + a.w * a.w);
+      v[j] = a;
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)p.n_out + p.eps);
+  const uint2* g = (const uint2*)p.next_gain;
+  uint2* xs = (uint2*)p.next_planes;
+  const size_t plane = (size_t)p.B * nv;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int k = tid + j * DUALAR_WG;
+    if (k < nv) {
+      const uint2 gg = g[k];
+      float o[4] = {v[j].x * inv * bf16_bits_to_f32(gg.x & 0xffffu), v[j].y * inv * bf16_bits_to_f32(gg.x >> 16),
+                    v[j].z * inv * bf16_bits_to_f32(gg.y & 0xffffu), v[j].w * inv * bf16_bits_to_f32(gg.y >> 16)};
+      uint32_t t[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t a0 = f32_to_bf16_rne(o[e]);
+        const float r1 = o[e] - bf16_bits_to_f32(a0);
+        const uint16_t a1 = f32_to_bf16_rne(r1);
+        t[0][e] = a0;
+        t[1][e] = a1;
+        t[2][e] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(a1));
+      }
+      const size_t at = (size_t)b * nv + k;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) xs[q * plane + at] = make_uint2(t[q][0] | (t[q][1] << 16), t[q][2] | (t[q][3] << 16));
+    }
+  }
+}
+
 template <int NR, int WAVES, int T>
 static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, bool* ok) {
   using G = Gm<NR, WAVES, T>;
@@ -435,7 +512,12 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
     *err = hipErrorInvalidValue;
     return true;
   }
-  if (p.ksw > 1) {
+  const bool fuse_next = p.next_planes && p.mode == GEMV_ADD && p.ksw > 1 && p.n_out % 4 == 0 &&
+                        p.n_out <= 4 * 4 * DUALAR_WG;
+  if (p.next_done) *p.next_done = fuse_next ? 1 : 0;
+  if (fuse_next) {
+    hipLaunchKernelGGL(finish_split_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
+  } else if (p.ksw > 1) {
     const size_t n = (size_t)p.B * p.n_out;
     hipLaunchKernelGGL(mfma_finish_kernel, dim3((unsigned)((n + DUALAR_WG - 1) / DUALAR_WG)), dim3(DUALAR_WG), 0, s, p);
   }

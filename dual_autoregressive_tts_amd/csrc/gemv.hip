@@ -532,6 +532,7 @@ template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s)
     if (launch_gemm_mfma(p, s, &e)) return e;   // 8+ activation rows on the matrix cores
   }
   if (p.xplanes || p.yplanes) return hipErrorInvalidValue;   // planes exist on the matrix-core path only
+  if (p.next_done) *p.next_done = 0;
   if (p.mode == GEMV_SWIGLU) return pick_bt<T, 2>(p, s);
   return pick_bt<T, 1>(p, s);
 }

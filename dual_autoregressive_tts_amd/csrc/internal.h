@@ -31,6 +31,10 @@ struct GemvParams {
   // [3][B][n_out] instead of y (GEMV_STORE / GEMV_SWIGLU)
   const void* xplanes;
   void* yplanes;
+  // GEMV_ADD with split-K partials only: also RMS-normalise each output row
+  // with next_gain and write it as planes [3][B][n_out] for the next
+  // product; *next_done is set to 1 when this happened (else 0)
+  const void* next_gain; void* next_planes; int* next_done;
   int ksw, ldp;                  // set by the launcher
   int zswz;                      // set by the launcher: activation tiles of a swizzled 1-D grid (0 = 3-D grid)
 };
