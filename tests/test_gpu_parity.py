@@ -417,6 +417,23 @@ def test_s2_full_fp32_kv_strict(s2_full):
     assert max(worst.values()) < 2e-4
 
 
+@pytest.mark.timeout(900)
+def test_s2_full_batch8_matrix_cores(s2_full):
+    # Batch 8 of the full S2 shapes: every product on the matrix cores (the
+    # tied head as 4-wave x 2-tile blocks, split-K with fused finish + norm
+    # across the 36 slow layers), chunked prefill of ragged prompts, top-p on
+    # the 4,097 slow candidates.  fp32 K/V keeps the plain 2e-3 bar.
+    m, w = s2_full
+    m = dict(m, kv_dtype="f32")
+    plen = np.array([24, 9, 17, 3, 24, 12, 20, 6], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=8)
+    U = synth.make_uniforms((3, 8, m["num_codebooks"]), seed=8)
+    c, worst = run_and_compare(m, w, P, plen, 2, dict(greedy=0, temperature=1.0, top_p=0.9), U,
+                               tag="s2-full-b8")
+    assert sum(c) >= 8
+    assert max(worst.values()) < 2e-3
+
+
 @pytest.mark.timeout(600)
 def test_s2_full_bf16_kv(s2_full):
     m, w = s2_full
