@@ -132,6 +132,82 @@ __device__ __forceinline__ int block_count(int c, int* sh) {
   return r;
 }
 
+// Top-p order: sort the candidates' e = exp((z - zmax) / T) by (e desc, index
+// asc) into ev/ix (NP = 1024*E entries, padding e = 0).  Bitonic network on
+// 64-bit keys (e bits << 16 | 0xffff - index: larger key first), E
+// consecutive entries per thread held in registers: strides below E are
+// swapped in registers, strides below 64*E with lane shuffles inside the
+// wave, and only the larger ones go through LDS with a barrier.
+template <int E, class CandId, class CandOk>
+__device__ __forceinline__ void topp_sort(const float* z, const SampleParams& p, int nc, float zmax, float invT,
+                                          float* ev, uint16_t* ix, CandId cand_id, CandOk cand_ok) {
+  constexpr int NP = SMP_THREADS * E;
+  const int tid = threadIdx.x;
+  uint64_t key[E];
+#pragma unroll
+  for (int s = 0; s < E; ++s) {
+    const int i = tid * E + s;
+    float e = 0.f;
+    if (i < nc && cand_ok(i)) e = expf((z[cand_id(i)] - zmax) * invT);
+    key[s] = ((uint64_t)__float_as_uint(e) << 16) | (uint64_t)(0xffffu - (unsigned)i);
+  }
+  uint32_t* kh = (uint32_t*)ev;          // exchange area: high words in ev, low 16 bits in ix
+  for (int kk = 2; kk <= NP; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+          const int sp = s ^ j;
+          if (sp > s) {
+            const int i = tid * E + s;
+            const bool first = (i & kk) == 0;      // this run in target order
+            const uint64_t a = key[s], b = key[sp];
+            if ((a < b) == first) { key[s] = b; key[sp] = a; }
+          }
+        }
+      } else {
+        const int tj = j / E;                     // partner thread = tid ^ tj
+        uint64_t other[E];
+        if (tj < 64) {
+#pragma unroll
+          for (int s = 0; s < E; ++s) {
+            const unsigned lo = __shfl_xor((unsigned)key[s], tj);
+            const unsigned hi = __shfl_xor((unsigned)(key[s] >> 32), tj);
+            other[s] = ((uint64_t)hi << 32) | lo;
+          }
+        } else {
+          __syncthreads();
+#pragma unroll
+          for (int s = 0; s < E; ++s) {
+            kh[tid * E + s] = (uint32_t)(key[s] >> 16);
+            ix[tid * E + s] = (uint16_t)(key[s] & 0xffffu);
+          }
+          __syncthreads();
+          const int pt = tid ^ tj;
+#pragma unroll
+          for (int s = 0; s < E; ++s) other[s] = ((uint64_t)kh[pt * E + s] << 16) | ix[pt * E + s];
+        }
+        const bool lower = (tid & tj) == 0;        // I hold the lower index of each pair
+#pragma unroll
+        for (int s = 0; s < E; ++s) {
+          const int i = tid * E + s;
+          const bool first = (i & kk) == 0;
+          const uint64_t a = key[s], b = other[s];
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          key[s] = (lower == first) ? hi : lo;
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < E; ++s) {
+    ev[tid * E + s] = __uint_as_float((uint32_t)(key[s] >> 16));
+    ix[tid * E + s] = (uint16_t)(0xffffu - (unsigned)(key[s] & 0xffffu));
+  }
+  __syncthreads();
+}
+
 template <typename T>
 __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
   const int b = blockIdx.x;
@@ -184,33 +260,9 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
     while (NP < nc) NP <<= 1;
     const float zmax = best.v;
     const float invT = 1.0f / p.temperature;
-    for (int i = tid; i < NP; i += SMP_THREADS) {
-      float e = 0.f;
-      if (i < nc && cand_ok(i)) e = expf((z[cand_id(i)] - zmax) * invT);
-      ev[i] = e;
-      ix[i] = (uint16_t)i;
-    }
-    __syncthreads();
-    // bitonic sort, order: e descending, then index ascending
-    for (int kk = 2; kk <= NP; kk <<= 1) {
-      for (int j = kk >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < NP; i += SMP_THREADS) {
-          const int l = i ^ j;
-          if (l > i) {
-            const float ei = ev[i], el = ev[l];
-            const int ii = ix[i], il = ix[l];
-            // "i before l" under the target order
-            const bool i_first = (ei > el) || (ei == el && ii < il);
-            const bool up = (i & kk) == 0;   // this run sorted in target order
-            if (up != i_first) {
-              ev[i] = el; ev[l] = ei;
-              ix[i] = (uint16_t)il; ix[l] = (uint16_t)ii;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
+    if (NP < SMP_THREADS * 4) NP = SMP_THREADS * 4;
+    if (NP == SMP_THREADS * 4) topp_sort<4>(z, p, nc, zmax, invT, ev, ix, cand_id, cand_ok);
+    else topp_sort<8>(z, p, nc, zmax, invT, ev, ix, cand_id, cand_ok);
     // inclusive scan: each thread owns NP/1024 consecutive entries (or one)
     const int per = NP >= SMP_THREADS ? NP / SMP_THREADS : 1;
     const int beg = tid * per;
