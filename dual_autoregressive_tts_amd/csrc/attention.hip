@@ -26,7 +26,16 @@
 #define ATT_MAXCH 256
 #define ATT_MAXSPLIT 4096   // max_seq_len <= 65536 and chunks of >= 16 positions
 
-template <typename T, typename KT, int IT, int REP>
+typedef __bf16 att_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float att_f32x4 __attribute__((ext_vector_type(4)));
+
+// MQK (bf16 cache, head_dim 128, IT = 4 or 8): the scores come from
+// v_mfma_f32_16x16x32_bf16 with 16 cache positions as the A operand (lane l:
+// position l%16, dims 8*(l/16)..+8 of a 32-dim step, read straight from the
+// cache) and the rep query heads as the B operand (three bf16 terms of the
+// fp32 q, so the product is the fp32 one), instead of per-lane dot products
+// and 16-lane reductions.  The V side is unchanged.
+template <typename T, typename KT, int IT, int REP, bool MQK = false>
 __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int pos = p.pos ? p.pos[b] : p.pos_const;
@@ -49,6 +58,8 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
   __shared__ float sc[REP][ATT_MAXCH];
   __shared__ float accs[4][REP][ATT_MAXHD];
   __shared__ float ml[REP][2];
+  constexpr int GW = MQK ? IT / 4 : 1;        // MQK: 16-position groups per wave
+  __shared__ __attribute__((aligned(16))) uint16_t qp[MQK ? 3 : 1][REP][MQK ? ATT_MAXHD : 1];
 
   const size_t head_base = ((size_t)b * p.KV + g) * p.max_pos;
   const char* kbase = (const char*)p.kcache + head_base * hd * sizeof(KT);
@@ -59,13 +70,26 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
   // appended, read entry 0 of this head instead and discard it.
   u32x4 kr[IT], vr[IT];
   int jj[IT];
+  u32x4 kq[GW][4];
+  int kpos[GW];
+  if constexpr (MQK) {
+#pragma unroll
+    for (int mm = 0; mm < GW; ++mm) {
+      const int j = c0 + 16 * (wave + 4 * mm) + (lane & 15);
+      kpos[mm] = j;
+      const bool ok = j < c1 && j != pos;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kq[mm][ks] = ld_vec(kbase + ((size_t)(ok ? j : 0) * hd + 32 * ks + 8 * (lane >> 4)) * sizeof(KT));
+    }
+  }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int j = c0 + (it * 4 + wave) * PPW + grp;
     jj[it] = j;
     const bool ok = j < c1 && j != pos;
     const size_t off = ((size_t)(ok ? j : 0) * hd + sub * EPL) * sizeof(KT);
-    kr[it] = ld_vec(kbase + off);
+    if constexpr (!MQK) kr[it] = ld_vec(kbase + off);
     vr[it] = ld_vec(vbase + off);
   }
 
@@ -148,6 +172,47 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
   __syncthreads();
 
   // ---- 4a. scores ----
+  if constexpr (MQK) {
+    // q as three bf16 planes (rep rows), then 3 MFMAs per 32-dim step
+    for (int i = tid; i < rep * ATT_MAXHD; i += DUALAR_WG) {
+      const int hl = i / ATT_MAXHD, d = i % ATT_MAXHD;
+      const float v = qs[hl][d];
+      const uint16_t a0 = f32_to_bf16_rne(v);
+      const float r1 = v - bf16_bits_to_f32(a0);
+      const uint16_t a1 = f32_to_bf16_rne(r1);
+      qp[0][hl][d] = a0;
+      qp[1][hl][d] = a1;
+      qp[2][hl][d] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(a1));
+    }
+    __syncthreads();
+    const int col = lane & 15;                  // query head (B column)
+    const bool live_col = col < rep;
+#pragma unroll
+    for (int mm = 0; mm < GW; ++mm) {
+      att_f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        att_bf16x8 a = __builtin_bit_cast(att_bf16x8, kq[mm][ks]);
+        if (kpos[mm] == pos) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] = (__bf16)knew[32 * ks + 8 * (lane >> 4) + e];
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 bq = live_col ? *(const u32x4*)&qp[q][live_col ? col : 0][32 * ks + 8 * (lane >> 4)] : z;
+          acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(att_bf16x8, bq), acc4, 0, 0, 0);
+        }
+      }
+      if (live_col) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = c0 + 16 * (wave + 4 * mm) + 4 * (lane >> 4) + r;
+          if (j < c1) sc[col][j - c0] = acc4[r];
+        }
+      }
+    }
+  } else {
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int j = jj[it];
@@ -166,6 +231,7 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
       d = group_sum(d, LPP);
       if (sub == 0 && j < c1) sc[hl][j - c0] = d;
     }
+  }
   }
   __syncthreads();
 
@@ -300,7 +366,15 @@ template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p0, 
   p.max_splits = (p.lmax + p.chunk - 1) / p.chunk;
   dim3 grid(p.max_splits, p.KV, p.B);
   const int rep = p.H / p.KV;
-#define ATT_GO(IT, REP) hipLaunchKernelGGL((attn_partial_kernel<T, KT, IT, REP>), grid, dim3(DUALAR_WG), 0, s, p)
+  // the matrix-core score path: bf16 cache, head_dim 128, 4+ loads per lane
+  const bool mqk = sizeof(KT) == 2 && p.hd == 128 && p.it >= 4;
+#define ATT_GO(IT, REP)                                                                                      \
+  do {                                                                                                       \
+    if constexpr (sizeof(KT) == 2 && IT >= 4) {                                                              \
+      if (mqk) { hipLaunchKernelGGL((attn_partial_kernel<T, KT, IT, REP, true>), grid, dim3(DUALAR_WG), 0, s, p); break; } \
+    }                                                                                                        \
+    hipLaunchKernelGGL((attn_partial_kernel<T, KT, IT, REP>), grid, dim3(DUALAR_WG), 0, s, p);               \
+  } while (0)
 #define ATT_REP(IT)                       \
   if (rep == 1) ATT_GO(IT, 1);            \
   else if (rep == 2) ATT_GO(IT, 2);       \

@@ -394,10 +394,12 @@ class DualAROracle:
     def fast_logits(self, x):
         return self.w["fast_output"] @ rms_norm(x, self.w["fast_norm"], self.eps)
 
-    def fast_frame(self, h_slow, q0: int, s: Sampling, u=None):
+    def fast_frame(self, h_slow, q0: int, s: Sampling, u=None, force=None):
         """Ten (N) fast passes for one frame: pass 0 writes h_slow into slot 0
         (its output is not used); pass k = 1..N-1 embeds q^(k-1) at position k
-        and samples q^(k) from the unmasked fast head.  Returns q^(0..N-1)."""
+        and samples q^(k) from the unmasked fast head.  Returns q^(0..N-1).
+        force: codes q^(0..N-1) to take instead of sampling (the logits are
+        still computed), so that another evaluation can follow this path."""
         F = self.fast
         Kf = np.zeros((F.n_layer, self.N, F.n_kv_head, F.head_dim), dtype=self.dt)
         Vf = np.zeros_like(Kf)
@@ -409,7 +411,7 @@ class DualAROracle:
             x = self._fast_pass(x, k, Kf, Vf)
             lg = self.fast_logits(x)
             flog.append(lg)
-            codes.append(sample_token(lg, s, None if u is None else u[k]))
+            codes.append(int(force[k]) if force is not None else sample_token(lg, s, None if u is None else u[k]))
             self.count.fast_samples += 1
         self.taps["fast_logits"] = np.array(flog)
         return codes
@@ -428,30 +430,32 @@ class DualAROracle:
         return np.array([self.fast_logits(X[k]) for k in range(1, self.N)])
 
     # --- one frame: slow pass -> biased sample -> fast loop ----------------
-    def _finish_frame(self, seq: SeqState, h, s: Sampling, u):
+    def _finish_frame(self, seq: SeqState, h, s: Sampling, u, force=None):
         logits = self.slow_logits(h)
         self.taps["slow_hidden"] = h
         self.taps["slow_logits"] = logits
-        ident = self.slow_sample(logits, s, None if u is None else u[0], seq.frames)
+        ident = int(force[0]) if force is not None else \
+            self.slow_sample(logits, s, None if u is None else u[0], seq.frames)
         if ident == self.end:
             seq.done = True
             return [ident] + [-1] * self.N
-        codes = self.fast_frame(h, ident - self.sb, s, u)
+        codes = self.fast_frame(h, ident - self.sb, s, u, None if force is None else force[1:])
         frame = [ident] + codes
         seq.next_col = np.array(frame)
         seq.frames += 1
         return frame
 
-    def prefill(self, seq: SeqState, prompt, s: Sampling, u=None):
+    def prefill(self, seq: SeqState, prompt, s: Sampling, u=None, force=None):
         """Run the slow AR over a prompt [N+1][P] (causal, all positions at
-        once) and emit frame 0 from the last position."""
+        once) and emit frame 0 from the last position (force: take that frame
+        instead of sampling it)."""
         prompt = np.asarray(prompt)
         P = prompt.shape[1]
         X = np.stack([self.embed(prompt[:, t]) for t in range(P)])
         H = self.slow_seq(seq, X, 0)
         self.count.slow_passes += 1
         seq.pos = P
-        return self._finish_frame(seq, H[-1], s, u)
+        return self._finish_frame(seq, H[-1], s, u, force)
 
     def prefill_stepwise(self, seq: SeqState, prompt, s: Sampling, u=None):
         """Same as `prefill`, one position at a time through the cache."""
@@ -462,13 +466,14 @@ class DualAROracle:
         seq.pos = P
         return self._finish_frame(seq, h, s, u)
 
-    def decode_frame(self, seq: SeqState, s: Sampling, u=None):
+    def decode_frame(self, seq: SeqState, s: Sampling, u=None, force=None):
         """One frame: fuse the previous frame, one slow pass at the next
-        position, biased sample, fast loop."""
+        position, biased sample, fast loop (force: take this frame instead of
+        sampling it)."""
         if seq.done:
             return [-1] * (self.N + 1)
         x = self.embed(seq.next_col)
         self.taps["fused_x"] = x
         h = self.slow_step(seq, x, seq.pos)
         seq.pos += 1
-        return self._finish_frame(seq, h, s, u)
+        return self._finish_frame(seq, h, s, u, force)

@@ -79,16 +79,16 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
             bound = dict.fromkeys(worst, tol)
             bound["fused_x"] = 1e-5
             if floor and in_step:
-                o32fr = o32.prefill(seq32, prompts[b][:, :plen[b]], osamp, None if u is None else u[0]) if f == 0 \
-                    else o32.decode_frame(seq32, osamp, None if u is None else u[f])
+                # the fp32 oracle takes the fp64 oracle's ids (its own draws may
+                # flip on near-ties), so both evaluate the same path
+                o32fr = o32.prefill(seq32, prompts[b][:, :plen[b]], osamp, None if u is None else u[0], force=ofr) \
+                    if f == 0 else o32.decode_frame(seq32, osamp, None if u is None else u[f], force=ofr)
                 if ofr[0] != -1:
                     for k in ("fused_x", "slow_hidden", "slow_logits"):
                         if k in o.taps and k in o32.taps and (f > 0 or k != "fused_x"):
                             fl[k] = max(fl[k], rel_l2(o32.taps[k], o.taps[k]))
-                    if o32fr[:2] == ofr[:2] and ofr[0] != m["end_id"]:
-                        kd = next((i for i in range(1, N) if o32fr[1 + i] != ofr[1 + i]), N)
-                        fl["fast_logits"] = max(fl["fast_logits"],
-                                                rel_l2(o32.taps["fast_logits"][:kd], o.taps["fast_logits"][:kd]))
+                    if ofr[0] != m["end_id"]:
+                        fl["fast_logits"] = max(fl["fast_logits"], rel_l2(o32.taps["fast_logits"], o.taps["fast_logits"]))
                 in_step = o32fr == ofr
             if floor:
                 for k in ("slow_hidden", "slow_logits", "fast_logits"):
@@ -418,20 +418,28 @@ def test_s2_full_fp32_kv_strict(s2_full):
 
 
 @pytest.mark.timeout(900)
-def test_s2_full_batch8_matrix_cores(s2_full):
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+def test_s2_full_batch8_matrix_cores(s2_full, kv):
     # Batch 8 of the full S2 shapes: every product on the matrix cores (the
     # tied head as 4-wave x 2-tile blocks, split-K with fused finish + norm
     # across the 36 slow layers), chunked prefill of ragged prompts, top-p on
-    # the 4,097 slow candidates.  fp32 K/V keeps the plain 2e-3 bar.
+    # the 4,097 slow candidates.  fp32 K/V keeps the plain 2e-3 bar.  bf16 K/V
+    # also takes the matrix-core attention scores and the fp32-oracle floor;
+    # it samples greedily, because its ~1e-3 logit drift (the fp32 oracle's
+    # own) puts top-p draws over these near-uniform random-weight
+    # distributions on near-ties at once, leaving nothing to compare.
     m, w = s2_full
-    m = dict(m, kv_dtype="f32")
+    m = dict(m, kv_dtype=kv)
     plen = np.array([24, 9, 17, 3, 24, 12, 20, 6], dtype=np.int32)
     P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=8)
-    U = synth.make_uniforms((3, 8, m["num_codebooks"]), seed=8)
-    c, worst = run_and_compare(m, w, P, plen, 2, dict(greedy=0, temperature=1.0, top_p=0.9), U,
-                               tag="s2-full-b8")
+    if kv == "f32":
+        samp, U = dict(greedy=0, temperature=1.0, top_p=0.9), synth.make_uniforms((3, 8, m["num_codebooks"]), seed=8)
+    else:
+        samp, U = dict(greedy=1), None
+    c, worst = run_and_compare(m, w, P, plen, 2, samp, U, tag=f"s2-full-b8-kv{kv}", floor=kv == "bf16")
     assert sum(c) >= 8
-    assert max(worst.values()) < 2e-3
+    if kv == "f32":
+        assert max(worst.values()) < 2e-3
 
 
 @pytest.mark.timeout(600)

@@ -461,3 +461,29 @@ def test_tiny_workload_decodes_semantic_frames():
         assert m["semantic_begin_id"] <= f[0] <= m["semantic_end_id"]
         assert f[1] == f[0] - m["semantic_begin_id"]
         assert all(0 <= q < m["codebook_size"] for q in f[1:])
+
+
+def test_forced_frames_follow_the_given_path():
+    # `force` replaces only the sampling decisions: forcing the oracle's own
+    # draws reproduces its frames and taps exactly; forcing other codes makes
+    # them the frame (used to evaluate a second precision along one path).
+    m = synth.model("tiny")
+    w = synth.weights_as_f32(m, synth.make_weights(m, seed=0))
+    P = synth.make_prompts(m, ("fixed", 4, 16, 12), [32])
+    s = Sampling(greedy=False, temperature=1.0, top_p=0.9)
+    U = synth.make_uniforms((3, 1, m["num_codebooks"]), seed=1)[:, 0, :].astype(np.float64)
+    a = DualAROracle(m, w, max_seq=40)
+    sa = a.new_sequence()
+    f0 = a.prefill(sa, P[0], s, U[0])
+    f1 = a.decode_frame(sa, s, U[1])
+    ta = {k: v.copy() for k, v in a.taps.items()}
+    b = DualAROracle(m, w, max_seq=40)
+    sb = b.new_sequence()
+    assert b.prefill(sb, P[0], s, U[0], force=f0) == f0
+    assert b.decode_frame(sb, s, U[1], force=f1) == f1
+    for k, v in ta.items():
+        assert np.array_equal(v, b.taps[k]), k
+    alt = list(f0)
+    alt[3] = (alt[3] + 1) % m["codebook_size"]
+    c = DualAROracle(m, w, max_seq=40)
+    assert c.prefill(c.new_sequence(), P[0], s, U[0], force=alt) == alt
