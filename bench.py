@@ -2,6 +2,7 @@
 dominant kernel and the CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W] [--workload s2_b1|s2_b32|fast_s2|fast_s2_b16|tiny_b1]
+                    [--semantic-head]
 
 A step is one decode frame of the whole hot path (fusion, slow pass, biased
 sample, ten fast passes with their samples) over one batch.  Inputs are
@@ -104,6 +105,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--prompt-len", type=int, default=None,
                     help="override the prompt length (same three-segment layout); for counter runs")
+    ap.add_argument("--semantic-head", action="store_true",
+                    help="slow head over the semantic rows and the end row only (identical draws)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -132,6 +135,8 @@ def main():
     wl_name, b_over, desc = WORKLOADS[args.workload]
     wl = synth.WORKLOADS[wl_name]
     m = synth.model(wl["model"])
+    if args.semantic_head:
+        m = dict(m, semantic_head=1)
     B = b_over or wl["batch"]
     fast_only = wl.get("fast_only", False)
     K = args.steps if args.steps is not None else min(wl["frames"], 256)
@@ -208,7 +213,7 @@ def main():
         step_bytes = 0
         for f in range(K):
             L = [int(p) + W + f + 1 for p in plen]
-            step_bytes += reporting.frame_bytes(m, L)["total"]
+            step_bytes += reporting.frame_bytes(m, L, semantic_head=args.semantic_head)["total"]
     step_gbps = step_bytes / (ms / 1e3) / 1e9
 
     # ---- live per-launch timing (HIP events on the context's stream) ----
@@ -260,7 +265,8 @@ def main():
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if m["weight_dtype"] == "bf16" else "f32",
         "data": "synthetic (seeded random-init weights of the S2 shapes, synthetic prompts)",
-        "config": {"workload": f"{args.workload}: {desc}", "batch": B,
+        "config": {"workload": f"{args.workload}: {desc}" + (", semantic-candidate slow head" if args.semantic_head
+                                                               else ", full-vocabulary slow head"), "batch": B,
                    "prompt_len": None if fast_only else [int(x) for x in plen][:4] + (["..."] if B > 4 else []),
                    "accumulate": "f32", "kv_cache": m["weight_dtype"]},
         "codec_tokens_per_s": round(reporting.codec_tokens_per_s(fps, N), 1),

@@ -36,7 +36,7 @@ class Config(C.Structure):
         "semantic_begin_id", "semantic_end_id", "end_id", "scale_codebook_embeddings")] + [
         ("rope_base", C.c_float), ("norm_eps", C.c_float),
         ("weight_dtype", C.c_int32), ("max_batch", C.c_int32), ("max_seq_len", C.c_int32),
-        ("kv_dtype", C.c_int32), ("prefill_chunk", C.c_int32)]
+        ("kv_dtype", C.c_int32), ("prefill_chunk", C.c_int32), ("semantic_head", C.c_int32)]
 
 
 _LAYER_FIELDS = ("attention_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w1", "w3", "w2")
@@ -133,6 +133,7 @@ def make_config(m: dict, max_batch: int, max_seq_len: int, inherit_fast: bool = 
     kv = m.get("kv_dtype")
     c.kv_dtype = -1 if kv is None else (BF16 if kv == "bf16" else F32)
     c.prefill_chunk = prefill_chunk
+    c.semantic_head = int(m.get("semantic_head", 0))
     return c
 
 
@@ -221,20 +222,24 @@ class DualAR:
             raise DualARError(-1, f"{what}: expected contiguous cuda {dtype} {tuple(shape)}, got "
                                   f"{t.dtype} {tuple(t.shape)} on {t.device}")
 
-    def _taps(self, B, with_fused=True):
+    def _taps(self, B, with_fused=True, which=True):
+        """Tap buffers: which = True for all, or a collection of tap names."""
         torch, m, N = self.torch, self.m, self.N
         td = {"slow_hidden": torch.empty((B, m["dim"]), device="cuda"),
               "slow_logits": torch.empty((B, m["vocab_size"]), device="cuda"),
               "fast_logits": torch.empty((B, N - 1, m["codebook_size"]), device="cuda")}
         if with_fused:
             td["fused_x"] = torch.empty((B, m["dim"]), device="cuda")
+        if which is not True:
+            td = {k: v for k, v in td.items() if k in which}
         tp = Taps(*[td[k].data_ptr() if k in td else None
                     for k in ("fused_x", "slow_hidden", "slow_logits", "fast_logits")])
         return tp, td
 
-    def prefill(self, tokens, prompt_len, sampling: Sampling, uniforms=None, taps: bool = False):
+    def prefill(self, tokens, prompt_len, sampling: Sampling, uniforms=None, taps=False):
         """tokens: cuda int32 [B][N+1][T]; prompt_len: host ints [B].  Returns
-        frame 0 [B][N+1], or (frame 0, taps) when taps is set."""
+        frame 0 [B][N+1], or (frame 0, taps) when taps is set (True, or the
+        names of the taps wanted)."""
         torch = self.torch
         B, _, T = tokens.shape
         self._need(tokens, (B, self.N + 1, T), torch.int32, "tokens")
@@ -243,7 +248,7 @@ class DualAR:
             raise DualARError(-1, "prompt_len must have one entry per sequence")
         plen = (C.c_int32 * B)(*[int(x) for x in prompt_len])
         frame0 = torch.empty((B, self.N + 1), dtype=torch.int32, device="cuda")
-        tp, td = self._taps(B, with_fused=False) if taps else (None, None)
+        tp, td = self._taps(B, with_fused=False, which=taps) if taps else (None, None)
         self._check(self.lib.dualar_prefill(self.h, B, _ptr(tokens), T, plen, C.byref(sampling),
                                             _ptr(uniforms), _ptr(frame0), C.byref(tp) if tp is not None else None))
         self.batch = B
@@ -256,7 +261,7 @@ class DualAR:
         self._need(uniforms, (n, B, N), torch.float32, "uniforms")
         self._need(codes, (B, n, N + 1), torch.int32, "codes")
         emitted = torch.empty(B, dtype=torch.int32, device="cuda")
-        tp, td = self._taps(B) if taps else (None, None)
+        tp, td = self._taps(B, which=taps) if taps else (None, None)
         self._check(self.lib.dualar_decode_frames(self.h, n, C.byref(sampling), _ptr(uniforms), _ptr(codes),
                                                   _ptr(emitted), C.byref(tp) if tp is not None else None))
         return codes, emitted, td

@@ -36,6 +36,7 @@ struct Resolved {  // config with the inherit-on-unset fallback applied
   int dtype, kvdtype, max_batch, max_seq;
   size_t esz, kvesz;
   int pc;   // prefill: positions per sequence per step (rows = max_batch * pc)
+  int semantic_head;
 };
 
 struct Layout {
@@ -100,6 +101,8 @@ bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
   REQ(r->max_batch >= 1 && r->max_batch <= 256, "max_batch out of range [1, 256]");
   REQ(c->prefill_chunk >= 0 && c->prefill_chunk <= 4096, "prefill_chunk out of range [0, 4096]");
   r->pc = c->prefill_chunk > 0 ? c->prefill_chunk : std::max(1, 2048 / r->max_batch);
+  REQ(c->semantic_head == 0 || c->semantic_head == 1, "semantic_head must be 0 or 1");
+  r->semantic_head = c->semantic_head;
   REQ(r->max_seq >= 2 && r->max_seq <= 65536, "max_seq_len out of range [2, 65536]");
 #undef REQ
   return true;
@@ -358,6 +361,35 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   return DUALAR_OK;
 }
 
+// Fast pass 0 through the last fast layer: its attention output, O and FFN
+// feed only pass 0's logits, which are never used, so only the K/V rows of
+// the QKV product run and k, v (QK-norm, RoPE at position 0) are appended to
+// cache slot 0 -- the entries the later passes read.
+template <typename T, typename KT>
+dualar_status run_layer_kv_only(dualar_ctx* c, Stack& S, int l, float* x, int B, bool in_planes) {
+  const Resolved& r = c->r;
+  const Layout& L = c->L;
+  const dualar_layer_weights& w = S.lw[l];
+  float* qkv = (float*)(c->ws + L.qkv);
+  GemvParams g{};
+  g.w[0] = w.wk; g.w[1] = w.wv;
+  g.rows[0] = S.KV * S.hd; g.rows[1] = S.KV * S.hd; g.n_seg = 2;
+  g.K = S.dim; g.n_out = 2 * S.KV * S.hd;
+  g.x = x; g.ldx = S.dim; g.gain = w.attention_norm; g.eps = r.eps;
+  g.y = qkv + (size_t)S.H * S.hd; g.ldy = L.qkv_ld; g.B = B; g.mode = GEMV_STORE;
+  if (sizeof(T) == 2 && B >= 8 && in_planes) g.xplanes = c->ws + L.xn;
+  HIPCHK(gemv<T>(c, g));
+  PrefillParams a{};
+  a.qkv = qkv; a.ld_qkv = L.qkv_ld;
+  a.kcache = S.k + (size_t)l * S.layer_stride * r.kvesz;
+  a.vcache = S.v + (size_t)l * S.layer_stride * r.kvesz;
+  a.max_pos = S.max_pos; a.pos = nullptr; a.pos_const = 0; a.C = 1; a.rope = S.rope;
+  a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
+  a.H = S.H; a.KV = S.KV; a.hd = S.hd; a.R = B; a.B = B;
+  HIPCHK((launch_kv_append<T, KT>(a, c->stream)));
+  return DUALAR_OK;
+}
+
 struct FrameIO {
   const dualar_sampling* s;
   const float* uniforms; int u_fs, u_rs;
@@ -406,20 +438,41 @@ dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
   if (!io.fast_only) {
     if (io.taps && io.taps->slow_hidden)
       HIPCHK(hipMemcpyAsync(io.taps->slow_hidden, xs, (size_t)B * r.dim * 4, hipMemcpyDeviceToDevice, c->stream));
+    // The tied head over the whole vocabulary, or (semantic_head, unless the
+    // caller asks for the full logits) over the only rows the biased sample
+    // can pick: the C semantic ids and the end id, in id order.
+    const bool restricted = r.semantic_head && !(io.taps && io.taps->slow_logits);
     GemvParams g{};
-    g.w[0] = c->w.tok_embedding; g.rows[0] = r.V; g.n_seg = 1; g.K = r.dim; g.n_out = r.V;
+    if (restricted) {
+      const char* emb = (const char*)c->w.tok_embedding;
+      const void* sem = emb + (size_t)r.sb * r.dim * r.esz;
+      const void* end = emb + (size_t)r.end_id * r.dim * r.esz;
+      const bool end_first = r.end_id < r.sb;
+      g.w[0] = end_first ? end : sem; g.rows[0] = end_first ? 1 : r.C;
+      g.w[1] = end_first ? sem : end; g.rows[1] = end_first ? r.C : 1;
+      g.n_seg = 2; g.n_out = r.C + 1;
+    } else {
+      g.w[0] = c->w.tok_embedding; g.rows[0] = r.V; g.n_seg = 1; g.n_out = r.V;
+    }
+    g.K = r.dim;
     g.x = xs; g.ldx = r.dim; g.gain = c->w.norm; g.eps = r.eps;
-    g.y = (float*)(c->ws + L.logits); g.ldy = r.V; g.B = B; g.mode = GEMV_STORE;
+    g.y = (float*)(c->ws + L.logits); g.ldy = g.n_out; g.B = B; g.mode = GEMV_STORE;
     HIPCHK(gemv<T>(c, g));
     if (io.taps && io.taps->slow_logits)
       HIPCHK(hipMemcpyAsync(io.taps->slow_logits, c->ws + L.logits, (size_t)B * r.V * 4, hipMemcpyDeviceToDevice,
                             c->stream));
-    HIPCHK(sample<T>(c, sample_params<T>(c, io, B, 1, 0, xf)));
+    SampleParams sp = sample_params<T>(c, io, B, 1, 0, xf);
+    if (restricted) { sp.restricted = 1; sp.ld = r.C + 1; }
+    HIPCHK(sample<T>(c, sp));
   }
   // fast pass 0: the slow hidden state at depth position 0
   bool pl = false;
-  for (int l = 0; l < r.fn_layer; ++l) {
+  for (int l = 0; l + 1 < r.fn_layer; ++l) {
     dualar_status st = run_layer<T, KT>(c, c->fast, l, xs, B, nullptr, 0, 1, pl);
+    if (st) return st;
+  }
+  {
+    dualar_status st = run_layer_kv_only<T, KT>(c, c->fast, r.fn_layer - 1, xs, B, pl);
     if (st) return st;
   }
   for (int k = 1; k < r.N; ++k) {

@@ -505,9 +505,15 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   if (p.xplanes) p.xn = const_cast<void*>(p.xplanes);   // input already split by its producer
   else hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
   bool ok = false;
-  if (p.mode == GEMV_SWIGLU) launch_gm<2, 4, 1>(p, p0.ksw, 256, s, &ok);
-  else if (p.n_out >= 16384) launch_gm<1, 4, 2>(p, p0.ksw, 256, s, &ok);
-  else launch_gm<1, 2, 1>(p, p0.ksw, 512, s, &ok);
+  int cfg = p0.gm_cfg;
+  if (!cfg) cfg = p.mode == GEMV_SWIGLU ? 2 : (p.n_out >= 16384 ? 3 : 1);
+  const bool glu = p.mode == GEMV_SWIGLU;
+  switch (cfg) {   // (NR, WAVES, T), slots = workgroups the chip holds at once (LDS bound)
+    case 1: if (glu) launch_gm<2, 2, 1>(p, p0.ksw, 256, s, &ok); else launch_gm<1, 2, 1>(p, p0.ksw, 512, s, &ok); break;
+    case 2: if (glu) launch_gm<2, 4, 1>(p, p0.ksw, 256, s, &ok); else launch_gm<1, 4, 1>(p, p0.ksw, 256, s, &ok); break;
+    case 3: if (!glu) launch_gm<1, 4, 2>(p, p0.ksw, 256, s, &ok); break;
+    default: break;
+  }
   if (!ok) {
     *err = hipErrorInvalidValue;
     return true;

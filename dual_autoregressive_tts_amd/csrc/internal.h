@@ -37,6 +37,7 @@ struct GemvParams {
   const void* next_gain; void* next_planes; int* next_done;
   int ksw, ldp;                  // set by the launcher
   int zswz;                      // set by the launcher: activation tiles of a swizzled 1-D grid (0 = 3-D grid)
+  int gm_cfg;                    // matrix-core workgroup shape (0 = the launcher's choice; 1..5 forced, for tuning)
 };
 
 // Decode attention for one new position per sequence, split along the
@@ -71,7 +72,8 @@ struct PrefillParams {
   float* qbuf; int ld_q;              // [R][H*hd]
   void* kcache; void* vcache;         // this layer: [max_batch][KV][max_pos][hd]
   int max_pos;
-  const int* pos;                     // [R]
+  const int* pos;                     // [R], or NULL: every row at pos_const
+  int pos_const;
   int C;                              // rows per sequence
   const float2* rope;                 // [max_pos][hd/2] (cos, sin)
   const void* q_norm; const void* k_norm; float eps;
@@ -95,6 +97,7 @@ struct SeqState {
 // Candidate set / bookkeeping for the sampler.
 struct SampleParams {
   const float* logits; int ld;
+  int restricted;               // slow: logits hold the C+1 candidates in id order (else the vocabulary)
   int B;
   int slow;                     // 1: semantic ids + end id, 0: all C fast codes
   int sb, se, end_id, C, N;
@@ -134,6 +137,8 @@ template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s)
 bool launch_gemm_mfma(const GemvParams& p, hipStream_t s, hipError_t* err);
 template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 template <typename T, typename KT> hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
+// k/v append only (no q, no attention): rows are sequences, grid (R, KV)
+template <typename T, typename KT> hipError_t launch_kv_append(const PrefillParams& p, hipStream_t s);
 template <typename T> hipError_t launch_sample(const SampleParams& p, hipStream_t s);
 template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s);
 template <typename T> hipError_t launch_fast_begin(const FastBeginParams& p, hipStream_t s);

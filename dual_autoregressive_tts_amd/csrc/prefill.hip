@@ -1,7 +1,8 @@
 // Prefill of a chunk of prompt positions for every sequence at once (the
 // causal form of the slow-AR forward; decode is the one-position case).
 //
-// prefill_append_kernel, grid (R, H + KV), one wave: row r's q head (QK-norm
+// prefill_append_kernel, grid (R, H + KV) (or (R, KV) from head H for the k/v
+// append alone), one wave: row r's q head (QK-norm
 // with the per-head [hd] gain, RoPE at the row's position, times
 // 1/sqrt(hd)) goes to qbuf; its k head (QK-norm, RoPE) and v head are
 // rounded to the cache type and written at the row's position.  The
@@ -22,9 +23,9 @@
 #define PF_MAXHD 128
 
 template <typename T, typename KT>
-__global__ void __launch_bounds__(64) prefill_append_kernel(PrefillParams p) {
-  const int r = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
-  const int pos = p.pos[r];
+__global__ void __launch_bounds__(64) prefill_append_kernel(PrefillParams p, int head0) {
+  const int r = blockIdx.x, hh = head0 + blockIdx.y, lane = threadIdx.x;
+  const int pos = p.pos ? p.pos[r] : p.pos_const;
   if (pos < 0) return;
   const int b = r / p.C, hd = p.hd;
   const bool live = 2 * lane < hd;
@@ -187,7 +188,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillParams p) {
 template <typename T, typename KT>
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   if (p.hd % 16 != 0 || p.hd > PF_MAXHD || p.H % p.KV != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_append_kernel<T, KT>), dim3(p.R, p.H + p.KV), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((prefill_append_kernel<T, KT>), dim3(p.R, p.H + p.KV), dim3(64), 0, s, p, 0);
   const int rep = p.H / p.KV;
   const int qb = 64 / rep;
   const dim3 grid((p.C + qb - 1) / qb, p.KV, p.B);
@@ -201,6 +202,17 @@ hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, typename KT>
+hipError_t launch_kv_append(const PrefillParams& p, hipStream_t s) {
+  if (p.hd > PF_MAXHD) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_append_kernel<T, KT>), dim3(p.R, p.KV), dim3(64), 0, s, p, p.H);
+  return hipGetLastError();
+}
+
+template hipError_t launch_kv_append<float, float>(const PrefillParams&, hipStream_t);
+template hipError_t launch_kv_append<bf16_t, bf16_t>(const PrefillParams&, hipStream_t);
+template hipError_t launch_kv_append<bf16_t, float>(const PrefillParams&, hipStream_t);
+template hipError_t launch_kv_append<float, bf16_t>(const PrefillParams&, hipStream_t);
 template hipError_t launch_prefill_attn<float, float>(const PrefillParams&, hipStream_t);
 template hipError_t launch_prefill_attn<bf16_t, bf16_t>(const PrefillParams&, hipStream_t);
 template hipError_t launch_prefill_attn<bf16_t, float>(const PrefillParams&, hipStream_t);

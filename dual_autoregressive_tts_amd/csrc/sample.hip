@@ -148,7 +148,7 @@ __device__ __forceinline__ void topp_sort(const float* z, const SampleParams& p,
   for (int s = 0; s < E; ++s) {
     const int i = tid * E + s;
     float e = 0.f;
-    if (i < nc && cand_ok(i)) e = expf((z[cand_id(i)] - zmax) * invT);
+    if (i < nc && cand_ok(i)) e = expf((z[p.restricted ? i : cand_id(i)] - zmax) * invT);
     key[s] = ((uint64_t)__float_as_uint(e) << 16) | (uint64_t)(0xffffu - (unsigned)i);
   }
   uint32_t* kh = (uint32_t*)ev;          // exchange area: high words in ev, low 16 bits in ix
@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
   int bad = 0;
   for (int i = tid; i < nc; i += SMP_THREADS) {
     if (!cand_ok(i)) continue;
-    const float v = z[cand_id(i)];
+    const float v = z[p.restricted ? i : cand_id(i)];
     if (!(v == v) || v == INFINITY) bad = 1;
     best = better(best, Best{v, i});
   }

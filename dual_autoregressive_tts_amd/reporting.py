@@ -43,17 +43,32 @@ def fast_pass_weight_elems(m: dict) -> int:
     return m["n_fast_layer"] * per + m["codebook_size"] * m["fast_dim"] + m["fast_dim"]
 
 
-def frame_bytes(m: dict, ctx_lengths, fast_only: bool = False) -> dict:
+def fast_pass0_weight_elems(m: dict) -> int:
+    """What fast pass 0 reads here: its logits are never used, so it runs the
+    first n_fast_layer - 1 layers and, of the last one, only the attention
+    norm, the K/V projections and the k QK-norm gain (the cache entries of
+    slot 0); no Q, O, FFN or fast head."""
+    per = _layer_elems(m["fast_dim"], m["fast_n_head"], m["fast_n_kv_head"], m["fast_head_dim"],
+                       m["fast_ffn_dim"], m["fast_qk_norm"])
+    last = m["fast_dim"] + 2 * m["fast_n_kv_head"] * m["fast_head_dim"] * m["fast_dim"] + \
+        (m["fast_head_dim"] if m["fast_qk_norm"] else 0)
+    return (m["n_fast_layer"] - 1) * per + last
+
+
+def frame_bytes(m: dict, ctx_lengths, fast_only: bool = False, semantic_head: bool = False) -> dict:
     """Algorithmic HBM bytes of one decode frame-step over a batch whose
     sequences attend over `ctx_lengths` slow positions (new one included).
 
     Weights are read once per step whatever the batch; K/V and gathers scale
-    with the batch."""
+    with the batch.  Fast weights: passes 1..N-1 read the whole fast stack
+    and head, pass 0 what `fast_pass0_weight_elems` counts.  With
+    semantic_head the slow head reads only the C semantic rows and the end
+    row."""
     esz = 2 if m["weight_dtype"] == "bf16" else 4
     kvesz = 2 if m.get("kv_dtype", m["weight_dtype"]) == "bf16" else 4
     N, D = m["num_codebooks"], m["dim"]
     B = len(ctx_lengths)
-    fast_w = N * fast_pass_weight_elems(m) * esz
+    fast_w = ((N - 1) * fast_pass_weight_elems(m) + fast_pass0_weight_elems(m)) * esz
     # fast K/V: pass k reads slots 0..k-1 and writes slot k, every layer
     fkv = m["n_fast_layer"] * 2 * m["fast_n_kv_head"] * m["fast_head_dim"] * kvesz
     fast_kv = B * fkv * sum(k + 1 for k in range(N))
@@ -61,7 +76,10 @@ def frame_bytes(m: dict, ctx_lengths, fast_only: bool = False) -> dict:
     out = {"fast_weights": fast_w, "fast_kv": fast_kv, "gathers": fast_gather}
     if not fast_only:
         skv = m["n_layer"] * 2 * m["n_kv_head"] * m["head_dim"] * kvesz
-        out["slow_weights"] = slow_step_weight_elems(m) * esz
+        sw = slow_step_weight_elems(m)
+        if semantic_head:
+            sw -= (m["vocab_size"] - m["codebook_size"] - 1) * m["dim"]
+        out["slow_weights"] = sw * esz
         # a sequence attending over L positions reads L-1 cached entries and appends one
         out["slow_kv"] = sum(int(L) for L in ctx_lengths) * skv
         out["gathers"] += B * (N + 1) * D * esz   # fusion rows

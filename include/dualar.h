@@ -86,6 +86,13 @@ typedef struct {
                                     step (0 = max(1, 2048 / max_batch)); the
                                     workspace holds max_batch * prefill_chunk
                                     activation rows                             */
+  int32_t semantic_head;         /* 0: the tied head computes the whole
+                                    vocabulary, as [P2] "The slow AR is Qwen3-4B"
+                                    describes (then the bias masks it); 1: only
+                                    the C semantic rows and the end row, the
+                                    ids the biased sample can pick (same draws;
+                                    the full head still runs when the
+                                    slow_logits tap is requested)              */
 } dualar_config;
 
 /* One transformer layer.  q_norm / k_norm are [head_dim] gains shared by all

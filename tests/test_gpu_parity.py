@@ -24,7 +24,7 @@ def _dev():
 
 
 def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=REL_L2, min_frames=0,
-                    tag="", weights_f32=None, floor=False, prefill_chunk=0):
+                    tag="", weights_f32=None, floor=False, prefill_chunk=0, slow_logits_tap=True):
     """Prefill + n_frames single-frame decode calls on the GPU; the oracle
     replays every sequence.  Returns per-row counts of frames compared.
 
@@ -42,11 +42,13 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
     S = DualAR.sampling(min_frames=min_frames, **samp)
     tok = torch.from_numpy(np.ascontiguousarray(prompts)).cuda()
     U = None if uniforms is None else torch.from_numpy(np.ascontiguousarray(uniforms)).cuda()
-    f0, t0 = ctx.prefill(tok, plen, S, None if U is None else U[0], taps=True)
+    # without the slow_logits tap a semantic-head context runs its restricted head
+    which = True if slow_logits_tap else ("fused_x", "slow_hidden", "fast_logits")
+    f0, t0 = ctx.prefill(tok, plen, S, None if U is None else U[0], taps=which)
     g_frames = [f0.cpu().numpy()]
     g_taps = [{k: v.cpu().numpy() for k, v in t0.items()}]
     for f in range(n_frames):
-        codes, emitted, taps = ctx.decode_frames(1, S, None if U is None else U[1 + f:2 + f], taps=True)
+        codes, emitted, taps = ctx.decode_frames(1, S, None if U is None else U[1 + f:2 + f], taps=which)
         g_frames.append(codes[:, 0].cpu().numpy())
         g_taps.append({k: v.cpu().numpy() for k, v in taps.items()})
     g_emitted = emitted.cpu().numpy()
@@ -117,7 +119,13 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
             bias = o.bias.copy()
             if f < osamp.min_frames:          # frames emitted before this one = f
                 bias[m["end_id"]] = -np.inf
-            if gfr[0] != ofr[0]:
+            if gfr[0] != ofr[0] and "slow_logits" not in t:
+                # restricted head, no GPU slow logits: greedy only, and the
+                # oracle's own top-1 gap must be within the 1e-2 reach
+                assert osamp.greedy, (tag, b, f, "slow id without slow logits")
+                mg = decision_margin(o.taps["slow_logits"] + bias, True)
+                assert mg <= 1e-2, (tag, b, f, "slow id", gfr[0], ofr[0], "oracle margin", mg)
+            elif gfr[0] != ofr[0]:
                 mg = check_decision(t["slow_logits"][b] + bias, o.taps["slow_logits"] + bias, gfr[0], ofr[0],
                                     osamp, None if u is None else u[f][0], (tag, b, f, "slow id"))
             else:
@@ -183,6 +191,19 @@ def test_tiny_ragged_batch_top_p(tiny):
     c, _ = run_and_compare(m, w, P, plen, 8, dict(greedy=0, temperature=1.0, top_p=0.9), U, tol=1e-4,
                            tag="tiny-topp")
     assert sum(c) >= 30
+
+
+def test_tiny_semantic_head(tiny):
+    # the slow head over the C semantic rows and the end row only: the same
+    # draws (the other logits are masked to -inf anyway)
+    m, w = tiny
+    m = dict(m, semantic_head=1)
+    plen = np.array([32, 7, 1, 45, 20], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=4)
+    c, worst = run_and_compare(m, w, P, plen, 6, dict(greedy=1), tol=1e-4, tag="tiny-semhead",
+                               slow_logits_tap=False)
+    assert sum(c) >= 20
+    assert "slow_logits" not in worst or worst["slow_logits"] == 0.0
 
 
 @pytest.mark.parametrize("pc", [1, 3, 16, 64])
@@ -418,7 +439,7 @@ def test_s2_full_fp32_kv_strict(s2_full):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("kv", ["f32", "bf16"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "f32-semhead"])
 def test_s2_full_batch8_matrix_cores(s2_full, kv):
     # Batch 8 of the full S2 shapes: every product on the matrix cores (the
     # tied head as 4-wave x 2-tile blocks, split-K with fused finish + norm
@@ -428,15 +449,20 @@ def test_s2_full_batch8_matrix_cores(s2_full, kv):
     # it samples greedily, because its ~1e-3 logit drift (the fp32 oracle's
     # own) puts top-p draws over these near-uniform random-weight
     # distributions on near-ties at once, leaving nothing to compare.
+    # f32-semhead runs the slow head over the 4,096 semantic rows and the end
+    # row only (greedy; the GPU then has no full-vocabulary slow logits).
     m, w = s2_full
-    m = dict(m, kv_dtype=kv)
+    semhead = kv.endswith("semhead")
+    kv = kv.split("-")[0]
+    m = dict(m, kv_dtype=kv, semantic_head=int(semhead))
     plen = np.array([24, 9, 17, 3, 24, 12, 20, 6], dtype=np.int32)
     P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=8)
-    if kv == "f32":
+    if kv == "f32" and not semhead:
         samp, U = dict(greedy=0, temperature=1.0, top_p=0.9), synth.make_uniforms((3, 8, m["num_codebooks"]), seed=8)
     else:
         samp, U = dict(greedy=1), None
-    c, worst = run_and_compare(m, w, P, plen, 2, samp, U, tag=f"s2-full-b8-kv{kv}", floor=kv == "bf16")
+    c, worst = run_and_compare(m, w, P, plen, 2, samp, U, tag=f"s2-full-b8-kv{kv}{'-semhead' if semhead else ''}",
+                               floor=kv == "bf16", slow_logits_tap=not semhead)
     assert sum(c) >= 8
     if kv == "f32":
         assert max(worst.values()) < 2e-3

@@ -41,8 +41,16 @@ def test_weights_per_frame_model():
 def test_frame_bytes_s2():
     m = synth.model("s2")
     fb = rp.frame_bytes(m, [1025])
-    # weights with fast QK-norm on: 16,348,828,672 B per frame
-    assert fb["slow_weights"] + fb["fast_weights"] == 16348828672
+    # The pages' model, fast QK-norm on: 16,348,828,672 B per frame.  This path
+    # skips what fast pass 0 never uses: the fast head (4,096 x 2,560) and its
+    # norm (2,560) and, of the last fast layer, Q (4,096 x 2,560), O
+    # (2,560 x 4,096), W1/W3/W2 (3 x 9,728 x 2,560), the FFN norm and the q
+    # QK-norm gain.
+    skipped = 4096 * 2560 + 2560 + 4096 * 2560 + 2560 * 4096 + 3 * 9728 * 2560 + 2560 + 128
+    assert fb["slow_weights"] + fb["fast_weights"] == 16348828672 - 2 * skipped
     assert fb["slow_kv"] == 147456 * 1025
     fo = rp.frame_bytes(m, [1, 1], fast_only=True)
-    assert fo["fast_weights"] == 10 * 2 * rp.fast_pass_weight_elems(m)
+    assert fo["fast_weights"] == 10 * 2 * rp.fast_pass_weight_elems(m) - 2 * skipped
+    # semantic head: 4,097 of the 155,776 rows
+    fs = rp.frame_bytes(m, [1025], semantic_head=True)
+    assert fb["slow_weights"] - fs["slow_weights"] == 2 * (155776 - 4097) * 2560
