@@ -218,40 +218,41 @@ def main():
 
     # ---- live per-launch timing (HIP events on the context's stream) ----
     Pf = args.profile_frames
-    a0 = W + K
-    ctx.profile_begin(K_GEMV)
-    run(a0, a0 + Pf // 2)
-    g = ctx.profile_end()
-    ctx.profile_begin(K_GEMV_SWIGLU)
-    run(a0 + Pf // 2, a0 + Pf)
-    f = ctx.profile_end()
-    gemv_avg_us = g["total_ms"] * 1e3 / g["launches"]
-    gemv_gbps = g["bytes"] / (g["total_ms"] * 1e-3) / 1e9
-    gemv_share = g["total_ms"] / ((Pf // 2) * ms_per_step)
-    sw_avg_us = f["total_ms"] * 1e3 / f["launches"]
-    sw_bytes = f["bytes"] / f["launches"]
-    sw_gbps = sw_bytes / (sw_avg_us * 1e-6) / 1e9
-    log(f"[bench] GEMV family: {g['launches']} launches, avg {gemv_avg_us:.2f} us, {gemv_gbps:.0f} GB/s, "
-        f"{100 * gemv_share:.1f}% of step time")
-    log(f"[bench] SwiGLU gate|up GEMV: {f['launches']} launches, avg {sw_avg_us:.2f} us, "
-        f"{sw_bytes / 1e6:.2f} MB/launch, {sw_gbps:.0f} GB/s")
-    roofline = {"bound": "hbm",
-                "kernel": "gemv_rx_kernel<bf16, 2 rows/wave, gate+up, 5 units> (SwiGLU W1|W3 GEMV, "
-                          "2 x 9728 x 2560 bf16)" if not m["weight_dtype"] == "f32" else "SwiGLU W1|W3 GEMV",
-                "achieved": round(sw_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(sw_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                "avg_launch_us": round(sw_avg_us, 3), "bytes_per_launch": round(sw_bytes),
-                "launches_profiled": f["launches"],
-                "gemv_family": {"achieved_GBps": round(gemv_gbps, 1), "avg_launch_us": round(gemv_avg_us, 3),
-                                "launches": g["launches"], "share_of_step_time": round(gemv_share, 4)}}
-    extra = {}
-    if not fast_only:
-        ctx.profile_begin(K_ATTN)
-        run(W + K + Pf, W + K + Pf + 1)   # nothing left to decode: profile needs one more frame
-        a = ctx.profile_end()
-        extra["attention"] = {"avg_launch_us": round(a["total_ms"] * 1e3 / max(a["launches"], 1), 3),
-                              "launches": a["launches"]}
-    ctx.sync()
+    roofline, extra = None, {}
+    if Pf >= 2:   # (0 for profiler runs that only want the timed frames)
+        a0 = W + K
+        ctx.profile_begin(K_GEMV)
+        run(a0, a0 + Pf // 2)
+        g = ctx.profile_end()
+        ctx.profile_begin(K_GEMV_SWIGLU)
+        run(a0 + Pf // 2, a0 + Pf)
+        f = ctx.profile_end()
+        gemv_avg_us = g["total_ms"] * 1e3 / g["launches"]
+        gemv_gbps = g["bytes"] / (g["total_ms"] * 1e-3) / 1e9
+        gemv_share = g["total_ms"] / ((Pf // 2) * ms_per_step)
+        sw_avg_us = f["total_ms"] * 1e3 / f["launches"]
+        sw_bytes = f["bytes"] / f["launches"]
+        sw_gbps = sw_bytes / (sw_avg_us * 1e-6) / 1e9
+        log(f"[bench] GEMV family: {g['launches']} launches, avg {gemv_avg_us:.2f} us, {gemv_gbps:.0f} GB/s, "
+            f"{100 * gemv_share:.1f}% of step time")
+        log(f"[bench] SwiGLU gate|up GEMV: {f['launches']} launches, avg {sw_avg_us:.2f} us, "
+            f"{sw_bytes / 1e6:.2f} MB/launch, {sw_gbps:.0f} GB/s")
+        roofline = {"bound": "hbm",
+                    "kernel": "gemv_rx_kernel<bf16, 2 rows/wave, gate+up, 5 units> (SwiGLU W1|W3 GEMV, "
+                              "2 x 9728 x 2560 bf16)" if not m["weight_dtype"] == "f32" else "SwiGLU W1|W3 GEMV",
+                    "achieved": round(sw_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(sw_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "avg_launch_us": round(sw_avg_us, 3), "bytes_per_launch": round(sw_bytes),
+                    "launches_profiled": f["launches"],
+                    "gemv_family": {"achieved_GBps": round(gemv_gbps, 1), "avg_launch_us": round(gemv_avg_us, 3),
+                                    "launches": g["launches"], "share_of_step_time": round(gemv_share, 4)}}
+        if not fast_only:
+            ctx.profile_begin(K_ATTN)
+            run(W + K + Pf, W + K + Pf + 1)   # nothing left to decode: profile needs one more frame
+            a = ctx.profile_end()
+            extra["attention"] = {"avg_launch_us": round(a["total_ms"] * 1e3 / max(a["launches"], 1), 3),
+                                  "launches": a["launches"]}
+        ctx.sync()
 
     cpu = None
     if not args.no_cpu_baseline:

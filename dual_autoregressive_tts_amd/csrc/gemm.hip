@@ -76,14 +76,16 @@ struct RowSpace {
     swiglu = p.mode == GEMV_SWIGLU;
     ld = (size_t)p.K * 2;
   }
+  // (Written as two 64-bit selects by offset: a three-way pointer select
+  // is otherwise lowered to a per-lane indexed load from a stack array.)
   __device__ __forceinline__ const char* row(int r, int s) const {
-    uint64_t base;
+    uint64_t base = w0;
     if (swiglu) {
-      base = s == 0 ? w0 : w1;
+      base += s == 0 ? 0 : w1 - w0;
     } else {
-      const int q1 = r - r0, q2 = q1 - r1;
-      base = r < r0 ? w0 : (q1 < r1 ? w1 : w2);
-      r = r < r0 ? r : (q1 < r1 ? q1 : q2);
+      const bool in1 = r >= r0, in2 = r >= r0 + r1;
+      base += in2 ? w2 - w0 : (in1 ? w1 - w0 : 0);
+      r -= in2 ? r0 + r1 : (in1 ? r0 : 0);
     }
     return (const char*)base + (size_t)r * ld;
   }
@@ -459,6 +461,241 @@ __global__ void __launch_bounds__(DUALAR_WG) finish_split_kernel(GemvParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K form for the decode shapes (one or two activation tiles, K of
+// 2560..9728, a few dozen row tiles).  Split-K over a grid sized to the
+// chip leaves whole rounds of workgroups waiting on a few (76 row blocks x 4
+// splits = 304 workgroups for 256 compute units take two rounds), and short
+// K ranges spend most of their time filling the pipeline.  Here the tiles'
+// 64-wide chunks, in (tile, chunk) order, are dealt out as U work units:
+// workgroup g of the grid (one per slot the chip holds) takes q or q + 1
+// consecutive units, so every workgroup streams the same number of weight
+// bytes, and its copy pipeline runs on across tile boundaries.  Where a
+// workgroup's range leaves a tile it writes that tile's partial sums to slot
+// (g - first owner of the tile) of the tile's partial area, laid out
+// [slot][segment s][activation row 0..31][tile row] so that a finish kernel
+// reads each activation row's sums as contiguous runs; it adds a tile's
+// slots in slot order and applies the epilogue.
+// ---------------------------------------------------------------------------
+
+// Workgroup that owns unit u when U = q*G + r units go q + 1 to each of the
+// first r workgroups and q to the rest.
+__host__ __device__ __forceinline__ int sk_owner(int u, int q, int r) {
+  const int big = r * (q + 1);
+  return u < big ? u / (q + 1) : r + (u - big) / q;
+}
+
+template <int NR, int WAVES, int T>
+struct Sk {
+  static constexpr int BLOCKS = WAVES * T;                 // 32-row blocks per tile
+  static constexpr int ROWS = 32 * BLOCKS;
+  static constexpr int TE = NR * 32 * ROWS;                 // floats per partial tile
+};
+
+// Grid G (= sk_q*G + sk_r units), THREADS threads, STG copy stages.
+template <int NR, int WAVES, int T, int STG>
+__global__ void __launch_bounds__(64 * WAVES) mfma_sk_kernel(GemvParams p) {
+  using G = Gm<NR, WAVES, T>;
+  static_assert(STG == 3 || STG == 4, "stages");
+  __shared__ __attribute__((aligned(1024))) char lds[STG][G::STAGE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = blockIdx.x, q = p.sk_q, rr = p.sk_r, nch = p.sk_nch;
+  const int u0 = g * q + min(g, rr);
+  const int nf = q + (g < rr ? 1 : 0);
+  if (nf == 0) return;
+  const int Z = (p.B + 31) / 32;
+
+  // issue side: tile / chunk of the next chunk to copy
+  int it = u0 / nch, ic = u0 % nch;
+  // compute side: tile / chunk of the next chunk to multiply
+  int ct = it, cc = ic;
+  GmSrc<G> src;
+  gm_sources<NR, G>(p, src, (it / Z) * G::ROWS, (it % Z) * 32, 0, wave, lane);
+  auto issue = [&](char* stage) {
+    gm_issue<G>(src, stage, ic, wave);
+    if (++ic == nch) {
+      ic = 0;
+      ++it;
+      gm_sources<NR, G>(p, src, (it / Z) * G::ROWS, (it % Z) * 32, 0, wave, lane);
+    }
+  };
+
+  f32x16 acc[T][NR][3];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+    for (int s = 0; s < NR; ++s)
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tt][s][j][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < STG - 1; ++s)
+    if (s < nf) issue(lds[s]);
+
+  bool drain = false;   // partial-sum stores are in flight: wait for everything
+  for (int f0 = 0; f0 < nf; f0 += STG) {
+#pragma unroll
+    for (int s = 0; s < STG; ++s) {
+      const int f = f0 + s;
+      if (f >= nf) break;
+      // chunks copied so far: min(nf, f + STG - 1); those after f may stay in flight
+      const int ahead = min(nf - 1 - f, STG - 2);
+      if (drain || ahead == 0) wait_vm_barrier<0>();
+      else if (ahead == 1) wait_vm_barrier<G::DMA>();
+      else wait_vm_barrier<2 * G::DMA>();
+      drain = false;
+      if (f + STG - 1 < nf) issue(lds[(s + STG - 1) % STG]);
+      gm_compute<NR, T, G>(lds[s], wave, lane, acc);
+      if (++cc == nch || f == nf - 1) {
+        const int slot = g - sk_owner(ct * nch, q, rr);
+        float* dst = p.part + ((size_t)ct * p.sk_smax + slot) * Sk<NR, WAVES, T>::TE;
+        // register r of lane l holds tile row (r/4)*8 + (l/32)*4 + r%4 of
+        // the wave's 32-row block, activation row l % 32
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+          for (int sN = 0; sN < NR; ++sN) {
+            float* d = dst + (size_t)(sN * 32 + (lane & 31)) * G::ROWS + 32 * (wave * T + tt) + 4 * (lane >> 5);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float4 v;
+              v.x = acc[tt][sN][0][4 * j + 0] + (acc[tt][sN][1][4 * j + 0] + acc[tt][sN][2][4 * j + 0]);
+              v.y = acc[tt][sN][0][4 * j + 1] + (acc[tt][sN][1][4 * j + 1] + acc[tt][sN][2][4 * j + 1]);
+              v.z = acc[tt][sN][0][4 * j + 2] + (acc[tt][sN][1][4 * j + 2] + acc[tt][sN][2][4 * j + 2]);
+              v.w = acc[tt][sN][0][4 * j + 3] + (acc[tt][sN][1][4 * j + 3] + acc[tt][sN][2][4 * j + 3]);
+              *(float4*)(d + 8 * j) = v;
+            }
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[tt][sN][j][r] = 0.f;
+          }
+        drain = true;
+        cc = 0;
+        ++ct;
+      }
+    }
+  }
+}
+
+#define SK_KB 8   // partial slots loaded together
+
+// Sum each tile's slots (slot order) and apply the epilogue.  Thread th of
+// tile t takes four consecutive tile rows (th % (ROWS/4)) of activation row
+// th / (ROWS/4), for each of the NR segments.
+template <int NR, int WAVES, int T>
+__global__ void __launch_bounds__(DUALAR_WG) sk_finish_kernel(GemvParams p) {
+  using S = Sk<NR, WAVES, T>;
+  constexpr int ROWS = S::ROWS, PER_TILE = 32 * ROWS / 4;
+  const int Z = (p.B + 31) / 32;
+  const int tiles = ((p.n_out + ROWS - 1) / ROWS) * Z;
+  const size_t gid = (size_t)blockIdx.x * DUALAR_WG + threadIdx.x;
+  const int t = (int)(gid / PER_TILE), th = (int)(gid % PER_TILE);
+  if (t >= tiles) return;
+  const int bl = th / (ROWS / 4), r4 = th % (ROWS / 4);
+  const int b = (t % Z) * 32 + bl;
+  const int n0 = (t / Z) * ROWS + 4 * r4;
+  if (b >= p.B || n0 >= p.n_out) return;
+  const int nch = p.sk_nch;
+  const int nsl = sk_owner(t * nch + nch - 1, p.sk_q, p.sk_r) - sk_owner(t * nch, p.sk_q, p.sk_r) + 1;
+  const float* base = p.part + (size_t)t * p.sk_smax * S::TE + (size_t)bl * ROWS + 4 * r4;
+  float4 v[NR];
+#pragma unroll
+  for (int s = 0; s < NR; ++s) v[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < nsl; k0 += SK_KB) {
+    float4 a[SK_KB][NR];
+#pragma unroll
+    for (int u = 0; u < SK_KB; ++u)
+#pragma unroll
+      for (int s = 0; s < NR; ++s)
+        if (k0 + u < nsl) a[u][s] = *(const float4*)(base + (size_t)(k0 + u) * S::TE + (size_t)s * 32 * ROWS);
+#pragma unroll
+    for (int u = 0; u < SK_KB; ++u)
+#pragma unroll
+      for (int s = 0; s < NR; ++s)
+        if (k0 + u < nsl) {
+          v[s].x += a[u][s].x; v[s].y += a[u][s].y; v[s].z += a[u][s].z; v[s].w += a[u][s].w;
+        }
+  }
+  const float g4[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+  const float u4[4] = {v[NR - 1].x, v[NR - 1].y, v[NR - 1].z, v[NR - 1].w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int n = n0 + e;
+    if (n >= p.n_out) break;
+    float out;
+    if (p.mode == GEMV_SWIGLU) out = silu_f(g4[e]) * u4[e];
+    else if (p.mode == GEMV_ADD) out = p.res[(size_t)b * p.ldres + n] + g4[e];
+    else out = g4[e];
+    if (p.yplanes) store_planes((uint16_t*)p.yplanes, (size_t)p.B * p.n_out, (size_t)b * p.n_out + n, out);
+    else p.y[(size_t)b * p.ldy + n] = out;
+  }
+}
+
+// Stream-K plan: U = tiles x chunks work units dealt to the grid (false
+// when there is no partial buffer or the partial tiles do not fit it).
+template <int NR, int WAVES, int T>
+static bool sk_plan(GemvParams& p, int slots, int* ng_out) {
+  using S = Sk<NR, WAVES, T>;
+  constexpr int ROWS = 32 * WAVES * T;
+  const int Z = (p.B + 31) / 32;
+  const int tiles = ((p.n_out + ROWS - 1) / ROWS) * Z;
+  const int nch = p.K / GM_KC;
+  const long long U = (long long)tiles * nch;
+  if (!p.part || U >= (1LL << 30)) return false;
+  int ng = slots;
+  if (U < 4LL * ng) ng = (int)std::max(1LL, U / 4);      // at least four chunks per workgroup
+  const int q = (int)(U / ng), r = (int)(U % ng);
+  int smax = 1;
+  for (int t = 0; t < tiles; ++t) smax = std::max(smax, sk_owner(t * nch + nch - 1, q, r) - sk_owner(t * nch, q, r) + 1);
+  if ((size_t)tiles * smax * S::TE > p.part_elems) return false;
+  p.sk_q = q;
+  p.sk_r = r;
+  p.sk_smax = smax;
+  p.sk_nch = nch;
+  *ng_out = ng;
+  return true;
+}
+
+template <int NR, int WAVES, int T>
+static void sk_finish(GemvParams& p, hipStream_t s) {
+  using S = Sk<NR, WAVES, T>;
+  constexpr int ROWS = 32 * WAVES * T;
+  const int tiles = ((p.n_out + ROWS - 1) / ROWS) * ((p.B + 31) / 32);
+  const size_t n = (size_t)tiles * 32 * S::ROWS / 4;
+  hipLaunchKernelGGL((sk_finish_kernel<NR, WAVES, T>), dim3((unsigned)((n + DUALAR_WG - 1) / DUALAR_WG)),
+                     dim3(DUALAR_WG), 0, s, p);
+  // A residual product whose output feeds the next product: RMS-normalise
+  // each finished row with next_gain and split it into planes (the rows are
+  // read once more; one workgroup per row, like the finish itself would need).
+  const bool next = p.next_planes && p.mode == GEMV_ADD && p.n_out <= NORM_MAXV * 4 * DUALAR_WG &&
+                    p.n_out % 4 == 0;
+  if (p.next_done) *p.next_done = next ? 1 : 0;
+  if (next) {
+    GemvParams q = p;
+    q.x = p.y;
+    q.ldx = p.ldy;
+    q.K = p.n_out;
+    q.gain = p.next_gain;
+    q.xn = p.next_planes;
+    hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, q);
+  }
+}
+
+// Plans and launches the stream-K form; false when it does not apply (no
+// partial buffer, or the partial tiles do not fit it).  `slots` = workgroups
+// the chip holds at once.
+template <int NR, int WAVES, int T, int STG>
+static bool launch_sk(GemvParams& p, int slots, hipStream_t s) {
+  int ng = 0;
+  if (!sk_plan<NR, WAVES, T>(p, slots, &ng)) return false;
+  hipLaunchKernelGGL((mfma_sk_kernel<NR, WAVES, T, STG>), dim3(ng), dim3(64 * WAVES), 0, s, p);
+  sk_finish<NR, WAVES, T>(p, s);
+  return true;
+}
+
 template <int NR, int WAVES, int T>
 static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, bool* ok) {
   using G = Gm<NR, WAVES, T>;
@@ -506,8 +743,33 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   else hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
   bool ok = false;
   int cfg = p0.gm_cfg;
-  if (!cfg) cfg = p.mode == GEMV_SWIGLU ? 2 : (p.n_out >= 16384 ? 3 : 1);
   const bool glu = p.mode == GEMV_SWIGLU;
+  const int z_tiles = (p.B + 31) / 32;
+  if (!cfg) {
+    // stream-K for the decode shapes; the tall head (hundreds of row tiles)
+    // balances well as it is and its partials would be as large as its output
+    if (z_tiles <= 2 && p.K / GM_KC >= 8 && p0.ksw == 0 && p.n_out < 16384) cfg = 11;
+    else cfg = glu ? 2 : (p.n_out >= 16384 ? 3 : 1);
+  }
+  if (cfg >= 11) {   // stream-K shapes (slots: one 4-wave workgroup per compute unit)
+    bool done = false;
+    switch (cfg) {
+      case 11: done = glu ? launch_sk<2, 4, 1, 3>(p, 256, s) : launch_sk<1, 4, 1, 4>(p, 256, s); break;
+      case 12: done = glu ? false : launch_sk<1, 4, 2, 3>(p, 256, s); break;
+      case 13: done = glu ? launch_sk<2, 2, 1, 3>(p, 256, s) : launch_sk<1, 2, 1, 4>(p, 512, s); break;
+      case 14: done = glu ? false : launch_sk<1, 4, 1, 3>(p, 256, s); break;
+      default: break;
+    }
+    if (done) {
+      *err = hipGetLastError();
+      return true;
+    }
+    if (p0.gm_cfg) {
+      *err = hipErrorInvalidValue;
+      return true;
+    }
+    cfg = glu ? 2 : (p.n_out >= 16384 ? 3 : 1);   // partial tiles do not fit: split-K form
+  }
   switch (cfg) {   // (NR, WAVES, T), slots = workgroups the chip holds at once (LDS bound)
     case 1: if (glu) launch_gm<2, 2, 1>(p, p0.ksw, 256, s, &ok); else launch_gm<1, 2, 1>(p, p0.ksw, 512, s, &ok); break;
     case 2: if (glu) launch_gm<2, 4, 1>(p, p0.ksw, 256, s, &ok); else launch_gm<1, 4, 1>(p, p0.ksw, 256, s, &ok); break;

@@ -38,6 +38,10 @@ struct GemvParams {
   int ksw, ldp;                  // set by the launcher
   int zswz;                      // set by the launcher: activation tiles of a swizzled 1-D grid (0 = 3-D grid)
   int gm_cfg;                    // matrix-core workgroup shape (0 = the launcher's choice; 1..5 forced, for tuning)
+  // set by the launcher for the stream-K form: U = tiles * chunks-per-tile
+  // work units dealt to the grid, workgroup g taking sk_q (+1 if g < sk_r)
+  // consecutive units; partial tiles at part + (tile * sk_smax + slot) * TE
+  int sk_q, sk_r, sk_smax, sk_nch;
 };
 
 // Decode attention for one new position per sequence, split along the
