@@ -133,7 +133,9 @@ Layout layout(const Resolved& r) {
   // prefill chunk: activations, positions, rotated q of every row
   L.x_pre = take((size_t)L.rows * r.dim * 4);
   L.ppos = take((size_t)L.rows * 4);
-  L.qbuf = take((size_t)L.rows * L.att_ld * 4);
+  // prefill: q rows (fp32); decode: the query planes of the batched
+  // attention ([3][max_batch][att_ld] bf16)
+  L.qbuf = take(std::max((size_t)L.rows * L.att_ld * 4, (size_t)r.max_batch * L.att_ld * 6));
   L.logits = take((size_t)r.max_batch * r.V * 4);
   L.flog = take((size_t)r.max_batch * r.C * 4);
   const int maxH = std::max(r.H, r.fH), maxhd = std::max(r.hd, r.fhd);
@@ -323,6 +325,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.part = (float*)(c->ws + L.part);
   a.counters = (unsigned*)(c->ws + L.counters);
   a.out = att; a.ld_out = L.att_ld; a.out_planes = planes; a.B = B;
+  a.q_planes = (uint16_t*)(c->ws + L.qbuf);   // the prefill q buffer is free while decoding
   HIPCHK(prof_pre(c, DUALAR_K_ATTN));
   HIPCHK((launch_attn<T, KT>(a, c->stream)));
   if (c->prof_cls == DUALAR_K_ATTN) {

@@ -305,6 +305,352 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
   }
 }
 
+// Query preparation for the flash-decoding form, grid (B, H + KV), one
+// wave: query head hh gets QK-norm, RoPE at the row's position and the
+// 1/sqrt(hd) scale, and is stored as three bf16 terms (planes [3][B][H*hd]);
+// KV head hh - H gets QK-norm and RoPE on k, and k, v rounded to the cache
+// type are appended at the position.  Same arithmetic as the other attention
+// kernels, so the cache entries do not depend on the form.
+template <typename T, typename KT>
+__global__ void __launch_bounds__(64) attn_prep_kernel(AttnParams p) {
+  const int b = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
+  const int pos = p.pos ? p.pos[b] : p.pos_const;
+  if (pos < 0) return;
+  const int hd = p.hd;
+  const bool live = 2 * lane < hd;
+  const int pl = live ? 2 * lane : 0;
+  const float* row = p.qkv + (size_t)b * p.ld_qkv;
+  const float2 cs = p.rope[(size_t)pos * (hd / 2) + (live ? lane : 0)];
+  if (hh < p.H) {
+    const float* qp = row + (size_t)hh * hd;
+    float a = live ? qp[pl] : 0.f, c = live ? qp[pl + 1] : 0.f;
+    if (p.q_norm) {
+      const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)hd + p.eps);
+      a = a * inv * ElemT<T>::load(p.q_norm, pl);
+      c = c * inv * ElemT<T>::load(p.q_norm, pl + 1);
+    }
+    const float qscale = 1.0f / sqrtf((float)hd);
+    if (live) {
+      const size_t plane = (size_t)p.B * p.H * hd, at = ((size_t)b * p.H + hh) * hd + pl;
+      store_planes(p.q_planes, plane, at, (a * cs.x - c * cs.y) * qscale);
+      store_planes(p.q_planes, plane, at + 1, (a * cs.y + c * cs.x) * qscale);
+    }
+    return;
+  }
+  const int g = hh - p.H;
+  const size_t at = (((size_t)b * p.KV + g) * p.max_pos + pos) * hd;
+  const float* kp = row + (size_t)p.H * hd + (size_t)g * hd;
+  float a = live ? kp[pl] : 0.f, c = live ? kp[pl + 1] : 0.f;
+  if (p.k_norm) {
+    const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)hd + p.eps);
+    a = a * inv * ElemT<T>::load(p.k_norm, pl);
+    c = c * inv * ElemT<T>::load(p.k_norm, pl + 1);
+  }
+  if (live) {
+    ElemT<KT>::store(p.kcache, at + pl, ElemT<KT>::round(a * cs.x - c * cs.y));
+    ElemT<KT>::store(p.kcache, at + pl + 1, ElemT<KT>::round(a * cs.y + c * cs.x));
+  }
+  const float* vp = row + (size_t)(p.H + p.KV) * hd + (size_t)g * hd;
+  for (int d = lane; d < hd; d += 64) ElemT<KT>::store(p.vcache, at + d, ElemT<KT>::round(vp[d]));
+}
+
+// Flash-decoding form for the batched bf16 cache with head_dim 128 (up to
+// 64 sequences), after attn_prep_kernel.  The work is balanced across the
+// grid like a stream-K product: the 128-position tiles of every (sequence,
+// KV head), in (sequence, head, tile) order, are U work units, and
+// workgroup g takes q or q + 1 consecutive ones (U = q*G + r, the first r
+// workgroups taking one more).  Sequence lengths differ by up to 8x, so
+// fixed splits leave most of the chip idle while the longest heads finish.
+// A workgroup's units fall into segments of one head; for each it runs the
+// tile loop below and writes the segment's (P.V, m, l) to slot
+// (g - first workgroup of the head) of the head's partial area, or the
+// final output when it holds the whole head.
+//
+// Tile loop: in each tile wave w owns positions 32w..32w+31 for both the
+// scores and P.V, so the waves run their tiles independently (no barrier
+// inside the loop).  Per tile a wave
+//   - has the tile's K (A-operand layout of v_mfma_f32_16x16x32_bf16:
+//     16 positions x 32 dims per step, two 16-position groups) and V (16
+//     lanes x 8 dims per position, four positions per load) in registers,
+//     loaded two tiles ahead (two register buffers);
+//   - gets the scores of its 32 positions for the rep query heads from the
+//     matrix cores (q as three bf16 terms read straight from the prepared
+//     planes: the fp32 product), reduces each head's max and sum across the
+//     four lanes that hold it, and keeps a running max m and sum l per head;
+//   - passes the probabilities through a wave-private LDS slot into the P.V
+//     layout and rescales its accumulators by e^(m_old - m_new).
+// Positions past the segment are loaded from entry 0 (cached) and left out
+// of the scores and the P.V, so every load of the loop is unconditional and
+// the compiler's waits keep both buffers in flight.
+#define FL_TILE 128
+#define FL_MAXB 64
+
+// Tiles of each sequence and their exclusive prefix over sequences (times
+// KV), one sequence per lane (B <= 64): lanes >= B hold the total.
+__device__ __forceinline__ void fl_prefix(const AttnParams& p, int lane, int* E, int* cnt) {
+  int n = 0;
+  if (lane < p.B) {
+    const int pos = p.pos ? p.pos[lane] : p.pos_const;
+    n = pos < 0 ? 0 : ((pos + 1 + FL_TILE - 1) / FL_TILE) * p.KV;
+  }
+  int x = n;       // inclusive scan
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  *E = x - n;
+  *cnt = n;
+}
+
+__device__ __forceinline__ int fl_owner(int u, int q, int r) {
+  const int big = r * (q + 1);
+  return u < big ? u / (q + 1) : r + (u - big) / q;
+}
+
+template <int REP>
+__global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, int ng) {
+  constexpr int HD = 128, GW = 2, IT = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane & 15, grp = lane >> 4;     // P.V layout: dims 8*sub.., position 4*it + grp
+  const int col = lane & 15;                      // query head (B column) of the score layout
+  const bool live_col = col < REP;
+
+  __shared__ __attribute__((aligned(16))) float pw[4][4][8][REP];   // [wave][grp][it][head]
+  __shared__ float accs[4][REP][HD];
+  __shared__ float mlw[4][REP][2];
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[3][REP][HD];  // the segment's q terms
+
+  int E, cnt;
+  fl_prefix(p, lane, &E, &cnt);
+  const int U = __shfl(E + cnt, 63, 64);
+  const int wg = blockIdx.x;
+  const int q = U / ng, rr = U % ng;
+  const int u0 = wg * q + min(wg, rr), u1 = u0 + q + (wg < rr ? 1 : 0);
+
+  for (int u = u0; u < u1;) {
+    // the segment's head
+    const int b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(E <= u)) - 1);
+    const int Eb = __builtin_amdgcn_readfirstlane(__shfl(E, b, 64));
+    const int ntb = __builtin_amdgcn_readfirstlane(__shfl(cnt, b, 64)) / p.KV;
+    const int g = (u - Eb) / ntb, t0 = (u - Eb) % ntb;
+    const int hfirst = Eb + g * ntb, hend = hfirst + ntb;
+    const int useg = min(u1, hend);
+    const int pos = p.pos ? p.pos[b] : p.pos_const;
+    const int c0 = t0 * FL_TILE, c1 = min((useg - hfirst) * FL_TILE, pos + 1);
+    const int ntile = useg - u;
+    const int slot = wg - fl_owner(hfirst, q, rr);
+    const bool whole = u == hfirst && useg == hend;
+    u = useg;
+
+    const size_t head_base = ((size_t)b * p.KV + g) * p.max_pos;
+    const char* kbase = (const char*)p.kcache + head_base * HD * 2;
+    const char* vbase = (const char*)p.vcache + head_base * HD * 2;
+
+    u32x4 ka[GW][4], va[IT], kb[GW][4], vb[IT];
+    auto load_tile = [&](u32x4 (&kk)[GW][4], u32x4 (&vv)[IT], int t) __attribute__((always_inline)) {
+      const int base = c0 + t * FL_TILE + 32 * wave;
+#pragma unroll
+      for (int mm = 0; mm < GW; ++mm) {
+        const int j = base + 16 * mm + (lane & 15);
+        const size_t e = (size_t)(j < c1 ? j : 0) * HD + 8 * (lane >> 4);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kk[mm][ks] = ld_vec(kbase + (e + 32 * ks) * 2);
+      }
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int j = base + 4 * it + grp;
+        vv[it] = ld_vec(vbase + ((size_t)(j < c1 ? j : 0) * HD + sub * 8) * 2);
+      }
+    };
+    // the segment's q terms into LDS (3 x REP x 128 bf16, 16 bytes per thread)
+    {
+      const size_t plane = (size_t)p.B * p.H * HD;
+      const uint16_t* qsrc = p.q_planes + ((size_t)b * p.H + g * REP) * HD;
+      for (int i = tid; i < 3 * REP * HD / 8; i += DUALAR_WG) {
+        const int qq = i / (REP * HD / 8), r = i % (REP * HD / 8);
+        *(u32x4*)(&qlds[0][0][0] + (size_t)i * 8) = ld_vec(qsrc + qq * plane + (size_t)r * 8);
+      }
+    }
+    load_tile(ka, va, 0);
+    load_tile(kb, vb, 1);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    float m_run = -INFINITY, l_run = 0.f;     // for head `col` (lanes with col < REP)
+    float acc[REP][8];
+#pragma unroll
+    for (int hl = 0; hl < REP; ++hl)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hl][e] = 0.f;
+
+    auto tile = [&](const u32x4 (&kk)[GW][4], const u32x4 (&vv)[IT], int t) __attribute__((always_inline)) {
+      const int base = c0 + t * FL_TILE + 32 * wave;
+      float sv[GW][4];
+#pragma unroll
+      for (int mm = 0; mm < GW; ++mm) {
+        att_f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const att_bf16x8 a = __builtin_bit_cast(att_bf16x8, kk[mm][ks]);
+#pragma unroll
+          for (int qq = 0; qq < 3; ++qq) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 bq = live_col ? *(const u32x4*)&qlds[qq][live_col ? col : 0][32 * ks + 8 * (lane >> 4)] : z;
+            acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(att_bf16x8, bq), acc4, 0, 0, 0);
+          }
+        }
+        // acc4[r]: position base + 16 mm + 4 (lane >> 4) + r, head col
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[mm][r] = base + 16 * mm + 4 * (lane >> 4) + r < c1 ? acc4[r] : -INFINITY;
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int mm = 0; mm < GW; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sv[mm][r]);
+      mt = max_xor32(max_xor16(mt));          // over the wave's 32 positions of head col
+      const float m_new = fmaxf(m_run, mt);
+      // a wave whose positions so far are all past the segment keeps m = -inf, p = 0
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int mm = 0; mm < GW; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = expf(sv[mm][r] - m_use);
+          ls += pv;
+          const int qp = 16 * mm + 4 * (lane >> 4) + r;        // position in the wave's 32
+          if (live_col) pw[wave][qp & 3][qp >> 2][col] = pv;
+        }
+      ls = add_xor32(add_xor16(ls));
+      const float cf = expf(m_run - m_use);   // 0 while m_run = -inf
+      l_run = l_run * cf + ls;
+      m_run = m_new;
+#pragma unroll
+      for (int hl = 0; hl < REP; ++hl) {       // lane hl holds head hl
+        const float ch = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cf), hl));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hl][e] *= ch;
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const float* pr = &pw[wave][grp][0][0];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        // past the segment: p = 0, and the entry loaded in its place may be
+        // one that was never written (a depth-cache slot on the first frame)
+        if (base + 4 * it + grp >= c1) continue;
+        float vf[8];
+        ElemT<bf16_t>::unpack(vv[it], vf);
+#pragma unroll
+        for (int hl = 0; hl < REP; ++hl) {
+          const float pj = pr[it * REP + hl];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hl][e] = fmaf(pj, vf[e], acc[hl][e]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+
+    for (int t = 0; t < ntile; t += 2) {
+      tile(ka, va, t);
+      load_tile(ka, va, t + 2);
+      if (t + 1 < ntile) tile(kb, vb, t + 1);
+      load_tile(kb, vb, t + 3);
+    }
+
+    // ---- combine: the four position groups of each wave, then the waves ----
+#pragma unroll
+    for (int hl = 0; hl < REP; ++hl)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hl][e] = across_groups_sum(acc[hl][e], 16);
+    if (grp == 0) {
+#pragma unroll
+      for (int hl = 0; hl < REP; ++hl)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accs[wave][hl][sub * 8 + e] = acc[hl][e];
+    }
+    if (lane < REP) { mlw[wave][lane][0] = m_run; mlw[wave][lane][1] = l_run; }
+    __syncthreads();
+    for (int i = tid; i < REP * HD; i += DUALAR_WG) {
+      const int hl = i / HD, e = i % HD;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, mlw[w][hl][0]);
+      float o = 0.f, l = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = mlw[w][hl][0] == -INFINITY ? 0.f : expf(mlw[w][hl][0] - M);
+        o += f * accs[w][hl][e];
+        l += f * mlw[w][hl][1];
+      }
+      if (whole) {
+        const size_t colx = (size_t)(g * REP + hl) * HD + e;
+        if (p.out_planes) store_planes(p.out_planes, (size_t)p.B * p.H * HD, (size_t)b * p.H * HD + colx, o / l);
+        else p.out[(size_t)b * p.ld_out + colx] = o / l;
+      } else {
+        float* pp = p.part + (((size_t)b * p.H + g * REP + hl) * p.max_splits + slot) * (HD + 2);
+        pp[e] = o;
+        if (e == 0) { pp[HD] = M; pp[HD + 1] = l; }
+      }
+    }
+    __syncthreads();     // accs / mlw are reused by the next segment
+  }
+}
+
+// Merge for the balanced form: grid (B, H), the slots of head (b, h / rep)
+// are those of the workgroups its tiles went to (none to merge when one
+// workgroup held the whole head).
+__global__ void __launch_bounds__(128) attn_flash_merge_kernel(AttnParams p, int ng) {
+  const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
+  const int pos = p.pos ? p.pos[b] : p.pos_const;
+  if (pos < 0) return;
+  int E, cnt;
+  fl_prefix(p, lane, &E, &cnt);
+  const int U = __shfl(E + cnt, 63, 64);
+  const int q = U / ng, rr = U % ng;
+  const int Eb = __shfl(E, b, 64), ntb = __shfl(cnt, b, 64) / p.KV;
+  const int g = h / (p.H / p.KV);
+  const int hfirst = Eb + g * ntb;
+  const int n_slots = fl_owner(hfirst + ntb - 1, q, rr) - fl_owner(hfirst, q, rr) + 1;
+  if (n_slots == 1) return;                    // the flash kernel wrote o
+  const int hd = p.hd;
+  const float* pp = p.part + ((size_t)b * p.H + h) * p.max_splits * (hd + 2);
+  __shared__ float wsh[FL_MAXB * 4 + 8];
+  __shared__ float red[2];
+  __shared__ float lred[2];
+  float mloc = -INFINITY;
+  for (int s = t; s < n_slots; s += 128) mloc = fmaxf(mloc, pp[(size_t)s * (hd + 2) + hd]);
+  mloc = wave_max(mloc);
+  if (lane == 0) red[wv] = mloc;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
+  float lloc = 0.f;
+  for (int s = t; s < n_slots; s += 128) {
+    const float* qv = pp + (size_t)s * (hd + 2);
+    const float w = expf(qv[hd] - M);
+    wsh[s] = w;
+    lloc += qv[hd + 1] * w;
+  }
+  lloc = wave_sum(lloc);
+  if (lane == 0) lred[wv] = lloc;
+  __syncthreads();
+  const float lsum = lred[0] + lred[1];
+  if (t >= hd) return;
+  float o = 0.f;
+  for (int s0 = 0; s0 < n_slots; s0 += 8) {
+    float ov[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ov[i] = pp[(size_t)min(s0 + i, n_slots - 1) * (hd + 2) + t];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (s0 + i < n_slots) o = fmaf(ov[i], wsh[s0 + i], o);
+  }
+  if (p.out_planes) store_planes(p.out_planes, (size_t)p.B * p.H * hd, (size_t)b * p.H * hd + (size_t)h * hd + t, o / lsum);
+  else p.out[(size_t)b * p.ld_out + (size_t)h * hd + t] = o / lsum;
+}
+
 // One workgroup per (sequence, query head) merges the split partials:
 // M = max_s m_s and the weights w_s = e^(m_s - M) are computed for all splits
 // at once (one split per thread), then o[e] = sum_s w_s o_s[e] / sum_s w_s l_s
@@ -360,12 +706,34 @@ int attn_chunk(int kv_esz, int hd, int it) {
   return 4 * (64 / lpp) * it;
 }
 
+#define FL_SLOTS 512   // workgroups of the balanced flash-decoding form (two per compute unit)
+
 template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p0, hipStream_t s) {
   AttnParams p = p0;
+  const int rep = p.H / p.KV;
+  if constexpr (sizeof(KT) == 2) {
+    // the balanced flash-decoding form: bf16 cache, head_dim 128, batched
+    if (p.hd == 128 && p.it >= 8 && p.q_planes && p.B <= FL_MAXB && (rep == 1 || rep == 2 || rep == 4)) {
+      const int nt_max = (p.lmax + FL_TILE - 1) / FL_TILE;
+      // upper bound of the units: every row at lmax
+      const long long u_max = (long long)p.B * p.KV * nt_max;
+      const int ng = (int)std::min<long long>(FL_SLOTS, std::max<long long>(1, u_max));
+      // slots per head: at most the head's tiles + 1 (a workgroup holds >= 1 unit
+      // whenever U >= ng; with U < ng some hold none and the rest one each)
+      p.max_splits = nt_max + 1;
+      hipLaunchKernelGGL((attn_prep_kernel<T, KT>), dim3(p.B, p.H + p.KV), dim3(64), 0, s, p);
+      switch (rep) {
+        case 1: hipLaunchKernelGGL((attn_flash_kernel<1>), dim3(ng), dim3(DUALAR_WG), 0, s, p, ng); break;
+        case 2: hipLaunchKernelGGL((attn_flash_kernel<2>), dim3(ng), dim3(DUALAR_WG), 0, s, p, ng); break;
+        default: hipLaunchKernelGGL((attn_flash_kernel<4>), dim3(ng), dim3(DUALAR_WG), 0, s, p, ng); break;
+      }
+      hipLaunchKernelGGL(attn_flash_merge_kernel, dim3(p.B, p.H), dim3(128), 0, s, p, ng);
+      return hipGetLastError();
+    }
+  }
   p.chunk = attn_chunk((int)sizeof(KT), p.hd, p.it);
   p.max_splits = (p.lmax + p.chunk - 1) / p.chunk;
   dim3 grid(p.max_splits, p.KV, p.B);
-  const int rep = p.H / p.KV;
   // the matrix-core score path: bf16 cache, head_dim 128, 4+ loads per lane
   const bool mqk = sizeof(KT) == 2 && p.hd == 128 && p.it >= 4;
 #define ATT_GO(IT, REP)                                                                                      \

@@ -63,6 +63,7 @@ struct AttnParams {
   unsigned* counters;                 // [B][KV], zero between launches
   float* out; int ld_out;             // [B][H*hd]
   uint16_t* out_planes;               // if set: o as planes [3][B][H*hd] instead of out
+  uint16_t* q_planes;                 // scratch [3][B][H*hd] (flash-decoding form)
   int B;
 };
 

@@ -255,6 +255,21 @@ def test_tiny_bf16_batched_matrix_cores(B):
     assert sum(c) >= 2 * B
 
 
+@pytest.mark.timeout(600)
+def test_bf16_batched_long_context(tiny):
+    # bf16 cache, head_dim 128, 4 query heads per KV head, 9 sequences with
+    # contexts of 300..1400: decode attention walks several 128-position
+    # tiles per workgroup and several workgroups per head (merged), with the
+    # new position in the last, ragged tile.
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
+                    n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1, fast_head_dim=128)
+    w = synth.make_weights(m, seed=6)
+    plen = np.array([1400, 300, 777, 1024, 513, 640, 1151, 385, 900], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=6)
+    c, worst = run_and_compare(m, w, P, plen, 3, dict(greedy=1), tag="bf16-long", floor=True)
+    assert sum(c) >= 18
+
+
 def test_end_token_stops_and_pads(tiny):
     m, w = tiny
     w = {k: v.copy() for k, v in w.items()}
