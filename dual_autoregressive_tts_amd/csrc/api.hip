@@ -320,7 +320,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.max_pos = S.max_pos; a.pos = pos_dev; a.pos_const = pos_const; a.rope = S.rope;
   a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
   a.H = S.H; a.KV = S.KV; a.hd = S.hd;
-  a.it = B == 1 ? 2 : (B <= 4 ? 4 : 8);
+  a.it = B <= 4 ? 4 : 8;   // (batch 1: 4 loads per lane measured 12.0 us per layer, 2 loads 14.7 us)
   a.lmax = Lmax;
   a.part = (float*)(c->ws + L.part);
   a.counters = (unsigned*)(c->ws + L.counters);
