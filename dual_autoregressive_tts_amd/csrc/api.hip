@@ -298,6 +298,18 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g.y = qkv; g.ldy = L.qkv_ld; g.B = B; g.mode = GEMV_STORE;
   if (planes && in_planes) g.xplanes = xn;
   in_planes = false;
+  // batched decode with a bf16 cache: the QKV finish also prepares the
+  // attention (QK-norm, RoPE, q terms, k/v append) when it can
+  int prepped = 0;
+  if (planes && rows_per_seq == 0 && sizeof(KT) == 2) {
+    g.prep.rope = S.rope; g.prep.pos = pos_dev; g.prep.pos_const = pos_const;
+    g.prep.q_norm = S.qk ? w.q_norm : nullptr; g.prep.k_norm = S.qk ? w.k_norm : nullptr;
+    g.prep.H = S.H; g.prep.KV = S.KV; g.prep.hd = S.hd; g.prep.max_pos = S.max_pos;
+    g.prep.kcache = S.k + (size_t)l * S.layer_stride * r.kvesz;
+    g.prep.vcache = S.v + (size_t)l * S.layer_stride * r.kvesz;
+    g.prep.q_planes = (uint16_t*)(c->ws + L.qbuf);
+    g.prep_done = &prepped;
+  }
   HIPCHK(gemv<T>(c, g));
   if (rows_per_seq > 0) {
     // prefill chunk: QK-norm, RoPE, append for every row, then causal attention
@@ -326,6 +338,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.counters = (unsigned*)(c->ws + L.counters);
   a.out = att; a.ld_out = L.att_ld; a.out_planes = planes; a.B = B;
   a.q_planes = (uint16_t*)(c->ws + L.qbuf);   // the prefill q buffer is free while decoding
+  a.prepped = prepped;
   HIPCHK(prof_pre(c, DUALAR_K_ATTN));
   HIPCHK((launch_attn<T, KT>(a, c->stream)));
   if (c->prof_cls == DUALAR_K_ATTN) {

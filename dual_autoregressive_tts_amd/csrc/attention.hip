@@ -721,7 +721,7 @@ template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p0, 
       // slots per head: at most the head's tiles + 1 (a workgroup holds >= 1 unit
       // whenever U >= ng; with U < ng some hold none and the rest one each)
       p.max_splits = nt_max + 1;
-      hipLaunchKernelGGL((attn_prep_kernel<T, KT>), dim3(p.B, p.H + p.KV), dim3(64), 0, s, p);
+      if (!p.prepped) hipLaunchKernelGGL((attn_prep_kernel<T, KT>), dim3(p.B, p.H + p.KV), dim3(64), 0, s, p);
       switch (rep) {
         case 1: hipLaunchKernelGGL((attn_flash_kernel<1>), dim3(ng), dim3(DUALAR_WG), 0, s, p, ng); break;
         case 2: hipLaunchKernelGGL((attn_flash_kernel<2>), dim3(ng), dim3(DUALAR_WG), 0, s, p, ng); break;

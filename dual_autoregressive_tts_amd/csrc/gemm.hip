@@ -621,6 +621,50 @@ __global__ void __launch_bounds__(DUALAR_WG) sk_finish_kernel(GemvParams p) {
   }
   const float g4[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
   const float u4[4] = {v[NR - 1].x, v[NR - 1].y, v[NR - 1].z, v[NR - 1].w};
+  if (NR == 1 && p.prep.q_planes) {
+    // QKV output feeding the attention: tile t / Z is head hh, and the 32
+    // threads of this activation row (one half-wave) hold its 128 dims, four
+    // each: RMS over the half-wave, RoPE on the two local pairs.
+    const QkPrep& q = p.prep;
+    const int hh = t / Z, d0 = 4 * r4, hd = q.hd;
+    const int pos = q.pos ? q.pos[b] : q.pos_const;
+    float a[4] = {g4[0], g4[1], g4[2], g4[3]};
+    *(float4*)(p.y + (size_t)b * p.ldy + n0) = make_float4(a[0], a[1], a[2], a[3]);
+    const bool isq = hh < q.H, isk = !isq && hh < q.H + q.KV;
+    if (isq || isk) {
+      const void* gain = isq ? q.q_norm : q.k_norm;
+      if (gain) {
+        const float ss = group_sum((a[0] * a[0] + a[1] * a[1]) + (a[2] * a[2] + a[3] * a[3]), 32);
+        const float inv = 1.0f / sqrtf(ss / (float)hd + p.eps);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = a[e] * inv * bf16_bits_to_f32(((const uint16_t*)gain)[d0 + e]);
+      }
+      if (pos < 0) return;
+      const float2* rp = q.rope + (size_t)pos * (hd / 2) + d0 / 2;
+      float r[4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float2 cs = rp[k];
+        r[2 * k] = a[2 * k] * cs.x - a[2 * k + 1] * cs.y;
+        r[2 * k + 1] = a[2 * k] * cs.y + a[2 * k + 1] * cs.x;
+      }
+      if (isq) {
+        const float qscale = 1.0f / sqrtf((float)hd);
+        const size_t plane = (size_t)p.B * q.H * hd, at = ((size_t)b * q.H + hh) * hd + d0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_planes(q.q_planes, plane, at + e, r[e] * qscale);
+      } else {
+        uint16_t* kc = (uint16_t*)q.kcache + (((size_t)b * q.KV + (hh - q.H)) * q.max_pos + pos) * hd + d0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kc[e] = f32_to_bf16_rne(r[e]);
+      }
+    } else if (pos >= 0) {
+      uint16_t* vc = (uint16_t*)q.vcache + (((size_t)b * q.KV + (hh - q.H - q.KV)) * q.max_pos + pos) * hd + d0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vc[e] = f32_to_bf16_rne(a[e]);
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int n = n0 + e;
@@ -665,6 +709,11 @@ static void sk_finish(GemvParams& p, hipStream_t s) {
   constexpr int ROWS = 32 * WAVES * T;
   const int tiles = ((p.n_out + ROWS - 1) / ROWS) * ((p.B + 31) / 32);
   const size_t n = (size_t)tiles * 32 * S::ROWS / 4;
+  // the attention preparation applies when one row tile is one head
+  const bool prep = NR == 1 && p.prep.q_planes && p.mode == GEMV_STORE && !p.yplanes && S::ROWS == p.prep.hd &&
+                    p.n_out == (p.prep.H + 2 * p.prep.KV) * p.prep.hd;
+  if (!prep) p.prep.q_planes = nullptr;
+  if (p.prep_done) *p.prep_done = prep ? 1 : 0;
   hipLaunchKernelGGL((sk_finish_kernel<NR, WAVES, T>), dim3((unsigned)((n + DUALAR_WG - 1) / DUALAR_WG)),
                      dim3(DUALAR_WG), 0, s, p);
   // A residual product whose output feeds the next product: RMS-normalise
@@ -770,6 +819,7 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
     }
     cfg = glu ? 2 : (p.n_out >= 16384 ? 3 : 1);   // partial tiles do not fit: split-K form
   }
+  if (p.prep_done) *p.prep_done = 0;
   switch (cfg) {   // (NR, WAVES, T), slots = workgroups the chip holds at once (LDS bound)
     case 1: if (glu) launch_gm<2, 2, 1>(p, p0.ksw, 256, s, &ok); else launch_gm<1, 2, 1>(p, p0.ksw, 512, s, &ok); break;
     case 2: if (glu) launch_gm<2, 4, 1>(p, p0.ksw, 256, s, &ok); else launch_gm<1, 4, 1>(p, p0.ksw, 256, s, &ok); break;

@@ -5,6 +5,19 @@
 
 enum GemvMode { GEMV_STORE = 0, GEMV_ADD = 1, GEMV_SWIGLU = 2 };
 
+// Attention preparation that a QKV product's finish can apply to its output
+// (bf16 weights and cache, head_dim = the product's row tile): QK-norm, RoPE
+// and the score scale on q, written as three bf16 terms; QK-norm and RoPE on
+// k, and k and v appended to the cache at the row's position.
+struct QkPrep {
+  const float2* rope;                 // [max_pos][hd/2] (cos, sin)
+  const int* pos; int pos_const;      // row b's position (pos == NULL: pos_const)
+  const void* q_norm; const void* k_norm;
+  int H, KV, hd, max_pos;
+  void* kcache; void* vcache;         // this layer: [max_batch][KV][max_pos][hd] bf16
+  uint16_t* q_planes;                 // [3][B][H*hd]; NULL = no preparation
+};
+
 // y[b, :] = W . f(x[b, :]) for b < B, where f is RMSNorm-with-gain when
 // `gain` is set and the identity otherwise.  W is up to three [rows_i, K]
 // segments whose outputs are concatenated (STORE/ADD), or the gate/up pair
@@ -42,6 +55,9 @@ struct GemvParams {
   // work units dealt to the grid, workgroup g taking sk_q (+1 if g < sk_r)
   // consecutive units; partial tiles at part + (tile * sk_smax + slot) * TE
   int sk_q, sk_r, sk_smax, sk_nch;
+  // QKV product only: prepare the attention in the finish when the stream-K
+  // form runs (*prep_done = 1; y is written as well)
+  QkPrep prep; int* prep_done;
 };
 
 // Decode attention for one new position per sequence, split along the
@@ -64,6 +80,7 @@ struct AttnParams {
   float* out; int ld_out;             // [B][H*hd]
   uint16_t* out_planes;               // if set: o as planes [3][B][H*hd] instead of out
   uint16_t* q_planes;                 // scratch [3][B][H*hd] (flash-decoding form)
+  int prepped;                        // q_planes and the appended k/v are already written
   int B;
 };
 
