@@ -678,6 +678,68 @@ __global__ void __launch_bounds__(DUALAR_WG) sk_finish_kernel(GemvParams p) {
   }
 }
 
+// The stream-K finish of a residual product whose output feeds the next
+// product, one 1,024-thread workgroup per activation row b (n_out <= 4,096,
+// a multiple of 4): thread k sums the slots of output float4 k (contiguous
+// runs of a tile's row-major partial area, all loads issued together), adds
+// the residual, writes y, and the workgroup then RMS-normalises the row with
+// next_gain and writes it as three bf16 planes for the next product.
+#define SKR_T 1024
+template <int WAVES, int T>
+__global__ void __launch_bounds__(SKR_T) sk_finish_rows_kernel(GemvParams p) {
+  using S = Sk<1, WAVES, T>;
+  constexpr int ROWS = S::ROWS;
+  constexpr int KB = 16;                      // slots loaded together
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float red[SKR_T / 64];
+  const int nv = p.n_out / 4, Z = (p.B + 31) / 32, nch = p.sk_nch;
+  const bool live = tid < nv;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (live) {
+    const int n = 4 * tid, t = (n / ROWS) * Z + b / 32;
+    const float* src = p.part + (size_t)t * p.sk_smax * S::TE + (size_t)(b & 31) * ROWS + n % ROWS;
+    const int nsl = sk_owner(t * nch + nch - 1, p.sk_q, p.sk_r) - sk_owner(t * nch, p.sk_q, p.sk_r) + 1;
+    for (int k0 = 0; k0 < nsl; k0 += KB) {
+      float4 a[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+        if (k0 + u < nsl) a[u] = *(const float4*)(src + (size_t)(k0 + u) * S::TE);
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+        if (k0 + u < nsl) { v.x += a[u].x; v.y += a[u].y; v.z += a[u].z; v.w += a[u].w; }
+    }
+    const float4 r = *(const float4*)(p.res + (size_t)b * p.ldres + n);
+    v.x = r.x + v.x; v.y = r.y + v.y; v.z = r.z + v.z; v.w = r.w + v.w;
+    *(float4*)(p.y + (size_t)b * p.ldy + n) = v;
+  }
+  float ss = (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < SKR_T / 64; ++w) tot += red[w];
+  if (!live) return;
+  const float inv = 1.0f / sqrtf(tot / (float)p.n_out + p.eps);
+  const uint2 gg = ((const uint2*)p.next_gain)[tid];
+  const float o[4] = {v.x * inv * bf16_bits_to_f32(gg.x & 0xffffu), v.y * inv * bf16_bits_to_f32(gg.x >> 16),
+                      v.z * inv * bf16_bits_to_f32(gg.y & 0xffffu), v.w * inv * bf16_bits_to_f32(gg.y >> 16)};
+  uint32_t tt[3][4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t a0 = f32_to_bf16_rne(o[e]);
+    const float r1 = o[e] - bf16_bits_to_f32(a0);
+    const uint16_t a1 = f32_to_bf16_rne(r1);
+    tt[0][e] = a0;
+    tt[1][e] = a1;
+    tt[2][e] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(a1));
+  }
+  uint2* xs = (uint2*)p.next_planes;
+  const size_t plane = (size_t)p.B * nv, at = (size_t)b * nv + tid;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) xs[q * plane + at] = make_uint2(tt[q][0] | (tt[q][1] << 16), tt[q][2] | (tt[q][3] << 16));
+}
+
 // Stream-K plan: U = tiles x chunks work units dealt to the grid (false
 // when there is no partial buffer or the partial tiles do not fit it).
 template <int NR, int WAVES, int T>
@@ -708,6 +770,15 @@ static void sk_finish(GemvParams& p, hipStream_t s) {
   using S = Sk<NR, WAVES, T>;
   constexpr int ROWS = 32 * WAVES * T;
   const int tiles = ((p.n_out + ROWS - 1) / ROWS) * ((p.B + 31) / 32);
+  // a residual product feeding the next one: finish and normalise per row
+  const bool rows = NR == 1 && p.next_planes && p.mode == GEMV_ADD && !p.yplanes && p.n_out % 4 == 0 &&
+                    p.n_out <= 4 * SKR_T;
+  if (rows) {
+    if (p.next_done) *p.next_done = 1;
+    if (p.prep_done) *p.prep_done = 0;
+    hipLaunchKernelGGL((sk_finish_rows_kernel<WAVES, T>), dim3(p.B), dim3(SKR_T), 0, s, p);
+    return;
+  }
   const size_t n = (size_t)tiles * 32 * S::ROWS / 4;
   // the attention preparation applies when one row tile is one head
   const bool prep = NR == 1 && p.prep.q_planes && p.mode == GEMV_STORE && !p.yplanes && S::ROWS == p.prep.hd &&
