@@ -1,7 +1,7 @@
 """Benchmark: Dual-AR frames/s on one MI355X, with the HBM roofline of the
 dominant kernel and the CPU oracle timed beside it.
 
-    python bench.py [--steps K] [--warmup W] [--workload s2_b1|s2_b32|fast_s2|fast_s2_b16|tiny_b1]
+    python bench.py [--steps K] [--warmup W] [--workload s2_b1|s2_b32|s2_prefill|fast_s2|fast_s2_b16|tiny_b1]
                     [--semantic-head]
 
 A step is one decode frame of the whole hot path (fusion, slow pass, biased
@@ -32,7 +32,10 @@ WORKLOADS = {
     "fast_s2": ("fast_s2", 1, "S2-shaped fast AR alone, batch 1, greedy"),
     "fast_s2_b16": ("fast_s2", 16, "S2-shaped fast AR alone, batch 16, greedy"),
     "tiny_b1": ("tiny_b1", None, "tiny fp32 Dual-AR, batch 1, 32-token prompt, greedy"),
+    "s2_prefill": ("s2_prefill", None, "full S2-shaped prefill of 16,384 frame positions at batch 4 "
+                                       "(time to frame 0), then 64 greedy decode frames"),
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def log(*a):
@@ -254,6 +257,18 @@ def main():
                                   "launches": a["launches"]}
         ctx.sync()
 
+    prefill = {}
+    if wl_name == "s2_prefill" and ttff_ms:
+        # the prefill is the matrix-core roofline case: its flops over the time to frame 0
+        fl = reporting.prefill_flops(m, plen)
+        tf = fl["total"] / (ttff_ms * 1e-3) / 1e12
+        prefill["prefill"] = {"tokens": fl["tokens"], "flops": fl["total"], "linear_flops": fl["linear"],
+                              "attention_flops": fl["attention"], "ms": round(ttff_ms, 2),
+                              "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                           "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 5),
+                                           "traffic": None}}
+        log(f"[bench] prefill: {fl['total'] / 1e12:.0f} TFLOP in {ttff_ms:.0f} ms = {tf:.1f} TFLOP/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         del dev_w
@@ -275,6 +290,7 @@ def main():
         "step_hbm": {"bytes_per_step": round(step_bytes / K), "achieved_GBps": round(step_gbps, 1),
                      "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
         "ttff_ms": None if ttff_ms is None else round(ttff_ms, 2),
+        **prefill,
         "roofline": roofline,
         "cpu_baseline": cpu,
         **extra,

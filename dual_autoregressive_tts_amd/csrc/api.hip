@@ -147,7 +147,7 @@ Layout layout(const Resolved& r) {
   // planes written by a producer (attention output, SwiGLU output) for the
   // next product, while xn may still be read
   L.xn2 = take((size_t)L.rows * std::max(std::max(r.dim, r.ffn), std::max(r.fffn, L.att_ld)) * 6);
-  L.gpart_elems = r.max_batch >= 8 ? (size_t)32 * r.max_batch *
+  L.gpart_elems = r.max_batch >= 2 ? (size_t)32 * std::max(r.max_batch, 32) *
                                          std::max(std::max(2 * r.ffn, 2 * r.fffn), std::max(L.qkv_ld, r.dim))
                                    : 0;
   L.gpart = take(L.gpart_elems * 4);
@@ -284,7 +284,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   // With 8+ rows and bf16 weights the products run on the matrix cores, which
   // read their input as bf16 planes: the attention and SwiGLU outputs are then
   // written as planes (xn2) and the next product reads them directly.
-  uint16_t* planes = (sizeof(T) == 2 && B >= 8) ? (uint16_t*)(c->ws + L.xn2) : nullptr;
+  uint16_t* planes = (sizeof(T) == 2 && B >= 2) ? (uint16_t*)(c->ws + L.xn2) : nullptr;
   // The residual products (O, W2) split K over workgroups at these sizes; their
   // finish then also writes the next product's normalised input planes (xn).
   void* const xn = c->ws + L.xn;
@@ -393,7 +393,7 @@ dualar_status run_layer_kv_only(dualar_ctx* c, Stack& S, int l, float* x, int B,
   g.K = S.dim; g.n_out = 2 * S.KV * S.hd;
   g.x = x; g.ldx = S.dim; g.gain = w.attention_norm; g.eps = r.eps;
   g.y = qkv + (size_t)S.H * S.hd; g.ldy = L.qkv_ld; g.B = B; g.mode = GEMV_STORE;
-  if (sizeof(T) == 2 && B >= 8 && in_planes) g.xplanes = c->ws + L.xn;
+  if (sizeof(T) == 2 && B >= 2 && in_planes) g.xplanes = c->ws + L.xn;
   HIPCHK(gemv<T>(c, g));
   PrefillParams a{};
   a.qkv = qkv; a.ld_qkv = L.qkv_ld;

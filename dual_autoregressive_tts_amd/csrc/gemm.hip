@@ -851,13 +851,13 @@ static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, b
   *ok = true;
 }
 
-// Matrix-core path for bf16 weights, B >= 8, K a multiple of 64 (returns
+// Matrix-core path for bf16 weights, B >= 2, K a multiple of 64 (returns
 // false when it does not apply).  Shapes: SwiGLU 4 waves x 128 rows x (gate,
 // up); tall products (>= 16384 rows, e.g. the tied head) 4 waves x 2 tiles =
 // 256 rows; the rest 2 waves x 64 rows.  `slots` is how many such
 // workgroups the chip holds at once (LDS bound).
 bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
-  if (p0.B < 8 || p0.K % GM_KC != 0 || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
+  if (p0.B < 2 || p0.K % GM_KC != 0 || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
   GemvParams p = p0;
   if (p.xplanes) p.xn = const_cast<void*>(p.xplanes);   // input already split by its producer
   else hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);

@@ -529,7 +529,7 @@ static hipError_t pick_bt(const GemvParams& p, hipStream_t s) {
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     hipError_t e;
-    if (launch_gemm_mfma(p, s, &e)) return e;   // 8+ activation rows on the matrix cores
+    if (launch_gemm_mfma(p, s, &e)) return e;   // 2+ activation rows on the matrix cores
   }
   if (p.xplanes || p.yplanes) return hipErrorInvalidValue;   // planes exist on the matrix-core path only
   if (p.next_done) *p.next_done = 0;

@@ -34,7 +34,7 @@ struct GemvParams {
   const float* res; int ldres;   // GEMV_ADD: y = res + W.x (res may alias y)
   int B;
   int mode;
-  // scratch for the matrix-core path (B >= 8): the (normalised)
+  // scratch for the matrix-core path (B >= 2): the (normalised)
   // activations as three bf16 planes [3][B][K] (6*B*K bytes) and split-K
   // partial sums (part_elems floats)
   void* xn;

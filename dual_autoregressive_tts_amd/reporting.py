@@ -85,3 +85,19 @@ def frame_bytes(m: dict, ctx_lengths, fast_only: bool = False, semantic_head: bo
         out["gathers"] += B * (N + 1) * D * esz   # fusion rows
     out["total"] = sum(out.values())
     return out
+
+
+def prefill_flops(m: dict, prompt_lengths) -> dict:
+    """Arithmetic of a prefill (counted as multiply-add = 2 flops, bf16 MFMA
+    work as the pages' model would do it): the slow layers' products over
+    every prompt position, and causal attention, where position t of a
+    sequence attends to positions 0..t (q.k and p.v: 4*hd flops per pair and
+    query head).  The head, the sampler and the fast AR run once, for frame
+    0, and are not counted."""
+    per_layer = m["dim"] * (m["n_head"] * m["head_dim"] + 2 * m["n_kv_head"] * m["head_dim"]) + \
+        m["n_head"] * m["head_dim"] * m["dim"] + 3 * m["dim"] * m["ffn_dim"]
+    tokens = int(sum(int(t) for t in prompt_lengths))
+    linear = 2 * tokens * m["n_layer"] * per_layer
+    pairs = sum(int(t) * (int(t) + 1) // 2 for t in prompt_lengths)
+    attention = 4 * m["head_dim"] * m["n_head"] * m["n_layer"] * pairs
+    return {"linear": linear, "attention": attention, "total": linear + attention, "tokens": tokens}
