@@ -185,11 +185,207 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillParams p) {
     if (e < ne4) *(float4*)(dst + 16 * e + 4 * sl) = make_float4(o[e].x * inv, o[e].y * inv, o[e].z * inv, o[e].w * inv);
 }
 
+// Matrix-core causal attention for a bf16 cache with head_dim 128 and four
+// query heads per KV head.  Grid (ceil(C/32), KV, B), 256 threads: the
+// workgroup takes 32 consecutive positions of sequence b (rows b*C + i0..)
+// and wave w takes query head 4g + w.  Key blocks of 32 positions, from 0
+// to the block's last position, go through LDS (K row-swizzled, V
+// transposed and padded), loaded one block ahead into registers:
+//   scores S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K as the A operand:
+//   32 keys x 16 dims; q^T as the B operand: 32 queries, three bf16 terms of
+//   the fp32 q held in registers), so lane l holds 16 keys of query l % 32
+//   and the running max / sum of a query are a 16-value reduction plus one
+//   lane swap;
+//   O += P V with P as the A operand, taken from the same registers (three
+//   bf16 terms of the fp32 probabilities), which fixes the key order of a
+//   16-key step as 16s + 4h + {0..3, 8..11} in lane half h; V^T in LDS
+//   supplies the same keys for each output dim as two 8-byte reads.
+// All products are exact fp32 products of the stored operands, accumulated
+// in fp32.  Masked scores (key > query position, padding rows) are -inf.
+#define PF_QB 32
+#define PF_VTS 36                 // V^T row stride in 2-byte units (32 keys + 4 pad)
+typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float pf_f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void pf_split3(const float (&x)[8], pf_bf16x8* t) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 a0 = (__bf16)x[e];
+    const float r1 = x[e] - (float)a0;
+    const __bf16 a1 = (__bf16)r1;
+    t[0][e] = a0;
+    t[1][e] = a1;
+    t[2][e] = (__bf16)(r1 - (float)a1);
+  }
+}
+
+__global__ void __launch_bounds__(256) prefill_flash_kernel(PrefillParams p) {
+  constexpr int HD = 128;
+  const int qb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int i0 = qb * PF_QB;
+  const int last = min(i0 + PF_QB, p.C) - 1;
+  const int pmax = p.pos[b * p.C + last];
+  if (pmax < 0) return;                          // the whole block is padding (uniform)
+  const int nkb = pmax / 32 + 1;
+
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][32 * 128];          // K rows, 16-byte pieces swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][HD * PF_VTS];       // V^T, padded rows
+  __shared__ __attribute__((aligned(16))) float qv[4][32];                   // per-wave per-query scalars
+
+  // this lane's query (B column) and its three q terms for the eight 16-dim steps
+  const int iq = i0 + col;
+  const int posq = iq < p.C ? p.pos[b * p.C + iq] : -1;
+  const int hq = g * 4 + wave;
+  pf_bf16x8 qt[8][3];
+  {
+    const float* qrow = p.qbuf + (size_t)(b * p.C + (iq < p.C ? iq : last)) * p.ld_q + (size_t)hq * HD + 8 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      float x[8];
+      const float4 a = *(const float4*)(qrow + 16 * s), c = *(const float4*)(qrow + 16 * s + 4);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+      pf_split3(x, qt[s]);
+    }
+  }
+  const size_t head_base = ((size_t)b * p.KV + g) * p.max_pos;
+  const char* kg = (const char*)p.kcache + head_base * HD * 2;
+  const char* vg = (const char*)p.vcache + head_base * HD * 2;
+  // block loads: 32 keys x 16 pieces of 16 bytes = 512 pieces, two per thread
+  u32x4 kr[2], vr[2];
+  auto load_block = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i, key = kb * 32 + (u >> 4), pc = u & 15;
+      const size_t off = ((size_t)(key <= pmax ? key : 0) * HD + pc * 8) * 2;
+      kr[i] = ld_vec(kg + off);
+      vr[i] = ld_vec(vg + off);
+    }
+  };
+  auto store_block = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i, key = u >> 4, pc = u & 15;
+      *(u32x4*)&ks[buf][key * 128 + ((pc ^ (key & 15)) << 3)] = kr[i];
+      const uint32_t v4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vt[buf][(pc * 8 + e) * PF_VTS + key] = (uint16_t)((e & 1) ? (v4[e >> 1] >> 16) : (v4[e >> 1] & 0xffffu));
+    }
+  };
+
+  pf_f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;          // query col (both lane halves agree)
+  float* qvw = qv[wave];
+
+  load_block(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    store_block(buf);
+    if (kb + 1 < nkb) load_block(kb + 1);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // ---- S^T = K q^T: 32 keys x 32 queries ----
+    pf_f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int pc = 2 * s + h;
+      const pf_bf16x8 a = *(const pf_bf16x8*)&ks[buf][col * 128 + ((pc ^ (col & 15)) << 3)];
+#pragma unroll
+      for (int t = 0; t < 3; ++t) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qt[s][t], sacc, 0, 0, 0);
+    }
+    // register r holds key kb*32 + (r/4)*8 + 4h + r%4 of query col
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb * 32 + (r >> 2) * 8 + 4 * h + (r & 3);
+      if (key > posq) sacc[r] = -INFINITY;
+      mt = fmaxf(mt, sacc[r]);
+    }
+    mt = max_xor32(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    float pr[16], ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = expf(sacc[r] - m_use);
+      ls += pr[r];
+    }
+    ls = add_xor32(ls);
+    const float cf = expf(m_run - m_use);       // 0 while m_run = -inf
+    l_run = l_run * cf + ls;
+    m_run = m_new;
+    // rescale O: its rows are queries (r/4)*8 + 4h + r%4; the factors go through LDS
+    if (h == 0) qvw[col] = cf;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    float cq[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 c4 = *(const float4*)&qvw[8 * j + 4 * h];
+      cq[4 * j] = c4.x; cq[4 * j + 1] = c4.y; cq[4 * j + 2] = c4.z; cq[4 * j + 3] = c4.w;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= cq[r];
+    // ---- O += P V ----
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = pr[8 * s + j];
+      pf_bf16x8 pt[3];
+      pf_split3(x, pt);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        // V^T row of dim 32 dt + col, keys 16s + 4h + {0..3} and + 8
+        const uint16_t* vrow = &vt[buf][(32 * dt + col) * PF_VTS + 16 * s + 4 * h];
+        const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 8);
+        const u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
+        const pf_bf16x8 bb = __builtin_bit_cast(pf_bf16x8, bv);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pt[t], bb, o[dt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // ---- normalise and store: O row (r/4)*8 + 4h + r%4 is query i0 + that ----
+  if (h == 0) qvw[col] = l_run;
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qi = (r >> 2) * 8 + 4 * h + (r & 3);
+    const int iqo = i0 + qi;
+    if (iqo >= p.C) continue;
+    const int row = b * p.C + iqo;
+    if (p.pos[row] < 0) continue;
+    const float inv = 1.0f / qvw[qi];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const size_t colx = (size_t)hq * HD + 32 * dt + col;
+      const float v = o[dt][r] * inv;
+      if (p.out_planes) store_planes(p.out_planes, (size_t)p.R * p.H * HD, (size_t)row * p.H * HD + colx, v);
+      else p.out[(size_t)row * p.ld_out + colx] = v;
+    }
+  }
+}
+
 template <typename T, typename KT>
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   if (p.hd % 16 != 0 || p.hd > PF_MAXHD || p.H % p.KV != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_append_kernel<T, KT>), dim3(p.R, p.H + p.KV), dim3(64), 0, s, p, 0);
   const int rep = p.H / p.KV;
+  if (sizeof(KT) == 2 && p.hd == 128 && rep == 4) {
+    hipLaunchKernelGGL(prefill_flash_kernel, dim3((p.C + PF_QB - 1) / PF_QB, p.KV, p.B), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   const int qb = 64 / rep;
   const dim3 grid((p.C + qb - 1) / qb, p.KV, p.B);
   switch (rep) {
