@@ -111,7 +111,7 @@ def make_config(m: dict, max_batch: int, max_seq_len: int, inherit_fast: bool = 
     """Model dict (synth.MODELS layout) -> dualar_config.  With inherit_fast,
     fast_* sizes are passed as 0 (inherit) where they equal the slow ones.
     prefill_chunk: prompt positions per sequence per prefill step (0 = the
-    library's choice, 2048 rows per step)."""
+    library's choice, 8192 rows per step)."""
     c = Config()
     for f in ("n_layer", "dim", "n_head", "n_kv_head", "head_dim", "ffn_dim", "vocab_size",
               "n_fast_layer", "fast_dim", "fast_n_head", "fast_n_kv_head", "fast_head_dim",

@@ -100,7 +100,7 @@ bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
   REQ(r->eps >= 0.0f && isfinite(r->eps), "norm_eps must be >= 0");
   REQ(r->max_batch >= 1 && r->max_batch <= 256, "max_batch out of range [1, 256]");
   REQ(c->prefill_chunk >= 0 && c->prefill_chunk <= 4096, "prefill_chunk out of range [0, 4096]");
-  r->pc = c->prefill_chunk > 0 ? c->prefill_chunk : std::max(1, 2048 / r->max_batch);
+  r->pc = c->prefill_chunk > 0 ? c->prefill_chunk : std::min(4096, std::max(1, 8192 / r->max_batch));
   REQ(c->semantic_head == 0 || c->semantic_head == 1, "semantic_head must be 0 or 1");
   r->semantic_head = c->semantic_head;
   REQ(r->max_seq >= 2 && r->max_seq <= 65536, "max_seq_len out of range [2, 65536]");

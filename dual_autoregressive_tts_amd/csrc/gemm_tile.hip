@@ -1,0 +1,244 @@
+// Matrix products over many activation rows (the prefill steps: every
+// sequence's chunk of prompt positions at once) on the gfx950 matrix cores:
+// Y[b][n] = sum_k W[n][k] X[b][k], with the activations as three bf16 terms
+// (planes, x = t0 + t1 + t2 up to 2^-24 |x|) and bf16 weights, accumulated in
+// fp32 -- the same product as the decode-shaped kernels, which stream each
+// weight row once per 32 activation rows.  At hundreds of rows that re-reads
+// the weights many times over; here a workgroup owns a 2-D output tile of
+// NROWS weight rows x BROWS activation rows, so each loaded operand byte
+// feeds BROWS (weights) or NROWS (activations) multiply-adds per term.
+//
+// v_mfma_f32_32x32x16_bf16 with the activation term as the A operand (lane l
+// holds X_t[b0 + l%32][k + 8*(l/32) .. +8]) and the weights as the B operand
+// (lane l holds W[n0 + l%32][k + 8*(l/32) .. +8]): D[b][n] in register r of
+// lane l is row b = (r/4)*8 + (l/32)*4 + r%4, column n = l%32, so the 32
+// lanes of a half-wave store 32 consecutive outputs of one row.  The three
+// terms go into one accumulator (terms of one k-step in order t0, t1, t2).
+//
+// Four waves as 2 (weight rows) x 2 (activation rows); a wave owns 32*WN
+// weight rows x 32*WB activation rows.  K is walked in chunks of 32 (64
+// bytes per row); each chunk of weights (NROWS x 64 B) and activation planes
+// (3 x BROWS x 64 B) is copied by LDS DMA, 16 rows per instruction, piece p
+// of row r stored at slot p ^ ((r >> 2) & 3) so that the operand reads of 16
+// consecutive rows hit distinct banks.  Three stages: two chunks in flight
+// while one is multiplied; one barrier per chunk.
+//
+// SwiGLU tiles hold NROWS/2 output columns: wave half h (weight rows
+// [h*32*WN, (h+1)*32*WN)) holds gate rows then up rows of 16*WN columns, so
+// silu(gate) * up is formed in registers.
+//
+// Tiles are numbered in groups of TL_GB activation tiles (all weight tiles
+// of a group, then the next group) and dealt to the 8 XCDs in contiguous
+// ranges (workgroup id % 8 is its XCD): the ~32 workgroups an XCD runs at
+// once then cover about 4 weight tiles x 8 activation tiles and share both
+// operands through that XCD's L2.
+#include "mfma.h"
+
+#define TL_KC 32
+#define TL_GB 8
+
+template <int WN, int WB> struct Tl {
+  static constexpr int NROWS = 64 * WN;   // weight rows per tile
+  static constexpr int BROWS = 64 * WB;   // activation rows per tile
+  static constexpr int W_BYTES = NROWS * TL_KC * 2;
+  static constexpr int X_BYTES = 3 * BROWS * TL_KC * 2;
+  static constexpr int STAGE = W_BYTES + X_BYTES;
+  static constexpr int W_INSTR = W_BYTES / 1024 / 4;   // DMA instructions per wave per chunk
+  static constexpr int X_INSTR = X_BYTES / 1024 / 4;
+  static constexpr int DMA = W_INSTR + X_INSTR;
+  static_assert(W_BYTES % 4096 == 0 && X_BYTES % 4096 == 0, "DMA split");
+  static_assert(WN % 2 == 0, "SwiGLU pairs gate and up blocks");
+};
+
+template <int WN, int WB> struct TlSrc {
+  const char* w[Tl<WN, WB>::W_INSTR];
+  const char* x[Tl<WN, WB>::X_INSTR];
+};
+
+template <int WN, int WB>
+__device__ __forceinline__ void tl_issue(const TlSrc<WN, WB>& src, char* stage, int c, int wave) {
+  using L = Tl<WN, WB>;
+#pragma unroll
+  for (int j = 0; j < L::W_INSTR; ++j) dma16(src.w[j] + (size_t)c * TL_KC * 2, stage + (wave * L::W_INSTR + j) * 1024);
+  char* xs = stage + L::W_BYTES;
+#pragma unroll
+  for (int j = 0; j < L::X_INSTR; ++j) dma16(src.x[j] + (size_t)c * TL_KC * 2, xs + (wave * L::X_INSTR + j) * 1024);
+}
+
+// The two 16-wide k-steps of one chunk: the wave's WB x 3 activation
+// fragments and WN weight fragments, then 3*WN*WB products ordered so that
+// consecutive ones use different accumulators.
+template <int WN, int WB>
+__device__ __forceinline__ void tl_compute(const char* stage, int wn, int wb, int lane, f32x16 (*acc)[WB]) {
+  using L = Tl<WN, WB>;
+  const char* xs = stage + L::W_BYTES;
+  const int h = lane >> 5, l32 = lane & 31, sw = (l32 >> 2) & 3;
+#pragma unroll
+  for (int t = 0; t < TL_KC / 16; ++t) {
+    const int slot = ((2 * t + h) ^ sw) << 4;
+    bf16x8 xf[WB][3], wf[WN];
+#pragma unroll
+    for (int j = 0; j < WB; ++j)
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        xf[j][q] = *(const bf16x8*)(xs + q * (L::BROWS * 64) + (32 * (wb * WB + j) + l32) * 64 + slot);
+#pragma unroll
+    for (int i = 0; i < WN; ++i) wf[i] = *(const bf16x8*)(stage + (32 * (wn * WN + i) + l32) * 64 + slot);
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int i = 0; i < WN; ++i)
+#pragma unroll
+        for (int j = 0; j < WB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[j][q], wf[i], acc[i][j], 0, 0, 0);
+  }
+}
+
+// One-dimensional grid of 8 * ceil(tiles / 8) workgroups of 256 threads.
+// The host guarantees K % 32 == 0, B >= 1 and n_out >= 1.
+template <int WN, int WB>
+__global__ void __launch_bounds__(256, 1) mfma_tile_kernel(GemvParams p) {
+  using L = Tl<WN, WB>;
+  __shared__ __attribute__((aligned(1024))) char smem[3 * L::STAGE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave >> 1, wb = wave & 1;
+  const bool glu = p.mode == GEMV_SWIGLU;
+  const int cols = glu ? L::NROWS / 2 : L::NROWS;   // output columns per tile
+  const int tn = (p.n_out + cols - 1) / cols, tb = (p.B + L::BROWS - 1) / L::BROWS;
+  const int tiles = tn * tb, per = (tiles + 7) / 8;
+  const int li = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (li >= tiles) return;
+  const int grp = li / (TL_GB * tn), fb = grp * TL_GB, gs = min(TL_GB, tb - fb), rem = li - grp * TL_GB * tn;
+  const int n0 = (rem / gs) * cols, b0 = (fb + rem % gs) * L::BROWS;
+
+  // DMA sources of chunk 0: instruction i covers LDS rows 16 i .. 16 i + 15,
+  // lane -> row 16 i + lane/4, slot lane%4 (piece slot ^ ((row >> 2) & 3))
+  TlSrc<WN, WB> src;
+  {
+    const RowSpace rs(p);
+#pragma unroll
+    for (int j = 0; j < L::W_INSTR; ++j) {
+      const int r = 16 * (wave * L::W_INSTR + j) + (lane >> 2);
+      const int piece = (lane & 3) ^ ((r >> 2) & 3);
+      int n, seg = 0;
+      if (glu) {
+        const int within = r % (32 * WN);
+        seg = within / (16 * WN);
+        n = n0 + (r / (32 * WN)) * 16 * WN + within % (16 * WN);
+      } else {
+        n = n0 + r;
+      }
+      src.w[j] = rs.row(min(n, p.n_out - 1), seg) + piece * 16;
+    }
+    const uint16_t* xs = (const uint16_t*)p.xn;
+    const size_t plane = (size_t)p.B * p.K;
+#pragma unroll
+    for (int j = 0; j < L::X_INSTR; ++j) {
+      const int i = wave * L::X_INSTR + j;
+      const int q = i / (L::BROWS / 16), rr = 16 * (i % (L::BROWS / 16)) + (lane >> 2);
+      const int piece = (lane & 3) ^ ((rr >> 2) & 3);
+      const int b = min(b0 + rr, p.B - 1);   // rows past B: loaded, never stored
+      src.x[j] = (const char*)(xs + q * plane + (size_t)b * p.K) + piece * 16;
+    }
+  }
+
+  f32x16 acc[WN][WB];
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Chunk c is multiplied from stage c % 3 while chunks c+1 and c+2 are in
+  // flight.  Before chunk c+2 overwrites stage (c+2) % 3, every wave's copies
+  // of chunk c have landed (at most the next chunk's DMA outstanding) and
+  // every wave is done with chunk c-1 (barrier).  The steady loop has no
+  // branches; the last two chunks follow it.
+  const int nch = p.K / TL_KC;
+  tl_issue<WN, WB>(src, smem, 0, wave);
+  if (nch > 1) tl_issue<WN, WB>(src, smem + L::STAGE, 1, wave);
+  int cs = 0;   // stage of chunk c
+  for (int c = 0; c + 2 < nch; ++c) {
+    wait_vm_barrier<L::DMA>();
+    const int ns = cs == 0 ? 2 : cs - 1;   // (c + 2) % 3
+    tl_issue<WN, WB>(src, smem + ns * L::STAGE, c + 2, wave);
+    tl_compute<WN, WB>(smem + cs * L::STAGE, wn, wb, lane, acc);
+    cs = cs == 2 ? 0 : cs + 1;
+  }
+  if (nch > 1) {
+    wait_vm_barrier<L::DMA>();
+    tl_compute<WN, WB>(smem + cs * L::STAGE, wn, wb, lane, acc);
+    cs = cs == 2 ? 0 : cs + 1;
+  }
+  wait_vm_barrier<0>();
+  tl_compute<WN, WB>(smem + cs * L::STAGE, wn, wb, lane, acc);
+
+  // Epilogue straight from the accumulators: lanes 0..31 hold 32 consecutive
+  // columns of row b, lanes 32..63 the same columns of row b + 4.
+  const int l32 = lane & 31, h = lane >> 5;
+  const size_t plane_out = (size_t)p.B * p.n_out;
+  auto put = [&](int b, int n, float out) {
+    if (p.yplanes) store_planes((uint16_t*)p.yplanes, plane_out, (size_t)b * p.n_out + n, out);
+    else p.y[(size_t)b * p.ldy + n] = out;
+  };
+  if (glu) {
+#pragma unroll
+    for (int i = 0; i < WN / 2; ++i) {
+      const int n = n0 + wn * 16 * WN + 32 * i + l32;
+      if (n >= p.n_out) continue;
+#pragma unroll
+      for (int j = 0; j < WB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int b = b0 + 32 * (wb * WB + j) + (r >> 2) * 8 + h * 4 + (r & 3);
+          if (b < p.B) put(b, n, silu_f(acc[i][j][r]) * acc[i + WN / 2][j][r]);
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < WN; ++i) {
+    const int n = n0 + 32 * (wn * WN + i) + l32;
+    if (n >= p.n_out) continue;
+#pragma unroll
+    for (int j = 0; j < WB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int b = b0 + 32 * (wb * WB + j) + (r >> 2) * 8 + h * 4 + (r & 3);
+        if (b >= p.B) continue;
+        const float v = acc[i][j][r];
+        put(b, n, p.mode == GEMV_ADD ? p.res[(size_t)b * p.ldres + n] + v : v);
+      }
+  }
+}
+
+// Launch the tiled product (cfg 1: 256 weight rows x 128 activation rows,
+// cfg 2: 128 x 128).  The input planes are at p.xn.  Returns false when the
+// shape does not apply.
+bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
+  if (p.K % TL_KC != 0 || p.B < 1 || p.n_out < 1) return false;
+  auto grid = [&](int nrows, int brows) {
+    const int cols = p.mode == GEMV_SWIGLU ? nrows / 2 : nrows;
+    const int tiles = ((p.n_out + cols - 1) / cols) * ((p.B + brows - 1) / brows);
+    return dim3(8 * ((tiles + 7) / 8));
+  };
+  switch (cfg) {
+    case 1: hipLaunchKernelGGL((mfma_tile_kernel<4, 2>), grid(256, 128), dim3(256), 0, s, p); return true;
+    case 2: hipLaunchKernelGGL((mfma_tile_kernel<2, 2>), grid(128, 128), dim3(256), 0, s, p); return true;
+    default: return false;
+  }
+}
+
+// Tile shape for a product: the larger tile feeds twice the multiply-adds
+// per loaded byte, the smaller one fills the chip in finer steps.  Estimated
+// time = rounds of 256 resident workgroups x work per tile, the small tile
+// taken as 15% less efficient per multiply-add.
+int gemm_tile_choice(const GemvParams& p) {
+  auto rounds = [&](int nrows, int brows) {
+    const int cols = p.mode == GEMV_SWIGLU ? nrows / 2 : nrows;
+    const long tiles = (long)((p.n_out + cols - 1) / cols) * ((p.B + brows - 1) / brows);
+    return (tiles + 255) / 256;
+  };
+  return rounds(128, 128) * 115 < rounds(256, 128) * 200 ? 2 : 1;
+}

@@ -157,6 +157,9 @@ struct FastBeginParams {
 
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
 bool launch_gemm_mfma(const GemvParams& p, hipStream_t s, hipError_t* err);
+// tiled matrix-core product for hundreds of activation rows (input planes at p.xn)
+bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s);
+int gemm_tile_choice(const GemvParams& p);
 template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 template <typename T, typename KT> hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 // k/v append only (no q, no attention): rows are sequences, grid (R, KV)

@@ -83,7 +83,8 @@ typedef struct {
   int32_t max_seq_len;           /* slow-AR positions per sequence              */
   int32_t kv_dtype;              /* K/V cache type: dualar_dtype, -1 = weight_dtype */
   int32_t prefill_chunk;         /* prompt positions per sequence per prefill
-                                    step (0 = max(1, 2048 / max_batch)); the
+                                    step (0 = min(4096, max(1, 8192 /
+                                    max_batch))); the
                                     workspace holds max_batch * prefill_chunk
                                     activation rows                             */
   int32_t semantic_head;         /* 0: the tied head computes the whole
