@@ -233,12 +233,13 @@ bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
 // Tile shape for a product: the larger tile feeds twice the multiply-adds
 // per loaded byte, the smaller one fills the chip in finer steps.  Estimated
 // time = rounds of 256 resident workgroups x work per tile, the small tile
-// taken as 15% less efficient per multiply-add.
+// taken as 37% less efficient per multiply-add (as measured on the S2
+// prefill: ~30% against ~41% of the matrix-core peak).
 int gemm_tile_choice(const GemvParams& p) {
   auto rounds = [&](int nrows, int brows) {
     const int cols = p.mode == GEMV_SWIGLU ? nrows / 2 : nrows;
     const long tiles = (long)((p.n_out + cols - 1) / cols) * ((p.B + brows - 1) / brows);
     return (tiles + 255) / 256;
   };
-  return rounds(128, 128) * 115 < rounds(256, 128) * 200 ? 2 : 1;
+  return rounds(128, 128) * 137 < rounds(256, 128) * 200 ? 2 : 1;
 }

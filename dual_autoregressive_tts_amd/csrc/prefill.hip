@@ -186,26 +186,12 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillParams p) {
 }
 
 // Matrix-core causal attention for a bf16 cache with head_dim 128 and four
-// query heads per KV head.  Grid (ceil(C/32), KV, B), 256 threads: the
-// workgroup takes 32 consecutive positions of sequence b (rows b*C + i0..)
-// and wave w takes query head 4g + w.  Key blocks of 32 positions, from 0
-// to the block's last position, go through LDS (K row-swizzled, V
-// transposed and padded), loaded one block ahead into registers:
-//   scores S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K as the A operand:
-//   32 keys x 16 dims; q^T as the B operand: 32 queries, three bf16 terms of
-//   the fp32 q held in registers), so lane l holds 16 keys of query l % 32
-//   and the running max / sum of a query are a 16-value reduction plus one
-//   lane swap;
-//   O += P V with P as the A operand, taken from the same registers (three
-//   bf16 terms of the fp32 probabilities), which fixes the key order of a
-//   16-key step as 16s + 4h + {0..3, 8..11} in lane half h; V^T in LDS
-//   supplies the same keys for each output dim as two 8-byte reads.
-// All products are exact fp32 products of the stored operands, accumulated
-// in fp32.  Masked scores (key > query position, padding rows) are -inf.
-#define PF_QB 32
+// query heads per KV head (prefill_flash16_kernel below).  All products are
+// exact fp32 products of the stored operands (q and the probabilities as
+// three bf16 terms), accumulated in fp32.  Masked scores (key > query
+// position, padding rows) are -inf.
 #define PF_VTS 36                 // V^T row stride in 2-byte units (32 keys + 4 pad)
 typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
-typedef float pf_f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ void pf_split3(const float (&x)[8], pf_bf16x8* t) {
 #pragma unroll
@@ -219,31 +205,56 @@ __device__ __forceinline__ void pf_split3(const float (&x)[8], pf_bf16x8* t) {
   }
 }
 
-__global__ void __launch_bounds__(256) prefill_flash_kernel(PrefillParams p) {
+// Grid: one workgroup of 256 threads per (16 consecutive positions of
+// sequence b, KV head g); wave w takes query head 4g + w.  The 1-D grid maps
+// id -> (query block qb, g, b) with the query blocks in descending order, so
+// the blocks with the most keys start first.  Key blocks of 32 positions,
+// from 0 to the block's last position, go through LDS (K row-swizzled, V
+// transposed with padded rows), loaded one block ahead into registers.  Per
+// key block, on v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T as two 16-key x 16-query products (K as the A operand: lane
+//   l holds key l%16 of the half, dims 32s + 8(l/16) .. +8; q^T as the B
+//   operand: query l%16, the same dims, three bf16 terms held in registers),
+//   so lane l holds keys 16h + 4(l/16) + {0..3}, h = 0, 1, of query l%16;
+//   O^T += V^T P^T with P^T as the B operand straight from those registers
+//   (three bf16 terms; k index 8(l/16) + j is key 16(j/4) + 4(l/16) + j%4)
+//   and V^T as the A operand (dim 16 dt + l%16, the same keys: two 8-byte
+//   LDS reads), so lane l holds O^T rows 16 dt + 4(l/16) + r of query l%16
+//   and the running max, sum and rescale of its query are lane-local after
+//   reductions over the four lanes of a query.
+// Sixteen queries per wave keep a wave at ~160 registers, so three waves
+// share each SIMD and one wave's softmax and LDS waits hide under another's
+// products (32 queries per wave with 32x32 products needed 318 registers:
+// one wave per SIMD, 1.7 s against 1.05 s for the 16,384-position prefill).
+#define PF16_QB 16
+typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) prefill_flash16_kernel(PrefillParams p, int nqb) {
   constexpr int HD = 128;
-  const int qb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, col = lane & 31;
-  const int i0 = qb * PF_QB;
-  const int last = min(i0 + PF_QB, p.C) - 1;
+  const int per_qb = p.KV * p.B;
+  const int qb = nqb - 1 - (int)blockIdx.x / per_qb, rest = (int)blockIdx.x % per_qb;
+  const int g = rest % p.KV, b = rest / p.KV;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
+  const int i0 = qb * PF16_QB;
+  const int last = min(i0 + PF16_QB, p.C) - 1;
   const int pmax = p.pos[b * p.C + last];
   if (pmax < 0) return;                          // the whole block is padding (uniform)
   const int nkb = pmax / 32 + 1;
 
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][32 * 128];          // K rows, 16-byte pieces swizzled
   __shared__ __attribute__((aligned(16))) uint16_t vt[2][HD * PF_VTS];       // V^T, padded rows
-  __shared__ __attribute__((aligned(16))) float qv[4][32];                   // per-wave per-query scalars
 
-  // this lane's query (B column) and its three q terms for the eight 16-dim steps
+  // this lane's query and its three q terms for the four 32-dim steps
   const int iq = i0 + col;
   const int posq = iq < p.C ? p.pos[b * p.C + iq] : -1;
   const int hq = g * 4 + wave;
-  pf_bf16x8 qt[8][3];
+  pf_bf16x8 qt[4][3];
   {
-    const float* qrow = p.qbuf + (size_t)(b * p.C + (iq < p.C ? iq : last)) * p.ld_q + (size_t)hq * HD + 8 * h;
+    const float* qrow = p.qbuf + (size_t)(b * p.C + (iq < p.C ? iq : last)) * p.ld_q + (size_t)hq * HD + 8 * grp;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < 4; ++s) {
       float x[8];
-      const float4 a = *(const float4*)(qrow + 16 * s), c = *(const float4*)(qrow + 16 * s + 4);
+      const float4 a = *(const float4*)(qrow + 32 * s), c = *(const float4*)(qrow + 32 * s + 4);
       x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
       pf_split3(x, qt[s]);
     }
@@ -274,13 +285,12 @@ __global__ void __launch_bounds__(256) prefill_flash_kernel(PrefillParams p) {
     }
   };
 
-  pf_f32x16 o[4];
+  pf_f32x4 o[8];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;          // query col (both lane halves agree)
-  float* qvw = qv[wave];
+    for (int r = 0; r < 4; ++r) o[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;          // of query col (the four lanes of a query agree)
 
   load_block(0);
   for (int kb = 0; kb < nkb; ++kb) {
@@ -288,91 +298,76 @@ __global__ void __launch_bounds__(256) prefill_flash_kernel(PrefillParams p) {
     store_block(buf);
     if (kb + 1 < nkb) load_block(kb + 1);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // ---- S^T = K q^T: 32 keys x 32 queries ----
-    pf_f32x16 sacc;
+    // ---- S^T = K q^T: two halves of 16 keys x 16 queries ----
+    pf_f32x4 sacc[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int pc = 2 * s + h;
-      const pf_bf16x8 a = *(const pf_bf16x8*)&ks[buf][col * 128 + ((pc ^ (col & 15)) << 3)];
+      for (int r = 0; r < 4; ++r) sacc[h][r] = 0.f;
+      const int key = 16 * h + col;
 #pragma unroll
-      for (int t = 0; t < 3; ++t) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qt[s][t], sacc, 0, 0, 0);
+      for (int s = 0; s < 4; ++s) {
+        const int pc = 4 * s + grp;
+        const pf_bf16x8 a = *(const pf_bf16x8*)&ks[buf][key * 128 + ((pc ^ (key & 15)) << 3)];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qt[s][t], sacc[h], 0, 0, 0);
+      }
     }
-    // register r holds key kb*32 + (r/4)*8 + 4h + r%4 of query col
+    // register r of half h: key kb*32 + 16h + 4 grp + r of query col
     float mt = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb * 32 + (r >> 2) * 8 + 4 * h + (r & 3);
-      if (key > posq) sacc[r] = -INFINITY;
-      mt = fmaxf(mt, sacc[r]);
-    }
-    mt = max_xor32(mt);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kb * 32 + 16 * h + 4 * grp + r;
+        if (key > posq) sacc[h][r] = -INFINITY;
+        mt = fmaxf(mt, sacc[h][r]);
+      }
+    mt = max_xor32(max_xor16(mt));
     const float m_new = fmaxf(m_run, mt);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    float pr[16], ls = 0.f;
+    float x[8], ls = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pr[r] = expf(sacc[r] - m_use);
-      ls += pr[r];
+    for (int j = 0; j < 8; ++j) {
+      x[j] = expf(sacc[j >> 2][j & 3] - m_use);
+      ls += x[j];
     }
-    ls = add_xor32(ls);
+    ls = add_xor32(add_xor16(ls));
     const float cf = expf(m_run - m_use);       // 0 while m_run = -inf
     l_run = l_run * cf + ls;
     m_run = m_new;
-    // rescale O: its rows are queries (r/4)*8 + 4h + r%4; the factors go through LDS
-    if (h == 0) qvw[col] = cf;
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    float cq[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 c4 = *(const float4*)&qvw[8 * j + 4 * h];
-      cq[4 * j] = c4.x; cq[4 * j + 1] = c4.y; cq[4 * j + 2] = c4.z; cq[4 * j + 3] = c4.w;
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[dt][r] *= cf;
+    // ---- O^T += V^T P^T ----
+    pf_bf16x8 pt[3];
+    pf_split3(x, pt);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      // V^T row of dim 16 dt + col, keys 4 grp + {0..3} and 16 + 4 grp + {0..3}
+      const uint16_t* vrow = &vt[buf][(16 * dt + col) * PF_VTS + 4 * grp];
+      const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 16);
+      const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+      const pf_bf16x8 aa = __builtin_bit_cast(pf_bf16x8, av);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, pt[t], o[dt], 0, 0, 0);
     }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= cq[r];
-    // ---- O += P V ----
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = pr[8 * s + j];
-      pf_bf16x8 pt[3];
-      pf_split3(x, pt);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        // V^T row of dim 32 dt + col, keys 16s + 4h + {0..3} and + 8
-        const uint16_t* vrow = &vt[buf][(32 * dt + col) * PF_VTS + 16 * s + 4 * h];
-        const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 8);
-        const u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
-        const pf_bf16x8 bb = __builtin_bit_cast(pf_bf16x8, bv);
-#pragma unroll
-        for (int t = 0; t < 3; ++t) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pt[t], bb, o[dt], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
   }
-  // ---- normalise and store: O row (r/4)*8 + 4h + r%4 is query i0 + that ----
-  if (h == 0) qvw[col] = l_run;
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // ---- normalise and store: lane holds dims 16 dt + 4 grp + r of query col ----
+  if (iq >= p.C || posq < 0) return;
+  const int row = b * p.C + iq;
+  const float inv = 1.0f / l_run;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int qi = (r >> 2) * 8 + 4 * h + (r & 3);
-    const int iqo = i0 + qi;
-    if (iqo >= p.C) continue;
-    const int row = b * p.C + iqo;
-    if (p.pos[row] < 0) continue;
-    const float inv = 1.0f / qvw[qi];
+  for (int dt = 0; dt < 8; ++dt) {
+    const size_t colx = (size_t)hq * HD + 16 * dt + 4 * grp;
+    if (p.out_planes) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const size_t colx = (size_t)hq * HD + 32 * dt + col;
-      const float v = o[dt][r] * inv;
-      if (p.out_planes) store_planes(p.out_planes, (size_t)p.R * p.H * HD, (size_t)row * p.H * HD + colx, v);
-      else p.out[(size_t)row * p.ld_out + colx] = v;
+      for (int r = 0; r < 4; ++r)
+        store_planes(p.out_planes, (size_t)p.R * p.H * HD, (size_t)row * p.H * HD + colx + r, o[dt][r] * inv);
+    } else {
+      *(float4*)(p.out + (size_t)row * p.ld_out + colx) =
+          make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
     }
   }
 }
@@ -383,7 +378,8 @@ hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   hipLaunchKernelGGL((prefill_append_kernel<T, KT>), dim3(p.R, p.H + p.KV), dim3(64), 0, s, p, 0);
   const int rep = p.H / p.KV;
   if (sizeof(KT) == 2 && p.hd == 128 && rep == 4) {
-    hipLaunchKernelGGL(prefill_flash_kernel, dim3((p.C + PF_QB - 1) / PF_QB, p.KV, p.B), dim3(256), 0, s, p);
+    const int nqb = (p.C + PF16_QB - 1) / PF16_QB;
+    hipLaunchKernelGGL(prefill_flash16_kernel, dim3(nqb * p.KV * p.B), dim3(256), 0, s, p, nqb);
     return hipGetLastError();
   }
   const int qb = 64 / rep;
