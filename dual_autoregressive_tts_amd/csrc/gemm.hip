@@ -35,6 +35,9 @@
 
 #define GM_KC 64                     // k per chunk
 #define GM_STAGES 3
+#ifndef GM_SK_CFG
+#define GM_SK_CFG 15                 // stream-K shape of the decode products (11..16)
+#endif
 #define GM_TILE_ROWS 256             // from this many activation rows: 2-D tiles (gemm_tile.hip)
 
 // Workgroup shape: WAVES waves, each owning T 32-row output tiles (times NR
@@ -105,8 +108,8 @@ __device__ __forceinline__ void gm_issue(const GmSrc<G>& src, char* stage, int c
 // term has its own accumulator, so the three products of a step do not wait
 // on each other.
 template <int NR, int T, class G>
-__device__ __forceinline__ void gm_compute(const char* stage, int wave, int lane, f32x16 (*acc)[NR][3]) {
-  const char* xs = stage + G::W_BYTES;
+__device__ __forceinline__ void gm_compute_wx(const char* stage, const char* xs, int wave, int lane,
+                                              f32x16 (*acc)[NR][3]) {
   const int h = lane >> 5, b = lane & 31;
   const int bsw = (b >> 1) & 7;
 #pragma unroll
@@ -126,6 +129,10 @@ __device__ __forceinline__ void gm_compute(const char* stage, int wave, int lane
           acc[tt][s][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, tx[q], acc[tt][s][q], 0, 0, 0);
       }
   }
+}
+template <int NR, int T, class G>
+__device__ __forceinline__ void gm_compute(const char* stage, int wave, int lane, f32x16 (*acc)[NR][3]) {
+  gm_compute_wx<NR, T, G>(stage, stage + G::W_BYTES, wave, lane, acc);
 }
 
 // One pipeline step: chunk cc from stage S; chunk cc+2 goes to stage
@@ -523,6 +530,160 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_sk_kernel(GemvParams p) {
   }
 }
 
+// Wave-specialised stream-K.  In mfma_sk_kernel every LDS stage holds a
+// weight chunk and the 12 KB of activation planes it is multiplied with, and
+// a wave's copies complete in issue order, so at most 48-64 KB of weights
+// are ever in flight per compute unit.  Here WAVES compute waves copy only
+// the weight chunks (WS stages, WS - 1 chunks ahead) and multiply, and one
+// more wave copies only the planes (XS slots, XS - 1 chunks ahead): each
+// wave's vmcnt then counts one kind of copy, waiting for a chunk's planes
+// never waits for newer weight copies, and the LDS the planes no longer
+// share holds a deeper weight pipeline (96 KB in flight).  One barrier per
+// chunk for all waves; the partial tiles and their finish are those of
+// mfma_sk_kernel.
+template <int NR, int WAVES, int T, int WS, int XS>
+struct Skw {
+  using G = Gm<NR, WAVES, T>;
+  static constexpr int WI = G::W_BYTES / 1024 / WAVES;   // weight copies per compute wave per chunk
+  static constexpr int XI = G::X_BYTES / 1024;           // plane copies per chunk (the plane wave)
+  static constexpr int LDS = WS * G::W_BYTES + XS * G::X_BYTES;
+  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(WS >= 2 && XS >= 2 && (WS - 2) * WI < 64 && (XS - 2) * XI < 64, "vmcnt range");
+};
+
+// s_waitcnt vmcnt(a * STEP) + barrier for a runtime a in 0..MAXA.
+template <int STEP, int MAXA> __device__ __forceinline__ void wait_ahead_barrier(int a) {
+  if constexpr (MAXA <= 0) {
+    wait_vm_barrier<0>();
+  } else {
+    if (a >= MAXA) wait_vm_barrier<MAXA * STEP>();
+    else wait_ahead_barrier<STEP, MAXA - 1>(a);
+  }
+}
+
+template <int NR, int WAVES, int T, int WS, int XS>
+__global__ void __launch_bounds__(64 * (WAVES + 1)) mfma_skw_kernel(GemvParams p) {
+  using G = Gm<NR, WAVES, T>;
+  using K = Skw<NR, WAVES, T, WS, XS>;
+  __shared__ __attribute__((aligned(1024))) char lds[K::LDS];
+  char* const wst = lds;                        // weight stage i at wst + i * W_BYTES
+  char* const xsl = lds + WS * G::W_BYTES;      // plane slot i at xsl + i * X_BYTES
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = blockIdx.x, q = p.sk_q, rr = p.sk_r, nch = p.sk_nch;
+  const int u0 = g * q + min(g, rr);
+  const int nf = q + (g < rr ? 1 : 0);
+  if (nf == 0) return;
+  const int Z = (p.B + 31) / 32;
+
+  if (wave == WAVES) {
+    // ---- the plane wave: chunk f's planes to slot f % XS ----
+    const uint16_t* xs = (const uint16_t*)p.xn;
+    const size_t plane = (size_t)p.B * p.K;
+    const char* src[K::XI];
+    int xt = u0 / nch, xc = u0 % nch;
+    auto sources = [&]() {
+      const int b0 = (xt % Z) * 32;
+#pragma unroll
+      for (int j = 0; j < K::XI; ++j) {
+        const int qq = j >> 2, r8 = 8 * (j & 3) + (lane >> 3);
+        const int piece = (lane & 7) ^ ((r8 >> 1) & 7);
+        const int b = b0 + r8 < p.B ? b0 + r8 : 0;   // padding columns: never stored
+        src[j] = (const char*)(xs + qq * plane + (size_t)b * p.K + piece * 8);
+      }
+    };
+    auto issue = [&](int f) {
+      char* dst = xsl + (f % XS) * G::X_BYTES;
+#pragma unroll
+      for (int j = 0; j < K::XI; ++j) dma16(src[j] + (size_t)xc * GM_KC * 2, dst + j * 1024);
+      if (++xc == nch) {
+        xc = 0;
+        ++xt;
+        sources();
+      }
+    };
+    sources();
+    for (int f = 0; f < XS - 1 && f < nf; ++f) issue(f);
+    for (int f = 0; f < nf; ++f) {
+      wait_ahead_barrier<K::XI, XS - 2>(min(nf - 1 - f, XS - 2));
+      if (f + XS - 1 < nf) issue(f + XS - 1);
+    }
+    return;
+  }
+
+  // ---- compute waves: weight chunk f to stage f % WS, multiply ----
+  const RowSpace rs(p);
+  const char* src[K::WI];
+  int it = u0 / nch, ic = u0 % nch;
+  auto sources = [&]() {
+    const int n0 = (it / Z) * G::ROWS;
+#pragma unroll
+    for (int j = 0; j < K::WI; ++j) {
+      const int i = wave * K::WI + j;
+      const int r = 8 * i + (lane >> 3);
+      const int piece = (lane & 7) ^ ((r >> 1) & 7);
+      const int n = min(n0 + r % G::ROWS, p.n_out - 1);
+      src[j] = rs.row(n, r / G::ROWS) + (size_t)piece * 16;
+    }
+  };
+  auto issue = [&](int f) {
+    char* dst = wst + (f % WS) * G::W_BYTES;
+#pragma unroll
+    for (int j = 0; j < K::WI; ++j) dma16(src[j] + (size_t)ic * GM_KC * 2, dst + (wave * K::WI + j) * 1024);
+    if (++ic == nch) {
+      ic = 0;
+      ++it;
+      sources();
+    }
+  };
+  f32x16 acc[T][NR][3];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+    for (int s = 0; s < NR; ++s)
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tt][s][j][r] = 0.f;
+
+  sources();
+  for (int f = 0; f < WS - 1 && f < nf; ++f) issue(f);
+  int ct = u0 / nch, cc = u0 % nch;   // compute side: tile / chunk of the next chunk to multiply
+  bool drain = false;   // partial-sum stores are in flight: wait for everything
+  for (int f = 0; f < nf; ++f) {
+    if (drain) wait_vm_barrier<0>();
+    else wait_ahead_barrier<K::WI, WS - 2>(min(nf - 1 - f, WS - 2));
+    drain = false;
+    if (f + WS - 1 < nf) issue(f + WS - 1);
+    gm_compute_wx<NR, T, G>(wst + (f % WS) * G::W_BYTES, xsl + (f % XS) * G::X_BYTES, wave, lane, acc);
+    if (++cc == nch || f == nf - 1) {
+      const int slot = g - sk_owner(ct * nch, q, rr);
+      float* dst = p.part + ((size_t)ct * p.sk_smax + slot) * Sk<NR, WAVES, T>::TE;
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+        for (int sN = 0; sN < NR; ++sN) {
+          float* d = dst + (size_t)(sN * 32 + (lane & 31)) * G::ROWS + 32 * (wave * T + tt) + 4 * (lane >> 5);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float4 v;
+            v.x = acc[tt][sN][0][4 * j + 0] + (acc[tt][sN][1][4 * j + 0] + acc[tt][sN][2][4 * j + 0]);
+            v.y = acc[tt][sN][0][4 * j + 1] + (acc[tt][sN][1][4 * j + 1] + acc[tt][sN][2][4 * j + 1]);
+            v.z = acc[tt][sN][0][4 * j + 2] + (acc[tt][sN][1][4 * j + 2] + acc[tt][sN][2][4 * j + 2]);
+            v.w = acc[tt][sN][0][4 * j + 3] + (acc[tt][sN][1][4 * j + 3] + acc[tt][sN][2][4 * j + 3]);
+            *(float4*)(d + 8 * j) = v;
+          }
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[tt][sN][j][r] = 0.f;
+        }
+      drain = true;
+      cc = 0;
+      ++ct;
+    }
+  }
+}
+
 #define SK_KB 8   // partial slots loaded together
 
 // Sum each tile's slots (slot order) and apply the epilogue.  Thread th of
@@ -747,6 +908,15 @@ static void sk_finish(GemvParams& p, hipStream_t s) {
   }
 }
 
+template <int NR, int WAVES, int T, int WS, int XS>
+static bool launch_skw(GemvParams& p, hipStream_t s) {
+  int ng = 0;
+  if (!sk_plan<NR, WAVES, T>(p, 256, &ng)) return false;
+  hipLaunchKernelGGL((mfma_skw_kernel<NR, WAVES, T, WS, XS>), dim3(ng), dim3(64 * (WAVES + 1)), 0, s, p);
+  sk_finish<NR, WAVES, T>(p, s);
+  return true;
+}
+
 // Plans and launches the stream-K form; false when it does not apply (no
 // partial buffer, or the partial tiles do not fit it).  `slots` = workgroups
 // the chip holds at once.
@@ -818,7 +988,7 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   if (!cfg) {
     // stream-K for the decode shapes; the tall head (hundreds of row tiles)
     // balances well as it is and its partials would be as large as its output
-    if (z_tiles <= 2 && p.K / GM_KC >= 8 && p0.ksw == 0 && p.n_out < 16384) cfg = 11;
+    if (z_tiles <= 2 && p.K / GM_KC >= 8 && p0.ksw == 0 && p.n_out < 16384) cfg = GM_SK_CFG;
     else cfg = glu ? 2 : (p.n_out >= 16384 ? 3 : 1);
   }
   if (cfg >= 11) {   // stream-K shapes (slots: one 4-wave workgroup per compute unit)
@@ -828,6 +998,8 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
       case 12: done = glu ? false : launch_sk<1, 4, 2, 3>(p, 256, s); break;
       case 13: done = glu ? launch_sk<2, 2, 1, 3>(p, 256, s) : launch_sk<1, 2, 1, 4>(p, 512, s); break;
       case 14: done = glu ? false : launch_sk<1, 4, 1, 3>(p, 256, s); break;
+      case 15: done = glu ? launch_skw<2, 4, 1, 4, 2>(p, s) : launch_skw<1, 4, 1, 7, 3>(p, s); break;
+      case 16: done = glu ? launch_skw<2, 4, 1, 4, 2>(p, s) : launch_skw<1, 4, 2, 4, 2>(p, s); break;
       default: break;
     }
     if (done) {
