@@ -188,6 +188,9 @@ struct dualar_ctx {
   std::vector<int> plen;
   int frames_done = 0;   // decode frames since prefill (same for every sequence)
   std::vector<int> step_pos;  // host mirror of the positions of the current slow step
+  // prefill step: activation tiles (GEMM_TILE_BROWS rows) that hold prompt rows
+  uint64_t pf_live[2] = {0, 0};
+  int pf_masked = 0;
   SeqState st;
   // measurement (dualar_profile_begin/end)
   int prof_cls = -1;
@@ -265,6 +268,15 @@ double attn_positions(dualar_ctx* c, int B) {
   return s;
 }
 
+// Prefill steps: only the activation tiles that hold prompt rows go to the
+// products' 2-D tile form.
+void live_tiles(const dualar_ctx* c, GemvParams& g, int rows_per_seq) {
+  if (rows_per_seq <= 0 || !c->pf_masked) return;
+  g.live_bt[0] = c->pf_live[0];
+  g.live_bt[1] = c->pf_live[1];
+  g.bt_masked = 1;
+}
+
 // One transformer layer over B activation rows.  Decode: row b is sequence
 // b at position pos_dev[b] (or pos_const).  Prefill (rows_per_seq > 0): row r
 // is position pos_dev[r] of sequence r / rows_per_seq (-1 = padding).
@@ -296,6 +308,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g.K = S.dim; g.n_out = (S.H + 2 * S.KV) * S.hd;
   g.x = x; g.ldx = S.dim; g.gain = w.attention_norm; g.eps = r.eps;
   g.y = qkv; g.ldy = L.qkv_ld; g.B = B; g.mode = GEMV_STORE;
+  live_tiles(c, g, rows_per_seq);
   if (planes && in_planes) g.xplanes = xn;
   in_planes = false;
   // batched decode with a bf16 cache: the QKV finish also prepares the
@@ -352,6 +365,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g = GemvParams{};
   g.w[0] = w.wo; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.H * S.hd; g.n_out = S.dim;
   g.x = att; g.ldx = L.att_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
+  live_tiles(c, g, rows_per_seq);
   g.xplanes = planes;
   if (planes) { g.next_gain = w.ffn_norm; g.next_planes = xn; g.next_done = &fused; g.eps = r.eps; }
   HIPCHK(gemv<T>(c, g));
@@ -360,6 +374,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g.w[0] = w.w1; g.w[1] = w.w3; g.rows[0] = S.ffn; g.rows[1] = S.ffn; g.n_seg = 2;
   g.K = S.dim; g.n_out = S.ffn; g.x = x; g.ldx = S.dim; g.gain = w.ffn_norm; g.eps = r.eps;
   g.y = ffn; g.ldy = L.ffn_ld; g.B = B; g.mode = GEMV_SWIGLU;
+  live_tiles(c, g, rows_per_seq);
   g.yplanes = planes;
   if (fused) g.xplanes = xn;
   HIPCHK(gemv<T>(c, g));
@@ -367,6 +382,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g = GemvParams{};
   g.w[0] = w.w2; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.ffn; g.n_out = S.dim;
   g.x = ffn; g.ldx = L.ffn_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
+  live_tiles(c, g, rows_per_seq);
   g.xplanes = planes;
   fused = 0;
   if (planes && l + 1 < S.n_layer) {
@@ -548,6 +564,18 @@ dualar_status do_prefill(dualar_ctx* c, int B, const int* tokens, int t_max, con
   for (int k = 0; k < n_steps; ++k) {
     const int s0 = t_max - (n_steps - k) * C;     // global step of row i = 0
     for (int b = 0; b < B; ++b) c->step_pos[b] = s0 + C - 1 - (t_max - c->plen[b]);
+    // row b*C + i is position s0 + i - (t_max - plen[b]), a prompt row when >= 0
+    const int nbt = (B * C + GEMM_TILE_BROWS - 1) / GEMM_TILE_BROWS;
+    c->pf_masked = nbt <= 128;
+    c->pf_live[0] = c->pf_live[1] = 0;
+    if (c->pf_masked) {
+      for (int b = 0; b < B; ++b) {
+        const int first = std::max(0, (t_max - c->plen[b]) - s0);
+        if (first >= C) continue;
+        for (int j = (b * C + first) / GEMM_TILE_BROWS; j <= (b * C + C - 1) / GEMM_TILE_BROWS; ++j)
+          c->pf_live[j >> 6] |= 1ull << (j & 63);
+      }
+    }
     dualar_status st = embed<T>(c, B, tokens, t_max, s0, 1, C);
     if (st) return st;
     bool pl = false;
@@ -556,6 +584,7 @@ dualar_status do_prefill(dualar_ctx* c, int B, const int* tokens, int t_max, con
       if (st) return st;
     }
   }
+  c->pf_masked = 0;
   // the last row of every sequence is its position plen - 1
   HIPCHK(hipMemcpy2DAsync(c->ws + c->L.x_slow, (size_t)r.dim * 4, xp + (size_t)(C - 1) * r.dim, (size_t)C * r.dim * 4,
                           (size_t)r.dim * 4, B, hipMemcpyDeviceToDevice, c->stream));

@@ -36,7 +36,7 @@
 #define GM_KC 64                     // k per chunk
 #define GM_STAGES 3
 #ifndef GM_SK_CFG
-#define GM_SK_CFG 15                 // stream-K shape of the decode products (11..16)
+#define GM_SK_CFG 15                 // stream-K shape of the decode products (11..15)
 #endif
 #define GM_TILE_ROWS 256             // from this many activation rows: 2-D tiles (gemm_tile.hip)
 
@@ -538,8 +538,13 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_sk_kernel(GemvParams p) {
 // more wave copies only the planes (XS slots, XS - 1 chunks ahead): each
 // wave's vmcnt then counts one kind of copy, waiting for a chunk's planes
 // never waits for newer weight copies, and the LDS the planes no longer
-// share holds a deeper weight pipeline (96 KB in flight).  One barrier per
-// chunk for all waves; the partial tiles and their finish are those of
+// share holds the weight pipeline.  The planes must be copied as far ahead
+// as the weights: a compute unit's copies appear to be served in issue
+// order across its waves, so planes issued one chunk ahead still wait
+// behind every weight chunk in flight (batch 32: weights 2 chunks ahead and
+// planes 1 ahead took 36.8 us for W1|W3, both 2 ahead 33.9 us; for the
+// other products 4 and 4 matched 5 and 3, 6 and 4).  One barrier per chunk
+// for all waves; the partial tiles and their finish are those of
 // mfma_sk_kernel.
 template <int NR, int WAVES, int T, int WS, int XS>
 struct Skw {
@@ -998,8 +1003,7 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
       case 12: done = glu ? false : launch_sk<1, 4, 2, 3>(p, 256, s); break;
       case 13: done = glu ? launch_sk<2, 2, 1, 3>(p, 256, s) : launch_sk<1, 2, 1, 4>(p, 512, s); break;
       case 14: done = glu ? false : launch_sk<1, 4, 1, 3>(p, 256, s); break;
-      case 15: done = glu ? launch_skw<2, 4, 1, 4, 2>(p, s) : launch_skw<1, 4, 1, 7, 3>(p, s); break;
-      case 16: done = glu ? launch_skw<2, 4, 1, 4, 2>(p, s) : launch_skw<1, 4, 2, 4, 2>(p, s); break;
+      case 15: done = glu ? launch_skw<2, 4, 1, 3, 3>(p, s) : launch_skw<1, 4, 1, 5, 5>(p, s); break;
       default: break;
     }
     if (done) {

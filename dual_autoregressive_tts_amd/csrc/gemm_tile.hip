@@ -48,6 +48,7 @@ template <int WN, int WB> struct Tl {
   static constexpr int DMA = W_INSTR + X_INSTR;
   static_assert(W_BYTES % 4096 == 0 && X_BYTES % 4096 == 0, "DMA split");
   static_assert(WN % 2 == 0, "SwiGLU pairs gate and up blocks");
+  static_assert(BROWS == GEMM_TILE_BROWS, "the prefill live-tile mask counts tiles of GEMM_TILE_BROWS rows");
 };
 
 template <int WN, int WB> struct TlSrc {
@@ -94,6 +95,16 @@ __device__ __forceinline__ void tl_compute(const char* stage, int wn, int wb, in
   }
 }
 
+// Index of the n-th set bit (from 0) of the two-word mask, n < its population.
+__device__ __forceinline__ int nth_live_tile(const uint64_t (&m)[2], int n) {
+  const int c0 = __popcll(m[0]);
+  const int word = n < c0 ? 0 : 1;
+  uint64_t w = word ? m[1] : m[0];
+  if (word) n -= c0;
+  for (int i = 0; i < n; ++i) w &= w - 1;   // clear the n lowest set bits
+  return 64 * word + __ffsll((long long)w) - 1;
+}
+
 // One-dimensional grid of 8 * ceil(tiles / 8) workgroups of 256 threads.
 // The host guarantees K % 32 == 0, B >= 1 and n_out >= 1.
 template <int WN, int WB>
@@ -104,12 +115,16 @@ __global__ void __launch_bounds__(256, 1) mfma_tile_kernel(GemvParams p) {
   const int wn = wave >> 1, wb = wave & 1;
   const bool glu = p.mode == GEMV_SWIGLU;
   const int cols = glu ? L::NROWS / 2 : L::NROWS;   // output columns per tile
-  const int tn = (p.n_out + cols - 1) / cols, tb = (p.B + L::BROWS - 1) / L::BROWS;
+  // activation tiles: all of them, or the live ones of a prefill step
+  const int tb = p.bt_masked ? __popcll(p.live_bt[0]) + __popcll(p.live_bt[1]) : (p.B + L::BROWS - 1) / L::BROWS;
+  const int tn = (p.n_out + cols - 1) / cols;
   const int tiles = tn * tb, per = (tiles + 7) / 8;
   const int li = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (li >= tiles) return;
   const int grp = li / (TL_GB * tn), fb = grp * TL_GB, gs = min(TL_GB, tb - fb), rem = li - grp * TL_GB * tn;
-  const int n0 = (rem / gs) * cols, b0 = (fb + rem % gs) * L::BROWS;
+  int bt = fb + rem % gs;
+  if (p.bt_masked) bt = nth_live_tile(p.live_bt, bt);
+  const int n0 = (rem / gs) * cols, b0 = bt * L::BROWS;
 
   // DMA sources of chunk 0: instruction i covers LDS rows 16 i .. 16 i + 15,
   // lane -> row 16 i + lane/4, slot lane%4 (piece slot ^ ((row >> 2) & 3))
@@ -218,14 +233,17 @@ __global__ void __launch_bounds__(256, 1) mfma_tile_kernel(GemvParams p) {
 // shape does not apply.
 bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
   if (p.K % TL_KC != 0 || p.B < 1 || p.n_out < 1) return false;
-  auto grid = [&](int nrows, int brows) {
+  const int tb = p.bt_masked ? __builtin_popcountll(p.live_bt[0]) + __builtin_popcountll(p.live_bt[1])
+                            : (p.B + GEMM_TILE_BROWS - 1) / GEMM_TILE_BROWS;
+  if (tb == 0) return true;   // a prefill step without prompt rows: nothing to compute
+  auto grid = [&](int nrows) {
     const int cols = p.mode == GEMV_SWIGLU ? nrows / 2 : nrows;
-    const int tiles = ((p.n_out + cols - 1) / cols) * ((p.B + brows - 1) / brows);
+    const int tiles = ((p.n_out + cols - 1) / cols) * tb;
     return dim3(8 * ((tiles + 7) / 8));
   };
   switch (cfg) {
-    case 1: hipLaunchKernelGGL((mfma_tile_kernel<4, 2>), grid(256, 128), dim3(256), 0, s, p); return true;
-    case 2: hipLaunchKernelGGL((mfma_tile_kernel<2, 2>), grid(128, 128), dim3(256), 0, s, p); return true;
+    case 1: hipLaunchKernelGGL((mfma_tile_kernel<4, 2>), grid(256), dim3(256), 0, s, p); return true;
+    case 2: hipLaunchKernelGGL((mfma_tile_kernel<2, 2>), grid(128), dim3(256), 0, s, p); return true;
     default: return false;
   }
 }
@@ -236,10 +254,12 @@ bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
 // taken as 37% less efficient per multiply-add (as measured on the S2
 // prefill: ~30% against ~41% of the matrix-core peak).
 int gemm_tile_choice(const GemvParams& p) {
-  auto rounds = [&](int nrows, int brows) {
+  const int tb = p.bt_masked ? __builtin_popcountll(p.live_bt[0]) + __builtin_popcountll(p.live_bt[1])
+                            : (p.B + GEMM_TILE_BROWS - 1) / GEMM_TILE_BROWS;
+  auto rounds = [&](int nrows) {
     const int cols = p.mode == GEMV_SWIGLU ? nrows / 2 : nrows;
-    const long tiles = (long)((p.n_out + cols - 1) / cols) * ((p.B + brows - 1) / brows);
+    const long tiles = (long)((p.n_out + cols - 1) / cols) * tb;
     return (tiles + 255) / 256;
   };
-  return rounds(128, 128) * 137 < rounds(256, 128) * 200 ? 2 : 1;
+  return rounds(128) * 137 < rounds(256) * 200 ? 2 : 1;
 }

@@ -58,7 +58,13 @@ struct GemvParams {
   // QKV product only: prepare the attention in the finish when the stream-K
   // form runs (*prep_done = 1; y is written as well)
   QkPrep prep; int* prep_done;
+  // prefill steps: bit j of live_bt set = activation rows [GEMM_TILE_BROWS j,
+  // GEMM_TILE_BROWS (j + 1)) hold at least one prompt position; the 2-D tile
+  // form deals out only those tiles (the outputs of padding rows are never
+  // read).  bt_masked = 0: every row is live.
+  uint64_t live_bt[2]; int bt_masked;
 };
+#define GEMM_TILE_BROWS 128   // activation rows per tile of the 2-D tile form
 
 // Decode attention for one new position per sequence, split along the
 // context; also applies QK-norm + RoPE to the new q and k and appends the
