@@ -15,7 +15,7 @@
 // lanes of a half-wave store 32 consecutive outputs of one row.  The three
 // terms go into one accumulator (terms of one k-step in order t0, t1, t2).
 //
-// Four waves as 2 (weight rows) x 2 (activation rows); a wave owns 32*WN
+// GN x GW waves as GN (weight rows) x GW (activation rows); a wave owns 32*WN
 // weight rows x 32*WB activation rows.  K is walked in chunks of 32 (64
 // bytes per row); each chunk of weights (NROWS x 64 B) and activation planes
 // (3 x BROWS x 64 B) is copied by LDS DMA, 16 rows per instruction, piece p
@@ -23,7 +23,7 @@
 // consecutive rows hit distinct banks.  Three stages: two chunks in flight
 // while one is multiplied; one barrier per chunk.
 //
-// SwiGLU tiles hold NROWS/2 output columns: wave half h (weight rows
+// SwiGLU tiles hold NROWS/2 output columns: wave row h (weight rows
 // [h*32*WN, (h+1)*32*WN)) holds gate rows then up rows of 16*WN columns, so
 // silu(gate) * up is formed in registers.
 //
@@ -37,28 +37,29 @@
 #define TL_KC 32
 #define TL_GB 8
 
-template <int WN, int WB> struct Tl {
-  static constexpr int NROWS = 64 * WN;   // weight rows per tile
-  static constexpr int BROWS = 64 * WB;   // activation rows per tile
+template <int WN, int WB, int GN, int GW> struct Tl {
+  static constexpr int WAVES = GN * GW;   // GN wave rows (weights) x GW wave columns (activations)
+  static constexpr int NROWS = 32 * WN * GN;   // weight rows per tile
+  static constexpr int BROWS = 32 * WB * GW;   // activation rows per tile
   static constexpr int W_BYTES = NROWS * TL_KC * 2;
   static constexpr int X_BYTES = 3 * BROWS * TL_KC * 2;
   static constexpr int STAGE = W_BYTES + X_BYTES;
-  static constexpr int W_INSTR = W_BYTES / 1024 / 4;   // DMA instructions per wave per chunk
-  static constexpr int X_INSTR = X_BYTES / 1024 / 4;
+  static constexpr int W_INSTR = W_BYTES / 1024 / WAVES;   // DMA instructions per wave per chunk
+  static constexpr int X_INSTR = X_BYTES / 1024 / WAVES;
   static constexpr int DMA = W_INSTR + X_INSTR;
-  static_assert(W_BYTES % 4096 == 0 && X_BYTES % 4096 == 0, "DMA split");
+  static_assert(W_BYTES % (1024 * WAVES) == 0 && X_BYTES % (1024 * WAVES) == 0, "DMA split");
   static_assert(WN % 2 == 0, "SwiGLU pairs gate and up blocks");
   static_assert(BROWS == GEMM_TILE_BROWS, "the prefill live-tile mask counts tiles of GEMM_TILE_BROWS rows");
 };
 
-template <int WN, int WB> struct TlSrc {
-  const char* w[Tl<WN, WB>::W_INSTR];
-  const char* x[Tl<WN, WB>::X_INSTR];
+template <int WN, int WB, int GN, int GW> struct TlSrc {
+  const char* w[Tl<WN, WB, GN, GW>::W_INSTR];
+  const char* x[Tl<WN, WB, GN, GW>::X_INSTR];
 };
 
-template <int WN, int WB>
-__device__ __forceinline__ void tl_issue(const TlSrc<WN, WB>& src, char* stage, int c, int wave) {
-  using L = Tl<WN, WB>;
+template <int WN, int WB, int GN, int GW>
+__device__ __forceinline__ void tl_issue(const TlSrc<WN, WB, GN, GW>& src, char* stage, int c, int wave) {
+  using L = Tl<WN, WB, GN, GW>;
 #pragma unroll
   for (int j = 0; j < L::W_INSTR; ++j) dma16(src.w[j] + (size_t)c * TL_KC * 2, stage + (wave * L::W_INSTR + j) * 1024);
   char* xs = stage + L::W_BYTES;
@@ -69,9 +70,9 @@ __device__ __forceinline__ void tl_issue(const TlSrc<WN, WB>& src, char* stage, 
 // The two 16-wide k-steps of one chunk: the wave's WB x 3 activation
 // fragments and WN weight fragments, then 3*WN*WB products ordered so that
 // consecutive ones use different accumulators.
-template <int WN, int WB>
+template <int WN, int WB, int GN, int GW>
 __device__ __forceinline__ void tl_compute(const char* stage, int wn, int wb, int lane, f32x16 (*acc)[WB]) {
-  using L = Tl<WN, WB>;
+  using L = Tl<WN, WB, GN, GW>;
   const char* xs = stage + L::W_BYTES;
   const int h = lane >> 5, l32 = lane & 31, sw = (l32 >> 2) & 3;
 #pragma unroll
@@ -107,12 +108,12 @@ __device__ __forceinline__ int nth_live_tile(const uint64_t (&m)[2], int n) {
 
 // One-dimensional grid of 8 * ceil(tiles / 8) workgroups of 256 threads.
 // The host guarantees K % 32 == 0, B >= 1 and n_out >= 1.
-template <int WN, int WB>
-__global__ void __launch_bounds__(256, 1) mfma_tile_kernel(GemvParams p) {
-  using L = Tl<WN, WB>;
+template <int WN, int WB, int GN, int GW>
+__global__ void __launch_bounds__(64 * GN * GW, 1) mfma_tile_kernel(GemvParams p) {
+  using L = Tl<WN, WB, GN, GW>;
   __shared__ __attribute__((aligned(1024))) char smem[3 * L::STAGE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wn = wave >> 1, wb = wave & 1;
+  const int wn = wave / GW, wb = wave % GW;
   const bool glu = p.mode == GEMV_SWIGLU;
   const int cols = glu ? L::NROWS / 2 : L::NROWS;   // output columns per tile
   // activation tiles: all of them, or the live ones of a prefill step
@@ -128,7 +129,7 @@ __global__ void __launch_bounds__(256, 1) mfma_tile_kernel(GemvParams p) {
 
   // DMA sources of chunk 0: instruction i covers LDS rows 16 i .. 16 i + 15,
   // lane -> row 16 i + lane/4, slot lane%4 (piece slot ^ ((row >> 2) & 3))
-  TlSrc<WN, WB> src;
+  TlSrc<WN, WB, GN, GW> src;
   {
     const RowSpace rs(p);
 #pragma unroll
@@ -171,23 +172,23 @@ __global__ void __launch_bounds__(256, 1) mfma_tile_kernel(GemvParams p) {
   // every wave is done with chunk c-1 (barrier).  The steady loop has no
   // branches; the last two chunks follow it.
   const int nch = p.K / TL_KC;
-  tl_issue<WN, WB>(src, smem, 0, wave);
-  if (nch > 1) tl_issue<WN, WB>(src, smem + L::STAGE, 1, wave);
+  tl_issue<WN, WB, GN, GW>(src, smem, 0, wave);
+  if (nch > 1) tl_issue<WN, WB, GN, GW>(src, smem + L::STAGE, 1, wave);
   int cs = 0;   // stage of chunk c
   for (int c = 0; c + 2 < nch; ++c) {
     wait_vm_barrier<L::DMA>();
     const int ns = cs == 0 ? 2 : cs - 1;   // (c + 2) % 3
-    tl_issue<WN, WB>(src, smem + ns * L::STAGE, c + 2, wave);
-    tl_compute<WN, WB>(smem + cs * L::STAGE, wn, wb, lane, acc);
+    tl_issue<WN, WB, GN, GW>(src, smem + ns * L::STAGE, c + 2, wave);
+    tl_compute<WN, WB, GN, GW>(smem + cs * L::STAGE, wn, wb, lane, acc);
     cs = cs == 2 ? 0 : cs + 1;
   }
   if (nch > 1) {
     wait_vm_barrier<L::DMA>();
-    tl_compute<WN, WB>(smem + cs * L::STAGE, wn, wb, lane, acc);
+    tl_compute<WN, WB, GN, GW>(smem + cs * L::STAGE, wn, wb, lane, acc);
     cs = cs == 2 ? 0 : cs + 1;
   }
   wait_vm_barrier<0>();
-  tl_compute<WN, WB>(smem + cs * L::STAGE, wn, wb, lane, acc);
+  tl_compute<WN, WB, GN, GW>(smem + cs * L::STAGE, wn, wb, lane, acc);
 
   // Epilogue straight from the accumulators: lanes 0..31 hold 32 consecutive
   // columns of row b, lanes 32..63 the same columns of row b + 4.
@@ -228,9 +229,10 @@ __global__ void __launch_bounds__(256, 1) mfma_tile_kernel(GemvParams p) {
   }
 }
 
-// Launch the tiled product (cfg 1: 256 weight rows x 128 activation rows,
-// cfg 2: 128 x 128).  The input planes are at p.xn.  Returns false when the
-// shape does not apply.
+// Launch the tiled product: cfg 1: 256 weight rows x 128 activation rows, 4
+// waves; cfg 2: 128 x 128, 4 waves; cfg 3: 256 x 128, 8 waves of 64 x 64.
+// The input planes are at p.xn.  Returns false when the shape does not
+// apply.
 bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
   if (p.K % TL_KC != 0 || p.B < 1 || p.n_out < 1) return false;
   const int tb = p.bt_masked ? __builtin_popcountll(p.live_bt[0]) + __builtin_popcountll(p.live_bt[1])
@@ -242,24 +244,15 @@ bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
     return dim3(8 * ((tiles + 7) / 8));
   };
   switch (cfg) {
-    case 1: hipLaunchKernelGGL((mfma_tile_kernel<4, 2>), grid(256), dim3(256), 0, s, p); return true;
-    case 2: hipLaunchKernelGGL((mfma_tile_kernel<2, 2>), grid(128), dim3(256), 0, s, p); return true;
+    case 1: hipLaunchKernelGGL((mfma_tile_kernel<4, 2, 2, 2>), grid(256), dim3(256), 0, s, p); return true;
+    case 2: hipLaunchKernelGGL((mfma_tile_kernel<2, 2, 2, 2>), grid(128), dim3(256), 0, s, p); return true;
+    case 3: hipLaunchKernelGGL((mfma_tile_kernel<2, 2, 4, 2>), grid(256), dim3(512), 0, s, p); return true;
     default: return false;
   }
 }
 
-// Tile shape for a product: the larger tile feeds twice the multiply-adds
-// per loaded byte, the smaller one fills the chip in finer steps.  Estimated
-// time = rounds of 256 resident workgroups x work per tile, the small tile
-// taken as 37% less efficient per multiply-add (as measured on the S2
-// prefill: ~30% against ~41% of the matrix-core peak).
-int gemm_tile_choice(const GemvParams& p) {
-  const int tb = p.bt_masked ? __builtin_popcountll(p.live_bt[0]) + __builtin_popcountll(p.live_bt[1])
-                            : (p.B + GEMM_TILE_BROWS - 1) / GEMM_TILE_BROWS;
-  auto rounds = [&](int nrows) {
-    const int cols = p.mode == GEMV_SWIGLU ? nrows / 2 : nrows;
-    const long tiles = (long)((p.n_out + cols - 1) / cols) * tb;
-    return (tiles + 255) / 256;
-  };
-  return rounds(128) * 137 < rounds(256) * 200 ? 2 : 1;
-}
+// Tile shape for a product.  The 8-wave 256 x 128 tile (two waves per SIMD,
+// so one wave's LDS waits and barrier hide under the other's products) ran
+// the S2 prefill products at 37-48 % of the matrix-core peak over the three
+// terms, against 30-41 % for the 4-wave tiles at any shape.
+int gemm_tile_choice(const GemvParams&) { return 3; }
