@@ -18,6 +18,7 @@
 // fp32 throughout; K/V are read at the cache's precision.
 #include "common.h"
 #include "internal.h"
+#include "mfma.h"
 
 #define PF_TK 32          // cache positions per LDS tile
 #define PF_MAXHD 128
@@ -190,8 +191,9 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillParams p) {
 // exact fp32 products of the stored operands (q and the probabilities as
 // three bf16 terms), accumulated in fp32.  Masked scores (key > query
 // position, padding rows) are -inf.
-#define PF_VTS 36                 // V^T row stride in 2-byte units (32 keys + 4 pad)
+#define PF_STG 3                  // K/V block stages: two blocks in flight while one is used
 typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short pf_s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void pf_split3(const float (&x)[8], pf_bf16x8* t) {
 #pragma unroll
@@ -209,20 +211,27 @@ __device__ __forceinline__ void pf_split3(const float (&x)[8], pf_bf16x8* t) {
 // sequence b, KV head g); wave w takes query head 4g + w.  The 1-D grid maps
 // id -> (query block qb, g, b) with the query blocks in descending order, so
 // the blocks with the most keys start first.  Key blocks of 32 positions,
-// from 0 to the block's last position, go through LDS (K row-swizzled, V
-// transposed with padded rows), loaded one block ahead into registers.  Per
-// key block, on v_mfma_f32_16x16x32_bf16:
+// from 0 to the block's last position, are copied into LDS by LDS DMA
+// (global_load_lds_dwordx4), K and V alike as 256-byte key rows whose
+// 16-byte pieces sit at slot piece ^ (key & 15), PF_STG stages deep (each
+// wave copies a quarter of a block; its own vmcnt wait plus the barrier
+// make the block visible).  Per key block, on v_mfma_f32_16x16x32_bf16:
 //   S^T = K Q^T as two 16-key x 16-query products (K as the A operand: lane
 //   l holds key l%16 of the half, dims 32s + 8(l/16) .. +8; q^T as the B
 //   operand: query l%16, the same dims, three bf16 terms held in registers),
 //   so lane l holds keys 16h + 4(l/16) + {0..3}, h = 0, 1, of query l%16;
 //   O^T += V^T P^T with P^T as the B operand straight from those registers
 //   (three bf16 terms; k index 8(l/16) + j is key 16(j/4) + 4(l/16) + j%4)
-//   and V^T as the A operand (dim 16 dt + l%16, the same keys: two 8-byte
-//   LDS reads), so lane l holds O^T rows 16 dt + 4(l/16) + r of query l%16
-//   and the running max, sum and rescale of its query are lane-local after
-//   reductions over the four lanes of a query.
-// Sixteen queries per wave keep a wave at ~160 registers, so three waves
+//   and V^T as the A operand, read from the row-major V block with the
+//   gfx950 transposing LDS read ds_read_b64_tr_b16: within each 16-lane
+//   group, lane j receives element j%4 of the 8-byte words read by lanes
+//   4e + j/4 (e = 0..3), so lane (g, i) reading 4 consecutive dims
+//   16 dt + 4(i%4) of key 4g + i/4 (+16) hands lane (g, d) the four keys
+//   its operand needs for dim 16 dt + d.  Lane l holds O^T rows
+//   16 dt + 4(l/16) + r of query l%16, so the running max, sum and rescale
+//   of its query are lane-local after reductions over the four lanes of a
+//   query.
+// Sixteen queries per wave keep a wave at ~150 registers, so three waves
 // share each SIMD and one wave's softmax and LDS waits hide under another's
 // products (32 queries per wave with 32x32 products needed 318 registers:
 // one wave per SIMD, 1.7 s against 1.05 s for the 16,384-position prefill).
@@ -241,8 +250,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   if (pmax < 0) return;                          // the whole block is padding (uniform)
   const int nkb = pmax / 32 + 1;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][32 * 128];          // K rows, 16-byte pieces swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][HD * PF_VTS];       // V^T, padded rows
+  // [stage][K, V][32 key rows of 256 bytes, pieces swizzled]
+  __shared__ __attribute__((aligned(1024))) char kv[PF_STG][2][32 * 256];
 
   // this lane's query and its three q terms for the four 32-dim steps
   const int iq = i0 + col;
@@ -262,26 +271,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   const size_t head_base = ((size_t)b * p.KV + g) * p.max_pos;
   const char* kg = (const char*)p.kcache + head_base * HD * 2;
   const char* vg = (const char*)p.vcache + head_base * HD * 2;
-  // block loads: 32 keys x 16 pieces of 16 bytes = 512 pieces, two per thread
-  u32x4 kr[2], vr[2];
-  auto load_block = [&](int kb) __attribute__((always_inline)) {
+  // block kb to stage st: 16 DMA instructions of 4 key rows (1 KB) each, four
+  // per wave (waves 0-1: K, 2-3: V); lane l takes piece (l%16) ^ (key & 15)
+  // of key 4i + l/16, which lands at slot l%16 of that row
+  auto issue = [&](int kb, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = tid + 256 * i, key = kb * 32 + (u >> 4), pc = u & 15;
-      const size_t off = ((size_t)(key <= pmax ? key : 0) * HD + pc * 8) * 2;
-      kr[i] = ld_vec(kg + off);
-      vr[i] = ld_vec(vg + off);
-    }
-  };
-  auto store_block = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = tid + 256 * i, key = u >> 4, pc = u & 15;
-      *(u32x4*)&ks[buf][key * 128 + ((pc ^ (key & 15)) << 3)] = kr[i];
-      const uint32_t v4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vt[buf][(pc * 8 + e) * PF_VTS + key] = (uint16_t)((e & 1) ? (v4[e >> 1] >> 16) : (v4[e >> 1] & 0xffffu));
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * wave + j, isv = i >> 3, ii = i & 7;
+      const int kl = 4 * ii + (lane >> 4), key = kb * 32 + kl;
+      const int piece = (lane & 15) ^ (kl & 15);
+      const char* src = (isv ? vg : kg) + ((size_t)(key <= pmax ? key : 0) * HD + piece * 8) * 2;
+      dma16(src, &kv[st][isv][ii * 1024]);
     }
   };
 
@@ -292,12 +292,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     for (int r = 0; r < 4; ++r) o[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;          // of query col (the four lanes of a query agree)
 
-  load_block(0);
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
+  int st = 0;
   for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    store_block(buf);
-    if (kb + 1 < nkb) load_block(kb + 1);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // this wave's copies of block kb are done once at most the next block's
+    // four are outstanding; after the barrier every wave's are, and every
+    // wave is done with the stage block kb + 2 overwrites
+    if (kb + 1 < nkb) wait_vm_barrier<4>();
+    else wait_vm_barrier<0>();
+    if (kb + 2 < nkb) issue(kb + 2, st == 0 ? 2 : st - 1);
+    const char* ks = kv[st][0];
+    const char* vs = kv[st][1];
     // ---- S^T = K q^T: two halves of 16 keys x 16 queries ----
     pf_f32x4 sacc[2];
 #pragma unroll
@@ -308,7 +314,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int pc = 4 * s + grp;
-        const pf_bf16x8 a = *(const pf_bf16x8*)&ks[buf][key * 128 + ((pc ^ (key & 15)) << 3)];
+        const pf_bf16x8 a = *(const pf_bf16x8*)(ks + key * 256 + ((pc ^ (key & 15)) << 4));
 #pragma unroll
         for (int t = 0; t < 3; ++t) sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qt[s][t], sacc[h], 0, 0, 0);
       }
@@ -343,16 +349,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     // ---- O^T += V^T P^T ----
     pf_bf16x8 pt[3];
     pf_split3(x, pt);
+    // lane (grp, i) reads dims 16 dt + 4(i%4) .. +3 of key 4 grp + i/4 (+16)
+    const int vkey = 4 * grp + (col >> 2), vd = 4 * (col & 3);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      // V^T row of dim 16 dt + col, keys 4 grp + {0..3} and 16 + 4 grp + {0..3}
-      const uint16_t* vrow = &vt[buf][(16 * dt + col) * PF_VTS + 4 * grp];
-      const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 16);
-      const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-      const pf_bf16x8 aa = __builtin_bit_cast(pf_bf16x8, av);
+      const int d = 16 * dt + vd, pd = d >> 3, w = (d & 7) * 2;
+      typedef __attribute__((address_space(3))) pf_s16x4* lds_s16x4;
+      const char* a0 = vs + vkey * 256 + ((pd ^ (vkey & 15)) << 4) + w;
+      const char* a1 = vs + (vkey + 16) * 256 + ((pd ^ ((vkey + 16) & 15)) << 4) + w;
+      const pf_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(lds_void*)a0);
+      const pf_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(lds_void*)a1);
+      const pf_s16x4 both[2] = {lo, hi};
+      const pf_bf16x8 aa = __builtin_bit_cast(pf_bf16x8, both);
 #pragma unroll
       for (int t = 0; t < 3; ++t) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, pt[t], o[dt], 0, 0, 0);
     }
+    st = st == 2 ? 0 : st + 1;
   }
   // ---- normalise and store: lane holds dims 16 dt + 4 grp + r of query col ----
   if (iq >= p.C || posq < 0) return;
