@@ -23,6 +23,10 @@ What is computed, in the pages' order:
   * Multi-codebook fusion, Eq. 1 of the S2 report with the sqrt(N+1) divide
     applied by `forward_generate` when `scale_codebook_embeddings` is on
     ([P2] "Two autoregressions ...", Eq. 1 and the paragraph after it).
+  * Optional repetition-aware loop breaker (RAS) of the slow sample: a second
+    draw at temperature 1.0 and top-p 0.9 replaces the normal one when the
+    normal one repeats a semantic token of the last 10 frames ([P2] "Two
+    autoregressions ...", the loop-breaker paragraph after Eq. 1).
 
 Precision: every activation, norm, softmax and accumulation is float64.  The
 rounding points that belong to the method are kept: the weights are the
@@ -40,7 +44,12 @@ Readings where the pages are silent (each repeated in the design notes):
   scores are scaled by 1/sqrt(head_dim); greedy ties go to the lowest id;
   top-p keeps the shortest (prob desc, id asc) prefix whose cumulative sum
   reaches top_p and picks the first kept token whose renormalised
-  cumulative sum exceeds the supplied uniform u.
+  cumulative sum exceeds the supplied uniform u.  RAS: the window holds the
+  slow ids the sequence emitted in its previous ras_window frames (frame 0
+  of the prefill included, the prompt's own columns not); the second draw
+  uses the same biased logits with its own uniform (slot N of the frame's
+  draws), also after a greedy normal draw; <|im_end|> is never replaced;
+  the id finally emitted enters the window; fast draws are unaffected.
 
 Parity unpinned (no real S2 weights exist here): agreement with the released
 checkpoint's outputs, and the readings above measured against it.
@@ -157,6 +166,9 @@ class Sampling:
     temperature: float = 1.0
     top_p: float = 1.0
     min_frames: int = 0
+    ras_window: int = 0            # 0: off; [P2] sets 10
+    ras_temperature: float = 1.0   # [P2]: the second draw at temperature 1.0 ...
+    ras_top_p: float = 0.9         # ... and top-p 0.9
 
 
 def sample_token(logits, s: Sampling, u=None) -> int:
@@ -214,6 +226,7 @@ class SeqState:
     next_col: np.ndarray | None = None
     frames: int = 0
     done: bool = False
+    ras_hist: list = field(default_factory=list)   # slow ids emitted, oldest first
 
 
 @dataclass
@@ -383,6 +396,20 @@ class DualAROracle:
             bias[self.end] = -np.inf
         return sample_token(logits + bias, s, u)
 
+    def slow_sample_ras(self, seq: SeqState, logits, s: Sampling, u):
+        """The slow draw with the loop breaker ([P2] "Two autoregressions ...",
+        loop-breaker paragraph): draw normally; if that id is a semantic token
+        among the ids emitted in the last `ras_window` frames, take a second
+        draw at (ras_temperature, ras_top_p) with the frame's extra uniform
+        u[N] instead.  Returns (id, whether the second draw was used)."""
+        ident = self.slow_sample(logits, s, None if u is None else u[0], seq.frames)
+        if s.ras_window <= 0 or ident == self.end or ident not in seq.ras_hist[-s.ras_window:]:
+            return ident, False
+        if u is None or len(u) <= self.N:
+            raise ValueError("the loop breaker's draw needs a uniform in slot N of the frame's draws")
+        s2 = Sampling(greedy=False, temperature=s.ras_temperature, top_p=s.ras_top_p, min_frames=s.min_frames)
+        return self.slow_sample(logits, s2, u[self.N], seq.frames), True
+
     # --- fast AR ---------------------------------------------------------------
     def _fast_pass(self, x, k: int, Kf, Vf):
         for i, lw in enumerate(self.fast.layers):
@@ -434,8 +461,12 @@ class DualAROracle:
         logits = self.slow_logits(h)
         self.taps["slow_hidden"] = h
         self.taps["slow_logits"] = logits
-        ident = int(force[0]) if force is not None else \
-            self.slow_sample(logits, s, None if u is None else u[0], seq.frames)
+        if force is not None:
+            ident = int(force[0])
+        else:
+            ident, self.taps["ras_used"] = self.slow_sample_ras(seq, logits, s, u)
+        if s.ras_window > 0 and ident != self.end:
+            seq.ras_hist.append(ident)
         if ident == self.end:
             seq.done = True
             return [ident] + [-1] * self.N

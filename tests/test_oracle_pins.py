@@ -487,3 +487,85 @@ def test_forced_frames_follow_the_given_path():
     alt[3] = (alt[3] + 1) % m["codebook_size"]
     c = DualAROracle(m, w, max_seq=40)
     assert c.prefill(c.new_sequence(), P[0], s, U[0], force=alt) == alt
+
+
+# --------------------------------------------------------------------------
+# RAS loop breaker ([P2] "Two autoregressions ...", the loop-breaker
+# paragraph after Eq. 1): a second slow draw at temperature 1.0, top-p 0.9,
+# used when the normal draw repeats a semantic token of the last 10 frames
+# --------------------------------------------------------------------------
+
+def test_ras_loop_breaker_closed_form():
+    m = mini_model()
+    o = DualAROracle(m, f32_weights(m), max_seq=4)
+    N, end = m["num_codebooks"], m["end_id"]
+    d, e = 205, 210
+    z = np.zeros(m["vocab_size"])
+    z[d], z[e] = 10.0, 9.9
+    # Two dominant semantic logits, the 15 other allowed ids at 0: at T = 1,
+    # p_d = e^10 / Z = 0.5248, p_e = 0.4749 (Z = e^10 + e^9.9 + 15), so the
+    # top-p 0.9 nucleus is {d, e} and renormalised d holds 1 / (1 + e^-0.1) =
+    # 0.52498 of it: u = 0.9 draws e, u = 0.3 draws d.
+    s = Sampling(greedy=True, ras_window=10)
+    u = np.full(N + 1, 0.3)
+    u[N] = 0.9
+    seq = o.new_sequence()
+    seq.ras_hist = [d] + [201, 202, 203] * 3 + [204]       # d 11 frames back: outside
+    assert o.slow_sample_ras(seq, z, s, u) == (d, False)
+    seq.ras_hist = [d] + [201, 202, 203] * 3               # d 10 frames back: inside
+    assert o.slow_sample_ras(seq, z, s, u) == (e, True)
+    # the second draw uses its own uniform (slot N), and may return the same id
+    u2 = np.full(N + 1, 0.9)
+    u2[N] = 0.3
+    assert o.slow_sample_ras(seq, z, s, u2) == (d, True)
+    # off: the plain greedy id
+    assert o.slow_sample_ras(seq, z, Sampling(greedy=True), u) == (d, False)
+    # <|im_end|> is not a semantic token: never replaced
+    z_end = z.copy()
+    z_end[end] = 20.0
+    assert o.slow_sample_ras(seq, z_end, s, u) == (end, False)
+    # top-p normal draws: u[0] = 0.3 draws d (a repeat: replaced by the second
+    # draw, u[N] = 0.9 -> e); u[0] = 0.95 draws e (no repeat: kept)
+    s_tp = Sampling(greedy=False, temperature=1.0, top_p=0.9, ras_window=10)
+    assert o.slow_sample_ras(seq, z, s_tp, u) == (e, True)
+    u3 = u.copy()
+    u3[0] = 0.95
+    assert o.slow_sample_ras(seq, z, s_tp, u3) == (e, False)
+    # while <|im_end|> is still masked (min_frames) the second draw cannot take it
+    z_end2 = z.copy()
+    z_end2[end] = 9.95
+    s_mf = Sampling(greedy=True, ras_window=10, min_frames=5)
+    for uu in np.linspace(0.0, 0.999, 25):
+        u4 = u.copy()
+        u4[N] = uu
+        got, used = o.slow_sample_ras(seq, z_end2, s_mf, u4)
+        assert used and got in (d, e)
+
+
+def test_ras_window_is_the_emitted_ids():
+    # decoding with the loop breaker on: the window is exactly the slow ids
+    # emitted so far (frame 0 included), and an emitted id that differs from
+    # the plain draw always follows a repeat inside the window
+    m = mini_model()
+    o = DualAROracle(m, f32_weights(m), max_seq=64)
+    N, end = m["num_codebooks"], m["end_id"]
+    prompt = synth.make_prompts(m, ("fixed", 2, 4, 2), [8])[0]
+    U = np.random.default_rng(5).random((24, N + 1))
+    s = Sampling(greedy=True, ras_window=3)
+    seq = o.new_sequence()
+    emitted, used = [], 0
+    for f in range(24):
+        hist = list(seq.ras_hist)
+        fr = o.prefill(seq, prompt, s, U[0]) if f == 0 else o.decode_frame(seq, s, U[f])
+        if fr[0] == -1:
+            break
+        plain = o.slow_sample(o.taps["slow_logits"], Sampling(greedy=True), None, f)
+        if o.taps["ras_used"]:
+            used += 1
+            assert plain in hist[-3:]
+        else:
+            assert fr[0] == plain and (plain == end or plain not in hist[-3:])
+        if fr[0] != end:
+            emitted.append(fr[0])
+    assert seq.ras_hist == emitted
+    assert used > 0          # the greedy mini model repeats itself: the breaker fires
