@@ -282,6 +282,7 @@ class DualAROracle:
         self.bias = bias
         self.count = Counters()
         self.taps = {}
+        self.ras_used = False    # the last slow draw came from the loop breaker
 
     # --- cache helpers -----------------------------------------------------
     def _kv(self, t):
@@ -462,9 +463,9 @@ class DualAROracle:
         self.taps["slow_hidden"] = h
         self.taps["slow_logits"] = logits
         if force is not None:
-            ident = int(force[0])
+            ident, self.ras_used = int(force[0]), False
         else:
-            ident, self.taps["ras_used"] = self.slow_sample_ras(seq, logits, s, u)
+            ident, self.ras_used = self.slow_sample_ras(seq, logits, s, u)
         if s.ras_window > 0 and ident != self.end:
             seq.ras_hist.append(ident)
         if ident == self.end:

@@ -560,7 +560,7 @@ def test_ras_window_is_the_emitted_ids():
         if fr[0] == -1:
             break
         plain = o.slow_sample(o.taps["slow_logits"], Sampling(greedy=True), None, f)
-        if o.taps["ras_used"]:
+        if o.ras_used:
             used += 1
             assert plain in hist[-3:]
         else:
