@@ -2,7 +2,7 @@
 dominant kernel and the CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W] [--workload s2_b1|s2_b32|s2_prefill|fast_s2|fast_s2_b16|tiny_b1]
-                    [--semantic-head]
+                    [--semantic-head] [--ras]
 
 A step is one decode frame of the whole hot path (fusion, slow pass, biased
 sample, ten fast passes with their samples) over one batch.  Inputs are
@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--prompt-len", type=int, default=None,
                     help="override the prompt length (same three-segment layout); for counter runs")
+    ap.add_argument("--ras", action="store_true",
+                    help="turn on the slow loop breaker (window 10, second draw at T=1.0, top-p 0.9)")
     ap.add_argument("--semantic-head", action="store_true",
                     help="slow head over the semantic rows and the end row only (identical draws)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -154,8 +156,10 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] weights on device ({sum(t.numel() * t.element_size() for t in dev_w.values()) / 1e9:.2f} GB)")
 
+    ras = 10 if args.ras and not fast_only else 0
     S = DualAR.sampling(greedy=samp["greedy"], temperature=samp["temperature"], top_p=samp["top_p"],
-                        min_frames=1 << 30)   # fixed-length runs: <|im_end|> stays masked
+                        min_frames=1 << 30,   # fixed-length runs: <|im_end|> stays masked
+                        ras_window=ras, ras_temperature=1.0, ras_top_p=0.9)
     P_frames = W + K + args.profile_frames + 1
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -180,8 +184,8 @@ def main():
         prompts = synth.make_prompts(m, layout, plen, seed=args.seed)
         ctx = DualAR(m, dev_w, max_batch=B, max_seq_len=int(plen.max()) + P_frames + 2)
         U = None
-        if not samp["greedy"]:
-            U = torch.from_numpy(synth.make_uniforms((1 + P_frames, B, N), seed=args.seed)).cuda()
+        if not samp["greedy"] or ras:
+            U = torch.from_numpy(synth.make_uniforms((1 + P_frames, B, N + (ras > 0)), seed=args.seed)).cuda()
         T = torch.from_numpy(prompts).cuda()
         torch.cuda.synchronize()
         e0, e1 = ev(), ev()
@@ -282,7 +286,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if m["weight_dtype"] == "bf16" else "f32",
         "data": "synthetic (seeded random-init weights of the S2 shapes, synthetic prompts)",
         "config": {"workload": f"{args.workload}: {desc}" + (", semantic-candidate slow head" if args.semantic_head
-                                                               else ", full-vocabulary slow head"), "batch": B,
+                                                               else ", full-vocabulary slow head")
+                   + (", loop breaker on (window 10)" if ras else ""), "batch": B,
                    "prompt_len": None if fast_only else [int(x) for x in plen][:4] + (["..."] if B > 4 else []),
                    "accumulate": "f32", "kv_cache": m["weight_dtype"]},
         "codec_tokens_per_s": round(reporting.codec_tokens_per_s(fps, N), 1),

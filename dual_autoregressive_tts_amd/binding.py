@@ -54,7 +54,8 @@ class Weights(C.Structure):
 
 class Sampling(C.Structure):
     _fields_ = [("temperature", C.c_float), ("top_p", C.c_float), ("greedy", C.c_int32),
-                ("min_frames", C.c_int32)]
+                ("min_frames", C.c_int32), ("ras_window", C.c_int32), ("ras_temperature", C.c_float),
+                ("ras_top_p", C.c_float)]
 
 
 class Taps(C.Structure):
@@ -211,8 +212,12 @@ class DualAR:
             raise DualARError(st, self.lib.dualar_last_error(self.h).decode())
 
     @staticmethod
-    def sampling(greedy=True, temperature=1.0, top_p=1.0, min_frames=0) -> Sampling:
-        return Sampling(float(temperature), float(top_p), int(bool(greedy)), int(min_frames))
+    def sampling(greedy=True, temperature=1.0, top_p=1.0, min_frames=0, ras_window=0, ras_temperature=1.0,
+                 ras_top_p=0.9) -> Sampling:
+        """ras_window > 0 turns on the slow loop breaker (the pages' window is
+        10); its draws then take slot N of N + 1 uniforms per sequence."""
+        return Sampling(float(temperature), float(top_p), int(bool(greedy)), int(min_frames), int(ras_window),
+                        float(ras_temperature), float(ras_top_p))
 
     def _need(self, t, shape, dtype, what):
         torch = self.torch
@@ -243,7 +248,7 @@ class DualAR:
         torch = self.torch
         B, _, T = tokens.shape
         self._need(tokens, (B, self.N + 1, T), torch.int32, "tokens")
-        self._need(uniforms, (B, self.N), torch.float32, "uniforms")
+        self._need(uniforms, (B, self.N + (sampling.ras_window > 0)), torch.float32, "uniforms")
         if len(prompt_len) != B:
             raise DualARError(-1, "prompt_len must have one entry per sequence")
         plen = (C.c_int32 * B)(*[int(x) for x in prompt_len])
@@ -258,7 +263,7 @@ class DualAR:
         torch = self.torch
         B, N, m = self.batch, self.N, self.m
         codes = out if out is not None else torch.empty((B, n, N + 1), dtype=torch.int32, device="cuda")
-        self._need(uniforms, (n, B, N), torch.float32, "uniforms")
+        self._need(uniforms, (n, B, N + (sampling.ras_window > 0)), torch.float32, "uniforms")
         self._need(codes, (B, n, N + 1), torch.int32, "codes")
         emitted = torch.empty(B, dtype=torch.int32, device="cuda")
         tp, td = self._taps(B, which=taps) if taps else (None, None)

@@ -42,7 +42,7 @@ struct Resolved {  // config with the inherit-on-unset fallback applied
 struct Layout {
   size_t kslow, vslow, kfast, vfast, rope_s, rope_f, x_slow, x_fast, qkv, att, ffn, logits, flog, part,
       xn, xn2, gpart, gpart_elems, x_pre, ppos, qbuf,
-      counters, st_pos, st_done, st_frames, st_cur, st_plen, st_fidx, st_status, total;
+      counters, st_pos, st_done, st_frames, st_cur, st_plen, st_fidx, st_status, st_ras, total;
   size_t slow_layer_stride, fast_layer_stride;  // elements per layer of a cache
   int max_splits, qkv_ld, att_ld, ffn_ld;
   int rows;     // activation rows the buffers hold: max(max_batch, max_batch * pc)
@@ -158,6 +158,7 @@ Layout layout(const Resolved& r) {
   L.st_plen = take(r.max_batch * 4);
   L.st_fidx = take(4);
   L.st_status = take(4);
+  L.st_ras = take((size_t)r.max_batch * DUALAR_RAS_MAX_WINDOW * 4);   // loop-breaker windows
   L.total = off;
   return L;
 }
@@ -439,6 +440,8 @@ SampleParams sample_params(dualar_ctx* c, const FrameIO& io, int B, int slow, in
   sp.B = B; sp.slow = slow; sp.sb = r.sb; sp.se = r.se; sp.end_id = r.end_id; sp.C = r.C; sp.N = r.N;
   sp.k = k; sp.greedy = io.s->greedy || !io.uniforms; sp.temperature = io.s->temperature;
   sp.top_p = io.s->top_p; sp.min_frames = io.s->min_frames;
+  sp.ras_window = io.fast_only ? 0 : io.s->ras_window;
+  sp.ras_temperature = io.s->ras_temperature; sp.ras_top_p = io.s->ras_top_p;
   sp.uniforms = io.uniforms; sp.u_frame_stride = io.u_fs; sp.u_row_stride = io.u_rs;
   sp.codes = io.codes; sp.c_row_stride = io.c_rs; sp.c_frame_stride = io.c_fs;
   sp.c_col = io.fast_only ? k : (slow ? 0 : 1 + k);
@@ -647,6 +650,8 @@ dualar_status dispatch(dualar_ctx* c, F&& f) {
   return f(float{}, float{});
 }
 
+static_assert(RAS_HIST_STRIDE == DUALAR_RAS_MAX_WINDOW, "loop-breaker window stride");
+
 dualar_status check_sampling(dualar_ctx* c, const dualar_sampling* s, const float* uniforms) {
   if (!s) return fail(c, DUALAR_ERR_INVALID_ARG, "sampling is NULL");
   if (!s->greedy) {
@@ -656,6 +661,15 @@ dualar_status check_sampling(dualar_ctx* c, const dualar_sampling* s, const floa
     if (!(s->top_p > 0.0f && s->top_p <= 1.0f)) return fail(c, DUALAR_ERR_INVALID_ARG, "top_p must be in (0, 1]");
   }
   if (s->min_frames < 0) return fail(c, DUALAR_ERR_INVALID_ARG, "min_frames must be >= 0");
+  if (s->ras_window < 0 || s->ras_window > DUALAR_RAS_MAX_WINDOW)
+    return fail(c, DUALAR_ERR_INVALID_ARG, "ras_window must be in [0, DUALAR_RAS_MAX_WINDOW]");
+  if (s->ras_window > 0) {
+    if (!uniforms) return fail(c, DUALAR_ERR_INVALID_ARG, "the loop breaker needs uniforms (slot N)");
+    if (!(s->ras_temperature > 0.0f) || !isfinite(s->ras_temperature))
+      return fail(c, DUALAR_ERR_INVALID_ARG, "ras_temperature must be > 0");
+    if (!(s->ras_top_p > 0.0f && s->ras_top_p <= 1.0f))
+      return fail(c, DUALAR_ERR_INVALID_ARG, "ras_top_p must be in (0, 1]");
+  }
   return DUALAR_OK;
 }
 
@@ -724,6 +738,7 @@ dualar_status dualar_create(const dualar_config* cfg, const dualar_weights* w, v
   c->st.frames = (int*)(c->ws + L.st_frames); c->st.cur = (int*)(c->ws + L.st_cur);
   c->st.plen = (int*)(c->ws + L.st_plen); c->st.frame_idx = (int*)(c->ws + L.st_fidx);
   c->st.status = (int*)(c->ws + L.st_status);
+  c->st.ras_hist = (int*)(c->ws + L.st_ras);
 
   // RoPE tables: theta_i = base^(-2i/hd), angle p*theta_i in double, cos/sin
   // rounded to bf16 (the bf16 table of the pages).  Stored as (cos, sin) fp32.
@@ -771,7 +786,8 @@ dualar_status dualar_prefill(dualar_ctx_t* c, int32_t batch, const int32_t* toke
   c->batch = batch;
   c->frames_done = 0;
   c->ready = false;
-  FrameIO io{s, uniforms, 0, c->r.N, frame0, c->r.N + 1, 0, taps, false};
+  const int urs = c->r.N + (s->ras_window > 0 ? 1 : 0);   // draws per sequence (slot N: the loop breaker's)
+  FrameIO io{s, uniforms, 0, urs, frame0, c->r.N + 1, 0, taps, false};
   dualar_status st = dispatch(c, [&](auto wt, auto kt) {
     return do_prefill<decltype(wt), decltype(kt)>(c, batch, tokens, t_max, io);
   });
@@ -791,7 +807,8 @@ dualar_status dualar_decode_frames(dualar_ctx_t* c, int32_t n_frames, const dual
     if ((long long)c->plen[b] + c->frames_done + n_frames > c->r.max_seq)
       return fail(c, DUALAR_ERR_CONTEXT_FULL, "decode would pass max_seq_len");
   const int N = c->r.N;
-  FrameIO io{s, uniforms, c->batch * N, N, codes, (long long)n_frames * (N + 1), N + 1, taps, false};
+  const int urs = N + (s->ras_window > 0 ? 1 : 0);   // draws per sequence (slot N: the loop breaker's)
+  FrameIO io{s, uniforms, c->batch * urs, urs, codes, (long long)n_frames * (N + 1), N + 1, taps, false};
   dualar_status st = dispatch(c, [&](auto wt, auto kt) {
     return do_decode<decltype(wt), decltype(kt)>(c, n_frames, io);
   });

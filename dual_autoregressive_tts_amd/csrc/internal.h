@@ -120,7 +120,9 @@ struct SeqState {
   int* plen;       // [max_batch] prompt lengths
   int* frame_idx;  // [1] frame index inside the current call
   int* status;     // [1] latched device faults
+  int* ras_hist;   // [max_batch][RAS_HIST_STRIDE] loop-breaker windows: slot f % window = slow id of frame f
 };
+#define RAS_HIST_STRIDE 16   // = DUALAR_RAS_MAX_WINDOW
 
 // Candidate set / bookkeeping for the sampler.
 struct SampleParams {
@@ -131,6 +133,7 @@ struct SampleParams {
   int sb, se, end_id, C, N;
   int k;                        // codebook index written (0 = slow sample)
   int greedy; float temperature, top_p; int min_frames;
+  int ras_window; float ras_temperature, ras_top_p;   // slow loop breaker (0 = off); its draw is slot N
   const float* uniforms; int u_frame_stride; int u_row_stride;   // uniforms[f*fs + b*rs + slot]
   int* codes; long long c_row_stride; int c_frame_stride; int c_col;   // codes out (NULL = none)
   const void* fast_emb; int fast_dim; float* x_next;   // x_next[b] = E_fast[q] (NULL = none)

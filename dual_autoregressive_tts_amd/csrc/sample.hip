@@ -218,6 +218,7 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
   __shared__ int shc[SMP_THREADS / 64];
   __shared__ float wsum[SMP_THREADS / 64];
   __shared__ int choice;
+  __shared__ int ras_hit;
 
   const int f = *p.st.frame_idx;
   const int was_done = p.st.done[b];
@@ -252,14 +253,13 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
   if (bad) atomicOr(p.st.status, ST_NONFINITE);
   best = block_best(best, shb);
 
-  if (p.greedy) {
-    if (tid == 0) choice = best.i;
-  } else {
+  // top-p draw with uniform u: every thread takes part; sets choice
+  auto topp = [&](float temperature, float top_p, float u) __attribute__((always_inline)) {
     // ---- top-p ----
     int NP = 1;
     while (NP < nc) NP <<= 1;
     const float zmax = best.v;
-    const float invT = 1.0f / p.temperature;
+    const float invT = 1.0f / temperature;
     if (NP < SMP_THREADS * 4) NP = SMP_THREADS * 4;
     if (NP == SMP_THREADS * 4) topp_sort<4>(z, p, nc, zmax, invT, ev, ix, cand_id, cand_ok);
     else topp_sort<8>(z, p, nc, zmax, invT, ev, ix, cand_id, cand_ok);
@@ -287,21 +287,51 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
       for (int q = 0; q < per; ++q) ev[beg + q] += off;
     __syncthreads();
     const float total = ev[NP - 1];
-    const float thr = p.top_p * total;
+    const float thr = top_p * total;
     int cnt = 0;
     for (int i = tid; i < NP; i += SMP_THREADS) cnt += ev[i] < thr;
     int n_keep = block_count(cnt, shc) + 1;
     if (n_keep > nc) n_keep = nc;
     const float kept = ev[n_keep - 1];
-    const float u = p.uniforms[(size_t)f * p.u_frame_stride + (size_t)b * p.u_row_stride + p.k];
     const float target = u * kept;
     int c2 = 0;
     for (int i = tid; i < n_keep; i += SMP_THREADS) c2 += ev[i] <= target;
     int pick = block_count(c2, shc);
     if (pick > n_keep - 1) pick = n_keep - 1;
     if (tid == 0) choice = ix[pick];
+  };
+  const float* ub = p.uniforms ? p.uniforms + (size_t)f * p.u_frame_stride + (size_t)b * p.u_row_stride : nullptr;
+  if (p.greedy) {
+    if (tid == 0) choice = best.i;
+  } else {
+    topp(p.temperature, p.top_p, ub[p.k]);
   }
   __syncthreads();
+
+  // Loop breaker ([P2] "Two autoregressions ...", the paragraph after Eq. 1):
+  // a slow draw that repeats a semantic id of the sequence's last ras_window
+  // frames is replaced by a second top-p draw with its own uniform (slot N);
+  // the id emitted enters the window (slot frames % ras_window).
+  if (p.slow && p.ras_window > 0) {
+    const int fr = p.st.frames[b];
+    int* hist = p.st.ras_hist + (size_t)b * RAS_HIST_STRIDE;
+    if (tid == 0) {
+      const int id0 = cand_id((choice >= 0 && choice < nc) ? choice : 0);
+      int hit = 0;
+      if (id0 != p.end_id)
+        for (int i = 0; i < min(fr, p.ras_window); ++i) hit |= hist[i] == id0;
+      ras_hit = hit;
+    }
+    __syncthreads();
+    if (ras_hit) {
+      topp(p.ras_temperature, p.ras_top_p, ub[p.N]);
+      __syncthreads();
+    }
+    if (tid == 0) {
+      const int id1 = cand_id((choice >= 0 && choice < nc) ? choice : 0);
+      if (id1 != p.end_id) hist[fr % p.ras_window] = id1;
+    }
+  }
 
   const int ci = (choice >= 0 && choice < nc) ? choice : 0;   // NaN logits: stay in range
   const int id = cand_id(ci);

@@ -127,12 +127,25 @@ typedef struct {
  * top-p driven by caller-supplied uniforms.  Top-p keeps the shortest
  * prefix, in (probability desc, id asc) order, whose mass reaches top_p and
  * draws the first kept id whose renormalised cumulative mass exceeds u.
- * <|im_end|> stays masked until a sequence has emitted min_frames frames. */
+ * <|im_end|> stays masked until a sequence has emitted min_frames frames.
+ *
+ * Loop breaker (RAS, [P2] "Two autoregressions, because ten codebooks is
+ * ten times the sequence", the paragraph after Eq. 1): with ras_window > 0
+ * every slow draw that repeats a semantic id the sequence emitted in its
+ * previous ras_window frames is replaced by a second top-p draw at
+ * (ras_temperature, ras_top_p) from the same biased logits.  The uniforms
+ * then hold N + 1 draws per (frame, sequence), slot N being the second
+ * draw's, and may not be NULL.  <|im_end|> is never replaced; the id
+ * emitted enters the window.  dualar_fast_frames ignores it (no slow draw). */
+#define DUALAR_RAS_MAX_WINDOW 16
 typedef struct {
   float temperature;             /* > 0 */
   float top_p;                   /* (0, 1] */
   int32_t greedy;                /* 1: argmax (lowest id on ties) */
   int32_t min_frames;
+  int32_t ras_window;            /* 0 = off, 1..DUALAR_RAS_MAX_WINDOW ([P2]: 10) */
+  float ras_temperature;         /* > 0 when ras_window > 0 ([P2]: 1.0) */
+  float ras_top_p;               /* (0, 1] when ras_window > 0 ([P2]: 0.9) */
 } dualar_sampling;
 
 /* Optional fp32 device buffers filled with the LAST frame of a call. */
@@ -162,7 +175,8 @@ dualar_status dualar_create(const dualar_config *cfg, const dualar_weights *w,
  *              a semantic position is fused as in decode, a text position
  *              takes its LM embedding alone.
  *   prompt_len host int32 [batch], 1 <= prompt_len[b] <= t_max.
- *   uniforms   device fp32 [batch][N] for top-p, or NULL when greedy.
+ *   uniforms   device fp32 [batch][N] for top-p, or NULL when greedy;
+ *              [batch][N + 1] with the loop breaker on (slot N).
  *   frame0     device int32 [batch][N+1]: (id, q^(0..N-1)); a sequence whose
  *              first sample is <|im_end|> gets (end_id, -1, ..., -1).
  *   taps       NULL, or buffers for frame 0's slow hidden state, slow logits
@@ -176,7 +190,8 @@ dualar_status dualar_prefill(dualar_ctx_t *ctx, int32_t batch, const int32_t *to
 
 /* Decode n_frames frames for every sequence of the last prefill.
  *   uniforms  device fp32 [n_frames][batch][N] (slot 0: slow draw, slot k:
- *             draw of q^(k)), or NULL when greedy.
+ *             draw of q^(k)), or NULL when greedy; [n_frames][batch][N + 1]
+ *             with the loop breaker on (slot N: its second draw).
  *   codes     device int32 [batch][n_frames][N+1]; rows after a sequence has
  *             ended are -1; the row that samples <|im_end|> is
  *             (end_id, -1, ..., -1).

@@ -24,7 +24,8 @@ def _dev():
 
 
 def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=REL_L2, min_frames=0,
-                    tag="", weights_f32=None, floor=False, prefill_chunk=0, slow_logits_tap=True):
+                    tag="", weights_f32=None, floor=False, prefill_chunk=0, slow_logits_tap=True, ras=0,
+                    stats=None):
     """Prefill + n_frames single-frame decode calls on the GPU; the oracle
     replays every sequence.  Returns per-row counts of frames compared.
 
@@ -39,7 +40,7 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
     say(f"[{tag}] GPU: B={B} prompt_len={list(plen)[:8]} frames={n_frames} greedy={greedy}")
     dw = upload(m, w_np)
     ctx = DualAR(m, dw, max_batch=B, max_seq_len=int(max(plen)) + n_frames + 2, prefill_chunk=prefill_chunk)
-    S = DualAR.sampling(min_frames=min_frames, **samp)
+    S = DualAR.sampling(min_frames=min_frames, ras_window=ras, **samp)
     tok = torch.from_numpy(np.ascontiguousarray(prompts)).cuda()
     U = None if uniforms is None else torch.from_numpy(np.ascontiguousarray(uniforms)).cuda()
     # without the slow_logits tap a semantic-head context runs its restricted head
@@ -60,7 +61,8 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
     say(f"[{tag}] oracle")
     wf = weights_f32 if weights_f32 is not None else synth.weights_as_f32(m, w_np)
     osamp = OSampling(greedy=bool(greedy), temperature=samp.get("temperature", 1.0),
-                      top_p=samp.get("top_p", 1.0), min_frames=min_frames)
+                      top_p=samp.get("top_p", 1.0), min_frames=min_frames, ras_window=ras)
+    ras_used = 0
     compared = []
     worst = {"fused_x": 0.0, "slow_hidden": 0.0, "slow_logits": 0.0, "fast_logits": 0.0}
     floors = []
@@ -78,6 +80,7 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
             ofr = o.prefill(seq, prompts[b][:, :plen[b]], osamp, None if u is None else u[0]) if f == 0 \
                 else o.decode_frame(seq, osamp, None if u is None else u[f])
             gfr = g_frames[f][b].tolist()
+            ras_used += int(ras > 0 and o.ras_used and ofr[0] != -1)
             bound = dict.fromkeys(worst, tol)
             bound["fused_x"] = 1e-5
             if floor and in_step:
@@ -125,6 +128,19 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
                 assert osamp.greedy, (tag, b, f, "slow id without slow logits")
                 mg = decision_margin(o.taps["slow_logits"] + bias, True)
                 assert mg <= 1e-2, (tag, b, f, "slow id", gfr[0], ofr[0], "oracle margin", mg)
+            elif gfr[0] != ofr[0] and ras:
+                # loop breaker: the normal draws are compared first; where they
+                # agree both sides hold the same window, so the breaker fired on
+                # both or on neither
+                zg, zo = t["slow_logits"][b] + bias, o.taps["slow_logits"] + bias
+                ng, no = sample_token(zg, osamp, u[f][0]), sample_token(zo, osamp, u[f][0])
+                if ng != no:
+                    mg = check_decision(zg, zo, ng, no, osamp, u[f][0], (tag, b, f, "slow id (normal draw)"))
+                else:
+                    assert o.ras_used, (tag, b, f, "slow id differs with no loop-breaker draw", gfr[0], ofr[0])
+                    s2 = OSampling(greedy=False, temperature=osamp.ras_temperature, top_p=osamp.ras_top_p,
+                                   min_frames=min_frames)
+                    mg = check_decision(zg, zo, gfr[0], ofr[0], s2, u[f][N], (tag, b, f, "slow id (loop breaker)"))
             elif gfr[0] != ofr[0]:
                 mg = check_decision(t["slow_logits"][b] + bias, o.taps["slow_logits"] + bias, gfr[0], ofr[0],
                                     osamp, None if u is None else u[f][0], (tag, b, f, "slow id"))
@@ -141,6 +157,10 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
         if n_ok == n_frames + 1 and not seq.done:
             assert g_emitted[b] == seq.frames, (tag, b, g_emitted[b], seq.frames)
     say(f"[{tag}] frames compared per row {compared}; worst rel L2 {worst}")
+    if ras:
+        say(f"[{tag}] loop-breaker draws taken by the oracle: {ras_used}")
+    if stats is not None:
+        stats["ras_used"] = ras_used
     if floor:
         say(f"[{tag}] fp32-oracle distance to the fp64 oracle per row: {floors}")
     return compared, worst
@@ -204,6 +224,24 @@ def test_tiny_semantic_head(tiny):
                                slow_logits_tap=False)
     assert sum(c) >= 20
     assert "slow_logits" not in worst or worst["slow_logits"] == 0.0
+
+
+@pytest.mark.parametrize("greedy", [1, 0])
+def test_tiny_loop_breaker(tiny, greedy):
+    # The slow loop breaker with the pages' window of 10 frames: a draw that
+    # repeats a semantic id of the last 10 emitted frames is replaced by a
+    # second draw at T = 1.0, top-p 0.9 from slot N of the frame's uniforms.
+    # The greedy tiny model repeats itself, so the breaker fires.
+    m, w = tiny
+    plen = np.array([32, 7, 45], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=6)
+    U = synth.make_uniforms((17, 3, m["num_codebooks"] + 1), seed=6)
+    samp = dict(greedy=1) if greedy else dict(greedy=0, temperature=0.7, top_p=0.8)
+    stats = {}
+    c, _ = run_and_compare(m, w, P, plen, 16, samp, U, tol=1e-4, tag=f"tiny-ras-g{greedy}", ras=10, stats=stats)
+    assert sum(c) >= 24
+    if greedy:
+        assert stats["ras_used"] > 0
 
 
 @pytest.mark.parametrize("pc", [1, 3, 16, 64])
