@@ -65,7 +65,7 @@ class Taps(C.Structure):
 
 # Every symbol the header declares.
 EXPORTS = ("dualar_workspace_bytes", "dualar_create", "dualar_prefill", "dualar_decode_frames",
-           "dualar_fast_frames", "dualar_sync", "dualar_profile_begin", "dualar_profile_end",
+           "dualar_fast_frames", "dualar_fast_teacher_forced", "dualar_sync", "dualar_profile_begin", "dualar_profile_end",
            "dualar_destroy", "dualar_status_string", "dualar_last_error")
 K_GEMV, K_ATTN, K_SAMPLE, K_EMBED, K_GEMV_SWIGLU = 0, 1, 2, 3, 4
 
@@ -91,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.dualar_decode_frames.restype = I32
     lib.dualar_fast_frames.argtypes = [VP, I32, I32, VP, VP, P(Sampling), VP, VP, P(Taps)]
     lib.dualar_fast_frames.restype = I32
+    lib.dualar_fast_teacher_forced.argtypes = [VP, I32, VP, VP, VP]
+    lib.dualar_fast_teacher_forced.restype = I32
     lib.dualar_sync.argtypes = [VP, P(I32)]
     lib.dualar_sync.restype = I32
     lib.dualar_profile_begin.argtypes = [VP, I32]
@@ -270,6 +272,18 @@ class DualAR:
         self._check(self.lib.dualar_decode_frames(self.h, n, C.byref(sampling), _ptr(uniforms), _ptr(codes),
                                                   _ptr(emitted), C.byref(tp) if tp is not None else None))
         return codes, emitted, td
+
+    def fast_teacher_forced(self, hidden, codes, out=None):
+        """hidden: cuda fp32 [n][fast_dim]; codes: cuda int32 [n][N].  Returns
+        the fast head's logits [n][N][C] (slot k >= 1 predicts q^(k))."""
+        torch, m, N = self.torch, self.m, self.N
+        n = hidden.shape[0]
+        self._need(hidden, (n, m["dim"]), torch.float32, "hidden")
+        self._need(codes, (n, N), torch.int32, "codes")
+        logits = out if out is not None else torch.empty((n, N, m["codebook_size"]), device="cuda")
+        self._need(logits, (n, N, m["codebook_size"]), torch.float32, "logits")
+        self._check(self.lib.dualar_fast_teacher_forced(self.h, n, _ptr(hidden), _ptr(codes), _ptr(logits)))
+        return logits
 
     def fast_frames(self, hidden, q0, sampling: Sampling, uniforms=None, taps: bool = False, out=None):
         """hidden: cuda fp32 [F][B][dim]; q0: cuda int32 [F][B] -> codes [B][F][N]."""

@@ -287,7 +287,7 @@ void live_tiles(const dualar_ctx* c, GemvParams& g, int rows_per_seq) {
 // exit, whether this layer did the same for layer l + 1.
 template <typename T, typename KT>
 dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const int* pos_dev,
-                        int pos_const, int Lmax, bool& in_planes, int rows_per_seq = 0) {
+                        int pos_const, int Lmax, bool& in_planes, int rows_per_seq = 0, bool depth_tf = false) {
   const Resolved& r = c->r;
   const Layout& L = c->L;
   const dualar_layer_weights& w = S.lw[l];
@@ -325,7 +325,15 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     g.prep_done = &prepped;
   }
   HIPCHK(gemv<T>(c, g));
-  if (rows_per_seq > 0) {
+  if (depth_tf) {
+    // teacher-forced fast AR: groups of rows_per_seq rows, causal along depth
+    PrefillParams a{};
+    a.qkv = qkv; a.ld_qkv = L.qkv_ld; a.C = rows_per_seq; a.rope = S.rope;
+    a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
+    a.H = S.H; a.KV = S.KV; a.hd = S.hd;
+    a.out = att; a.ld_out = L.att_ld; a.out_planes = planes; a.R = B; a.B = B / rows_per_seq;
+    HIPCHK((launch_depth_attn<T, KT>(a, c->stream)));
+  } else if (rows_per_seq > 0) {
     // prefill chunk: QK-norm, RoPE, append for every row, then causal attention
     PrefillParams a{};
     a.qkv = qkv; a.ld_qkv = L.qkv_ld;
@@ -555,6 +563,31 @@ dualar_status embed(dualar_ctx* c, int B, const int* tokens, int t_max, int step
 // step t + t_max - plen[b]) and walked in steps of pc positions, every
 // sequence's pc rows at once, so every prompt ends in the last step.  Its
 // last row per sequence then feeds frame 0.
+// Teacher-forced fast AR over n (hidden state, codes) pairs: n*N rows through
+// the fast layers at once (causal along depth inside each pair), then
+// fast_norm and the fast head for every row.
+template <typename T, typename KT>
+dualar_status do_fast_tf(dualar_ctx* c, int n, const float* hidden, const int32_t* codes, float* logits) {
+  const Resolved& r = c->r;
+  const int M = n * r.N;
+  float* x = (float*)(c->ws + c->L.x_pre);
+  TfParams e{};
+  e.hidden = hidden; e.codes = codes; e.fast_emb = c->w.fast_embeddings; e.x = x;
+  e.n = n; e.N = r.N; e.C = r.C; e.dim = r.dim; e.status = c->st.status;
+  HIPCHK(launch_tf_embed<T>(e, c->stream));
+  bool pl = false;
+  for (int l = 0; l < r.fn_layer; ++l) {
+    dualar_status st = run_layer<T, KT>(c, c->fast, l, x, M, nullptr, 0, r.N, pl, r.N, true);
+    if (st) return st;
+  }
+  GemvParams g{};
+  g.w[0] = c->w.fast_output; g.rows[0] = r.C; g.n_seg = 1; g.K = r.dim; g.n_out = r.C;
+  g.x = x; g.ldx = r.dim; g.gain = c->w.fast_norm; g.eps = r.eps;
+  g.y = logits; g.ldy = r.C; g.B = M; g.mode = GEMV_STORE;
+  HIPCHK(gemv<T>(c, g));
+  return DUALAR_OK;
+}
+
 template <typename T, typename KT>
 dualar_status do_prefill(dualar_ctx* c, int B, const int* tokens, int t_max, const FrameIO& io) {
   const Resolved& r = c->r;
@@ -834,6 +867,22 @@ dualar_status dualar_fast_frames(dualar_ctx_t* c, int32_t batch, int32_t n_frame
   FrameIO io{s, uniforms, batch * N, N, codes, (long long)n_frames * N, N, taps, true};
   return dispatch(c, [&](auto wt, auto kt) {
     return do_fast<decltype(wt), decltype(kt)>(c, batch, n_frames, hidden, q0, io);
+  });
+}
+
+dualar_status dualar_fast_teacher_forced(dualar_ctx_t* c, int32_t n, const float* hidden, const int32_t* codes,
+                                        float* logits) {
+  if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
+  if (!hidden || !codes || !logits) return fail(c, DUALAR_ERR_INVALID_ARG, "hidden/codes/logits is NULL");
+  const int N = c->r.N;
+  if (n < 1 || (long long)n * N > c->L.rows)
+    return fail(c, DUALAR_ERR_INVALID_ARG, "n out of range [1, max_batch * prefill_chunk / num_codebooks]");
+  if (N > 16 || c->fast.hd > 128 || c->fast.hd % 2 || c->fast.H / c->fast.KV > 8)
+    return fail(c, DUALAR_ERR_INVALID_ARG, "teacher-forced form needs N <= 16, fast head_dim <= 128 (even), "
+                                           "<= 8 query heads per KV head");
+  // the activation buffers are scratch between calls: the decode state is untouched
+  return dispatch(c, [&](auto wt, auto kt) {
+    return do_fast_tf<decltype(wt), decltype(kt)>(c, n, hidden, codes, logits);
   });
 }
 

@@ -155,6 +155,17 @@ struct EmbedParams {
   SeqState st;
 };
 
+// Teacher-forced fast AR rows: row i*N + k is the slow hidden state of
+// pair i (k = 0) or E_F[codes[i][k - 1]] (k >= 1).
+struct TfParams {
+  const float* hidden;     // [n][dim]
+  const int* codes;        // [n][N]
+  const void* fast_emb;    // [C][dim]
+  float* x;                // [n*N][dim]
+  int n, N, C, dim;
+  int* status;             // out-of-range codes latch ST_BAD_TOKEN
+};
+
 struct FastBeginParams {
   const float* hidden; const int* q0;   // [n_frames][B][dim], [n_frames][B]
   const void* fast_emb; int dim, C, N;
@@ -176,6 +187,10 @@ template <typename T, typename KT> hipError_t launch_kv_append(const PrefillPara
 template <typename T> hipError_t launch_sample(const SampleParams& p, hipStream_t s);
 template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s);
 template <typename T> hipError_t launch_fast_begin(const FastBeginParams& p, hipStream_t s);
+template <typename T> hipError_t launch_tf_embed(const TfParams& p, hipStream_t s);
+// causal attention along depth inside each group of C rows (grid (B, KV)), with
+// the decode arithmetic for QK-norm, RoPE at position row % C and the cache rounding
+template <typename T, typename KT> hipError_t launch_depth_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_frame_reset(SeqState st, hipStream_t s);
 hipError_t launch_frame_end(SeqState st, int B, int advance_pos, hipStream_t s);
 hipError_t launch_prefill_begin(SeqState st, const int* plen_host, int B, int N, hipStream_t s);

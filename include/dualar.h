@@ -216,6 +216,24 @@ dualar_status dualar_fast_frames(dualar_ctx_t *ctx, int32_t batch, int32_t n_fra
                                  const dualar_sampling *s, const float *uniforms,
                                  int32_t *codes, const dualar_taps *taps);
 
+/* Teacher-forced fast AR (the training forward of [P1] "Fast Transformer:
+ * The Codebook Decoder", Step 3, in scoring form): for each of n pairs of a
+ * slow hidden state and that frame's codes, the fast layers run over
+ * [h, E_F(q^(0)), ..., E_F(q^(N-2))] with causal attention along depth, all
+ * pairs at once (n*N rows through the products), then fast_norm and the
+ * fast head on every row.
+ *   hidden  device fp32 [n][fast_dim]
+ *   codes   device int32 [n][N], 0 <= code < C (q^(N-1) is not read; an
+ *           out-of-range code is latched for dualar_sync and row 0 used)
+ *   logits  device fp32 [n][N][C]: slot k >= 1 holds the logits of q^(k)
+ *           given q^(0..k-1); slot 0 is the head over the hidden state
+ *           itself, which the method does not use.
+ * n * N must not exceed max_batch * prefill_chunk (the prefill rows of the
+ * workspace).  Needs N <= 16, fast head_dim <= 128 and <= 8 query heads per
+ * KV head.  The decode state of the context is not touched. */
+dualar_status dualar_fast_teacher_forced(dualar_ctx_t *ctx, int32_t n, const float *hidden,
+                                         const int32_t *codes, float *logits);
+
 /* Block until the stream's work is done; report latched device faults.
  * *device_status (host, may be NULL) receives the raw status word. */
 dualar_status dualar_sync(dualar_ctx_t *ctx, int32_t *device_status);

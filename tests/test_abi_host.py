@@ -114,5 +114,6 @@ def test_null_context_calls(lib):
     assert lib.dualar_prefill(None, 1, None, 1, None, C.byref(s), None, None, None) == -1
     assert lib.dualar_decode_frames(None, 1, C.byref(s), None, None, None, None) == -1
     assert lib.dualar_fast_frames(None, 1, 1, None, None, C.byref(s), None, None, None) == -1
+    assert lib.dualar_fast_teacher_forced(None, 1, None, None, None) == -1
     assert lib.dualar_sync(None, None) == -1
     lib.dualar_destroy(None)

@@ -527,3 +527,63 @@ def test_s2_full_bf16_kv(s2_full):
     P = synth.make_prompts(m, ("fixed", 5, 20, 15), [40], seed=0)
     c, worst = run_and_compare(m, w, P, [40], 2, dict(greedy=1), tag="s2-full-kvbf16", floor=True)
     assert c[0] >= 2
+
+
+# ----------------------------------------------------------------------------
+# teacher-forced fast AR (the scoring / training form, all pairs at once)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [5, 100])
+def test_tiny_fast_teacher_forced(tiny, n):
+    # n (hidden state, codes) pairs -> n*N rows through the fast layers with
+    # causal attention along depth; slot k >= 1 of each pair must equal the
+    # oracle's teacher-forced logits of q^(k) (fp32 weights: 1e-4)
+    DualAR, upload = _dev()
+    m, w = tiny
+    N, C = m["num_codebooks"], m["codebook_size"]
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal((n, m["dim"])).astype(np.float32)
+    codes = rng.integers(0, C, size=(n, N)).astype(np.int32)
+    say(f"[tiny-tf] GPU n={n}")
+    ctx = DualAR(m, upload(m, w), max_batch=1, max_seq_len=16)
+    got = ctx.fast_teacher_forced(torch.from_numpy(h).cuda(), torch.from_numpy(codes).cuda()).cpu().numpy()
+    assert ctx.sync() == 0
+    ctx.close()
+    o = DualAROracle(m, synth.weights_as_f32(m, w), max_seq=8)
+    worst = 0.0
+    for i in range(n):
+        ref = o.fast_teacher_forced(h[i].astype(np.float64), codes[i].tolist())
+        e = rel_l2(got[i, 1:], ref)
+        worst = max(worst, e)
+        assert e <= 1e-4, (i, e)
+    say(f"[tiny-tf] worst rel L2 {worst:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_s2_fast_teacher_forced(s2_fast):
+    # S2 fast shapes in bf16: 32 pairs = 320 rows, so every product runs on
+    # the 2-D matrix-core tiles
+    DualAR, upload = _dev()
+    m, w = s2_fast
+    N, C, n = m["num_codebooks"], m["codebook_size"], 32
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal((n, m["fast_dim"])).astype(np.float32)
+    codes = rng.integers(0, C, size=(n, N)).astype(np.int32)
+    dev = upload(m, dict(w))
+    dummy = torch.zeros(16, dtype=torch.bfloat16, device="cuda")
+    for name, _, _ in synth.tensor_specs(m):
+        dev.setdefault(name, dummy)
+    say(f"[s2-tf] GPU n={n}")
+    ctx = DualAR(m, dev, max_batch=1, max_seq_len=16)
+    got = ctx.fast_teacher_forced(torch.from_numpy(h).cuda(), torch.from_numpy(codes).cuda()).cpu().numpy()
+    assert ctx.sync() == 0
+    ctx.close()
+    say("[s2-tf] oracle")
+    fo = _FastOracle(m, synth.weights_as_f32(m, w))
+    worst = 0.0
+    for i in range(n):
+        ref = fo.o.fast_teacher_forced(h[i].astype(np.float64), codes[i].tolist())
+        e = rel_l2(got[i, 1:], ref)
+        worst = max(worst, e)
+        assert e <= REL_L2, (i, e)
+    say(f"[s2-tf] worst rel L2 {worst:.2e}")
