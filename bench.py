@@ -1,7 +1,7 @@
 """Benchmark: Dual-AR frames/s on one MI355X, with the HBM roofline of the
 dominant kernel and the CPU oracle timed beside it.
 
-    python bench.py [--steps K] [--warmup W] [--workload s2_b1|s2_b32|s2_prefill|fast_s2|fast_s2_b16|tiny_b1]
+    python bench.py [--steps K] [--warmup W] [--workload s2_b1|s2_b32|s2_prefill|s2_fast_tf|fast_s2|fast_s2_b16|tiny_b1]
                     [--semantic-head] [--ras]
 
 A step is one decode frame of the whole hot path (fusion, slow pass, biased
@@ -34,6 +34,8 @@ WORKLOADS = {
     "tiny_b1": ("tiny_b1", None, "tiny fp32 Dual-AR, batch 1, 32-token prompt, greedy"),
     "s2_prefill": ("s2_prefill", None, "full S2-shaped prefill of 16,384 frame positions at batch 4 "
                                        "(time to frame 0), then 64 greedy decode frames"),
+    "s2_fast_tf": ("fast_s2", None, "S2-shaped teacher-forced fast AR: 819 (hidden state, codes) pairs, "
+                                    "8,190 rows through the fast layers and head per step"),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
@@ -97,6 +99,73 @@ def cpu_baseline(m, w, fast_only, seed, budget_s=20.0):
                       f"<2% to the oracle's per-frame work)"}
 
 
+def bench_fast_tf(args, torch, synth, DualAR, upload_weights, reporting):
+    """The teacher-forced fast AR (scoring form): K timed steps, each one call
+    over n pairs; frames/s counts pairs (one frame's fast AR each)."""
+    wl = synth.WORKLOADS["fast_s2"]
+    m = synth.model(wl["model"])
+    N, n = m["num_codebooks"], 819
+    K = args.steps if args.steps is not None else 20
+    W = args.warmup
+    t0 = time.time()
+    w = synth.make_weights(m, seed=args.seed)
+    log(f"[bench] s2_fast_tf: weights generated in {time.time() - t0:.1f}s")
+    dev_w = upload_weights(m, w)
+    ctx = DualAR(m, dev_w, max_batch=2, max_seq_len=16)       # 2 x 4,096 prefill rows >= n*N
+    rng = np.random.default_rng(args.seed)
+    h = torch.from_numpy(rng.standard_normal((n, m["fast_dim"])).astype(np.float32)).cuda()
+    codes = torch.from_numpy(rng.integers(0, m["codebook_size"], size=(n, N)).astype(np.int32)).cuda()
+    out = torch.empty((n, N, m["codebook_size"]), device="cuda")
+    for _ in range(W):
+        ctx.fast_teacher_forced(h, codes, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        ctx.fast_teacher_forced(h, codes, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    assert ctx.sync() == 0
+    fl = reporting.fast_tf_flops(m, n)
+    tf = fl["total"] / (ms * 1e-3) / 1e12
+    log(f"[bench] {K} steps of {n} pairs: {ms:.3f} ms/step, {n / ms * 1e3:.0f} frames/s, {tf:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import DualAROracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+        except Exception:
+            cores = os.cpu_count()
+        shell = dict(m, n_layer=1, dim=m["fast_dim"], vocab_size=m["codebook_size"] + 64, semantic_begin_id=0,
+                     semantic_end_id=m["codebook_size"] - 1, end_id=m["codebook_size"] + 8)
+        spec = {nm: sh for nm, sh, _ in synth.tensor_specs(shell)}
+        lw = _LazyF32(m, w)
+        wf = {nm: (lw[nm] if nm.startswith("fast_") else np.zeros(sh, dtype=np.float32)) for nm, sh in spec.items()}
+        o = DualAROracle(shell, wf, max_seq=8)
+        hh, cc = h.cpu().numpy(), codes.cpu().numpy()
+        cnt, t1 = 0, time.time()
+        while cnt < 64 and (cnt == 0 or time.time() - t1 < 20.0):
+            o.fast_teacher_forced(hh[cnt].astype(np.float64), cc[cnt].tolist())
+            cnt += 1
+        cpu = {"value": cnt / (time.time() - t1), "unit": "frames/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"{cnt} teacher-forced pairs one at a time, float64 oracle"}
+    ctx.close()
+    print(json.dumps({
+        "metric": METRIC, "value": round(n / ms * 1e3, 3), "unit": "frames/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded random-init weights of the S2 shapes, random hidden states "
+                                 "and codes)",
+        "config": {"workload": f"s2_fast_tf: {WORKLOADS['s2_fast_tf'][2]}", "pairs": n, "rows": fl["rows"],
+                   "accumulate": "f32", "kv_cache": m["weight_dtype"]},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 5), "traffic": None,
+                     "flops_per_step": fl["total"]},
+        "cpu_baseline": cpu,
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +206,8 @@ def main():
     from dual_autoregressive_tts_amd import DualAR, reporting
     from dual_autoregressive_tts_amd.binding import K_ATTN, K_GEMV, K_GEMV_SWIGLU, upload_weights
 
+    if args.workload == "s2_fast_tf":
+        return bench_fast_tf(args, torch, synth, DualAR, upload_weights, reporting)
     wl_name, b_over, desc = WORKLOADS[args.workload]
     wl = synth.WORKLOADS[wl_name]
     m = synth.model(wl["model"])

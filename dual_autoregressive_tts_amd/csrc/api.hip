@@ -877,9 +877,10 @@ dualar_status dualar_fast_teacher_forced(dualar_ctx_t* c, int32_t n, const float
   const int N = c->r.N;
   if (n < 1 || (long long)n * N > c->L.rows)
     return fail(c, DUALAR_ERR_INVALID_ARG, "n out of range [1, max_batch * prefill_chunk / num_codebooks]");
-  if (N > 16 || c->fast.hd > 128 || c->fast.hd % 2 || c->fast.H / c->fast.KV > 8)
-    return fail(c, DUALAR_ERR_INVALID_ARG, "teacher-forced form needs N <= 16, fast head_dim <= 128 (even), "
-                                           "<= 8 query heads per KV head");
+  if (N > 11 || c->fast.hd > 128 || c->fast.hd % 4 || c->fast.H / c->fast.KV > 8 ||
+      (c->fast.H / c->fast.KV) & (c->fast.H / c->fast.KV - 1))
+    return fail(c, DUALAR_ERR_INVALID_ARG, "teacher-forced form needs N <= 11, fast head_dim <= 128 (a multiple "
+                                           "of 4), 1, 2, 4 or 8 query heads per KV head");
   // the activation buffers are scratch between calls: the decode state is untouched
   return dispatch(c, [&](auto wt, auto kt) {
     return do_fast_tf<decltype(wt), decltype(kt)>(c, n, hidden, codes, logits);

@@ -101,3 +101,18 @@ def prefill_flops(m: dict, prompt_lengths) -> dict:
     pairs = sum(int(t) * (int(t) + 1) // 2 for t in prompt_lengths)
     attention = 4 * m["head_dim"] * m["n_head"] * m["n_layer"] * pairs
     return {"linear": linear, "attention": attention, "total": linear + attention, "tokens": tokens}
+
+
+def fast_tf_flops(m: dict, n: int) -> dict:
+    """Arithmetic of one teacher-forced fast-AR call over n (hidden state,
+    codes) pairs: the fast layers and the fast head over n*N rows (2 flops
+    per weight per row: the 414.2 M weights of one fast pass on the S2
+    shapes), and causal attention along depth, where depth position k attends
+    to positions 0..k (4*hd flops per attended position and query head)."""
+    N, d = m["num_codebooks"], m["fast_dim"]
+    H, KV, hd, f = m["fast_n_head"], m["fast_n_kv_head"], m["fast_head_dim"], m["fast_ffn_dim"]
+    per_layer = d * (H + 2 * KV) * hd + H * hd * d + 3 * d * f
+    rows = n * N
+    linear = 2 * rows * (m["n_fast_layer"] * per_layer + m["codebook_size"] * d)
+    attention = 4 * hd * H * m["n_fast_layer"] * n * (N * (N + 1) // 2)
+    return {"linear": linear, "attention": attention, "total": linear + attention, "rows": rows}

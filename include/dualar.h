@@ -229,8 +229,9 @@ dualar_status dualar_fast_frames(dualar_ctx_t *ctx, int32_t batch, int32_t n_fra
  *           given q^(0..k-1); slot 0 is the head over the hidden state
  *           itself, which the method does not use.
  * n * N must not exceed max_batch * prefill_chunk (the prefill rows of the
- * workspace).  Needs N <= 16, fast head_dim <= 128 and <= 8 query heads per
- * KV head.  The decode state of the context is not touched. */
+ * workspace).  Needs N <= 11, a fast head_dim <= 128 that is a multiple of
+ * 4, and 1, 2, 4 or 8 query heads per KV head (else
+ * DUALAR_ERR_INVALID_ARG).  The decode state of the context is not touched. */
 dualar_status dualar_fast_teacher_forced(dualar_ctx_t *ctx, int32_t n, const float *hidden,
                                          const int32_t *codes, float *logits);
 

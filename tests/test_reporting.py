@@ -66,3 +66,18 @@ def test_prefill_flops_config5():
     assert f["linear"] == 2 * 65536 * 36 * per_layer
     assert f["attention"] == 4 * 128 * 32 * 36 * 4 * (16384 * 16385 // 2)
     assert 4.75e14 < f["linear"] < 4.77e14 and 3.16e14 < f["attention"] < 3.18e14
+
+
+def test_fast_tf_flops_s2():
+    # one teacher-forced row reads the weights of one fast pass: four layers
+    # plus the 4,096-row head, 414.2 M on the S2 shapes ([P2], golden file)
+    import json
+    import os
+    from dual_autoregressive_tts_amd import reporting
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "s2_page_numbers.json")))
+    m = synth.model("s2")
+    f = reporting.fast_tf_flops(m, 819)
+    assert f["rows"] == 8190
+    per_row = f["linear"] / (2 * f["rows"])
+    assert abs(per_row / 1e6 - gold["fast_pass_weights_M"]["value"]) < 0.05
+    assert f["attention"] == 4 * 128 * 32 * 4 * 819 * 55
