@@ -984,7 +984,7 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   const bool glu = p.mode == GEMV_SWIGLU;
   const int z_tiles = (p.B + 31) / 32;
   if (!cfg && p.B >= GM_TILE_ROWS) cfg = 20 + gemm_tile_choice(p);
-  if (cfg >= 21 && cfg <= 23) {   // 2-D output tiles (prefill steps)
+  if (cfg >= 21 && cfg <= 24) {   // 2-D output tiles (prefill steps)
     if (p.prep_done) *p.prep_done = 0;
     if (p.next_done) *p.next_done = 0;
     *err = launch_gemm_tile(p, cfg - 20, s) ? hipGetLastError() : hipErrorInvalidValue;

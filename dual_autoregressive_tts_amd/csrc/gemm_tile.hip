@@ -37,7 +37,7 @@
 #define TL_KC 32
 #define TL_GB 8
 
-template <int WN, int WB, int GN, int GW> struct Tl {
+template <int WN, int WB, int GN, int GW, int STG = 3> struct Tl {
   static constexpr int WAVES = GN * GW;   // GN wave rows (weights) x GW wave columns (activations)
   static constexpr int NROWS = 32 * WN * GN;   // weight rows per tile
   static constexpr int BROWS = 32 * WB * GW;   // activation rows per tile
@@ -108,10 +108,11 @@ __device__ __forceinline__ int nth_live_tile(const uint64_t (&m)[2], int n) {
 
 // One-dimensional grid of 8 * ceil(tiles / 8) workgroups of 256 threads.
 // The host guarantees K % 32 == 0, B >= 1 and n_out >= 1.
-template <int WN, int WB, int GN, int GW>
+template <int WN, int WB, int GN, int GW, int STG = 3>
 __global__ void __launch_bounds__(64 * GN * GW, 1) mfma_tile_kernel(GemvParams p) {
   using L = Tl<WN, WB, GN, GW>;
-  __shared__ __attribute__((aligned(1024))) char smem[3 * L::STAGE];
+  static_assert(STG == 2 || STG == 3, "stages");
+  __shared__ __attribute__((aligned(1024))) char smem[STG * L::STAGE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave / GW, wb = wave % GW;
   const bool glu = p.mode == GEMV_SWIGLU;
@@ -172,23 +173,37 @@ __global__ void __launch_bounds__(64 * GN * GW, 1) mfma_tile_kernel(GemvParams p
   // every wave is done with chunk c-1 (barrier).  The steady loop has no
   // branches; the last two chunks follow it.
   const int nch = p.K / TL_KC;
-  tl_issue<WN, WB, GN, GW>(src, smem, 0, wave);
-  if (nch > 1) tl_issue<WN, WB, GN, GW>(src, smem + L::STAGE, 1, wave);
-  int cs = 0;   // stage of chunk c
-  for (int c = 0; c + 2 < nch; ++c) {
-    wait_vm_barrier<L::DMA>();
-    const int ns = cs == 0 ? 2 : cs - 1;   // (c + 2) % 3
-    tl_issue<WN, WB, GN, GW>(src, smem + ns * L::STAGE, c + 2, wave);
+  if constexpr (STG == 3) {
+    tl_issue<WN, WB, GN, GW>(src, smem, 0, wave);
+    if (nch > 1) tl_issue<WN, WB, GN, GW>(src, smem + L::STAGE, 1, wave);
+    int cs = 0;   // stage of chunk c
+    for (int c = 0; c + 2 < nch; ++c) {
+      wait_vm_barrier<L::DMA>();
+      const int ns = cs == 0 ? 2 : cs - 1;   // (c + 2) % 3
+      tl_issue<WN, WB, GN, GW>(src, smem + ns * L::STAGE, c + 2, wave);
+      tl_compute<WN, WB, GN, GW>(smem + cs * L::STAGE, wn, wb, lane, acc);
+      cs = cs == 2 ? 0 : cs + 1;
+    }
+    if (nch > 1) {
+      wait_vm_barrier<L::DMA>();
+      tl_compute<WN, WB, GN, GW>(smem + cs * L::STAGE, wn, wb, lane, acc);
+      cs = cs == 2 ? 0 : cs + 1;
+    }
+    wait_vm_barrier<0>();
     tl_compute<WN, WB, GN, GW>(smem + cs * L::STAGE, wn, wb, lane, acc);
-    cs = cs == 2 ? 0 : cs + 1;
-  }
-  if (nch > 1) {
-    wait_vm_barrier<L::DMA>();
+  } else {
+    // two stages: chunk c+1 is in flight while chunk c is multiplied
+    tl_issue<WN, WB, GN, GW>(src, smem, 0, wave);
+    int cs = 0;
+    for (int c = 0; c + 1 < nch; ++c) {
+      wait_vm_barrier<0>();
+      tl_issue<WN, WB, GN, GW>(src, smem + (cs ^ 1) * L::STAGE, c + 1, wave);
+      tl_compute<WN, WB, GN, GW>(smem + cs * L::STAGE, wn, wb, lane, acc);
+      cs ^= 1;
+    }
+    wait_vm_barrier<0>();
     tl_compute<WN, WB, GN, GW>(smem + cs * L::STAGE, wn, wb, lane, acc);
-    cs = cs == 2 ? 0 : cs + 1;
   }
-  wait_vm_barrier<0>();
-  tl_compute<WN, WB, GN, GW>(smem + cs * L::STAGE, wn, wb, lane, acc);
 
   // Epilogue straight from the accumulators: lanes 0..31 hold 32 consecutive
   // columns of row b, lanes 32..63 the same columns of row b + 4.
@@ -230,7 +245,8 @@ __global__ void __launch_bounds__(64 * GN * GW, 1) mfma_tile_kernel(GemvParams p
 }
 
 // Launch the tiled product: cfg 1: 256 weight rows x 128 activation rows, 4
-// waves; cfg 2: 128 x 128, 4 waves; cfg 3: 256 x 128, 8 waves of 64 x 64.
+// waves; cfg 2: 128 x 128, 4 waves; cfg 3: 256 x 128, 8 waves of 64 x 64;
+// cfg 4: 512 x 128, 8 waves of 128 x 64, two stages.
 // The input planes are at p.xn.  Returns false when the shape does not
 // apply.
 bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
@@ -247,6 +263,7 @@ bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
     case 1: hipLaunchKernelGGL((mfma_tile_kernel<4, 2, 2, 2>), grid(256), dim3(256), 0, s, p); return true;
     case 2: hipLaunchKernelGGL((mfma_tile_kernel<2, 2, 2, 2>), grid(128), dim3(256), 0, s, p); return true;
     case 3: hipLaunchKernelGGL((mfma_tile_kernel<2, 2, 4, 2>), grid(256), dim3(512), 0, s, p); return true;
+    case 4: hipLaunchKernelGGL((mfma_tile_kernel<4, 2, 4, 2, 2>), grid(512), dim3(512), 0, s, p); return true;
     default: return false;
   }
 }
@@ -254,5 +271,8 @@ bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
 // Tile shape for a product.  The 8-wave 256 x 128 tile (two waves per SIMD,
 // so one wave's LDS waits and barrier hide under the other's products) ran
 // the S2 prefill products at 37-48 % of the matrix-core peak over the three
-// terms, against 30-41 % for the 4-wave tiles at any shape.
-int gemm_tile_choice(const GemvParams&) { return 3; }
+// terms, against 30-41 % for the 4-wave tiles at any shape.  Wide products
+// take the 8-wave 512 x 128 tile (waves of 128 x 64 read 0.42 KB of operand
+// fragments per product instead of 0.67 KB; two stages to fit LDS): 2-3 %
+// faster there; on 2,560 output rows it would leave a quarter round.
+int gemm_tile_choice(const GemvParams& p) { return p.n_out >= 4096 ? 4 : 3; }
