@@ -354,7 +354,11 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.max_pos = S.max_pos; a.pos = pos_dev; a.pos_const = pos_const; a.rope = S.rope;
   a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
   a.H = S.H; a.KV = S.KV; a.hd = S.hd;
-  a.it = B <= 4 ? 4 : 8;   // (batch 1: 4 loads per lane measured 12.0 us per layer, 2 loads 14.7 us)
+  // Up to batch 4 with contexts of at most 2,048 positions: the split form
+  // with 4 loads per lane (batch 1, 1k context: 12.0 us per layer against 14.7
+  // with 2).  Otherwise the balanced flash-decoding form (it = 8): at batch 4
+  // and 16k positions the split form needs 256 splits per head and a merge.
+  a.it = (B <= 4 && Lmax <= 2048) ? 4 : 8;
   a.lmax = Lmax;
   a.part = (float*)(c->ws + L.part);
   a.counters = (unsigned*)(c->ws + L.counters);

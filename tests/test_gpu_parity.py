@@ -308,6 +308,20 @@ def test_bf16_batched_long_context(tiny):
     assert sum(c) >= 18
 
 
+def test_bf16_small_batch_long_context():
+    # batch 3 with contexts past 2,048 positions takes the balanced
+    # flash-decoding form (tiles over all (sequence, KV head) pairs, heads
+    # split over workgroups and merged); batch 1 past 2,048 too, with the
+    # separate query preparation (no batched QKV finish at batch 1)
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
+                    n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1, fast_head_dim=128)
+    w = synth.make_weights(m, seed=7)
+    for plen in (np.array([2300, 2100, 2600], dtype=np.int32), np.array([2200], dtype=np.int32)):
+        P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=7)
+        c, worst = run_and_compare(m, w, P, plen, 3, dict(greedy=1), tag=f"bf16-long-b{len(plen)}", floor=True)
+        assert sum(c) >= 3 * len(plen)
+
+
 def test_end_token_stops_and_pads(tiny):
     m, w = tiny
     w = {k: v.copy() for k, v in w.items()}
