@@ -302,6 +302,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   // finish then also writes the next product's normalised input planes (xn).
   void* const xn = c->ws + L.xn;
   int fused = 0;
+  bool o_done = false;
   GemvParams g{};
   // q | k | v = W_qkv . RMSNorm(x)
   g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
@@ -345,6 +346,22 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     a.H = S.H; a.KV = S.KV; a.hd = S.hd;
     a.out = att; a.ld_out = L.att_ld; a.out_planes = planes; a.R = B; a.B = B / rows_per_seq;
     HIPCHK((launch_prefill_attn<T, KT>(a, c->stream)));
+  } else if (B == 1 && !pos_dev && sizeof(T) == 2 && sizeof(KT) == 2 &&
+             attn_o_b1_fits(S.H, S.KV, S.hd, S.dim, pos_const + 1)) {
+    // fast AR at batch 1: the depth attention runs inside the O product
+    AttnOParams a{};
+    a.qkv = qkv;
+    a.kcache = S.k + (size_t)l * S.layer_stride * r.kvesz;
+    a.vcache = S.v + (size_t)l * S.layer_stride * r.kvesz;
+    a.max_pos = S.max_pos; a.pos = pos_const; a.rope = S.rope;
+    a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
+    a.H = S.H; a.KV = S.KV; a.hd = S.hd;
+    a.wo = w.wo; a.x = x; a.dim = S.dim;
+    HIPCHK(prof_pre(c, DUALAR_K_GEMV));
+    HIPCHK(launch_attn_o_b1(a, c->stream));
+    HIPCHK(prof_post(c, DUALAR_K_GEMV, (double)S.dim * S.H * S.hd * r.esz +
+                                           (double)(pos_const + 1) * 2.0 * S.KV * S.hd * r.kvesz));
+    o_done = true;
   } else {
   // attention over the cache (+QK-norm, RoPE, append)
   AttnParams a{};
@@ -375,6 +392,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   }
   }
   // x += Wo . o
+  if (!o_done) {
   g = GemvParams{};
   g.w[0] = w.wo; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.H * S.hd; g.n_out = S.dim;
   g.x = att; g.ldx = L.att_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
@@ -382,6 +400,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   g.xplanes = planes;
   if (planes) { g.next_gain = w.ffn_norm; g.next_planes = xn; g.next_done = &fused; g.eps = r.eps; }
   HIPCHK(gemv<T>(c, g));
+  }
   // h = silu(W1 n) * (W3 n), n = RMSNorm(x)
   g = GemvParams{};
   g.w[0] = w.w1; g.w[1] = w.w3; g.rows[0] = S.ffn; g.rows[1] = S.ffn; g.n_seg = 2;

@@ -1,0 +1,254 @@
+// Batch-1 attention over a short cache fused with the O product and its
+// residual: x += W_o . softmax(q K^T / sqrt(hd)) V.
+//
+// The fast AR attends along codebook depth, so its cache never holds more
+// than num_codebooks (10) positions ([P2] "Two autoregressions…": the fast
+// loop and its per-frame cache).  At batch 1 a separate attention launch
+// costs a full dispatch for a few KB of work, while the O product that
+// follows streams 21 MB of weights that do not depend on the attention.
+// Here every workgroup issues its small attention loads, then its share of
+// W_o, and computes the attention for all query heads while the weights are
+// in flight; the attention output never leaves the workgroup.
+//
+// Shape (S2 fast AR): H = 32 query heads, KV = 8 KV heads, head_dim 128,
+// bf16 weights and cache, at most 16 positions.  A workgroup is 8 waves;
+// wave w owns KV head w and its query heads 4w..4w+3 (contiguous grouping),
+// which are exactly columns [512 w, 512 w + 512) of W_o: the wave's
+// attention output is the wave's eighth of the product input.  Two waves
+// per SIMD hide each other's reduction and matrix-core latencies.
+//
+// Arithmetic follows the other decode attention kernels: per-head RMSNorm
+// of q and k with one [hd] gain, RoPE on interleaved pairs from the bf16
+// table, the 1/sqrt(hd) scale folded into q, the new k and v rounded to the
+// cache type before use, scores on the matrix cores with q as three bf16
+// terms (the fp32 product), fp32 softmax and accumulation.  Every workgroup
+// computes the same values; workgroup 0 alone appends k and v.
+#include "common.h"
+#include "internal.h"
+
+namespace {
+constexpr int HD = 128;      // head_dim
+constexpr int REP = 4;       // query heads per KV head (= per wave)
+constexpr int NW = 8;        // waves per workgroup (= KV heads)
+constexpr int MAXL = 16;     // positions
+constexpr int WGT = NW * 64;
+typedef __bf16 att_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float att_f32x4 __attribute__((ext_vector_type(4)));
+}
+
+template <int R>
+__global__ void __launch_bounds__(WGT) attn_o_b1_kernel(AttnOParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t qp[NW][3][REP][HD];   // q as three bf16 terms
+  __shared__ __attribute__((aligned(16))) float kn[NW][HD];
+  __shared__ __attribute__((aligned(16))) float sc[NW][REP][MAXL];
+  __shared__ __attribute__((aligned(16))) float os[NW][REP * HD];
+  __shared__ float part[NW][R];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = wave;                       // KV head
+  const int pos = p.pos, L = pos + 1;
+  const int K = p.H * HD;
+  const int row0 = blockIdx.x * R;
+
+  // ---- 1. attention inputs, issued before the weights ----
+  const float* qkv = p.qkv;
+  float2 q2[REP];
+#pragma unroll
+  for (int h4 = 0; h4 < REP; ++h4) q2[h4] = *(const float2*)(qkv + (size_t)(g * REP + h4) * HD + 2 * lane);
+  const float2 k2 = *(const float2*)(qkv + (size_t)p.H * HD + (size_t)g * HD + 2 * lane);
+  const float2 v2 = *(const float2*)(qkv + (size_t)(p.H + p.KV) * HD + (size_t)g * HD + 2 * lane);
+  uint32_t qg = 0x3f803f80u, kg = 0x3f803f80u;   // bf16 pair (1, 1)
+  if (p.q_norm) qg = ((const uint32_t*)p.q_norm)[lane];
+  if (p.k_norm) kg = ((const uint32_t*)p.k_norm)[lane];
+  const float2 cs = p.rope[(size_t)pos * (HD / 2) + lane];
+  const float xres = (threadIdx.x < R && row0 + (int)threadIdx.x < p.dim) ? p.x[row0 + threadIdx.x] : 0.f;
+  // cached K as the A operand of the score product (16 positions x 32 dims
+  // per step): lane l holds position l % 16, dims 32 ks + 8 (l / 16) .. +8;
+  // lanes at or past pos read position 0 (always written) and never use it
+  const int jm = lane & 15, kq = lane >> 4;
+  const int jl = jm < pos ? jm : 0;
+  u32x4 kc[4];
+  {
+    const char* src = (const char*)p.kcache + (((size_t)g * p.max_pos + jl) * HD + 8 * kq) * sizeof(bf16_t);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kc[ks] = ld_vec(src + 64 * ks);
+  }
+  // cached V in the dim layout: lane l holds dims 2l, 2l+1 of every position
+  uint32_t vc[MAXL];
+  {
+    const uint32_t* src = (const uint32_t*)((const char*)p.vcache + ((size_t)g * p.max_pos * HD + 2 * lane) * sizeof(bf16_t));
+#pragma unroll
+    for (int jj = 0; jj < MAXL; ++jj) {
+      vc[jj] = 0u;
+      if (jj < pos) vc[jj] = src[(size_t)jj * (HD / 2)];
+    }
+  }
+
+  // ---- 2. this workgroup's rows of W_o, the wave's 512 columns ----
+  u32x4 w[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(row0 + r, p.dim - 1);
+    w[r] = ld_stream((const char*)p.wo + ((size_t)row * K + (size_t)wave * 512 + lane * 8) * sizeof(bf16_t));
+  }
+
+  // ---- 3. q: QK-norm, RoPE, score scale; new k: QK-norm, RoPE, rounding ----
+  const float qscale = 1.0f / sqrtf((float)HD);
+  const float qga = bf16_bits_to_f32(qg & 0xffffu), qgc = bf16_bits_to_f32(qg >> 16);
+  const float kga = bf16_bits_to_f32(kg & 0xffffu), kgc = bf16_bits_to_f32(kg >> 16);
+#pragma unroll
+  for (int h4 = 0; h4 < REP; ++h4) {
+    float a = q2[h4].x, c = q2[h4].y;
+    if (p.q_norm) {
+      const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)HD + p.eps);
+      a = a * inv * qga;
+      c = c * inv * qgc;
+    }
+    const float ra = (a * cs.x - c * cs.y) * qscale, rc = (a * cs.y + c * cs.x) * qscale;
+    // three bf16 terms t0 + t1 + t2 of each value, so that the bf16 product
+    // with the (bf16) keys is the fp32 one
+    const uint16_t a0 = f32_to_bf16_rne(ra), c0 = f32_to_bf16_rne(rc);
+    const float a1f = ra - bf16_bits_to_f32(a0), c1f = rc - bf16_bits_to_f32(c0);
+    const uint16_t a1 = f32_to_bf16_rne(a1f), c1 = f32_to_bf16_rne(c1f);
+    const uint16_t a2 = f32_to_bf16_rne(a1f - bf16_bits_to_f32(a1));
+    const uint16_t c2 = f32_to_bf16_rne(c1f - bf16_bits_to_f32(c1));
+    *(uint32_t*)&qp[wave][0][h4][2 * lane] = (uint32_t)a0 | ((uint32_t)c0 << 16);
+    *(uint32_t*)&qp[wave][1][h4][2 * lane] = (uint32_t)a1 | ((uint32_t)c1 << 16);
+    *(uint32_t*)&qp[wave][2][h4][2 * lane] = (uint32_t)a2 | ((uint32_t)c2 << 16);
+  }
+  float vn0, vn1;
+  {
+    float a = k2.x, c = k2.y;
+    if (p.k_norm) {
+      const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)HD + p.eps);
+      a = a * inv * kga;
+      c = c * inv * kgc;
+    }
+    const uint16_t ka = f32_to_bf16_rne(a * cs.x - c * cs.y);
+    const uint16_t kb = f32_to_bf16_rne(a * cs.y + c * cs.x);
+    const uint16_t va = f32_to_bf16_rne(v2.x), vb = f32_to_bf16_rne(v2.y);
+    kn[wave][2 * lane] = bf16_bits_to_f32(ka);
+    kn[wave][2 * lane + 1] = bf16_bits_to_f32(kb);
+    vn0 = bf16_bits_to_f32(va);
+    vn1 = bf16_bits_to_f32(vb);
+    if (blockIdx.x == 0) {
+      const size_t at = ((size_t)g * p.max_pos + pos) * HD + 2 * lane;
+      *(uint32_t*)((char*)p.kcache + at * sizeof(bf16_t)) = (uint32_t)ka | ((uint32_t)kb << 16);
+      *(uint32_t*)((char*)p.vcache + at * sizeof(bf16_t)) = (uint32_t)va | ((uint32_t)vb << 16);
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. scores on the matrix cores: S^T = K . q^T ----
+  // A = 16 positions x 32 dims of K (bf16, exact), B = 32 dims x 16 columns
+  // (column n: query head n % 4, one bf16 term of q per product, the three
+  // accumulated); lane l gets S[4 (l / 16) + r][l % 16].
+  {
+    att_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      att_bf16x8 a = __builtin_bit_cast(att_bf16x8, kc[ks]);
+      if (jm == pos) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (__bf16)kn[wave][32 * ks + 8 * kq + e];
+      }
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const u32x4 b = *(const u32x4*)&qp[wave][t][jm & 3][32 * ks + 8 * kq];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(att_bf16x8, b), acc, 0, 0, 0);
+      }
+    }
+    if (jm < REP) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jj = 4 * kq + r;
+        if (jj < L) sc[wave][jm][jj] = acc[r];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. softmax: lane (head l / 16, position l % 16) ----
+  {
+    const int h4 = lane >> 4, jj = lane & 15;
+    const float s = jj < L ? sc[wave][h4][jj] : -INFINITY;
+    float m = fmaxf(s, xor1_of(s));
+    m = fmaxf(m, xor2_of(m));
+    m = fmaxf(m, mir8_of(m));
+    m = fmaxf(m, mir16_of(m));
+    const float e = jj < L ? expf(s - m) : 0.f;
+    const float l = group_sum(e, 16);
+    sc[wave][h4][jj] = e / l;
+  }
+  __syncthreads();
+
+  // ---- 6. P.V in the dim layout, then the wave's eighth of the product input ----
+  float pr[REP][MAXL];
+#pragma unroll
+  for (int h4 = 0; h4 < REP; ++h4)
+#pragma unroll
+    for (int qd = 0; qd < MAXL / 4; ++qd) {
+      const float4 t = *(const float4*)&sc[wave][h4][4 * qd];
+      pr[h4][4 * qd] = t.x; pr[h4][4 * qd + 1] = t.y; pr[h4][4 * qd + 2] = t.z; pr[h4][4 * qd + 3] = t.w;
+    }
+  float o[REP][2];
+#pragma unroll
+  for (int h4 = 0; h4 < REP; ++h4) o[h4][0] = o[h4][1] = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < MAXL; ++jj) {
+    if (jj < L) {
+      float va, vb;
+      if (jj == pos) { va = vn0; vb = vn1; }
+      else { va = bf16_bits_to_f32(vc[jj] & 0xffffu); vb = bf16_bits_to_f32(vc[jj] >> 16); }
+#pragma unroll
+      for (int h4 = 0; h4 < REP; ++h4) {
+        o[h4][0] = fmaf(pr[h4][jj], va, o[h4][0]);
+        o[h4][1] = fmaf(pr[h4][jj], vb, o[h4][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h4 = 0; h4 < REP; ++h4) *(float2*)&os[wave][h4 * HD + 2 * lane] = make_float2(o[h4][0], o[h4][1]);
+  __syncthreads();
+  float ov[8];
+  {
+    const float4 t0 = *(const float4*)&os[wave][lane * 8];
+    const float4 t1 = *(const float4*)&os[wave][lane * 8 + 4];
+    ov[0] = t0.x; ov[1] = t0.y; ov[2] = t0.z; ov[3] = t0.w;
+    ov[4] = t1.x; ov[5] = t1.y; ov[6] = t1.z; ov[7] = t1.w;
+  }
+
+  // ---- 7. dot products, the eight column blocks summed in order, residual ----
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float wf[8];
+    ElemT<bf16_t>::unpack(w[r], wf);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(wf[e], ov[e], acc);
+    acc = wave_sum(acc);
+    if (lane == 0) part[wave][r] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < R && row0 + (int)threadIdx.x < p.dim) {
+    const int r = threadIdx.x;
+    float v = part[0][r];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) v += part[q][r];
+    p.x[row0 + r] = xres + v;
+  }
+}
+
+#ifndef ATTN_O_ROWS
+#define ATTN_O_ROWS 10
+#endif
+
+bool attn_o_b1_fits(int H, int KV, int hd, int dim, int L) {
+  return KV == NW && H == NW * REP && hd == HD && L >= 1 && L <= MAXL && dim > 0;
+}
+
+hipError_t launch_attn_o_b1(const AttnOParams& p, hipStream_t s) {
+  if (!attn_o_b1_fits(p.H, p.KV, p.hd, p.dim, p.pos + 1) || p.pos >= p.max_pos) return hipErrorInvalidValue;
+  const int nwg = (p.dim + ATTN_O_ROWS - 1) / ATTN_O_ROWS;
+  hipLaunchKernelGGL((attn_o_b1_kernel<ATTN_O_ROWS>), dim3(nwg), dim3(WGT), 0, s, p);
+  return hipGetLastError();
+}

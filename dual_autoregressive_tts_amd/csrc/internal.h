@@ -90,6 +90,22 @@ struct AttnParams {
   int B;
 };
 
+// Batch-1 attention over a short cache (at most 16 positions: the fast AR's
+// depth cache) fused with the O product and its residual: x += W_o . attn.
+// Also applies QK-norm + RoPE to the new q and k and appends k, v at pos.
+struct AttnOParams {
+  const float* qkv;                   // q | k | v of the one row
+  void* kcache; void* vcache;         // this layer, sequence 0: [KV][max_pos][hd] bf16
+  int max_pos, pos;                   // attends to positions 0..pos
+  const float2* rope;                 // [max_pos][hd/2] (cos, sin)
+  const void* q_norm; const void* k_norm; float eps;
+  int H, KV, hd;
+  const void* wo;                     // [dim][H*hd] bf16
+  float* x; int dim;                  // residual row, updated in place
+};
+bool attn_o_b1_fits(int H, int KV, int hd, int dim, int L);
+hipError_t launch_attn_o_b1(const AttnOParams& p, hipStream_t s);
+
 // Prefill of a chunk of positions: rows r = b*C + i hold position pos[r] of
 // sequence b (-1 = padding).  prefill_append_kernel applies QK-norm and RoPE
 // to every row's q and k, writes q (scaled by 1/sqrt(hd)) to qbuf and
