@@ -389,6 +389,110 @@ __global__ void __launch_bounds__(DUALAR_WG) gemv_ks_kernel(GemvParams p) {
   }
 }
 
+// One activation row, bf16 rows of U units (512 elements): one workgroup per
+// R consecutive output rows, sized so that the product is about one
+// workgroup per compute unit.  The NW waves split into NR segment groups
+// (gate, up for SwiGLU) of NWS = NW / NR waves; wave w of a group owns units
+// u = w, w + NWS, ... of every row of the workgroup, so each lane keeps
+// R * ceil(U / NWS) 16-byte weight loads in flight behind its activation
+// slice.  Fewer, larger workgroups than the 4-wave kernels: at batch 1 the
+// per-workgroup dispatch and ramp are a visible share of a 20-100 MB
+// product.  The RMSNorm prologue's sum of squares meets in LDS (each unit
+// belongs to one wave of a group); per-wave partial dot products are summed
+// over the group's waves in order.
+template <int NW, int R, int NR, int U>
+__global__ void __launch_bounds__(NW * 64) gemv_wide_kernel(GemvParams p) {
+  constexpr int NWS = NW / NR;
+  constexpr int UPW = (U + NWS - 1) / NWS;
+  __shared__ float part[NR][R][NWS];
+  __shared__ float ssq[NWS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = wave / NWS, wv = wave % NWS;
+  const int row0 = blockIdx.x * R;
+
+  // 1. the activation slices of the wave's units (+ gain)
+  float xv[UPW][8];
+  u32x4 gv[UPW];
+#pragma unroll
+  for (int i = 0; i < UPW; ++i) {
+    const int u = wv + NWS * i;
+    const bool live = u < U;
+    const float* xs = p.x + (size_t)(live ? u : 0) * 512 + lane * 8;
+    const float4 a = *(const float4*)xs, b = *(const float4*)(xs + 4);
+    xv[i][0] = live ? a.x : 0.f; xv[i][1] = live ? a.y : 0.f; xv[i][2] = live ? a.z : 0.f; xv[i][3] = live ? a.w : 0.f;
+    xv[i][4] = live ? b.x : 0.f; xv[i][5] = live ? b.y : 0.f; xv[i][6] = live ? b.z : 0.f; xv[i][7] = live ? b.w : 0.f;
+    if (p.gain) gv[i] = ld_vec((const char*)p.gain + ((size_t)(live ? u : 0) * 512 + lane * 8) * sizeof(bf16_t));
+  }
+  // 2. weights
+  u32x4 w[R][UPW];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(row0 + r, p.n_out - 1);
+    // SwiGLU: the wave's segment (gate or up) by a compare, not an index
+    // into the argument array (which would go through scratch)
+    const char* base = (NR == 2 ? (const char*)(seg == 0 ? p.w[0] : p.w[1]) + (size_t)row * p.K * sizeof(bf16_t)
+                                : seg_row<bf16_t>(p, row, 0)) + (size_t)lane * 8 * sizeof(bf16_t);
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int u = min(wv + NWS * i, U - 1);
+      w[r][i] = ld_stream(base + (size_t)u * 512 * sizeof(bf16_t));
+    }
+  }
+  // 3. RMSNorm * gain: the group's waves hold every unit once
+  if (p.gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += xv[i][e] * xv[i][e];
+    ss = wave_sum(ss);
+    if (lane == 0 && seg == 0) ssq[wv] = ss;
+    __syncthreads();
+    float tot = ssq[0];
+#pragma unroll
+    for (int q = 1; q < NWS; ++q) tot += ssq[q];
+    const float inv = 1.0f / sqrtf(tot / (float)p.K + p.eps);
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      float g[8];
+      ElemT<bf16_t>::unpack(gv[i], g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[i][e] = xv[i][e] * inv * g[e];
+    }
+  }
+  // 4. dot products over the wave's units, reduced across the wave
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      float wf[8];
+      ElemT<bf16_t>::unpack(w[r][i], wf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(wf[e], xv[i][e], acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) part[seg][r][wv] = acc;
+  }
+  __syncthreads();
+  // 5. epilogue: one thread per row
+  if ((int)threadIdx.x < R && row0 + (int)threadIdx.x < p.n_out) {
+    const int r = threadIdx.x, row = row0 + r;
+    float v[NR];
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      v[s] = part[s][r][0];
+#pragma unroll
+      for (int q = 1; q < NWS; ++q) v[s] += part[s][r][q];
+    }
+    float out;
+    if (p.mode == GEMV_SWIGLU) out = silu_f(v[0]) * v[NR - 1];
+    else if (p.mode == GEMV_ADD) out = p.res[row] + v[0];
+    else out = v[0];
+    p.y[row] = out;
+  }
+}
+
 template <typename T, int BT, int RPW, int NR>
 __global__ void __launch_bounds__(DUALAR_WG) gemv_loop_kernel(GemvParams p) {
   extern __shared__ float xs[];  // [BT][K]
@@ -482,11 +586,38 @@ static hipError_t go_ks(const GemvParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NW, int R, int NR, int U>
+static hipError_t go_wide(const GemvParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_wide_kernel<NW, R, NR, U>), dim3((p.n_out + R - 1) / R), dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+#ifndef GEMV_WIDE
+#define GEMV_WIDE 1
+#endif
+#ifndef WIDE_O_R
+#define WIDE_O_R 10
+#endif
+#ifndef WIDE_W2_NW
+#define WIDE_W2_NW 10
+#endif
+
 // One activation row of bf16 rows of 2560 / 4096 / 9728: the variants that
-// measured fastest for each S2 matrix (rows per wave, k-split).
+// measured fastest for each S2 matrix (rows per wave, k-split; or the wide
+// form with about one workgroup per compute unit for the S2 row counts).
 template <typename T, int NR>
 static bool pick_b1(const GemvParams& p, hipStream_t s, hipError_t* e) {
   if constexpr (sizeof(T) == 2) {
+    if (GEMV_WIDE) {
+      // the wide form for the long rows of O and W2 (5.8 / 10.0 us against
+      // 6.6 / 10.9 us); with 5 units per row it has too few waves per SIMD
+      // and the 4-wave kernels stay faster (QKV, W1|W3, fast head)
+      const int units = p.K / 512;
+      if constexpr (NR == 1) {
+        if (units == 8 && p.n_out == 2560) { *e = go_wide<8, WIDE_O_R, 1, 8>(p, s); return true; }        // O
+        if (units == 19 && p.n_out == 2560) { *e = go_wide<WIDE_W2_NW, 10, 1, 19>(p, s); return true; }  // W2
+      }
+    }
     const int units = p.K / (64 * ElemT<T>::EPV);
     if (units == 5) {
       if (NR == 1 && p.n_out >= 65536) *e = go<T, 1, 4, NR, 5>(p, s);  // tied head
