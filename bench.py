@@ -40,6 +40,39 @@ WORKLOADS = {
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+# HBM bytes per dispatch of the roofline kernel (the batch-1 SwiGLU W1|W3
+# GEMV), from rocprofv3 --pmc runs of `bench.py --steps 4 --warmup 2
+# --profile-frames 0 --no-cpu-baseline` restricted to gemv_rx_kernel:
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) times the factor the same
+# counter reads for a plain 1 GiB device copy (bench.py --copy-calibration).
+# The figures hold for the kernel text they were taken on: if the source of
+# gemv_rx_kernel changes, `traffic` is reported as null until they are
+# measured again.
+ROOFLINE_COUNTERS = {
+    "fetch_kib": 48746.695, "fetch_scale": 1073741824 / 1024 / 524300.3125,
+    "write_kib": 38.05, "write_scale": 1073741824 / 1024 / 1048576.0,
+}
+ROOFLINE_KERNEL_SHA256 = "896f099c92dd1480f9cae59c9e461a974a00feaeec347ad0b0be964cd656bd96"
+
+
+def _gemv_rx_source_sha256():
+    import hashlib
+    src = open(os.path.join(ROOT, "dual_autoregressive_tts_amd", "csrc", "gemv.hip")).read()
+    i = src.index("__global__ void __launch_bounds__(DUALAR_WG) gemv_rx_kernel(")
+    i = src.rindex("template", 0, i)
+    j = src.index("\n}\n", i) + 3
+    return hashlib.sha256(src[i:j].encode()).hexdigest()
+
+
+def roofline_traffic():
+    """Measured HBM bytes per launch of the roofline kernel, or None when
+    they are incomplete or were taken on other kernel text."""
+    c = ROOFLINE_COUNTERS
+    if c["write_kib"] is None or _gemv_rx_source_sha256() != ROOFLINE_KERNEL_SHA256:
+        return None
+    return round(c["fetch_kib"] * 1024 * c["fetch_scale"] + c["write_kib"] * 1024 * c["write_scale"])
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -319,7 +352,8 @@ def main():
                     "kernel": "gemv_rx_kernel<bf16, 2 rows/wave, gate+up, 5 units> (SwiGLU W1|W3 GEMV, "
                               "2 x 9728 x 2560 bf16)" if not m["weight_dtype"] == "f32" else "SwiGLU W1|W3 GEMV",
                     "achieved": round(sw_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(sw_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "frac": round(sw_gbps / HBM_PEAK_GBPS, 4),
+                    "traffic": roofline_traffic() if (B == 1 and m["weight_dtype"] == "bf16") else None,
                     "avg_launch_us": round(sw_avg_us, 3), "bytes_per_launch": round(sw_bytes),
                     "launches_profiled": f["launches"],
                     "gemv_family": {"achieved_GBps": round(gemv_gbps, 1), "avg_launch_us": round(gemv_avg_us, 3),

@@ -206,6 +206,13 @@ struct dualar_ctx {
 
 namespace {
 
+#ifndef MERGE_O_IT_FIRST
+#define MERGE_O_IT_FIRST 8   // loads per lane of the split form tried first (8 or 16)
+#endif
+#ifndef MERGE_O_FUSE
+#define MERGE_O_FUSE 1
+#endif
+
 dualar_status fail(dualar_ctx* c, dualar_status s, const std::string& m) {
   if (c) c->err = m; else g_create_err = m;
   return s;
@@ -217,7 +224,11 @@ dualar_status fail(dualar_ctx* c, dualar_status s, const std::string& m) {
 bool prof_on(dualar_ctx* c, int cls, bool swiglu = false) {
   return c->prof_cls == cls || (swiglu && c->prof_cls == DUALAR_K_GEMV_SWIGLU);
 }
+// The start event is recorded on the stream; a launcher of one kernel then
+// re-records both events at that kernel's own start and end (launch_timed),
+// otherwise prof_post records the stop event after the launches.
 hipError_t prof_pre(dualar_ctx* c, int cls, bool swiglu = false) {
+  g_launch_ev = LaunchEvents{nullptr, nullptr};   // never left armed by a failed launch
   if (!prof_on(c, cls, swiglu)) return hipSuccess;
   while (c->ev.size() < c->ev_used + 2) {
     hipEvent_t e;
@@ -225,11 +236,14 @@ hipError_t prof_pre(dualar_ctx* c, int cls, bool swiglu = false) {
     if (er != hipSuccess) return er;
     c->ev.push_back(e);
   }
+  g_launch_ev = LaunchEvents{c->ev[c->ev_used], c->ev[c->ev_used + 1]};
   return hipEventRecord(c->ev[c->ev_used], c->stream);
 }
 hipError_t prof_post(dualar_ctx* c, int cls, double bytes, bool swiglu = false) {
   if (!prof_on(c, cls, swiglu)) return hipSuccess;
-  hipError_t er = hipEventRecord(c->ev[c->ev_used + 1], c->stream);
+  const bool taken = g_launch_ev.start == nullptr;   // recorded by the kernel launch itself
+  g_launch_ev = LaunchEvents{nullptr, nullptr};
+  hipError_t er = taken ? hipSuccess : hipEventRecord(c->ev[c->ev_used + 1], c->stream);
   c->ev_used += 2;
   c->prof_launches += 1;
   c->prof_bytes += bytes;
@@ -376,6 +390,17 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   // with 2).  Otherwise the balanced flash-decoding form (it = 8): at batch 4
   // and 16k positions the split form needs 256 splits per head and a merge.
   a.it = (B <= 4 && Lmax <= 2048) ? 4 : 8;
+  // Batch 1, bf16 weights, the S2 head shape: the split form with at most
+  // merge_o_b1_max_splits() chunks of 128 or 256 positions, its merge done by
+  // the O product (each lane merges the eight values it multiplies).
+  int mo_chunk = 0;
+  if (MERGE_O_FUSE && B == 1 && pos_dev && sizeof(T) == 2 && attn_o_b1_fits(S.H, S.KV, S.hd, S.dim, 1)) {
+    for (int it : {MERGE_O_IT_FIRST, 24 - MERGE_O_IT_FIRST}) {
+      const int ch = attn_chunk((int)r.kvesz, S.hd, it);
+      if ((Lmax + ch - 1) / ch <= merge_o_b1_max_splits()) { a.it = it; mo_chunk = ch; break; }
+    }
+  }
+  a.no_merge = mo_chunk > 0;
   a.lmax = Lmax;
   a.part = (float*)(c->ws + L.part);
   a.counters = (unsigned*)(c->ws + L.counters);
@@ -389,6 +414,18 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     double pos_sum = pos_dev ? attn_positions(c, B) : (double)B * (pos_const + 1);
     HIPCHK(prof_post(c, DUALAR_K_ATTN, pos_sum * 2.0 * S.KV * S.hd * r.kvesz +
                                            4.0 * B * ((S.H + 2 * S.KV) * S.hd + S.H * S.hd)));
+  }
+  if (mo_chunk) {
+    // x += Wo . merge(partials)
+    MergeOParams mo{};
+    mo.part = a.part; mo.chunk = mo_chunk; mo.max_splits = (Lmax + mo_chunk - 1) / mo_chunk;
+    mo.att = att; mo.pos = pos_dev; mo.H = S.H; mo.hd = S.hd;
+    mo.wo = w.wo; mo.x = x; mo.dim = S.dim;
+    HIPCHK(prof_pre(c, DUALAR_K_GEMV));
+    HIPCHK(launch_merge_o_b1(mo, c->stream));
+    HIPCHK(prof_post(c, DUALAR_K_GEMV, (double)S.dim * S.H * S.hd * r.esz +
+                                           (double)mo.max_splits * S.H * (S.hd + 2) * 4.0));
+    o_done = true;
   }
   }
   // x += Wo . o

@@ -713,7 +713,7 @@ template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p0, 
   const int rep = p.H / p.KV;
   if constexpr (sizeof(KT) == 2) {
     // the balanced flash-decoding form: bf16 cache, head_dim 128, batched
-    if (p.hd == 128 && p.it >= 8 && p.q_planes && p.B <= FL_MAXB && (rep == 1 || rep == 2 || rep == 4)) {
+    if (!p.no_merge && p.hd == 128 && p.it >= 8 && p.q_planes && p.B <= FL_MAXB && (rep == 1 || rep == 2 || rep == 4)) {
       const int nt_max = (p.lmax + FL_TILE - 1) / FL_TILE;
       // upper bound of the units: every row at lmax
       const long long u_max = (long long)p.B * p.KV * nt_max;
@@ -750,11 +750,12 @@ template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p0, 
   else ATT_GO(IT, 8);
   if (p.it == 2) { ATT_REP(2) }
   else if (p.it == 4) { ATT_REP(4) }
+  else if (p.it == 16) { ATT_REP(16) }
   else { ATT_REP(8) }
 #undef ATT_REP
 #undef ATT_GO
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.max_splits == 1) return e;
+  if (e != hipSuccess || p.max_splits == 1 || p.no_merge) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(p.B, p.H), dim3(MERGE_T), 0, s, p);
   return hipGetLastError();
 }

@@ -249,6 +249,113 @@ bool attn_o_b1_fits(int H, int KV, int hd, int dim, int L) {
 hipError_t launch_attn_o_b1(const AttnOParams& p, hipStream_t s) {
   if (!attn_o_b1_fits(p.H, p.KV, p.hd, p.dim, p.pos + 1) || p.pos >= p.max_pos) return hipErrorInvalidValue;
   const int nwg = (p.dim + ATTN_O_ROWS - 1) / ATTN_O_ROWS;
-  hipLaunchKernelGGL((attn_o_b1_kernel<ATTN_O_ROWS>), dim3(nwg), dim3(WGT), 0, s, p);
+  launch_timed(attn_o_b1_kernel<ATTN_O_ROWS>, dim3(nwg), dim3(WGT), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Batch-1 merge of the split attention partials fused with the O product
+// (slow AR, split form): x += W_o . o with o_h = sum_s e^(m_s - M) o_s /
+// sum_s e^(m_s - M) l_s over the splits s of head h, M = max_s m_s.
+// The wide O layout puts KV head w's query heads 4w..4w+3 on wave w and
+// columns 8 (l % 16) .. +8 of head 4w + l / 16 on lane l, so every lane
+// merges exactly the eight values it multiplies, from at most MAXS splits
+// (loads issued before the weights).  With one split the split kernel has
+// written o itself and the lane reads it.
+template <int R, int MAXS>
+__global__ void __launch_bounds__(WGT) merge_o_b1_kernel(MergeOParams p) {
+  __shared__ float part[NW][R];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * R;
+  const int K = p.H * HD;
+  const int L = p.pos[0] + 1;
+  const int ns = (L + p.chunk - 1) / p.chunk;
+  const int h = wave * REP + (lane >> 4), d0 = (lane & 15) * 8;
+
+  // 1. partials (or o), residual, then the weights
+  float2 po[MAXS][4];
+  float pm[MAXS], pl[MAXS];
+  float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
+  if (ns == 1) {
+    const float* src = p.att + (size_t)h * HD + d0;
+    o0 = *(const float4*)src;
+    o1 = *(const float4*)(src + 4);
+  } else {
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+      if (s < ns) {
+        const float* q = p.part + ((size_t)h * p.max_splits + s) * (HD + 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) po[s][i] = *(const float2*)(q + d0 + 2 * i);
+        pm[s] = q[HD];
+        pl[s] = q[HD + 1];
+      }
+    }
+  }
+  const float xres = (threadIdx.x < R && row0 + (int)threadIdx.x < p.dim) ? p.x[row0 + threadIdx.x] : 0.f;
+  u32x4 w[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(row0 + r, p.dim - 1);
+    w[r] = ld_stream((const char*)p.wo + ((size_t)row * K + (size_t)wave * 512 + lane * 8) * sizeof(bf16_t));
+  }
+
+  // 2. merge, splits in order
+  float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+  if (ns > 1) {
+    float M = pm[0];
+#pragma unroll
+    for (int s = 1; s < MAXS; ++s)
+      if (s < ns) M = fmaxf(M, pm[s]);
+    float lsum = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+      if (s < ns) {
+        const float ws = expf(pm[s] - M);
+        lsum = fmaf(pl[s], ws, lsum);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(po[s][i].x, ws, acc[2 * i]);
+          acc[2 * i + 1] = fmaf(po[s][i].y, ws, acc[2 * i + 1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] = acc[e] / lsum;
+  }
+
+  // 3. dot products, the eight column blocks summed in order, residual
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float wf[8];
+    ElemT<bf16_t>::unpack(w[r], wf);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(wf[e], ov[e], acc);
+    acc = wave_sum(acc);
+    if (lane == 0) part[wave][r] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < R && row0 + (int)threadIdx.x < p.dim) {
+    const int r = threadIdx.x;
+    float v = part[0][r];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) v += part[q][r];
+    p.x[row0 + r] = xres + v;
+  }
+}
+
+#ifndef MERGE_O_MAXS
+#define MERGE_O_MAXS 10
+#endif
+
+int merge_o_b1_max_splits() { return MERGE_O_MAXS; }
+
+hipError_t launch_merge_o_b1(const MergeOParams& p, hipStream_t s) {
+  if (!attn_o_b1_fits(p.H, p.H / REP, p.hd, p.dim, 1) || p.max_splits > MERGE_O_MAXS || p.chunk <= 0)
+    return hipErrorInvalidValue;
+  const int nwg = (p.dim + ATTN_O_ROWS - 1) / ATTN_O_ROWS;
+  launch_timed(merge_o_b1_kernel<ATTN_O_ROWS, MERGE_O_MAXS>, dim3(nwg), dim3(WGT), 0, s, p);
   return hipGetLastError();
 }

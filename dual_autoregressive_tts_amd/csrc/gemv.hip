@@ -19,6 +19,8 @@
 #include "common.h"
 #include "internal.h"
 
+thread_local LaunchEvents g_launch_ev{nullptr, nullptr};
+
 template <typename T> __device__ __forceinline__ const char* seg_row(const GemvParams& p, int row, int s) {
   // SwiGLU: s selects gate (w[0]) or up (w[1]) at the same row.
   if (p.mode == GEMV_SWIGLU) return (const char*)p.w[s] + (size_t)row * p.K * sizeof(T);
@@ -571,24 +573,24 @@ static hipError_t go(const GemvParams& p, hipStream_t s) {
   dim3 grid((p.n_out + 4 * RPW - 1) / (4 * RPW), (p.B + BT - 1) / BT);
   const size_t lds = (size_t)BT * p.K * sizeof(float);
   if constexpr (NU > 0 && BT == 1)
-    hipLaunchKernelGGL((gemv_rx_kernel<T, RPW, NR, NU>), grid, dim3(DUALAR_WG), 0, s, p);
+    launch_timed(gemv_rx_kernel<T, RPW, NR, NU>, grid, dim3(DUALAR_WG), 0, s, p);
   else if constexpr (NU > 0)
-    hipLaunchKernelGGL((gemv_unrolled_kernel<T, BT, RPW, NR, NU>), grid, dim3(DUALAR_WG), lds, s, p);
+    launch_timed(gemv_unrolled_kernel<T, BT, RPW, NR, NU>, grid, dim3(DUALAR_WG), (uint32_t)lds, s, p);
   else
-    hipLaunchKernelGGL((gemv_loop_kernel<T, BT, RPW, NR>), grid, dim3(DUALAR_WG), lds, s, p);
+    launch_timed(gemv_loop_kernel<T, BT, RPW, NR>, grid, dim3(DUALAR_WG), (uint32_t)lds, s, p);
   return hipGetLastError();
 }
 
 template <typename T, int RPW, int NR, int NU, int KS>
 static hipError_t go_ks(const GemvParams& p, hipStream_t s) {
   dim3 grid((p.n_out + (4 / KS) * RPW - 1) / ((4 / KS) * RPW));
-  hipLaunchKernelGGL((gemv_ks_kernel<T, RPW, NR, NU, KS>), grid, dim3(DUALAR_WG), 0, s, p);
+  launch_timed(gemv_ks_kernel<T, RPW, NR, NU, KS>, grid, dim3(DUALAR_WG), 0, s, p);
   return hipGetLastError();
 }
 
 template <int NW, int R, int NR, int U>
 static hipError_t go_wide(const GemvParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_wide_kernel<NW, R, NR, U>), dim3((p.n_out + R - 1) / R), dim3(NW * 64), 0, s, p);
+  launch_timed(gemv_wide_kernel<NW, R, NR, U>, dim3((p.n_out + R - 1) / R), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -1,7 +1,25 @@
 // Internal launch interface between the C-ABI layer and the kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
+
+// Kernel-timing events for the next single-kernel launch (profiling only).
+// When set, the launch hands them to hipExtLaunchKernel, which records them
+// at the kernel's own start and end (no marker packets around it), and
+// clears them; launchers of several kernels leave them untouched.
+struct LaunchEvents { hipEvent_t start, stop; };
+extern thread_local LaunchEvents g_launch_ev;
+
+template <typename K, typename... A>
+inline void launch_timed(K kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, A... args) {
+  if (g_launch_ev.start) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, g_launch_ev.start, g_launch_ev.stop, 0u, args...);
+    g_launch_ev = LaunchEvents{nullptr, nullptr};
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
+}
 
 enum GemvMode { GEMV_STORE = 0, GEMV_ADD = 1, GEMV_SWIGLU = 2 };
 
@@ -87,6 +105,7 @@ struct AttnParams {
   uint16_t* out_planes;               // if set: o as planes [3][B][H*hd] instead of out
   uint16_t* q_planes;                 // scratch [3][B][H*hd] (flash-decoding form)
   int prepped;                        // q_planes and the appended k/v are already written
+  int no_merge;                       // split form: leave the partials for a fused merge
   int B;
 };
 
@@ -105,6 +124,21 @@ struct AttnOParams {
 };
 bool attn_o_b1_fits(int H, int KV, int hd, int dim, int L);
 hipError_t launch_attn_o_b1(const AttnOParams& p, hipStream_t s);
+
+// Batch-1 merge of the split attention partials (AttnParams::part of the
+// split form, run with no_merge) fused with the O product and its residual.
+// Same head shape as attn_o_b1 (H = 32, KV = 8, hd = 128, bf16 weights).
+struct MergeOParams {
+  const float* part; int max_splits, chunk;   // [H][max_splits][hd + 2] (o, m, l); the split form's chunk
+  const float* att;                   // o when the context fits one chunk
+  const int* pos;                     // device [1]: the row's position (context pos + 1)
+  int H, hd;
+  const void* wo;                     // [dim][H*hd] bf16
+  float* x; int dim;                  // residual row, updated in place
+};
+int merge_o_b1_max_splits();
+hipError_t launch_merge_o_b1(const MergeOParams& p, hipStream_t s);
+int attn_chunk(int kv_esz, int hd, int it);
 
 // Prefill of a chunk of positions: rows r = b*C + i hold position pos[r] of
 // sequence b (-1 = padding).  prefill_append_kernel applies QK-norm and RoPE

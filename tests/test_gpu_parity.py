@@ -322,6 +322,25 @@ def test_bf16_small_batch_long_context():
         assert sum(c) >= 3 * len(plen)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("plen,kv", [(600, "bf16"), (1100, "bf16"), (1500, "bf16"), (300, "f32")])
+def test_batch1_s2_heads_merged_in_o_product(plen, kv):
+    # batch 1 with the S2 head shape (32 query / 8 KV heads of 128): the slow
+    # attention runs in chunks (128 positions at 600 and 1,100: 5 and 9
+    # splits; 256 at 1,500 so that at most 10 splits remain; 64 with an fp32
+    # cache) and the O product merges each head's partials itself; the fast
+    # layers attend inside the O product.  Dim 512 keeps the oracle's replay
+    # short.
+    m = synth.model("tiny", weight_dtype="bf16", kv_dtype=kv, dim=512, ffn_dim=1024, fast_dim=512,
+                    fast_ffn_dim=1024, n_head=32, n_kv_head=8, head_dim=128, fast_n_head=32,
+                    fast_n_kv_head=8, fast_head_dim=128)
+    w = synth.make_weights(m, seed=8)
+    P = synth.make_prompts(m, ("ragged", 1, 1), np.array([plen], dtype=np.int32), seed=8)
+    c, worst = run_and_compare(m, w, P, np.array([plen], dtype=np.int32), 3, dict(greedy=1),
+                               tag=f"b1-merge-o-{plen}-{kv}", floor=(kv == "bf16"))
+    assert sum(c) >= 3
+
+
 def test_end_token_stops_and_pads(tiny):
     m, w = tiny
     w = {k: v.copy() for k, v in w.items()}
