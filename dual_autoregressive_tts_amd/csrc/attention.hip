@@ -727,7 +727,9 @@ template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p0, 
         case 2: hipLaunchKernelGGL((attn_flash_kernel<2>), dim3(ng), dim3(DUALAR_WG), 0, s, p, ng); break;
         default: hipLaunchKernelGGL((attn_flash_kernel<4>), dim3(ng), dim3(DUALAR_WG), 0, s, p, ng); break;
       }
-      hipLaunchKernelGGL(attn_flash_merge_kernel, dim3(p.B, p.H), dim3(128), 0, s, p, ng);
+      // with every context inside one tile (the fast AR's depth cache) each
+      // head is one unit in one workgroup, which writes o itself: no merge
+      if (nt_max > 1) hipLaunchKernelGGL(attn_flash_merge_kernel, dim3(p.B, p.H), dim3(128), 0, s, p, ng);
       return hipGetLastError();
     }
   }
