@@ -212,6 +212,9 @@ namespace {
 #ifndef MERGE_O_FUSE
 #define MERGE_O_FUSE 1
 #endif
+#ifndef ATTN_SPLIT8
+#define ATTN_SPLIT8 1
+#endif
 
 dualar_status fail(dualar_ctx* c, dualar_status s, const std::string& m) {
   if (c) c->err = m; else g_create_err = m;
@@ -408,7 +411,15 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.q_planes = (uint16_t*)(c->ws + L.qbuf);   // the prefill q buffer is free while decoding
   a.prepped = prepped;
   HIPCHK(prof_pre(c, DUALAR_K_ATTN));
-  HIPCHK((launch_attn<T, KT>(a, c->stream)));
+  bool split8 = false;
+  if (ATTN_SPLIT8 && mo_chunk && sizeof(KT) == 2) {
+    // batch 1, bf16 cache: the 8-wave split kernel (same partial layout)
+    AttnParams b = a;
+    b.chunk = mo_chunk; b.max_splits = (Lmax + mo_chunk - 1) / mo_chunk;
+    split8 = launch_attn_split_b1(b, c->stream);
+    if (split8) HIPCHK(hipGetLastError());
+  }
+  if (!split8) HIPCHK((launch_attn<T, KT>(a, c->stream)));
   if (c->prof_cls == DUALAR_K_ATTN) {
     // cache bytes: every attended position of every row, K and V, plus the append
     double pos_sum = pos_dev ? attn_positions(c, B) : (double)B * (pos_const + 1);

@@ -359,3 +359,214 @@ hipError_t launch_merge_o_b1(const MergeOParams& p, hipStream_t s) {
   launch_timed(merge_o_b1_kernel<ATTN_O_ROWS, MERGE_O_MAXS>, dim3(nwg), dim3(WGT), 0, s, p);
   return hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// Batch-1 split attention over the slow cache (bf16, S2 head shape), for the
+// merge inside the O product: workgroup (split, g) takes 8 * NPW consecutive
+// positions of KV head g and its 4 query heads, one wave per NPW positions.
+// Waves 0-3 prepare one query head each (QK-norm, RoPE, score scale, three
+// bf16 terms), the workgroup holding the new position appends k and v; then
+// every wave scores its positions on the matrix cores, takes a wave-local
+// softmax (max m_w, sum l_w) and its unnormalised P.V in registers, and the
+// eight waves' (m_w, l_w, o_w) are combined once in LDS into the split's
+// (o, m, l) -- or o / l when the context is one split.  Same partial layout
+// and arithmetic steps as the other decode attention kernels.
+template <int NPW>
+__global__ void __launch_bounds__(WGT) attn_split_b1_kernel(AttnParams p) {
+  constexpr int GW = NPW / 16;                 // 16-position score groups per wave
+  constexpr int CH = NW * NPW;                 // positions per split
+  __shared__ __attribute__((aligned(16))) uint16_t qp[3][REP][HD];
+  __shared__ __attribute__((aligned(16))) float kn[HD];
+  __shared__ float vn[HD];
+  __shared__ __attribute__((aligned(16))) float pe[NW][REP][NPW];
+  __shared__ float mw[NW][REP], lw[NW][REP];
+  __shared__ __attribute__((aligned(16))) float ow[NW][REP][HD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int split = blockIdx.x, g = blockIdx.y;
+  const int pos = p.pos ? p.pos[0] : p.pos_const;
+  const int L = pos + 1;
+  const int n_splits = (L + CH - 1) / CH;
+  if (split >= n_splits) return;
+  const int c0 = split * CH, c1 = min(c0 + CH, L);
+  const int w0 = c0 + wave * NPW;              // the wave's first position
+  const bool has_new = pos >= c0 && pos < c1;
+  const size_t head_base = (size_t)g * p.max_pos;
+  const char* kbase = (const char*)p.kcache + head_base * HD * sizeof(bf16_t);
+  const uint32_t* vbase = (const uint32_t*)((const char*)p.vcache + head_base * HD * sizeof(bf16_t));
+
+  // ---- 1. loads: K (score operand), V (dim layout), q / new k, v, gains, RoPE ----
+  const int jm = lane & 15, kq = lane >> 4;
+  u32x4 kc[GW][4];
+#pragma unroll
+  for (int mm = 0; mm < GW; ++mm) {
+    const int j = w0 + 16 * mm + jm;
+    const int jl = (j < c1 && j != pos) ? j : 0;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kc[mm][ks] = ld_vec(kbase + ((size_t)jl * HD + 32 * ks + 8 * kq) * sizeof(bf16_t));
+  }
+  uint32_t vc[NPW];
+#pragma unroll
+  for (int jj = 0; jj < NPW; ++jj) {
+    const int j = w0 + jj;
+    vc[jj] = 0u;
+    if (j < c1 && j != pos) vc[jj] = vbase[(size_t)j * (HD / 2) + lane];
+  }
+  const float* row = p.qkv;
+  float2 qv = make_float2(0.f, 0.f), kv2 = qv, vv2 = qv;
+  if (wave < REP) qv = *(const float2*)(row + (size_t)(g * REP + wave) * HD + 2 * lane);
+  if (has_new && wave == REP) {
+    kv2 = *(const float2*)(row + (size_t)p.H * HD + (size_t)g * HD + 2 * lane);
+    vv2 = *(const float2*)(row + (size_t)(p.H + p.KV) * HD + (size_t)g * HD + 2 * lane);
+  }
+  uint32_t qg = 0x3f803f80u, kg = 0x3f803f80u;   // bf16 pair (1, 1)
+  if (p.q_norm) qg = ((const uint32_t*)p.q_norm)[lane];
+  if (p.k_norm) kg = ((const uint32_t*)p.k_norm)[lane];
+  const float2 cs = p.rope[(size_t)pos * (HD / 2) + lane];
+
+  // ---- 2. q (waves 0-3) and the new k, v (wave 4 of the split holding pos) ----
+  if (wave < REP) {
+    float a = qv.x, c = qv.y;
+    if (p.q_norm) {
+      const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)HD + p.eps);
+      a = a * inv * bf16_bits_to_f32(qg & 0xffffu);
+      c = c * inv * bf16_bits_to_f32(qg >> 16);
+    }
+    const float qscale = 1.0f / sqrtf((float)HD);
+    const float ra = (a * cs.x - c * cs.y) * qscale, rc = (a * cs.y + c * cs.x) * qscale;
+    const uint16_t a0 = f32_to_bf16_rne(ra), c0b = f32_to_bf16_rne(rc);
+    const float a1f = ra - bf16_bits_to_f32(a0), c1f = rc - bf16_bits_to_f32(c0b);
+    const uint16_t a1 = f32_to_bf16_rne(a1f), c1b = f32_to_bf16_rne(c1f);
+    const uint16_t a2 = f32_to_bf16_rne(a1f - bf16_bits_to_f32(a1));
+    const uint16_t c2 = f32_to_bf16_rne(c1f - bf16_bits_to_f32(c1b));
+    *(uint32_t*)&qp[0][wave][2 * lane] = (uint32_t)a0 | ((uint32_t)c0b << 16);
+    *(uint32_t*)&qp[1][wave][2 * lane] = (uint32_t)a1 | ((uint32_t)c1b << 16);
+    *(uint32_t*)&qp[2][wave][2 * lane] = (uint32_t)a2 | ((uint32_t)c2 << 16);
+  } else if (has_new && wave == REP) {
+    float a = kv2.x, c = kv2.y;
+    if (p.k_norm) {
+      const float inv = 1.0f / sqrtf(wave_sum(a * a + c * c) / (float)HD + p.eps);
+      a = a * inv * bf16_bits_to_f32(kg & 0xffffu);
+      c = c * inv * bf16_bits_to_f32(kg >> 16);
+    }
+    const uint16_t ka = f32_to_bf16_rne(a * cs.x - c * cs.y);
+    const uint16_t kb = f32_to_bf16_rne(a * cs.y + c * cs.x);
+    const uint16_t va = f32_to_bf16_rne(vv2.x), vb = f32_to_bf16_rne(vv2.y);
+    kn[2 * lane] = bf16_bits_to_f32(ka);
+    kn[2 * lane + 1] = bf16_bits_to_f32(kb);
+    vn[2 * lane] = bf16_bits_to_f32(va);
+    vn[2 * lane + 1] = bf16_bits_to_f32(vb);
+    const size_t at = (head_base + pos) * HD + 2 * lane;
+    *(uint32_t*)((char*)p.kcache + at * sizeof(bf16_t)) = (uint32_t)ka | ((uint32_t)kb << 16);
+    *(uint32_t*)((char*)p.vcache + at * sizeof(bf16_t)) = (uint32_t)va | ((uint32_t)vb << 16);
+  }
+  __syncthreads();
+
+  // ---- 3. scores on the matrix cores, column n = query head n % 4 ----
+  // lane l gets S[position 4 (l / 16) + r of group mm][head (l % 16) % 4]
+  float sv[GW][4];
+#pragma unroll
+  for (int mm = 0; mm < GW; ++mm) {
+    att_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      att_bf16x8 a = __builtin_bit_cast(att_bf16x8, kc[mm][ks]);
+      if (w0 + 16 * mm + jm == pos) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (__bf16)kn[32 * ks + 8 * kq + e];
+      }
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const u32x4 b = *(const u32x4*)&qp[t][jm & 3][32 * ks + 8 * kq];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(att_bf16x8, b), acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[mm][r] = (w0 + 16 * mm + 4 * kq + r < c1) ? acc[r] : -INFINITY;
+  }
+
+  // ---- 4. wave-local softmax over the wave's positions (per head column) ----
+  float m = -INFINITY;
+#pragma unroll
+  for (int mm = 0; mm < GW; ++mm)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = fmaxf(m, sv[mm][r]);
+  m = max_xor16(m);
+  m = max_xor32(m);
+  float ls = 0.f;
+#pragma unroll
+  for (int mm = 0; mm < GW; ++mm)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = sv[mm][r] == -INFINITY ? 0.f : expf(sv[mm][r] - m);
+      sv[mm][r] = e;
+      ls += e;
+    }
+  ls = add_xor16(ls);
+  ls = add_xor32(ls);
+  if (jm < REP) {
+#pragma unroll
+    for (int mm = 0; mm < GW; ++mm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pe[wave][jm][16 * mm + 4 * kq + r] = sv[mm][r];
+    if (kq == 0) { mw[wave][jm] = m; lw[wave][jm] = ls; }
+  }
+  __syncthreads();
+
+  // ---- 5. the wave's unnormalised P.V (lane: dims 2l, 2l+1 of the 4 heads) ----
+  float o[REP][2];
+#pragma unroll
+  for (int h = 0; h < REP; ++h) o[h][0] = o[h][1] = 0.f;
+#pragma unroll
+  for (int q4 = 0; q4 < NPW / 4; ++q4) {
+    float4 pv[REP];
+#pragma unroll
+    for (int h = 0; h < REP; ++h) pv[h] = *(const float4*)&pe[wave][h][4 * q4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int jj = 4 * q4 + r;
+      float va = bf16_bits_to_f32(vc[jj] & 0xffffu), vb = bf16_bits_to_f32(vc[jj] >> 16);
+      if (w0 + jj == pos) { va = vn[2 * lane]; vb = vn[2 * lane + 1]; }
+#pragma unroll
+      for (int h = 0; h < REP; ++h) {
+        const float pj = r == 0 ? pv[h].x : r == 1 ? pv[h].y : r == 2 ? pv[h].z : pv[h].w;
+        o[h][0] = fmaf(pj, va, o[h][0]);
+        o[h][1] = fmaf(pj, vb, o[h][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < REP; ++h) *(float2*)&ow[wave][h][2 * lane] = make_float2(o[h][0], o[h][1]);
+  __syncthreads();
+
+  // ---- 6. combine the waves (thread t: head t / 128, dim t % 128), waves in order ----
+  {
+    const int h = threadIdx.x >> 7, d = threadIdx.x & 127;
+    float M = mw[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, mw[w][h]);
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = mw[w][h] == -INFINITY ? 0.f : expf(mw[w][h] - M);
+      acc = fmaf(f, ow[w][h][d], acc);
+      lsum = fmaf(f, lw[w][h], lsum);
+    }
+    const int hh = g * REP + h;
+    if (n_splits == 1) {
+      p.out[(size_t)hh * HD + d] = acc / lsum;
+    } else {
+      float* pp = p.part + ((size_t)hh * p.max_splits + split) * (HD + 2);
+      pp[d] = acc;
+      if (d == 0) { pp[HD] = M; pp[HD + 1] = lsum; }
+    }
+  }
+}
+
+// chunk = 8 waves x 16 or 32 positions; returns false for other chunks
+bool launch_attn_split_b1(const AttnParams& p, hipStream_t s) {
+  if (p.B != 1 || p.H != NW * REP || p.KV != NW || p.hd != HD || p.max_splits < 1) return false;
+  if (p.chunk == NW * 16) hipLaunchKernelGGL(attn_split_b1_kernel<16>, dim3(p.max_splits, p.KV), dim3(WGT), 0, s, p);
+  else if (p.chunk == NW * 32) hipLaunchKernelGGL(attn_split_b1_kernel<32>, dim3(p.max_splits, p.KV), dim3(WGT), 0, s, p);
+  else return false;
+  return true;
+}

@@ -137,6 +137,9 @@ struct MergeOParams {
   float* x; int dim;                  // residual row, updated in place
 };
 int merge_o_b1_max_splits();
+// batch-1 split attention (bf16 cache, S2 head shape) for chunks of 128 or 256
+// positions, writing the split form's partials; false if the shape does not fit
+bool launch_attn_split_b1(const AttnParams& p, hipStream_t s);
 hipError_t launch_merge_o_b1(const MergeOParams& p, hipStream_t s);
 int attn_chunk(int kv_esz, int hd, int it);
 
