@@ -136,12 +136,15 @@ __global__ void __launch_bounds__(WGT) attn_o_b1_kernel(AttnOParams p) {
       *(uint32_t*)((char*)p.vcache + at * sizeof(bf16_t)) = (uint32_t)va | ((uint32_t)vb << 16);
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();   // qp[wave], kn[wave]: this wave's own
 
-  // ---- 4. scores on the matrix cores: S^T = K . q^T ----
+  // ---- 4. scores on the matrix cores: S^T = K . q^T, softmax in registers ----
   // A = 16 positions x 32 dims of K (bf16, exact), B = 32 dims x 16 columns
   // (column n: query head n % 4, one bf16 term of q per product, the three
-  // accumulated); lane l gets S[4 (l / 16) + r][l % 16].
+  // accumulated); lane l gets S[4 (l / 16) + r][l % 16].  The four lanes of
+  // a column (l / 16 = 0..3) hold its 16 positions: max and sum across them
+  // by the row / half swaps.  All LDS data from here to the product input is
+  // the wave's own: wave-level barriers only.
   {
     att_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -157,29 +160,29 @@ __global__ void __launch_bounds__(WGT) attn_o_b1_kernel(AttnOParams p) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(att_bf16x8, b), acc, 0, 0, 0);
       }
     }
+    float sv[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = 4 * kq + r < L ? acc[r] : -INFINITY;
+      m = fmaxf(m, sv[r]);
+    }
+    m = max_xor16(m);
+    m = max_xor32(m);
+    float l = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = 4 * kq + r < L ? expf(sv[r] - m) : 0.f;
+      l += sv[r];
+    }
+    l = add_xor16(l);
+    l = add_xor32(l);
     if (jm < REP) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int jj = 4 * kq + r;
-        if (jj < L) sc[wave][jm][jj] = acc[r];
-      }
+      for (int r = 0; r < 4; ++r) sc[wave][jm][4 * kq + r] = sv[r] / l;
     }
   }
-  __syncthreads();
-
-  // ---- 5. softmax: lane (head l / 16, position l % 16) ----
-  {
-    const int h4 = lane >> 4, jj = lane & 15;
-    const float s = jj < L ? sc[wave][h4][jj] : -INFINITY;
-    float m = fmaxf(s, xor1_of(s));
-    m = fmaxf(m, xor2_of(m));
-    m = fmaxf(m, mir8_of(m));
-    m = fmaxf(m, mir16_of(m));
-    const float e = jj < L ? expf(s - m) : 0.f;
-    const float l = group_sum(e, 16);
-    sc[wave][h4][jj] = e / l;
-  }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
 
   // ---- 6. P.V in the dim layout, then the wave's eighth of the product input ----
   float pr[REP][MAXL];
@@ -208,7 +211,7 @@ __global__ void __launch_bounds__(WGT) attn_o_b1_kernel(AttnOParams p) {
   }
 #pragma unroll
   for (int h4 = 0; h4 < REP; ++h4) *(float2*)&os[wave][h4 * HD + 2 * lane] = make_float2(o[h4][0], o[h4][1]);
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();   // os[wave]: this wave's own
   float ov[8];
   {
     const float4 t0 = *(const float4*)&os[wave][lane * 8];
