@@ -597,6 +597,12 @@ static hipError_t go_wide(const GemvParams& p, hipStream_t s) {
 #ifndef GEMV_WIDE
 #define GEMV_WIDE 1
 #endif
+#ifndef B1_QKV_RPW
+#define B1_QKV_RPW 3
+#endif
+#ifndef B1_W13_RPW
+#define B1_W13_RPW 2
+#endif
 #ifndef WIDE_O_R
 #define WIDE_O_R 10
 #endif
@@ -623,7 +629,9 @@ static bool pick_b1(const GemvParams& p, hipStream_t s, hipError_t* e) {
     const int units = p.K / (64 * ElemT<T>::EPV);
     if (units == 5) {
       if (NR == 1 && p.n_out >= 65536) *e = go<T, 1, 4, NR, 5>(p, s);  // tied head
-      else *e = go<T, 1, 2, NR, 5>(p, s);                               // QKV, W1|W3, fast head
+      else if (NR == 2) *e = go<T, 1, B1_W13_RPW, NR, 5>(p, s);         // W1|W3
+      else if (p.n_out == 6144) *e = go<T, 1, B1_QKV_RPW, NR, 5>(p, s);  // QKV
+      else *e = go<T, 1, 2, NR, 5>(p, s);                               // fast head, K|V rows
       return true;
     }
     if constexpr (NR == 1) {
