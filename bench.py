@@ -348,9 +348,17 @@ def main():
             f"{100 * gemv_share:.1f}% of step time")
         log(f"[bench] SwiGLU gate|up GEMV: {f['launches']} launches, avg {sw_avg_us:.2f} us, "
             f"{sw_bytes / 1e6:.2f} MB/launch, {sw_gbps:.0f} GB/s")
+        if m["weight_dtype"] == "f32":
+            kname = "SwiGLU W1|W3 GEMV"
+        elif B == 1:
+            kname = ("gemv_rx_kernel<bf16, 2 rows/wave, gate+up, 5 units> (SwiGLU W1|W3 GEMV, "
+                     "2 x 9728 x 2560 bf16)")
+        else:
+            kname = ("mfma_skw_kernel<2, 4, 1, 3, 3> + sk_finish_kernel<2, 4, 1> (SwiGLU W1|W3 stream-K "
+                     "matrix-core product and its finish, 2 x 9728 x 2560 bf16, %d activation rows; "
+                     "timed together)" % B)
         roofline = {"bound": "hbm",
-                    "kernel": "gemv_rx_kernel<bf16, 2 rows/wave, gate+up, 5 units> (SwiGLU W1|W3 GEMV, "
-                              "2 x 9728 x 2560 bf16)" if not m["weight_dtype"] == "f32" else "SwiGLU W1|W3 GEMV",
+                    "kernel": kname,
                     "achieved": round(sw_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(sw_gbps / HBM_PEAK_GBPS, 4),
                     "traffic": roofline_traffic() if (B == 1 and m["weight_dtype"] == "bf16") else None,
