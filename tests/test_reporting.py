@@ -81,3 +81,26 @@ def test_fast_tf_flops_s2():
     per_row = f["linear"] / (2 * f["rows"])
     assert abs(per_row / 1e6 - gold["fast_pass_weights_M"]["value"]) < 0.05
     assert f["attention"] == 4 * 128 * 32 * 4 * 819 * 55
+
+
+def test_roofline_traffic_follows_the_measured_kernel(monkeypatch):
+    # bench.py reports the HBM counters' bytes per launch of the roofline
+    # kernel only while gemv_rx_kernel's source is the text they were taken on
+    import bench
+    t = bench.roofline_traffic()
+    assert t is not None
+    algo = 2 * 9728 * 2560 * 2 + 4 * 2560 + 4 * 9728          # weights + x + out of one launch
+    assert algo <= t <= 1.01 * algo                           # read once: within 1 % of the algorithmic bytes
+    src = open(os.path.join(bench.ROOT, "dual_autoregressive_tts_amd", "csrc", "gemv.hip")).read()
+    changed = src.replace("// 4. dot products", "// 4. dot products (edited)", 1)
+    assert changed != src
+    real_open = open
+
+    def fake_open(path, *a, **k):
+        if str(path).endswith(os.path.join("csrc", "gemv.hip")):
+            import io
+            return io.StringIO(changed)
+        return real_open(path, *a, **k)
+
+    monkeypatch.setattr("builtins.open", fake_open)
+    assert bench.roofline_traffic() is None
