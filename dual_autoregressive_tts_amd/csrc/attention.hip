@@ -706,13 +706,127 @@ int attn_chunk(int kv_esz, int hd, int it) {
   return 4 * (64 / lpp) * it;
 }
 
+#ifndef ATTN_DEPTH
+#define ATTN_DEPTH 1
+#endif
 #define FL_SLOTS 512   // workgroups of the balanced flash-decoding form (two per compute unit)
+
+// Batched attention over a short cache (at most 16 positions: the fast AR's
+// depth cache), bf16 cache, head_dim 128, 4 query heads per KV head, after
+// the QKV finish (or attn_prep_kernel) has written q as three bf16 terms and
+// appended k, v.  One wave per (row, KV head): K rows and the q terms go
+// straight into the matrix-core operands (positions as A, query heads as B),
+// softmax in registers across the four lane groups of a column, then P.V in
+// the dim layout (lane l: dims 2l, 2l+1 of the 4 heads) with the output
+// written as three bf16 planes (or fp32).  Same arithmetic steps as the
+// other decode attention kernels.
+__global__ void __launch_bounds__(64) attn_depth_kernel(AttnParams p) {
+  constexpr int HD = 128, REP = 4, MAXL = 16;
+  __shared__ __attribute__((aligned(16))) float pe[REP][MAXL];
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / p.KV, g = blockIdx.x % p.KV;
+  const int pos = p.pos ? p.pos[b] : p.pos_const;
+  if (pos < 0) return;                        // inactive row
+  const int L = pos + 1;
+  const int jm = lane & 15, kq = lane >> 4;
+  const size_t head_base = ((size_t)b * p.KV + g) * p.max_pos;
+  const char* kbase = (const char*)p.kcache + head_base * HD * sizeof(bf16_t);
+  const uint32_t* vbase = (const uint32_t*)((const char*)p.vcache + head_base * HD * sizeof(bf16_t));
+  // operands: K (A, positions past the context read position 0 and are
+  // masked), the q terms (B, column n = query head n % 4), V (dim layout)
+  u32x4 ka[4], qb[3][4];
+  {
+    const int jl = jm < L ? jm : 0;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ka[ks] = ld_vec(kbase + ((size_t)jl * HD + 32 * ks + 8 * kq) * sizeof(bf16_t));
+    const size_t plane = (size_t)p.B * p.H * HD;
+    const uint16_t* qsrc = p.q_planes + ((size_t)b * p.H + g * REP + (jm & 3)) * HD + 8 * kq;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qb[t][ks] = ld_vec(qsrc + t * plane + 32 * ks);
+  }
+  uint32_t vc[MAXL];
+#pragma unroll
+  for (int jj = 0; jj < MAXL; ++jj) {
+    vc[jj] = 0u;
+    if (jj < L) vc[jj] = vbase[(size_t)jj * (HD / 2) + lane];
+  }
+  att_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(att_bf16x8, ka[ks]),
+                                                    __builtin_bit_cast(att_bf16x8, qb[t][ks]), acc, 0, 0, 0);
+  // lane l holds S[position 4 (l / 16) + r][head (l % 16) % 4]
+  float sv[4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sv[r] = 4 * kq + r < L ? acc[r] : -INFINITY;
+    m = fmaxf(m, sv[r]);
+  }
+  m = max_xor32(max_xor16(m));
+  float l = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sv[r] = 4 * kq + r < L ? expf(sv[r] - m) : 0.f;
+    l += sv[r];
+  }
+  l = add_xor32(add_xor16(l));
+  if (jm < REP) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pe[jm][4 * kq + r] = sv[r] / l;
+  }
+  __builtin_amdgcn_wave_barrier();
+  float o[REP][2];
+#pragma unroll
+  for (int h = 0; h < REP; ++h) o[h][0] = o[h][1] = 0.f;
+#pragma unroll
+  for (int q4 = 0; q4 < MAXL / 4; ++q4) {
+    if (4 * q4 < L) {
+      float4 pv[REP];
+#pragma unroll
+      for (int h = 0; h < REP; ++h) pv[h] = *(const float4*)&pe[h][4 * q4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jj = 4 * q4 + r;
+        const float va = bf16_bits_to_f32(vc[jj] & 0xffffu), vb = bf16_bits_to_f32(vc[jj] >> 16);
+#pragma unroll
+        for (int h = 0; h < REP; ++h) {
+          const float pj = r == 0 ? pv[h].x : r == 1 ? pv[h].y : r == 2 ? pv[h].z : pv[h].w;
+          o[h][0] = fmaf(pj, va, o[h][0]);
+          o[h][1] = fmaf(pj, vb, o[h][1]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < REP; ++h) {
+    const size_t col = (size_t)(g * REP + h) * HD + 2 * lane;
+    if (p.out_planes) {
+      const size_t plane = (size_t)p.B * p.H * HD, at = (size_t)b * p.H * HD + col;
+      store_planes(p.out_planes, plane, at, o[h][0]);
+      store_planes(p.out_planes, plane, at + 1, o[h][1]);
+    } else {
+      p.out[(size_t)b * p.ld_out + col] = o[h][0];
+      p.out[(size_t)b * p.ld_out + col + 1] = o[h][1];
+    }
+  }
+}
 
 template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p0, hipStream_t s) {
   AttnParams p = p0;
   const int rep = p.H / p.KV;
   if constexpr (sizeof(KT) == 2) {
     // the balanced flash-decoding form: bf16 cache, head_dim 128, batched
+    // contexts of at most 16 positions (the depth cache): one wave per (row, KV head)
+    if (!p.no_merge && p.hd == 128 && p.it >= 8 && p.q_planes && rep == 4 && p.lmax <= 16 && ATTN_DEPTH) {
+      if (!p.prepped) hipLaunchKernelGGL((attn_prep_kernel<T, KT>), dim3(p.B, p.H + p.KV), dim3(64), 0, s, p);
+      hipLaunchKernelGGL(attn_depth_kernel, dim3(p.B * p.KV), dim3(64), 0, s, p);
+      return hipGetLastError();
+    }
     if (!p.no_merge && p.hd == 128 && p.it >= 8 && p.q_planes && p.B <= FL_MAXB && (rep == 1 || rep == 2 || rep == 4)) {
       const int nt_max = (p.lmax + FL_TILE - 1) / FL_TILE;
       // upper bound of the units: every row at lmax
