@@ -9,6 +9,7 @@ from .dualar_oracle import (  # noqa: F401
     Sampling,
     bf16_round,
     count_params,
+    dequant_w4,
     param_shapes,
     rope_table,
     sample_token,

@@ -132,6 +132,40 @@ def bf16_round(x) -> np.ndarray:
     return np.ldexp(np.round(m * 256.0), e - 8)   # np.round: half to even
 
 
+def dequant_w4(weights: dict, group: int = 128) -> dict:
+    """The weights of a W4A16 model as the method uses them: every
+    `name.q4` (packed 4-bit values, [rows, K/2] bytes) with its `name.s4`
+    (one scale per row and group of `group` consecutive inputs) becomes the
+    matrix `name` = q * scale in float64.
+
+    [P3] (the W4A16 "late12attn" S2 model card) names the variant but prints
+    no format; the format read here (the same one the synthetic W4A16 model
+    is written in) is: byte j of a row holds input 2j in its low nibble and
+    2j+1 in its high nibble, each a two's-complement integer in [-8, 7].
+    Parity unpinned against any real quantised checkpoint."""
+    out = {}
+    for k, v in weights.items():
+        if k.endswith(".s4"):
+            continue
+        if not k.endswith(".q4"):
+            out[k] = v
+            continue
+        name = k[:-3]
+        b = np.asarray(v, dtype=np.uint8)
+        nib = np.empty((b.shape[0], 2 * b.shape[1]), dtype=np.int64)
+        nib[:, 0::2] = b & 0xF
+        nib[:, 1::2] = b >> 4
+        q = np.where(nib >= 8, nib - 16, nib).astype(F64)
+        sc = np.asarray(weights[name + ".s4"])
+        if not np.issubdtype(sc.dtype, np.floating):
+            raise ValueError(f"{name}: scales must be given as values, not bit patterns")
+        sc = sc.astype(F64)
+        if sc.shape[1] * group != q.shape[1]:
+            raise ValueError(f"{name}: scales {sc.shape} do not cover {q.shape[1]} inputs in groups of {group}")
+        out[name] = q * np.repeat(sc, group, axis=1)
+    return out
+
+
 def rms_norm(x, g, eps):
     """x / sqrt(mean(x^2) + eps) * g over the last axis."""
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g

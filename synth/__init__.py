@@ -18,5 +18,9 @@ from .inputs import (  # noqa: F401
     model,
     prompt_lengths,
     tensor_specs,
+    W4_GROUP,
+    make_w4_model,
+    quantize_w4,
+    w4_names,
     weights_as_f32,
 )

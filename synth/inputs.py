@@ -196,10 +196,70 @@ def make_weights(m: dict, seed: int = 0, threads: int | None = None, only=None) 
 
 
 def weights_as_f32(m: dict, w: dict) -> dict:
-    """float32 view of the weights (bf16 values are exact in fp32)."""
+    """float32 view of the weights (bf16 values are exact in fp32).  Packed
+    4-bit matrices (".q4") are passed through as they are."""
     if m["weight_dtype"] == "bf16":
-        return {k: bf16_bits_to_f32(v).reshape(v.shape) for k, v in w.items()}
+        return {k: (v if k.endswith(".q4") else bf16_bits_to_f32(v).reshape(v.shape)) for k, v in w.items()}
     return dict(w)
+
+
+# ----------------------------------------------------------------------------
+# W4A16 synthetic models (4-bit weights in groups, bf16 scales)
+# ----------------------------------------------------------------------------
+# The pages name a W4A16 variant of S2 that keeps the attention of its last 12
+# layers in bf16, and give no recipe.  The synthetic W4A16 model here uses
+# symmetric 4-bit groups of W4_GROUP consecutive input elements with a bf16
+# scale per (row, group): scale = bf16(max |w| / 7), q = clamp(rne(w / scale),
+# -8, 7), stored two per byte (element 2j in the low nibble of byte j, 2j+1
+# in the high nibble, two's complement).  The model's weight is q * scale.
+
+W4_GROUP = 128
+W4_MATS = ("wq", "wk", "wv", "wo", "w1", "w3", "w2")
+
+
+def w4_names(m: dict) -> list:
+    """Matrices stored as 4-bit groups when m["w4a16"] is set: every linear
+    matrix of the slow and fast layers except the attention projections of
+    the last m["w4_bf16_attn_layers"] (default 12) slow layers."""
+    if not m.get("w4a16"):
+        return []
+    keep = m.get("w4_bf16_attn_layers", 12)
+    out = []
+    for i in range(m["n_layer"]):
+        late = i >= m["n_layer"] - keep
+        out += [f"layers.{i}.{k}" for k in W4_MATS if not (late and k in ("wq", "wk", "wv", "wo"))]
+    for i in range(m["n_fast_layer"]):
+        out += [f"fast_layers.{i}.{k}" for k in W4_MATS]
+    return out
+
+
+def quantize_w4(bits: np.ndarray):
+    """bf16 bits [rows, K] -> (packed uint8 [rows, K/2], scales bf16 bits [rows, K/W4_GROUP])."""
+    w = bf16_bits_to_f32(bits).reshape(bits.shape).astype(np.float64)
+    rows, K = w.shape
+    if K % W4_GROUP:
+        raise ValueError(f"row length {K} is not a multiple of {W4_GROUP}")
+    g = w.reshape(rows, K // W4_GROUP, W4_GROUP)
+    amax = np.abs(g).max(axis=2)
+    sbits = f32_to_bf16_bits((amax / 7.0).astype(np.float32))
+    s = bf16_bits_to_f32(sbits).reshape(amax.shape).astype(np.float64)
+    s_safe = np.where(s > 0, s, 1.0)
+    q = np.clip(np.round(g / s_safe[:, :, None]), -8, 7).astype(np.int64).reshape(rows, K)   # round half to even
+    u = (q & 0xF).astype(np.uint8)
+    packed = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sbits.reshape(rows, K // W4_GROUP)
+
+
+def make_w4_model(m: dict, w: dict) -> dict:
+    """The W4A16 form of a bf16 weight set: each matrix of w4_names(m) is
+    replaced by name.q4 (packed) and name.s4 (scales); the rest is kept."""
+    if m["weight_dtype"] != "bf16":
+        raise ValueError("W4A16 models start from bf16 weights")
+    out = dict(w)
+    for name in w4_names(m):
+        q, s = quantize_w4(out.pop(name))
+        out[name + ".q4"], out[name + ".s4"] = q, s
+    return out
 
 
 # ----------------------------------------------------------------------------

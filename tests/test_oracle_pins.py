@@ -569,3 +569,63 @@ def test_ras_window_is_the_emitted_ids():
             emitted.append(fr[0])
     assert seq.ras_hist == emitted
     assert used > 0          # the greedy mini model repeats itself: the breaker fires
+
+
+# ----------------------------------------------------------------------------
+# W4A16 weights (the survey's NEXT 4): the oracle's dequantisation
+# ----------------------------------------------------------------------------
+
+def test_w4_nibble_order_and_sign():
+    # every 4-bit code in both nibble positions: byte j = (hi << 4) | lo holds
+    # inputs 2j (lo) and 2j+1 (hi), two's complement
+    from oracle import dequant_w4
+    codes = np.arange(16)
+    packed = (codes | (codes[::-1] << 4)).astype(np.uint8)[None, :]       # 16 bytes, 32 inputs
+    d = dequant_w4({"m.q4": packed, "m.s4": np.array([[0.25]], dtype=np.float32)}, group=32)["m"][0]
+    signed = np.where(codes >= 8, codes - 16, codes)
+    assert np.array_equal(d[0::2], signed * 0.25)
+    assert np.array_equal(d[1::2], signed[::-1] * 0.25)
+
+
+def test_w4_scales_per_group():
+    from oracle import dequant_w4
+    packed = np.full((2, 8), 0x11, dtype=np.uint8)                          # q = 1 everywhere
+    sc = np.array([[1.0, 2.0, 4.0, 8.0], [0.5, 0.5, 0.5, 0.5]], dtype=np.float32)
+    d = dequant_w4({"m.q4": packed, "m.s4": sc}, group=4)["m"]
+    assert np.array_equal(d[0], np.repeat([1.0, 2.0, 4.0, 8.0], 4))
+    assert np.array_equal(d[1], np.full(16, 0.5))
+    with pytest.raises(ValueError):
+        dequant_w4({"m.q4": packed, "m.s4": sc.view(np.uint32)}, group=4)   # bit patterns, not values
+
+
+def test_w4_round_trip_against_the_quantiser():
+    # independent code paths: synth packs, the oracle unpacks.  Each weight
+    # moves by at most half a step, the largest |w| of a group keeps its sign
+    # and lands within a step, and values already on the grid come back exact.
+    from oracle import dequant_w4
+    g = np.random.Generator(np.random.PCG64(7))
+    w = (g.standard_normal((6, 256)) * 0.02).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(w)
+    wb = synth.bf16_bits_to_f32(bits).reshape(w.shape).astype(np.float64)
+    q, s = synth.quantize_w4(bits)
+    sf = synth.bf16_bits_to_f32(s).reshape(s.shape)
+    d = dequant_w4({"m.q4": q, "m.s4": sf}, group=synth.W4_GROUP)["m"]
+    step = np.repeat(sf.astype(np.float64), synth.W4_GROUP, axis=1)
+    # |w| / s <= 7 * (1 + 2^-8) after the bf16 rounding of the scale, so no clamp at 7 bites
+    assert np.all(np.abs(d - wb) <= 0.5 * step + 1e-12)
+    on_grid = np.round(np.clip(wb / step, -7, 7)) * step
+    q2, s2 = synth.quantize_w4(synth.f32_to_bf16_bits(on_grid.astype(np.float32)))
+    # on-grid values whose bf16 rounding is exact reproduce themselves
+    exact = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(on_grid.astype(np.float32))).reshape(on_grid.shape) == on_grid
+    d2 = dequant_w4({"m.q4": q2, "m.s4": synth.bf16_bits_to_f32(s2).reshape(s2.shape)}, group=synth.W4_GROUP)["m"]
+    assert np.allclose(d2[exact], on_grid[exact], rtol=0, atol=1e-3 * np.abs(on_grid).max())
+
+
+def test_w4_model_keeps_the_late_attention_in_bf16():
+    m = synth.model("s2", w4a16=1)
+    names = set(synth.w4_names(m))
+    assert "layers.0.wq" in names and "layers.23.wo" in names and "layers.23.w2" in names
+    assert "layers.24.wq" not in names and "layers.35.wo" not in names      # the last 12 layers' attention
+    assert "layers.24.w1" in names and "layers.35.w2" in names
+    assert "fast_layers.3.wq" in names and "fast_output" not in names and "tok_embedding" not in names
+    assert len(names) == 24 * 7 + 12 * 3 + 4 * 7
