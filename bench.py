@@ -36,6 +36,9 @@ WORKLOADS = {
                                        "(time to frame 0), then 64 greedy decode frames"),
     "s2_fast_tf": ("fast_s2", None, "S2-shaped teacher-forced fast AR: 819 (hidden state, codes) pairs, "
                                     "8,190 rows through the fast layers and head per step"),
+    "s2_b1_w4": ("s2_b1", None, "full S2-shaped Dual-AR decode, batch 1, W4A16 weights (4-bit groups of 128 "
+                                "with bf16 scales; the last 12 slow layers' attention, the embeddings and "
+                                "heads in bf16), 1,024-token prompt, greedy"),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
@@ -244,6 +247,9 @@ def main():
     wl_name, b_over, desc = WORKLOADS[args.workload]
     wl = synth.WORKLOADS[wl_name]
     m = synth.model(wl["model"])
+    w4 = args.workload.endswith("_w4")
+    if w4:
+        m = dict(m, w4a16=1)
     if args.semantic_head:
         m = dict(m, semantic_head=1)
     B = b_over or wl["batch"]
@@ -256,6 +262,10 @@ def main():
     t0 = time.time()
     w = synth.make_weights(m, seed=args.seed)
     log(f"[bench] {args.workload}: weights generated in {time.time() - t0:.1f}s")
+    if w4:
+        t0 = time.time()
+        w = synth.make_w4_model(m, w)
+        log(f"[bench] {len(synth.w4_names(m))} matrices as 4-bit groups in {time.time() - t0:.1f}s")
     dev_w = upload_weights(m, w)
     torch.cuda.synchronize()
     log(f"[bench] weights on device ({sum(t.numel() * t.element_size() for t in dev_w.values()) / 1e9:.2f} GB)")
@@ -286,7 +296,9 @@ def main():
             plen = np.full(B, P, dtype=np.int32)
             layout = ("fixed", P // 8, P // 2, P - P // 8 - P // 2)
         prompts = synth.make_prompts(m, layout, plen, seed=args.seed)
-        ctx = DualAR(m, dev_w, max_batch=B, max_seq_len=int(plen.max()) + P_frames + 2)
+        # 4-bit weights run as vector GEMVs only: the prompt one position per step
+        ctx = DualAR(m, dev_w, max_batch=B, max_seq_len=int(plen.max()) + P_frames + 2,
+                     prefill_chunk=1 if w4 else 0)
         U = None
         if not samp["greedy"] or ras:
             U = torch.from_numpy(synth.make_uniforms((1 + P_frames, B, N + (ras > 0)), seed=args.seed)).cuda()
@@ -324,7 +336,8 @@ def main():
         step_bytes = 0
         for f in range(K):
             L = [int(p) + W + f + 1 for p in plen]
-            step_bytes += reporting.frame_bytes(m, L, semantic_head=args.semantic_head)["total"]
+            step_bytes += reporting.frame_bytes(m, L, semantic_head=args.semantic_head,
+                                                w4_names=synth.w4_names(m))["total"]
     step_gbps = step_bytes / (ms / 1e3) / 1e9
 
     # ---- live per-launch timing (HIP events on the context's stream) ----
@@ -348,7 +361,10 @@ def main():
             f"{100 * gemv_share:.1f}% of step time")
         log(f"[bench] SwiGLU gate|up GEMV: {f['launches']} launches, avg {sw_avg_us:.2f} us, "
             f"{sw_bytes / 1e6:.2f} MB/launch, {sw_gbps:.0f} GB/s")
-        if m["weight_dtype"] == "f32":
+        if w4:
+            kname = ("gemv_w4_kernel<2, 2, 2> (SwiGLU W1|W3 GEMV, 2 x 9728 x 2560 as 4-bit groups of 128 with "
+                     "bf16 scales)")
+        elif m["weight_dtype"] == "f32":
             kname = "SwiGLU W1|W3 GEMV"
         elif B == 1:
             kname = ("gemv_rx_kernel<bf16, 2 rows/wave, gate+up, 5 units> (SwiGLU W1|W3 GEMV, "
@@ -361,7 +377,7 @@ def main():
                     "kernel": kname,
                     "achieved": round(sw_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(sw_gbps / HBM_PEAK_GBPS, 4),
-                    "traffic": roofline_traffic() if (B == 1 and m["weight_dtype"] == "bf16") else None,
+                    "traffic": roofline_traffic() if (B == 1 and m["weight_dtype"] == "bf16" and not w4) else None,
                     "avg_launch_us": round(sw_avg_us, 3), "bytes_per_launch": round(sw_bytes),
                     "launches_profiled": f["launches"],
                     "gemv_family": {"achieved_GBps": round(gemv_gbps, 1), "avg_launch_us": round(gemv_avg_us, 3),
@@ -387,7 +403,7 @@ def main():
         log(f"[bench] prefill: {fl['total'] / 1e12:.0f} TFLOP in {ttff_ms:.0f} ms = {tf:.1f} TFLOP/s")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not w4:   # the oracle baseline is timed on the bf16 model
         del dev_w
         torch.cuda.empty_cache()
         cpu = cpu_baseline(m, w, fast_only, args.seed)

@@ -46,10 +46,18 @@ class LayerWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in _LAYER_FIELDS]
 
 
+W4_MATS = ("wq", "wk", "wv", "wo", "w1", "w3", "w2")
+
+
+class LayerW4(C.Structure):
+    _fields_ = [("q4", C.c_void_p * 7), ("s4", C.c_void_p * 7)]
+
+
 class Weights(C.Structure):
     _fields_ = [("tok_embedding", C.c_void_p), ("codebook_embedding", C.c_void_p), ("norm", C.c_void_p),
                 ("layers", C.POINTER(LayerWeights)), ("fast_layers", C.POINTER(LayerWeights)),
-                ("fast_embeddings", C.c_void_p), ("fast_norm", C.c_void_p), ("fast_output", C.c_void_p)]
+                ("fast_embeddings", C.c_void_p), ("fast_norm", C.c_void_p), ("fast_output", C.c_void_p),
+                ("layers_w4", C.POINTER(LayerW4)), ("fast_layers_w4", C.POINTER(LayerW4))]
 
 
 class Sampling(C.Structure):
@@ -150,7 +158,9 @@ def upload_weights(m: dict, w: dict, device="cuda"):
     out = {}
     for k, v in w.items():
         t = torch.from_numpy(np.ascontiguousarray(v))
-        if m["weight_dtype"] == "bf16":
+        if k.endswith(".q4"):
+            pass                                     # packed 4-bit values stay bytes
+        elif m["weight_dtype"] == "bf16":
             t = t.view(torch.int16).view(torch.bfloat16)
         out[k] = t.to(device)
     return out
@@ -198,6 +208,18 @@ class DualAR:
                     setattr(arr[i], f, None if t is None else t.data_ptr())
             self._keep.append(arr)
             return arr
+        def layers_w4(prefix, n):
+            # None (NULL) unless some matrix of these layers is given as 4-bit groups
+            if not any(k.startswith(prefix + ".") and k.endswith(".q4") for k in w):
+                return None
+            arr = (LayerW4 * n)()
+            for i in range(n):
+                for j, f in enumerate(W4_MATS):
+                    q, sc = w.get(f"{prefix}.{i}.{f}.q4"), w.get(f"{prefix}.{i}.{f}.s4")
+                    arr[i].q4[j] = None if q is None else q.data_ptr()
+                    arr[i].s4[j] = None if sc is None else sc.data_ptr()
+            self._keep.append(arr)
+            return arr
         s = Weights()
         s.tok_embedding = w["tok_embedding"].data_ptr()
         s.codebook_embedding = w["codebook_embedding"].data_ptr()
@@ -207,6 +229,8 @@ class DualAR:
         s.fast_embeddings = w["fast_embeddings"].data_ptr()
         s.fast_norm = w["fast_norm"].data_ptr()
         s.fast_output = w["fast_output"].data_ptr()
+        s.layers_w4 = layers_w4("layers", m["n_layer"])
+        s.fast_layers_w4 = layers_w4("fast_layers", m["n_fast_layer"])
         return s
 
     def _check(self, st):

@@ -166,6 +166,7 @@ Layout layout(const Resolved& r) {
 struct Stack {
   int n_layer, dim, H, KV, hd, ffn, qk;
   std::vector<dualar_layer_weights> lw;
+  std::vector<dualar_layer_w4> l4;   // 4-bit forms (all NULL without them)
   char* k; char* v;        // cache bases
   size_t layer_stride;     // elements
   int max_pos;
@@ -264,7 +265,8 @@ hipError_t gemv(dualar_ctx* c, const GemvParams& g0) {
   if (e != hipSuccess) return e;
   e = launch_gemv<T>(g, c->stream);
   if (e != hipSuccess) return e;
-  const double wbytes = (double)g.n_out * (sw ? 2 : 1) * g.K * c->r.esz;
+  const double wbytes = g.q4[0] ? (double)g.n_out * (sw ? 2 : 1) * (g.K / 2 + g.K / 128 * 2)
+                               : (double)g.n_out * (sw ? 2 : 1) * g.K * c->r.esz;
   const double act = 4.0 * g.B * ((double)g.K + g.n_out * (g.mode == GEMV_ADD ? 2 : 1));
   return prof_post(c, DUALAR_K_GEMV, wbytes + act, sw);
 }
@@ -308,6 +310,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   const Resolved& r = c->r;
   const Layout& L = c->L;
   const dualar_layer_weights& w = S.lw[l];
+  const dualar_layer_w4& w4 = S.l4[l];      // 4-bit forms (NULL: bf16)
   float* qkv = (float*)(c->ws + L.qkv);
   float* att = (float*)(c->ws + L.att);
   float* ffn = (float*)(c->ws + L.ffn);
@@ -323,6 +326,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   GemvParams g{};
   // q | k | v = W_qkv . RMSNorm(x)
   g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
+  for (int j = 0; j < 3; ++j) { g.q4[j] = w4.q4[j]; g.s4[j] = w4.s4[j]; }
   g.rows[0] = S.H * S.hd; g.rows[1] = S.KV * S.hd; g.rows[2] = S.KV * S.hd; g.n_seg = 3;
   g.K = S.dim; g.n_out = (S.H + 2 * S.KV) * S.hd;
   g.x = x; g.ldx = S.dim; g.gain = w.attention_norm; g.eps = r.eps;
@@ -363,7 +367,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     a.H = S.H; a.KV = S.KV; a.hd = S.hd;
     a.out = att; a.ld_out = L.att_ld; a.out_planes = planes; a.R = B; a.B = B / rows_per_seq;
     HIPCHK((launch_prefill_attn<T, KT>(a, c->stream)));
-  } else if (B == 1 && !pos_dev && sizeof(T) == 2 && sizeof(KT) == 2 &&
+  } else if (B == 1 && !pos_dev && sizeof(T) == 2 && sizeof(KT) == 2 && !w4.q4[3] &&
              attn_o_b1_fits(S.H, S.KV, S.hd, S.dim, pos_const + 1)) {
     // fast AR at batch 1: the depth attention runs inside the O product
     AttnOParams a{};
@@ -397,7 +401,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   // merge_o_b1_max_splits() chunks of 128 or 256 positions, its merge done by
   // the O product (each lane merges the eight values it multiplies).
   int mo_chunk = 0;
-  if (MERGE_O_FUSE && B == 1 && pos_dev && sizeof(T) == 2 && attn_o_b1_fits(S.H, S.KV, S.hd, S.dim, 1)) {
+  if (MERGE_O_FUSE && B == 1 && pos_dev && sizeof(T) == 2 && !w4.q4[3] && attn_o_b1_fits(S.H, S.KV, S.hd, S.dim, 1)) {
     for (int it : {MERGE_O_IT_FIRST, 24 - MERGE_O_IT_FIRST}) {
       const int ch = attn_chunk((int)r.kvesz, S.hd, it);
       if ((Lmax + ch - 1) / ch <= merge_o_b1_max_splits()) { a.it = it; mo_chunk = ch; break; }
@@ -442,7 +446,8 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   // x += Wo . o
   if (!o_done) {
   g = GemvParams{};
-  g.w[0] = w.wo; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.H * S.hd; g.n_out = S.dim;
+  g.w[0] = w.wo; g.q4[0] = w4.q4[3]; g.s4[0] = w4.s4[3];
+  g.rows[0] = S.dim; g.n_seg = 1; g.K = S.H * S.hd; g.n_out = S.dim;
   g.x = att; g.ldx = L.att_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
   live_tiles(c, g, rows_per_seq);
   g.xplanes = planes;
@@ -452,6 +457,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   // h = silu(W1 n) * (W3 n), n = RMSNorm(x)
   g = GemvParams{};
   g.w[0] = w.w1; g.w[1] = w.w3; g.rows[0] = S.ffn; g.rows[1] = S.ffn; g.n_seg = 2;
+  g.q4[0] = w4.q4[4]; g.q4[1] = w4.q4[5]; g.s4[0] = w4.s4[4]; g.s4[1] = w4.s4[5];
   g.K = S.dim; g.n_out = S.ffn; g.x = x; g.ldx = S.dim; g.gain = w.ffn_norm; g.eps = r.eps;
   g.y = ffn; g.ldy = L.ffn_ld; g.B = B; g.mode = GEMV_SWIGLU;
   live_tiles(c, g, rows_per_seq);
@@ -460,7 +466,8 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   HIPCHK(gemv<T>(c, g));
   // x += W2 . h
   g = GemvParams{};
-  g.w[0] = w.w2; g.rows[0] = S.dim; g.n_seg = 1; g.K = S.ffn; g.n_out = S.dim;
+  g.w[0] = w.w2; g.q4[0] = w4.q4[6]; g.s4[0] = w4.s4[6];
+  g.rows[0] = S.dim; g.n_seg = 1; g.K = S.ffn; g.n_out = S.dim;
   g.x = ffn; g.ldx = L.ffn_ld; g.y = x; g.ldy = S.dim; g.res = x; g.ldres = S.dim; g.B = B; g.mode = GEMV_ADD;
   live_tiles(c, g, rows_per_seq);
   g.xplanes = planes;
@@ -482,9 +489,11 @@ dualar_status run_layer_kv_only(dualar_ctx* c, Stack& S, int l, float* x, int B,
   const Resolved& r = c->r;
   const Layout& L = c->L;
   const dualar_layer_weights& w = S.lw[l];
+  const dualar_layer_w4& w4 = S.l4[l];
   float* qkv = (float*)(c->ws + L.qkv);
   GemvParams g{};
   g.w[0] = w.wk; g.w[1] = w.wv;
+  g.q4[0] = w4.q4[1]; g.q4[1] = w4.q4[2]; g.s4[0] = w4.s4[1]; g.s4[1] = w4.s4[2];
   g.rows[0] = S.KV * S.hd; g.rows[1] = S.KV * S.hd; g.n_seg = 2;
   g.K = S.dim; g.n_out = 2 * S.KV * S.hd;
   g.x = x; g.ldx = S.dim; g.gain = w.attention_norm; g.eps = r.eps;
@@ -805,16 +814,42 @@ dualar_status dualar_create(const dualar_config* cfg, const dualar_weights* w, v
   if (!P(w->tok_embedding) || !P(w->codebook_embedding) || !P(w->norm) || !P(w->fast_embeddings) ||
       !P(w->fast_norm) || !P(w->fast_output))
     return fail(c, DUALAR_ERR_INVALID_ARG, "a weight pointer is NULL or not 16-byte aligned");
-  auto layer_ok = [&](const dualar_layer_weights& l, int qk) {
-    return P(l.attention_norm) && P(l.wq) && P(l.wk) && P(l.wv) && P(l.wo) && P(l.ffn_norm) && P(l.w1) &&
-           P(l.w3) && P(l.w2) && (!qk || (P(l.q_norm) && P(l.k_norm)));
+  // a matrix may be absent from dualar_layer_weights when its 4-bit form is given
+  auto has4 = [&](const dualar_layer_w4* a, int i, int j) { return a && a[i].q4[j]; };
+  auto layer_ok = [&](const dualar_layer_weights& l, int qk, const dualar_layer_w4* a, int i) {
+    const void* m[7] = {l.wq, l.wk, l.wv, l.wo, l.w1, l.w3, l.w2};
+    for (int j = 0; j < 7; ++j)
+      if (!P(m[j]) && !has4(a, i, j)) return false;
+    return P(l.attention_norm) && P(l.ffn_norm) && (!qk || (P(l.q_norm) && P(l.k_norm)));
   };
   for (int i = 0; i < r.n_layer; ++i)
-    if (!layer_ok(w->layers[i], r.slow_qk))
+    if (!layer_ok(w->layers[i], r.slow_qk, w->layers_w4, i))
       return fail(c, DUALAR_ERR_INVALID_ARG, "a slow layer weight is NULL or not 16-byte aligned");
   for (int i = 0; i < r.fn_layer; ++i)
-    if (!layer_ok(w->fast_layers[i], r.fast_qk))
+    if (!layer_ok(w->fast_layers[i], r.fast_qk, w->fast_layers_w4, i))
       return fail(c, DUALAR_ERR_INVALID_ARG, "a fast layer weight is NULL or not 16-byte aligned");
+  // 4-bit matrices: batch 1 and one prefill position per step (vector GEMVs only)
+  auto w4_check = [&](const dualar_layer_w4* a, int n, int dim, int H, int KV, int hd, int ffn) -> const char* {
+    if (!a) return nullptr;
+    const int in[7] = {dim, dim, dim, H * hd, dim, dim, ffn};
+    for (int i = 0; i < n; ++i) {
+      for (int j = 0; j < 7; ++j) {
+        if (!a[i].q4[j]) continue;
+        if (!P(a[i].q4[j]) || !P(a[i].s4[j])) return "a 4-bit matrix or its scales is NULL or not 16-byte aligned";
+        if (in[j] % 128) return "a 4-bit matrix's rows are not a whole number of 128-input groups";
+      }
+      if ((!a[i].q4[0]) != (!a[i].q4[1]) || (!a[i].q4[0]) != (!a[i].q4[2])) return "wq, wk, wv must be all 4-bit or all bf16";
+      if ((!a[i].q4[4]) != (!a[i].q4[5])) return "w1 and w3 must both be 4-bit or both bf16";
+    }
+    return nullptr;
+  };
+  if (w->layers_w4 || w->fast_layers_w4) {
+    if (r.esz != 2 || r.max_batch != 1 || r.pc != 1)
+      return fail(c, DUALAR_ERR_INVALID_ARG, "4-bit matrices need bf16 weights, max_batch 1 and prefill_chunk 1");
+    const char* e = w4_check(w->layers_w4, r.n_layer, r.dim, r.H, r.KV, r.hd, r.ffn);
+    if (!e) e = w4_check(w->fast_layers_w4, r.fn_layer, r.dim, r.fH, r.fKV, r.fhd, r.fffn);
+    if (e) return fail(c, DUALAR_ERR_INVALID_ARG, e);
+  }
   const Layout L = layout(r);
   if (!workspace) return fail(c, DUALAR_ERR_INVALID_ARG, "workspace is NULL");
   if (((uintptr_t)workspace) % ALIGN) return fail(c, DUALAR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -825,19 +860,23 @@ dualar_status dualar_create(const dualar_config* cfg, const dualar_weights* w, v
   c = new dualar_ctx();
   c->r = r; c->L = L; c->w = *w; c->ws = (char*)workspace; c->stream = (hipStream_t)hip_stream;
   if (hipGetDevice(&c->device) != hipSuccess) { delete c; return fail(nullptr, DUALAR_ERR_HIP, "hipGetDevice failed"); }
-  auto mk = [&](Stack& S, const dualar_layer_weights* lw, int n, int dim, int H, int KV, int hd, int ffn, int qk,
-                size_t k, size_t v, size_t stride, int max_pos, size_t rope) {
+  auto mk = [&](Stack& S, const dualar_layer_weights* lw, const dualar_layer_w4* l4, int n, int dim, int H, int KV,
+                int hd, int ffn, int qk, size_t k, size_t v, size_t stride, int max_pos, size_t rope) {
     S.n_layer = n; S.dim = dim; S.H = H; S.KV = KV; S.hd = hd; S.ffn = ffn; S.qk = qk;
     S.lw.assign(lw, lw + n);
+    if (l4) S.l4.assign(l4, l4 + n);
+    else S.l4.assign(n, dualar_layer_w4{});
     S.k = c->ws + k; S.v = c->ws + v; S.layer_stride = stride; S.max_pos = max_pos;
     S.rope = (const float2*)(c->ws + rope);
   };
-  mk(c->slow, w->layers, r.n_layer, r.dim, r.H, r.KV, r.hd, r.ffn, r.slow_qk, L.kslow, L.vslow, L.slow_layer_stride,
-     r.max_seq, L.rope_s);
-  mk(c->fast, w->fast_layers, r.fn_layer, r.dim, r.fH, r.fKV, r.fhd, r.fffn, r.fast_qk, L.kfast, L.vfast,
-     L.fast_layer_stride, r.N, L.rope_f);
+  mk(c->slow, w->layers, w->layers_w4, r.n_layer, r.dim, r.H, r.KV, r.hd, r.ffn, r.slow_qk, L.kslow, L.vslow,
+     L.slow_layer_stride, r.max_seq, L.rope_s);
+  mk(c->fast, w->fast_layers, w->fast_layers_w4, r.fn_layer, r.dim, r.fH, r.fKV, r.fhd, r.fffn, r.fast_qk, L.kfast,
+     L.vfast, L.fast_layer_stride, r.N, L.rope_f);
   c->w.layers = c->slow.lw.data();
   c->w.fast_layers = c->fast.lw.data();
+  c->w.layers_w4 = nullptr;          // kept per stack (S.l4)
+  c->w.fast_layers_w4 = nullptr;
   c->st.pos = (int*)(c->ws + L.st_pos); c->st.done = (int*)(c->ws + L.st_done);
   c->st.frames = (int*)(c->ws + L.st_frames); c->st.cur = (int*)(c->ws + L.st_cur);
   c->st.plen = (int*)(c->ws + L.st_plen); c->st.frame_idx = (int*)(c->ws + L.st_fidx);

@@ -563,6 +563,124 @@ __global__ void __launch_bounds__(DUALAR_WG) gemv_loop_kernel(GemvParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// 4-bit weights (W4A16), one activation row
+// ---------------------------------------------------------------------------
+// Rows of K inputs as packed 4-bit two's-complement values (input 2j in the
+// low nibble of byte j) with a bf16 scale per group of 128 inputs.  Lane l
+// takes the 16-byte chunks c = l, l + 64, ... (32 inputs, inside one group)
+// of every row it owns; the weights and scales are loaded first, then the
+// (normalised) activation row is staged in LDS.  Per chunk, v' = v ^ 8
+// turns each nibble into v + 8 in [0, 15], whose bytes convert to floats in
+// one step, and the chunk adds scale * (sum v' x - 8 sum x) to its row; the
+// sum of x is shared by all rows of the lane.
+template <int NR>
+__device__ __forceinline__ const char* w4_row(const GemvParams& p, int row, int s, const uint16_t** sc) {
+  int seg = 0;
+  if (p.mode == GEMV_SWIGLU) seg = s;
+  else if (row >= p.rows[0]) {
+    row -= p.rows[0];
+    seg = 1;
+    if (row >= p.rows[1]) { row -= p.rows[1]; seg = 2; }
+  }
+  const void* q = seg == 0 ? p.q4[0] : seg == 1 ? p.q4[1] : p.q4[2];
+  const void* g = seg == 0 ? p.s4[0] : seg == 1 ? p.s4[1] : p.s4[2];
+  *sc = (const uint16_t*)g + (size_t)row * (p.K / 128);
+  return (const char*)q + (size_t)row * (p.K / 2);
+}
+
+template <int RPW, int NR, int CPL>
+__global__ void __launch_bounds__(DUALAR_WG) gemv_w4_kernel(GemvParams p) {
+  extern __shared__ float xs[];      // [K] the activation row
+  __shared__ float red[1][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+  const int nch = p.K / 32;
+
+  // 1. packed weights and their scales
+  u32x4 wq[RPW][NR][CPL];
+  uint32_t sc[RPW][NR][CPL];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = min(row0 + r, p.n_out - 1);
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      const uint16_t* sb;
+      const char* qb = w4_row<NR>(p, row, s, &sb);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = min(lane + 64 * i, nch - 1);
+        wq[r][s][i] = ld_stream(qb + (size_t)c * 16);
+        sc[r][s][i] = sb[c / 4];
+      }
+    }
+  }
+  // 2. the activation row (+ RMSNorm * gain) in LDS
+  stage_x<bf16_t, 1>(p, xs, red, 0);
+
+  // 3. dot products chunk by chunk
+  float acc[RPW][NR][1];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int s = 0; s < NR; ++s) acc[r][s][0] = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nch) break;
+    float xv[32];
+#pragma unroll
+    for (int e = 0; e < 32; e += 4) {
+      const float4 t = *(const float4*)&xs[32 * c + e];
+      xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
+    }
+    float sx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) sx += xv[e];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        const u32x4 q = wq[r][s][i];
+        const uint32_t qd[4] = {q.x, q.y, q.z, q.w};
+        float d = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t u = qd[k] ^ 0x88888888u;
+          const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            d = fmaf((float)((lo >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b], d);
+            d = fmaf((float)((hi >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b + 1], d);
+          }
+        }
+        acc[r][s][0] = fmaf(bf16_bits_to_f32(sc[r][s][i]), d - 8.f * sx, acc[r][s][0]);
+      }
+  }
+  gemv_epilogue<RPW, NR, 1>(p, acc, row0, 0);
+}
+
+template <int NR, int CPL>
+static hipError_t go_w4(const GemvParams& p, hipStream_t s) {
+  constexpr int RPW = 2;
+  dim3 grid((p.n_out + 4 * RPW - 1) / (4 * RPW));
+  launch_timed(gemv_w4_kernel<RPW, NR, CPL>, grid, dim3(DUALAR_WG), (uint32_t)(p.K * sizeof(float)), s, p);
+  return hipGetLastError();
+}
+
+template <int NR>
+static hipError_t launch_w4(const GemvParams& p, hipStream_t s) {
+  if (p.B != 1 || p.K % 128 || p.xplanes || p.yplanes) return hipErrorInvalidValue;
+  switch ((p.K / 32 + 63) / 64) {
+    case 1: return go_w4<NR, 1>(p, s);
+    case 2: return go_w4<NR, 2>(p, s);
+    case 3: return go_w4<NR, 3>(p, s);
+    case 4: return go_w4<NR, 4>(p, s);
+    case 5: return go_w4<NR, 5>(p, s);
+    default: return hipErrorInvalidValue;   // rows longer than 10,240 inputs
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launch selection
 // ---------------------------------------------------------------------------
 // NU > 0 and BT == 1: register-staged kernel (one activation row, the
@@ -668,6 +786,11 @@ static hipError_t pick_bt(const GemvParams& p, hipStream_t s) {
 }
 
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s) {
+  if (p.q4[0]) {
+    if constexpr (sizeof(T) != 2) return hipErrorInvalidValue;
+    if (p.next_done) *p.next_done = 0;
+    return p.mode == GEMV_SWIGLU ? launch_w4<2>(p, s) : launch_w4<1>(p, s);
+  }
   if constexpr (sizeof(T) == 2) {
     hipError_t e;
     if (launch_gemm_mfma(p, s, &e)) return e;   // 2+ activation rows on the matrix cores

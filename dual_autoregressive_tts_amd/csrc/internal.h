@@ -42,6 +42,9 @@ struct QkPrep {
 // (w[0], w[1]) of a SwiGLU FFN whose output is silu(W1 h) * (W3 h).
 struct GemvParams {
   const void* w[3];
+  // 4-bit form of the segments (batch 1 only): q4[i] = packed [rows_i][K/2]
+  // bytes, s4[i] = bf16 scales [rows_i][K/128]; q4[0] == NULL: bf16 w[]
+  const void* q4[3]; const void* s4[3];
   int rows[3];
   int n_seg;
   int K;

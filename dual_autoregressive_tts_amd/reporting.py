@@ -55,7 +55,39 @@ def fast_pass0_weight_elems(m: dict) -> int:
     return (m["n_fast_layer"] - 1) * per + last
 
 
-def frame_bytes(m: dict, ctx_lengths, fast_only: bool = False, semantic_head: bool = False) -> dict:
+def _mat_shape(m: dict, name: str):
+    """(rows, inputs) of a layer matrix `layers.i.wq`-style name."""
+    fast = name.startswith("fast_layers.")
+    pre = "fast_" if fast else ""
+    dim = m["fast_dim"] if fast else m["dim"]
+    H, KV, hd = m[pre + "n_head"], m[pre + "n_kv_head"], m[pre + "head_dim"]
+    ffn = m["fast_ffn_dim"] if fast else m["ffn_dim"]
+    return {"wq": (H * hd, dim), "wk": (KV * hd, dim), "wv": (KV * hd, dim), "wo": (dim, H * hd),
+            "w1": (ffn, dim), "w3": (ffn, dim), "w2": (dim, ffn)}[name.rsplit(".", 1)[1]]
+
+
+def w4_read_delta(m: dict, w4_names, fast_only: bool = False) -> int:
+    """Change of a frame-step's weight bytes when the named matrices are 4-bit
+    groups of 128 with bf16 scales (rows * (K/2 + K/64) bytes per read instead
+    of rows * K * 2): slow matrices are read once per frame, fast ones by
+    passes 1..N-1, and by pass 0 for all layers but the last, of which pass 0
+    reads the K and V rows only."""
+    N, nf = m["num_codebooks"], m["n_fast_layer"]
+    d = 0
+    for name in w4_names:
+        rows, K = _mat_shape(m, name)
+        per = rows * (K // 2 + K // 64) - rows * K * 2
+        if name.startswith("fast_layers."):
+            layer, mat = int(name.split(".")[1]), name.rsplit(".", 1)[1]
+            reads = N - 1 + (1 if layer < nf - 1 or mat in ("wk", "wv") else 0)
+            d += reads * per
+        elif not fast_only:
+            d += per
+    return d
+
+
+def frame_bytes(m: dict, ctx_lengths, fast_only: bool = False, semantic_head: bool = False,
+                w4_names=()) -> dict:
     """Algorithmic HBM bytes of one decode frame-step over a batch whose
     sequences attend over `ctx_lengths` slow positions (new one included).
 
@@ -83,6 +115,8 @@ def frame_bytes(m: dict, ctx_lengths, fast_only: bool = False, semantic_head: bo
         # a sequence attending over L positions reads L-1 cached entries and appends one
         out["slow_kv"] = sum(int(L) for L in ctx_lengths) * skv
         out["gathers"] += B * (N + 1) * D * esz   # fusion rows
+    if w4_names:
+        out["w4_delta"] = w4_read_delta(m, w4_names, fast_only)
     out["total"] = sum(out.values())
     return out
 

@@ -108,10 +108,27 @@ typedef struct {
   const void *w2;                /* [dim, ffn]  (down)         */
 } dualar_layer_weights;
 
+/* W4A16 form of a layer's linear matrices ([P3], the model card of a W4A16
+ * S2 variant that keeps the attention of its last 12 layers in bf16; it
+ * prints no format, so the format is this library's reading).  For each of
+ * wq, wk, wv, wo, w1, w3, w2 (index 0..6): q4 = NULL uses the bf16 matrix of
+ * dualar_layer_weights; otherwise q4 holds the matrix [rows, in] as 4-bit
+ * two's-complement values, two per byte ([rows, in/2] bytes; input 2j in the
+ * low nibble of byte j, 2j+1 in the high one) and s4 its bf16 scales
+ * [rows, in/128], one per row and group of 128 consecutive inputs; the
+ * weight is q * scale.  Device pointers, 16-byte aligned.  wq/wk/wv must be
+ * all 4-bit or all bf16, and so must w1/w3.  Only for bf16 models with
+ * max_batch = 1 and prefill_chunk = 1 (the products run as vector GEMVs);
+ * dualar_create rejects other uses with DUALAR_ERR_INVALID_ARG. */
+typedef struct {
+  const void *q4[7];             /* wq, wk, wv, wo, w1, w3, w2, or NULL */
+  const void *s4[7];
+} dualar_layer_w4;
+
 /* All device pointers, each 16-byte aligned (tensors are read with 16-byte
  * vector loads; dualar_create rejects others with DUALAR_ERR_INVALID_ARG);
- * the two layer arrays are HOST arrays of n_layer and n_fast_layer entries
- * (copied at create). */
+ * the layer arrays are HOST arrays of n_layer and n_fast_layer entries
+ * (copied at create); layers_w4 / fast_layers_w4 may be NULL (all bf16). */
 typedef struct {
   const void *tok_embedding;        /* [vocab, dim]; also the tied slow head   */
   const void *codebook_embedding;   /* [N*C, dim]; codebook k = rows k*C..     */
@@ -121,6 +138,8 @@ typedef struct {
   const void *fast_embeddings;      /* [C, fast_dim]                           */
   const void *fast_norm;            /* [fast_dim]                              */
   const void *fast_output;          /* [C, fast_dim]                           */
+  const dualar_layer_w4 *layers_w4;       /* NULL or n_layer entries           */
+  const dualar_layer_w4 *fast_layers_w4;  /* NULL or n_fast_layer entries      */
 } dualar_weights;
 
 /* Sampling ([P2] `decode_one_token_ar` excerpt): greedy, or temperature +

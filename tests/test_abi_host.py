@@ -97,6 +97,42 @@ def test_create_checks_before_device(lib):
     assert not h.value
 
 
+def test_create_checks_w4_forms(lib):
+    # 4-bit matrices (W4A16): batch 1 and one prefill position per step only;
+    # a 4-bit form may stand in for a missing bf16 matrix, not a missing one of
+    # both; q/k/v share a form; pointers 16-byte aligned
+    import torch
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
+                    n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1, fast_head_dim=128)
+    w = _fake_weights(m)
+    l4 = (bd.LayerW4 * m["n_layer"])()
+    for j in range(7):
+        l4[0].q4[j] = 8192
+        l4[0].s4[j] = 8192
+    w.layers_w4 = l4
+    w.layers[0].wq = None                                   # given in 4-bit form only
+    h = C.c_void_p()
+
+    def create(batch, pc):
+        cfg = bd.make_config(m, batch, 64, prefill_chunk=pc)
+        need = lib.dualar_workspace_bytes(C.byref(cfg))
+        return lib.dualar_create(C.byref(cfg), C.byref(w), C.c_void_p(256), need, None, C.byref(h))
+
+    assert create(2, 1) == -1
+    assert create(1, 0) == -1 and b"prefill_chunk 1" in lib.dualar_last_error(None)
+    if not torch.cuda.is_available():
+        assert create(1, 1) == -2                           # valid: fails only for want of a device
+    l4[0].q4[1] = None                                      # wk bf16 while wq, wv are 4-bit
+    assert create(1, 1) == -1 and b"all 4-bit or all bf16" in lib.dualar_last_error(None)
+    l4[0].q4[1] = 8192
+    l4[0].s4[6] = 8192 + 2                                  # unaligned scales
+    assert create(1, 1) == -1 and b"aligned" in lib.dualar_last_error(None)
+    l4[0].s4[6] = 8192
+    l4[0].q4[0] = l4[0].q4[1] = l4[0].q4[2] = None          # wq now missing in both forms
+    assert create(1, 1) == -1
+    assert not h.value
+
+
 def test_create_without_gpu_reports_no_device(lib):
     import torch
     if torch.cuda.is_available():

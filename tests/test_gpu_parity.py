@@ -341,6 +341,42 @@ def test_batch1_s2_heads_merged_in_o_product(plen, kv):
     assert sum(c) >= 3
 
 
+# ----------------------------------------------------------------------------
+# W4A16 (the survey's NEXT 4): 4-bit weight groups, batch 1
+# ----------------------------------------------------------------------------
+
+def _w4_case(m, seed, plen, frames, tag):
+    from oracle import dequant_w4
+    w4 = synth.make_w4_model(m, synth.make_weights(m, seed=seed))
+    wf = dequant_w4(synth.weights_as_f32(m, w4))          # the oracle's own q * scale
+    P = synth.make_prompts(m, ("ragged", 1, 1), np.array([plen], dtype=np.int32), seed=seed)
+    return run_and_compare(m, w4, P, np.array([plen], dtype=np.int32), frames, dict(greedy=1), tag=tag,
+                           weights_f32=wf, floor=m.get("kv_dtype", "bf16") == "bf16", prefill_chunk=1)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_w4a16_batch1_small(kv):
+    # rows of 512 and 1,024 inputs (one 16-byte chunk per lane); slow layer 0
+    # fully 4-bit, layer 1 keeps its attention in bf16; fast layers 4-bit
+    m = synth.model("tiny", weight_dtype="bf16", kv_dtype=kv, dim=512, ffn_dim=1024, fast_dim=512,
+                    fast_ffn_dim=1024, n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1,
+                    fast_head_dim=128, w4a16=1, w4_bf16_attn_layers=1)
+    c, worst = _w4_case(m, 9, 40, 4, f"w4-small-{kv}")
+    assert sum(c) >= 4
+
+
+@pytest.mark.timeout(900)
+def test_w4a16_batch1_s2_shapes():
+    # the S2 shapes (rows of 2,560 / 4,096 / 9,728 inputs: 2 and 5 chunks per
+    # lane) with 3 slow layers: layers 0-1 fully 4-bit, layer 2 keeps its
+    # attention in bf16 (so its O product takes the fused bf16 kernels), the
+    # fast layers 4-bit (their O product then runs beside a separate attention)
+    m = synth.model("s2", n_layer=3, w4a16=1, w4_bf16_attn_layers=1)
+    c, worst = _w4_case(m, 10, 40, 2, "w4-s2")
+    assert sum(c) >= 2
+
+
 def test_end_token_stops_and_pads(tiny):
     m, w = tiny
     w = {k: v.copy() for k, v in w.items()}

@@ -104,3 +104,28 @@ def test_roofline_traffic_follows_the_measured_kernel(monkeypatch):
 
     monkeypatch.setattr("builtins.open", fake_open)
     assert bench.roofline_traffic() is None
+
+
+def test_w4_frame_bytes_by_enumeration():
+    # the 4-bit byte change of a frame-step against a direct count over the
+    # model's tensors: every 4-bit matrix costs rows * (K/2 + K/128 * 2) bytes
+    # per read instead of rows * K * 2; slow matrices are read once, fast
+    # matrices N-1 times plus pass 0 (the last layer's K and V rows only)
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
+                    n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1, fast_head_dim=128,
+                    w4a16=1, w4_bf16_attn_layers=1)
+    names = set(synth.w4_names(m))
+    shapes = {n: s for n, s, _ in synth.tensor_specs(m)}
+    N, nf = m["num_codebooks"], m["n_fast_layer"]
+    want = 0
+    for n in names:
+        rows, K = shapes[n]
+        per = rows * (K // 2 + K // 128 * 2) - rows * K * 2
+        if n.startswith("fast_layers."):
+            last = int(n.split(".")[1]) == nf - 1
+            want += per * ((N - 1) + (0 if last and n.rsplit(".", 1)[1] not in ("wk", "wv") else 1))
+        else:
+            want += per
+    b0 = rp.frame_bytes(m, [40])["total"]
+    b4 = rp.frame_bytes(m, [40], w4_names=sorted(names))
+    assert b4["w4_delta"] == want and b4["total"] == b0 + want
