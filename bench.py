@@ -362,7 +362,7 @@ def main():
         log(f"[bench] SwiGLU gate|up GEMV: {f['launches']} launches, avg {sw_avg_us:.2f} us, "
             f"{sw_bytes / 1e6:.2f} MB/launch, {sw_gbps:.0f} GB/s")
         if w4:
-            kname = ("gemv_w4_kernel<2, 2, 2> (SwiGLU W1|W3 GEMV, 2 x 9728 x 2560 as 4-bit groups of 128 with "
+            kname = ("gemv_w4_kernel<2, 2, 5, 1, false> (SwiGLU W1|W3 GEMV, 2 x 9728 x 2560 as 4-bit groups of 128 with "
                      "bf16 scales)")
         elif m["weight_dtype"] == "f32":
             kname = "SwiGLU W1|W3 GEMV"

@@ -407,6 +407,10 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
       if ((Lmax + ch - 1) / ch <= merge_o_b1_max_splits()) { a.it = it; mo_chunk = ch; break; }
     }
   }
+  // Batch 1 with a 4-bit O matrix: the same 8-wave split kernel in chunks of
+  // 128 positions, then the plain merge writes o for the 4-bit O product.
+  const int w4_chunk = (ATTN_SPLIT8 && B == 1 && sizeof(T) == 2 && sizeof(KT) == 2 && w4.q4[3])
+                           ? attn_chunk((int)r.kvesz, S.hd, 8) : 0;
   a.no_merge = mo_chunk > 0;
   a.lmax = Lmax;
   a.part = (float*)(c->ws + L.part);
@@ -416,12 +420,13 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.prepped = prepped;
   HIPCHK(prof_pre(c, DUALAR_K_ATTN));
   bool split8 = false;
-  if (ATTN_SPLIT8 && mo_chunk && sizeof(KT) == 2) {
+  if (ATTN_SPLIT8 && (mo_chunk || w4_chunk) && sizeof(KT) == 2) {
     // batch 1, bf16 cache: the 8-wave split kernel (same partial layout)
     AttnParams b = a;
-    b.chunk = mo_chunk; b.max_splits = (Lmax + mo_chunk - 1) / mo_chunk;
+    b.chunk = mo_chunk ? mo_chunk : w4_chunk; b.max_splits = (Lmax + b.chunk - 1) / b.chunk;
     split8 = launch_attn_split_b1(b, c->stream);
     if (split8) HIPCHK(hipGetLastError());
+    if (split8 && !mo_chunk) HIPCHK(launch_attn_merge(b, c->stream));
   }
   if (!split8) HIPCHK((launch_attn<T, KT>(a, c->stream)));
   if (c->prof_cls == DUALAR_K_ATTN) {
@@ -836,7 +841,7 @@ dualar_status dualar_create(const dualar_config* cfg, const dualar_weights* w, v
       for (int j = 0; j < 7; ++j) {
         if (!a[i].q4[j]) continue;
         if (!P(a[i].q4[j]) || !P(a[i].s4[j])) return "a 4-bit matrix or its scales is NULL or not 16-byte aligned";
-        if (in[j] % 128) return "a 4-bit matrix's rows are not a whole number of 128-input groups";
+        if (in[j] % 512 || in[j] > 10240) return "a 4-bit matrix's rows must be a multiple of 512 inputs, at most 10,240";
       }
       if ((!a[i].q4[0]) != (!a[i].q4[1]) || (!a[i].q4[0]) != (!a[i].q4[2])) return "wq, wk, wv must be all 4-bit or all bf16";
       if ((!a[i].q4[4]) != (!a[i].q4[5])) return "w1 and w3 must both be 4-bit or both bf16";

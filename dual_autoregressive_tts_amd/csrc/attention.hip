@@ -701,6 +701,14 @@ __global__ void __launch_bounds__(MERGE_T) attn_merge_kernel(AttnParams p) {
   else p.out[(size_t)b * p.ld_out + (size_t)h * hd + t] = o / lsum;
 }
 
+// The plain merge alone, for a caller that ran its own split kernel with the
+// same partial layout (one slot of hd + 2 floats per head and split).
+hipError_t launch_attn_merge(const AttnParams& p, hipStream_t s) {
+  if (p.max_splits <= 1) return hipSuccess;   // the split kernel wrote o
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(p.B, p.H), dim3(MERGE_T), 0, s, p);
+  return hipGetLastError();
+}
+
 int attn_chunk(int kv_esz, int hd, int it) {
   const int lpp = hd * kv_esz / 16;
   return 4 * (64 / lpp) * it;

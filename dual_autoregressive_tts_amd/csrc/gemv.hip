@@ -566,13 +566,18 @@ __global__ void __launch_bounds__(DUALAR_WG) gemv_loop_kernel(GemvParams p) {
 // 4-bit weights (W4A16), one activation row
 // ---------------------------------------------------------------------------
 // Rows of K inputs as packed 4-bit two's-complement values (input 2j in the
-// low nibble of byte j) with a bf16 scale per group of 128 inputs.  Lane l
-// takes the 16-byte chunks c = l, l + 64, ... (32 inputs, inside one group)
-// of every row it owns; the weights and scales are loaded first, then the
-// (normalised) activation row is staged in LDS.  Per chunk, v' = v ^ 8
-// turns each nibble into v + 8 in [0, 15], whose bytes convert to floats in
-// one step, and the chunk adds scale * (sum v' x - 8 sum x) to its row; the
-// sum of x is shared by all rows of the lane.
+// low nibble of byte j) with a bf16 scale per group of 128 inputs.  A row is
+// read in units of 512 inputs: lane l takes dword l of each unit (inputs
+// 8l .. 8l+7, all in group l/16 of the unit), so one wave load covers 256
+// contiguous bytes of a row and every lane of a wave has work for any K that
+// is a multiple of 512.  As in the bf16 register-staged kernels, each lane
+// loads its activation (and gain) slice before its weights, and the RMSNorm
+// sum of squares is a wave reduction (with KS > 1 the KS waves of a row
+// group split the units and meet in LDS).  Per dword, t' = t ^ 8 turns each
+// nibble into v + 8 in [0, 15]; the low nibbles convert from their bytes,
+// the high ones from their bytes as 16 (v + 8) against activations
+// pre-divided by 16 (exact), and the lane adds scale * (sum t' x - 8 sum x)
+// to its row.
 template <int NR>
 __device__ __forceinline__ const char* w4_row(const GemvParams& p, int row, int s, const uint16_t** sc) {
   int seg = 0;
@@ -588,95 +593,193 @@ __device__ __forceinline__ const char* w4_row(const GemvParams& p, int row, int 
   return (const char*)q + (size_t)row * (p.K / 2);
 }
 
-template <int RPW, int NR, int CPL>
+template <int RPW, int NR, int NUP, int KS, bool RAG>
 __global__ void __launch_bounds__(DUALAR_WG) gemv_w4_kernel(GemvParams p) {
-  extern __shared__ float xs[];      // [K] the activation row
-  __shared__ float red[1][4];
+  // RAG: the units do not divide evenly among the KS waves, so the last
+  // wave's trailing units are dead (their loads are clamped, their x zeroed)
+  __shared__ float part[4][RPW][NR];
+  __shared__ float ssq[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * 4 + wave) * RPW;
-  const int nch = p.K / 32;
+  const int kp = wave % KS;
+  const int row0 = (blockIdx.x * (4 / KS) + wave / KS) * RPW;
+  const int U = p.K >> 9;
+  const int u0 = kp * NUP;
+  auto unit = [&](int u) { return RAG ? min(u0 + u, U - 1) : u0 + u; };
 
-  // 1. packed weights and their scales
-  u32x4 wq[RPW][NR][CPL];
-  uint32_t sc[RPW][NR][CPL];
+  // 1. activation slice (+ gain slice): inputs 8 (64 u + lane) .. + 7
+  float xv[NUP][8];
+#pragma unroll
+  for (int u = 0; u < NUP; ++u) {
+    const float* xb = p.x + (size_t)(unit(u) * 64 + lane) * 8;
+    const float4 a = *(const float4*)xb, b = *(const float4*)(xb + 4);
+    const bool live = !RAG || u0 + u < U;
+    xv[u][0] = live ? a.x : 0.f; xv[u][1] = live ? a.y : 0.f; xv[u][2] = live ? a.z : 0.f; xv[u][3] = live ? a.w : 0.f;
+    xv[u][4] = live ? b.x : 0.f; xv[u][5] = live ? b.y : 0.f; xv[u][6] = live ? b.z : 0.f; xv[u][7] = live ? b.w : 0.f;
+  }
+  u32x4 gv[NUP];
+  if (p.gain) {
+#pragma unroll
+    for (int u = 0; u < NUP; ++u) gv[u] = ld_vec((const char*)p.gain + (size_t)(unit(u) * 64 + lane) * 16);
+  }
+  // 2. packed weights and their scales
+  uint32_t wq[NUP][RPW][NR], sc[NUP][RPW][NR];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int row = min(row0 + r, p.n_out - 1);
 #pragma unroll
     for (int s = 0; s < NR; ++s) {
       const uint16_t* sb;
-      const char* qb = w4_row<NR>(p, row, s, &sb);
+      const uint32_t* qb = (const uint32_t*)w4_row<NR>(p, row, s, &sb);
+      if constexpr (!RAG) {
+        qb += u0 * 64 + lane;
+        sb += u0 * 4 + (lane >> 4);
+      }
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = min(lane + 64 * i, nch - 1);
-        wq[r][s][i] = ld_stream(qb + (size_t)c * 16);
-        sc[r][s][i] = sb[c / 4];
+      for (int u = 0; u < NUP; ++u) {
+        if constexpr (RAG) {
+          const int d = unit(u) * 64 + lane;
+          wq[u][r][s] = __builtin_nontemporal_load(qb + d);
+          sc[u][r][s] = sb[d >> 4];
+        } else {
+          wq[u][r][s] = __builtin_nontemporal_load(qb + 64 * u);
+          sc[u][r][s] = sb[4 * u];
+        }
       }
     }
   }
-  // 2. the activation row (+ RMSNorm * gain) in LDS
-  stage_x<bf16_t, 1>(p, xs, red, 0);
-
-  // 3. dot products chunk by chunk
+  // 3. RMSNorm: x * gain here, the 1 / rms factor on the finished sums
+  float inv = 1.f;
+  if (p.gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < NUP; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += xv[u][e] * xv[u][e];
+    ss = wave_sum(ss);
+    float tot = ss;
+    if constexpr (KS > 1) {
+      if (lane == 0) ssq[wave] = ss;
+      __syncthreads();
+      tot = 0.f;
+      for (int q = 0; q < KS; ++q) tot += ssq[wave - kp + q];
+    }
+    inv = 1.0f / sqrtf(tot / (float)p.K + p.eps);
+#pragma unroll
+    for (int u = 0; u < NUP; ++u) {
+      float g[8];
+      ElemT<bf16_t>::unpack(gv[u], g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[u][e] *= g[e];
+    }
+  }
+  // 4. -8 sum x per unit (shared by every row), odd inputs / 16
+  float m8[NUP];
+#pragma unroll
+  for (int u = 0; u < NUP; ++u) {
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t += xv[u][e];
+    m8[u] = -8.f * t;
+#pragma unroll
+    for (int e = 1; e < 8; e += 2) xv[u][e] *= 0.0625f;
+  }
+  // 5. dot products
   float acc[RPW][NR][1];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
     for (int s = 0; s < NR; ++s) acc[r][s][0] = 0.f;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= nch) break;
-    float xv[32];
-#pragma unroll
-    for (int e = 0; e < 32; e += 4) {
-      const float4 t = *(const float4*)&xs[32 * c + e];
-      xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
-    }
-    float sx = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) sx += xv[e];
+  for (int u = 0; u < NUP; ++u)
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
       for (int s = 0; s < NR; ++s) {
-        const u32x4 q = wq[r][s][i];
-        const uint32_t qd[4] = {q.x, q.y, q.z, q.w};
-        float d = 0.f;
+        const uint32_t t = wq[u][r][s] ^ 0x88888888u;
+        uint32_t lo = t & 0x0F0F0F0Fu, hi = t & 0xF0F0F0F0u;
+        // hide the known-zero bits, so that each byte converts in one
+        // v_cvt_f32_ubyte{0..3} rather than a bit-field extract and a convert
+        __asm__("" : "+v"(lo), "+v"(hi));
+        float d = m8[u];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t u = qd[k] ^ 0x88888888u;
-          const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            d = fmaf((float)((lo >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b], d);
-            d = fmaf((float)((hi >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b + 1], d);
-          }
+        for (int b = 0; b < 4; ++b) {
+          d = fmaf((float)((lo >> (8 * b)) & 0xFFu), xv[u][2 * b], d);
+          d = fmaf((float)((hi >> (8 * b)) & 0xFFu), xv[u][2 * b + 1], d);
         }
-        acc[r][s][0] = fmaf(bf16_bits_to_f32(sc[r][s][i]), d - 8.f * sx, acc[r][s][0]);
+        acc[r][s][0] = fmaf(bf16_bits_to_f32(sc[u][r][s]), d, acc[r][s][0]);
       }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int s = 0; s < NR; ++s) acc[r][s][0] *= inv;
+  if constexpr (KS == 1) {
+    gemv_epilogue<RPW, NR, 1>(p, acc, row0, 0);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        const float v = wave_sum(acc[r][s][0]);
+        if (lane == 0) part[wave][r][s] = v;
+      }
+    __syncthreads();
+    if (kp != 0 || lane != 0) return;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = row0 + r;
+      if (row >= p.n_out) continue;
+      float v[NR];
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        v[s] = 0.f;
+        for (int q = 0; q < KS; ++q) v[s] += part[wave + q][r][s];
+      }
+      float out;
+      if (p.mode == GEMV_SWIGLU) out = silu_f(v[0]) * v[NR - 1];
+      else if (p.mode == GEMV_ADD) out = p.res[row] + v[0];
+      else out = v[0];
+      p.y[row] = out;
+    }
   }
-  gemv_epilogue<RPW, NR, 1>(p, acc, row0, 0);
 }
 
-template <int NR, int CPL>
+#ifndef W4_RPW1
+#define W4_RPW1 2
+#endif
+#ifndef W4_RPW2
+#define W4_RPW2 2
+#endif
+
+template <int NR, int NUP, int KS>
 static hipError_t go_w4(const GemvParams& p, hipStream_t s) {
-  constexpr int RPW = 2;
-  dim3 grid((p.n_out + 4 * RPW - 1) / (4 * RPW));
-  launch_timed(gemv_w4_kernel<RPW, NR, CPL>, grid, dim3(DUALAR_WG), (uint32_t)(p.K * sizeof(float)), s, p);
+  constexpr int RPW = NR == 2 ? W4_RPW2 : W4_RPW1;
+  constexpr int rows = (4 / KS) * RPW;
+  const dim3 grid((p.n_out + rows - 1) / rows);
+  if (NUP * KS == p.K / 512)
+    launch_timed(gemv_w4_kernel<RPW, NR, NUP, KS, false>, grid, dim3(DUALAR_WG), 0, s, p);
+  else
+    launch_timed(gemv_w4_kernel<RPW, NR, NUP, KS, true>, grid, dim3(DUALAR_WG), 0, s, p);
   return hipGetLastError();
 }
 
+// Units per wave at most 5: one wave per row group up to 2,560 inputs, two
+// up to 5,120, four up to 10,240.
 template <int NR>
 static hipError_t launch_w4(const GemvParams& p, hipStream_t s) {
-  if (p.B != 1 || p.K % 128 || p.xplanes || p.yplanes) return hipErrorInvalidValue;
-  switch ((p.K / 32 + 63) / 64) {
-    case 1: return go_w4<NR, 1>(p, s);
-    case 2: return go_w4<NR, 2>(p, s);
-    case 3: return go_w4<NR, 3>(p, s);
-    case 4: return go_w4<NR, 4>(p, s);
-    case 5: return go_w4<NR, 5>(p, s);
-    default: return hipErrorInvalidValue;   // rows longer than 10,240 inputs
+  if (p.B != 1 || p.K % 512 || p.K > 10240 || p.xplanes || p.yplanes) return hipErrorInvalidValue;
+  const int U = p.K / 512;
+  switch (U) {
+    case 1: return go_w4<NR, 1, 1>(p, s);
+    case 2: return go_w4<NR, 2, 1>(p, s);
+    case 3: return go_w4<NR, 3, 1>(p, s);
+    case 4: return go_w4<NR, 4, 1>(p, s);
+    case 5: return go_w4<NR, 5, 1>(p, s);
+    case 6: return go_w4<NR, 3, 2>(p, s);
+    case 7: case 8: return go_w4<NR, 4, 2>(p, s);
+    case 9: case 10: return go_w4<NR, 5, 2>(p, s);
+    case 11: case 12: return go_w4<NR, 3, 4>(p, s);
+    case 13: case 14: case 15: case 16: return go_w4<NR, 4, 4>(p, s);
+    default: return go_w4<NR, 5, 4>(p, s);   // 17 .. 20 units
   }
 }
 

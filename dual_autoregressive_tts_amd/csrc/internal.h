@@ -145,6 +145,7 @@ int merge_o_b1_max_splits();
 bool launch_attn_split_b1(const AttnParams& p, hipStream_t s);
 hipError_t launch_merge_o_b1(const MergeOParams& p, hipStream_t s);
 int attn_chunk(int kv_esz, int hd, int it);
+hipError_t launch_attn_merge(const AttnParams& p, hipStream_t s);
 
 // Prefill of a chunk of positions: rows r = b*C + i hold position pos[r] of
 // sequence b (-1 = padding).  prefill_append_kernel applies QK-norm and RoPE

@@ -117,7 +117,8 @@ typedef struct {
  * low nibble of byte j, 2j+1 in the high one) and s4 its bf16 scales
  * [rows, in/128], one per row and group of 128 consecutive inputs; the
  * weight is q * scale.  Device pointers, 16-byte aligned.  wq/wk/wv must be
- * all 4-bit or all bf16, and so must w1/w3.  Only for bf16 models with
+ * all 4-bit or all bf16, and so must w1/w3.  A 4-bit matrix's rows must be
+ * a multiple of 512 inputs, at most 10,240.  Only for bf16 models with
  * max_batch = 1 and prefill_chunk = 1 (the products run as vector GEMVs);
  * dualar_create rejects other uses with DUALAR_ERR_INVALID_ARG. */
 typedef struct {

@@ -357,8 +357,9 @@ def _w4_case(m, seed, plen, frames, tag):
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("kv", ["bf16", "f32"])
 def test_w4a16_batch1_small(kv):
-    # rows of 512 and 1,024 inputs (one 16-byte chunk per lane); slow layer 0
-    # fully 4-bit, layer 1 keeps its attention in bf16; fast layers 4-bit
+    # rows of 512 and 1,024 inputs (one and two units of 512 per wave); slow
+    # layer 0 fully 4-bit, layer 1 keeps its attention in bf16; fast layers
+    # 4-bit (a head shape the split attention kernels do not take)
     m = synth.model("tiny", weight_dtype="bf16", kv_dtype=kv, dim=512, ffn_dim=1024, fast_dim=512,
                     fast_ffn_dim=1024, n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1,
                     fast_head_dim=128, w4a16=1, w4_bf16_attn_layers=1)
@@ -368,12 +369,14 @@ def test_w4a16_batch1_small(kv):
 
 @pytest.mark.timeout(900)
 def test_w4a16_batch1_s2_shapes():
-    # the S2 shapes (rows of 2,560 / 4,096 / 9,728 inputs: 2 and 5 chunks per
-    # lane) with 3 slow layers: layers 0-1 fully 4-bit, layer 2 keeps its
-    # attention in bf16 (so its O product takes the fused bf16 kernels), the
-    # fast layers 4-bit (their O product then runs beside a separate attention)
+    # the S2 shapes (rows of 2,560 / 4,096 / 9,728 inputs: 5 units of 512 in
+    # one wave, 8 over two waves, 19 over four with one dead unit) with 3 slow
+    # layers: layers 0-1 fully 4-bit, layer 2 keeps its attention in bf16 (so
+    # its O product takes the fused bf16 kernels), the fast layers 4-bit.  A
+    # 300-token prompt: the 4-bit-O slow layers attend in 3 splits of 128
+    # positions joined by the plain merge; the fast layers in one split.
     m = synth.model("s2", n_layer=3, w4a16=1, w4_bf16_attn_layers=1)
-    c, worst = _w4_case(m, 10, 40, 2, "w4-s2")
+    c, worst = _w4_case(m, 10, 300, 2, "w4-s2")
     assert sum(c) >= 2
 
 
