@@ -743,6 +743,206 @@ __global__ void __launch_bounds__(DUALAR_WG) gemv_w4_kernel(GemvParams p) {
   }
 }
 
+// 4-bit weights on the matrix cores (v_mfma_f32_16x16x32_bf16): a workgroup
+// owns 16 output rows (x NR segments) and its NWV waves split the row's
+// 128-input groups (chunks; one bf16 scale each) in ranges of NCH.  Per chunk
+// and segment, lane (q = lane / 16, n = lane % 16) loads 16 bytes of row n:
+// dwords 4q .. 4q+3, i.e. the 8-input octets 4q + i, i = 0..3.  Product step i
+// takes octet 4q + i from every lane: B = the 16 rows' weights (one dword,
+// eight nibbles, is one lane's fragment), A = the activation as three bf16
+// terms in rows 0..2 (rows 3..15 feed only D rows that are never read).  A
+// nibble t' = v + 8 becomes the exact bf16 128 + t' by a byte permute with
+// the constant byte 0x43, so the products give sum (136 + v) x; the
+// accumulator starts at -136 sum x for the chunk, and row n's chunk result
+// d0 + d1 + d2 is scaled into its sum.  The wave builds its own range's
+// activation terms in LDS (per product step: 4 octet slots x 3 terms x
+// 16 bytes), in the octet order the permute produces: inputs 0 2 4 6 1 3 5 7.
+// RMSNorm: the terms are of x * gain, and 1 / rms scales the finished sums.
+typedef __bf16 w4m_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float w4m_f32x4 __attribute__((ext_vector_type(4)));
+
+template <int NR, int NCH, int NWV>
+__global__ void __launch_bounds__(NWV * 64) gemv_w4m_kernel(GemvParams p) {
+  extern __shared__ u32x4 xa[];                 // [NWV][NCH * 4 steps][12 slots]
+  __shared__ float part[NWV][NR][16];
+  __shared__ float ssq[NWV];
+  __shared__ float sxs[NWV][NCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, n = lane & 15;
+  const int C = p.K >> 7;
+  const int c0 = wave * NCH;
+  const int cnt = min(NCH, C - c0);              // chunks of this wave (<= 0: none)
+  const int r0 = blockIdx.x * 16;
+  u32x4* xw = xa + (size_t)wave * NCH * 4 * 12;
+
+  // 1. activation octets of the wave's range: octet o -> lane o % 64, pass o / 64
+  constexpr int NO = (16 * NCH + 63) / 64;
+  float xv[NO][8];
+  u32x4 gv[NO];
+#pragma unroll
+  for (int it = 0; it < NO; ++it) {
+    const int o = lane + 64 * it;
+    const int og = min(max(16 * c0 + o, 0), 16 * C - 1);
+    const float* xb = p.x + (size_t)og * 8;
+    const float4 a = *(const float4*)xb, b = *(const float4*)(xb + 4);
+    xv[it][0] = a.x; xv[it][1] = a.y; xv[it][2] = a.z; xv[it][3] = a.w;
+    xv[it][4] = b.x; xv[it][5] = b.y; xv[it][6] = b.z; xv[it][7] = b.w;
+    if (p.gain) gv[it] = ld_vec((const char*)p.gain + (size_t)og * 16);
+  }
+  // 2. weights and scales of the 16 rows
+  u32x4 wq[NCH][NR];
+  uint32_t sc[NCH][NR];
+  {
+    const int row = min(r0 + n, p.n_out - 1);
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      const uint16_t* sb;
+      const char* qb = w4_row<NR>(p, row, s, &sb);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int cc = min(c0 + c, C - 1);
+        wq[c][s] = ld_stream(qb + (size_t)cc * 64 + q * 16);
+        sc[c][s] = sb[cc];
+      }
+    }
+  }
+  // 3. x * gain as three bf16 terms into LDS; chunk sums; sum of squares
+  float ss = 0.f;
+#pragma unroll
+  for (int it = 0; it < NO; ++it) {
+    const int o = lane + 64 * it;
+    const bool live = o < 16 * cnt;
+    float g[8];
+    if (p.gain) ElemT<bf16_t>::unpack(gv[it], g);
+    float sx = 0.f;
+    uint32_t t0[4], t1[4], t2[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      // fragment pair e2 holds inputs (2 e2, 2 e2 + 2) for e2 < 2, (2 e2 - 3, 2 e2 - 1) after
+      const int ea = e2 < 2 ? 4 * e2 : 4 * (e2 - 2) + 1, eb = ea + 2;
+      uint32_t h[2], m[2], l[2];
+      const int es[2] = {ea, eb};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float x = live ? xv[it][es[k]] : 0.f;
+        ss = fmaf(x, x, ss);
+        const float xg = p.gain ? x * g[es[k]] : x;
+        h[k] = f32_to_bf16_rne(xg);
+        const float r1 = xg - bf16_bits_to_f32(h[k]);
+        m[k] = f32_to_bf16_rne(r1);
+        const float r2 = r1 - bf16_bits_to_f32(m[k]);
+        l[k] = f32_to_bf16_rne(r2);
+        sx += bf16_bits_to_f32(h[k]) + bf16_bits_to_f32(m[k]) + bf16_bits_to_f32(l[k]);
+      }
+      t0[e2] = h[0] | (h[1] << 16);
+      t1[e2] = m[0] | (m[1] << 16);
+      t2[e2] = l[0] | (l[1] << 16);
+    }
+    if (live) {
+      const int j = o >> 4, oo = o & 15;         // local chunk, octet in the chunk
+      u32x4* slot = xw + (size_t)(4 * j + (oo & 3)) * 12 + (oo >> 2) * 3;
+      slot[0] = u32x4{t0[0], t0[1], t0[2], t0[3]};
+      slot[1] = u32x4{t1[0], t1[1], t1[2], t1[3]};
+      slot[2] = u32x4{t2[0], t2[1], t2[2], t2[3]};
+    }
+    sx = group_sum(sx, 16);                      // the 16 octets of chunk 4 it + q
+    if (n == 0 && 4 * it + q < cnt) sxs[wave][4 * it + q] = sx;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) ssq[wave] = ss;
+  __builtin_amdgcn_wave_barrier();               // xw, sxs[wave]: this wave's own
+  __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0): the LDS writes are done
+
+  // 4. the products
+  float acc[NR];
+#pragma unroll
+  for (int s = 0; s < NR; ++s) acc[s] = 0.f;
+  const int slot_a = q * 3 + min(n, 2);          // A row n (term n for n < 3), octet slot q
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c < cnt) {
+    const float m136 = -136.f * sxs[wave][c];
+    u32x4 av[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av[i] = xw[(size_t)(4 * c + i) * 12 + slot_a];
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      w4m_f32x4 d = {m136, 0.f, 0.f, 0.f};
+      const uint32_t wd[4] = {wq[c][s].x, wq[c][s].y, wq[c][s].z, wq[c][s].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t t = wd[i] ^ 0x88888888u;
+        const uint32_t lo = t & 0x0F0F0F0Fu, hi = (t >> 4) & 0x0F0F0F0Fu;
+        // bytes (v, 0x43, v', 0x43): two exact bf16 values 128 + t'
+        const u32x4 b = {__builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u),
+                         __builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u),
+                         __builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u),
+                         __builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u)};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(w4m_bf16x8, av[i]),
+                                                    __builtin_bit_cast(w4m_bf16x8, b), d, 0, 0, 0);
+      }
+      acc[s] = fmaf(bf16_bits_to_f32(sc[c][s]), (d[0] + d[1]) + d[2], acc[s]);
+    }
+    }
+  }
+  // 5. lanes 0..15 hold row n's partial sums; the waves meet in LDS
+  if (q == 0) {
+#pragma unroll
+    for (int s = 0; s < NR; ++s) part[wave][s][n] = acc[s];
+  }
+  __syncthreads();
+  if (threadIdx.x >= 16) return;
+  const int row = r0 + threadIdx.x;
+  if (row >= p.n_out) return;
+  float inv = 1.f;
+  if (p.gain) {
+    float tot = 0.f;
+    for (int w = 0; w < NWV; ++w) tot += ssq[w];
+    inv = 1.0f / sqrtf(tot / (float)p.K + p.eps);
+  }
+  float v[NR];
+#pragma unroll
+  for (int s = 0; s < NR; ++s) {
+    v[s] = 0.f;
+    for (int w = 0; w < NWV; ++w) v[s] += part[w][s][threadIdx.x];
+    v[s] *= inv;
+  }
+  float out;
+  if (p.mode == GEMV_SWIGLU) out = silu_f(v[0]) * v[NR - 1];
+  else if (p.mode == GEMV_ADD) out = p.res[row] + v[0];
+  else out = v[0];
+  p.y[row] = out;
+}
+
+#ifndef W4_MFMA
+#define W4_MFMA 1
+#endif
+
+template <int NR, int NCH, int NWV>
+static hipError_t go_w4m(const GemvParams& p, hipStream_t s) {
+  const size_t lds = (size_t)NWV * NCH * 4 * 12 * 16;
+  launch_timed(gemv_w4m_kernel<NR, NCH, NWV>, dim3((p.n_out + 15) / 16), dim3(NWV * 64), (uint32_t)lds, s, p);
+  return hipGetLastError();
+}
+
+// Chunks of 128 inputs per row: 20 (2,560), 32 (4,096), 76 (9,728).  The
+// matrix-core form serves the single-segment products (QKV, O, W2: 6.00 /
+// 5.70 / 8.56 us at the S2 shapes against 6.54 / 5.86 / 8.73 us for the
+// VALU form, with 8 or 16 waves per workgroup; 4 waves were slower); the
+// gate|up product stays on the VALU form (11.2 us against 12.0 / 12.5 us).
+template <int NR>
+static bool launch_w4m(const GemvParams& p, hipStream_t s, hipError_t* e) {
+  if (!W4_MFMA || NR != 1 || p.B != 1 || p.K % 128 || p.xplanes || p.yplanes) return false;
+  if constexpr (NR == 1) {
+    const int C = p.K / 128;
+    if (C <= 24) { *e = go_w4m<1, 3, 8>(p, s); return true; }
+    if (C <= 32) { *e = go_w4m<1, 2, 16>(p, s); return true; }
+    if (C <= 48) { *e = go_w4m<1, 3, 16>(p, s); return true; }
+    if (C <= 80) { *e = go_w4m<1, 5, 16>(p, s); return true; }
+  }
+  return false;
+}
+
 #ifndef W4_RPW1
 #define W4_RPW1 2
 #endif
@@ -892,6 +1092,8 @@ template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s)
   if (p.q4[0]) {
     if constexpr (sizeof(T) != 2) return hipErrorInvalidValue;
     if (p.next_done) *p.next_done = 0;
+    hipError_t e;
+    if (p.mode != GEMV_SWIGLU && launch_w4m<1>(p, s, &e)) return e;
     return p.mode == GEMV_SWIGLU ? launch_w4<2>(p, s) : launch_w4<1>(p, s);
   }
   if constexpr (sizeof(T) == 2) {
