@@ -43,37 +43,42 @@ WORKLOADS = {
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-# HBM bytes per dispatch of the roofline kernel (the batch-1 SwiGLU W1|W3
-# GEMV), from rocprofv3 --pmc runs of `bench.py --steps 4 --warmup 2
-# --profile-frames 0 --no-cpu-baseline` restricted to gemv_rx_kernel:
-# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) times the factor the same
-# counter reads for a plain 1 GiB device copy (bench.py --copy-calibration).
-# The figures hold for the kernel text they were taken on: if the source of
-# gemv_rx_kernel changes, `traffic` is reported as null until they are
-# measured again.
+# HBM bytes per dispatch of the roofline kernels (the batch-1 SwiGLU W1|W3
+# GEMV: bf16 `gemv_rx_kernel`, 4-bit `gemv_w4_kernel`), from rocprofv3 --pmc
+# runs restricted to that kernel (bf16: `bench.py --steps 4 --warmup 2
+# --profile-frames 0 --no-cpu-baseline`; 4-bit: the same with `--workload
+# s2_b1_w4 --prompt-len 16`): FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+# times the factor the same counter reads for a plain 1 GiB device copy
+# (bench.py --copy-calibration).  The figures hold for the kernel text they
+# were taken on: if a kernel's source changes, `traffic` is reported as null
+# until they are measured again.
+_FETCH_SCALE = 1073741824 / 1024 / 524300.3125
+_WRITE_SCALE = 1073741824 / 1024 / 1048576.0
 ROOFLINE_COUNTERS = {
-    "fetch_kib": 48746.695, "fetch_scale": 1073741824 / 1024 / 524300.3125,
-    "write_kib": 38.05, "write_scale": 1073741824 / 1024 / 1048576.0,
+    "gemv_rx_kernel": {"fetch_kib": 48746.695, "write_kib": 38.05,
+                       "sha256": "896f099c92dd1480f9cae59c9e461a974a00feaeec347ad0b0be964cd656bd96"},
+    "gemv_w4_kernel": {"fetch_kib": 12721.425, "write_kib": 38.0,
+                       "sha256": "56e7cfaa8dc156927292197036e869ffd7b4068527330939f40693f0a8368b6e"},
 }
-ROOFLINE_KERNEL_SHA256 = "896f099c92dd1480f9cae59c9e461a974a00feaeec347ad0b0be964cd656bd96"
 
 
-def _gemv_rx_source_sha256():
+def kernel_source_sha256(name):
+    """SHA-256 of a kernel's text in gemv.hip: its template line to its closing brace."""
     import hashlib
     src = open(os.path.join(ROOT, "dual_autoregressive_tts_amd", "csrc", "gemv.hip")).read()
-    i = src.index("__global__ void __launch_bounds__(DUALAR_WG) gemv_rx_kernel(")
+    i = src.index(f"__global__ void __launch_bounds__(DUALAR_WG) {name}(")
     i = src.rindex("template", 0, i)
     j = src.index("\n}\n", i) + 3
     return hashlib.sha256(src[i:j].encode()).hexdigest()
 
 
-def roofline_traffic():
-    """Measured HBM bytes per launch of the roofline kernel, or None when
-    they are incomplete or were taken on other kernel text."""
-    c = ROOFLINE_COUNTERS
-    if c["write_kib"] is None or _gemv_rx_source_sha256() != ROOFLINE_KERNEL_SHA256:
+def roofline_traffic(name="gemv_rx_kernel"):
+    """Measured HBM bytes per launch of a roofline kernel, or None when they
+    are missing or were taken on other kernel text."""
+    c = ROOFLINE_COUNTERS.get(name)
+    if not c or c["write_kib"] is None or kernel_source_sha256(name) != c["sha256"]:
         return None
-    return round(c["fetch_kib"] * 1024 * c["fetch_scale"] + c["write_kib"] * 1024 * c["write_scale"])
+    return round(c["fetch_kib"] * 1024 * _FETCH_SCALE + c["write_kib"] * 1024 * _WRITE_SCALE)
 
 
 def log(*a):
@@ -377,7 +382,8 @@ def main():
                     "kernel": kname,
                     "achieved": round(sw_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(sw_gbps / HBM_PEAK_GBPS, 4),
-                    "traffic": roofline_traffic() if (B == 1 and m["weight_dtype"] == "bf16" and not w4) else None,
+                    "traffic": (roofline_traffic("gemv_w4_kernel") if w4 else roofline_traffic("gemv_rx_kernel")
+                                if (B == 1 and m["weight_dtype"] == "bf16") else None),
                     "avg_launch_us": round(sw_avg_us, 3), "bytes_per_launch": round(sw_bytes),
                     "launches_profiled": f["launches"],
                     "gemv_family": {"achieved_GBps": round(gemv_gbps, 1), "avg_launch_us": round(gemv_avg_us, 3),

@@ -106,6 +106,17 @@ def test_roofline_traffic_follows_the_measured_kernel(monkeypatch):
     assert bench.roofline_traffic() is None
 
 
+def test_w4_roofline_traffic_reads_weights_once():
+    # the 4-bit W1|W3 kernel's counters: 4-bit weights, bf16 scales, x, out
+    import bench
+    t = bench.roofline_traffic("gemv_w4_kernel")
+    assert t is not None
+    algo = 2 * 9728 * 2560 // 2 + 2 * 9728 * 20 * 2 + 4 * 2560 + 4 * 9728
+    assert algo == 25731072
+    assert algo <= t <= 1.02 * algo
+    assert bench.roofline_traffic("no_such_kernel") is None
+
+
 def test_w4_frame_bytes_by_enumeration():
     # the 4-bit byte change of a frame-step against a direct count over the
     # model's tensors: every 4-bit matrix costs rows * (K/2 + K/128 * 2) bytes
