@@ -1030,6 +1030,9 @@ static hipError_t go_wide(const GemvParams& p, hipStream_t s) {
 #ifndef WIDE_W2_NW
 #define WIDE_W2_NW 10
 #endif
+#ifndef WIDE_W2_R
+#define WIDE_W2_R 10
+#endif
 
 // One activation row of bf16 rows of 2560 / 4096 / 9728: the variants that
 // measured fastest for each S2 matrix (rows per wave, k-split; or the wide
@@ -1044,7 +1047,7 @@ static bool pick_b1(const GemvParams& p, hipStream_t s, hipError_t* e) {
       const int units = p.K / 512;
       if constexpr (NR == 1) {
         if (units == 8 && p.n_out == 2560) { *e = go_wide<8, WIDE_O_R, 1, 8>(p, s); return true; }        // O
-        if (units == 19 && p.n_out == 2560) { *e = go_wide<WIDE_W2_NW, 10, 1, 19>(p, s); return true; }  // W2
+        if (units == 19 && p.n_out == 2560) { *e = go_wide<WIDE_W2_NW, WIDE_W2_R, 1, 19>(p, s); return true; }  // W2
       }
     }
     const int units = p.K / (64 * ElemT<T>::EPV);
