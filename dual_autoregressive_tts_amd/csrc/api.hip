@@ -207,16 +207,6 @@ struct dualar_ctx {
 
 namespace {
 
-#ifndef MERGE_O_IT_FIRST
-#define MERGE_O_IT_FIRST 8   // loads per lane of the split form tried first (8 or 16)
-#endif
-#ifndef MERGE_O_FUSE
-#define MERGE_O_FUSE 1
-#endif
-#ifndef ATTN_SPLIT8
-#define ATTN_SPLIT8 1
-#endif
-
 dualar_status fail(dualar_ctx* c, dualar_status s, const std::string& m) {
   if (c) c->err = m; else g_create_err = m;
   return s;
@@ -401,15 +391,15 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   // merge_o_b1_max_splits() chunks of 128 or 256 positions, its merge done by
   // the O product (each lane merges the eight values it multiplies).
   int mo_chunk = 0;
-  if (MERGE_O_FUSE && B == 1 && pos_dev && sizeof(T) == 2 && !w4.q4[3] && attn_o_b1_fits(S.H, S.KV, S.hd, S.dim, 1)) {
-    for (int it : {MERGE_O_IT_FIRST, 24 - MERGE_O_IT_FIRST}) {
+  if (B == 1 && pos_dev && sizeof(T) == 2 && !w4.q4[3] && attn_o_b1_fits(S.H, S.KV, S.hd, S.dim, 1)) {
+    for (int it : {8, 16}) {   // 128-position chunks, else 256
       const int ch = attn_chunk((int)r.kvesz, S.hd, it);
       if ((Lmax + ch - 1) / ch <= merge_o_b1_max_splits()) { a.it = it; mo_chunk = ch; break; }
     }
   }
   // Batch 1 with a 4-bit O matrix: the same 8-wave split kernel in chunks of
   // 128 positions, then the plain merge writes o for the 4-bit O product.
-  const int w4_chunk = (ATTN_SPLIT8 && B == 1 && sizeof(T) == 2 && sizeof(KT) == 2 && w4.q4[3])
+  const int w4_chunk = (B == 1 && sizeof(T) == 2 && sizeof(KT) == 2 && w4.q4[3])
                            ? attn_chunk((int)r.kvesz, S.hd, 8) : 0;
   a.no_merge = mo_chunk > 0;
   a.lmax = Lmax;
@@ -420,7 +410,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.prepped = prepped;
   HIPCHK(prof_pre(c, DUALAR_K_ATTN));
   bool split8 = false;
-  if (ATTN_SPLIT8 && (mo_chunk || w4_chunk) && sizeof(KT) == 2) {
+  if ((mo_chunk || w4_chunk) && sizeof(KT) == 2) {
     // batch 1, bf16 cache: the 8-wave split kernel (same partial layout)
     AttnParams b = a;
     b.chunk = mo_chunk ? mo_chunk : w4_chunk; b.max_splits = (Lmax + b.chunk - 1) / b.chunk;

@@ -714,9 +714,6 @@ int attn_chunk(int kv_esz, int hd, int it) {
   return 4 * (64 / lpp) * it;
 }
 
-#ifndef ATTN_DEPTH
-#define ATTN_DEPTH 1
-#endif
 #define FL_SLOTS 512   // workgroups of the balanced flash-decoding form (two per compute unit)
 
 // Batched attention over a short cache (at most 16 positions: the fast AR's
@@ -830,7 +827,7 @@ template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p0, 
   if constexpr (sizeof(KT) == 2) {
     // the balanced flash-decoding form: bf16 cache, head_dim 128, batched
     // contexts of at most 16 positions (the depth cache): one wave per (row, KV head)
-    if (!p.no_merge && p.hd == 128 && p.it >= 8 && p.q_planes && rep == 4 && p.lmax <= 16 && ATTN_DEPTH) {
+    if (!p.no_merge && p.hd == 128 && p.it >= 8 && p.q_planes && rep == 4 && p.lmax <= 16) {
       if (!p.prepped) hipLaunchKernelGGL((attn_prep_kernel<T, KT>), dim3(p.B, p.H + p.KV), dim3(64), 0, s, p);
       hipLaunchKernelGGL(attn_depth_kernel, dim3(p.B * p.KV), dim3(64), 0, s, p);
       return hipGetLastError();

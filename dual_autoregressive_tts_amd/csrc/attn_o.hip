@@ -241,9 +241,9 @@ __global__ void __launch_bounds__(WGT) attn_o_b1_kernel(AttnOParams p) {
   }
 }
 
-#ifndef ATTN_O_ROWS
-#define ATTN_O_ROWS 10
-#endif
+// 10 rows of W_o per workgroup: 256 workgroups of 8 waves, about one per
+// compute unit (5 and 20 rows were slower).
+constexpr int ATTN_O_ROWS = 10;
 
 bool attn_o_b1_fits(int H, int KV, int hd, int dim, int L) {
   return KV == NW && H == NW * REP && hd == HD && L >= 1 && L <= MAXL && dim > 0;
@@ -349,9 +349,9 @@ __global__ void __launch_bounds__(WGT) merge_o_b1_kernel(MergeOParams p) {
   }
 }
 
-#ifndef MERGE_O_MAXS
-#define MERGE_O_MAXS 10
-#endif
+// At most 10 splits merged inside the O product (the split kernel's chunks
+// grow from 128 to 256 positions past 1,280 positions to stay within it).
+constexpr int MERGE_O_MAXS = 10;
 
 int merge_o_b1_max_splits() { return MERGE_O_MAXS; }
 

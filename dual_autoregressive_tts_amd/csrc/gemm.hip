@@ -35,9 +35,6 @@
 
 #define GM_KC 64                     // k per chunk
 #define GM_STAGES 3
-#ifndef GM_SK_CFG
-#define GM_SK_CFG 15                 // stream-K shape of the decode products (11..15)
-#endif
 #define GM_TILE_ROWS 256             // from this many activation rows: 2-D tiles (gemm_tile.hip)
 
 // Workgroup shape: WAVES waves, each owning T 32-row output tiles (times NR
@@ -442,98 +439,10 @@ struct Sk {
   static constexpr int TE = NR * 32 * ROWS;                 // floats per partial tile
 };
 
-// Grid G (= sk_q*G + sk_r units), THREADS threads, STG copy stages.
-template <int NR, int WAVES, int T, int STG>
-__global__ void __launch_bounds__(64 * WAVES) mfma_sk_kernel(GemvParams p) {
-  using G = Gm<NR, WAVES, T>;
-  static_assert(STG == 3 || STG == 4, "stages");
-  __shared__ __attribute__((aligned(1024))) char lds[STG][G::STAGE];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = blockIdx.x, q = p.sk_q, rr = p.sk_r, nch = p.sk_nch;
-  const int u0 = g * q + min(g, rr);
-  const int nf = q + (g < rr ? 1 : 0);
-  if (nf == 0) return;
-  const int Z = (p.B + 31) / 32;
-
-  // issue side: tile / chunk of the next chunk to copy
-  int it = u0 / nch, ic = u0 % nch;
-  // compute side: tile / chunk of the next chunk to multiply
-  int ct = it, cc = ic;
-  GmSrc<G> src;
-  gm_sources<NR, G>(p, src, (it / Z) * G::ROWS, (it % Z) * 32, 0, wave, lane);
-  auto issue = [&](char* stage) {
-    gm_issue<G>(src, stage, ic, wave);
-    if (++ic == nch) {
-      ic = 0;
-      ++it;
-      gm_sources<NR, G>(p, src, (it / Z) * G::ROWS, (it % Z) * 32, 0, wave, lane);
-    }
-  };
-
-  f32x16 acc[T][NR][3];
-#pragma unroll
-  for (int tt = 0; tt < T; ++tt)
-#pragma unroll
-    for (int s = 0; s < NR; ++s)
-#pragma unroll
-      for (int j = 0; j < 3; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tt][s][j][r] = 0.f;
-
-#pragma unroll
-  for (int s = 0; s < STG - 1; ++s)
-    if (s < nf) issue(lds[s]);
-
-  bool drain = false;   // partial-sum stores are in flight: wait for everything
-  for (int f0 = 0; f0 < nf; f0 += STG) {
-#pragma unroll
-    for (int s = 0; s < STG; ++s) {
-      const int f = f0 + s;
-      if (f >= nf) break;
-      // chunks copied so far: min(nf, f + STG - 1); those after f may stay in flight
-      const int ahead = min(nf - 1 - f, STG - 2);
-      if (drain || ahead == 0) wait_vm_barrier<0>();
-      else if (ahead == 1) wait_vm_barrier<G::DMA>();
-      else wait_vm_barrier<2 * G::DMA>();
-      drain = false;
-      if (f + STG - 1 < nf) issue(lds[(s + STG - 1) % STG]);
-      gm_compute<NR, T, G>(lds[s], wave, lane, acc);
-      if (++cc == nch || f == nf - 1) {
-        const int slot = g - sk_owner(ct * nch, q, rr);
-        float* dst = p.part + ((size_t)ct * p.sk_smax + slot) * Sk<NR, WAVES, T>::TE;
-        // register r of lane l holds tile row (r/4)*8 + (l/32)*4 + r%4 of
-        // the wave's 32-row block, activation row l % 32
-#pragma unroll
-        for (int tt = 0; tt < T; ++tt)
-#pragma unroll
-          for (int sN = 0; sN < NR; ++sN) {
-            float* d = dst + (size_t)(sN * 32 + (lane & 31)) * G::ROWS + 32 * (wave * T + tt) + 4 * (lane >> 5);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float4 v;
-              v.x = acc[tt][sN][0][4 * j + 0] + (acc[tt][sN][1][4 * j + 0] + acc[tt][sN][2][4 * j + 0]);
-              v.y = acc[tt][sN][0][4 * j + 1] + (acc[tt][sN][1][4 * j + 1] + acc[tt][sN][2][4 * j + 1]);
-              v.z = acc[tt][sN][0][4 * j + 2] + (acc[tt][sN][1][4 * j + 2] + acc[tt][sN][2][4 * j + 2]);
-              v.w = acc[tt][sN][0][4 * j + 3] + (acc[tt][sN][1][4 * j + 3] + acc[tt][sN][2][4 * j + 3]);
-              *(float4*)(d + 8 * j) = v;
-            }
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[tt][sN][j][r] = 0.f;
-          }
-        drain = true;
-        cc = 0;
-        ++ct;
-      }
-    }
-  }
-}
-
-// Wave-specialised stream-K.  In mfma_sk_kernel every LDS stage holds a
-// weight chunk and the 12 KB of activation planes it is multiplied with, and
-// a wave's copies complete in issue order, so at most 48-64 KB of weights
-// are ever in flight per compute unit.  Here WAVES compute waves copy only
+// Wave-specialised stream-K.  A form whose LDS stages each hold a weight
+// chunk and the 12 KB of activation planes it is multiplied with keeps at
+// most 48-64 KB of weights in flight per compute unit, because a wave's
+// copies complete in issue order.  Here WAVES compute waves copy only
 // the weight chunks (WS stages, WS - 1 chunks ahead) and multiply, and one
 // more wave copies only the planes (XS slots, XS - 1 chunks ahead): each
 // wave's vmcnt then counts one kind of copy, waiting for a chunk's planes
@@ -544,8 +453,7 @@ __global__ void __launch_bounds__(64 * WAVES) mfma_sk_kernel(GemvParams p) {
 // behind every weight chunk in flight (batch 32: weights 2 chunks ahead and
 // planes 1 ahead took 36.8 us for W1|W3, both 2 ahead 33.9 us; for the
 // other products 4 and 4 matched 5 and 3, 6 and 4).  One barrier per chunk
-// for all waves; the partial tiles and their finish are those of
-// mfma_sk_kernel.
+// for all waves; the partial tiles are laid out as described above.
 template <int NR, int WAVES, int T, int WS, int XS>
 struct Skw {
   using G = Gm<NR, WAVES, T>;
@@ -922,18 +830,6 @@ static bool launch_skw(GemvParams& p, hipStream_t s) {
   return true;
 }
 
-// Plans and launches the stream-K form; false when it does not apply (no
-// partial buffer, or the partial tiles do not fit it).  `slots` = workgroups
-// the chip holds at once.
-template <int NR, int WAVES, int T, int STG>
-static bool launch_sk(GemvParams& p, int slots, hipStream_t s) {
-  int ng = 0;
-  if (!sk_plan<NR, WAVES, T>(p, slots, &ng)) return false;
-  hipLaunchKernelGGL((mfma_sk_kernel<NR, WAVES, T, STG>), dim3(ng), dim3(64 * WAVES), 0, s, p);
-  sk_finish<NR, WAVES, T>(p, s);
-  return true;
-}
-
 template <int NR, int WAVES, int T>
 static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, bool* ok) {
   using G = Gm<NR, WAVES, T>;
@@ -980,44 +876,28 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   if (p.xplanes) p.xn = const_cast<void*>(p.xplanes);   // input already split by its producer
   else hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
   bool ok = false;
-  int cfg = p0.gm_cfg;
   const bool glu = p.mode == GEMV_SWIGLU;
   const int z_tiles = (p.B + 31) / 32;
-  if (!cfg && p.B >= GM_TILE_ROWS) cfg = 20 + gemm_tile_choice(p);
-  if (cfg >= 21 && cfg <= 24) {   // 2-D output tiles (prefill steps)
+  if (p.B >= GM_TILE_ROWS) {   // 2-D output tiles (prefill steps)
     if (p.prep_done) *p.prep_done = 0;
     if (p.next_done) *p.next_done = 0;
-    *err = launch_gemm_tile(p, cfg - 20, s) ? hipGetLastError() : hipErrorInvalidValue;
+    *err = launch_gemm_tile(p, gemm_tile_wide(p), s) ? hipGetLastError() : hipErrorInvalidValue;
     return true;
   }
-  if (!cfg) {
-    // stream-K for the decode shapes; the tall head (hundreds of row tiles)
-    // balances well as it is and its partials would be as large as its output
-    if (z_tiles <= 2 && p.K / GM_KC >= 8 && p0.ksw == 0 && p.n_out < 16384) cfg = GM_SK_CFG;
-    else cfg = glu ? 2 : (p.n_out >= 16384 ? 3 : 1);
-  }
-  if (cfg >= 11) {   // stream-K shapes (slots: one 4-wave workgroup per compute unit)
-    bool done = false;
-    switch (cfg) {
-      case 11: done = glu ? launch_sk<2, 4, 1, 3>(p, 256, s) : launch_sk<1, 4, 1, 4>(p, 256, s); break;
-      case 12: done = glu ? false : launch_sk<1, 4, 2, 3>(p, 256, s); break;
-      case 13: done = glu ? launch_sk<2, 2, 1, 3>(p, 256, s) : launch_sk<1, 2, 1, 4>(p, 512, s); break;
-      case 14: done = glu ? false : launch_sk<1, 4, 1, 3>(p, 256, s); break;
-      case 15: done = glu ? launch_skw<2, 4, 1, 3, 3>(p, s) : launch_skw<1, 4, 1, 5, 5>(p, s); break;
-      default: break;
-    }
-    if (done) {
+  // Stream-K (wave-specialised, one workgroup per compute unit) for the
+  // decode shapes; the tall head (hundreds of row tiles) balances well as it
+  // is and its partials would be as large as its output.
+  if (z_tiles <= 2 && p.K / GM_KC >= 8 && p0.ksw == 0 && p.n_out < 16384) {
+    if (glu ? launch_skw<2, 4, 1, 3, 3>(p, s) : launch_skw<1, 4, 1, 5, 5>(p, s)) {
       *err = hipGetLastError();
       return true;
     }
-    if (p0.gm_cfg) {
-      *err = hipErrorInvalidValue;
-      return true;
-    }
-    cfg = glu ? 2 : (p.n_out >= 16384 ? 3 : 1);   // partial tiles do not fit: split-K form
+    // partial tiles do not fit the partial buffer: the split-K form below
   }
+  // split-K form: (NR, WAVES, T), slots = workgroups the chip holds at once (LDS bound)
+  const int cfg = glu ? 2 : (p.n_out >= 16384 ? 3 : 1);
   if (p.prep_done) *p.prep_done = 0;
-  switch (cfg) {   // (NR, WAVES, T), slots = workgroups the chip holds at once (LDS bound)
+  switch (cfg) {
     case 1: if (glu) launch_gm<2, 2, 1>(p, p0.ksw, 256, s, &ok); else launch_gm<1, 2, 1>(p, p0.ksw, 512, s, &ok); break;
     case 2: if (glu) launch_gm<2, 4, 1>(p, p0.ksw, 256, s, &ok); else launch_gm<1, 4, 1>(p, p0.ksw, 256, s, &ok); break;
     case 3: if (!glu) launch_gm<1, 4, 2>(p, p0.ksw, 256, s, &ok); break;

@@ -244,12 +244,11 @@ __global__ void __launch_bounds__(64 * GN * GW, 1) mfma_tile_kernel(GemvParams p
   }
 }
 
-// Launch the tiled product: cfg 1: 256 weight rows x 128 activation rows, 4
-// waves; cfg 2: 128 x 128, 4 waves; cfg 3: 256 x 128, 8 waves of 64 x 64;
-// cfg 4: 512 x 128, 8 waves of 128 x 64, two stages.
-// The input planes are at p.xn.  Returns false when the shape does not
-// apply.
-bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
+// Launch the tiled product: the 8-wave 256 x 128 tile (waves of 64 x 64),
+// or with `wide` the 8-wave 512 x 128 tile (waves of 128 x 64, two
+// stages).  The input planes are at p.xn.  Returns false when the shape does
+// not apply.
+bool launch_gemm_tile(const GemvParams& p, bool wide, hipStream_t s) {
   if (p.K % TL_KC != 0 || p.B < 1 || p.n_out < 1) return false;
   const int tb = p.bt_masked ? __builtin_popcountll(p.live_bt[0]) + __builtin_popcountll(p.live_bt[1])
                             : (p.B + GEMM_TILE_BROWS - 1) / GEMM_TILE_BROWS;
@@ -259,20 +258,17 @@ bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s) {
     const int tiles = ((p.n_out + cols - 1) / cols) * tb;
     return dim3(8 * ((tiles + 7) / 8));
   };
-  switch (cfg) {
-    case 1: hipLaunchKernelGGL((mfma_tile_kernel<4, 2, 2, 2>), grid(256), dim3(256), 0, s, p); return true;
-    case 2: hipLaunchKernelGGL((mfma_tile_kernel<2, 2, 2, 2>), grid(128), dim3(256), 0, s, p); return true;
-    case 3: hipLaunchKernelGGL((mfma_tile_kernel<2, 2, 4, 2>), grid(256), dim3(512), 0, s, p); return true;
-    case 4: hipLaunchKernelGGL((mfma_tile_kernel<4, 2, 4, 2, 2>), grid(512), dim3(512), 0, s, p); return true;
-    default: return false;
-  }
+  if (wide) hipLaunchKernelGGL((mfma_tile_kernel<4, 2, 4, 2, 2>), grid(512), dim3(512), 0, s, p);
+  else hipLaunchKernelGGL((mfma_tile_kernel<2, 2, 4, 2>), grid(256), dim3(512), 0, s, p);
+  return true;
 }
 
 // Tile shape for a product.  The 8-wave 256 x 128 tile (two waves per SIMD,
 // so one wave's LDS waits and barrier hide under the other's products) ran
 // the S2 prefill products at 37-48 % of the matrix-core peak over the three
-// terms, against 30-41 % for the 4-wave tiles at any shape.  Wide products
-// take the 8-wave 512 x 128 tile (waves of 128 x 64 read 0.42 KB of operand
-// fragments per product instead of 0.67 KB; two stages to fit LDS): 2-3 %
-// faster there; on 2,560 output rows it would leave a quarter round.
-int gemm_tile_choice(const GemvParams& p) { return p.n_out >= 4096 ? 4 : 3; }
+// terms, against 30-41 % for 4-wave tiles (256 or 128 weight rows) at any
+// shape.  Wide products take the 8-wave 512 x 128 tile (waves of 128 x 64
+// read 0.42 KB of operand fragments per product instead of 0.67 KB; two
+// stages to fit LDS): 2-3 % faster there; on 2,560 output rows it would leave
+// a quarter round.
+bool gemm_tile_wide(const GemvParams& p) { return p.n_out >= 4096; }

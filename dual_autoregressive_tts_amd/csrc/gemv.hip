@@ -914,10 +914,6 @@ __global__ void __launch_bounds__(NWV * 64) gemv_w4m_kernel(GemvParams p) {
   p.y[row] = out;
 }
 
-#ifndef W4_MFMA
-#define W4_MFMA 1
-#endif
-
 template <int NR, int NCH, int NWV>
 static hipError_t go_w4m(const GemvParams& p, hipStream_t s) {
   const size_t lds = (size_t)NWV * NCH * 4 * 12 * 16;
@@ -932,7 +928,7 @@ static hipError_t go_w4m(const GemvParams& p, hipStream_t s) {
 // gate|up product stays on the VALU form (11.2 us against 12.0 / 12.5 us).
 template <int NR>
 static bool launch_w4m(const GemvParams& p, hipStream_t s, hipError_t* e) {
-  if (!W4_MFMA || NR != 1 || p.B != 1 || p.K % 128 || p.xplanes || p.yplanes) return false;
+  if (NR != 1 || p.B != 1 || p.K % 128 || p.xplanes || p.yplanes) return false;
   if constexpr (NR == 1) {
     const int C = p.K / 128;
     if (C <= 24) { *e = go_w4m<1, 3, 8>(p, s); return true; }
@@ -943,16 +939,11 @@ static bool launch_w4m(const GemvParams& p, hipStream_t s, hipError_t* e) {
   return false;
 }
 
-#ifndef W4_RPW1
-#define W4_RPW1 2
-#endif
-#ifndef W4_RPW2
-#define W4_RPW2 2
-#endif
-
+// Two rows per wave for every 4-bit product (4 rows per wave measured slower
+// for each of them: 3.24-3.44 ms per frame against 3.17).
 template <int NR, int NUP, int KS>
 static hipError_t go_w4(const GemvParams& p, hipStream_t s) {
-  constexpr int RPW = NR == 2 ? W4_RPW2 : W4_RPW1;
+  constexpr int RPW = 2;
   constexpr int rows = (4 / KS) * RPW;
   const dim3 grid((p.n_out + rows - 1) / rows);
   if (NUP * KS == p.K / 512)
@@ -1015,47 +1006,30 @@ static hipError_t go_wide(const GemvParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-#ifndef GEMV_WIDE
-#define GEMV_WIDE 1
-#endif
-#ifndef B1_QKV_RPW
-#define B1_QKV_RPW 3
-#endif
-#ifndef B1_W13_RPW
-#define B1_W13_RPW 2
-#endif
-#ifndef WIDE_O_R
-#define WIDE_O_R 10
-#endif
-#ifndef WIDE_W2_NW
-#define WIDE_W2_NW 10
-#endif
-#ifndef WIDE_W2_R
-#define WIDE_W2_R 10
-#endif
-
 // One activation row of bf16 rows of 2560 / 4096 / 9728: the variants that
 // measured fastest for each S2 matrix (rows per wave, k-split; or the wide
 // form with about one workgroup per compute unit for the S2 row counts).
 template <typename T, int NR>
 static bool pick_b1(const GemvParams& p, hipStream_t s, hipError_t* e) {
   if constexpr (sizeof(T) == 2) {
-    if (GEMV_WIDE) {
-      // the wide form for the long rows of O and W2 (5.8 / 10.0 us against
-      // 6.6 / 10.9 us); with 5 units per row it has too few waves per SIMD
-      // and the 4-wave kernels stay faster (QKV, W1|W3, fast head)
-      const int units = p.K / 512;
-      if constexpr (NR == 1) {
-        if (units == 8 && p.n_out == 2560) { *e = go_wide<8, WIDE_O_R, 1, 8>(p, s); return true; }        // O
-        if (units == 19 && p.n_out == 2560) { *e = go_wide<WIDE_W2_NW, WIDE_W2_R, 1, 19>(p, s); return true; }  // W2
-      }
+    // The wide form for the long rows of O and W2 (5.8 / 10.0 us against 6.6
+    // / 10.9 us for the k-split kernel); 8 waves x 10 rows for O, 10 waves x
+    // 10 rows for W2 (8 x 10, 8 x 8 and 12 x 12 were slower).  With 5 units
+    // per row it has too few waves per SIMD and the 4-wave kernels stay
+    // faster (QKV, W1|W3, fast head).
+    if constexpr (NR == 1) {
+      const int wunits = p.K / 512;
+      if (wunits == 8 && p.n_out == 2560) { *e = go_wide<8, 10, 1, 8>(p, s); return true; }     // O
+      if (wunits == 19 && p.n_out == 2560) { *e = go_wide<10, 10, 1, 19>(p, s); return true; }  // W2
     }
     const int units = p.K / (64 * ElemT<T>::EPV);
     if (units == 5) {
+      // rows per wave: 3 for QKV (512 workgroups; 7.6 us against 7.8), 2 for
+      // W1|W3 (1 / 3 / 4 rows took 18.7 / 19.9 / 19.7 us against 18.0)
       if (NR == 1 && p.n_out >= 65536) *e = go<T, 1, 4, NR, 5>(p, s);  // tied head
-      else if (NR == 2) *e = go<T, 1, B1_W13_RPW, NR, 5>(p, s);         // W1|W3
-      else if (p.n_out == 6144) *e = go<T, 1, B1_QKV_RPW, NR, 5>(p, s);  // QKV
-      else *e = go<T, 1, 2, NR, 5>(p, s);                               // fast head, K|V rows
+      else if (NR == 2) *e = go<T, 1, 2, NR, 5>(p, s);                 // W1|W3
+      else if (p.n_out == 6144) *e = go<T, 1, 3, NR, 5>(p, s);         // QKV
+      else *e = go<T, 1, 2, NR, 5>(p, s);                              // fast head, K|V rows
       return true;
     }
     if constexpr (NR == 1) {

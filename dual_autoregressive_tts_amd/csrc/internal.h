@@ -71,7 +71,6 @@ struct GemvParams {
   const void* next_gain; void* next_planes; int* next_done;
   int ksw, ldp;                  // set by the launcher
   int zswz;                      // set by the launcher: activation tiles of a swizzled 1-D grid (0 = 3-D grid)
-  int gm_cfg;                    // matrix-core workgroup shape (0 = the launcher's choice; 1..5 forced, for tuning)
   // set by the launcher for the stream-K form: U = tiles * chunks-per-tile
   // work units dealt to the grid, workgroup g taking sk_q (+1 if g < sk_r)
   // consecutive units; partial tiles at part + (tile * sk_smax + slot) * TE
@@ -235,8 +234,8 @@ struct FastBeginParams {
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
 bool launch_gemm_mfma(const GemvParams& p, hipStream_t s, hipError_t* err);
 // tiled matrix-core product for hundreds of activation rows (input planes at p.xn)
-bool launch_gemm_tile(const GemvParams& p, int cfg, hipStream_t s);
-int gemm_tile_choice(const GemvParams& p);
+bool launch_gemm_tile(const GemvParams& p, bool wide, hipStream_t s);
+bool gemm_tile_wide(const GemvParams& p);
 template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 template <typename T, typename KT> hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 // k/v append only (no q, no attention): rows are sequences, grid (R, KV)
