@@ -73,7 +73,8 @@ class Taps(C.Structure):
 
 # Every symbol the header declares.
 EXPORTS = ("dualar_workspace_bytes", "dualar_create", "dualar_prefill", "dualar_decode_frames",
-           "dualar_fast_frames", "dualar_fast_teacher_forced", "dualar_sync", "dualar_profile_begin", "dualar_profile_end",
+           "dualar_fast_frames", "dualar_fast_teacher_forced", "dualar_sync", "dualar_reset",
+           "dualar_profile_begin", "dualar_profile_end",
            "dualar_destroy", "dualar_status_string", "dualar_last_error")
 K_GEMV, K_ATTN, K_SAMPLE, K_EMBED, K_GEMV_SWIGLU = 0, 1, 2, 3, 4
 
@@ -103,6 +104,8 @@ def load_library(path: str = LIB_PATH):
     lib.dualar_fast_teacher_forced.restype = I32
     lib.dualar_sync.argtypes = [VP, P(I32)]
     lib.dualar_sync.restype = I32
+    lib.dualar_reset.argtypes = [VP, P(I32), I32]
+    lib.dualar_reset.restype = I32
     lib.dualar_profile_begin.argtypes = [VP, I32]
     lib.dualar_profile_begin.restype = I32
     lib.dualar_profile_end.argtypes = [VP, P(C.c_int64), P(C.c_double), P(C.c_double)]
@@ -333,6 +336,13 @@ class DualAR:
         n, ms, by = C.c_int64(), C.c_double(), C.c_double()
         self._check(self.lib.dualar_profile_end(self.h, C.byref(n), C.byref(ms), C.byref(by)))
         return {"launches": n.value, "total_ms": ms.value, "bytes": by.value}
+
+    def reset(self, seq_ids):
+        """Retire sequences of the current batch (host ints): later frames
+        emit -1 rows for them; the other sequences are unaffected."""
+        ids = [int(i) for i in seq_ids]
+        arr = (C.c_int32 * max(len(ids), 1))(*ids)
+        self._check(self.lib.dualar_reset(self.h, arr if ids else None, len(ids)))
 
     def sync(self) -> int:
         st = C.c_int32(0)

@@ -1006,6 +1006,19 @@ dualar_status dualar_sync(dualar_ctx_t* c, int32_t* device_status) {
   return DUALAR_OK;
 }
 
+dualar_status dualar_reset(dualar_ctx_t* c, const int32_t* seq_ids, int32_t n) {
+  if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
+  if (!c->ready) return fail(c, DUALAR_ERR_STATE, "reset before a successful prefill");
+  if (n < 0 || n > c->batch) return fail(c, DUALAR_ERR_INVALID_ARG, "n out of range [0, batch]");
+  if (n == 0) return DUALAR_OK;
+  if (!seq_ids) return fail(c, DUALAR_ERR_INVALID_ARG, "seq_ids is NULL");
+  for (int i = 0; i < n; ++i)
+    if (seq_ids[i] < 0 || seq_ids[i] >= c->batch)
+      return fail(c, DUALAR_ERR_INVALID_ARG, "a sequence id is outside [0, batch)");
+  HIPCHK(launch_seq_reset(c->st, seq_ids, n, c->batch, c->r.N, c->stream));
+  return DUALAR_OK;
+}
+
 dualar_status dualar_profile_begin(dualar_ctx_t* c, int32_t kernel_class) {
   if (!c) return fail(c, DUALAR_ERR_INVALID_ARG, "ctx is NULL");
   if (kernel_class < DUALAR_K_GEMV || kernel_class > DUALAR_K_GEMV_SWIGLU)

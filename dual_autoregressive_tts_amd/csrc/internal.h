@@ -176,9 +176,9 @@ struct SeqState {
   int* plen;       // [max_batch] prompt lengths
   int* frame_idx;  // [1] frame index inside the current call
   int* status;     // [1] latched device faults
-  int* ras_hist;   // [max_batch][RAS_HIST_STRIDE] loop-breaker windows: slot f % window = slow id of frame f
+  int* ras_hist;   // [max_batch][RAS_HIST_STRIDE] ring of emitted slow ids: slot f % RAS_HIST_STRIDE = frame f's
 };
-#define RAS_HIST_STRIDE 16   // = DUALAR_RAS_MAX_WINDOW
+#define RAS_HIST_STRIDE 16   // = DUALAR_RAS_MAX_WINDOW, a power of two
 
 // Candidate set / bookkeeping for the sampler.
 struct SampleParams {
@@ -250,3 +250,4 @@ template <typename T, typename KT> hipError_t launch_depth_attn(const PrefillPar
 hipError_t launch_frame_reset(SeqState st, hipStream_t s);
 hipError_t launch_frame_end(SeqState st, int B, int advance_pos, hipStream_t s);
 hipError_t launch_prefill_begin(SeqState st, const int* plen_host, int B, int N, hipStream_t s);
+hipError_t launch_seq_reset(SeqState st, const int* ids, int n, int B, int N, hipStream_t s);

@@ -310,26 +310,32 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
 
   // Loop breaker ([P2] "Two autoregressions ...", the paragraph after Eq. 1):
   // a slow draw that repeats a semantic id of the sequence's last ras_window
-  // frames is replaced by a second top-p draw with its own uniform (slot N);
-  // the id emitted enters the window (slot frames % ras_window).
-  if (p.slow && p.ras_window > 0) {
+  // frames is replaced by a second top-p draw with its own uniform (slot N).
+  // Every emitted slow id (but <|im_end|>) enters a ring of RAS_HIST_STRIDE
+  // slots at slot frames % RAS_HIST_STRIDE, whether or not the breaker is on
+  // for this call, so the window is always the last min(frames, ras_window)
+  // frames of this generation, also when calls change the window or turn
+  // the breaker on and off.
+  if (p.slow) {
     const int fr = p.st.frames[b];
     int* hist = p.st.ras_hist + (size_t)b * RAS_HIST_STRIDE;
-    if (tid == 0) {
-      const int id0 = cand_id((choice >= 0 && choice < nc) ? choice : 0);
-      int hit = 0;
-      if (id0 != p.end_id)
-        for (int i = 0; i < min(fr, p.ras_window); ++i) hit |= hist[i] == id0;
-      ras_hit = hit;
-    }
-    __syncthreads();
-    if (ras_hit) {
-      topp(p.ras_temperature, p.ras_top_p, ub[p.N]);
+    if (p.ras_window > 0) {
+      if (tid == 0) {
+        const int id0 = cand_id((choice >= 0 && choice < nc) ? choice : 0);
+        int hit = 0;
+        if (id0 != p.end_id)
+          for (int i = 0; i < min(fr, p.ras_window); ++i) hit |= hist[(fr - 1 - i) & (RAS_HIST_STRIDE - 1)] == id0;
+        ras_hit = hit;
+      }
       __syncthreads();
+      if (ras_hit) {
+        topp(p.ras_temperature, p.ras_top_p, ub[p.N]);
+        __syncthreads();
+      }
     }
     if (tid == 0) {
       const int id1 = cand_id((choice >= 0 && choice < nc) ? choice : 0);
-      if (id1 != p.end_id) hist[fr % p.ras_window] = id1;
+      if (id1 != p.end_id) hist[fr & (RAS_HIST_STRIDE - 1)] = id1;
     }
   }
 
@@ -408,8 +414,30 @@ __global__ void prefill_begin_kernel(SeqState st, PlenArg plen, int B, int N) {
     st.done[b] = 0;
     st.frames[b] = 0;
     for (int r = 0; r <= N; ++r) st.cur[b * (N + 1) + r] = 0;
+    for (int i = 0; i < RAS_HIST_STRIDE; ++i) st.ras_hist[b * RAS_HIST_STRIDE + i] = 0;
   }
   if (b == 0) *st.frame_idx = 0;
+}
+
+// Retire the sequences whose bit is set: finished (later frames emit -1 rows
+// and no samples), no frames emitted, no pending frame, an empty loop-breaker
+// window.  Their rows keep being computed on zero input with the batch, at
+// positions that keep advancing, and are never read by another sequence.
+struct SlotMask { uint64_t w[4]; };
+__global__ void seq_reset_kernel(SeqState st, SlotMask m, int B, int N) {
+  const int b = threadIdx.x;
+  if (b >= B || !((m.w[b >> 6] >> (b & 63)) & 1)) return;
+  st.done[b] = 1;
+  st.frames[b] = 0;
+  for (int r = 0; r <= N; ++r) st.cur[b * (N + 1) + r] = 0;
+  for (int i = 0; i < RAS_HIST_STRIDE; ++i) st.ras_hist[b * RAS_HIST_STRIDE + i] = 0;
+}
+
+hipError_t launch_seq_reset(SeqState st, const int* ids, int n, int B, int N, hipStream_t s) {
+  SlotMask m{};
+  for (int i = 0; i < n; ++i) m.w[ids[i] >> 6] |= 1ull << (ids[i] & 63);
+  hipLaunchKernelGGL(seq_reset_kernel, dim3(1), dim3(256), 0, s, st, m, B, N);
+  return hipGetLastError();
 }
 
 template <typename T> hipError_t launch_embed(const EmbedParams& p, hipStream_t s) {

@@ -255,6 +255,27 @@ dualar_status dualar_fast_frames(dualar_ctx_t *ctx, int32_t batch, int32_t n_fra
 dualar_status dualar_fast_teacher_forced(dualar_ctx_t *ctx, int32_t n, const float *hidden,
                                          const int32_t *codes, float *logits);
 
+/* Retire sequences of the current batch: each listed slot ends as a
+ * sequence that sampled <|im_end|> does ([P1] "Inference Pipeline",
+ * "generate: Full Sequence Generation": a generation emits frames until its
+ * end token; [P2] "Two autoregressions ...", the decode_one_token_ar loop),
+ * so that one finished or faulted sequence can be dropped without a new
+ * prefill of the whole batch.
+ *   seq_ids host int32 [n], each in [0, batch) of the last prefill
+ *           (duplicates allowed); n = 0 is a no-op.
+ * Enqueued on the context's stream.  The slot's frame count, pending frame
+ * and loop-breaker window are cleared; later dualar_decode_frames calls
+ * write -1 code rows for it and report 0 frames emitted, and the other
+ * sequences' codes and taps are bit-identical to a run without the reset.
+ * The slot's rows keep being computed (on zero input) with the batch, at
+ * positions that keep advancing, so the batch's context limit is unchanged.
+ * The next dualar_prefill brings every slot back.  Validation happens on the
+ * host before anything is enqueued: DUALAR_ERR_STATE before a successful
+ * prefill, DUALAR_ERR_INVALID_ARG for a NULL ctx or seq_ids (n > 0), n
+ * outside [0, batch] or an id outside [0, batch); a failing call changes
+ * nothing. */
+dualar_status dualar_reset(dualar_ctx_t *ctx, const int32_t *seq_ids, int32_t n);
+
 /* Block until the stream's work is done; report latched device faults.
  * *device_status (host, may be NULL) receives the raw status word. */
 dualar_status dualar_sync(dualar_ctx_t *ctx, int32_t *device_status);

@@ -10,6 +10,7 @@ from .dualar_oracle import (  # noqa: F401
     bf16_round,
     count_params,
     dequant_w4,
+    embed_column,
     param_shapes,
     rope_table,
     sample_token,

@@ -57,6 +57,7 @@ checkpoint's outputs, and the readings above measured against it.
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -166,6 +167,18 @@ def dequant_w4(weights: dict, group: int = 128) -> dict:
     return out
 
 
+_POOL = None
+
+
+def _pool():
+    """Threads for independent attention heads (plumbing, no arithmetic)."""
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
 def rms_norm(x, g, eps):
     """x / sqrt(mean(x^2) + eps) * g over the last axis."""
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
@@ -192,6 +205,27 @@ def apply_rope(x, cos, sin):
     out[..., 0::2] = a * cos - b * sin
     out[..., 1::2] = a * sin + b * cos
     return out
+
+
+def embed_column(col, tok_emb, cb_emb, sb: int, se: int, N: int, C: int, scale: bool) -> np.ndarray:
+    """Slow-AR input for one token column (id, q^(0..N-1)).
+
+    Semantic position (sb <= id <= se): (E_tok[id] + sum_k E_F[k*C + q^(k)])
+    / sqrt(N+1), the sum taken in the order E_tok first, then k = 0..N-1
+    ([P2] "Two autoregressions ...", Eq. 1 and the sqrt(N+1) paragraph).
+    Text position: E_tok[id] alone.  Every operation is done in the tables'
+    own precision: float64 tables give the oracle's value; float32 tables
+    give the float32 evaluation of the same formula (IEEE adds in that order
+    and an IEEE divide by the float32 value of sqrt(N+1)), which a float32
+    kernel that follows the formula reproduces bit for bit."""
+    ident = int(col[0])
+    x = np.array(tok_emb[ident], copy=True)
+    if sb <= ident <= se:
+        for k in range(N):
+            x = x + cb_emb[k * C + int(col[1 + k])]
+        if scale:
+            x = x / x.dtype.type(math.sqrt(N + 1.0))
+    return x
 
 
 @dataclass
@@ -260,7 +294,7 @@ class SeqState:
     next_col: np.ndarray | None = None
     frames: int = 0
     done: bool = False
-    ras_hist: list = field(default_factory=list)   # slow ids emitted, oldest first
+    ras_hist: list = field(default_factory=list)   # slow ids emitted (all frames), oldest first
 
 
 @dataclass
@@ -329,19 +363,10 @@ class DualAROracle:
 
     # --- a0: embedding + multi-codebook fusion -----------------------------
     def embed(self, col) -> np.ndarray:
-        """Slow-AR input for one token column (id, q^(0..N-1)).
-
-        Semantic position: (E_tok[id] + sum_k E_F[k*C + q^(k)]) / sqrt(N+1), the
-        sum taken in the order k = 0..N-1 ([P2] Eq. 1 and the sqrt(N+1)
-        divide).  Text position: E_tok[id] alone."""
-        ident = int(col[0])
-        x = self.w["tok_embedding"][ident].copy()
-        if self.sb <= ident <= self.se:
-            for k in range(self.N):
-                x = x + self.w["codebook_embedding"][k * self.C + int(col[1 + k])]
-            if self.cfg["scale_codebook_embeddings"]:
-                x = x / math.sqrt(self.N + 1.0)
-        return x
+        """Slow-AR input for one token column (id, q^(0..N-1)), in the
+        oracle's precision (see `embed_column`)."""
+        return embed_column(col, self.w["tok_embedding"], self.w["codebook_embedding"], self.sb, self.se,
+                            self.N, self.C, bool(self.cfg["scale_codebook_embeddings"]))
 
     # --- one transformer layer, one new position ---------------------------
     def _layer_step(self, P: _Part, lw, x, pos, K, V, cos, sin):
@@ -386,17 +411,33 @@ class DualAROracle:
         Kn = apply_rope(Kn, cos[pos][:, None, :], sin[pos][:, None, :])
         K[pos] = self._kv(Kn)
         V[pos] = self._kv(Vn)
-        L = pos0 + T
         rep = P.n_head // P.n_kv_head
-        mask = np.arange(L)[None, :] > pos[:, None]          # [T, L] future positions
         O = np.empty((T, P.n_head, P.head_dim), dtype=self.dt)
-        for hh in range(P.n_head):
+        # Causal attention, QB query rows at a time: the rows of a block
+        # attend to the keys up to the block's last position, and the keys
+        # past a row's own position get a -inf score (exp gives exactly 0).
+        # The blocks only skip scores that the mask would set to -inf.  The
+        # heads are independent and run on a thread pool (numpy releases the
+        # GIL), each with the same arithmetic as a serial loop.
+        QB = 256
+
+        def head(hh, r0, r1, Lb, future):
             g = hh // rep
-            S = Q[:, hh, :] @ K[:L, g, :].T / math.sqrt(P.head_dim)
-            S[mask] = -np.inf
-            Pm = np.exp(S - S.max(axis=1, keepdims=True))
-            Pm /= Pm.sum(axis=1, keepdims=True)
-            O[:, hh, :] = Pm @ V[:L, g, :]
+            S = Q[r0:r1, hh, :] @ K[:Lb, g, :].T
+            S /= math.sqrt(P.head_dim)
+            S += future
+            S -= S.max(axis=1, keepdims=True)
+            np.exp(S, out=S)                                  # softmax numerator
+            S /= S.sum(axis=1, keepdims=True)
+            O[r0:r1, hh, :] = S @ V[:Lb, g, :]
+
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1, user_api="blas"):       # one BLAS thread per head thread
+            for r0 in range(0, T, QB):
+                r1 = min(T, r0 + QB)
+                Lb = pos0 + r1
+                future = np.where(np.arange(Lb)[None, :] > pos[r0:r1, None], -np.inf, 0.0).astype(self.dt)
+                list(_pool().map(lambda hh: head(hh, r0, r1, Lb, future), range(P.n_head)))
         X = X + O.reshape(T, -1) @ lw["wo"].T
         H2 = rms_norm(X, lw["ffn_norm"], self.eps)
         return X + (silu(H2 @ lw["w1"].T) * (H2 @ lw["w3"].T)) @ lw["w2"].T
@@ -500,7 +541,9 @@ class DualAROracle:
             ident, self.ras_used = int(force[0]), False
         else:
             ident, self.ras_used = self.slow_sample_ras(seq, logits, s, u)
-        if s.ras_window > 0 and ident != self.end:
+        if ident != self.end:
+            # the loop breaker's window is the last frames' semantic ids,
+            # whatever sampling produced them
             seq.ras_hist.append(ident)
         if ident == self.end:
             seq.done = True

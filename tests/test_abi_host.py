@@ -152,4 +152,7 @@ def test_null_context_calls(lib):
     assert lib.dualar_fast_frames(None, 1, 1, None, None, C.byref(s), None, None, None) == -1
     assert lib.dualar_fast_teacher_forced(None, 1, None, None, None) == -1
     assert lib.dualar_sync(None, None) == -1
+    ids = (C.c_int32 * 1)(0)
+    assert lib.dualar_reset(None, ids, 1) == -1
+    assert lib.dualar_reset(None, None, 0) == -1
     lib.dualar_destroy(None)

@@ -1,14 +1,24 @@
 """The benchmark configurations at their full sizes, through the C ABI.
 
-The oracle cannot replay a 16,384-position prefill or 32 prompts of up to
-4,096 positions, so at these sizes the checks are
-  * sampled outputs the oracle computes one by one (teacher-forced fast AR:
-    every pair is independent), and
-  * properties that hold exactly at any size: every product, norm, split,
-    attention and sampling step works on one sequence (one row) at a time
-    with a reduction order that does not depend on the others, so a
-    sequence's results are bit-identical whatever the other sequences hold,
-    whatever the prefill step size, and from one run to the next.
+Against the oracle (the float64 CPU decoder replays whole sequences):
+  * s2_b1: the full S2-shaped model, bf16 K/V cache, the bench's 1,024-token
+    three-segment prompt, 8 greedy frames after frame 0, every tap and id;
+  * s2_b32: the bench's batch of 32 ragged prompts (741..4,025 positions),
+    top-p 0.9 with the bench's uniforms; the oracle replays the shortest and
+    the longest sequence -- on the bf16 cache (frame 0's taps, then frames up
+    to the first draw that differs within the logits' reach) and on an fp32
+    cache (the strict bound, ids for at least half of the frames);
+  * s2_prefill: the bench's launch configuration (4 sequences, 2,048
+    positions per sequence per step, 8,192 rows on the 2-D matrix-core
+    tiles) on 4,096-position all-frame prompts; the oracle replays one
+    sequence: frame 0 and one decode frame.
+Sampled outputs the oracle computes one by one: the teacher-forced fast AR
+over 819 pairs.  Properties that hold exactly at any size: every product,
+norm, split, attention and sampling step works on one sequence (one row) at
+a time with a reduction order that does not depend on the others, so a
+sequence's results are bit-identical whatever the other sequences hold,
+whatever the prefill step size, and from one run to the next (checked at
+the full 32-sequence batch and the 4 x 16,384-position prefill).
 """
 import numpy as np
 import pytest
@@ -17,6 +27,7 @@ import torch
 import synth
 from oracle import DualAROracle
 from tests.parity import REL_L2, rel_l2, say
+from tests.test_gpu_parity import run_and_compare
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +44,82 @@ def s2_weights():
     m = synth.model("s2")
     say("[full] generating 4.56 B weights")
     return m, synth.make_weights(m, seed=0)
+
+
+@pytest.fixture(scope="module")
+def s2_oracle_weights(s2_weights):
+    """The oracle's weights converted once: (float64, float32) dicts."""
+    m, w = s2_weights
+    say("[full] oracle weights (float32, float64)")
+    w32 = synth.weights_as_f32(m, w)
+    w64 = {k: np.asarray(v, dtype=np.float64) for k, v in w32.items()}
+    return w64, w32
+
+
+def _half(n_frames):
+    return (n_frames + 2) // 2       # at least half of frame 0 + n_frames
+
+
+@pytest.mark.timeout(900)
+def test_s2_b1_bench_config_vs_oracle(s2_weights, s2_oracle_weights):
+    # the s2_b1 bench line: full S2 shapes, bf16 K/V, the 1,024-token
+    # three-segment prompt, greedy, <|im_end|> held back as in the bench
+    m, w = s2_weights
+    w64, w32 = s2_oracle_weights
+    wl = synth.WORKLOADS["s2_b1"]
+    plen = synth.prompt_lengths(wl, seed=0)
+    P = synth.make_prompts(m, wl["prompt"], plen, seed=0)
+    F = 8
+    c, worst = run_and_compare(m, w, P, plen, F, dict(greedy=1), min_frames=1 << 30, tag="s2-b1-bench",
+                               floor=True, weights_f32=w32, weights_f64=w64)
+    assert c[0] >= _half(F), f"s2_b1: {c[0]} of {F + 1} frames compared (need {_half(F)})"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_s2_b32_bench_config_rows_vs_oracle(s2_weights, s2_oracle_weights, kv):
+    # the s2_b32 bench line: 32 ragged prompts, top-p 0.9 from the bench's
+    # seeded uniforms; the oracle replays the shortest and the longest row.
+    # bf16 cache: the fp32 rounding floor moves logits by ~1e-3, which swaps
+    # neighbours in the top-p order (the near-uniform candidates of random
+    # weights sit ~1e-3 apart), so the draws differ within reach after a
+    # frame or two; frame 0's taps (the batched ragged prefill up to 4,025
+    # positions) are always compared.  fp32 cache: the strict bound, and the
+    # ids must match for at least half of the frames.
+    m, w = s2_weights
+    w64, w32 = s2_oracle_weights
+    m = dict(m, kv_dtype=kv)
+    wl = synth.WORKLOADS["s2_b32"]
+    plen = synth.prompt_lengths(wl, seed=0)
+    P = synth.make_prompts(m, wl["prompt"], plen, seed=0)
+    F = 4
+    U = synth.make_uniforms((1 + F, len(plen), m["num_codebooks"]), seed=0)
+    rows = [int(np.argmin(plen)), int(np.argmax(plen))]
+    stats = {}
+    c, worst = run_and_compare(m, w, P, plen, F, dict(wl["sampling"]), U, min_frames=1 << 30,
+                               tag=f"s2-b32-bench-kv{kv}", floor=kv == "bf16", weights_f32=w32, weights_f64=w64,
+                               rows=rows, stats=stats)
+    say(f"[s2-b32-kv{kv}] rows {rows} (prompts {[int(plen[r]) for r in rows]}): frames compared {c}")
+    assert all(t >= 1 for t in stats["taps_compared"]), stats
+    if kv == "f32":
+        assert min(c) >= _half(F), f"s2_b32 fp32 cache: rows {rows} compared {c} of {F + 1} frames"
+        assert max(worst.values()) < REL_L2
+
+
+@pytest.mark.timeout(900)
+def test_s2_prefill_bench_launch_vs_oracle(s2_weights, s2_oracle_weights):
+    # the s2_prefill bench line's launch configuration (4 sequences x 2,048
+    # positions per step = 8,192 rows on the 2-D tiles, matrix-core causal
+    # attention over the growing cache) on 4,096-position all-frame prompts
+    m, w = s2_weights
+    w64, w32 = s2_oracle_weights
+    wl = synth.WORKLOADS["s2_prefill"]
+    plen = np.full(4, 4096, dtype=np.int32)
+    P = synth.make_prompts(m, ("frames", 4096), plen, seed=0)
+    F = 1
+    c, worst = run_and_compare(m, w, P, plen, F, dict(wl["sampling"]), min_frames=1 << 30, prefill_chunk=2048,
+                               tag="s2-prefill-4096", floor=True, weights_f32=w32, weights_f64=w64, rows=[0])
+    assert c[0] >= _half(F), f"s2_prefill: {c[0]} of {F + 1} frames compared"
 
 
 @pytest.mark.timeout(600)

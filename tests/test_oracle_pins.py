@@ -105,6 +105,35 @@ def test_fusion_indexing():
     assert np.allclose(o.embed(col), expect, rtol=1e-15)
 
 
+def test_fusion_float32_evaluation():
+    # The float32 evaluation of Eq. 1 (the precision the fused vector is
+    # compared in, bit for bit): with integer-valued tables every add is
+    # exact, so the one rounding left is the divide by the float32 square
+    # root of 11 -- the closed form 56 / sqrt(11) rounded twice; with random
+    # tables it stays within the float32 error bound of the float64 value.
+    from oracle import embed_column
+    N, C, D = 10, 16, 64
+    tok = np.ones((300, D), dtype=np.float32)
+    cb = np.repeat(np.arange(1, N + 1, dtype=np.float32), C)[:, None] * np.ones((1, D), np.float32)
+    col = [203, 3] + [5] * 9
+    x = embed_column(col, tok, cb, 200, 215, N, C, True)
+    assert x.dtype == np.float32
+    assert np.all(x == np.float32(56.0) / np.sqrt(np.float32(11.0)))
+    g = np.random.default_rng(3)
+    tok = g.standard_normal((300, D)).astype(np.float32)
+    cb = g.standard_normal((N * C, D)).astype(np.float32)
+    col = [209] + list(g.integers(0, C, N))
+    x32 = embed_column(col, tok, cb, 200, 215, N, C, True)
+    x64 = embed_column(col, tok.astype(np.float64), cb.astype(np.float64), 200, 215, N, C, True)
+    terms = np.abs(tok[209].astype(np.float64)) + sum(np.abs(cb[k * C + col[1 + k]].astype(np.float64))
+                                                      for k in range(N))
+    bound = (N + 3) * 2.0 ** -24 * terms / math.sqrt(11.0)
+    assert np.all(np.abs(x32 - x64) <= bound)
+    assert not np.array_equal(x32.astype(np.float64), x64)   # it is a float32 evaluation
+    # a text id takes its row alone, in either precision
+    assert np.array_equal(embed_column([7] + [0] * N, tok, cb, 200, 215, N, C, True), tok[7])
+
+
 # --------------------------------------------------------------------------
 # C4: the semantic logit mask
 # --------------------------------------------------------------------------
@@ -569,6 +598,38 @@ def test_ras_window_is_the_emitted_ids():
             emitted.append(fr[0])
     assert seq.ras_hist == emitted
     assert used > 0          # the greedy mini model repeats itself: the breaker fires
+
+
+def test_ras_window_spans_frames_with_the_breaker_off():
+    # [P2] loop-breaker paragraph: the window is the semantic tokens of the
+    # last 10 frames, whatever sampling emitted them.  Frames decoded with the
+    # breaker off still enter the window, and a call may change the window:
+    # each frame's decision looks at exactly the last `ras_window` emitted ids.
+    m = mini_model()
+    o = DualAROracle(m, f32_weights(m), max_seq=64)
+    N, end = m["num_codebooks"], m["end_id"]
+    prompt = synth.make_prompts(m, ("fixed", 2, 4, 2), [8])[0]
+    U = np.random.default_rng(7).random((24, N + 1))
+    windows = [0] * 6 + [3] * 8 + [5] * 10        # off, then 3, then 5
+    seq = o.new_sequence()
+    emitted, used = [], 0
+    for f, w in enumerate(windows):
+        s = Sampling(greedy=True, ras_window=w)
+        hist = list(seq.ras_hist)
+        assert hist == emitted
+        fr = o.prefill(seq, prompt, s, U[0]) if f == 0 else o.decode_frame(seq, s, U[f])
+        if fr[0] == -1:
+            break
+        plain = o.slow_sample(o.taps["slow_logits"], Sampling(greedy=True), None, f)
+        window = hist[-w:] if w > 0 else []
+        if o.ras_used:
+            used += 1
+            assert w > 0 and plain in window
+        else:
+            assert fr[0] == plain and (plain == end or plain not in window)
+        if fr[0] != end:
+            emitted.append(fr[0])
+    assert used > 0
 
 
 # ----------------------------------------------------------------------------
