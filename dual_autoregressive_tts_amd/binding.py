@@ -72,7 +72,7 @@ class Taps(C.Structure):
 
 
 # Every symbol the header declares.
-EXPORTS = ("dualar_workspace_bytes", "dualar_create", "dualar_prefill", "dualar_decode_frames",
+EXPORTS = ("dualar_workspace_bytes", "dualar_create", "dualar_create_static", "dualar_prefill", "dualar_decode_frames",
            "dualar_fast_frames", "dualar_fast_teacher_forced", "dualar_sync", "dualar_reset",
            "dualar_profile_begin", "dualar_profile_end",
            "dualar_destroy", "dualar_status_string", "dualar_last_error")
@@ -94,6 +94,8 @@ def load_library(path: str = LIB_PATH):
     lib.dualar_workspace_bytes.restype = C.c_size_t
     lib.dualar_create.argtypes = [P(Config), P(Weights), VP, C.c_size_t, VP, P(VP)]
     lib.dualar_create.restype = I32
+    lib.dualar_create_static.argtypes = [P(Config), P(Weights), VP, P(VP)]
+    lib.dualar_create_static.restype = I32
     lib.dualar_prefill.argtypes = [VP, I32, VP, I32, P(I32), P(Sampling), VP, VP, P(Taps)]
     lib.dualar_prefill.restype = I32
     lib.dualar_decode_frames.argtypes = [VP, I32, P(Sampling), VP, VP, VP, P(Taps)]
@@ -177,7 +179,9 @@ class DualAR:
     """One decode context (dualar_create) over device weights."""
 
     def __init__(self, m: dict, dev_weights: dict, max_batch: int, max_seq_len: int, stream=None,
-                 inherit_fast: bool = False, prefill_chunk: int = 0):
+                 inherit_fast: bool = False, prefill_chunk: int = 0, static_workspace: bool = False):
+        """static_workspace: dualar_create_static (the library's static device
+        workspace, nothing allocated here; one such context per GPU at a time)."""
         import torch
         self.torch = torch
         self.lib = load_library()
@@ -188,13 +192,17 @@ class DualAR:
         if self.ws_bytes == 0:
             raise DualARError(-1, "invalid config")
         self.dev_weights = dev_weights
-        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.workspace = None if static_workspace else torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._keep = []
         self.wstruct = self._weights_struct(dev_weights)
         h = C.c_void_p()
-        st = self.lib.dualar_create(C.byref(self.cfg), C.byref(self.wstruct), _ptr(self.workspace),
-                                    self.ws_bytes, C.c_void_p(self.stream.cuda_stream), C.byref(h))
+        if static_workspace:
+            st = self.lib.dualar_create_static(C.byref(self.cfg), C.byref(self.wstruct),
+                                               C.c_void_p(self.stream.cuda_stream), C.byref(h))
+        else:
+            st = self.lib.dualar_create(C.byref(self.cfg), C.byref(self.wstruct), _ptr(self.workspace),
+                                        self.ws_bytes, C.c_void_p(self.stream.cuda_stream), C.byref(h))
         if st != OK:
             raise DualARError(st, self.lib.dualar_last_error(None).decode())
         self.h = h

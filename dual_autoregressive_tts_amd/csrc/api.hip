@@ -14,6 +14,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -781,6 +782,43 @@ dualar_status check_sampling(dualar_ctx* c, const dualar_sampling* s, const floa
   return DUALAR_OK;
 }
 
+dualar_status create_ctx(const dualar_config* cfg, const dualar_weights* w, void* workspace,
+                         size_t workspace_bytes, void* hip_stream, dualar_ctx_t** out);
+
+}  // namespace
+
+// The workspace of dualar_create_static: a static device array that every GPU
+// the library runs on holds until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: only the address returned
+// by hipGetSymbolAddress for the current device may reach a kernel or a
+// copy.
+static __device__ __align__(256) char scratch[DUALAR_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];   // device address of `scratch` per device (nullptr: not looked up yet)
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current).
+dualar_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+    return fail(nullptr, DUALAR_ERR_NO_DEVICE, "no current HIP device for the static workspace");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(nullptr, DUALAR_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DUALAR_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -797,6 +835,33 @@ size_t dualar_workspace_bytes(const dualar_config* cfg) {
 
 dualar_status dualar_create(const dualar_config* cfg, const dualar_weights* w, void* workspace,
                             size_t workspace_bytes, void* hip_stream, dualar_ctx_t** out) {
+  return create_ctx(cfg, w, workspace, workspace_bytes, hip_stream, out);
+}
+
+dualar_status dualar_create_static(const dualar_config* cfg, const dualar_weights* w, void* hip_stream,
+                                   dualar_ctx_t** out) {
+  Resolved r;
+  std::string err;
+  if (!out) return fail(nullptr, DUALAR_ERR_INVALID_ARG, "out is NULL");
+  if (!resolve(cfg, &r, &err)) return fail(nullptr, DUALAR_ERR_INVALID_ARG, err);
+  const size_t need = layout(r).total;
+  if (need > sizeof(scratch)) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "the config needs a %zu-byte workspace; the static workspace holds %zu bytes", need,
+             sizeof(scratch));
+    return fail(nullptr, DUALAR_ERR_WORKSPACE, buf);
+  }
+  void* ws = nullptr;
+  if (dualar_status st = scratch_address(&ws)) return st;
+  return create_ctx(cfg, w, ws, sizeof(scratch), hip_stream, out);
+}
+
+}  // extern "C"
+
+namespace {
+
+dualar_status create_ctx(const dualar_config* cfg, const dualar_weights* w, void* workspace,
+                         size_t workspace_bytes, void* hip_stream, dualar_ctx_t** out) {
   dualar_ctx* c = nullptr;
   Resolved r;
   std::string err;
@@ -907,6 +972,10 @@ dualar_status dualar_create(const dualar_config* cfg, const dualar_weights* w, v
   *out = c;
   return DUALAR_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 dualar_status dualar_prefill(dualar_ctx_t* c, int32_t batch, const int32_t* tokens, int32_t t_max,
                              const int32_t* prompt_len, const dualar_sampling* s, const float* uniforms,

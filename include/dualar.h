@@ -189,6 +189,29 @@ dualar_status dualar_create(const dualar_config *cfg, const dualar_weights *w,
                             void *workspace, size_t workspace_bytes,
                             void *hip_stream, dualar_ctx_t **out);
 
+/* Largest workspace dualar_create_static can provide (32 MiB). */
+#define DUALAR_STATIC_WORKSPACE_BYTES (32u << 20)
+
+/* dualar_create without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array
+ * of DUALAR_STATIC_WORKSPACE_BYTES that the library holds on every GPU it
+ * runs on until the process ends; this call allocates no device memory (no
+ * hipMalloc / hipFree, no framework allocator).  Everything else is as in
+ * dualar_create: the same validation, the same initialisation (zeroed state,
+ * RoPE tables) enqueued on hip_stream, and the same kernels and results for
+ * every later call on the context.
+ * Fails with DUALAR_ERR_WORKSPACE (nothing created) when
+ * dualar_workspace_bytes(cfg) exceeds DUALAR_STATIC_WORKSPACE_BYTES (small
+ * models, batches and prefill chunks fit), and DUALAR_ERR_HIP if the
+ * array's device address cannot be obtained.
+ * Every context made by this call on one GPU uses the same array, which
+ * keeps what the last context wrote: at most one of them may be in use per
+ * GPU at a time; creating another (or using two at once) races on that
+ * memory.  Destroy as usual with dualar_destroy. */
+dualar_status dualar_create_static(const dualar_config *cfg, const dualar_weights *w,
+                                   void *hip_stream, dualar_ctx_t **out);
+
 /* Prefill a batch of prompts and emit frame 0 of every sequence.
  *   tokens     device int32 [batch][N+1][t_max]: row 0 = LM ids, rows 1..N =
  *              codebook ids q^(0..N-1) (read at semantic positions only);

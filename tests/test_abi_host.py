@@ -156,3 +156,25 @@ def test_null_context_calls(lib):
     assert lib.dualar_reset(None, ids, 1) == -1
     assert lib.dualar_reset(None, None, 0) == -1
     lib.dualar_destroy(None)
+
+
+def test_create_static_validation_without_gpu(lib):
+    # dualar_create_static: NULL out / bad config -> INVALID_ARG; a config
+    # whose workspace exceeds the static array -> WORKSPACE before any device
+    # call; a config that fits reaches the device lookup (NO_DEVICE here)
+    import torch
+    m = synth.model("tiny")
+    h = C.c_void_p()
+    small = bd.make_config(m, 1, 64, prefill_chunk=16)
+    assert lib.dualar_create_static(C.byref(small), C.byref(_fake_weights(m)), None, None) == -1
+    bad = bd.make_config(m, 1, 64, prefill_chunk=16)
+    bad.n_layer = 0
+    assert lib.dualar_create_static(C.byref(bad), C.byref(_fake_weights(m)), None, C.byref(h)) == -1
+    big = bd.make_config(m, 8, 4096)
+    assert lib.dualar_workspace_bytes(C.byref(big)) > 32 << 20
+    assert lib.dualar_create_static(C.byref(big), C.byref(_fake_weights(m)), None, C.byref(h)) == -3
+    assert b"static workspace" in lib.dualar_last_error(None) and not h.value
+    assert lib.dualar_workspace_bytes(C.byref(small)) <= 32 << 20
+    if not torch.cuda.is_available():
+        assert lib.dualar_create_static(C.byref(small), C.byref(_fake_weights(m)), None, C.byref(h)) == -2
+        assert not h.value

@@ -140,3 +140,22 @@ def test_w4_frame_bytes_by_enumeration():
     b0 = rp.frame_bytes(m, [40])["total"]
     b4 = rp.frame_bytes(m, [40], w4_names=sorted(names))
     assert b4["w4_delta"] == want and b4["total"] == b0 + want
+
+
+def test_bench_host_info_names_the_cpu_and_blas():
+    # cpu_baseline records the host it ran on: logical CPUs, CPU model, numpy
+    # and its BLAS thread pool
+    import bench
+    h = bench.host_info()
+    assert h["nproc"] == os.cpu_count() and h["numpy"]
+    assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)
+    assert h["blas"] is None or h["blas"]["threads"] >= 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
