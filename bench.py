@@ -339,12 +339,12 @@ def decode_workload(args, name, torch, synth, DualAR, reporting, kit, m, w, dev_
         ctx.profile_begin(K_GEMV_SWIGLU)
         run(a0 + Pf // 2, a0 + Pf)
         f = ctx.profile_end()
-        gemv_avg_us = g["total_ms"] * 1e3 / g["launches"]
-        gemv_gbps = g["bytes"] / (g["total_ms"] * 1e-3) / 1e9
+        gemv_avg_us = g["total_ms"] * 1e3 / max(g["launches"], 1)
+        gemv_gbps = g["bytes"] / max(g["total_ms"] * 1e-3, 1e-12) / 1e9
         gemv_share = g["total_ms"] / ((Pf // 2) * ms_per_step)
-        sw_avg_us = f["total_ms"] * 1e3 / f["launches"]
-        sw_bytes = f["bytes"] / f["launches"]
-        sw_gbps = sw_bytes / (sw_avg_us * 1e-6) / 1e9
+        sw_avg_us = f["total_ms"] * 1e3 / max(f["launches"], 1)
+        sw_bytes = f["bytes"] / max(f["launches"], 1)
+        sw_gbps = sw_bytes / max(sw_avg_us * 1e-6, 1e-12) / 1e9
         log(f"[bench] {name}: GEMV family: {g['launches']} launches, avg {gemv_avg_us:.2f} us, {gemv_gbps:.0f} GB/s, "
             f"{100 * gemv_share:.1f}% of step time")
         log(f"[bench] {name}: SwiGLU gate|up product: {f['launches']} launches, avg {sw_avg_us:.2f} us, "

@@ -14,8 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdualar.so")
-SOURCES = ["api.hip", "gemv.hip", "gemm.hip", "gemm_tile.hip", "attention.hip", "attn_o.hip", "prefill.hip", "depth.hip", "sample.hip",
-           "stack_b1.hip"]
+SOURCES = ["api.hip", "gemv.hip", "gemm.hip", "gemm_tile.hip", "attention.hip", "attn_o.hip", "prefill.hip", "depth.hip", "sample.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -43,8 +43,7 @@ struct Resolved {  // config with the inherit-on-unset fallback applied
 struct Layout {
   size_t kslow, vslow, kfast, vfast, rope_s, rope_f, x_slow, x_fast, qkv, att, ffn, logits, flog, part,
       xn, xn2, gpart, gpart_elems, x_pre, ppos, qbuf,
-      counters, st_pos, st_done, st_frames, st_cur, st_plen, st_fidx, st_status, st_ras,
-      sb_layers, sb_llx, sb_llqkv, sb_llh, total;
+      counters, st_pos, st_done, st_frames, st_cur, st_plen, st_fidx, st_status, st_ras, total;
   size_t slow_layer_stride, fast_layer_stride;  // elements per layer of a cache
   int max_splits, qkv_ld, att_ld, ffn_ld;
   int rows;     // activation rows the buffers hold: max(max_batch, max_batch * pc)
@@ -161,12 +160,6 @@ Layout layout(const Resolved& r) {
   L.st_fidx = take(4);
   L.st_status = take(4);
   L.st_ras = take((size_t)r.max_batch * DUALAR_RAS_MAX_WINDOW * 4);   // loop-breaker windows
-  // batch-1 persistent layer stack: device copies of the layers' weight
-  // pointers (slow, then fast) and the tagged hand-off words
-  L.sb_layers = take((size_t)(r.n_layer + r.fn_layer) * sizeof(B1Layer));
-  L.sb_llx = take((size_t)r.dim * 8);
-  L.sb_llqkv = take((size_t)L.qkv_ld * 8);
-  L.sb_llh = take((size_t)std::max(r.ffn, r.fffn) * 8);
   L.total = off;
   return L;
 }
@@ -203,9 +196,6 @@ struct dualar_ctx {
   int pf_masked = 0;
   SeqState st;
   // measurement (dualar_profile_begin/end)
-  // batch-1 persistent fast stack (stack_b1.hip): usable, and the next tag
-  bool sb_fast = false;
-  unsigned sb_tag = 0;
   int prof_cls = -1;
   std::vector<hipEvent_t> ev;
   size_t ev_used = 0;
@@ -517,44 +507,6 @@ dualar_status run_layer_kv_only(dualar_ctx* c, Stack& S, int l, float* x, int B,
   return DUALAR_OK;
 }
 
-// One fast pass (all fast layers) at depth position k for batch 1, in one
-// persistent launch; pass 0 computes only K and V in its last layer.
-hipError_t fast_stack_b1(dualar_ctx* c, float* x, int k, bool pass0) {
-  const Resolved& r = c->r;
-  const Layout& L = c->L;
-  const unsigned span = 4u * r.fn_layer + 4u;
-  if (c->sb_tag > 0xF0000000u) {
-    // tags are about to wrap: clear the hand-off words and start again
-    hipError_t e = hipMemsetAsync(c->ws + L.sb_llx, 0, L.total - L.sb_llx, c->stream);
-    if (e != hipSuccess) return e;
-    c->sb_tag = 0;
-  }
-  StackB1Params p{};
-  p.layers = (const B1Layer*)(c->ws + L.sb_layers) + r.n_layer;
-  p.n_layer = r.fn_layer;
-  p.kv_only_last = pass0 ? 1 : 0;
-  p.eps = r.eps;
-  p.x = x;
-  p.ll_x = (unsigned long long*)(c->ws + L.sb_llx);
-  p.ll_qkv = (unsigned long long*)(c->ws + L.sb_llqkv);
-  p.ll_h = (unsigned long long*)(c->ws + L.sb_llh);
-  p.kcache = c->fast.k; p.vcache = c->fast.v; p.layer_stride = c->fast.layer_stride;
-  p.max_pos = c->fast.max_pos; p.pos = k; p.rope = c->fast.rope;
-  p.tag0 = c->sb_tag;
-  c->sb_tag += span;
-  p.status = c->st.status;
-  p.spin_limit = 1 << 16;
-  hipError_t e = prof_pre(c, DUALAR_K_GEMV);
-  if (e != hipSuccess) return e;
-  e = launch_stack_b1(p, c->stream);
-  if (e != hipSuccess) return e;
-  // algorithmic bytes: the stack's weights (pass 0: the last layer's K, V rows and gain only)
-  const double per_layer = (double)r.dim * ((r.fH + 2 * r.fKV) * r.fhd) + (double)r.fH * r.fhd * r.dim +
-                           3.0 * r.dim * r.fffn + 2.0 * r.dim + (r.fast_qk ? 2.0 * r.fhd : 0.0);
-  const double last = pass0 ? (double)r.dim * 2 * r.fKV * r.fhd + r.dim + (r.fast_qk ? r.fhd : 0.0) : per_layer;
-  return prof_post(c, DUALAR_K_GEMV, ((r.fn_layer - 1) * per_layer + last) * r.esz);
-}
-
 struct FrameIO {
   const dualar_sampling* s;
   const float* uniforms; int u_fs, u_rs;
@@ -633,22 +585,18 @@ dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
     HIPCHK(sample<T>(c, sp));
   }
   // fast pass 0: the slow hidden state at depth position 0
-  const bool sb = c->sb_fast && B == 1;
   bool pl = false;
-  if (sb) {
-    HIPCHK(fast_stack_b1(c, xs, 0, true));
-  } else {
-    for (int l = 0; l + 1 < r.fn_layer; ++l) {
-      dualar_status st = run_layer<T, KT>(c, c->fast, l, xs, B, nullptr, 0, 1, pl);
-      if (st) return st;
-    }
+  for (int l = 0; l + 1 < r.fn_layer; ++l) {
+    dualar_status st = run_layer<T, KT>(c, c->fast, l, xs, B, nullptr, 0, 1, pl);
+    if (st) return st;
+  }
+  {
     dualar_status st = run_layer_kv_only<T, KT>(c, c->fast, r.fn_layer - 1, xs, B, pl);
     if (st) return st;
   }
   for (int k = 1; k < r.N; ++k) {
     pl = false;
-    if (sb) HIPCHK(fast_stack_b1(c, xf, k, false));
-    for (int l = 0; l < r.fn_layer && !sb; ++l) {
+    for (int l = 0; l < r.fn_layer; ++l) {
       dualar_status st = run_layer<T, KT>(c, c->fast, l, xf, B, nullptr, k, k + 1, pl);
       if (st) return st;
     }
@@ -1013,32 +961,11 @@ dualar_status create_ctx(const dualar_config* cfg, const dualar_weights* w, void
     return t;
   };
   std::vector<float2> ts = table(r.max_seq, r.hd), tf = table(r.N, r.fhd);
-  // device copies of the layer pointers for the persistent batch-1 stack
-  std::vector<B1Layer> lt;
-  for (const Stack* S : {&c->slow, &c->fast})
-    for (int i = 0; i < S->n_layer; ++i) {
-      const dualar_layer_weights& a = S->lw[i];
-      lt.push_back(B1Layer{a.attention_norm, a.wq, a.wk, a.wv, S->qk ? a.q_norm : nullptr, S->qk ? a.k_norm : nullptr,
-                           a.wo, a.ffn_norm, a.w1, a.w3, a.w2});
-    }
-  bool any_w4 = false;
-  for (const Stack* S : {&c->slow, &c->fast})
-    for (const dualar_layer_w4& a : S->l4)
-      for (int j = 0; j < 7; ++j) any_w4 |= a.q4[j] != nullptr;
-  {
-    int cus = 0;
-    const bool fits = r.dtype == DUALAR_BF16 && r.kvdtype == DUALAR_BF16 && r.max_batch == 1 && !any_w4 &&
-                      stack_b1_fits(r.dim, r.fH, r.fKV, r.fhd, r.fffn, r.N);
-    if (fits && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess)
-      c->sb_fast = (long long)stack_b1_max_blocks() * cus >= SB_GRID;
-  }
   hipError_t e1 = hipMemsetAsync(c->ws + L.counters, 0, L.total - L.counters, c->stream);
   hipError_t e2 = hipMemcpyAsync(c->ws + L.rope_s, ts.data(), ts.size() * sizeof(float2), hipMemcpyHostToDevice, c->stream);
   hipError_t e3 = hipMemcpyAsync(c->ws + L.rope_f, tf.data(), tf.size() * sizeof(float2), hipMemcpyHostToDevice, c->stream);
-  hipError_t e5 = hipMemcpyAsync(c->ws + L.sb_layers, lt.data(), lt.size() * sizeof(B1Layer), hipMemcpyHostToDevice,
-                                 c->stream);
   hipError_t e4 = hipStreamSynchronize(c->stream);   // host tables go out of scope
-  if (e1 || e2 || e3 || e4 || e5) {
+  if (e1 || e2 || e3 || e4) {
     delete c;
     return fail(nullptr, DUALAR_ERR_HIP, "workspace initialisation failed");
   }
@@ -1143,8 +1070,6 @@ dualar_status dualar_sync(dualar_ctx_t* c, int32_t* device_status) {
   if (st) {
     HIPCHK(hipMemset(c->st.status, 0, 4));
     if (st & ST_BAD_TOKEN) return fail(c, DUALAR_ERR_BAD_TOKEN, "an id outside its range reached the device");
-    if (st & ST_SYNC_TIMEOUT)
-      return fail(c, DUALAR_ERR_DEVICE_FAULT, "a persistent layer stack waited past its limit for another workgroup");
     return fail(c, DUALAR_ERR_DEVICE_FAULT, "a non-finite logit reached the sampler");
   }
   return DUALAR_OK;

@@ -9,7 +9,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define DUALAR_WG 256
 
 // Status bits latched in the workspace status word.
-enum { ST_BAD_TOKEN = 1, ST_NONFINITE = 2, ST_SYNC_TIMEOUT = 4 };
+enum { ST_BAD_TOKEN = 1, ST_NONFINITE = 2 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

@@ -127,32 +127,6 @@ struct AttnOParams {
 bool attn_o_b1_fits(int H, int KV, int hd, int dim, int L);
 hipError_t launch_attn_o_b1(const AttnOParams& p, hipStream_t s);
 
-// Batch-1 layer stack in one persistent launch (stack_b1.hip): S2 shapes
-// (dim 2560, 32 query / 8 KV heads of 128, FFN 9728), bf16 weights and
-// cache, SB_GRID workgroups that must all be resident at once.
-#define SB_GRID 256
-struct B1Layer {   // device-side copy of one layer's weight pointers
-  const void *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo, *ffn_norm, *w1, *w3, *w2;
-};
-struct StackB1Params {
-  const B1Layer* layers; int n_layer;
-  int kv_only_last;                   // last layer: K and V only, appended at pos (fast pass 0)
-  float eps;
-  float* x;                           // [dim] residual row, updated in place
-  unsigned long long* ll_x;           // [dim]   tagged hand-off words
-  unsigned long long* ll_qkv;         // [(H+2KV) hd]
-  unsigned long long* ll_h;           // [ffn]
-  void* kcache; void* vcache;         // layer 0 of the stack: [KV][max_pos][hd] bf16, layers layer_stride apart
-  size_t layer_stride;                // elements
-  int max_pos, pos;                   // attends to positions 0..pos (pos < 16)
-  const float2* rope;                 // [max_pos][hd/2] (cos, sin)
-  unsigned tag0;                      // tags of this launch are tag0 + 1 ..
-  int* status; int spin_limit;
-};
-bool stack_b1_fits(int dim, int H, int KV, int hd, int ffn, int n_pos);
-hipError_t launch_stack_b1(const StackB1Params& p, hipStream_t s);
-int stack_b1_max_blocks();   // workgroups of stack_b1_kernel one compute unit holds
-
 // Batch-1 merge of the split attention partials (AttnParams::part of the
 // split form, run with no_merge) fused with the O product and its residual.
 // Same head shape as attn_o_b1 (H = 32, KV = 8, hd = 128, bf16 weights).
