@@ -11,14 +11,13 @@
 // are the semantic ids and <|im_end|> (every other logit carries the -inf
 // bias, so it can never be drawn); the fast candidates are all C codes.
 // Greedy = argmax with the lowest id on ties.  Top-p: e_i = exp((z_i -
-// zmax)/T), a bitonic sort by (e desc, id asc) in LDS, an inclusive scan,
-// keep the shortest prefix whose mass reaches top_p * total, draw the first
-// kept index whose cumulative mass exceeds u * kept mass.
+// zmax)/T), in the order (e desc, id asc) keep the shortest prefix whose
+// mass reaches top_p * total, draw the first kept index whose cumulative
+// mass exceeds u * kept mass (found by radix selection, see tp_select).
 #include "common.h"
 #include "internal.h"
 
 #define SMP_THREADS 1024
-#define SMP_MAXN 8192
 
 // ---------------------------------------------------------------------------
 // fusion / embedding
@@ -121,90 +120,127 @@ __device__ __forceinline__ Best block_best(Best x, Best* sh) {
   return r;
 }
 
-__device__ __forceinline__ int block_count(int c, int* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  c = (int)wave_sum((float)c);   // counts <= 8192 are exact in fp32
-  if (lane == 0) sh[wave] = c;
-  __syncthreads();
-  int r = 0;
-  for (int w = 0; w < SMP_THREADS / 64; ++w) r += sh[w];
-  __syncthreads();
-  return r;
+
+// Top-p without a sort.  The candidates' order (e desc, index asc) is that
+// of the 45-bit keys e_bits << 13 | (8191 - i) (e >= 0, so its float bits
+// order as its value), and masses are fixed point, m = e * 2^40 rounded
+// (integer sums: the same in any order, so the draw is reproducible).  The
+// nucleus is the shortest prefix of the order whose mass reaches top_p * T,
+// i.e. it ends at the largest key K with mass(keys >= K) >= top_p * T; the
+// draw is the first kept candidate whose cumulative mass exceeds u * kept,
+// i.e. the largest key with mass(keys >= K) > u * kept.  Both keys are found
+// by a radix descent: 8 key bits per pass, a histogram of (mass, count) over
+// the candidates that share the bits found so far, suffix sums over the
+// 256 digits from the top, and the digit where the condition still holds;
+// a pass whose digit holds a single candidate ends the descent.
+#define TP_E 5                              // candidates per thread: nc <= 5120
+#define TP_IDX_BITS 13
+#define TP_KEY_BITS (32 + TP_IDX_BITS)
+#define TP_NB 256
+#define TP_WAVES (SMP_THREADS / 64)
+static_assert(TP_E * SMP_THREADS >= 4097, "the slow candidates fit");
+
+struct TopPShared {
+  unsigned long long mass[TP_WAVES][TP_NB];   // per-wave histograms
+  unsigned cnt[TP_WAVES][TP_NB];
+  unsigned long long wtot[TP_WAVES];
+  int cand_t[TP_NB / 64];                     // per digit wave: its chosen digit, or -1
+  unsigned long long cand_above[TP_NB / 64];
+  int cand_single[TP_NB / 64];
+  unsigned long long found_key, found_mass;
+};
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
-// Top-p order: sort the candidates' e = exp((z - zmax) / T) by (e desc, index
-// asc) into ev/ix (NP = 1024*E entries, padding e = 0).  Bitonic network on
-// 64-bit keys (e bits << 16 | 0xffff - index: larger key first), E
-// consecutive entries per thread held in registers: strides below E are
-// swapped in registers, strides below 64*E with lane shuffles inside the
-// wave, and only the larger ones go through LDS with a barrier.
-template <int E, class CandId, class CandOk>
-__device__ __forceinline__ void topp_sort(const float* z, const SampleParams& p, int nc, float zmax, float invT,
-                                          float* ev, uint16_t* ix, CandId cand_id, CandOk cand_ok) {
-  constexpr int NP = SMP_THREADS * E;
-  const int tid = threadIdx.x;
-  uint64_t key[E];
+// Sum of v over the workgroup (fixed order: lanes, then waves 0..15).
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, TopPShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_u64(v);
+  if (lane == 0) sh.wtot[wave] = v;
+  __syncthreads();
+  unsigned long long t = 0;
 #pragma unroll
-  for (int s = 0; s < E; ++s) {
-    const int i = tid * E + s;
-    float e = 0.f;
-    if (i < nc && cand_ok(i)) e = expf((z[p.restricted ? i : cand_id(i)] - zmax) * invT);
-    key[s] = ((uint64_t)__float_as_uint(e) << 16) | (uint64_t)(0xffffu - (unsigned)i);
-  }
-  uint32_t* kh = (uint32_t*)ev;          // exchange area: high words in ev, low 16 bits in ix
-  for (int kk = 2; kk <= NP; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      if (j < E) {
+  for (int w = 0; w < TP_WAVES; ++w) t += sh.wtot[w];
+  __syncthreads();
+  return t;
+}
+
+// The largest candidate key K with mass(keys >= K) >= thr (strict: > thr),
+// and mass(keys >= K).  The caller guarantees that the whole set satisfies
+// the condition.
+__device__ __forceinline__ void tp_select(const unsigned long long (&key)[TP_E], const unsigned long long (&m)[TP_E],
+                                          double thr, bool strict, TopPShared& sh, unsigned long long* k_out,
+                                          unsigned long long* m_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned long long P = 0, above = 0;
+  int lo = TP_KEY_BITS;
+  while (true) {
+    const int hi = lo;                       // bits [lo, hi) are this pass's digit
+    lo = hi > 8 ? hi - 8 : 0;
+    const int w = hi - lo;
+    for (int j = lane; j < TP_NB; j += 64) { sh.mass[wave][j] = 0ull; sh.cnt[wave][j] = 0u; }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int s = 0; s < E; ++s) {
-          const int sp = s ^ j;
-          if (sp > s) {
-            const int i = tid * E + s;
-            const bool first = (i & kk) == 0;      // this run in target order
-            const uint64_t a = key[s], b = key[sp];
-            if ((a < b) == first) { key[s] = b; key[sp] = a; }
-          }
-        }
-      } else {
-        const int tj = j / E;                     // partner thread = tid ^ tj
-        uint64_t other[E];
-        if (tj < 64) {
+    for (int s = 0; s < TP_E; ++s)
+      if (key[s] != 0ull && (key[s] >> hi) == P) {
+        const int d = (int)((key[s] >> lo) & ((1ull << w) - 1));
+        atomicAdd(&sh.mass[wave][d], m[s]);
+        atomicAdd(&sh.cnt[wave][d], 1u);
+      }
+    __syncthreads();
+    // digit t = tid (first four waves): its mass and count over the waves,
+    // then suffix sums from the top digit down
+    unsigned long long mt = 0, suf = 0;
+    unsigned ct = 0;
+    if (tid < TP_NB) {
 #pragma unroll
-          for (int s = 0; s < E; ++s) {
-            const unsigned lo = __shfl_xor((unsigned)key[s], tj);
-            const unsigned hi = __shfl_xor((unsigned)(key[s] >> 32), tj);
-            other[s] = ((uint64_t)hi << 32) | lo;
-          }
-        } else {
-          __syncthreads();
+      for (int ww = 0; ww < TP_WAVES; ++ww) { mt += sh.mass[ww][tid]; ct += sh.cnt[ww][tid]; }
+      suf = mt;     // inclusive suffix sum within the wave (lanes above this one)
 #pragma unroll
-          for (int s = 0; s < E; ++s) {
-            kh[tid * E + s] = (uint32_t)(key[s] >> 16);
-            ix[tid * E + s] = (uint16_t)(key[s] & 0xffffu);
-          }
-          __syncthreads();
-          const int pt = tid ^ tj;
-#pragma unroll
-          for (int s = 0; s < E; ++s) other[s] = ((uint64_t)kh[pt * E + s] << 16) | ix[pt * E + s];
-        }
-        const bool lower = (tid & tj) == 0;        // I hold the lower index of each pair
-#pragma unroll
-        for (int s = 0; s < E; ++s) {
-          const int i = tid * E + s;
-          const bool first = (i & kk) == 0;
-          const uint64_t a = key[s], b = other[s];
-          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-          key[s] = (lower == first) ? hi : lo;
-        }
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_down(suf, o);
+        if (lane + o < 64) suf += y;
+      }
+      if (lane == 0) sh.wtot[wave] = suf;
+    }
+    __syncthreads();
+    // the highest non-empty digit whose suffix mass meets the condition:
+    // the wanted key is the largest one that does, so it lies in that digit
+    if (tid < TP_NB) {
+      for (int ww = wave + 1; ww < TP_NB / 64; ++ww) suf += sh.wtot[ww];
+      const double s_t = (double)(above + suf);
+      const bool c_t = tid < (1 << w) && ct > 0u && (strict ? s_t > thr : s_t >= thr);
+      const unsigned long long bal = __ballot(c_t);
+      if (bal == 0ull) {
+        if (lane == 0) sh.cand_t[wave] = -1;
+      } else if (lane == 63 - __clzll(bal)) {
+        sh.cand_t[wave] = tid;
+        sh.cand_above[wave] = above + (suf - mt);
+        sh.cand_single[wave] = ct == 1u;
       }
     }
+    __syncthreads();
+    int bw = TP_NB / 64 - 1;
+    while (bw > 0 && sh.cand_t[bw] < 0) --bw;
+    // (a digit always qualifies: the set holds the wanted key)
+    const int dt = sh.cand_t[bw] < 0 ? 0 : sh.cand_t[bw];
+    P = (P << w) | (unsigned long long)dt;
+    above = sh.cand_above[bw];
+    const int single = sh.cand_single[bw];
+    __syncthreads();
+    if (single || lo == 0) break;
   }
-  __syncthreads();
+  // the one candidate with these high bits
 #pragma unroll
-  for (int s = 0; s < E; ++s) {
-    ev[tid * E + s] = __uint_as_float((uint32_t)(key[s] >> 16));
-    ix[tid * E + s] = (uint16_t)(0xffffu - (unsigned)(key[s] & 0xffffu));
-  }
+  for (int s = 0; s < TP_E; ++s)
+    if (key[s] != 0ull && (key[s] >> lo) == P) { sh.found_key = key[s]; sh.found_mass = m[s]; }
+  __syncthreads();
+  *k_out = sh.found_key;
+  *m_out = above + sh.found_mass;
   __syncthreads();
 }
 
@@ -212,11 +248,8 @@ template <typename T>
 __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  __shared__ float ev[SMP_MAXN];       // e values, then their inclusive scan
-  __shared__ uint16_t ix[SMP_MAXN];    // candidate index
+  __shared__ TopPShared tps;
   __shared__ Best shb[SMP_THREADS / 64];
-  __shared__ int shc[SMP_THREADS / 64];
-  __shared__ float wsum[SMP_THREADS / 64];
   __shared__ int choice;
   __shared__ int ras_hit;
 
@@ -255,50 +288,30 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
 
   // top-p draw with uniform u: every thread takes part; sets choice
   auto topp = [&](float temperature, float top_p, float u) __attribute__((always_inline)) {
-    // ---- top-p ----
-    int NP = 1;
-    while (NP < nc) NP <<= 1;
     const float zmax = best.v;
     const float invT = 1.0f / temperature;
-    if (NP < SMP_THREADS * 4) NP = SMP_THREADS * 4;
-    if (NP == SMP_THREADS * 4) topp_sort<4>(z, p, nc, zmax, invT, ev, ix, cand_id, cand_ok);
-    else topp_sort<8>(z, p, nc, zmax, invT, ev, ix, cand_id, cand_ok);
-    // inclusive scan: each thread owns NP/1024 consecutive entries (or one)
-    const int per = NP >= SMP_THREADS ? NP / SMP_THREADS : 1;
-    const int beg = tid * per;
-    float run = 0.f;
-    if (beg < NP) {
-      for (int q = 0; q < per; ++q) { run += ev[beg + q]; ev[beg + q] = run; }
-    }
-    // exclusive scan of thread totals (wave scan, then across waves)
-    const int lane = tid & 63, wave = tid >> 6;
-    float incl = run;
+    unsigned long long key[TP_E], m[TP_E];
+    unsigned long long tot = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
+    for (int s = 0; s < TP_E; ++s) {
+      const int i = tid + s * SMP_THREADS;
+      float e = 0.f;
+      if (i < nc && cand_ok(i)) e = expf((z[p.restricted ? i : cand_id(i)] - zmax) * invT);
+      // key 0 marks "no candidate": a candidate's key is never 0 (its index
+      // bits are 8191 - i > 0 for i < 8191)
+      key[s] = i < nc ? ((unsigned long long)__float_as_uint(e) << TP_IDX_BITS) |
+                            (unsigned long long)((1 << TP_IDX_BITS) - 1 - i)
+                      : 0ull;
+      m[s] = __float2ull_rn(e * 1099511627776.0f);   // e * 2^40
+      tot += m[s];
     }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    float woff = 0.f;
-    for (int w = 0; w < wave; ++w) woff += wsum[w];
-    const float off = woff + (incl - run);
-    if (beg < NP)
-      for (int q = 0; q < per; ++q) ev[beg + q] += off;
-    __syncthreads();
-    const float total = ev[NP - 1];
-    const float thr = top_p * total;
-    int cnt = 0;
-    for (int i = tid; i < NP; i += SMP_THREADS) cnt += ev[i] < thr;
-    int n_keep = block_count(cnt, shc) + 1;
-    if (n_keep > nc) n_keep = nc;
-    const float kept = ev[n_keep - 1];
-    const float target = u * kept;
-    int c2 = 0;
-    for (int i = tid; i < n_keep; i += SMP_THREADS) c2 += ev[i] <= target;
-    int pick = block_count(c2, shc);
-    if (pick > n_keep - 1) pick = n_keep - 1;
-    if (tid == 0) choice = ix[pick];
+    tot = block_sum_u64(tot, tps);
+    unsigned long long kb, kept;
+    tp_select(key, m, fmin((double)top_p * (double)tot, (double)tot), false, tps, &kb, &kept);
+    const double target = (double)u * (double)kept;
+    unsigned long long kd = kb, md;
+    if (target < (double)kept) tp_select(key, m, target, true, tps, &kd, &md);
+    if (tid == 0) choice = (1 << TP_IDX_BITS) - 1 - (int)(kd & ((1ull << TP_IDX_BITS) - 1));
   };
   const float* ub = p.uniforms ? p.uniforms + (size_t)f * p.u_frame_stride + (size_t)b * p.u_row_stride : nullptr;
   if (p.greedy) {
