@@ -466,7 +466,9 @@ def main():
         m = dict(m, w4a16=1)
     if args.semantic_head:
         m = dict(m, semantic_head=1)
-    K = args.steps if args.steps is not None else min(wl["frames"], 256)
+    # 20 steps per repetition unless given: five repetitions then span ~100
+    # frames, so the context (and the attention's share) grows by under 10 %
+    K = args.steps if args.steps is not None else 20
     W = args.warmup
     reps = max(1, args.reps)
 
