@@ -324,6 +324,20 @@ def test_tiny_temperature_top_p_half(tiny):
     assert sum(c) >= 8
 
 
+@pytest.mark.parametrize("top_p,temp", [(1.0, 2.0), (0.02, 0.5), (0.999, 1.0)])
+def test_tiny_top_p_extremes(tiny, top_p, temp):
+    # the sampler's nucleus at its ends: every candidate kept (top_p 1 at a
+    # high temperature: the draw walks the whole order), a nucleus of one or
+    # two tokens, and a boundary near the tail of the order
+    m, w = tiny
+    plen = np.array([7, 21, 3, 30, 16], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=9)
+    U = synth.make_uniforms((5, 5, m["num_codebooks"]), seed=9)
+    c, _ = run_and_compare(m, w, P, plen, 4, dict(greedy=0, temperature=temp, top_p=top_p), U, tol=1e-4,
+                           tag=f"tiny-topp{top_p}-T{temp}")
+    assert sum(c) >= 10
+
+
 @pytest.mark.parametrize("fast_qk", [1, 0])
 def test_tiny_bf16_kv(fast_qk):
     m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
@@ -335,10 +349,12 @@ def test_tiny_bf16_kv(fast_qk):
     assert sum(c) >= 12
 
 
-@pytest.mark.parametrize("B", [11, 33])
+@pytest.mark.parametrize("B", [11, 33, 70])
 def test_tiny_bf16_batched_matrix_cores(B):
-    # 8+ activation rows take the matrix-core GEMM (split-K partials, ragged
-    # batch tiles); top-p draws from supplied uniforms.
+    # 2+ activation rows take the matrix-core products: one or two 32-row
+    # activation tiles the stream-K form (11, 33), three the split-K form
+    # with its finish (70); ragged batch tiles; top-p draws from supplied
+    # uniforms.
     m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
                     n_head=8, n_kv_head=2, fast_n_head=8, fast_n_kv_head=2)
     w = synth.make_weights(m, seed=2)
