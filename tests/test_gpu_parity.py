@@ -338,6 +338,23 @@ def test_tiny_top_p_extremes(tiny, top_p, temp):
     assert sum(c) >= 10
 
 
+@pytest.mark.parametrize("greedy", [1, 0])
+def test_tiny_degenerate_shapes(greedy):
+    # the smallest model the config accepts: 2 codebooks of 2 codes (one fast
+    # draw per frame, a draw between two candidates), one slow and one fast
+    # layer (fast pass 0 is only the K/V rows of that layer)
+    m = synth.model("tiny", num_codebooks=2, codebook_size=2, semantic_begin_id=1024, semantic_end_id=1025,
+                    acoustic_size=2, n_layer=1, n_fast_layer=1)
+    w = synth.make_weights(m, seed=4)
+    plen = np.array([1, 9, 4], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=4)
+    U = synth.make_uniforms((7, 3, m["num_codebooks"]), seed=4)
+    samp = dict(greedy=1) if greedy else dict(greedy=0, temperature=1.0, top_p=0.9)
+    c, _ = run_and_compare(m, w, P, plen, 6, samp, None if greedy else U, tol=1e-4, min_frames=1 << 20,
+                           tag=f"tiny-degenerate-g{greedy}")
+    assert sum(c) >= 9
+
+
 @pytest.mark.parametrize("fast_qk", [1, 0])
 def test_tiny_bf16_kv(fast_qk):
     m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
