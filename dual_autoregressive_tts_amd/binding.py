@@ -13,11 +13,13 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdualar.so")
+# DUALAR_LIBRARY selects another build of the library (e.g. the checked one)
+LIB_PATH = os.environ.get("DUALAR_LIBRARY") or os.path.join(HERE, "libdualar.so")
+CHECKED_LIB_PATH = os.path.join(HERE, "libdualar_checked.so")
 
 OK = 0
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "NO_DEVICE", -3: "WORKSPACE", -4: "CONTEXT_FULL",
-          -5: "BAD_TOKEN", -6: "STATE", -7: "HIP", -8: "DEVICE_FAULT"}
+          -5: "BAD_TOKEN", -6: "STATE", -7: "HIP", -8: "DEVICE_FAULT", -9: "DEVICE_INDEX"}
 F32, BF16 = 0, 1
 
 
@@ -78,16 +80,17 @@ EXPORTS = ("dualar_workspace_bytes", "dualar_create", "dualar_create_static", "d
            "dualar_destroy", "dualar_status_string", "dualar_last_error")
 K_GEMV, K_ATTN, K_SAMPLE, K_EMBED, K_GEMV_SWIGLU = 0, 1, 2, 3, 4
 
-_lib = None
+_libs = {}
 
 
 def load_library(path: str = LIB_PATH):
-    """Load libdualar.so and declare its signatures (fails loudly if absent)."""
-    global _lib
-    if _lib is not None:
-        return _lib
+    """Load a build of the library (default libdualar.so) and declare its
+    signatures; fails loudly if it is absent.  Each path is loaded once."""
+    path = os.path.abspath(path)
+    if path in _libs:
+        return _libs[path]
     if not os.path.exists(path):
-        raise FileNotFoundError(f"{path} is not built; run `python -m dual_autoregressive_tts_amd.build`")
+        raise FileNotFoundError(f"{path} is not built; run `python -m dual_autoregressive_tts_amd.build --all`")
     lib = C.CDLL(path)
     P, I32, VP = C.POINTER, C.c_int32, C.c_void_p
     lib.dualar_workspace_bytes.argtypes = [P(Config)]
@@ -118,7 +121,7 @@ def load_library(path: str = LIB_PATH):
     lib.dualar_status_string.restype = C.c_char_p
     lib.dualar_last_error.argtypes = [VP]
     lib.dualar_last_error.restype = C.c_char_p
-    _lib = lib
+    _libs[path] = lib
     return lib
 
 
@@ -153,8 +156,8 @@ def make_config(m: dict, max_batch: int, max_seq_len: int, inherit_fast: bool = 
     return c
 
 
-def workspace_bytes(cfg: Config) -> int:
-    return int(load_library().dualar_workspace_bytes(C.byref(cfg)))
+def workspace_bytes(cfg: Config, lib=None) -> int:
+    return int((lib or load_library()).dualar_workspace_bytes(C.byref(cfg)))
 
 
 def upload_weights(m: dict, w: dict, device="cuda"):
@@ -179,16 +182,18 @@ class DualAR:
     """One decode context (dualar_create) over device weights."""
 
     def __init__(self, m: dict, dev_weights: dict, max_batch: int, max_seq_len: int, stream=None,
-                 inherit_fast: bool = False, prefill_chunk: int = 0, static_workspace: bool = False):
+                 inherit_fast: bool = False, prefill_chunk: int = 0, static_workspace: bool = False,
+                 library: str | None = None):
         """static_workspace: dualar_create_static (the library's static device
-        workspace, nothing allocated here; one such context per GPU at a time)."""
+        workspace, nothing allocated here; one such context per GPU at a time).
+        library: path of another build of the library (e.g. CHECKED_LIB_PATH)."""
         import torch
         self.torch = torch
-        self.lib = load_library()
+        self.lib = load_library() if library is None else load_library(library)
         self.m = m
         self.N = m["num_codebooks"]
         self.cfg = make_config(m, max_batch, max_seq_len, inherit_fast, prefill_chunk)
-        self.ws_bytes = workspace_bytes(self.cfg)
+        self.ws_bytes = workspace_bytes(self.cfg, self.lib)
         if self.ws_bytes == 0:
             raise DualARError(-1, "invalid config")
         self.dev_weights = dev_weights

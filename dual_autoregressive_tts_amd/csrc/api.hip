@@ -18,11 +18,25 @@
 #include <string>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/dualar.h"
 #include "common.h"
 #include "internal.h"
 
 namespace {
+
+// A host-side marker range around the enqueue of one part of the path
+// (dualar.prefill, dualar.frame, dualar.slow, dualar.head, dualar.fast,
+// dualar.fast_tf): rocprofv3 --marker-trace records it beside the kernels
+// launched inside it.  Without a profiler attached a push or pop is a call
+// that returns at once.
+struct MarkerRange {
+  explicit MarkerRange(const char* name) { roctxRangePush(name); }
+  ~MarkerRange() { roctxRangePop(); }
+  MarkerRange(const MarkerRange&) = delete;
+  MarkerRange& operator=(const MarkerRange&) = delete;
+};
 
 thread_local std::string g_create_err;
 
@@ -73,6 +87,12 @@ bool resolve(const dualar_config* c, Resolved* r, std::string* err) {
     *err = buf;                              \
     return false;                            \
   }
+  REQ(c->fast_dim >= 0 && c->fast_n_head >= 0 && c->fast_n_kv_head >= 0 && c->fast_head_dim >= 0 &&
+          c->fast_ffn_dim >= 0, "fast_* sizes must be >= 0 (0 = inherit)");
+  REQ(c->slow_qk_norm == 0 || c->slow_qk_norm == 1, "slow_qk_norm must be 0 or 1");
+  REQ(c->fast_qk_norm >= -1 && c->fast_qk_norm <= 1, "fast_qk_norm must be 1, 0 or -1 (inherit)");
+  REQ(c->scale_codebook_embeddings == 0 || c->scale_codebook_embeddings == 1,
+      "scale_codebook_embeddings must be 0 or 1");
   REQ(r->dtype == DUALAR_F32 || r->dtype == DUALAR_BF16, "weight_dtype must be DUALAR_F32 or DUALAR_BF16");
   REQ(r->kvdtype == DUALAR_F32 || r->kvdtype == DUALAR_BF16, "kv_dtype must be -1, DUALAR_F32 or DUALAR_BF16");
   r->esz = r->dtype == DUALAR_BF16 ? 2 : 4;
@@ -251,6 +271,8 @@ hipError_t gemv(dualar_ctx* c, const GemvParams& g0) {
   g.xn = (void*)(c->ws + c->L.xn);
   g.part = c->L.gpart_elems ? (float*)(c->ws + c->L.gpart) : nullptr;
   g.part_elems = c->L.gpart_elems;
+  g.status = c->st.status;
+  g.prep.status = c->st.status;
   const bool sw = g.mode == GEMV_SWIGLU;
   hipError_t e = prof_pre(c, DUALAR_K_GEMV, sw);
   if (e != hipSuccess) return e;
@@ -345,6 +367,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
     a.H = S.H; a.KV = S.KV; a.hd = S.hd;
     a.out = att; a.ld_out = L.att_ld; a.out_planes = planes; a.R = B; a.B = B / rows_per_seq;
+    a.status = c->st.status;
     HIPCHK((launch_depth_attn<T, KT>(a, c->stream)));
   } else if (rows_per_seq > 0) {
     // prefill chunk: QK-norm, RoPE, append for every row, then causal attention
@@ -357,6 +380,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
     a.H = S.H; a.KV = S.KV; a.hd = S.hd;
     a.out = att; a.ld_out = L.att_ld; a.out_planes = planes; a.R = B; a.B = B / rows_per_seq;
+    a.status = c->st.status;
     HIPCHK((launch_prefill_attn<T, KT>(a, c->stream)));
   } else if (B == 1 && !pos_dev && sizeof(T) == 2 && sizeof(KT) == 2 && !w4.q4[3] &&
              attn_o_b1_fits(S.H, S.KV, S.hd, S.dim, pos_const + 1)) {
@@ -369,6 +393,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
     a.H = S.H; a.KV = S.KV; a.hd = S.hd;
     a.wo = w.wo; a.x = x; a.dim = S.dim;
+    a.status = c->st.status;
     HIPCHK(prof_pre(c, DUALAR_K_GEMV));
     HIPCHK(launch_attn_o_b1(a, c->stream));
     HIPCHK(prof_post(c, DUALAR_K_GEMV, (double)S.dim * S.H * S.hd * r.esz +
@@ -383,6 +408,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   a.max_pos = S.max_pos; a.pos = pos_dev; a.pos_const = pos_const; a.rope = S.rope;
   a.q_norm = S.qk ? w.q_norm : nullptr; a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
   a.H = S.H; a.KV = S.KV; a.hd = S.hd;
+  a.status = c->st.status;
   // Up to batch 4 with contexts of at most 2,048 positions: the split form
   // with 4 loads per lane (batch 1, 1k context: 12.0 us per layer against 14.7
   // with 2).  Otherwise the balanced flash-decoding form (it = 8): at batch 4
@@ -432,6 +458,7 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
     mo.part = a.part; mo.chunk = mo_chunk; mo.max_splits = (Lmax + mo_chunk - 1) / mo_chunk;
     mo.att = att; mo.pos = pos_dev; mo.H = S.H; mo.hd = S.hd;
     mo.wo = w.wo; mo.x = x; mo.dim = S.dim;
+    mo.status = c->st.status;
     HIPCHK(prof_pre(c, DUALAR_K_GEMV));
     HIPCHK(launch_merge_o_b1(mo, c->stream));
     HIPCHK(prof_post(c, DUALAR_K_GEMV, (double)S.dim * S.H * S.hd * r.esz +
@@ -503,6 +530,7 @@ dualar_status run_layer_kv_only(dualar_ctx* c, Stack& S, int l, float* x, int B,
   a.max_pos = S.max_pos; a.pos = nullptr; a.pos_const = 0; a.C = 1; a.rope = S.rope;
   a.k_norm = S.qk ? w.k_norm : nullptr; a.eps = r.eps;
   a.H = S.H; a.KV = S.KV; a.hd = S.hd; a.R = B; a.B = B;
+  a.status = c->st.status;
   HIPCHK((launch_kv_append<T, KT>(a, c->stream)));
   return DUALAR_OK;
 }
@@ -555,6 +583,7 @@ dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
   float* xs = (float*)(c->ws + L.x_slow);
   float* xf = (float*)(c->ws + L.x_fast);
   if (!io.fast_only) {
+    MarkerRange mr("dualar.head");
     if (io.taps && io.taps->slow_hidden)
       HIPCHK(hipMemcpyAsync(io.taps->slow_hidden, xs, (size_t)B * r.dim * 4, hipMemcpyDeviceToDevice, c->stream));
     // The tied head over the whole vocabulary, or (semantic_head, unless the
@@ -584,6 +613,7 @@ dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
     if (restricted) { sp.restricted = 1; sp.ld = r.C + 1; }
     HIPCHK(sample<T>(c, sp));
   }
+  MarkerRange mr("dualar.fast");
   // fast pass 0: the slow hidden state at depth position 0
   bool pl = false;
   for (int l = 0; l + 1 < r.fn_layer; ++l) {
@@ -711,6 +741,7 @@ dualar_status do_decode(dualar_ctx* c, int n_frames, const FrameIO& io) {
   for (int b = 0; b < B; ++b) maxp = std::max(maxp, c->plen[b]);
   float* xs = (float*)(c->ws + c->L.x_slow);
   for (int f = 0; f < n_frames; ++f) {
+    MarkerRange mr("dualar.frame");
     dualar_status st = embed<T>(c, B, nullptr, 0, 0, 0);
     if (st) return st;
     const bool last = f == n_frames - 1;
@@ -719,10 +750,13 @@ dualar_status do_decode(dualar_ctx* c, int n_frames, const FrameIO& io) {
     const int Lmax = maxp + c->frames_done + f + 1;
     c->step_pos.resize(B);
     for (int b = 0; b < B; ++b) c->step_pos[b] = c->plen[b] + c->frames_done + f;
-    bool pl = false;
-    for (int l = 0; l < c->r.n_layer; ++l) {
-      st = run_layer<T, KT>(c, c->slow, l, xs, B, c->st.pos, 0, Lmax, pl);
-      if (st) return st;
+    {
+      MarkerRange ms("dualar.slow");
+      bool pl = false;
+      for (int l = 0; l < c->r.n_layer; ++l) {
+        st = run_layer<T, KT>(c, c->slow, l, xs, B, c->st.pos, 0, Lmax, pl);
+        if (st) return st;
+      }
     }
     FrameIO fio = io;
     if (!last) fio.taps = nullptr;
@@ -736,6 +770,7 @@ template <typename T, typename KT>
 dualar_status do_fast(dualar_ctx* c, int B, int n_frames, const float* hidden, const int* q0, const FrameIO& io) {
   HIPCHK(launch_frame_reset(c->st, c->stream));
   for (int f = 0; f < n_frames; ++f) {
+    MarkerRange mr("dualar.frame");
     FastBeginParams fb{};
     fb.hidden = hidden; fb.q0 = q0; fb.fast_emb = c->w.fast_embeddings; fb.dim = c->r.dim; fb.C = c->r.C;
     fb.N = c->r.N; fb.x_slow = (float*)(c->ws + c->L.x_slow); fb.x_fast = (float*)(c->ws + c->L.x_fast);
@@ -995,6 +1030,7 @@ dualar_status dualar_prefill(dualar_ctx_t* c, int32_t batch, const int32_t* toke
   c->ready = false;
   const int urs = c->r.N + (s->ras_window > 0 ? 1 : 0);   // draws per sequence (slot N: the loop breaker's)
   FrameIO io{s, uniforms, 0, urs, frame0, c->r.N + 1, 0, taps, false};
+  MarkerRange mr("dualar.prefill");
   dualar_status st = dispatch(c, [&](auto wt, auto kt) {
     return do_prefill<decltype(wt), decltype(kt)>(c, batch, tokens, t_max, io);
   });
@@ -1056,6 +1092,7 @@ dualar_status dualar_fast_teacher_forced(dualar_ctx_t* c, int32_t n, const float
     return fail(c, DUALAR_ERR_INVALID_ARG, "teacher-forced form needs N <= 11, fast head_dim <= 128 (a multiple "
                                            "of 4), 1, 2, 4 or 8 query heads per KV head");
   // the activation buffers are scratch between calls: the decode state is untouched
+  MarkerRange mr("dualar.fast_tf");
   return dispatch(c, [&](auto wt, auto kt) {
     return do_fast_tf<decltype(wt), decltype(kt)>(c, n, hidden, codes, logits);
   });
@@ -1070,7 +1107,8 @@ dualar_status dualar_sync(dualar_ctx_t* c, int32_t* device_status) {
   if (st) {
     HIPCHK(hipMemset(c->st.status, 0, 4));
     if (st & ST_BAD_TOKEN) return fail(c, DUALAR_ERR_BAD_TOKEN, "an id outside its range reached the device");
-    return fail(c, DUALAR_ERR_DEVICE_FAULT, "a non-finite logit reached the sampler");
+    if (st & ST_NONFINITE) return fail(c, DUALAR_ERR_DEVICE_FAULT, "a non-finite logit reached the sampler");
+    return fail(c, DUALAR_ERR_DEVICE_INDEX, "a device index check failed (checked build)");
   }
   return DUALAR_OK;
 }
@@ -1130,6 +1168,7 @@ const char* dualar_status_string(dualar_status s) {
     case DUALAR_ERR_STATE: return "bad state";
     case DUALAR_ERR_HIP: return "HIP error";
     case DUALAR_ERR_DEVICE_FAULT: return "device fault";
+    case DUALAR_ERR_DEVICE_INDEX: return "device index check failed";
   }
   return "unknown status";
 }

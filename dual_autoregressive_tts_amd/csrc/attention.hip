@@ -38,7 +38,7 @@ typedef float att_f32x4 __attribute__((ext_vector_type(4)));
 template <typename T, typename KT, int IT, int REP, bool MQK = false>
 __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int pos = p.pos ? p.pos[b] : p.pos_const;
+  const int pos = row_position(p.pos, p.pos_const, b, p.max_pos, p.status);
   if (pos < 0) return;                      // inactive row (prefill padding)
   const int L = pos + 1;
   const int n_splits = (L + p.chunk - 1) / p.chunk;
@@ -298,7 +298,7 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
       if (p.out_planes) store_planes(p.out_planes, (size_t)p.B * p.H * hd, (size_t)b * p.H * hd + col, o / ml[hl][1]);
       else p.out[(size_t)b * p.ld_out + col] = o / ml[hl][1];
     } else {
-      float* pp = p.part + (((size_t)b * p.H + g * rep + hl) * p.max_splits + split) * (hd + 2);
+      float* pp = p.part + (((size_t)b * p.H + g * rep + hl) * p.max_splits + checked_index(split, p.max_splits, p.status)) * (hd + 2);
       pp[e] = o;
       if (e == 0) { pp[hd] = ml[hl][0]; pp[hd + 1] = ml[hl][1]; }
     }
@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(DUALAR_WG) attn_partial_kernel(AttnParams p) {
 template <typename T, typename KT>
 __global__ void __launch_bounds__(64) attn_prep_kernel(AttnParams p) {
   const int b = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
-  const int pos = p.pos ? p.pos[b] : p.pos_const;
+  const int pos = row_position(p.pos, p.pos_const, b, p.max_pos, p.status);
   if (pos < 0) return;
   const int hd = p.hd;
   const bool live = 2 * lane < hd;
@@ -390,7 +390,7 @@ __global__ void __launch_bounds__(64) attn_prep_kernel(AttnParams p) {
 __device__ __forceinline__ void fl_prefix(const AttnParams& p, int lane, int* E, int* cnt) {
   int n = 0;
   if (lane < p.B) {
-    const int pos = p.pos ? p.pos[lane] : p.pos_const;
+    const int pos = row_position(p.pos, p.pos_const, lane, p.max_pos, p.status);
     n = pos < 0 ? 0 : ((pos + 1 + FL_TILE - 1) / FL_TILE) * p.KV;
   }
   int x = n;       // inclusive scan
@@ -436,7 +436,7 @@ __global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, 
     const int g = (u - Eb) / ntb, t0 = (u - Eb) % ntb;
     const int hfirst = Eb + g * ntb, hend = hfirst + ntb;
     const int useg = min(u1, hend);
-    const int pos = p.pos ? p.pos[b] : p.pos_const;
+    const int pos = row_position(p.pos, p.pos_const, b, p.max_pos, p.status);
     const int c0 = t0 * FL_TILE, c1 = min((useg - hfirst) * FL_TILE, pos + 1);
     const int ntile = useg - u;
     const int slot = wg - fl_owner(hfirst, q, rr);
@@ -589,7 +589,7 @@ __global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, 
         if (p.out_planes) store_planes(p.out_planes, (size_t)p.B * p.H * HD, (size_t)b * p.H * HD + colx, o / l);
         else p.out[(size_t)b * p.ld_out + colx] = o / l;
       } else {
-        float* pp = p.part + (((size_t)b * p.H + g * REP + hl) * p.max_splits + slot) * (HD + 2);
+        float* pp = p.part + (((size_t)b * p.H + g * REP + hl) * p.max_splits + checked_index(slot, p.max_splits, p.status)) * (HD + 2);
         pp[e] = o;
         if (e == 0) { pp[HD] = M; pp[HD + 1] = l; }
       }
@@ -604,7 +604,7 @@ __global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, 
 __global__ void __launch_bounds__(128) attn_flash_merge_kernel(AttnParams p, int ng) {
   const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
-  const int pos = p.pos ? p.pos[b] : p.pos_const;
+  const int pos = row_position(p.pos, p.pos_const, b, p.max_pos, p.status);
   if (pos < 0) return;
   int E, cnt;
   fl_prefix(p, lane, &E, &cnt);
@@ -659,7 +659,7 @@ __global__ void __launch_bounds__(128) attn_flash_merge_kernel(AttnParams p, int
 __global__ void __launch_bounds__(MERGE_T) attn_merge_kernel(AttnParams p) {
   const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
-  const int pos = p.pos ? p.pos[b] : p.pos_const;
+  const int pos = row_position(p.pos, p.pos_const, b, p.max_pos, p.status);
   if (pos < 0) return;
   const int n_splits = (pos + 1 + p.chunk - 1) / p.chunk;
   if (n_splits == 1) return;                   // the partial kernel wrote o
@@ -730,7 +730,7 @@ __global__ void __launch_bounds__(64) attn_depth_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float pe[REP][MAXL];
   const int lane = threadIdx.x;
   const int b = blockIdx.x / p.KV, g = blockIdx.x % p.KV;
-  const int pos = p.pos ? p.pos[b] : p.pos_const;
+  const int pos = row_position(p.pos, p.pos_const, b, p.max_pos, p.status);
   if (pos < 0) return;                        // inactive row
   const int L = pos + 1;
   const int jm = lane & 15, kq = lane >> 4;

@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(WGT) attn_o_b1_kernel(AttnOParams p) {
   __shared__ float part[NW][R];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = wave;                       // KV head
-  const int pos = p.pos, L = pos + 1;
+  const int pos = checked_index(p.pos, p.max_pos, p.status), L = pos + 1;
   const int K = p.H * HD;
   const int row0 = blockIdx.x * R;
 
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(WGT) merge_o_b1_kernel(MergeOParams p) {
   const int row0 = blockIdx.x * R;
   const int K = p.H * HD;
   const int L = p.pos[0] + 1;
-  const int ns = (L + p.chunk - 1) / p.chunk;
+  const int ns = checked_index((L + p.chunk - 1) / p.chunk - 1, min(p.max_splits, MAXS), p.status) + 1;
   const int h = wave * REP + (lane >> 4), d0 = (lane & 15) * 8;
 
   // 1. partials (or o), residual, then the weights
@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(WGT) attn_split_b1_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float ow[NW][REP][HD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, g = blockIdx.y;
-  const int pos = p.pos ? p.pos[0] : p.pos_const;
+  const int pos = row_position(p.pos, p.pos_const, 0, p.max_pos, p.status);
   const int L = pos + 1;
   const int n_splits = (L + CH - 1) / CH;
   if (split >= n_splits) return;
@@ -558,7 +558,7 @@ __global__ void __launch_bounds__(WGT) attn_split_b1_kernel(AttnParams p) {
     if (n_splits == 1) {
       p.out[(size_t)hh * HD + d] = acc / lsum;
     } else {
-      float* pp = p.part + ((size_t)hh * p.max_splits + split) * (HD + 2);
+      float* pp = p.part + ((size_t)hh * p.max_splits + checked_index(split, p.max_splits, p.status)) * (HD + 2);
       pp[d] = acc;
       if (d == 0) { pp[HD] = M; pp[HD + 1] = lsum; }
     }

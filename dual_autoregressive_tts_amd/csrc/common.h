@@ -9,7 +9,32 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define DUALAR_WG 256
 
 // Status bits latched in the workspace status word.
-enum { ST_BAD_TOKEN = 1, ST_NONFINITE = 2 };
+enum { ST_BAD_TOKEN = 1, ST_NONFINITE = 2, ST_INDEX = 4 };
+
+// Index checks of the checked build (compiled with -DDUALAR_DEVICE_CHECKS).
+// checked_index(i, n, status) is i when 0 <= i < n; otherwise it latches
+// ST_INDEX in the status word (when status is set) and returns 0, so the
+// access it guards stays inside its buffer and the call reports the failure
+// at dualar_sync instead of touching memory it does not own.  In the normal
+// build it is i itself and costs nothing.
+#ifdef DUALAR_DEVICE_CHECKS
+__device__ __forceinline__ long long checked_index_ll(long long i, long long n, int* status) {
+  if (i >= 0 && i < n) return i;
+  if (status) atomicOr(status, ST_INDEX);
+  return 0;
+}
+#define checked_index(i, n, status) ((decltype(i))checked_index_ll((long long)(i), (long long)(n), (status)))
+#else
+#define checked_index(i, n, status) (i)
+#endif
+
+// Row b's position (pos == NULL: pos_const for every row); a negative one
+// marks an inactive row.  The checked build holds the others below max_pos,
+// the length of the cache and of the RoPE table.
+__device__ __forceinline__ int row_position(const int* pos, int pos_const, int b, int max_pos, int* status) {
+  const int v = pos ? pos[b] : pos_const;
+  return v < 0 ? v : checked_index(v, max_pos, status);
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

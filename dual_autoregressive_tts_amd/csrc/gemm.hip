@@ -570,7 +570,7 @@ __global__ void __launch_bounds__(64 * (WAVES + 1)) mfma_skw_kernel(GemvParams p
     gm_compute_wx<NR, T, G>(wst + (f % WS) * G::W_BYTES, xsl + (f % XS) * G::X_BYTES, wave, lane, acc);
     if (++cc == nch || f == nf - 1) {
       const int slot = g - sk_owner(ct * nch, q, rr);
-      float* dst = p.part + ((size_t)ct * p.sk_smax + slot) * Sk<NR, WAVES, T>::TE;
+      float* dst = p.part + ((size_t)ct * p.sk_smax + checked_index(slot, p.sk_smax, p.status)) * Sk<NR, WAVES, T>::TE;
 #pragma unroll
       for (int tt = 0; tt < T; ++tt)
 #pragma unroll
@@ -644,7 +644,7 @@ __global__ void __launch_bounds__(DUALAR_WG) sk_finish_kernel(GemvParams p) {
     // each: RMS over the half-wave, RoPE on the two local pairs.
     const QkPrep& q = p.prep;
     const int hh = t / Z, d0 = 4 * r4, hd = q.hd;
-    const int pos = q.pos ? q.pos[b] : q.pos_const;
+    const int pos = row_position(q.pos, q.pos_const, b, q.max_pos, q.status);
     float a[4] = {g4[0], g4[1], g4[2], g4[3]};
     *(float4*)(p.y + (size_t)b * p.ldy + n0) = make_float4(a[0], a[1], a[2], a[3]);
     const bool isq = hh < q.H, isk = !isq && hh < q.H + q.KV;

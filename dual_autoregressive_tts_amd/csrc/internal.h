@@ -34,6 +34,7 @@ struct QkPrep {
   int H, KV, hd, max_pos;
   void* kcache; void* vcache;         // this layer: [max_batch][KV][max_pos][hd] bf16
   uint16_t* q_planes;                 // [3][B][H*hd]; NULL = no preparation
+  int* status;                        // checked build: index failures latch ST_INDEX
 };
 
 // y[b, :] = W . f(x[b, :]) for b < B, where f is RMSNorm-with-gain when
@@ -83,6 +84,7 @@ struct GemvParams {
   // form deals out only those tiles (the outputs of padding rows are never
   // read).  bt_masked = 0: every row is live.
   uint64_t live_bt[2]; int bt_masked;
+  int* status;                   // checked build: index failures latch ST_INDEX
 };
 #define GEMM_TILE_BROWS 128   // activation rows per tile of the 2-D tile form
 
@@ -109,6 +111,7 @@ struct AttnParams {
   int prepped;                        // q_planes and the appended k/v are already written
   int no_merge;                       // split form: leave the partials for a fused merge
   int B;
+  int* status;                        // checked build: index failures latch ST_INDEX
 };
 
 // Batch-1 attention over a short cache (at most 16 positions: the fast AR's
@@ -123,6 +126,7 @@ struct AttnOParams {
   int H, KV, hd;
   const void* wo;                     // [dim][H*hd] bf16
   float* x; int dim;                  // residual row, updated in place
+  int* status;                        // checked build: index failures latch ST_INDEX
 };
 bool attn_o_b1_fits(int H, int KV, int hd, int dim, int L);
 hipError_t launch_attn_o_b1(const AttnOParams& p, hipStream_t s);
@@ -137,6 +141,7 @@ struct MergeOParams {
   int H, hd;
   const void* wo;                     // [dim][H*hd] bf16
   float* x; int dim;                  // residual row, updated in place
+  int* status;                        // checked build: index failures latch ST_INDEX
 };
 int merge_o_b1_max_splits();
 // batch-1 split attention (bf16 cache, S2 head shape) for chunks of 128 or 256
@@ -165,6 +170,7 @@ struct PrefillParams {
   float* out; int ld_out;             // [R][H*hd]
   uint16_t* out_planes;               // if set: o as planes [3][R][H*hd] instead of out
   int R, B;
+  int* status;                        // checked build: index failures latch ST_INDEX
 };
 
 // Per-sequence decode state kept in the workspace.

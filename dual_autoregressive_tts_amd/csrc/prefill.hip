@@ -26,7 +26,7 @@
 template <typename T, typename KT>
 __global__ void __launch_bounds__(64) prefill_append_kernel(PrefillParams p, int head0) {
   const int r = blockIdx.x, hh = head0 + blockIdx.y, lane = threadIdx.x;
-  const int pos = p.pos ? p.pos[r] : p.pos_const;
+  const int pos = row_position(p.pos, p.pos_const, r, p.max_pos, p.status);
   if (pos < 0) return;
   const int b = r / p.C, hd = p.hd;
   const bool live = 2 * lane < hd;
@@ -80,7 +80,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillParams p) {
   const int pos = i < p.C ? p.pos[r] : -1;
   // positions grow with i inside a chunk: the block's last real row has the largest
   const int last = min(i0 + QB, p.C) - 1;
-  const int pmax = p.pos[b * p.C + last];
+  const int pmax = row_position(p.pos, 0, b * p.C + last, p.max_pos, p.status);
   if (pmax < 0) return;                         // whole block is padding (uniform)
 
   __shared__ __attribute__((aligned(16))) float Ks[PF_TK][PF_MAXHD];
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int i0 = qb * PF16_QB;
   const int last = min(i0 + PF16_QB, p.C) - 1;
-  const int pmax = p.pos[b * p.C + last];
+  const int pmax = row_position(p.pos, 0, b * p.C + last, p.max_pos, p.status);
   if (pmax < 0) return;                          // the whole block is padding (uniform)
   const int nkb = pmax / 32 + 1;
 

@@ -34,6 +34,12 @@
  *   - Work is enqueued asynchronously on the context's stream.  Faults found
  *     on the device (an out-of-range id in a prompt, a non-finite logit) are
  *     latched in a status word and reported by dualar_sync().
+ *   - The checked build of the library (libdualar_checked.so, compiled with
+ *     DUALAR_DEVICE_CHECKS) also checks, in the kernels, every cache
+ *     position it appends at or reads up to against max_seq_len and every
+ *     partial-sum slot against its buffer; a failing check keeps the access
+ *     inside the buffer, latches a status bit and makes dualar_sync() return
+ *     DUALAR_ERR_DEVICE_INDEX.  The normal build compiles the checks out.
  *   - A context is bound to one stream and one device and is not thread-safe.
  */
 #ifndef DUALAR_H
@@ -55,7 +61,8 @@ typedef enum {
   DUALAR_ERR_BAD_TOKEN = -5,     /* device saw an id outside its range     */
   DUALAR_ERR_STATE = -6,         /* call out of order (decode before prefill) */
   DUALAR_ERR_HIP = -7,           /* a HIP runtime call failed              */
-  DUALAR_ERR_DEVICE_FAULT = -8   /* device saw a non-finite logit          */
+  DUALAR_ERR_DEVICE_FAULT = -8,  /* device saw a non-finite logit          */
+  DUALAR_ERR_DEVICE_INDEX = -9   /* checked build only: a device index check failed */
 } dualar_status;
 
 typedef enum { DUALAR_F32 = 0, DUALAR_BF16 = 1 } dualar_dtype;
@@ -299,8 +306,12 @@ dualar_status dualar_fast_teacher_forced(dualar_ctx_t *ctx, int32_t n, const flo
  * nothing. */
 dualar_status dualar_reset(dualar_ctx_t *ctx, const int32_t *seq_ids, int32_t n);
 
-/* Block until the stream's work is done; report latched device faults.
- * *device_status (host, may be NULL) receives the raw status word. */
+/* Block until the stream's work is done; report latched device faults and
+ * clear them.  *device_status (host, may be NULL) receives the raw status
+ * word: bit 0 an id outside its range (DUALAR_ERR_BAD_TOKEN), bit 1 a
+ * non-finite logit (DUALAR_ERR_DEVICE_FAULT), bit 2 a failed index check of
+ * the checked build (DUALAR_ERR_DEVICE_INDEX); with several bits set the
+ * first of these is returned. */
 dualar_status dualar_sync(dualar_ctx_t *ctx, int32_t *device_status);
 
 /* Measurement: after dualar_profile_begin(ctx, class), every launch of that

@@ -18,12 +18,16 @@ def lib():
     return bd.load_library()
 
 
-def test_exports_every_declared_symbol(lib):
+@pytest.mark.parametrize("path", [bd.LIB_PATH, bd.CHECKED_LIB_PATH], ids=["normal", "checked"])
+def test_exports_every_declared_symbol(path):
+    # both builds of the library (the checked one has the device index checks)
+    lib = bd.load_library(path)
     hdr = open(os.path.join(ROOT, "include", "dualar.h")).read()
     declared = set(re.findall(r"\b(dualar_[a-z_]+)\s*\(", hdr))
     assert declared == set(bd.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
+    assert lib.dualar_status_string(-9) == b"device index check failed"
 
 
 def test_status_strings(lib):
