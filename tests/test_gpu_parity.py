@@ -688,6 +688,54 @@ def test_s2_full_batch8_matrix_cores(s2_full, kv):
 
 
 # ----------------------------------------------------------------------------
+# S2 layer shapes past the stream-K range, up to the largest batch
+# ----------------------------------------------------------------------------
+
+def _s2_layers_model(**kw):
+    # S2 layer shapes with two slow layers and one fast layer; a 12,288-id
+    # vocabulary (4,096 semantic ids) keeps the tied head and the oracle small
+    return synth.model("s2", n_layer=2, n_fast_layer=1, vocab_size=12288, text_vocab=8000, end_id=8000,
+                       semantic_begin_id=8192, semantic_end_id=8192 + 4095, **kw)
+
+
+@pytest.fixture(scope="module")
+def s2_layers():
+    m = _s2_layers_model()
+    say("[s2-layers] generating weights")
+    w = synth.make_weights(m, seed=12)
+    return m, w, synth.weights_as_f32(m, w)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("B,kv", [(96, "f32"), (96, "bf16"), (256, "f32")])
+def test_s2_layers_large_batch(s2_layers, B, kv):
+    # 96 rows: three activation tiles, so the split-K products with their
+    # finish kernels, and the split attention with matrix-core scores (the
+    # balanced flash form takes at most 64 rows); the fast layers' depth
+    # attention.  256 rows, the largest batch a context holds: the 2-D tile
+    # products in decode too, with the attention preparing its own q, k, v.
+    # fp32 cache: top-p 0.9, ids compared strictly; bf16 cache: greedy under
+    # the rounding-floor bound.  The oracle replays six rows: the first, the
+    # last, the shortest and longest prompts and two in between.
+    m, w, w32 = s2_layers
+    m = dict(m, kv_dtype=kv)
+    plen = synth.make_ctx_lengths(B, 1, 60, seed=B)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=B)
+    rows = sorted({0, B - 1, int(np.argmin(plen)), int(np.argmax(plen)), B // 3, (2 * B) // 3})
+    F = 3
+    if kv == "f32":
+        samp, U = dict(greedy=0, temperature=1.0, top_p=0.9), synth.make_uniforms((F + 1, B, m["num_codebooks"]), seed=B)
+    else:
+        samp, U = dict(greedy=1), None
+    c, worst = run_and_compare(m, w, P, plen, F, samp, U, tag=f"s2-layers-B{B}-kv{kv}", floor=kv == "bf16",
+                               weights_f32=w32, rows=rows)
+    say(f"[s2-layers B={B} kv {kv}] rows {rows}: frames compared {c}")
+    assert sum(c) >= len(rows) * (F + 1) // 2
+    if kv == "f32":
+        assert max(worst.values()) < REL_L2
+
+
+# ----------------------------------------------------------------------------
 # teacher-forced fast AR (the scoring / training form, all pairs at once)
 # ----------------------------------------------------------------------------
 
