@@ -384,6 +384,7 @@ __global__ void __launch_bounds__(64) attn_prep_kernel(AttnParams p) {
 // the compiler's waits keep both buffers in flight.
 #define FL_TILE 128
 #define FL_MAXB 64
+#define FL_SLOTS 512   // workgroups of the balanced flash-decoding form (two per compute unit)
 
 // Tiles of each sequence and their exclusive prefix over sequences (times
 // KV), one sequence per lane (B <= 64): lanes >= B hold the total.
@@ -617,7 +618,9 @@ __global__ void __launch_bounds__(128) attn_flash_merge_kernel(AttnParams p, int
   if (n_slots == 1) return;                    // the flash kernel wrote o
   const int hd = p.hd;
   const float* pp = p.part + ((size_t)b * p.H + h) * p.max_splits * (hd + 2);
-  __shared__ float wsh[FL_MAXB * 4 + 8];
+  // a head's tiles can go to as many workgroups as the grid has (one tile
+  // each when a few long heads make up the whole walk)
+  __shared__ float wsh[FL_SLOTS];
   __shared__ float red[2];
   __shared__ float lred[2];
   float mloc = -INFINITY;
@@ -630,7 +633,7 @@ __global__ void __launch_bounds__(128) attn_flash_merge_kernel(AttnParams p, int
   for (int s = t; s < n_slots; s += 128) {
     const float* qv = pp + (size_t)s * (hd + 2);
     const float w = expf(qv[hd] - M);
-    wsh[s] = w;
+    wsh[checked_index(s, FL_SLOTS, p.status)] = w;
     lloc += qv[hd + 1] * w;
   }
   lloc = wave_sum(lloc);
@@ -714,7 +717,6 @@ int attn_chunk(int kv_esz, int hd, int it) {
   return 4 * (64 / lpp) * it;
 }
 
-#define FL_SLOTS 512   // workgroups of the balanced flash-decoding form (two per compute unit)
 
 // Batched attention over a short cache (at most 16 positions: the fast AR's
 // depth cache), bf16 cache, head_dim 128, 4 query heads per KV head, after

@@ -412,6 +412,21 @@ def test_bf16_small_batch_long_context():
         assert sum(c) >= 3 * len(plen)
 
 
+@pytest.mark.timeout(900)
+def test_bf16_long_context_past_32k():
+    # positions past 32,767 (45,000 and 20,000 prompt positions at batch 2):
+    # RoPE rows of the bf16 table that far out, the chunked prefill over 11
+    # steps of 4,096 positions, then the flash-decoding form with ~350 tiles
+    # per head split over the grid and merged
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
+                    n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1, fast_head_dim=128)
+    w = synth.make_weights(m, seed=13)
+    plen = np.array([45000, 20000], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=13)
+    c, worst = run_and_compare(m, w, P, plen, 2, dict(greedy=1), tag="bf16-past-32k", floor=True)
+    assert sum(c) >= 3
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("plen,kv", [(600, "bf16"), (1100, "bf16"), (1500, "bf16"), (300, "f32")])
 def test_batch1_s2_heads_merged_in_o_product(plen, kv):
