@@ -428,6 +428,30 @@ def test_bf16_long_context_past_32k():
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("n_head,n_kv,hd,kv", [(4, 4, 128, "bf16"), (8, 1, 128, "bf16"), (8, 1, 64, "bf16"),
+                                               (8, 1, 128, "f32"), (8, 4, 128, "bf16")])
+@pytest.mark.parametrize("B", [1, 6])
+def test_head_shapes(n_head, n_kv, hd, kv, B):
+    # query heads per KV head 1, 2 and 8 (the S2 shape, 4, runs everywhere
+    # else), head_dim 64 and 128, bf16 and fp32 caches, in the slow and the
+    # fast layers alike; contexts up to 2,400 positions so that both the
+    # 4-load and the 8-load attention splits run: 1 query head per KV head
+    # takes the balanced flash-decoding form, 8 the split form with its
+    # merge (matrix-core scores for head_dim 128 with a bf16 cache)
+    m = synth.model("tiny", weight_dtype="bf16", kv_dtype=kv, dim=512, ffn_dim=1024, fast_dim=512,
+                    fast_ffn_dim=1024, n_head=n_head, n_kv_head=n_kv, head_dim=hd, fast_n_head=n_head,
+                    fast_n_kv_head=n_kv, fast_head_dim=hd)
+    w = synth.make_weights(m, seed=14)
+    plen = np.array([2400], dtype=np.int32) if B == 1 else synth.make_ctx_lengths(B, 100, 2400, seed=14)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=14)
+    c, worst = run_and_compare(m, w, P, plen, 2, dict(greedy=1), tag=f"heads-{n_head}-{n_kv}-{hd}-{kv}-B{B}",
+                               floor=kv == "bf16")
+    assert sum(c) >= (3 * B + 1) // 2
+    if kv == "f32":
+        assert max(worst.values()) < REL_L2
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("plen,kv", [(600, "bf16"), (1100, "bf16"), (1500, "bf16"), (300, "f32")])
 def test_batch1_s2_heads_merged_in_o_product(plen, kv):
     # batch 1 with the S2 head shape (32 query / 8 KV heads of 128): the slow
