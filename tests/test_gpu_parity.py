@@ -509,6 +509,21 @@ def test_w4a16_batch1_s2_shapes():
     assert sum(c) >= 2
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dim,ffn,n_head", [(10240, 5632, 8), (1536, 3072, 12)])
+def test_w4a16_row_lengths(dim, ffn, n_head):
+    # 4-bit rows of other lengths than the S2 ones: 10,240 inputs (the
+    # largest accepted: 20 units over four waves, 80 chunks on the matrix
+    # cores), 5,632 (11 units over four waves with one dead unit), 1,024,
+    # 1,536 (3 units in one wave), 3,072 (6 units over two waves); slow layer
+    # 1 keeps its attention in bf16
+    m = synth.model("tiny", weight_dtype="bf16", dim=dim, ffn_dim=ffn, fast_dim=dim, fast_ffn_dim=ffn,
+                    n_head=n_head, n_kv_head=n_head // 4, head_dim=128, fast_n_head=n_head,
+                    fast_n_kv_head=n_head // 4, fast_head_dim=128, w4a16=1, w4_bf16_attn_layers=1)
+    c, worst = _w4_case(m, 15, 30, 3, f"w4-rows-{dim}-{ffn}")
+    assert sum(c) >= 2
+
+
 def test_end_token_stops_and_pads(tiny):
     m, w = tiny
     w = {k: v.copy() for k, v in w.items()}
