@@ -355,6 +355,34 @@ def test_tiny_degenerate_shapes(greedy):
     assert sum(c) >= 9
 
 
+@pytest.mark.parametrize("N,C,heads,B", [(32, 1000, "small", 3), (32, 1000, "s2", 1), (32, 1000, "s2", 6),
+                                          (3, 4096, "small", 4)])
+def test_codebook_counts_and_sizes(N, C, heads, B):
+    # 32 codebooks, the most the config accepts (31 fast passes; the fast
+    # layers' depth cache then holds more than the 16 positions of the fused
+    # batch-1 attention + O kernel and of the one-wave depth attention, so
+    # the general attention forms run there), a codebook of 1,000 codes;
+    # 3 codebooks of 4,096.  "small": the fp32 model with 4 query heads of
+    # 64 (top-p, strict bound); "s2": bf16 weights and cache with the S2
+    # head shape at dim 512 (greedy, rounding-floor bound)
+    kw = dict(num_codebooks=N, codebook_size=C, semantic_begin_id=1024, semantic_end_id=1024 + C - 1,
+              acoustic_size=min(C, 256))
+    if heads == "s2":
+        kw.update(weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024, n_head=32, n_kv_head=8,
+                  head_dim=128, fast_n_head=32, fast_n_kv_head=8, fast_head_dim=128)
+    m = synth.model("tiny", **kw)
+    w = synth.make_weights(m, seed=16)
+    plen = synth.make_ctx_lengths(B, 1, 40, seed=16)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=16)
+    if heads == "small":
+        samp, U, tol = dict(greedy=0, temperature=1.0, top_p=0.9), synth.make_uniforms((4, B, N), seed=16), 1e-4
+    else:
+        samp, U, tol = dict(greedy=1), None, REL_L2
+    c, worst = run_and_compare(m, w, P, plen, 3, samp, U, tol=tol, min_frames=1 << 20,
+                               tag=f"codebooks-{N}x{C}-{heads}-B{B}", floor=heads == "s2")
+    assert sum(c) >= 2 * B
+
+
 @pytest.mark.parametrize("fast_qk", [1, 0])
 def test_tiny_bf16_kv(fast_qk):
     m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
