@@ -324,11 +324,13 @@ def test_tiny_temperature_top_p_half(tiny):
     assert sum(c) >= 8
 
 
-@pytest.mark.parametrize("top_p,temp", [(1.0, 2.0), (0.02, 0.5), (0.999, 1.0)])
+@pytest.mark.parametrize("top_p,temp", [(1.0, 2.0), (0.02, 0.5), (0.999, 1.0), (0.9, 0.05), (0.9, 20.0)])
 def test_tiny_top_p_extremes(tiny, top_p, temp):
     # the sampler's nucleus at its ends: every candidate kept (top_p 1 at a
     # high temperature: the draw walks the whole order), a nucleus of one or
-    # two tokens, and a boundary near the tail of the order
+    # two tokens, and a boundary near the tail of the order; temperatures
+    # of 0.05 (most masses underflow: the fixed-point masses of all but the
+    # top few candidates are 0) and 20 (nearly flat)
     m, w = tiny
     plen = np.array([7, 21, 3, 30, 16], dtype=np.int32)
     P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=9)
