@@ -442,6 +442,28 @@ def test_bf16_small_batch_long_context():
         assert sum(c) >= 3 * len(plen)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("plen,B", [(2046, 1), (2558, 1), (2046, 3), (16, 1), (126, 6)])
+def test_attention_form_boundaries(plen, B):
+    # decode frames whose context crosses the host's switches between the
+    # attention forms from one frame to the next: 2,048 positions (4-load to 8-load
+    # splits: batch 1 stays in the split form merged inside the O product,
+    # batch 3 moves from the split form to the flash form), 2,560 (batch 1:
+    # past 10 splits of 256 positions the O product no longer merges and the
+    # flash form takes over), 16 positions at batch 1 and 128 at batch 6
+    # (one attention chunk / flash tile to two); S2 head shape at dim 512,
+    # bf16 cache, five frames
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024, n_head=32,
+                    n_kv_head=8, head_dim=128, fast_n_head=32, fast_n_kv_head=8, fast_head_dim=128)
+    w = synth.make_weights(m, seed=17)
+    lens = np.full(B, plen, dtype=np.int32)
+    lens[1:] -= np.arange(1, B, dtype=np.int32)          # ragged by one position per row
+    P = synth.make_prompts(m, ("ragged", 1, 1), lens, seed=17)
+    c, worst = run_and_compare(m, w, P, lens, 5, dict(greedy=1), min_frames=1 << 20,
+                               tag=f"form-boundary-{plen}-B{B}", floor=True)
+    assert sum(c) >= 3 * B
+
+
 @pytest.mark.timeout(900)
 def test_bf16_long_context_past_32k():
     # positions past 32,767 (45,000 and 20,000 prompt positions at batch 2):
