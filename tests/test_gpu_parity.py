@@ -301,6 +301,25 @@ def test_tiny_loop_breaker_window_changes(tiny):
     assert stats["ras_used"] > 0
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("pc", [4096, 1000])
+def test_bf16_prefill_many_row_tiles(pc):
+    # 8 sequences of 700..4,096 positions with 4,096 or 1,000 positions per
+    # sequence per prefill step: 32,768 and 8,000 activation rows per step.
+    # Past 128 tiles of 128 rows the host passes no live-tile mask and the
+    # 2-D tile products run every tile, padding rows included; 1,000 leaves
+    # a ragged 64-row last tile and five steps with the padding in front
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
+                    n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1, fast_head_dim=128)
+    w = synth.make_weights(m, seed=18)
+    plen = synth.make_ctx_lengths(8, 700, 4096, seed=18)
+    plen[0] = 4096
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=18)
+    c, worst = run_and_compare(m, w, P, plen, 2, dict(greedy=1), tag=f"bf16-prefill-pc{pc}", floor=True,
+                               prefill_chunk=pc, rows=[0, 1, 4, 7])
+    assert sum(c) >= 6
+
+
 @pytest.mark.parametrize("pc", [1, 3, 16, 64])
 def test_tiny_prefill_chunking(tiny, pc):
     # Prefill walks the right-aligned prompts pc positions at a time (pc = 1
