@@ -682,6 +682,56 @@ def test_multi_frame_call_equals_single_frame_calls(tiny):
     assert torch.equal(ca.cpu(), cb.cpu())
 
 
+@pytest.mark.parametrize("wdtype", ["f32", "bf16"])
+def test_two_contexts_on_two_streams(wdtype):
+    # two contexts over the same device weights, each bound to its own stream
+    # (default priority), their calls interleaved with no synchronisation in
+    # between: each emits exactly what it emits alone.  The library keeps no
+    # state shared between contexts.  bf16: batch 3 and 9, so the matrix-core
+    # products, the flash-decoding attention and the sampler run on both
+    # streams at once.
+    DualAR, upload = _dev()
+    kw = {} if wdtype == "f32" else dict(weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
+                                         n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1,
+                                         fast_head_dim=128)
+    m = synth.model("tiny", **kw)
+    dw = upload(m, synth.make_weights(m, seed=19))
+    N = m["num_codebooks"]
+    plens = [np.array([30, 12, 41], dtype=np.int32), synth.make_ctx_lengths(9, 1, 300, seed=19)]
+    Ps = [torch.from_numpy(synth.make_prompts(m, ("ragged", 1, 1), pl, seed=19 + i)).cuda() for i, pl in enumerate(plens)]
+    Us = [torch.from_numpy(synth.make_uniforms((7, len(pl), N), seed=19 + i)).cuda() for i, pl in enumerate(plens)]
+    S = DualAR.sampling(greedy=False, top_p=0.9)
+
+    def calls(ctx, i):
+        # prefill, then decode calls of 2, 3 and 1 frames
+        yield lambda: ctx.prefill(Ps[i], plens[i], S, Us[i][0].contiguous())
+        yield lambda: ctx.decode_frames(2, S, Us[i][1:3].contiguous())[0]
+        yield lambda: ctx.decode_frames(3, S, Us[i][3:6].contiguous())[0]
+        yield lambda: ctx.decode_frames(1, S, Us[i][6:7].contiguous())[0]
+
+    alone = []
+    for i in range(2):
+        ctx = DualAR(m, dw, max_batch=len(plens[i]), max_seq_len=400)
+        alone.append([f().cpu() for f in calls(ctx, i)])
+        ctx.close()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ctxs = [DualAR(m, dw, max_batch=len(plens[i]), max_seq_len=400, stream=streams[i]) for i in range(2)]
+    gens = [calls(ctxs[i], i) for i in range(2)]
+    outs = [[], []]
+    for _ in range(4):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(next(gens[i])())
+    for i in range(2):
+        assert ctxs[i].sync() == 0
+    torch.cuda.synchronize()
+    for i in range(2):
+        for a, b in zip(alone[i], outs[i]):
+            assert torch.equal(a, b.cpu()), i
+        ctxs[i].close()
+
+
 # ----------------------------------------------------------------------------
 # S2-shaped fast AR alone (batch 1 and 16)
 # ----------------------------------------------------------------------------
