@@ -25,7 +25,7 @@ def _dev():
 
 def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=REL_L2, min_frames=0,
                     tag="", weights_f32=None, floor=False, prefill_chunk=0, slow_logits_tap=True, ras=0,
-                    stats=None, rows=None, weights_f64=None):
+                    stats=None, rows=None, weights_f64=None, seq_slack=2):
     """Prefill + n_frames single-frame decode calls on the GPU; the oracle
     replays every sequence (or the sequences in `rows`).  Returns per-row
     counts of frames compared (whole frames whose ids all matched) and the
@@ -54,7 +54,8 @@ def run_and_compare(m, w_np, prompts, plen, n_frames, samp, uniforms=None, tol=R
     ras = max(ras_f)
     say(f"[{tag}] GPU: B={B} prompt_len={list(plen)[:8]} frames={n_frames} greedy={greedy}")
     dw = upload(m, w_np)
-    ctx = DualAR(m, dw, max_batch=B, max_seq_len=int(max(plen)) + n_frames + 2, prefill_chunk=prefill_chunk)
+    # seq_slack: cache positions left over after the last frame (0 fills it)
+    ctx = DualAR(m, dw, max_batch=B, max_seq_len=int(max(plen)) + n_frames + seq_slack, prefill_chunk=prefill_chunk)
     S_f = [DualAR.sampling(min_frames=min_frames, ras_window=r, **samp) for r in ras_f]
     tok = torch.from_numpy(np.ascontiguousarray(prompts)).cuda()
     U = None if uniforms is None else torch.from_numpy(np.ascontiguousarray(uniforms)).cuda()
@@ -481,6 +482,23 @@ def test_attention_form_boundaries(plen, B):
     c, worst = run_and_compare(m, w, P, lens, 5, dict(greedy=1), min_frames=1 << 20,
                                tag=f"form-boundary-{plen}-B{B}", floor=True)
     assert sum(c) >= 3 * B
+
+
+@pytest.mark.parametrize("plen,B", [(509, 1), (636, 6), (2555, 1)])
+def test_cache_filled_to_the_last_position(plen, B):
+    # max_seq_len = the longest prompt + the frames: the last frame writes
+    # and attends to the cache's (and the RoPE table's) last position, with
+    # the 128-position attention chunks / flash tiles ending exactly there
+    # (512 and 640 positions; 2,560 at batch 1 past 10 splits of 256)
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024, n_head=32,
+                    n_kv_head=8, head_dim=128, fast_n_head=32, fast_n_kv_head=8, fast_head_dim=128)
+    w = synth.make_weights(m, seed=20)
+    lens = np.full(B, plen, dtype=np.int32)
+    lens[1:] -= 5 * np.arange(1, B, dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), lens, seed=20)
+    c, worst = run_and_compare(m, w, P, lens, 3, dict(greedy=1), min_frames=1 << 20, tag=f"cache-full-{plen}-B{B}",
+                               floor=True, seq_slack=0)
+    assert sum(c) >= 2 * B
 
 
 @pytest.mark.timeout(900)
