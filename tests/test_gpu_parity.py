@@ -405,6 +405,25 @@ def test_codebook_counts_and_sizes(N, C, heads, B):
     assert sum(c) >= 2 * B
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("wdtype,B", [("f32", 1), ("f32", 3), ("bf16", 1), ("bf16", 3)])
+def test_widest_model_dim(wdtype, B):
+    # dim 12,288, the widest the config accepts: rows of 24 units (bf16) or 48
+    # (fp32) take the general loop GEMV with the whole activation row staged
+    # in 48 KB of LDS; at batch 3 the fp32 products stage one row at a time
+    # (two or four would pass the LDS limit) and the bf16 ones run on the
+    # matrix cores
+    heads = {} if wdtype == "f32" else dict(n_head=8, n_kv_head=2, fast_n_head=8, fast_n_kv_head=2)   # 512-wide rows
+    m = synth.model("tiny", weight_dtype=wdtype, dim=12288, fast_dim=12288, ffn_dim=512, fast_ffn_dim=512,
+                    n_layer=1, n_fast_layer=1, **heads)
+    w = synth.make_weights(m, seed=21)
+    plen = synth.make_ctx_lengths(B, 5, 30, seed=21)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=21)
+    c, worst = run_and_compare(m, w, P, plen, 2, dict(greedy=1), tol=1e-4 if wdtype == "f32" else REL_L2,
+                               tag=f"dim12288-{wdtype}-B{B}", floor=False)
+    assert sum(c) >= 2 * B
+
+
 @pytest.mark.parametrize("fast_qk", [1, 0])
 def test_tiny_bf16_kv(fast_qk):
     m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024,
