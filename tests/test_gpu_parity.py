@@ -302,6 +302,20 @@ def test_tiny_loop_breaker_window_changes(tiny):
     assert stats["ras_used"] > 0
 
 
+def test_tiny_loop_breaker_widest_window(tiny):
+    # the widest window (DUALAR_RAS_MAX_WINDOW = 16, the whole per-sequence
+    # ring of emitted ids) over 30 frames, so that the ring wraps and the
+    # window reaches its oldest slot
+    m, w = tiny
+    plen = np.array([32, 7, 45], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=22)
+    U = synth.make_uniforms((31, 3, m["num_codebooks"] + 1), seed=22)
+    stats = {}
+    c, _ = run_and_compare(m, w, P, plen, 30, dict(greedy=1), U, tol=1e-4, tag="tiny-ras-16", ras=16, stats=stats)
+    assert sum(c) >= 45, c
+    assert stats["ras_used"] > 0
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("pc", [4096, 1000])
 def test_bf16_prefill_many_row_tiles(pc):
