@@ -31,8 +31,12 @@ __global__ void __launch_bounds__(DUALAR_WG) embed_kernel(EmbedParams p) {
   const int row = blockIdx.x;
   int b = row;
   const int tid = threadIdx.x;
+  // The column (N + 1 <= 33 ids) is read with compile-time indexes only, so
+  // it stays in registers (a runtime-indexed private array goes to scratch).
   int col[33];
   int act = 1;
+  const int* src;
+  size_t stride = 1;
   if (p.prefill) {
     b = row / p.rows_per_seq;
     const int i = row % p.rows_per_seq;
@@ -42,12 +46,11 @@ __global__ void __launch_bounds__(DUALAR_WG) embed_kernel(EmbedParams p) {
       if (p.pos_out) p.pos_out[row] = act ? t : -1;
       if (i == p.rows_per_seq - 1) p.st.pos[b] = act ? t : -1;
     }
-    if (act)
-      for (int r = 0; r <= p.N; ++r) col[r] = p.tokens[((size_t)b * (p.N + 1) + r) * p.t_max + t];
+    src = p.tokens + (size_t)b * (p.N + 1) * p.t_max + (act ? t : 0);
+    stride = (size_t)p.t_max;
   } else {
     act = !p.st.done[b];
-    if (act)
-      for (int r = 0; r <= p.N; ++r) col[r] = p.st.cur[b * (p.N + 1) + r];
+    src = p.st.cur + (size_t)b * (p.N + 1);
   }
   const int d = blockIdx.y * DUALAR_WG + tid;
   float* x = p.x + (size_t)row * p.dim;
@@ -55,12 +58,16 @@ __global__ void __launch_bounds__(DUALAR_WG) embed_kernel(EmbedParams p) {
     if (d < p.dim) x[d] = 0.f;
     return;
   }
+#pragma unroll
+  for (int r = 0; r < 33; ++r) col[r] = r <= p.N ? src[r * stride] : 0;
   int bad = 0;
   if (col[0] < 0 || col[0] >= p.V) { bad = 1; col[0] = 0; }
   const bool sem = col[0] >= p.sb && col[0] <= p.se;
-  if (sem)
-    for (int k = 0; k < p.N; ++k)
-      if (col[1 + k] < 0 || col[1 + k] >= p.C) { bad = 1; col[1 + k] = 0; }
+  if (sem) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      if (k < p.N && (col[1 + k] < 0 || col[1 + k] >= p.C)) { bad = 1; col[1 + k] = 0; }
+  }
   if (bad && blockIdx.y == 0 && tid == 0) atomicOr(p.st.status, ST_BAD_TOKEN);
   if (d >= p.dim) return;
   const float e0 = ElemT<T>::load(p.tok_emb, (size_t)col[0] * p.dim + d);
