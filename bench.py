@@ -279,9 +279,9 @@ def decode_workload(args, name, torch, synth, DualAR, reporting, kit, m, w, dev_
             plen = np.full(B, P, dtype=np.int32)
             layout = ("fixed", P // 8, P // 2, P - P // 8 - P // 2)
         prompts = synth.make_prompts(m, layout, plen, seed=args.seed)
-        # 4-bit weights run as vector GEMVs only: the prompt one position per step
-        ctx = DualAR(m, dev_w, max_batch=B, max_seq_len=int(plen.max()) + P_frames + 2,
-                     prefill_chunk=1 if w4 else 0)
+        # the default prefill chunk (4-bit weights too: their prefill steps run
+        # on the matrix-core 2-D tiles)
+        ctx = DualAR(m, dev_w, max_batch=B, max_seq_len=int(plen.max()) + P_frames + 2)
         U = None
         if not samp["greedy"] or ras:
             U = torch.from_numpy(synth.make_uniforms((1 + P_frames, B, N + (ras > 0)), seed=args.seed)).cuda()

@@ -192,6 +192,12 @@ struct Stack {
   size_t layer_stride;     // elements
   int max_pos;
   const float2* rope;
+  bool any_w4() const {
+    for (const dualar_layer_w4& l : l4)
+      for (const void* q : l.q4)
+        if (q) return true;
+    return false;
+  }
 };
 
 }  // namespace
@@ -698,7 +704,11 @@ template <typename T, typename KT>
 dualar_status do_prefill(dualar_ctx* c, int B, const int* tokens, int t_max, const FrameIO& io) {
   const Resolved& r = c->r;
   HIPCHK(launch_prefill_begin(c->st, c->plen.data(), B, r.N, c->stream));
-  const int C = std::min(r.pc, t_max);
+  int C = std::min(r.pc, t_max);
+  // 4-bit products over several rows run only on the 2-D tiles: a short
+  // prompt is then prefilled in one step of GEMM_TILE_MIN_ROWS rows (left
+  // padding; create guarantees prefill_chunk 1 or at least that many)
+  if (C > 1 && C < GEMM_TILE_MIN_ROWS && c->slow.any_w4()) C = GEMM_TILE_MIN_ROWS;
   const int n_steps = (t_max + C - 1) / C;
   float* xp = (float*)(c->ws + c->L.x_pre);
   const int* ppos = (const int*)(c->ws + c->L.ppos);
@@ -795,6 +805,7 @@ dualar_status dispatch(dualar_ctx* c, F&& f) {
 }
 
 static_assert(RAS_HIST_STRIDE == DUALAR_RAS_MAX_WINDOW, "loop-breaker window stride");
+static_assert(GEMM_TILE_MIN_ROWS == 256, "the 4-bit error messages name 256 rows");
 
 dualar_status check_sampling(dualar_ctx* c, const dualar_sampling* s, const float* uniforms) {
   if (!s) return fail(c, DUALAR_ERR_INVALID_ARG, "sampling is NULL");
@@ -923,7 +934,8 @@ dualar_status create_ctx(const dualar_config* cfg, const dualar_weights* w, void
   for (int i = 0; i < r.fn_layer; ++i)
     if (!layer_ok(w->fast_layers[i], r.fast_qk, w->fast_layers_w4, i))
       return fail(c, DUALAR_ERR_INVALID_ARG, "a fast layer weight is NULL or not 16-byte aligned");
-  // 4-bit matrices: batch 1 and one prefill position per step (vector GEMVs only)
+  // 4-bit matrices: batch 1 (vector GEMVs); prefill steps of one position
+  // (the same GEMVs) or of GEMM_TILE_MIN_ROWS+ positions (the 2-D tiles)
   auto w4_check = [&](const dualar_layer_w4* a, int n, int dim, int H, int KV, int hd, int ffn) -> const char* {
     if (!a) return nullptr;
     const int in[7] = {dim, dim, dim, H * hd, dim, dim, ffn};
@@ -939,8 +951,9 @@ dualar_status create_ctx(const dualar_config* cfg, const dualar_weights* w, void
     return nullptr;
   };
   if (w->layers_w4 || w->fast_layers_w4) {
-    if (r.esz != 2 || r.max_batch != 1 || r.pc != 1)
-      return fail(c, DUALAR_ERR_INVALID_ARG, "4-bit matrices need bf16 weights, max_batch 1 and prefill_chunk 1");
+    if (r.esz != 2 || r.max_batch != 1 || (r.pc != 1 && r.pc < GEMM_TILE_MIN_ROWS))
+      return fail(c, DUALAR_ERR_INVALID_ARG,
+                  "4-bit matrices need bf16 weights, max_batch 1 and prefill_chunk 1 or at least 256");
     const char* e = w4_check(w->layers_w4, r.n_layer, r.dim, r.H, r.KV, r.hd, r.ffn);
     if (!e) e = w4_check(w->fast_layers_w4, r.fn_layer, r.dim, r.fH, r.fKV, r.fhd, r.fffn);
     if (e) return fail(c, DUALAR_ERR_INVALID_ARG, e);
@@ -1091,6 +1104,9 @@ dualar_status dualar_fast_teacher_forced(dualar_ctx_t* c, int32_t n, const float
       (c->fast.H / c->fast.KV) & (c->fast.H / c->fast.KV - 1))
     return fail(c, DUALAR_ERR_INVALID_ARG, "teacher-forced form needs N <= 11, fast head_dim <= 128 (a multiple "
                                            "of 4), 1, 2, 4 or 8 query heads per KV head");
+  if (c->fast.any_w4() && (long long)n * N < GEMM_TILE_MIN_ROWS)
+    return fail(c, DUALAR_ERR_INVALID_ARG, "with 4-bit fast layers the teacher-forced form needs n * num_codebooks "
+                                           ">= 256 rows");
   // the activation buffers are scratch between calls: the decode state is untouched
   MarkerRange mr("dualar.fast_tf");
   return dispatch(c, [&](auto wt, auto kt) {

@@ -35,7 +35,7 @@
 
 #define GM_KC 64                     // k per chunk
 #define GM_STAGES 3
-#define GM_TILE_ROWS 256             // from this many activation rows: 2-D tiles (gemm_tile.hip)
+#define GM_TILE_ROWS GEMM_TILE_MIN_ROWS   // from this many activation rows: 2-D tiles (gemm_tile.hip)
 
 // Workgroup shape: WAVES waves, each owning T 32-row output tiles (times NR
 // segments); the workgroup covers ROWS = 32*WAVES*T output rows.
@@ -872,6 +872,7 @@ static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, b
 // workgroups the chip holds at once (LDS bound).
 bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   if (p0.B < 2 || p0.K % GM_KC != 0 || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
+  if (p0.q4[0] && p0.B < GM_TILE_ROWS) return false;   // 4-bit weights: the 2-D tile form only
   GemvParams p = p0;
   if (p.xplanes) p.xn = const_cast<void*>(p.xplanes);   // input already split by its producer
   else hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
@@ -881,7 +882,8 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   if (p.B >= GM_TILE_ROWS) {   // 2-D output tiles (prefill steps)
     if (p.prep_done) *p.prep_done = 0;
     if (p.next_done) *p.next_done = 0;
-    *err = launch_gemm_tile(p, gemm_tile_wide(p), s) ? hipGetLastError() : hipErrorInvalidValue;
+    const bool ok = p.q4[0] ? launch_gemm_tile_w4(p, s) : launch_gemm_tile(p, gemm_tile_wide(p), s);
+    *err = ok ? hipGetLastError() : hipErrorInvalidValue;
     return true;
   }
   // Stream-K (wave-specialised, one workgroup per compute unit) for the

@@ -1068,6 +1068,10 @@ static hipError_t pick_bt(const GemvParams& p, hipStream_t s) {
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s) {
   if (p.q4[0]) {
     if constexpr (sizeof(T) != 2) return hipErrorInvalidValue;
+    if (p.B >= 2) {   // prefill steps: the 2-D matrix-core tiles, from GEMM_TILE_MIN_ROWS rows
+      hipError_t e;
+      return launch_gemm_mfma(p, s, &e) ? e : hipErrorInvalidValue;
+    }
     if (p.next_done) *p.next_done = 0;
     hipError_t e;
     if (p.mode != GEMV_SWIGLU && launch_w4m<1>(p, s, &e)) return e;

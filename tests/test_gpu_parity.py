@@ -596,13 +596,13 @@ def test_batch1_s2_heads_merged_in_o_product(plen, kv):
 # W4A16 (the survey's NEXT 4): 4-bit weight groups, batch 1
 # ----------------------------------------------------------------------------
 
-def _w4_case(m, seed, plen, frames, tag):
+def _w4_case(m, seed, plen, frames, tag, prefill_chunk=1):
     from oracle import dequant_w4
     w4 = synth.make_w4_model(m, synth.make_weights(m, seed=seed))
     wf = dequant_w4(synth.weights_as_f32(m, w4))          # the oracle's own q * scale
     P = synth.make_prompts(m, ("ragged", 1, 1), np.array([plen], dtype=np.int32), seed=seed)
     return run_and_compare(m, w4, P, np.array([plen], dtype=np.int32), frames, dict(greedy=1), tag=tag,
-                           weights_f32=wf, floor=m.get("kv_dtype", "bf16") == "bf16", prefill_chunk=1)
+                           weights_f32=wf, floor=m.get("kv_dtype", "bf16") == "bf16", prefill_chunk=prefill_chunk)
 
 
 @pytest.mark.timeout(600)
@@ -643,6 +643,34 @@ def test_w4a16_row_lengths(dim, ffn, n_head):
                     n_head=n_head, n_kv_head=n_head // 4, head_dim=128, fast_n_head=n_head,
                     fast_n_kv_head=n_head // 4, fast_head_dim=128, w4a16=1, w4_bf16_attn_layers=1)
     c, worst = _w4_case(m, 15, 30, 3, f"w4-rows-{dim}-{ffn}")
+    assert sum(c) >= 2
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("plen", [300, 40])
+def test_w4a16_chunked_prefill_s2_shapes(plen):
+    # prefill steps of 256 positions: the 4-bit products on the matrix-core
+    # 2-D tiles (each group of 128 inputs summed on the matrix cores, then
+    # scaled in fp32).  A 300-token prompt takes two steps (the first one's
+    # rows 0..211 are left padding, so only its last activation tile is
+    # live), a 40-token prompt one padded step; the decode frames then run
+    # the 4-bit GEMVs.  Layers 0-1 fully 4-bit, layer 2 with bf16 attention.
+    m = synth.model("s2", n_layer=3, w4a16=1, w4_bf16_attn_layers=1)
+    c, worst = _w4_case(m, 10, plen, 2, f"w4-s2-pc256-{plen}", prefill_chunk=256)
+    assert sum(c) >= 2
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dim,ffn,n_head,kv", [(10240, 5632, 8, "bf16"), (1536, 3072, 12, "f32"),
+                                               (512, 1024, 4, "f32")])
+def test_w4a16_chunked_prefill_row_lengths(dim, ffn, n_head, kv):
+    # the 4-bit 2-D tiles at other row lengths: 10,240 inputs (80 scale groups,
+    # the LDS limit), 5,632, 3,072, 1,536, 1,024 and 512; a 600-token prompt in
+    # two steps of 512 positions (the first one ragged)
+    m = synth.model("tiny", weight_dtype="bf16", kv_dtype=kv, dim=dim, ffn_dim=ffn, fast_dim=dim, fast_ffn_dim=ffn,
+                    n_head=n_head, n_kv_head=n_head // 4, head_dim=128, fast_n_head=n_head,
+                    fast_n_kv_head=n_head // 4, fast_head_dim=128, w4a16=1, w4_bf16_attn_layers=1)
+    c, worst = _w4_case(m, 16, 600, 3, f"w4-pc512-{dim}-{ffn}", prefill_chunk=512)
     assert sum(c) >= 2
 
 
@@ -989,6 +1017,42 @@ def test_tiny_fast_teacher_forced(tiny, n):
         worst = max(worst, e)
         assert e <= 1e-4, (i, e)
     say(f"[tiny-tf] worst rel L2 {worst:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_w4a16_fast_teacher_forced():
+    # 4-bit fast layers in the teacher-forced form: 100 pairs x 4 codebooks =
+    # 400 rows on the 4-bit 2-D tiles, against the oracle on its own
+    # q * scale weights; 5 pairs (20 rows, fewer than the tiles take) are
+    # rejected before anything is enqueued
+    from oracle import dequant_w4
+    from dual_autoregressive_tts_amd import DualARError
+    DualAR, upload = _dev()
+    m = synth.model("tiny", weight_dtype="bf16", dim=512, ffn_dim=1024, fast_dim=512, fast_ffn_dim=1024, n_head=4,
+                    n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1, fast_head_dim=128, w4a16=1,
+                    w4_bf16_attn_layers=1)
+    w4 = synth.make_w4_model(m, synth.make_weights(m, seed=17))
+    wf = dequant_w4(synth.weights_as_f32(m, w4))
+    N, C, n = m["num_codebooks"], m["codebook_size"], 100
+    rng = np.random.default_rng(13)
+    h = torch.from_numpy(rng.standard_normal((n, m["fast_dim"])).astype(np.float32)).cuda()
+    codes = torch.from_numpy(rng.integers(0, C, size=(n, N)).astype(np.int32)).cuda()
+    say(f"[w4-tf] GPU n={n}")
+    ctx = DualAR(m, upload(m, w4), max_batch=1, max_seq_len=16)
+    with pytest.raises(DualARError) as e:
+        ctx.fast_teacher_forced(h[:5].contiguous(), codes[:5].contiguous())
+    assert e.value.name == "INVALID_ARG"
+    got = ctx.fast_teacher_forced(h, codes).cpu().numpy()
+    assert ctx.sync() == 0
+    ctx.close()
+    o = DualAROracle(m, wf, max_seq=8)
+    worst = 0.0
+    for i in range(n):
+        ref = o.fast_teacher_forced(h[i].cpu().numpy().astype(np.float64), codes[i].cpu().tolist())
+        e2 = rel_l2(got[i, 1:], ref)
+        worst = max(worst, e2)
+        assert e2 <= REL_L2, (i, e2)
+    say(f"[w4-tf] worst rel L2 {worst:.2e}")
 
 
 @pytest.mark.timeout(600)
