@@ -139,7 +139,10 @@ __device__ __forceinline__ Best block_best(Best x, Best* sh) {
 // by a radix descent: 8 key bits per pass, a histogram of (mass, count) over
 // the candidates that share the bits found so far, suffix sums over the
 // 256 digits from the top, and the digit where the condition still holds;
-// a pass whose digit holds a single candidate ends the descent.
+// a pass whose digit holds a single candidate ends the descent.  The
+// descent starts below the bits that every candidate key shares (the common
+// prefix of the smallest and the largest key): a digit there would hold the
+// whole set, so its pass would choose it without narrowing anything.
 #define TP_E 5                              // candidates per thread: nc <= 5120
 #define TP_IDX_BITS 13
 #define TP_KEY_BITS (32 + TP_IDX_BITS)
@@ -151,6 +154,7 @@ struct TopPShared {
   unsigned long long mass[TP_WAVES][TP_NB];   // per-wave histograms
   unsigned cnt[TP_WAVES][TP_NB];
   unsigned long long wtot[TP_WAVES];
+  unsigned long long wmin[TP_WAVES], wmax[TP_WAVES];
   int cand_t[TP_NB / 64];                     // per digit wave: its chosen digit, or -1
   unsigned long long cand_above[TP_NB / 64];
   int cand_single[TP_NB / 64];
@@ -176,16 +180,43 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
   return t;
 }
 
+// Smallest and largest candidate key over the workgroup (key 0 = none).
+__device__ __forceinline__ void block_key_range(const unsigned long long (&key)[TP_E], TopPShared& sh,
+                                                unsigned long long* kmin, unsigned long long* kmax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long lo = ~0ull, hi = 0ull;
+#pragma unroll
+  for (int s = 0; s < TP_E; ++s)
+    if (key[s] != 0ull) { lo = min(lo, key[s]); hi = max(hi, key[s]); }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo = min(lo, (unsigned long long)__shfl_xor(lo, o));
+    hi = max(hi, (unsigned long long)__shfl_xor(hi, o));
+  }
+  if (lane == 0) { sh.wmin[wave] = lo; sh.wmax[wave] = hi; }
+  __syncthreads();
+  lo = sh.wmin[0];
+  hi = sh.wmax[0];
+#pragma unroll
+  for (int w = 1; w < TP_WAVES; ++w) { lo = min(lo, sh.wmin[w]); hi = max(hi, sh.wmax[w]); }
+  __syncthreads();
+  *kmin = lo;
+  *kmax = hi;
+}
+
 // The largest candidate key K with mass(keys >= K) >= thr (strict: > thr),
 // and mass(keys >= K).  The caller guarantees that the whole set satisfies
 // the condition.
 __device__ __forceinline__ void tp_select(const unsigned long long (&key)[TP_E], const unsigned long long (&m)[TP_E],
                                           double thr, bool strict, TopPShared& sh, unsigned long long* k_out,
-                                          unsigned long long* m_out) {
+                                          unsigned long long* m_out, unsigned long long kmin,
+                                          unsigned long long kmax) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  unsigned long long P = 0, above = 0;
-  int lo = TP_KEY_BITS;
-  while (true) {
+  // bits [lo, TP_KEY_BITS) are common to every key (all of them when the
+  // set holds one candidate: keys are distinct); nothing lies above them
+  int lo = kmin == kmax ? 0 : 64 - __clzll(kmin ^ kmax);
+  unsigned long long P = kmin >> lo, above = 0;
+  while (lo > 0) {
     const int hi = lo;                       // bits [lo, hi) are this pass's digit
     lo = hi > 8 ? hi - 8 : 0;
     const int w = hi - lo;
@@ -239,7 +270,7 @@ __device__ __forceinline__ void tp_select(const unsigned long long (&key)[TP_E],
     above = sh.cand_above[bw];
     const int single = sh.cand_single[bw];
     __syncthreads();
-    if (single || lo == 0) break;
+    if (single) break;
   }
   // the one candidate with these high bits
 #pragma unroll
@@ -313,11 +344,14 @@ __global__ void __launch_bounds__(SMP_THREADS) sample_kernel(SampleParams p) {
       tot += m[s];
     }
     tot = block_sum_u64(tot, tps);
+    unsigned long long kmin, kmax;
+    block_key_range(key, tps, &kmin, &kmax);
     unsigned long long kb, kept;
-    tp_select(key, m, fmin((double)top_p * (double)tot, (double)tot), false, tps, &kb, &kept);
+    tp_select(key, m, fmin((double)top_p * (double)tot, (double)tot), false, tps, &kb, &kept, kmin, kmax);
     const double target = (double)u * (double)kept;
     unsigned long long kd = kb, md;
-    if (target < (double)kept) tp_select(key, m, target, true, tps, &kd, &md);
+    // the draw lies among the kept keys (>= kb)
+    if (target < (double)kept) tp_select(key, m, target, true, tps, &kd, &md, kb, kmax);
     if (tid == 0) choice = (1 << TP_IDX_BITS) - 1 - (int)(kd & ((1ull << TP_IDX_BITS) - 1));
   };
   const float* ub = p.uniforms ? p.uniforms + (size_t)f * p.u_frame_stride + (size_t)b * p.u_row_stride : nullptr;
