@@ -322,10 +322,12 @@ void live_tiles(const dualar_ctx* c, GemvParams& g, int rows_per_seq) {
 //
 // in_planes: on entry, the previous layer already wrote RMSNorm(x) with this
 // layer's attention gain as planes (xn), so the QKV product reads them; on
-// exit, whether this layer did the same for layer l + 1.
+// exit, whether this layer did the same for layer l + 1 (for the last layer:
+// with out_gain, the gain of the norm in front of the head, when given).
 template <typename T, typename KT>
 dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const int* pos_dev,
-                        int pos_const, int Lmax, bool& in_planes, int rows_per_seq = 0, bool depth_tf = false) {
+                        int pos_const, int Lmax, bool& in_planes, int rows_per_seq = 0, bool depth_tf = false,
+                        const void* out_gain = nullptr) {
   const Resolved& r = c->r;
   const Layout& L = c->L;
   const dualar_layer_weights& w = S.lw[l];
@@ -501,8 +503,9 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   live_tiles(c, g, rows_per_seq);
   g.xplanes = planes;
   fused = 0;
-  if (planes && l + 1 < S.n_layer) {
-    g.next_gain = S.lw[l + 1].attention_norm; g.next_planes = xn; g.next_done = &fused; g.eps = r.eps;
+  if (planes && (l + 1 < S.n_layer || out_gain)) {
+    g.next_gain = l + 1 < S.n_layer ? S.lw[l + 1].attention_norm : out_gain;
+    g.next_planes = xn; g.next_done = &fused; g.eps = r.eps;
   }
   HIPCHK(gemv<T>(c, g));
   in_planes = fused != 0;
@@ -583,7 +586,9 @@ hipError_t sample(dualar_ctx* c, const SampleParams& sp) {
 // Everything after the slow pass: head, slow sample, N fast passes.  With
 // fast_only, x_slow/x_fast/q0 were set by fast_begin and there is no slow head.
 template <typename T, typename KT>
-dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
+// head_planes: the last slow layer already wrote RMSNorm(x_slow) with the
+// final norm's gain as planes (xn) for the tied head.
+dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io, bool head_planes = false) {
   const Resolved& r = c->r;
   const Layout& L = c->L;
   float* xs = (float*)(c->ws + L.x_slow);
@@ -611,6 +616,7 @@ dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
     g.K = r.dim;
     g.x = xs; g.ldx = r.dim; g.gain = c->w.norm; g.eps = r.eps;
     g.y = (float*)(c->ws + L.logits); g.ldy = g.n_out; g.B = B; g.mode = GEMV_STORE;
+    if (head_planes) g.xplanes = c->ws + L.xn;
     HIPCHK(gemv<T>(c, g));
     if (io.taps && io.taps->slow_logits)
       HIPCHK(hipMemcpyAsync(io.taps->slow_logits, c->ws + L.logits, (size_t)B * r.V * 4, hipMemcpyDeviceToDevice,
@@ -633,13 +639,16 @@ dualar_status frame_tail(dualar_ctx* c, int B, const FrameIO& io) {
   for (int k = 1; k < r.N; ++k) {
     pl = false;
     for (int l = 0; l < r.fn_layer; ++l) {
-      dualar_status st = run_layer<T, KT>(c, c->fast, l, xf, B, nullptr, k, k + 1, pl);
+      // the last layer also writes the fast head's normalised input planes
+      dualar_status st = run_layer<T, KT>(c, c->fast, l, xf, B, nullptr, k, k + 1, pl, 0, false,
+                                          l + 1 == r.fn_layer ? c->w.fast_norm : nullptr);
       if (st) return st;
     }
     GemvParams g{};
     g.w[0] = c->w.fast_output; g.rows[0] = r.C; g.n_seg = 1; g.K = r.dim; g.n_out = r.C;
     g.x = xf; g.ldx = r.dim; g.gain = c->w.fast_norm; g.eps = r.eps;
     g.y = (float*)(c->ws + L.flog); g.ldy = r.C; g.B = B; g.mode = GEMV_STORE;
+    if (pl) g.xplanes = c->ws + L.xn;
     HIPCHK(gemv<T>(c, g));
     if (io.taps && io.taps->fast_logits)
       HIPCHK(hipMemcpy2DAsync(io.taps->fast_logits + (size_t)(k - 1) * r.C, (size_t)(r.N - 1) * r.C * 4,
@@ -760,17 +769,18 @@ dualar_status do_decode(dualar_ctx* c, int n_frames, const FrameIO& io) {
     const int Lmax = maxp + c->frames_done + f + 1;
     c->step_pos.resize(B);
     for (int b = 0; b < B; ++b) c->step_pos[b] = c->plen[b] + c->frames_done + f;
+    bool pl = false;   // after the loop: the tied head's input planes are written
     {
       MarkerRange ms("dualar.slow");
-      bool pl = false;
       for (int l = 0; l < c->r.n_layer; ++l) {
-        st = run_layer<T, KT>(c, c->slow, l, xs, B, c->st.pos, 0, Lmax, pl);
+        st = run_layer<T, KT>(c, c->slow, l, xs, B, c->st.pos, 0, Lmax, pl, 0, false,
+                              l + 1 == c->r.n_layer ? c->w.norm : nullptr);
         if (st) return st;
       }
     }
     FrameIO fio = io;
     if (!last) fio.taps = nullptr;
-    st = frame_tail<T, KT>(c, B, fio);
+    st = frame_tail<T, KT>(c, B, fio, pl);
     if (st) return st;
   }
   return DUALAR_OK;
