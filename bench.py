@@ -2,7 +2,7 @@
 dominant kernel and the CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W] [--reps R] [--workload s2_b1|s2_b32|s2_prefill|s2_fast_tf|fast_s2|
-                    fast_s2_b16|tiny_b1|s2_b1_w4] [--semantic-head] [--ras] [--no-batch32]
+                    fast_s2_b16|tiny_b1|s2_b1_w4|s2_b4_w4] [--semantic-head] [--ras] [--no-batch32]
 
 A step is one decode frame of the whole hot path (fusion, slow pass, biased
 sample, ten fast passes with their samples) over one batch.  Inputs are
@@ -43,6 +43,8 @@ WORKLOADS = {
     "s2_b1_w4": ("s2_b1", None, "full S2-shaped Dual-AR decode, batch 1, W4A16 weights (4-bit groups of 128 "
                                 "with bf16 scales; the last 12 slow layers' attention, the embeddings and "
                                 "heads in bf16), 1,024-token prompt, greedy"),
+    "s2_b4_w4": ("s2_b1", 4, "full S2-shaped Dual-AR decode, batch 4, W4A16 weights (as s2_b1_w4), "
+                             "1,024-token prompts, greedy"),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
@@ -272,7 +274,7 @@ def decode_workload(args, name, torch, synth, DualAR, reporting, kit, m, w, dev_
         run = lambda a, b: ctx.fast_frames(H[a:b], Q[a:b], S, None if U is None else U[a:b])  # noqa
         ttff_ms = None
     else:
-        plen = synth.prompt_lengths(wl, seed=args.seed)
+        plen = synth.prompt_lengths(dict(wl, batch=B), seed=args.seed)
         layout = wl["prompt"]
         if args.prompt_len:
             P = args.prompt_len
@@ -349,9 +351,12 @@ def decode_workload(args, name, torch, synth, DualAR, reporting, kit, m, w, dev_
             f"{100 * gemv_share:.1f}% of step time")
         log(f"[bench] {name}: SwiGLU gate|up product: {f['launches']} launches, avg {sw_avg_us:.2f} us, "
             f"{sw_bytes / 1e6:.2f} MB/launch, {sw_gbps:.0f} GB/s")
-        if w4:
+        if w4 and B == 1:
             kname = ("gemv_w4_kernel<2, 2, 5, 1, false> (SwiGLU W1|W3 GEMV, 2 x 9728 x 2560 as 4-bit groups of 128 with "
                      "bf16 scales)")
+        elif w4:
+            kname = ("gemv_w4b_kernel<2, 3, 8> (SwiGLU W1|W3 matrix-core GEMV over %d activation rows, 2 x 9728 x "
+                     "2560 as 4-bit groups of 128 with bf16 scales)" % B)
         elif m["weight_dtype"] == "f32":
             kname = "SwiGLU W1|W3 GEMV"
         elif B == 1:
@@ -365,7 +370,7 @@ def decode_workload(args, name, torch, synth, DualAR, reporting, kit, m, w, dev_
                     "kernel": kname,
                     "achieved": round(sw_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(sw_gbps / HBM_PEAK_GBPS, 4),
-                    "traffic": (roofline_traffic("gemv_w4_kernel") if w4 else roofline_traffic("gemv_rx_kernel")
+                    "traffic": ((roofline_traffic("gemv_w4_kernel") if w4 else roofline_traffic("gemv_rx_kernel"))
                                 if (B == 1 and m["weight_dtype"] == "bf16") else None),
                     "avg_launch_us": round(sw_avg_us, 3), "bytes_per_launch": round(sw_bytes),
                     "launches_profiled": f["launches"],

@@ -872,10 +872,17 @@ static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, b
 // workgroups the chip holds at once (LDS bound).
 bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   if (p0.B < 2 || p0.K % GM_KC != 0 || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
-  if (p0.q4[0] && p0.B < GM_TILE_ROWS) return false;   // 4-bit weights: the 2-D tile form only
+  // 4-bit weights: 2-4 rows or the 2-D tile form
+  if (p0.q4[0] && p0.B > GEMV_W4_MAX_ROWS && p0.B < GM_TILE_ROWS) return false;
   GemvParams p = p0;
   if (p.xplanes) p.xn = const_cast<void*>(p.xplanes);   // input already split by its producer
   else hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
+  if (p.q4[0] && p.B <= GEMV_W4_MAX_ROWS) {
+    if (p.prep_done) *p.prep_done = 0;
+    if (p.next_done) *p.next_done = 0;
+    if (!launch_gemv_w4_rows(p, s, err)) *err = hipErrorInvalidValue;
+    return true;
+  }
   bool ok = false;
   const bool glu = p.mode == GEMV_SWIGLU;
   const int z_tiles = (p.B + 31) / 32;

@@ -939,6 +939,162 @@ static bool launch_w4m(const GemvParams& p, hipStream_t s, hipError_t* e) {
   return false;
 }
 
+// ---------------------------------------------------------------------------
+// 4-bit weights, 2 to 4 activation rows (batched W4A16 decode)
+// ---------------------------------------------------------------------------
+// The matrix-core form above with the activations taken from the three bf16
+// planes [3][B][K] of the batched path (the input split, or a producer's
+// output planes), which already hold the normalised input: A row 4b + t of
+// v_mfma_f32_16x16x32_bf16 is term t of activation row b (t < 3, b < B; the
+// other rows are zero), so lane group q = b of the result holds row b's three
+// term sums.  The chunk loop has no branches (a wave's chunks past the row
+// are clamped loads with a zero scale) and the segment pointers are chosen by
+// selects among SGPR copies, so that every load is issued up front.  The
+// weights are unpacked exactly (the nibble's v + 8 less 8 in
+// the integer domain, then a convert: bf16 holds every value of [-8, 7]), so
+// every product is exact, as in the bf16 path.  (The batch-1 form's byte
+// permute to 136 + v with a -136 sum-of-x start measured a fast-logit
+// distance of 2.0e-3 at batch 4 on a bf16 cache, against 8.9e-4 exact.)
+// Per chunk of 128 inputs (one scale): 4 product steps; at step i lane
+// (q, n) takes octet 4q + i of its row, of the weights and of the activation
+// term alike.  A wave loads all of its chunks' weights first, then each
+// chunk's activation fragments one chunk ahead.  The fragments of A rows
+// that feed no result (t = 3, or b >= B) are loaded from a clamped row and
+// left unmasked, so every load is unconditional.
+__device__ __forceinline__ u32x4 w4b_unpack(uint32_t d) {
+  const uint32_t u = d ^ 0x88888888u;
+  uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+  __asm__("" : "+v"(lo), "+v"(hi));     // known-zero bits: one byte convert each
+  u32x4 o;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    o[b] = (uint32_t)f32_to_bf16_rne((float)((lo >> (8 * b)) & 0xFFu) - 8.0f) |
+           ((uint32_t)f32_to_bf16_rne((float)((hi >> (8 * b)) & 0xFFu) - 8.0f) << 16);
+  return o;
+}
+
+typedef __attribute__((address_space(1))) const u32x4 w4b_gvec;
+typedef __attribute__((address_space(1))) const uint16_t w4b_gu16;
+
+template <int NR, int NCH, int NWV>
+__global__ void __launch_bounds__(NWV * 64) gemv_w4b_kernel(GemvParams p) {
+  __shared__ float part[NWV][4][NR][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, n = lane & 15;
+  const int C = p.K >> 7;
+  const int c0 = wave * NCH;
+  const int cnt = min(NCH, C - c0);              // chunks of this wave (<= 0: none)
+  const int r0 = blockIdx.x * 16;
+  // weights and scales of the 16 rows
+  u32x4 wq[NCH][NR];
+  uint32_t sc[NCH][NR];
+  {
+    uint64_t q0 = (uint64_t)p.q4[0], q1 = (uint64_t)p.q4[1], q2 = (uint64_t)p.q4[2];
+    uint64_t s0 = (uint64_t)p.s4[0], s1 = (uint64_t)p.s4[1], s2 = (uint64_t)p.s4[2];
+    asm volatile("" : "+s"(q0), "+s"(q1), "+s"(q2), "+s"(s0), "+s"(s1), "+s"(s2));
+    const int row0 = min(r0 + n, p.n_out - 1);
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      int row = row0, seg = s;
+      if (NR == 1) {   // rows of up to three segments one after the other
+        seg = row >= p.rows[0] ? (row >= p.rows[0] + p.rows[1] ? 2 : 1) : 0;
+        row -= seg == 0 ? 0 : (seg == 1 ? p.rows[0] : p.rows[0] + p.rows[1]);
+      }
+      // (global address space: through a plain pointer rebuilt from an
+      // integer these would be flat loads)
+      const uint64_t qb = (seg == 0 ? q0 : (seg == 1 ? q1 : q2)) + (uint64_t)row * (p.K / 2) + q * 16;
+      const uint64_t sb = (seg == 0 ? s0 : (seg == 1 ? s1 : s2)) + (uint64_t)row * C * 2;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int cc = min(c0 + c, C - 1);
+        wq[c][s] = __builtin_nontemporal_load((w4b_gvec*)(qb + (uint64_t)cc * 64));
+        sc[c][s] = ((w4b_gu16*)sb)[cc];
+      }
+    }
+  }
+  // activation fragments: A row n = term (n & 3) of activation row n >> 2;
+  // rows with n & 3 == 3 or n >> 2 >= B read a clamped row: their result rows
+  // are never read
+  const int ab = min(n >> 2, p.B - 1), at = min(n & 3, 2);
+  const uint16_t* xp = (const uint16_t*)p.xn + ((size_t)at * p.B + ab) * p.K + 32 * q;
+  auto load_x = [&](u32x4 (&xa)[4], int c) __attribute__((always_inline)) {
+    const int cc = min(c0 + c, C - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xa[i] = ld_vec(xp + (size_t)cc * 128 + 8 * i);
+  };
+  float acc[NR];
+#pragma unroll
+  for (int s = 0; s < NR; ++s) acc[s] = 0.f;
+  u32x4 xc[4], xn[4];
+  load_x(xc, 0);
+  // keep every load above issued here: left alone, the scheduler sinks each
+  // chunk's weight loads to just before their use
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c + 1 < NCH) load_x(xn, c + 1);
+    __builtin_amdgcn_sched_barrier(0);   // the next chunk's fragments in flight during this one
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      w4m_f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      const uint32_t wd[4] = {wq[c][s].x, wq[c][s].y, wq[c][s].z, wq[c][s].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(w4m_bf16x8, xc[i]),
+                                                    __builtin_bit_cast(w4m_bf16x8, w4b_unpack(wd[i])), d, 0, 0, 0);
+      // chunks past the row (clamped loads) count with scale 0
+      acc[s] = fmaf(c < cnt ? bf16_bits_to_f32(sc[c][s]) : 0.f, (d[0] + d[1]) + d[2], acc[s]);
+    }
+    if (c + 1 < NCH) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xc[i] = xn[i];
+    }
+  }
+  // lane group q holds activation row q's sums; the waves meet in LDS
+#pragma unroll
+  for (int s = 0; s < NR; ++s) part[wave][q][s][n] = acc[s];
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int b = threadIdx.x >> 4, row = r0 + (threadIdx.x & 15);
+  if (b >= p.B || row >= p.n_out) return;
+  float v[NR];
+#pragma unroll
+  for (int s = 0; s < NR; ++s) {
+    v[s] = 0.f;
+    for (int w = 0; w < NWV; ++w) v[s] += part[w][b][s][threadIdx.x & 15];
+  }
+  float out;
+  if (p.mode == GEMV_SWIGLU) out = silu_f(v[0]) * v[NR - 1];
+  else if (p.mode == GEMV_ADD) out = p.res[(size_t)b * p.ldres + row] + v[0];
+  else out = v[0];
+  if (p.yplanes) store_planes((uint16_t*)p.yplanes, (size_t)p.B * p.n_out, (size_t)b * p.n_out + row, out);
+  else p.y[(size_t)b * p.ldy + row] = out;
+}
+
+template <int NR, int NCH, int NWV>
+static hipError_t go_w4b(const GemvParams& p, hipStream_t s) {
+  launch_timed(gemv_w4b_kernel<NR, NCH, NWV>, dim3((p.n_out + 15) / 16), dim3(NWV * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+// 2 to 4 activation rows with 4-bit weights, the input planes at p.xn
+// (K a multiple of 128, at most 10,240).
+bool launch_gemv_w4_rows(const GemvParams& p, hipStream_t s, hipError_t* e) {
+  if (p.B < 2 || p.B > 4 || p.K % 128 || p.K > 10240 || !p.q4[0]) return false;
+  const int C = p.K / 128;
+  if (p.mode == GEMV_SWIGLU) {
+    if (C <= 24) *e = go_w4b<2, 3, 8>(p, s);
+    else if (C <= 48) *e = go_w4b<2, 3, 16>(p, s);
+    else *e = go_w4b<2, 5, 16>(p, s);
+  } else {
+    if (C <= 24) *e = go_w4b<1, 3, 8>(p, s);
+    else if (C <= 32) *e = go_w4b<1, 2, 16>(p, s);
+    else if (C <= 48) *e = go_w4b<1, 3, 16>(p, s);
+    else *e = go_w4b<1, 5, 16>(p, s);
+  }
+  return true;
+}
+
 // Two rows per wave for every 4-bit product (4 rows per wave measured slower
 // for each of them: 3.24-3.44 ms per frame against 3.17).
 template <int NR, int NUP, int KS>
@@ -1068,7 +1224,7 @@ static hipError_t pick_bt(const GemvParams& p, hipStream_t s) {
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s) {
   if (p.q4[0]) {
     if constexpr (sizeof(T) != 2) return hipErrorInvalidValue;
-    if (p.B >= 2) {   // prefill steps: the 2-D matrix-core tiles, from GEMM_TILE_MIN_ROWS rows
+    if (p.B >= 2) {   // 2-4 rows, or prefill steps of GEMM_TILE_MIN_ROWS+ rows (the 2-D tiles)
       hipError_t e;
       return launch_gemm_mfma(p, s, &e) ? e : hipErrorInvalidValue;
     }

@@ -43,9 +43,9 @@ struct QkPrep {
 // (w[0], w[1]) of a SwiGLU FFN whose output is silu(W1 h) * (W3 h).
 struct GemvParams {
   const void* w[3];
-  // 4-bit form of the segments (batch 1, or GEMM_TILE_MIN_ROWS+ rows on the
-  // 2-D tiles): q4[i] = packed [rows_i][K/2] bytes, s4[i] = bf16 scales
-  // [rows_i][K/128]; q4[0] == NULL: bf16 w[]
+  // 4-bit form of the segments (1 to GEMV_W4_MAX_ROWS rows, or
+  // GEMM_TILE_MIN_ROWS+ rows on the 2-D tiles): q4[i] = packed [rows_i][K/2]
+  // bytes, s4[i] = bf16 scales [rows_i][K/128]; q4[0] == NULL: bf16 w[]
   const void* q4[3]; const void* s4[3];
   int rows[3];
   int n_seg;
@@ -245,6 +245,9 @@ bool launch_gemm_mfma(const GemvParams& p, hipStream_t s, hipError_t* err);
 bool launch_gemm_tile(const GemvParams& p, bool wide, hipStream_t s);
 // the same with 4-bit weights (p.q4, p.s4; K a multiple of 128, at most 10,240)
 bool launch_gemm_tile_w4(const GemvParams& p, hipStream_t s);
+// 4-bit weights with 2..GEMV_W4_MAX_ROWS activation rows, input planes at p.xn
+#define GEMV_W4_MAX_ROWS 4
+bool launch_gemv_w4_rows(const GemvParams& p, hipStream_t s, hipError_t* e);
 bool gemm_tile_wide(const GemvParams& p);
 template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 template <typename T, typename KT> hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);

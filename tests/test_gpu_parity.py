@@ -674,6 +674,49 @@ def test_w4a16_chunked_prefill_row_lengths(dim, ffn, n_head, kv):
     assert sum(c) >= 2
 
 
+def _w4_small(kv):
+    return synth.model("tiny", weight_dtype="bf16", kv_dtype=kv, dim=512, ffn_dim=1024, fast_dim=512,
+                       fast_ffn_dim=1024, n_head=4, n_kv_head=1, head_dim=128, fast_n_head=4, fast_n_kv_head=1,
+                       fast_head_dim=128, w4a16=1, w4_bf16_attn_layers=1)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B,kv,pc", [(2, "bf16", 1), (3, "f32", 1), (4, "bf16", 1), (4, "f32", 0)])
+def test_w4a16_small_batch(B, kv, pc):
+    # 4-bit products over 2-4 activation rows on the matrix cores (the batch's
+    # rows as product rows 4b + t, t the activation term, read from the
+    # input planes); ragged prompts, greedy, 5 frames; one position per
+    # prefill step, or (pc 0) one step of 256 padded positions per sequence on
+    # the 4-bit 2-D tiles
+    m = _w4_small(kv)
+    from oracle import dequant_w4
+    w4 = synth.make_w4_model(m, synth.make_weights(m, seed=18))
+    wf = dequant_w4(synth.weights_as_f32(m, w4))
+    plen = np.array([40, 17, 33, 25][:B], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=18)
+    c, worst = run_and_compare(m, w4, P, plen, 5, dict(greedy=1), tag=f"w4-b{B}-{kv}-pc{pc}", weights_f32=wf,
+                               floor=kv == "bf16", prefill_chunk=pc)
+    assert sum(c) >= 2 * B
+
+
+@pytest.mark.timeout(900)
+def test_w4a16_batch4_s2_shapes_top_p():
+    # the S2 shapes with 3 slow layers (layers 0-1 fully 4-bit, layer 2 with
+    # bf16 attention, 4-bit fast layers), batch 4, ragged prompts of 300, 120,
+    # 77 and 210 tokens (one prefill step on the 4-bit 2-D tiles), top-p 0.9
+    # on an fp32 cache, 3 frames
+    from oracle import dequant_w4
+    m = synth.model("s2", n_layer=3, w4a16=1, w4_bf16_attn_layers=1, kv_dtype="f32")
+    w4 = synth.make_w4_model(m, synth.make_weights(m, seed=19))
+    wf = dequant_w4(synth.weights_as_f32(m, w4))
+    plen = np.array([300, 120, 77, 210], dtype=np.int32)
+    P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=19)
+    U = synth.make_uniforms((4, 4, m["num_codebooks"]), seed=19)
+    c, worst = run_and_compare(m, w4, P, plen, 3, dict(greedy=0, temperature=1.0, top_p=0.9), U,
+                               tag="w4-s2-b4-topp", weights_f32=wf)
+    assert sum(c) >= 8
+
+
 def test_end_token_stops_and_pads(tiny):
     m, w = tiny
     w = {k: v.copy() for k, v in w.items()}
