@@ -875,14 +875,16 @@ bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   // 4-bit weights: 2-4 rows or the 2-D tile form
   if (p0.q4[0] && p0.B > GEMV_W4_MAX_ROWS && p0.B < GM_TILE_ROWS) return false;
   GemvParams p = p0;
-  if (p.xplanes) p.xn = const_cast<void*>(p.xplanes);   // input already split by its producer
-  else hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
   if (p.q4[0] && p.B <= GEMV_W4_MAX_ROWS) {
     if (p.prep_done) *p.prep_done = 0;
     if (p.next_done) *p.next_done = 0;
+    if (p.xplanes) p.xn = const_cast<void*>(p.xplanes);
+    else if (!gemv_w4_rows_normalises(p)) hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
     if (!launch_gemv_w4_rows(p, s, err)) *err = hipErrorInvalidValue;
     return true;
   }
+  if (p.xplanes) p.xn = const_cast<void*>(p.xplanes);   // input already split by its producer
+  else hipLaunchKernelGGL(xsplit_kernel, dim3(p.B), dim3(DUALAR_WG), 0, s, p);
   bool ok = false;
   const bool glu = p.mode == GEMV_SWIGLU;
   const int z_tiles = (p.B + 31) / 32;

@@ -976,15 +976,38 @@ __device__ __forceinline__ u32x4 w4b_unpack(uint32_t d) {
 typedef __attribute__((address_space(1))) const u32x4 w4b_gvec;
 typedef __attribute__((address_space(1))) const uint16_t w4b_gu16;
 
-template <int NR, int NCH, int NWV>
+// NORM: the input is x (fp32, RMSNorm with p.gain when set) rather than
+// planes: the workgroup splits x * gain into the three terms in LDS itself
+// (its input loads issued before the weights, so that waiting for them leaves
+// the weights in flight), sums each row's squares, and scales the finished
+// sums by 1 / rms -- no separate split launch.
+#define W4B_XU 8   // NORM: float4 input units per thread at most
+
+template <int NR, int NCH, int NWV, bool NORM>
 __global__ void __launch_bounds__(NWV * 64) gemv_w4b_kernel(GemvParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xl[];   // NORM: the input terms [3][B][K]
   __shared__ float part[NWV][4][NR][16];
+  __shared__ float ssw[NWV][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, n = lane & 15;
   const int C = p.K >> 7;
   const int c0 = wave * NCH;
   const int cnt = min(NCH, C - c0);              // chunks of this wave (<= 0: none)
   const int r0 = blockIdx.x * 16;
+  constexpr int NT = NWV * 64;
+  const int nx4 = p.B * p.K / 4;                 // NORM: float4 units of the input
+  float4 xv[NORM ? W4B_XU : 1];
+  uint2 gv[NORM ? W4B_XU : 1];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int u = 0; u < W4B_XU; ++u) {
+      const int e = 4 * min((int)threadIdx.x + u * NT, nx4 - 1);
+      const int b = e / p.K, k = e - b * p.K;
+      xv[u] = *(const float4*)(p.x + (size_t)b * p.ldx + k);
+      gv[u] = p.gain ? *(const uint2*)((const uint16_t*)p.gain + k) : make_uint2(0x3F803F80u, 0x3F803F80u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // weights and scales of the 16 rows
   u32x4 wq[NCH][NR];
   uint32_t sc[NCH][NR];
@@ -1012,11 +1035,49 @@ __global__ void __launch_bounds__(NWV * 64) gemv_w4b_kernel(GemvParams p) {
       }
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (NORM) {
+    // x * gain as three bf16 terms into LDS; each row's sum of squares of x
+#pragma unroll
+    for (int u = 0; u < W4B_XU; ++u) {
+      const int e4 = (int)threadIdx.x + u * NT;
+      if (e4 >= nx4) break;
+      const int e = 4 * e4, b = e / p.K, k = e - b * p.K;
+      const float xs[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+      const uint32_t gs[4] = {gv[u].x & 0xffffu, gv[u].x >> 16, gv[u].y & 0xffffu, gv[u].y >> 16};
+      uint32_t t[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+      float sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sq = fmaf(xs[j], xs[j], sq);
+        const float xg = xs[j] * bf16_bits_to_f32(gs[j]);
+        const uint32_t a0 = f32_to_bf16_rne(xg);
+        const float r1 = xg - bf16_bits_to_f32(a0);
+        const uint32_t a1 = f32_to_bf16_rne(r1);
+        const uint32_t a2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(a1));
+        t[0][j >> 1] |= a0 << (16 * (j & 1));
+        t[1][j >> 1] |= a1 << (16 * (j & 1));
+        t[2][j >> 1] |= a2 << (16 * (j & 1));
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss[r] += b == r ? sq : 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 3; ++tt)
+        *(uint2*)&xl[((size_t)tt * p.B + b) * p.K + k] = make_uint2(t[tt][0], t[tt][1]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = wave_sum(ss[r]);
+      if (lane == 0) ssw[wave][r] = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the weights stay in flight
+  }
   // activation fragments: A row n = term (n & 3) of activation row n >> 2;
   // rows with n & 3 == 3 or n >> 2 >= B read a clamped row: their result rows
   // are never read
   const int ab = min(n >> 2, p.B - 1), at = min(n & 3, 2);
-  const uint16_t* xp = (const uint16_t*)p.xn + ((size_t)at * p.B + ab) * p.K + 32 * q;
+  const uint16_t* xp = (NORM ? (const uint16_t*)xl : (const uint16_t*)p.xn) + ((size_t)at * p.B + ab) * p.K + 32 * q;
   auto load_x = [&](u32x4 (&xa)[4], int c) __attribute__((always_inline)) {
     const int cc = min(c0 + c, C - 1);
 #pragma unroll
@@ -1057,11 +1118,18 @@ __global__ void __launch_bounds__(NWV * 64) gemv_w4b_kernel(GemvParams p) {
   if (threadIdx.x >= 64) return;
   const int b = threadIdx.x >> 4, row = r0 + (threadIdx.x & 15);
   if (b >= p.B || row >= p.n_out) return;
+  float inv = 1.f;
+  if (NORM && p.gain) {
+    float tot = 0.f;
+    for (int w = 0; w < NWV; ++w) tot += ssw[w][b];
+    inv = 1.0f / sqrtf(tot / (float)p.K + p.eps);
+  }
   float v[NR];
 #pragma unroll
   for (int s = 0; s < NR; ++s) {
     v[s] = 0.f;
     for (int w = 0; w < NWV; ++w) v[s] += part[w][b][s][threadIdx.x & 15];
+    v[s] *= inv;
   }
   float out;
   if (p.mode == GEMV_SWIGLU) out = silu_f(v[0]) * v[NR - 1];
@@ -1072,25 +1140,41 @@ __global__ void __launch_bounds__(NWV * 64) gemv_w4b_kernel(GemvParams p) {
 }
 
 template <int NR, int NCH, int NWV>
-static hipError_t go_w4b(const GemvParams& p, hipStream_t s) {
-  launch_timed(gemv_w4b_kernel<NR, NCH, NWV>, dim3((p.n_out + 15) / 16), dim3(NWV * 64), 0, s, p);
+static hipError_t go_w4b(const GemvParams& p, bool norm, hipStream_t s) {
+  const dim3 grid((p.n_out + 15) / 16), block(NWV * 64);
+  if (norm)
+    launch_timed(gemv_w4b_kernel<NR, NCH, NWV, true>, grid, block, (uint32_t)(6 * p.B * p.K), s, p);
+  else
+    launch_timed(gemv_w4b_kernel<NR, NCH, NWV, false>, grid, block, 0u, s, p);
   return hipGetLastError();
 }
 
-// 2 to 4 activation rows with 4-bit weights, the input planes at p.xn
-// (K a multiple of 128, at most 10,240).
+// Threads per workgroup of the 4-bit batched form for a row of K inputs.
+static int w4b_threads(int K) { return K / 128 <= 24 ? 512 : 1024; }
+
+// Whether the 4-bit batched form splits (and normalises) its fp32 input
+// itself: the terms of the B rows must fit in LDS (64 KB) and the input in
+// W4B_XU float4 units per thread.
+bool gemv_w4_rows_normalises(const GemvParams& p) {
+  return !p.xplanes && 6 * p.B * p.K <= 65536 && p.B * p.K <= 4 * W4B_XU * w4b_threads(p.K) && p.K % 4 == 0;
+}
+
+// 2 to 4 activation rows with 4-bit weights: the input planes at p.xn, or
+// (gemv_w4_rows_normalises) the fp32 input at p.x (K a multiple of 128, at
+// most 10,240).
 bool launch_gemv_w4_rows(const GemvParams& p, hipStream_t s, hipError_t* e) {
   if (p.B < 2 || p.B > 4 || p.K % 128 || p.K > 10240 || !p.q4[0]) return false;
+  const bool norm = gemv_w4_rows_normalises(p);
   const int C = p.K / 128;
   if (p.mode == GEMV_SWIGLU) {
-    if (C <= 24) *e = go_w4b<2, 3, 8>(p, s);
-    else if (C <= 48) *e = go_w4b<2, 3, 16>(p, s);
-    else *e = go_w4b<2, 5, 16>(p, s);
+    if (C <= 24) *e = go_w4b<2, 3, 8>(p, norm, s);
+    else if (C <= 48) *e = go_w4b<2, 3, 16>(p, norm, s);
+    else *e = go_w4b<2, 5, 16>(p, norm, s);
   } else {
-    if (C <= 24) *e = go_w4b<1, 3, 8>(p, s);
-    else if (C <= 32) *e = go_w4b<1, 2, 16>(p, s);
-    else if (C <= 48) *e = go_w4b<1, 3, 16>(p, s);
-    else *e = go_w4b<1, 5, 16>(p, s);
+    if (C <= 24) *e = go_w4b<1, 3, 8>(p, norm, s);
+    else if (C <= 32) *e = go_w4b<1, 2, 16>(p, norm, s);
+    else if (C <= 48) *e = go_w4b<1, 3, 16>(p, norm, s);
+    else *e = go_w4b<1, 5, 16>(p, norm, s);
   }
   return true;
 }

@@ -248,6 +248,8 @@ bool launch_gemm_tile_w4(const GemvParams& p, hipStream_t s);
 // 4-bit weights with 2..GEMV_W4_MAX_ROWS activation rows, input planes at p.xn
 #define GEMV_W4_MAX_ROWS 4
 bool launch_gemv_w4_rows(const GemvParams& p, hipStream_t s, hipError_t* e);
+// whether that form splits (and normalises) its fp32 input itself (no planes given)
+bool gemv_w4_rows_normalises(const GemvParams& p);
 bool gemm_tile_wide(const GemvParams& p);
 template <typename T, typename KT> hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 template <typename T, typename KT> hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
