@@ -2,7 +2,7 @@
 dominant kernel and the CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W] [--reps R] [--workload s2_b1|s2_b32|s2_prefill|s2_fast_tf|fast_s2|
-                    fast_s2_b16|tiny_b1|s2_b1_w4|s2_b4_w4] [--semantic-head] [--ras] [--no-batch32]
+                    fast_s2_b16|tiny_b1|s2_b1_w4|s2_b4_w4|s2_b8_w4] [--semantic-head] [--ras] [--no-batch32]
 
 A step is one decode frame of the whole hot path (fusion, slow pass, biased
 sample, ten fast passes with their samples) over one batch.  Inputs are
@@ -44,6 +44,8 @@ WORKLOADS = {
                                 "with bf16 scales; the last 12 slow layers' attention, the embeddings and "
                                 "heads in bf16), 1,024-token prompt, greedy"),
     "s2_b4_w4": ("s2_b1", 4, "full S2-shaped Dual-AR decode, batch 4, W4A16 weights (as s2_b1_w4), "
+                             "1,024-token prompts, greedy"),
+    "s2_b8_w4": ("s2_b1", 8, "full S2-shaped Dual-AR decode, batch 8, W4A16 weights (as s2_b1_w4), "
                              "1,024-token prompts, greedy"),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0

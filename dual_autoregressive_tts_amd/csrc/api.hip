@@ -815,7 +815,7 @@ dualar_status dispatch(dualar_ctx* c, F&& f) {
 }
 
 static_assert(RAS_HIST_STRIDE == DUALAR_RAS_MAX_WINDOW, "loop-breaker window stride");
-static_assert(GEMM_TILE_MIN_ROWS == 256 && GEMV_W4_MAX_ROWS == 4, "the 4-bit error messages name 256 and 4 rows");
+static_assert(GEMM_TILE_MIN_ROWS == 256 && GEMV_W4_MAX_ROWS == 8, "the 4-bit error messages name 256 and 8 rows");
 
 dualar_status check_sampling(dualar_ctx* c, const dualar_sampling* s, const float* uniforms) {
   if (!s) return fail(c, DUALAR_ERR_INVALID_ARG, "sampling is NULL");
@@ -964,7 +964,7 @@ dualar_status create_ctx(const dualar_config* cfg, const dualar_weights* w, void
   if (w->layers_w4 || w->fast_layers_w4) {
     if (r.esz != 2 || r.max_batch > GEMV_W4_MAX_ROWS || (r.pc != 1 && r.pc < GEMM_TILE_MIN_ROWS))
       return fail(c, DUALAR_ERR_INVALID_ARG,
-                  "4-bit matrices need bf16 weights, max_batch at most 4 and prefill_chunk 1 or at least 256");
+                  "4-bit matrices need bf16 weights, max_batch at most 8 and prefill_chunk 1 or at least 256");
     const char* e = w4_check(w->layers_w4, r.n_layer, r.dim, r.H, r.KV, r.hd, r.ffn);
     if (!e) e = w4_check(w->fast_layers_w4, r.fn_layer, r.dim, r.fH, r.fKV, r.fhd, r.fffn);
     if (e) return fail(c, DUALAR_ERR_INVALID_ARG, e);

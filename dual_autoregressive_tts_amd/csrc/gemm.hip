@@ -872,7 +872,7 @@ static void launch_gm(GemvParams& p, int ksw_preset, int slots, hipStream_t s, b
 // workgroups the chip holds at once (LDS bound).
 bool launch_gemm_mfma(const GemvParams& p0, hipStream_t s, hipError_t* err) {
   if (p0.B < 2 || p0.K % GM_KC != 0 || !p0.xn || p0.K > NORM_MAXV * 4 * DUALAR_WG) return false;
-  // 4-bit weights: 2-4 rows or the 2-D tile form
+  // 4-bit weights: 2 to GEMV_W4_MAX_ROWS rows or the 2-D tile form
   if (p0.q4[0] && p0.B > GEMV_W4_MAX_ROWS && p0.B < GM_TILE_ROWS) return false;
   GemvParams p = p0;
   if (p.q4[0] && p.B <= GEMV_W4_MAX_ROWS) {

@@ -940,7 +940,7 @@ static bool launch_w4m(const GemvParams& p, hipStream_t s, hipError_t* e) {
 }
 
 // ---------------------------------------------------------------------------
-// 4-bit weights, 2 to 4 activation rows (batched W4A16 decode)
+// 4-bit weights, 2 to 8 activation rows (batched W4A16 decode)
 // ---------------------------------------------------------------------------
 // The matrix-core form above with the activations taken from the three bf16
 // planes [3][B][K] of the batched path (the input split, or a producer's
@@ -983,10 +983,13 @@ typedef __attribute__((address_space(1))) const uint16_t w4b_gu16;
 // sums by 1 / rms -- no separate split launch.
 #define W4B_XU 8   // NORM: float4 input units per thread at most
 
-template <int NR, int NCH, int NWV, bool NORM>
+// G groups of 4 activation rows (B <= 4 G): each unpacked weight fragment
+// feeds G products, one per group.
+template <int NR, int NCH, int NWV, bool NORM, int G>
 __global__ void __launch_bounds__(NWV * 64) gemv_w4b_kernel(GemvParams p) {
+  static_assert(!NORM || G == 1, "the input terms of more than 4 rows do not fit the LDS budget");
   extern __shared__ __attribute__((aligned(16))) uint16_t xl[];   // NORM: the input terms [3][B][K]
-  __shared__ float part[NWV][4][NR][16];
+  __shared__ float part[NWV][4 * G][NR][16];
   __shared__ float ssw[NWV][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, n = lane & 15;
@@ -1073,20 +1076,26 @@ __global__ void __launch_bounds__(NWV * 64) gemv_w4b_kernel(GemvParams p) {
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the weights stay in flight
   }
-  // activation fragments: A row n = term (n & 3) of activation row n >> 2;
-  // rows with n & 3 == 3 or n >> 2 >= B read a clamped row: their result rows
-  // are never read
-  const int ab = min(n >> 2, p.B - 1), at = min(n & 3, 2);
-  const uint16_t* xp = (NORM ? (const uint16_t*)xl : (const uint16_t*)p.xn) + ((size_t)at * p.B + ab) * p.K + 32 * q;
-  auto load_x = [&](u32x4 (&xa)[4], int c) __attribute__((always_inline)) {
+  // activation fragments: A row n of group g = term (n & 3) of activation
+  // row 4 g + (n >> 2); rows with n & 3 == 3 or past B read a clamped row:
+  // their result rows are never read
+  const int at = min(n & 3, 2);
+  const uint16_t* xbase = (NORM ? (const uint16_t*)xl : (const uint16_t*)p.xn) + (size_t)at * p.B * p.K + 32 * q;
+  auto load_x = [&](u32x4 (&xa)[G][4], int c) __attribute__((always_inline)) {
     const int cc = min(c0 + c, C - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = ld_vec(xp + (size_t)cc * 128 + 8 * i);
-  };
-  float acc[NR];
+    for (int g = 0; g < G; ++g) {
+      const uint16_t* xp = xbase + (size_t)min(4 * g + (n >> 2), p.B - 1) * p.K + (size_t)cc * 128;
 #pragma unroll
-  for (int s = 0; s < NR; ++s) acc[s] = 0.f;
-  u32x4 xc[4], xn[4];
+      for (int i = 0; i < 4; ++i) xa[g][i] = ld_vec(xp + 8 * i);
+    }
+  };
+  float acc[G][NR];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int s = 0; s < NR; ++s) acc[g][s] = 0.f;
+  u32x4 xc[G][4], xn[G][4];
   load_x(xc, 0);
   // keep every load above issued here: left alone, the scheduler sinks each
   // chunk's weight loads to just before their use
@@ -1097,25 +1106,38 @@ __global__ void __launch_bounds__(NWV * 64) gemv_w4b_kernel(GemvParams p) {
     __builtin_amdgcn_sched_barrier(0);   // the next chunk's fragments in flight during this one
 #pragma unroll
     for (int s = 0; s < NR; ++s) {
-      w4m_f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      w4m_f32x4 d[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) d[g] = w4m_f32x4{0.f, 0.f, 0.f, 0.f};
       const uint32_t wd[4] = {wq[c][s].x, wq[c][s].y, wq[c][s].z, wq[c][s].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(w4m_bf16x8, xc[i]),
-                                                    __builtin_bit_cast(w4m_bf16x8, w4b_unpack(wd[i])), d, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 w = w4b_unpack(wd[i]);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          d[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(w4m_bf16x8, xc[g][i]),
+                                                         __builtin_bit_cast(w4m_bf16x8, w), d[g], 0, 0, 0);
+      }
       // chunks past the row (clamped loads) count with scale 0
-      acc[s] = fmaf(c < cnt ? bf16_bits_to_f32(sc[c][s]) : 0.f, (d[0] + d[1]) + d[2], acc[s]);
+      const float scale = c < cnt ? bf16_bits_to_f32(sc[c][s]) : 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[g][s] = fmaf(scale, (d[g][0] + d[g][1]) + d[g][2], acc[g][s]);
     }
     if (c + 1 < NCH) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xc[i] = xn[i];
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xc[g][i] = xn[g][i];
     }
   }
-  // lane group q holds activation row q's sums; the waves meet in LDS
+  // lane group q of group g holds activation row 4 g + q's sums; the waves
+  // meet in LDS
 #pragma unroll
-  for (int s = 0; s < NR; ++s) part[wave][q][s][n] = acc[s];
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int s = 0; s < NR; ++s) part[wave][4 * g + q][s][n] = acc[g][s];
   __syncthreads();
-  if (threadIdx.x >= 64) return;
+  if (threadIdx.x >= 64 * G) return;
   const int b = threadIdx.x >> 4, row = r0 + (threadIdx.x & 15);
   if (b >= p.B || row >= p.n_out) return;
   float inv = 1.f;
@@ -1143,9 +1165,11 @@ template <int NR, int NCH, int NWV>
 static hipError_t go_w4b(const GemvParams& p, bool norm, hipStream_t s) {
   const dim3 grid((p.n_out + 15) / 16), block(NWV * 64);
   if (norm)
-    launch_timed(gemv_w4b_kernel<NR, NCH, NWV, true>, grid, block, (uint32_t)(6 * p.B * p.K), s, p);
+    launch_timed(gemv_w4b_kernel<NR, NCH, NWV, true, 1>, grid, block, (uint32_t)(6 * p.B * p.K), s, p);
+  else if (p.B <= 4)
+    launch_timed(gemv_w4b_kernel<NR, NCH, NWV, false, 1>, grid, block, 0u, s, p);
   else
-    launch_timed(gemv_w4b_kernel<NR, NCH, NWV, false>, grid, block, 0u, s, p);
+    launch_timed(gemv_w4b_kernel<NR, NCH, NWV, false, 2>, grid, block, 0u, s, p);
   return hipGetLastError();
 }
 
@@ -1156,14 +1180,15 @@ static int w4b_threads(int K) { return K / 128 <= 24 ? 512 : 1024; }
 // itself: the terms of the B rows must fit in LDS (64 KB) and the input in
 // W4B_XU float4 units per thread.
 bool gemv_w4_rows_normalises(const GemvParams& p) {
-  return !p.xplanes && 6 * p.B * p.K <= 65536 && p.B * p.K <= 4 * W4B_XU * w4b_threads(p.K) && p.K % 4 == 0;
+  return !p.xplanes && p.B <= 4 && 6 * p.B * p.K <= 65536 && p.B * p.K <= 4 * W4B_XU * w4b_threads(p.K) &&
+         p.K % 4 == 0;
 }
 
-// 2 to 4 activation rows with 4-bit weights: the input planes at p.xn, or
+// 2 to GEMV_W4_MAX_ROWS activation rows with 4-bit weights: the input planes at p.xn, or
 // (gemv_w4_rows_normalises) the fp32 input at p.x (K a multiple of 128, at
 // most 10,240).
 bool launch_gemv_w4_rows(const GemvParams& p, hipStream_t s, hipError_t* e) {
-  if (p.B < 2 || p.B > 4 || p.K % 128 || p.K > 10240 || !p.q4[0]) return false;
+  if (p.B < 2 || p.B > GEMV_W4_MAX_ROWS || p.K % 128 || p.K > 10240 || !p.q4[0]) return false;
   const bool norm = gemv_w4_rows_normalises(p);
   const int C = p.K / 128;
   if (p.mode == GEMV_SWIGLU) {
@@ -1308,7 +1333,7 @@ static hipError_t pick_bt(const GemvParams& p, hipStream_t s) {
 template <typename T> hipError_t launch_gemv(const GemvParams& p, hipStream_t s) {
   if (p.q4[0]) {
     if constexpr (sizeof(T) != 2) return hipErrorInvalidValue;
-    if (p.B >= 2) {   // 2-4 rows, or prefill steps of GEMM_TILE_MIN_ROWS+ rows (the 2-D tiles)
+    if (p.B >= 2) {   // 2 to GEMV_W4_MAX_ROWS rows, or prefill steps of GEMM_TILE_MIN_ROWS+ rows (the 2-D tiles)
       hipError_t e;
       return launch_gemm_mfma(p, s, &e) ? e : hipErrorInvalidValue;
     }

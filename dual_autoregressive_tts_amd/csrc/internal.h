@@ -246,7 +246,7 @@ bool launch_gemm_tile(const GemvParams& p, bool wide, hipStream_t s);
 // the same with 4-bit weights (p.q4, p.s4; K a multiple of 128, at most 10,240)
 bool launch_gemm_tile_w4(const GemvParams& p, hipStream_t s);
 // 4-bit weights with 2..GEMV_W4_MAX_ROWS activation rows, input planes at p.xn
-#define GEMV_W4_MAX_ROWS 4
+#define GEMV_W4_MAX_ROWS 8
 bool launch_gemv_w4_rows(const GemvParams& p, hipStream_t s, hipError_t* e);
 // whether that form splits (and normalises) its fp32 input itself (no planes given)
 bool gemv_w4_rows_normalises(const GemvParams& p);

@@ -126,7 +126,7 @@ typedef struct {
  * weight is q * scale.  Device pointers, 16-byte aligned.  wq/wk/wv must be
  * all 4-bit or all bf16, and so must w1/w3.  A 4-bit matrix's rows must be
  * a multiple of 512 inputs, at most 10,240.  Only for bf16 models with
- * max_batch <= 4 and prefill_chunk = 1 or >= 256 (decode products run as
+ * max_batch <= 8 and prefill_chunk = 1 or >= 256 (decode products run as
  * 4-bit GEMVs over the batch's rows; prefill steps of 256+ positions run on
  * the matrix cores with each group's sum scaled in fp32); dualar_create
  * rejects other uses with DUALAR_ERR_INVALID_ARG.  With 4-bit fast layers,

@@ -102,7 +102,7 @@ def test_create_checks_before_device(lib):
 
 
 def test_create_checks_w4_forms(lib):
-    # 4-bit matrices (W4A16): batches of at most 4, prefill steps of one
+    # 4-bit matrices (W4A16): batches of at most 8, prefill steps of one
     # position or of at least 256 (the 2-D tile form);
     # a 4-bit form may stand in for a missing bf16 matrix, not a missing one of
     # both; q/k/v share a form; pointers 16-byte aligned
@@ -123,11 +123,11 @@ def test_create_checks_w4_forms(lib):
         need = lib.dualar_workspace_bytes(C.byref(cfg))
         return lib.dualar_create(C.byref(cfg), C.byref(w), C.c_void_p(256), need, None, C.byref(h))
 
-    assert create(5, 1) == -1 and b"max_batch at most 4" in lib.dualar_last_error(None)
+    assert create(9, 1) == -1 and b"max_batch at most 8" in lib.dualar_last_error(None)
     for pc in (2, 255):
         assert create(1, pc) == -1 and b"prefill_chunk 1 or at least 256" in lib.dualar_last_error(None)
     if not torch.cuda.is_available():
-        for batch, pc in ((1, 1), (1, 256), (1, 0), (4, 1), (3, 0)):   # 0: the default chunk
+        for batch, pc in ((1, 1), (1, 256), (1, 0), (4, 1), (3, 0), (8, 1)):   # 0: the default chunk
             assert create(batch, pc) == -2                  # valid: fails only for want of a device
     l4[0].q4[1] = None                                      # wk bf16 while wq, wv are 4-bit
     assert create(1, 1) == -1 and b"all 4-bit or all bf16" in lib.dualar_last_error(None)

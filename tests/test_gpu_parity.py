@@ -681,18 +681,20 @@ def _w4_small(kv):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("B,kv,pc", [(2, "bf16", 1), (3, "f32", 1), (4, "bf16", 1), (4, "f32", 0)])
+@pytest.mark.parametrize("B,kv,pc", [(2, "bf16", 1), (3, "f32", 1), (4, "bf16", 1), (4, "f32", 0), (6, "f32", 1),
+                                    (8, "bf16", 1), (8, "f32", 0)])
 def test_w4a16_small_batch(B, kv, pc):
-    # 4-bit products over 2-4 activation rows on the matrix cores (the batch's
-    # rows as product rows 4b + t, t the activation term, read from the
-    # input planes); ragged prompts, greedy, 5 frames; one position per
-    # prefill step, or (pc 0) one step of 256 padded positions per sequence on
-    # the 4-bit 2-D tiles
+    # 4-bit products over 2-8 activation rows on the matrix cores (the batch's
+    # rows as product rows 4b + t, t the activation term, in one or two
+    # groups of four; up to 4 rows the kernel normalises and splits its input
+    # itself, above that it reads the input planes); ragged prompts, greedy,
+    # 5 frames; one position per prefill step, or (pc 0) one step of 256
+    # padded positions per sequence on the 4-bit 2-D tiles
     m = _w4_small(kv)
     from oracle import dequant_w4
     w4 = synth.make_w4_model(m, synth.make_weights(m, seed=18))
     wf = dequant_w4(synth.weights_as_f32(m, w4))
-    plen = np.array([40, 17, 33, 25][:B], dtype=np.int32)
+    plen = np.array([40, 17, 33, 25, 9, 31, 22, 38][:B], dtype=np.int32)
     P = synth.make_prompts(m, ("ragged", 1, 1), plen, seed=18)
     c, worst = run_and_compare(m, w4, P, plen, 5, dict(greedy=1), tag=f"w4-b{B}-{kv}-pc{pc}", weights_f32=wf,
                                floor=kv == "bf16", prefill_chunk=pc)
