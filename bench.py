@@ -52,14 +52,17 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 # HBM bytes per dispatch of the roofline kernels (the batch-1 SwiGLU W1|W3
-# GEMV: bf16 `gemv_rx_kernel`, 4-bit `gemv_w4_kernel`), from rocprofv3 --pmc
-# runs restricted to that kernel (bf16: `bench.py --steps 4 --warmup 2
-# --profile-frames 0 --no-cpu-baseline`; 4-bit: the same with `--workload
-# s2_b1_w4 --prompt-len 16`): FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
-# times the factor the same counter reads for a plain 1 GiB device copy
-# (bench.py --copy-calibration).  The figures hold for the kernel text they
-# were taken on: if a kernel's source changes, `traffic` is reported as null
-# until they are measured again.
+# GEMV: bf16 `gemv_rx_kernel`, 4-bit `gemv_w4_kernel`; at batch 32 the
+# stream-K W1|W3 product `mfma_skw_kernel<2, ...>` and its finish
+# `sk_finish_kernel<2, ...>`), from rocprofv3 --pmc runs restricted to that
+# kernel (bf16: `bench.py --steps 4 --warmup 2 --profile-frames 0
+# --no-cpu-baseline`; 4-bit: the same with `--workload s2_b1_w4 --prompt-len
+# 16`; batch 32: `--workload s2_b32 --steps 4 --warmup 2 --reps 1
+# --profile-frames 0 --no-cpu-baseline`): FETCH_SIZE and WRITE_SIZE (KiB per
+# dispatch) times the factor the same counter reads for a plain 1 GiB device
+# copy (bench.py --copy-calibration).  The figures hold for the kernel text
+# they were taken on: if a kernel's source changes, `traffic` is reported as
+# null until they are measured again.
 _FETCH_SCALE = 1073741824 / 1024 / 524300.3125
 _WRITE_SCALE = 1073741824 / 1024 / 1048576.0
 ROOFLINE_COUNTERS = {
@@ -67,14 +70,18 @@ ROOFLINE_COUNTERS = {
                        "sha256": "896f099c92dd1480f9cae59c9e461a974a00feaeec347ad0b0be964cd656bd96"},
     "gemv_w4_kernel": {"fetch_kib": 12721.425, "write_kib": 38.0,
                        "sha256": "56e7cfaa8dc156927292197036e869ffd7b4068527330939f40693f0a8368b6e"},
+    "mfma_skw_kernel": {"fetch_kib": 52029.7, "write_kib": 9888.1, "file": "gemm.hip",
+                        "sha256": "ab55fea37c92de250f2acc732bf687a8860b0d5ea2339bcc3dd5ed56bfce4415"},
+    "sk_finish_kernel": {"fetch_kib": 4987.0, "write_kib": 1824.0, "file": "gemm.hip",
+                         "sha256": "89c53e3a0000caa8d700f670a78d447ed45e23c1f718f4a65d564c5d2bf5a732"},
 }
 
 
-def kernel_source_sha256(name):
-    """SHA-256 of a kernel's text in gemv.hip: its template line to its closing brace."""
+def kernel_source_sha256(name, file="gemv.hip"):
+    """SHA-256 of a kernel's text in a csrc file: its template line to its closing brace."""
     import hashlib
-    src = open(os.path.join(ROOT, "dual_autoregressive_tts_amd", "csrc", "gemv.hip")).read()
-    i = src.index(f"__global__ void __launch_bounds__(DUALAR_WG) {name}(")
+    src = open(os.path.join(ROOT, "dual_autoregressive_tts_amd", "csrc", file)).read()
+    i = src.index(f" {name}(GemvParams p) {{")
     i = src.rindex("template", 0, i)
     j = src.index("\n}\n", i) + 3
     return hashlib.sha256(src[i:j].encode()).hexdigest()
@@ -84,9 +91,16 @@ def roofline_traffic(name="gemv_rx_kernel"):
     """Measured HBM bytes per launch of a roofline kernel, or None when they
     are missing or were taken on other kernel text."""
     c = ROOFLINE_COUNTERS.get(name)
-    if not c or c["write_kib"] is None or kernel_source_sha256(name) != c["sha256"]:
+    if not c or c["write_kib"] is None or kernel_source_sha256(name, c.get("file", "gemv.hip")) != c["sha256"]:
         return None
     return round(c["fetch_kib"] * 1024 * _FETCH_SCALE + c["write_kib"] * 1024 * _WRITE_SCALE)
+
+
+def b32_traffic():
+    """The batch-32 roofline pair (the stream-K W1|W3 product and its finish,
+    timed together): the sum of both kernels' measured bytes, or None."""
+    a, f = roofline_traffic("mfma_skw_kernel"), roofline_traffic("sk_finish_kernel")
+    return None if a is None or f is None else a + f
 
 
 def log(*a):
@@ -373,7 +387,8 @@ def decode_workload(args, name, torch, synth, DualAR, reporting, kit, m, w, dev_
                     "achieved": round(sw_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(sw_gbps / HBM_PEAK_GBPS, 4),
                     "traffic": ((roofline_traffic("gemv_w4_kernel") if w4 else roofline_traffic("gemv_rx_kernel"))
-                                if (B == 1 and m["weight_dtype"] == "bf16") else None),
+                                if (B == 1 and m["weight_dtype"] == "bf16") else
+                                b32_traffic() if (B == 32 and not w4 and m["weight_dtype"] == "bf16") else None),
                     "avg_launch_us": round(sw_avg_us, 3), "bytes_per_launch": round(sw_bytes),
                     "launches_profiled": f["launches"],
                     "gemv_family": {"achieved_GBps": round(gemv_gbps, 1), "avg_launch_us": round(gemv_avg_us, 3),

@@ -117,6 +117,23 @@ def test_w4_roofline_traffic_reads_weights_once():
     assert bench.roofline_traffic("no_such_kernel") is None
 
 
+def test_batch32_roofline_traffic_counts_the_stream_k_partials():
+    # batch 32: the stream-K W1|W3 product and its finish, timed together.
+    # Weights are read once (HBM bytes of the product >= the weights); the
+    # partial tiles the product writes are what its finish reads; the finish
+    # writes the SwiGLU output as three bf16 planes [3][32][9728]
+    import bench
+    p, f = bench.roofline_traffic("mfma_skw_kernel"), bench.roofline_traffic("sk_finish_kernel")
+    assert p is not None and f is not None and bench.b32_traffic() == p + f
+    weights = 2 * 9728 * 2560 * 2
+    c = bench.ROOFLINE_COUNTERS
+    wrote = c["mfma_skw_kernel"]["write_kib"] * 1024 * bench._WRITE_SCALE
+    read_back = c["sk_finish_kernel"]["fetch_kib"] * 1024 * bench._FETCH_SCALE
+    assert weights <= p - wrote <= 1.1 * weights
+    assert abs(read_back - wrote) <= 0.02 * wrote
+    assert abs(c["sk_finish_kernel"]["write_kib"] * 1024 - 3 * 32 * 9728 * 2) <= 4096
+
+
 def test_w4_frame_bytes_by_enumeration():
     # the 4-bit byte change of a frame-step against a direct count over the
     # model's tensors: every 4-bit matrix costs rows * (K/2 + K/128 * 2) bytes
