@@ -421,7 +421,9 @@ dualar_status run_layer(dualar_ctx* c, Stack& S, int l, float* x, int B, const i
   // with 4 loads per lane (batch 1, 1k context: 12.0 us per layer against 14.7
   // with 2).  Otherwise the balanced flash-decoding form (it = 8): at batch 4
   // and 16k positions the split form needs 256 splits per head and a merge.
-  a.it = (B <= 4 && Lmax <= 2048) ? 4 : 8;
+  // The fast layers' depth cache (at most 16 positions) takes it = 8 from
+  // batch 2 on, which selects the one-wave depth form where it applies.
+  a.it = (B <= 4 && Lmax <= 2048 && !(B >= 2 && !pos_dev && Lmax <= 16)) ? 4 : 8;
   // Batch 1, bf16 weights, the S2 head shape: the split form with at most
   // merge_o_b1_max_splits() chunks of 128 or 256 positions, its merge done by
   // the O product (each lane merges the eight values it multiplies).
