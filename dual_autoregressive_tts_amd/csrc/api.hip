@@ -1117,9 +1117,9 @@ dualar_status dualar_fast_teacher_forced(dualar_ctx_t* c, int32_t n, const float
       (c->fast.H / c->fast.KV) & (c->fast.H / c->fast.KV - 1))
     return fail(c, DUALAR_ERR_INVALID_ARG, "teacher-forced form needs N <= 11, fast head_dim <= 128 (a multiple "
                                            "of 4), 1, 2, 4 or 8 query heads per KV head");
-  if (c->fast.any_w4() && (long long)n * N < GEMM_TILE_MIN_ROWS)
+  if (c->fast.any_w4() && (long long)n * N > GEMV_W4_MAX_ROWS && (long long)n * N < GEMM_TILE_MIN_ROWS)
     return fail(c, DUALAR_ERR_INVALID_ARG, "with 4-bit fast layers the teacher-forced form needs n * num_codebooks "
-                                           ">= 256 rows");
+                                           "<= 8 or >= 256 rows");
   // the activation buffers are scratch between calls: the decode state is untouched
   MarkerRange mr("dualar.fast_tf");
   return dispatch(c, [&](auto wt, auto kt) {

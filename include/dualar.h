@@ -130,7 +130,7 @@ typedef struct {
  * 4-bit GEMVs over the batch's rows; prefill steps of 256+ positions run on
  * the matrix cores with each group's sum scaled in fp32); dualar_create
  * rejects other uses with DUALAR_ERR_INVALID_ARG.  With 4-bit fast layers,
- * dualar_fast_teacher_forced needs n * num_codebooks >= 256. */
+ * dualar_fast_teacher_forced needs n * num_codebooks <= 8 or >= 256. */
 typedef struct {
   const void *q4[7];             /* wq, wk, wv, wo, w1, w3, w2, or NULL */
   const void *s4[7];

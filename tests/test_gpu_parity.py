@@ -1067,9 +1067,10 @@ def test_tiny_fast_teacher_forced(tiny, n):
 @pytest.mark.timeout(600)
 def test_w4a16_fast_teacher_forced():
     # 4-bit fast layers in the teacher-forced form: 100 pairs x 4 codebooks =
-    # 400 rows on the 4-bit 2-D tiles, against the oracle on its own
-    # q * scale weights; 5 pairs (20 rows, fewer than the tiles take) are
-    # rejected before anything is enqueued
+    # 400 rows on the 4-bit 2-D tiles, and 2 pairs (8 rows) on the batched
+    # 4-bit GEMV, against the oracle on its own q * scale weights; 5 pairs
+    # (20 rows: more than the GEMV takes, fewer than the tiles) are rejected
+    # before anything is enqueued
     from oracle import dequant_w4
     from dual_autoregressive_tts_amd import DualARError
     DualAR, upload = _dev()
@@ -1088,6 +1089,7 @@ def test_w4a16_fast_teacher_forced():
         ctx.fast_teacher_forced(h[:5].contiguous(), codes[:5].contiguous())
     assert e.value.name == "INVALID_ARG"
     got = ctx.fast_teacher_forced(h, codes).cpu().numpy()
+    got2 = ctx.fast_teacher_forced(h[:2].contiguous(), codes[:2].contiguous()).cpu().numpy()
     assert ctx.sync() == 0
     ctx.close()
     o = DualAROracle(m, wf, max_seq=8)
@@ -1097,6 +1099,10 @@ def test_w4a16_fast_teacher_forced():
         e2 = rel_l2(got[i, 1:], ref)
         worst = max(worst, e2)
         assert e2 <= REL_L2, (i, e2)
+        if i < 2:
+            e3 = rel_l2(got2[i, 1:], ref)
+            worst = max(worst, e3)
+            assert e3 <= REL_L2, (i, e3)
     say(f"[w4-tf] worst rel L2 {worst:.2e}")
 
 
