@@ -946,8 +946,10 @@ static bool launch_w4m(const GemvParams& p, hipStream_t s, hipError_t* e) {
 // planes [3][B][K] of the batched path (the input split, or a producer's
 // output planes), which already hold the normalised input: A row 4b + t of
 // v_mfma_f32_16x16x32_bf16 is term t of activation row b (t < 3, b < B; the
-// other rows are zero), so lane group q = b of the result holds row b's three
-// term sums.  The chunk loop has no branches (a wave's chunks past the row
+// other rows repeat a clamped row and their results are never read), so lane
+// group q = b of the result holds row b's three term sums (with two groups
+// of four rows, a second product per weight fragment covers rows 4..7).  The
+// chunk loop has no branches (a wave's chunks past the row
 // are clamped loads with a zero scale) and the segment pointers are chosen by
 // selects among SGPR copies, so that every load is issued up front.  The
 // weights are unpacked exactly (the nibble's v + 8 less 8 in
