@@ -371,17 +371,23 @@ __global__ void __launch_bounds__(64) attn_prep_kernel(AttnParams p) {
 // inside the loop).  Per tile a wave
 //   - has the tile's K (A-operand layout of v_mfma_f32_16x16x32_bf16:
 //     16 positions x 32 dims per step, two 16-position groups) and V (16
-//     lanes x 8 dims per position, four positions per load) in registers,
-//     loaded two tiles ahead (two register buffers);
+//     lanes x 8 dims per position, four positions per load) in one register
+//     buffer each;
 //   - gets the scores of its 32 positions for the rep query heads from the
 //     matrix cores (q as three bf16 terms read straight from the prepared
-//     planes: the fp32 product), reduces each head's max and sum across the
-//     four lanes that hold it, and keeps a running max m and sum l per head;
+//     planes: the fp32 product), then issues the next tile's K into the
+//     buffer the scores no longer need;
+//   - reduces each head's max and sum across the four lanes that hold it and
+//     keeps a running max m and sum l per head;
 //   - passes the probabilities through a wave-private LDS slot into the P.V
-//     layout and rescales its accumulators by e^(m_old - m_new).
-// Positions past the segment are loaded from entry 0 (cached) and left out
-// of the scores and the P.V, so every load of the loop is unconditional and
-// the compiler's waits keep both buffers in flight.
+//     layout, rescales its accumulators by e^(m_old - m_new), adds P.V, and
+//     issues the next tile's V.
+// So each load is in flight behind half a tile of arithmetic.  Two whole
+// tiles in flight per wave (two register buffers, 242 registers), and K two
+// tiles ahead with V one (210), measured slower.  Positions
+// past the segment (and the tile after the last) are loaded from entry 0
+// (cached) and left out of the scores and the P.V, so every load of the
+// loop is unconditional and the compiler's waits are by count only.
 #define FL_TILE 128
 #define FL_MAXB 64
 #define FL_SLOTS 512   // workgroups of the balanced flash-decoding form (two per compute unit)
@@ -448,8 +454,8 @@ __global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, 
     const char* kbase = (const char*)p.kcache + head_base * HD * 2;
     const char* vbase = (const char*)p.vcache + head_base * HD * 2;
 
-    u32x4 ka[GW][4], va[IT], kb[GW][4], vb[IT];
-    auto load_tile = [&](u32x4 (&kk)[GW][4], u32x4 (&vv)[IT], int t) __attribute__((always_inline)) {
+    u32x4 ka[GW][4], va[IT];
+    auto load_k = [&](u32x4 (&kk)[GW][4], int t) __attribute__((always_inline)) {
       const int base = c0 + t * FL_TILE + 32 * wave;
 #pragma unroll
       for (int mm = 0; mm < GW; ++mm) {
@@ -458,6 +464,9 @@ __global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, 
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kk[mm][ks] = ld_vec(kbase + (e + 32 * ks) * 2);
       }
+    };
+    auto load_v = [&](u32x4 (&vv)[IT], int t) __attribute__((always_inline)) {
+      const int base = c0 + t * FL_TILE + 32 * wave;
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int j = base + 4 * it + grp;
@@ -473,8 +482,8 @@ __global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, 
         *(u32x4*)(&qlds[0][0][0] + (size_t)i * 8) = ld_vec(qsrc + qq * plane + (size_t)r * 8);
       }
     }
-    load_tile(ka, va, 0);
-    load_tile(kb, vb, 1);
+    load_k(ka, 0);
+    load_v(va, 0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     float m_run = -INFINITY, l_run = 0.f;     // for head `col` (lanes with col < REP)
@@ -484,7 +493,7 @@ __global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, 
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[hl][e] = 0.f;
 
-    auto tile = [&](const u32x4 (&kk)[GW][4], const u32x4 (&vv)[IT], int t) __attribute__((always_inline)) {
+    auto tile = [&](u32x4 (&kk)[GW][4], u32x4 (&vv)[IT], int t) __attribute__((always_inline)) {
       const int base = c0 + t * FL_TILE + 32 * wave;
       float sv[GW][4];
 #pragma unroll
@@ -504,6 +513,7 @@ __global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[mm][r] = base + 16 * mm + 4 * (lane >> 4) + r < c1 ? acc4[r] : -INFINITY;
       }
+      load_k(kk, t + 1);                      // the scores are done with this buffer
       float mt = -INFINITY;
 #pragma unroll
       for (int mm = 0; mm < GW; ++mm)
@@ -550,15 +560,11 @@ __global__ void __launch_bounds__(DUALAR_WG, 2) attn_flash_kernel(AttnParams p, 
           for (int e = 0; e < 8; ++e) acc[hl][e] = fmaf(pj, vf[e], acc[hl][e]);
         }
       }
+      load_v(vv, t + 1);                        // and the P.V with this one
       __builtin_amdgcn_wave_barrier();
     };
 
-    for (int t = 0; t < ntile; t += 2) {
-      tile(ka, va, t);
-      load_tile(ka, va, t + 2);
-      if (t + 1 < ntile) tile(kb, vb, t + 1);
-      load_tile(kb, vb, t + 3);
-    }
+    for (int t = 0; t < ntile; ++t) tile(ka, va, t);
 
     // ---- combine: the four position groups of each wave, then the waves ----
 #pragma unroll
