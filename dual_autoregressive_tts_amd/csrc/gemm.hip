@@ -618,6 +618,21 @@ __global__ void __launch_bounds__(DUALAR_WG) sk_finish_kernel(GemvParams p) {
   const int nch = p.sk_nch;
   const int nsl = sk_owner(t * nch + nch - 1, p.sk_q, p.sk_r) - sk_owner(t * nch, p.sk_q, p.sk_r) + 1;
   const float* base = p.part + (size_t)t * p.sk_smax * S::TE + (size_t)bl * ROWS + 4 * r4;
+  // The attention preparation's position and QK-norm gain go out with the
+  // slots, so only the RoPE table (indexed by the position) waits for them.
+  // Both loads are unconditional (a load under a branch would be waited for
+  // where the branch ends, before the slots are issued): where they do not
+  // apply they read the thread's first slot instead, and the value is unused.
+  const bool prep = NR == 1 && p.prep.q_planes;
+  const int hh_p = t / Z;
+  const uint16_t* qk_gain = (const uint16_t*)(hh_p < p.prep.H ? p.prep.q_norm : p.prep.k_norm);
+  const bool has_gain = prep && hh_p < p.prep.H + p.prep.KV && qk_gain;
+  const uint16_t* gsrc = has_gain ? qk_gain + 4 * r4 : (const uint16_t*)base;
+  const int* psrc = prep && p.prep.pos ? p.prep.pos + b : (const int*)base;
+  uint16_t graw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) graw[e] = gsrc[e];
+  const int praw = *psrc;
   float4 v[NR];
 #pragma unroll
   for (int s = 0; s < NR; ++s) v[s] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -644,7 +659,8 @@ __global__ void __launch_bounds__(DUALAR_WG) sk_finish_kernel(GemvParams p) {
     // each: RMS over the half-wave, RoPE on the two local pairs.
     const QkPrep& q = p.prep;
     const int hh = t / Z, d0 = 4 * r4, hd = q.hd;
-    const int pos = row_position(q.pos, q.pos_const, b, q.max_pos, q.status);
+    const int pv = q.pos ? praw : q.pos_const;
+    const int pos = pv < 0 ? pv : checked_index(pv, q.max_pos, q.status);
     float a[4] = {g4[0], g4[1], g4[2], g4[3]};
     *(float4*)(p.y + (size_t)b * p.ldy + n0) = make_float4(a[0], a[1], a[2], a[3]);
     const bool isq = hh < q.H, isk = !isq && hh < q.H + q.KV;
@@ -654,7 +670,7 @@ __global__ void __launch_bounds__(DUALAR_WG) sk_finish_kernel(GemvParams p) {
         const float ss = group_sum((a[0] * a[0] + a[1] * a[1]) + (a[2] * a[2] + a[3] * a[3]), 32);
         const float inv = 1.0f / sqrtf(ss / (float)hd + p.eps);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = a[e] * inv * bf16_bits_to_f32(((const uint16_t*)gain)[d0 + e]);
+        for (int e = 0; e < 4; ++e) a[e] = a[e] * inv * bf16_bits_to_f32(graw[e]);
       }
       if (pos < 0) return;
       const float2* rp = q.rope + (size_t)pos * (hd / 2) + d0 / 2;
@@ -712,8 +728,12 @@ __global__ void __launch_bounds__(SKR_T) sk_finish_rows_kernel(GemvParams p) {
   const int nv = p.n_out / 4, Z = (p.B + 31) / 32, nch = p.sk_nch;
   const bool live = tid < nv;
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint2 gg = make_uint2(0u, 0u);
   if (live) {
     const int n = 4 * tid, t = (n / ROWS) * Z + b / 32;
+    // the residual and the next gain go out with the slots: one memory round trip
+    const float4 r = *(const float4*)(p.res + (size_t)b * p.ldres + n);
+    gg = ((const uint2*)p.next_gain)[tid];
     const float* src = p.part + (size_t)t * p.sk_smax * S::TE + (size_t)(b & 31) * ROWS + n % ROWS;
     const int nsl = sk_owner(t * nch + nch - 1, p.sk_q, p.sk_r) - sk_owner(t * nch, p.sk_q, p.sk_r) + 1;
     for (int k0 = 0; k0 < nsl; k0 += KB) {
@@ -725,7 +745,6 @@ __global__ void __launch_bounds__(SKR_T) sk_finish_rows_kernel(GemvParams p) {
       for (int u = 0; u < KB; ++u)
         if (k0 + u < nsl) { v.x += a[u].x; v.y += a[u].y; v.z += a[u].z; v.w += a[u].w; }
     }
-    const float4 r = *(const float4*)(p.res + (size_t)b * p.ldres + n);
     v.x = r.x + v.x; v.y = r.y + v.y; v.z = r.z + v.z; v.w = r.w + v.w;
     *(float4*)(p.y + (size_t)b * p.ldy + n) = v;
   }
@@ -738,7 +757,6 @@ __global__ void __launch_bounds__(SKR_T) sk_finish_rows_kernel(GemvParams p) {
   for (int w = 0; w < SKR_T / 64; ++w) tot += red[w];
   if (!live) return;
   const float inv = 1.0f / sqrtf(tot / (float)p.n_out + p.eps);
-  const uint2 gg = ((const uint2*)p.next_gain)[tid];
   const float o[4] = {v.x * inv * bf16_bits_to_f32(gg.x & 0xffffu), v.y * inv * bf16_bits_to_f32(gg.x >> 16),
                       v.z * inv * bf16_bits_to_f32(gg.y & 0xffffu), v.w * inv * bf16_bits_to_f32(gg.y >> 16)};
   uint32_t tt[3][4];
