@@ -70,10 +70,10 @@ ROOFLINE_COUNTERS = {
                        "sha256": "896f099c92dd1480f9cae59c9e461a974a00feaeec347ad0b0be964cd656bd96"},
     "gemv_w4_kernel": {"fetch_kib": 12721.425, "write_kib": 38.0,
                        "sha256": "56e7cfaa8dc156927292197036e869ffd7b4068527330939f40693f0a8368b6e"},
-    "mfma_skw_kernel": {"fetch_kib": 52029.7, "write_kib": 9888.1, "file": "gemm.hip",
+    "mfma_skw_kernel": {"fetch_kib": 52015.6, "write_kib": 9888.1, "file": "gemm.hip",
                         "sha256": "ab55fea37c92de250f2acc732bf687a8860b0d5ea2339bcc3dd5ed56bfce4415"},
     "sk_finish_kernel": {"fetch_kib": 4987.0, "write_kib": 1824.0, "file": "gemm.hip",
-                         "sha256": "89c53e3a0000caa8d700f670a78d447ed45e23c1f718f4a65d564c5d2bf5a732"},
+                         "sha256": "6246a8116a74dce359ca6730f2ec28dff62bde13e0765a06fe9c3d9b100547fc"},
 }
 
 
